@@ -1,0 +1,106 @@
+"""Codecs of the KV-cache and Q formats, from their published definitions.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+* e4m3 ("float8_e4m3fn", the dtype the mjolnir-kernel runner maps fp8 Q and
+  fp8 KV to; wheel listing mjolnir/runner.py, ``_cutlass_dtype`` and the
+  ``FP8_MAX = 448`` constant): OCP 8-bit floating point, E4M3 variant — sign
+  bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+  subnormal (m/8 * 2^-6); no infinities; S.1111.111 is NaN; largest finite
+  magnitude 448.
+* e2m3 (the 6-bit KV format; PyPI project page, "fp6 (e2m3) KV in vLLM";
+  ``E2M3_MAX`` = 7.5 in mjolnir/backend.py, ``_install_fp6_scales``): OCP
+  Microscaling FP6 E2M3 — sign bit 5, exponent bits 4..3 with bias 1,
+  mantissa bits 2..0; exponent field 0 is subnormal (m/8); no NaN or
+  infinity; largest magnitude 7.5.
+* the packed 6-bit row: "e2m3 codes packed 4 per 3 bytes (little-endian
+  bitstream)" (mjolnir/runner.py, the comment above ``RUNNER_KV_FORMATS``).
+  Reading taken: code k of a row occupies stream bits [6k, 6k+6) and stream
+  bit 8B+j is bit j of byte B.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E2M3_MAX = 7.5
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one e4m3 code from its bit fields (NaN for S.1111.111)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e2m3_value(code: int) -> float:
+    """Value of one 6-bit e2m3 code from its bit fields."""
+    s = -1.0 if code & 0x20 else 1.0
+    e = (code >> 3) & 0x3
+    m = code & 0x7
+    if e == 0:
+        return s * (m / 8.0)
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 1)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+E2M3_TABLE = np.array([e2m3_value(c) for c in range(64)], dtype=np.float64)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e2m3_decode(codes: np.ndarray) -> np.ndarray:
+    return E2M3_TABLE[np.asarray(codes, dtype=np.uint8) & 0x3F]
+
+
+# finite non-negative e4m3 values in code order 0x00..0x7E (strictly increasing)
+_E4M3_POS = E4M3_TABLE[:0x7F]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round fp32 values to the nearest e4m3 code, ties to the even code.
+
+    Round-to-nearest-even over the finite e4m3 values, with the sign kept
+    (so -0 and tiny negatives give 0x80).  Domain: |x| <= 464, the midpoint
+    above 448 (the quantizer never leaves it: |x/s| <= 448 * (1 + 2^-23)).
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    if np.any(~np.isfinite(a)) or np.any(a > 464.0):
+        raise ValueError("e4m3_encode: value outside the rounding domain |x| <= 464")
+    # nearest of the candidates below and above a
+    hi = np.searchsorted(_E4M3_POS, a, side="left")  # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3_POS[hi] - a
+    d_lo = a - _E4M3_POS[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    # above 448 (hi clamped to 0x7E): 448 is the nearest finite value
+    code = np.where(a >= _E4M3_POS[0x7E], 0x7E, np.where(pick_hi, hi, lo))
+    sign = np.signbit(x)
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def unpack_6bit(rows: np.ndarray, n: int) -> np.ndarray:
+    """(..., 3n/4) bytes -> (..., n) codes of the little-endian 6-bit stream.
+
+    Written bit by bit from the stream definition: bit j (0..5) of code k is
+    stream bit 6k+j, which is bit (6k+j) % 8 of byte (6k+j) // 8.
+    """
+    rows = np.asarray(rows, dtype=np.uint8)
+    assert rows.shape[-1] * 8 == n * 6
+    out = np.zeros(rows.shape[:-1] + (n,), dtype=np.uint8)
+    k = np.arange(n)
+    for j in range(6):
+        bit = 6 * k + j  # stream bit j of every code k
+        v = (rows[..., bit // 8] >> (bit % 8).astype(np.uint8)) & 1
+        out |= (v << j).astype(np.uint8)
+    return out

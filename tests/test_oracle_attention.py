@@ -1,0 +1,185 @@
+"""Pins of the attention oracle: dense reduction against torch's
+scaled_dot_product_attention in fp64, physical-page permutation invariance,
+split-count invariance of the LSE merge, softmax row sums, closed-form special
+cases, the fp6 scale folding identity and HND/NHD equivalence."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as A
+from oracle.formats import e4m3_decode, e2m3_decode, unpack_6bit
+
+
+def _ref_sdpa(qrows, K, V, allowed, scale):
+    """Library route: torch SDPA in fp64 on the CPU with an explicit boolean mask."""
+    q = torch.from_numpy(qrows)[None, None]
+    k = torch.from_numpy(K)[None, None]
+    v = torch.from_numpy(V)[None, None]
+    m = torch.from_numpy(allowed)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)[0, 0].numpy()
+
+
+def _small(key, **kw):
+    wl = synth.build(synth.spec_for(key, small=True, **kw))
+    return wl, wl.host()
+
+
+def _args(wl):
+    s = wl.spec
+    return dict(q_len=s.q_len, h_q=s.h_q, h_k=s.h_k, d=s.d, page_size=s.page_size, kv_format=s.kv_format)
+
+
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5"])
+def test_matches_sdpa_per_head(key):
+    wl, h = _small(key)
+    s = wl.spec
+    from oracle.qquant import quantize_q
+    codes, qd = quantize_q(h["q"], s.b, s.q_len, s.h_k, h["q_mul"])
+    O, LSE = A.decode_step(h, causal=s.causal, **_args(wl))
+    for i in range(s.b):
+        for g in range(s.h_k):
+            qrows, K, V = A.head_inputs(h, i, g, q_codes=codes, q_descale=qd, **_args(wl))
+            allowed = A.visible(K.shape[0], s.q_len, s.h_r, s.causal)
+            ref = _ref_sdpa(qrows, K, V, allowed, h["softmax_scale"]).reshape(s.q_len, s.h_r, s.d)
+            if h["o_mul"] is not None:
+                ref = ref * h["o_mul"][g * s.h_r:(g + 1) * s.h_r][None]
+            got = O[i * s.q_len:(i + 1) * s.q_len, g * s.h_r:(g + 1) * s.h_r]
+            assert np.max(np.abs(got - ref)) < 1e-12
+            # LSE against a direct logsumexp of the visible logits
+            sc = h["softmax_scale"] * qrows @ K.T
+            lse = np.array([np.log(np.sum(np.exp(sc[r][allowed[r]] - sc[r][allowed[r]].max())))
+                            + sc[r][allowed[r]].max() for r in range(sc.shape[0])])
+            assert np.max(np.abs(LSE[i * s.q_len:(i + 1) * s.q_len, g * s.h_r:(g + 1) * s.h_r].reshape(-1)
+                                 - lse)) < 1e-12
+
+
+def test_gather_identity_table_is_dense_slice():
+    # one page holding the whole sequence, identity block table: the gather is a plain slice
+    rng = np.random.default_rng(0)
+    L, h_k, row = 48, 3, 128
+    pool = rng.integers(0, 256, size=(2, h_k, L, row), dtype=np.uint8)  # HND, page size L
+    flat = pool.reshape(-1)
+    st = (pool.strides[0], pool.strides[2], pool.strides[1])
+    for g in range(h_k):
+        got = A.gather_codes(flat, st, L, np.array([1]), L, g, row)
+        assert np.array_equal(got, pool[1, g])
+
+
+def test_physical_page_permutation_is_exactly_invariant():
+    wl, h = _small("cfg2")
+    s = wl.spec
+    O1, L1 = A.decode_step(h, causal=True, **_args(wl))
+    # move every page to a new physical slot and rewrite the block table to match
+    kp = h["k_pool"].reshape(-1, h["k_strides"][0])
+    vp = h["v_pool"].reshape(-1, h["v_strides"][0])
+    perm = np.random.default_rng(1).permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    h2 = dict(h, k_pool=kp[perm].reshape(-1), v_pool=vp[perm].reshape(-1), block_table=inv[h["block_table"]])
+    O2, L2 = A.decode_step(h2, causal=True, **_args(wl))
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c"])
+def test_split_merge_invariance(key):
+    wl, h = _small(key)
+    s = wl.spec
+    rng = np.random.default_rng(2)
+    from oracle.qquant import quantize_q
+    codes, qd = quantize_q(h["q"], s.b, s.q_len, s.h_k)
+    for i in range(s.b):
+        qrows, K, V = A.head_inputs(h, i, 1, q_codes=codes, q_descale=qd, **_args(wl))
+        allowed = A.visible(K.shape[0], s.q_len, s.h_r, s.causal)
+        O, lse, P = A.attend(qrows, K, V, allowed, h["softmax_scale"])
+        assert np.max(np.abs(P.sum(axis=1) - 1.0)) < 1e-12  # softmax rows sum to 1
+        for nsplit in (1, 2, 3, 7, 16):
+            cuts = np.sort(rng.choice(np.arange(1, K.shape[0]), size=nsplit - 1, replace=False)) if nsplit > 1 else []
+            bounds = [0, *cuts.tolist(), K.shape[0]] if nsplit > 1 else [0, K.shape[0]]
+            parts = [A.partial(qrows, K, V, allowed, h["softmax_scale"], a, b) for a, b in zip(bounds, bounds[1:])]
+            Om, lm = A.merge(parts)
+            assert np.max(np.abs(Om - O)) < 1e-12
+            assert np.max(np.abs(lm - lse)) < 1e-12
+
+
+def test_special_cases():
+    rng = np.random.default_rng(4)
+    d, n = 128, 6
+    qrows = rng.standard_normal((n, d))
+    K = rng.standard_normal((37, d))
+    V = rng.standard_normal((37, d))
+    allowed = np.ones((n, 37), dtype=bool)
+    # constant V -> O = V
+    Vc = np.tile(rng.standard_normal(d), (37, 1))
+    O, _, _ = A.attend(qrows, K, Vc, allowed, 0.1)
+    assert np.max(np.abs(O - Vc[0])) < 1e-12
+    # L = 1 -> O = V_0, LSE = the single logit
+    O, lse, _ = A.attend(qrows, K[:1], V[:1], allowed[:, :1], 0.1)
+    assert np.max(np.abs(O - V[0])) < 1e-15
+    assert np.max(np.abs(lse - 0.1 * qrows @ K[0])) < 1e-12
+    # all-zero K -> uniform weights -> mean of V over the visible keys, LSE = ln(count)
+    vis = A.visible(37, 3, 2, True)
+    O, lse, _ = A.attend(qrows, np.zeros_like(K), V, vis, 0.1)
+    for r in range(n):
+        assert np.max(np.abs(O[r] - V[vis[r]].mean(axis=0))) < 1e-12
+        assert abs(lse[r] - math.log(vis[r].sum())) < 1e-12
+    # q_len == 1: causal and non-causal masks agree; causal last token == non-causal
+    assert np.array_equal(A.visible(50, 1, 4, True), A.visible(50, 1, 4, False))
+    c, nc = A.visible(50, 4, 2, True), A.visible(50, 4, 2, False)
+    assert np.array_equal(c[-2:], nc[-2:])
+    assert c[0].sum() == 47 and c[2].sum() == 48
+    # no visible key -> O = 0, LSE = -inf
+    O, lse, _ = A.attend(qrows, K[:0], V[:0], allowed[:, :0], 0.1)
+    assert np.all(O == 0) and np.all(np.isneginf(lse))
+
+
+def test_empty_sequence_in_a_batch():
+    wl, h = _small("cfg2", lens=(0, 300, 129, 1))
+    O, LSE = A.decode_step(h, causal=True, **_args(wl))
+    assert np.all(O[0] == 0) and np.all(np.isneginf(LSE[0]))
+    assert np.all(np.isfinite(O[1:]))
+
+
+def test_fp6_folding_identity():
+    """Channel scales folded into Q and O equal attention on explicitly
+    dequantized K/V (the identities in mjolnir/backend.py, _install_fp6_scales)."""
+    wl, h = _small("cfg5")
+    s = wl.spec
+    O, _ = A.decode_step(h, causal=True, quantize=False, **_args(wl))
+    ks = wl.k_channel_scale.numpy().astype(np.float64)
+    vs = wl.v_channel_scale.numpy().astype(np.float64)
+    for i in range(s.b):
+        for g in (0, s.h_k - 1):
+            L = int(h["seq_lens"][i])
+            kc = A.gather_codes(h["k_pool"], h["k_strides"], s.page_size, h["block_table"][i], L, g, 96)
+            vc = A.gather_codes(h["v_pool"], h["v_strides"], s.page_size, h["block_table"][i], L, g, 96)
+            K = e2m3_decode(unpack_6bit(kc, 128)) * ks[g]
+            V = e2m3_decode(unpack_6bit(vc, 128)) * vs[g]
+            q = h["q"][i, g * s.h_r:(g + 1) * s.h_r].astype(np.float64)
+            ref = _ref_sdpa(q, K, V, np.ones((s.h_r, L), bool), h["softmax_scale"])
+            assert np.max(np.abs(O[i, g * s.h_r:(g + 1) * s.h_r] - ref)) < 1e-12
+
+
+def test_hnd_and_nhd_layouts_agree():
+    wl, h = _small("cfg2")
+    s = wl.spec
+    # rebuild the same logical cache in the token-major layout
+    kp = wl.k_pool.permute(0, 2, 1, 3).contiguous()
+    vp = wl.v_pool.permute(0, 2, 1, 3).contiguous()
+    h2 = dict(h, k_pool=kp.numpy().reshape(-1), v_pool=vp.numpy().reshape(-1),
+              k_strides=(kp.stride(0), kp.stride(1), kp.stride(2)),
+              v_strides=(vp.stride(0), vp.stride(1), vp.stride(2)))
+    O1, L1 = A.decode_step(h, causal=True, **_args(wl))
+    O2, L2 = A.decode_step(h2, causal=True, **_args(wl))
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_descale_kinds_scale_linearly():
+    wl, h = _small("cfg4c")
+    s = wl.spec
+    O, _ = A.decode_step(h, causal=True, **_args(wl))
+    h2 = dict(h, v_descale=h["v_descale"] * 2.0)
+    O2, _ = A.decode_step(h2, causal=True, **_args(wl))
+    assert np.max(np.abs(O2 - 2.0 * O)) < 1e-12
