@@ -1,0 +1,255 @@
+/*
+ * mj.h -- paged decode attention over a quantized (e4m3 / packed e2m3) KV
+ * cache on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * One decode step is four calls on one HIP stream:
+ *
+ *   mj_plan_split_kv   host: the split-KV plan, copied (async) into a
+ *                      fixed-address device buffer          (outside capture)
+ *   mj_quantize_q      device: dynamic e4m3 Q per (sequence, KV head)
+ *   mj_paged_decode    device: paged online-softmax attention
+ *   mj_merge_lse       device: log-sum-exp merge of the split partials
+ *                      (call it iff the plan says with_reduction)
+ *
+ * The method is the one the mjolnir-kernel 0.1.0 pages describe (PyPI project
+ * page and sdist README, section "What it does", steps 1-4; wheel listing
+ * mjolnir/runner.py, T5DecodeRunner.plan / .run / ._launch).  Their Thor
+ * (sm_110) kernel design is prior art only; nothing here follows it.
+ *
+ * Conventions for every call:
+ *  - Ownership: the caller allocates and owns every buffer (device memory,
+ *    pinned host staging).  The library never allocates, frees or
+ *    synchronizes; device calls only enqueue work on `stream` and borrow the
+ *    pointers until that work has run.
+ *  - Errors: every call returns an mj_status; invalid arguments are rejected
+ *    on the host before anything is enqueued (no partial launches).  Nothing
+ *    aborts or throws across the ABI.
+ *  - Graph capture: mj_quantize_q, mj_paged_decode and mj_merge_lse are
+ *    capture-safe (their grids depend only on the config, q_len and
+ *    num_seqs; every per-step value is read from device memory).
+ *    mj_plan_split_kv must run outside capture; a captured graph replays any
+ *    later plan written to the same plan buffer.
+ *  - Shapes: head_dim is 128; page sizes 16, 32, 64, 128 (README
+ *    "Requirements"); h_q % h_k == 0.
+ */
+#ifndef MJ_H
+#define MJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MJ_ABI_VERSION 1
+
+typedef enum mj_status {
+  MJ_OK = 0,
+  MJ_EINVAL = -1,        /* null pointer, bad value, plan/launch mismatch        */
+  MJ_EUNSUPPORTED = -2,  /* head_dim != 128, page size, h_q % h_k, kv format      */
+  MJ_EALIGN = -3,        /* a base pointer or stride is not 16-byte aligned       */
+  MJ_ECAPACITY = -4,     /* num_seqs / q_len / block table / buffer too small     */
+  MJ_EHIP = -5           /* a HIP runtime call or kernel launch failed            */
+} mj_status;
+
+typedef enum mj_kv_format {
+  MJ_KV_E4M3 = 0,  /* one OCP e4m3 (float8_e4m3fn) byte per value, 128-byte rows  */
+  MJ_KV_E2M3 = 1   /* OCP MX e2m3 6-bit codes, 4 per 3 bytes, 96-byte rows:
+                      code k of a row is stream bits [6k, 6k+6), stream bit 8B+j
+                      being bit j of byte B (runner.py, comment above
+                      RUNNER_KV_FORMATS: "little-endian bitstream")             */
+} mj_kv_format;
+
+/* Shape of a K or V descale tensor (runner.py, T5DecodeRunner.run: k_scale /
+ * v_scale are fp32 with 1 element, (h_k,) or (b, h_k)). */
+typedef enum mj_scale_kind {
+  MJ_SCALE_TENSOR = 0,   /* descale[0]                       */
+  MJ_SCALE_HEAD = 1,     /* descale[g], g = KV head          */
+  MJ_SCALE_SEQ_HEAD = 2  /* descale[i * h_k + g]             */
+} mj_scale_kind;
+
+/* Static configuration of one decode site (one KV-cache group).  Every size a
+ * captured graph depends on (grid sizes, plan and workspace layout) is a
+ * function of this struct and q_len only. */
+typedef struct mj_config {
+  int32_t h_q;             /* query heads                                      */
+  int32_t h_k;             /* KV heads, h_q % h_k == 0                          */
+  int32_t head_dim;        /* must be 128                                       */
+  int32_t page_size;       /* tokens per page: 16, 32, 64 or 128                */
+  int32_t max_num_seqs;    /* largest batch any plan or launch uses             */
+  int32_t max_q_len;       /* largest q_len (1 + speculative tokens), >= 1      */
+  int32_t max_splits;      /* most KV chunks per sequence; 1 = never split      */
+  int32_t num_cus;         /* compute units to plan for; 0 = ask the device     */
+  int32_t wgs_per_cu;      /* decode workgroups per CU in one wave; 0 = 2       */
+  int32_t kv_tile_tokens;  /* plan granularity in tokens (multiple of 16); 0=128*/
+  int32_t slots_override;  /* work items per wave; 0 = num_cus*wgs_per_cu/h_k   */
+  int32_t kv_format;       /* mj_kv_format                                      */
+} mj_config;
+
+/* What a plan decided (runner.py, StepPlan). */
+typedef struct mj_plan_info {
+  int32_t num_work;        /* grid size of mj_paged_decode = capacity for q_len */
+  int32_t slots;           /* work items that fill one wave (S)                  */
+  int32_t chunk_tiles;     /* chunk length in kv tiles                          */
+  int32_t num_chunks;      /* items with a non-empty KV range                   */
+  int32_t with_reduction;  /* 1: some sequence is split; call mj_merge_lse      */
+  int32_t num_seqs;
+  int32_t q_len;
+  int32_t kv_tile_tokens;
+} mj_plan_info;
+
+/* Arguments of mj_paged_decode.  All strides are in BYTES for the KV cache and
+ * in ELEMENTS (bf16) for the output. */
+typedef struct mj_decode_args {
+  /* Q from mj_quantize_q */
+  const uint8_t* q8;          /* (num_seqs, h_k, q_len*h_r, 128) e4m3, contiguous */
+  const float* q_descale;     /* (num_seqs, h_k)                                  */
+  int32_t num_seqs;
+  int32_t q_len;              /* 1 .. max_q_len                                   */
+  int32_t causal;             /* q_len > 1: 1 = causal block, 0 = every query
+                                 token sees every key (parallel drafter)          */
+  /* KV cache: token j of sequence i, KV head g, starts at byte
+     page*page_stride + (j % page_size)*slot_stride + g*head_stride of the
+     pool, page = block_table[i*bt_row_stride + j/page_size].  HND and NHD
+     (and K|V-interleaved pools) differ only in these strides.               */
+  const void* k_cache;
+  int64_t k_page_stride, k_slot_stride, k_head_stride;
+  const void* v_cache;
+  int64_t v_page_stride, v_slot_stride, v_head_stride;
+  int64_t num_pages;          /* pages in each pool; a block-table entry outside
+                                 [0, num_pages) masks its tokens (never read)      */
+  const float* k_descale;     /* fp32 per mj_scale_kind                           */
+  int32_t k_descale_kind;
+  const float* v_descale;
+  int32_t v_descale_kind;
+  /* paging */
+  const int32_t* block_table; /* int32, row i at block_table + i*bt_row_stride    */
+  int64_t bt_row_stride;      /* elements                                          */
+  int32_t max_blocks_per_seq; /* valid columns per row; tokens beyond
+                                 max_blocks_per_seq*page_size are never read       */
+  const int32_t* seq_lens;    /* device (num_seqs,), tokens incl. the q_len new   */
+  /* plan (device buffer written by mj_plan_split_kv) */
+  const int32_t* plan;
+  int32_t num_work;           /* mj_plan_info.num_work                            */
+  int32_t with_reduction;     /* mj_plan_info.with_reduction                      */
+  void* workspace;            /* split partials; >= mj_workspace_bytes(cfg)       */
+  size_t workspace_bytes;
+  /* math */
+  float softmax_scale;        /* natural-log scale of Q.K (1/sqrt(128) usually)   */
+  const float* o_mul;         /* nullable (h_q, 128) fp32: O *= o_mul (fp6 V
+                                 channel scales folded into the output)           */
+  /* outputs */
+  void* out;                  /* bf16 (num_seqs*q_len, h_q, 128) through strides  */
+  int64_t out_tok_stride, out_head_stride;
+  float* lse;                 /* nullable (num_seqs*q_len, h_q) fp32, natural log */
+} mj_decode_args;
+
+typedef struct mj_merge_args {
+  const int32_t* plan;
+  int32_t num_seqs;
+  int32_t q_len;
+  const void* workspace;
+  size_t workspace_bytes;
+  void* out;                  /* same output as mj_paged_decode                   */
+  int64_t out_tok_stride, out_head_stride;
+  float* lse;                 /* nullable                                          */
+} mj_merge_args;
+
+/* ------------------------------------------------------------------------ */
+const char* mj_status_string(mj_status s);
+int32_t mj_abi_version(void);
+
+/* Validate a config (shapes, formats, limits).  Host only. */
+mj_status mj_config_check(const mj_config* cfg);
+
+/* Byte sizes of the caller-allocated buffers; 0 for an invalid config.
+ * Plan buffer: int32 [work: cap_max x 4][n_splits: max_num_seqs]
+ * [split_begin: max_num_seqs], cap_max = the largest capacity over q_len.
+ * Workspace: fp32 split partials sized by the largest slot count, not by the
+ * batch (the plan splits only batches smaller than one wave). */
+size_t mj_plan_buffer_bytes(const mj_config* cfg);
+size_t mj_workspace_bytes(const mj_config* cfg);
+
+/* Capacity (= decode grid size) for q_len; -1 on error.  Host only (queries
+ * the current device when cfg->num_cus == 0). */
+int32_t mj_plan_capacity(const mj_config* cfg, int32_t q_len);
+
+/* The split-KV plan (README "What it does", step 1; runner.py
+ * T5DecodeRunner.plan and __init__ "Capacity per q_len"):
+ *   slots S = max(1, num_cus*wgs_per_cu / (h_k*ceil(q_len*h_r/64))), or the
+ *   override; capacity = max(S, max_num_seqs); tiles_i =
+ *   ceil((seq_lens_host[i] + margin) / kv_tile_tokens).  A batch smaller
+ *   than S (and max_splits > 1) is split with the smallest chunk c >=
+ *   ceil(max tiles / max_splits) whose item count sum_i max(1,ceil(tiles_i/c))
+ *   fits S; otherwise one item per sequence.  Items (seq, tile_begin,
+ *   tile_end, split) are sequence-major and padded with (-1,0,0,0).
+ * mj_plan_compute writes the whole plan image into plan_host
+ * (mj_plan_buffer_bytes bytes) without touching the device.
+ * mj_plan_split_kv does the same into `host_staging` (pinned, caller-owned;
+ * must not be rewritten until the copy has run on `stream`) and enqueues one
+ * hipMemcpyAsync of it into `plan_dev`.
+ * Errors: EINVAL (null, num_seqs < 1, q_len out of 1..max_q_len, negative
+ * length or margin), ECAPACITY (num_seqs > max_num_seqs, a sequence needs
+ * more than max_blocks_per_seq pages), EHIP. */
+mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, int32_t num_seqs, int32_t q_len,
+                          int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_host, mj_plan_info* info);
+mj_status mj_plan_split_kv(const mj_config* cfg, const int32_t* seq_lens_host, int32_t num_seqs, int32_t q_len,
+                           int32_t margin, int32_t max_blocks_per_seq, int32_t* host_staging, int32_t* plan_dev,
+                           mj_plan_info* info, hipStream_t stream);
+
+/* Dynamic e4m3 quantization of Q per (sequence, KV head) (README "What it
+ * does", step 2; runner.py T5DecodeRunner.run, fp8-Q branch): over the q_len
+ * tokens and h_r heads of KV head g, x = fp32(q) [* q_mul], amax =
+ * max(max|x|, 1e-6f), s = amax / 448 (IEEE fp32 division), code =
+ * RNE_e4m3(x / s) (IEEE division), q_descale[i*h_k+g] = s.  Rows are packed
+ * t*h_r + r for token t, query head g*h_r + r.
+ *   q: bf16, element (token, head, c) at q[token*q_tok_stride +
+ *      head*q_head_stride + c], token = i*q_len + t (a strided view of a
+ *      fused QKV buffer works); 16-byte aligned, strides multiples of 8.
+ *   q_mul: nullable (h_q, 128) fp32 (fp6 K channel scales folded into Q).
+ *   q8: (num_seqs, h_k, q_len*h_r, 128) bytes; q_descale: (num_seqs, h_k).
+ * Errors: EINVAL, EALIGN, ECAPACITY, EHIP. */
+mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                        const float* q_mul, int32_t num_seqs, int32_t q_len, uint8_t* q8, float* q_descale,
+                        hipStream_t stream);
+
+/* Paged decode attention (README "What it does", step 3): for every plan item
+ * (sequence i, token range) and KV head g, logit = softmax_scale *
+ * q_descale[i,g] * k_descale * sum_c dec(q8)*dec(k) over the keys the row may
+ * see (causal token t of a q_len block sees keys 0 .. L-q_len+t; q_len == 1
+ * or non-causal: 0 .. L-1), online softmax, O = v_descale * sum_j p_j dec(v_j)
+ * [* o_mul].  A sequence with one item writes bf16 O and LSE directly; a
+ * split sequence writes fp32 partials (unnormalized O, running max, sum) to
+ * the workspace for mj_merge_lse.  A row that sees no key writes O = 0,
+ * LSE = -inf.
+ * Errors: EINVAL (nulls, num_work/with_reduction not those of a plan for
+ * this config and q_len, causal q_len>1 with ... see docs), EALIGN
+ * (k/v/q8/out bases or strides not 16-byte / 8-element aligned),
+ * ECAPACITY (num_seqs, q_len, workspace), EUNSUPPORTED, EHIP. */
+mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* args, hipStream_t stream);
+
+/* Log-sum-exp merge of the split partials (README "What it does", step 4):
+ * for each split sequence, M = max_s m_s, O = sum_s e^{m_s-M} O_s /
+ * sum_s e^{m_s-M} l_s, LSE = M + ln sum_s e^{m_s-M} l_s; writes bf16 O and
+ * LSE.  Sequences with a single item are left untouched (mj_paged_decode
+ * already wrote them).  Errors: EINVAL, ECAPACITY, EALIGN, EHIP. */
+mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* args, hipStream_t stream);
+
+/* Test probes (not part of a decode step).
+ * mj_debug_gather_kv copies the codes of tokens 0..seq_len-1 of one
+ * (sequence, KV head) from the K (which = 0) or V (which = 1) pool into
+ * dense_out (seq_len x row bytes), using the decode kernel's own address
+ * computation.  mj_debug_decode_codes decodes n codes (one per byte; e2m3
+ * codes in the low 6 bits) with the kernel's own decoder into fp32. */
+mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, int32_t seq, int32_t head,
+                             int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream);
+mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MJ_H */

@@ -1,0 +1,119 @@
+"""Python binding of the mj C ABI (paged decode attention over an e4m3 /
+packed-e2m3 KV cache on MI355X).
+
+The functions below carry the C names and only marshal arguments: every step
+of the decode path runs in the HIP kernels of ``libmj.so``.  PyTorch supplies
+device memory and the current HIP stream.  Importing works without a GPU
+(host-only entry points such as ``mj_plan_compute`` run on the CPU); a missing
+library raises ImportError -- there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._abi import (  # noqa: F401
+    Config, PlanInfo, DecodeArgs, MergeArgs, MjError, KV_FORMATS, SCALE_KINDS,
+    MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
+)
+
+lib()  # fail loudly at import if the library is missing
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def mj_config(*, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, num_cus=0, wgs_per_cu=0,
+              kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128) -> Config:
+    c = Config(h_q=h_q, h_k=h_k, head_dim=head_dim, page_size=page_size, max_num_seqs=max_num_seqs,
+               max_q_len=max_q_len, max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
+               kv_tile_tokens=kv_tile_tokens, slots_override=slots_override,
+               kv_format=KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format)
+    return c
+
+
+def mj_config_check(cfg: Config) -> int:
+    return lib().mj_config_check(ctypes.byref(cfg))
+
+
+def mj_plan_buffer_bytes(cfg: Config) -> int:
+    return lib().mj_plan_buffer_bytes(ctypes.byref(cfg))
+
+
+def mj_workspace_bytes(cfg: Config) -> int:
+    return lib().mj_workspace_bytes(ctypes.byref(cfg))
+
+
+def mj_plan_capacity(cfg: Config, q_len: int) -> int:
+    return lib().mj_plan_capacity(ctypes.byref(cfg), q_len)
+
+
+def mj_plan_compute(cfg: Config, seq_lens, q_len: int, margin: int = 0, max_blocks_per_seq: int = 1 << 30):
+    """Host-only plan: returns (plan image as int32 array, PlanInfo)."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    n = mj_plan_buffer_bytes(cfg) // 4
+    if n == 0:
+        check(mj_config_check(cfg) or MJ_EINVAL, "mj_plan_buffer_bytes")
+    out = np.zeros(n, dtype=np.int32)
+    info = PlanInfo()
+    st = lib().mj_plan_compute(ctypes.byref(cfg), lens.ctypes.data_as(ctypes.c_void_p), len(lens), q_len, margin,
+                               max_blocks_per_seq, out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(info))
+    check(st, "mj_plan_compute")
+    return out, info
+
+
+def mj_plan_split_kv(cfg: Config, seq_lens, q_len: int, margin: int, max_blocks_per_seq: int, host_staging,
+                     plan_dev, stream=None) -> PlanInfo:
+    """Plan into pinned ``host_staging`` (torch int32, pinned) and enqueue its
+    copy into ``plan_dev`` (torch int32 on the GPU) on ``stream``."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    info = PlanInfo()
+    st = lib().mj_plan_split_kv(ctypes.byref(cfg), lens.ctypes.data_as(ctypes.c_void_p), len(lens), q_len, margin,
+                                max_blocks_per_seq, _ptr(host_staging), _ptr(plan_dev), ctypes.byref(info),
+                                _stream(stream))
+    check(st, "mj_plan_split_kv")
+    return info
+
+
+def mj_quantize_q(cfg: Config, q, q_mul, num_seqs: int, q_len: int, q8, q_descale, stream=None):
+    """q: bf16 torch view (tokens, h_q, 128) with unit channel stride."""
+    assert q.stride(2) == 1
+    st = lib().mj_quantize_q(ctypes.byref(cfg), _ptr(q), q.stride(0), q.stride(1), _ptr(q_mul), num_seqs, q_len,
+                             _ptr(q8), _ptr(q_descale), _stream(stream))
+    check(st, "mj_quantize_q")
+
+
+def mj_paged_decode(cfg: Config, args: DecodeArgs, stream=None):
+    check(lib().mj_paged_decode(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_paged_decode")
+
+
+def mj_merge_lse(cfg: Config, args: MergeArgs, stream=None):
+    check(lib().mj_merge_lse(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_merge_lse")
+
+
+def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_len: int, which: int, dense_out,
+                       stream=None):
+    st = lib().mj_debug_gather_kv(ctypes.byref(cfg), ctypes.byref(args), seq, head, seq_len, which, _ptr(dense_out),
+                                  _stream(stream))
+    check(st, "mj_debug_gather_kv")
+
+
+def mj_debug_decode_codes(kv_format, codes, out, stream=None):
+    fmt = KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format
+    check(lib().mj_debug_decode_codes(fmt, _ptr(codes), codes.numel(), _ptr(out), _stream(stream)),
+          "mj_debug_decode_codes")
+
+
+from .runner import DecodeStep  # noqa: E402,F401

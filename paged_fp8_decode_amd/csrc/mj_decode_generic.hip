@@ -1,0 +1,262 @@
+// Generic paged decode kernel: any n_q (row tiles of up to 64 query rows),
+// both KV formats, causal or not.  One workgroup of 256 threads per (plan
+// item, KV head, row tile).  It stages 32-token K/V tiles through LDS as fp32
+// and runs a textbook online softmax; it is the simple, always-correct path
+// the specialised streaming kernels are checked against and fall back to.
+//
+// Method (mjolnir-kernel README "What it does", steps 3-4; wheel page
+// mjolnir/runner.py, T5DecodeRunner.run): keys come from pages through the
+// block table and the pool's byte strides; logits are
+// softmax_scale * q_descale * k_descale * sum_c dec(q)dec(k), kept in log2
+// units (exp2) internally; a sequence with one plan item writes bf16 O and
+// the natural-log LSE, a split sequence writes fp32 partials (O unnormalised,
+// running max in log2 units, running sum) for the merge.
+#include "mj_device.h"
+#include "mj_internal.h"
+
+namespace mj {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKT = 32;  // tokens per LDS tile
+constexpr int kRT = 64;  // query rows per workgroup
+
+template <int FMT>
+__device__ __forceinline__ void load_row16(const uint8_t* row, int chunk, float out[16]) {
+  if constexpr (FMT == 0) {  // e4m3: 16 bytes at chunk*16
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + chunk * 16);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[e] = e4m3_raw((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+  } else {  // e2m3: 12 bytes at chunk*12 hold codes 16*chunk .. 16*chunk+15
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(row + chunk * 12);
+    uint32_t c[16];
+    unpack16_e2m3(src[0], src[1], src[2], c);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[e] = e2m3_raw(c[e]);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p) {
+  __shared__ float q_s[kRT][kHeadDim];
+  __shared__ float k_s[kKT][kHeadDim + 1];
+  __shared__ float v_s[kKT][kHeadDim];
+  __shared__ float s_s[kRT][kKT + 1];
+  __shared__ float m_s[kRT], l_s[kRT], a_s[kRT];
+  __shared__ int ok_s[kKT];
+
+  const int w = blockIdx.x;
+  const int g = blockIdx.y % p.h_k;
+  const int rt = blockIdx.y / p.h_k;
+  const int tid = threadIdx.x;
+  const int seq = p.work[4 * w];
+  if (seq < 0 || seq >= p.num_seqs) return;
+  const int row0 = rt * kRT;
+  const int nr = min(kRT, p.n_q - row0);
+  if (nr <= 0) return;
+
+  int L = p.seq_lens[seq];
+  L = max(0, min(L, p.max_blocks * p.page_size));
+  const int j0 = p.work[4 * w + 1] * p.kv_tile;
+  const int j1 = min(p.work[4 * w + 2] * p.kv_tile, L);
+  const bool single = p.n_splits[seq] <= 1;
+  const bool causal = p.causal && p.q_len > 1;
+  const int lim0 = L - p.q_len;  // causal: token t sees keys j <= lim0 + t
+
+  const float rescale = FMT == 0 ? kE4m3Rescale : kE2m3Rescale;
+  const float qs = p.q_descale[(int64_t)seq * p.h_k + g] * p.scale_log2;
+  const float kd = load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * rescale;
+  const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k) * rescale;
+  const uint8_t* qsrc = p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + row0) * kHeadDim;
+  for (int e = tid; e < nr * kHeadDim; e += kThreads) q_s[e >> 7][e & 127] = e4m3_value(qsrc[e]) * qs;
+  if (tid < kRT) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.0f;
+  }
+  const int32_t* bt_row = p.bt + (int64_t)seq * p.bt_stride;
+  const int c = tid & 127;
+  const int rb = tid >> 7;
+  float acc[kRT / 2];
+#pragma unroll
+  for (int k = 0; k < kRT / 2; ++k) acc[k] = 0.0f;
+  __syncthreads();
+
+  for (int t0 = j0; t0 < j1; t0 += kKT) {
+    {  // K and V tile: thread -> (token, 16-value chunk)
+      const int tok = tid >> 3, ch = tid & 7;
+      const int j = t0 + tok;
+      float kv[16], vv[16];
+      bool ok = j < j1;
+      int64_t pg = -1;
+      if (ok) {
+        pg = page_of(bt_row, j, p.page_shift, p.num_pages);
+        ok = pg >= 0;
+      }
+      if (ok) {
+        const int slot = j & (p.page_size - 1);
+        load_row16<FMT>(p.k + kv_offset(pg, slot, g, p.k_sp, p.k_ss, p.k_sh), ch, kv);
+        load_row16<FMT>(p.v + kv_offset(pg, slot, g, p.v_sp, p.v_ss, p.v_sh), ch, vv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) kv[e] = vv[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        k_s[tok][ch * 16 + e] = kv[e] * kd;
+        v_s[tok][ch * 16 + e] = vv[e] * vd;
+      }
+      if (ch == 0) ok_s[tok] = ok;
+    }
+    __syncthreads();
+    {  // logits (log2 units), masked
+      const int tok = tid & 31, rg = tid >> 5;
+      const int j = t0 + tok;
+      for (int r = rg; r < nr; r += 8) {
+        float s = 0.0f;
+#pragma unroll 16
+        for (int cc = 0; cc < kHeadDim; ++cc) s += q_s[r][cc] * k_s[tok][cc];
+        const int t = (row0 + r) / p.h_r;
+        const bool vis = ok_s[tok] && (!causal || j <= lim0 + t);
+        s_s[r][tok] = vis ? s : -INFINITY;
+      }
+    }
+    __syncthreads();
+    if (tid < nr) {  // online softmax row update
+      const float m_old = m_s[tid];
+      float mx = m_old;
+      for (int j = 0; j < kKT; ++j) mx = fmaxf(mx, s_s[tid][j]);
+      float alpha = 1.0f, sum = 0.0f;
+      if (mx != -INFINITY) {
+        alpha = exp2f(m_old - mx);  // m_old = -inf -> 0
+        for (int j = 0; j < kKT; ++j) {
+          const float pj = exp2f(s_s[tid][j] - mx);  // -inf -> 0
+          s_s[tid][j] = pj;
+          sum += pj;
+        }
+      } else {
+        for (int j = 0; j < kKT; ++j) s_s[tid][j] = 0.0f;
+      }
+      l_s[tid] = l_s[tid] * alpha + sum;
+      m_s[tid] = mx;
+      a_s[tid] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRT / 2; ++k) {
+      const int r = rb + 2 * k;
+      if (r < nr) {
+        float o = acc[k] * a_s[r];
+#pragma unroll 8
+        for (int j = 0; j < kKT; ++j) o += s_s[r][j] * v_s[j][c];
+        acc[k] = o;
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int k = 0; k < kRT / 2; ++k) {
+    const int r = rb + 2 * k;
+    if (r >= nr) continue;
+    const int row = row0 + r;
+    const int t = row / p.h_r;
+    const int h = g * p.h_r + (row - t * p.h_r);
+    const float om = p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + c] : 1.0f;
+    const float l = l_s[r];
+    if (single) {
+      const float o = l > 0.0f ? acc[k] / l * om : 0.0f;
+      p.out[((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c] = f32_to_bf16(o);
+      if (c == 0 && p.lse) p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = l > 0.0f ? (m_s[r] + log2f(l)) * kLn2 : -INFINITY;
+    } else if (w < p.part_items) {
+      const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + row;
+      p.o_part[idx * kHeadDim + c] = acc[k] * om;
+      if (c == 0) {
+        p.m_part[idx] = m_s[r];
+        p.l_part[idx] = l;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of split partials: one workgroup per (sequence, KV head).
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
+  const int seq = blockIdx.x;
+  const int g = blockIdx.y;
+  const int n = p.n_splits[seq];
+  if (n <= 1) return;
+  const int w0 = p.split_begin[seq];
+  if (w0 < 0 || w0 + n > p.part_items) return;
+  const int c = threadIdx.x & 127;
+  for (int r = threadIdx.x >> 7; r < p.n_q; r += 2) {
+    float M = -INFINITY;
+    for (int s = 0; s < n; ++s) M = fmaxf(M, p.m_part[((int64_t)(w0 + s) * p.h_k + g) * p.nqp + r]);
+    float o = 0.0f, lse = -INFINITY;
+    if (M != -INFINITY) {
+      float num = 0.0f, den = 0.0f;
+      for (int s = 0; s < n; ++s) {
+        const int64_t idx = ((int64_t)(w0 + s) * p.h_k + g) * p.nqp + r;
+        const float wt = exp2f(p.m_part[idx] - M);
+        den += wt * p.l_part[idx];
+        num += wt * p.o_part[idx * kHeadDim + c];
+      }
+      o = num / den;
+      lse = (M + log2f(den)) * kLn2;
+    }
+    const int t = r / p.h_r;
+    const int h = g * p.h_r + (r - t * p.h_r);
+    p.out[((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c] = f32_to_bf16(o);
+    if (c == 0 && p.lse) p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = lse;
+  }
+}
+
+// Probe: dense copy of one (sequence, head)'s codes through the same
+// page / slot / stride arithmetic the decode kernels use.
+__global__ void gather_kernel(GatherParams p) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)p.seq_len * p.row_bytes) return;
+  const int j = (int)(e / p.row_bytes);
+  const int b = (int)(e - (int64_t)j * p.row_bytes);
+  const int64_t pg = page_of(p.bt + (int64_t)p.seq * p.bt_stride, j, p.page_shift, p.num_pages);
+  const int page_size = 1 << p.page_shift;
+  p.out[e] = pg < 0 ? 0 : p.pool[kv_offset(pg, j & (page_size - 1), p.head, p.sp, p.ss, p.sh) + b];
+}
+
+// Probe: the kernels' code decoders on raw codes.
+__global__ void decode_codes_kernel(int fmt, const uint8_t* codes, int n, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = fmt == 0 ? e4m3_value(codes[i]) : e2m3_value(codes[i] & 63u);
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s) {
+  const dim3 grid(p.num_work, p.h_k * row_tiles);
+  if (kv_format == 0)
+    hipLaunchKernelGGL(decode_generic_kernel<0>, grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(p.num_seqs, p.h_k), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.seq_len * p.row_bytes;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_codes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, kv_format, codes, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace mj

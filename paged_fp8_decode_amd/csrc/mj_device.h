@@ -1,0 +1,94 @@
+// Device-side helpers shared by the mj kernels (gfx950, wave64).
+//
+// Formats (the e4m3 / e2m3 codes the mjolnir-kernel pages name; bit layouts
+// from the OCP OFP8 and OCP MX specifications):
+//   e4m3: s.eeee.mmm, bias 7, subnormal at e == 0, max 448.
+//   e2m3: s.ee.mmm (6 bits), bias 1, subnormal at e == 0, max 7.5.
+// Both decode by moving the exponent/mantissa bits into an fp32 bit pattern
+// with the same mantissa alignment and rescaling by a power of two: an fp32
+// with exponent field e and mantissa m/8 is 2^(e-127)(1+m/8), and its
+// subnormals (e == 0) are 2^-126 (m/8), so one multiply by 2^120 (e4m3) or
+// 2^126 (e2m3) maps both normal and subnormal codes exactly.  Callers fold
+// that power of two into the descale they multiply by anyway.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mj {
+
+constexpr int kHeadDim = 128;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kE4m3Rescale = 1.329227995784916e+36f;  // 2^120
+constexpr float kE2m3Rescale = 8.507059173023462e+37f;  // 2^126
+
+__device__ __forceinline__ float bits_to_float(uint32_t u) { return __uint_as_float(u); }
+
+// e4m3 code (low 8 bits) -> fp32 bit pattern whose value is 2^-120 * value.
+__device__ __forceinline__ float e4m3_raw(uint32_t c) {
+  return bits_to_float(((c & 0x80u) << 24) | ((c & 0x7Fu) << 20));
+}
+// e2m3 code (low 6 bits) -> fp32 whose value is 2^-126 * value.
+__device__ __forceinline__ float e2m3_raw(uint32_t c) {
+  return bits_to_float(((c & 0x20u) << 26) | ((c & 0x1Fu) << 20));
+}
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return e4m3_raw(c) * kE4m3Rescale; }
+__device__ __forceinline__ float e2m3_value(uint32_t c) { return e2m3_raw(c) * kE2m3Rescale; }
+
+// Round an fp32 to the nearest e4m3 code, ties to even.  Domain: finite
+// |x| <= 464 (the Q quantizer stays within 448 * (1 + 2^-23)).
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  u &= 0x7FFFFFFFu;
+  uint32_t code;
+  if (u >= 0x3C800000u) {  // >= 2^-6: normal e4m3; keep 3 of 23 mantissa bits
+    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  } else {  // subnormal range: multiples of 2^-9 (8 * 2^-9 is the min normal)
+    code = (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);
+  }
+  return sign | code;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Descale lookup for the three descale shapes (tensor, per KV head, per
+// (sequence, KV head)).
+__device__ __forceinline__ float load_descale(const float* d, int kind, int seq, int g, int h_k) {
+  return kind == 0 ? d[0] : (kind == 1 ? d[g] : d[(int64_t)seq * h_k + g]);
+}
+
+// Physical page of token j of a sequence, or -1 if the block-table entry is
+// outside [0, num_pages).
+__device__ __forceinline__ int64_t page_of(const int32_t* bt_row, int j, int page_shift, int64_t num_pages) {
+  const int64_t pg = bt_row[j >> page_shift];
+  return (pg >= 0 && pg < num_pages) ? pg : -1;
+}
+
+// Byte offset of (page, slot, head) in a pool with byte strides.
+__device__ __forceinline__ int64_t kv_offset(int64_t page, int slot, int head, int64_t sp, int64_t ss, int64_t sh) {
+  return page * sp + (int64_t)slot * ss + (int64_t)head * sh;
+}
+
+// 16 e2m3 codes from 12 packed bytes (three little-endian dwords).
+__device__ __forceinline__ void unpack16_e2m3(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t out[16]) {
+  // stream bit b of the 96-bit group is bit b%32 of word b/32
+  const uint64_t lo = (uint64_t)w0 | ((uint64_t)w1 << 32);
+  const uint64_t hi = (uint64_t)w1 | ((uint64_t)w2 << 32);  // starts at stream bit 32
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int b = 6 * k;
+    out[k] = b + 6 <= 64 ? (uint32_t)((lo >> b) & 63u) : (uint32_t)((hi >> (b - 32)) & 63u);
+  }
+}
+
+}  // namespace mj

@@ -1,0 +1,400 @@
+// Host side of the mj C ABI: configuration checks, the split-KV planner,
+// argument validation and kernel launches.  Never allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "mj.h"
+#include "mj_internal.h"
+
+namespace {
+
+constexpr int kRowTile = 64;      // query rows one decode workgroup covers
+constexpr int kDefaultWgsPerCu = 2;
+constexpr int kDefaultKvTile = 128;
+constexpr int kMaxRows = 1024;    // sanity bound on q_len * h_r
+
+struct Derived {
+  int num_cus, wgs_per_cu, kv_tile, h_r, nq_max;
+  int cap_max, slots_max;
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+mj_status check_config(const mj_config* c) {
+  if (!c) return MJ_EINVAL;
+  if (c->h_q < 1 || c->h_k < 1 || c->max_num_seqs < 1 || c->max_q_len < 1 || c->max_splits < 1) return MJ_EINVAL;
+  if (c->num_cus < 0 || c->wgs_per_cu < 0 || c->kv_tile_tokens < 0 || c->slots_override < 0) return MJ_EINVAL;
+  if (c->kv_tile_tokens % 16 != 0) return MJ_EINVAL;
+  if (c->h_q % c->h_k != 0) return MJ_EUNSUPPORTED;
+  if (c->head_dim != 128) return MJ_EUNSUPPORTED;
+  if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64 && c->page_size != 128) return MJ_EUNSUPPORTED;
+  if (c->kv_format != MJ_KV_E4M3 && c->kv_format != MJ_KV_E2M3) return MJ_EUNSUPPORTED;
+  if ((int64_t)c->max_q_len * (c->h_q / c->h_k) > kMaxRows) return MJ_ECAPACITY;
+  return MJ_OK;
+}
+
+int row_tiles(const mj_config* c, int q_len) { return (q_len * (c->h_q / c->h_k) + kRowTile - 1) / kRowTile; }
+
+int slots_for(const mj_config* c, const Derived& d, int q_len) {
+  if (c->slots_override > 0) return c->slots_override;
+  const int64_t denom = (int64_t)c->h_k * row_tiles(c, q_len);
+  return (int)std::max<int64_t>(1, ((int64_t)d.num_cus * d.wgs_per_cu) / denom);
+}
+
+int cap_for(const mj_config* c, const Derived& d, int q_len) { return std::max(slots_for(c, d, q_len), c->max_num_seqs); }
+
+mj_status derive(const mj_config* c, Derived* d) {
+  mj_status st = check_config(c);
+  if (st != MJ_OK) return st;
+  d->num_cus = c->num_cus;
+  if (d->num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MJ_EHIP;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return MJ_EHIP;
+    d->num_cus = n;
+  }
+  d->wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : kDefaultWgsPerCu;
+  d->kv_tile = c->kv_tile_tokens ? c->kv_tile_tokens : kDefaultKvTile;
+  d->h_r = c->h_q / c->h_k;
+  d->nq_max = c->max_q_len * d->h_r;
+  d->cap_max = 0;
+  d->slots_max = 0;
+  for (int ql = 1; ql <= c->max_q_len; ++ql) {
+    d->cap_max = std::max(d->cap_max, cap_for(c, *d, ql));
+    d->slots_max = std::max(d->slots_max, slots_for(c, *d, ql));
+  }
+  return MJ_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WorkspaceLayout {
+  size_t o_off, m_off, l_off, total;
+};
+
+WorkspaceLayout workspace_layout(const mj_config* c, const Derived& d) {
+  const size_t rows = (size_t)d.slots_max * c->h_k * d.nq_max;
+  WorkspaceLayout w;
+  w.o_off = 0;
+  w.m_off = round256(rows * 128 * sizeof(float));
+  w.l_off = w.m_off + round256(rows * sizeof(float));
+  w.total = w.l_off + round256(rows * sizeof(float));
+  return w;
+}
+
+size_t plan_ints(const mj_config* c, const Derived& d) { return (size_t)4 * d.cap_max + 2 * (size_t)c->max_num_seqs; }
+
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mj_status_string(mj_status s) {
+  switch (s) {
+    case MJ_OK: return "ok";
+    case MJ_EINVAL: return "invalid argument";
+    case MJ_EUNSUPPORTED: return "unsupported shape or format";
+    case MJ_EALIGN: return "misaligned pointer or stride";
+    case MJ_ECAPACITY: return "capacity exceeded";
+    case MJ_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t mj_abi_version(void) { return MJ_ABI_VERSION; }
+
+mj_status mj_config_check(const mj_config* cfg) { return check_config(cfg); }
+
+size_t mj_plan_buffer_bytes(const mj_config* cfg) {
+  Derived d;
+  if (derive(cfg, &d) != MJ_OK) return 0;
+  return plan_ints(cfg, d) * sizeof(int32_t);
+}
+
+size_t mj_workspace_bytes(const mj_config* cfg) {
+  Derived d;
+  if (derive(cfg, &d) != MJ_OK) return 0;
+  return workspace_layout(cfg, d).total;
+}
+
+int32_t mj_plan_capacity(const mj_config* cfg, int32_t q_len) {
+  Derived d;
+  if (derive(cfg, &d) != MJ_OK || q_len < 1 || q_len > cfg->max_q_len) return -1;
+  return cap_for(cfg, d, q_len);
+}
+
+mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, int32_t num_seqs, int32_t q_len,
+                          int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_host, mj_plan_info* info) {
+  Derived d;
+  mj_status st = derive(cfg, &d);
+  if (st != MJ_OK) return st;
+  if (!seq_lens_host || !plan_host || !info || num_seqs < 1 || q_len < 1 || margin < 0 || max_blocks_per_seq < 1)
+    return MJ_EINVAL;
+  if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  int64_t max_tiles = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int64_t L = seq_lens_host[i];
+    if (L < 0) return MJ_EINVAL;
+    if ((L + cfg->page_size - 1) / cfg->page_size > max_blocks_per_seq) return MJ_ECAPACITY;
+    max_tiles = std::max(max_tiles, (L + margin + d.kv_tile - 1) / d.kv_tile);
+  }
+  auto tiles = [&](int i) -> int64_t { return ((int64_t)seq_lens_host[i] + margin + d.kv_tile - 1) / d.kv_tile; };
+  auto ceil_div = [](int64_t a, int64_t b) -> int64_t { return (a + b - 1) / b; };
+
+  const int S = slots_for(cfg, d, q_len);
+  const int cap = cap_for(cfg, d, q_len);
+  const bool split = cfg->max_splits > 1 && num_seqs < S;
+  int64_t c = std::max<int64_t>(1, max_tiles);
+  if (split) {
+    // smallest chunk >= ceil(max_tiles / max_splits) whose item count fits S;
+    // the count only falls as the chunk grows, and at c = max_tiles it is
+    // num_seqs < S, so a bisection finds it.
+    int64_t lo = std::max<int64_t>(1, ceil_div(max_tiles, cfg->max_splits));
+    int64_t hi = std::max<int64_t>(lo, max_tiles);
+    auto count = [&](int64_t ch) {
+      int64_t n = 0;
+      for (int i = 0; i < num_seqs; ++i) n += std::max<int64_t>(1, ceil_div(tiles(i), ch));
+      return n;
+    };
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (count(mid) <= S) hi = mid; else lo = mid + 1;
+    }
+    c = lo;
+  }
+
+  const size_t total = plan_ints(cfg, d);
+  std::fill(plan_host, plan_host + total, 0);
+  int32_t* work = plan_host;
+  int32_t* nspl = plan_host + 4 * (size_t)d.cap_max;
+  int32_t* sbeg = nspl + cfg->max_num_seqs;
+  int w = 0, chunks = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int64_t t = tiles(i);
+    const int64_t n = split ? std::max<int64_t>(1, ceil_div(t, c)) : 1;
+    nspl[i] = (int32_t)n;
+    sbeg[i] = w;
+    for (int64_t s = 0; s < n; ++s, ++w) {
+      const int64_t b = split ? s * c : 0;
+      const int64_t e = split ? std::min((s + 1) * c, t) : t;
+      work[4 * w + 0] = i;
+      work[4 * w + 1] = (int32_t)b;
+      work[4 * w + 2] = (int32_t)e;
+      work[4 * w + 3] = (int32_t)s;
+      chunks += e > b;
+    }
+  }
+  if (w > cap) return MJ_EINVAL;  // cannot happen: split plans fit S <= cap, others use num_seqs <= cap
+  for (; w < d.cap_max; ++w) {
+    work[4 * w + 0] = -1;
+    work[4 * w + 1] = work[4 * w + 2] = work[4 * w + 3] = 0;
+  }
+  for (int i = num_seqs; i < cfg->max_num_seqs; ++i) {
+    nspl[i] = 1;
+    sbeg[i] = 0;
+  }
+  info->num_work = cap;
+  info->slots = S;
+  info->chunk_tiles = (int32_t)c;
+  info->num_chunks = chunks;
+  info->with_reduction = split ? 1 : 0;
+  info->num_seqs = num_seqs;
+  info->q_len = q_len;
+  info->kv_tile_tokens = d.kv_tile;
+  return MJ_OK;
+}
+
+mj_status mj_plan_split_kv(const mj_config* cfg, const int32_t* seq_lens_host, int32_t num_seqs, int32_t q_len,
+                           int32_t margin, int32_t max_blocks_per_seq, int32_t* host_staging, int32_t* plan_dev,
+                           mj_plan_info* info, hipStream_t stream) {
+  if (!plan_dev) return MJ_EINVAL;
+  mj_status st = mj_plan_compute(cfg, seq_lens_host, num_seqs, q_len, margin, max_blocks_per_seq, host_staging, info);
+  if (st != MJ_OK) return st;
+  const size_t bytes = mj_plan_buffer_bytes(cfg);
+  if (hipMemcpyAsync(plan_dev, host_staging, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return MJ_EHIP;
+  return MJ_OK;
+}
+
+mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+                        const float* q_mul, int32_t num_seqs, int32_t q_len, uint8_t* q8, float* q_descale,
+                        hipStream_t stream) {
+  mj_status st = check_config(cfg);
+  if (st != MJ_OK) return st;
+  if (!q || !q8 || !q_descale || num_seqs < 1 || q_len < 1 || q_tok_stride < 0 || q_head_stride < 0) return MJ_EINVAL;
+  if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  if (!aligned(q, 16) || q_tok_stride % 8 || q_head_stride % 8 || !aligned(q8, 16) || !aligned(q_descale, 4) ||
+      (q_mul && !aligned(q_mul, 16)))
+    return MJ_EALIGN;
+  mj::QQuantParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_ts = q_tok_stride;
+  p.q_hs = q_head_stride;
+  p.q_mul = q_mul;
+  p.q8 = q8;
+  p.q_descale = q_descale;
+  p.num_seqs = num_seqs;
+  p.q_len = q_len;
+  p.h_k = cfg->h_k;
+  p.h_r = cfg->h_q / cfg->h_k;
+  p.n_q = q_len * p.h_r;
+  return mj::launch_qquant(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_decode_args* a, mj::DecodeParams* p) {
+  if (!a->q8 || !a->q_descale || !a->k_cache || !a->v_cache || !a->k_descale || !a->v_descale || !a->block_table ||
+      !a->seq_lens || !a->plan || !a->out)
+    return MJ_EINVAL;
+  if (a->num_seqs < 1 || a->q_len < 1) return MJ_EINVAL;
+  if (a->num_seqs > cfg->max_num_seqs || a->q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  if (a->k_descale_kind < 0 || a->k_descale_kind > 2 || a->v_descale_kind < 0 || a->v_descale_kind > 2)
+    return MJ_EINVAL;
+  if (a->num_pages < 1 || a->max_blocks_per_seq < 1 || a->bt_row_stride < a->max_blocks_per_seq) return MJ_EINVAL;
+  if (!std::isfinite(a->softmax_scale)) return MJ_EINVAL;
+  if (a->k_page_stride < 0 || a->k_slot_stride < 0 || a->k_head_stride < 0 || a->v_page_stride < 0 ||
+      a->v_slot_stride < 0 || a->v_head_stride < 0 || a->out_tok_stride < 0 || a->out_head_stride < 0)
+    return MJ_EINVAL;
+  if (!aligned(a->q8, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16) ||
+      a->k_page_stride % 16 || a->k_slot_stride % 16 || a->k_head_stride % 16 || a->v_page_stride % 16 ||
+      a->v_slot_stride % 16 || a->v_head_stride % 16 || a->out_tok_stride % 8 || a->out_head_stride % 8 ||
+      (a->o_mul && !aligned(a->o_mul, 16)))
+    return MJ_EALIGN;
+  if (a->num_work != cap_for(cfg, d, a->q_len)) return MJ_EINVAL;
+  const bool split = cfg->max_splits > 1 && a->num_seqs < slots_for(cfg, d, a->q_len);
+  if ((a->with_reduction != 0) != split) return MJ_EINVAL;
+  const WorkspaceLayout wl = workspace_layout(cfg, d);
+  if (split && (!a->workspace || a->workspace_bytes < wl.total)) return MJ_ECAPACITY;
+  if (a->workspace && !aligned(a->workspace, 256)) return MJ_EALIGN;
+
+  char* ws = static_cast<char*>(a->workspace);
+  const bool has_ws = ws && a->workspace_bytes >= wl.total;
+  p->q8 = a->q8;
+  p->q_descale = a->q_descale;
+  p->k = static_cast<const uint8_t*>(a->k_cache);
+  p->v = static_cast<const uint8_t*>(a->v_cache);
+  p->k_sp = a->k_page_stride;
+  p->k_ss = a->k_slot_stride;
+  p->k_sh = a->k_head_stride;
+  p->v_sp = a->v_page_stride;
+  p->v_ss = a->v_slot_stride;
+  p->v_sh = a->v_head_stride;
+  p->num_pages = a->num_pages;
+  p->kd = a->k_descale;
+  p->vd = a->v_descale;
+  p->kd_kind = a->k_descale_kind;
+  p->vd_kind = a->v_descale_kind;
+  p->bt = a->block_table;
+  p->bt_stride = a->bt_row_stride;
+  p->max_blocks = a->max_blocks_per_seq;
+  p->seq_lens = a->seq_lens;
+  p->work = a->plan;
+  p->n_splits = a->plan + 4 * (size_t)d.cap_max;
+  p->split_begin = p->n_splits + cfg->max_num_seqs;
+  p->o_part = has_ws ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+  p->m_part = has_ws ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+  p->l_part = has_ws ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+  p->nqp = d.nq_max;
+  p->part_items = has_ws ? d.slots_max : 0;
+  p->scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p->o_mul = a->o_mul;
+  p->out = static_cast<uint16_t*>(a->out);
+  p->out_ts = a->out_tok_stride;
+  p->out_hs = a->out_head_stride;
+  p->lse = a->lse;
+  p->num_seqs = a->num_seqs;
+  p->q_len = a->q_len;
+  p->h_q = cfg->h_q;
+  p->h_k = cfg->h_k;
+  p->h_r = d.h_r;
+  p->n_q = a->q_len * d.h_r;
+  p->page_size = cfg->page_size;
+  p->page_shift = ilog2(cfg->page_size);
+  p->kv_tile = d.kv_tile;
+  p->causal = a->causal ? 1 : 0;
+  p->num_work = a->num_work;
+  return MJ_OK;
+}
+
+mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* a, hipStream_t stream) {
+  Derived d;
+  mj_status st = derive(cfg, &d);
+  if (st != MJ_OK) return st;
+  if (!a) return MJ_EINVAL;
+  mj::DecodeParams p;
+  st = fill_decode(cfg, d, a, &p);
+  if (st != MJ_OK) return st;
+  return mj::launch_decode(p, cfg->kv_format, row_tiles(cfg, a->q_len), stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t stream) {
+  Derived d;
+  mj_status st = derive(cfg, &d);
+  if (st != MJ_OK) return st;
+  if (!a || !a->plan || !a->workspace || !a->out || a->num_seqs < 1 || a->q_len < 1) return MJ_EINVAL;
+  if (a->num_seqs > cfg->max_num_seqs || a->q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  if (a->out_tok_stride < 0 || a->out_head_stride < 0) return MJ_EINVAL;
+  const WorkspaceLayout wl = workspace_layout(cfg, d);
+  if (a->workspace_bytes < wl.total) return MJ_ECAPACITY;
+  if (!aligned(a->workspace, 256) || !aligned(a->out, 16) || a->out_tok_stride % 8 || a->out_head_stride % 8)
+    return MJ_EALIGN;
+  const char* ws = static_cast<const char*>(a->workspace);
+  mj::MergeParams p;
+  p.n_splits = a->plan + 4 * (size_t)d.cap_max;
+  p.split_begin = p.n_splits + cfg->max_num_seqs;
+  p.o_part = reinterpret_cast<const float*>(ws + wl.o_off);
+  p.m_part = reinterpret_cast<const float*>(ws + wl.m_off);
+  p.l_part = reinterpret_cast<const float*>(ws + wl.l_off);
+  p.nqp = d.nq_max;
+  p.part_items = d.slots_max;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.out_ts = a->out_tok_stride;
+  p.out_hs = a->out_head_stride;
+  p.lse = a->lse;
+  p.num_seqs = a->num_seqs;
+  p.q_len = a->q_len;
+  p.h_q = cfg->h_q;
+  p.h_k = cfg->h_k;
+  p.h_r = d.h_r;
+  p.n_q = a->q_len * d.h_r;
+  return mj::launch_merge(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int32_t seq, int32_t head,
+                             int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream) {
+  mj_status st = check_config(cfg);
+  if (st != MJ_OK) return st;
+  if (!a || !dense_out || !a->block_table || (which != 0 && which != 1)) return MJ_EINVAL;
+  if (seq < 0 || head < 0 || head >= cfg->h_k || seq_len < 0 || a->num_pages < 1) return MJ_EINVAL;
+  if ((int64_t)seq_len > (int64_t)a->max_blocks_per_seq * cfg->page_size) return MJ_ECAPACITY;
+  mj::GatherParams p;
+  p.pool = static_cast<const uint8_t*>(which == 0 ? a->k_cache : a->v_cache);
+  if (!p.pool) return MJ_EINVAL;
+  p.sp = which == 0 ? a->k_page_stride : a->v_page_stride;
+  p.ss = which == 0 ? a->k_slot_stride : a->v_slot_stride;
+  p.sh = which == 0 ? a->k_head_stride : a->v_head_stride;
+  p.num_pages = a->num_pages;
+  p.bt = a->block_table;
+  p.bt_stride = a->bt_row_stride;
+  p.seq = seq;
+  p.head = head;
+  p.seq_len = seq_len;
+  p.row_bytes = cfg->kv_format == MJ_KV_E4M3 ? 128 : 96;
+  p.page_shift = ilog2(cfg->page_size);
+  p.out = dense_out;
+  return mj::launch_gather(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream) {
+  if (!codes || !out || n < 0 || (kv_format != MJ_KV_E4M3 && kv_format != MJ_KV_E2M3)) return MJ_EINVAL;
+  return mj::launch_decode_codes(kv_format, codes, n, out, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal (host <-> kernel) interface of the mj library.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mj {
+
+// Parameters of the Q quantization kernel.
+struct QQuantParams {
+  const uint16_t* q;  // bf16
+  int64_t q_ts, q_hs;  // token / head strides, elements
+  const float* q_mul;  // nullable (h_q, 128)
+  uint8_t* q8;         // (b, h_k, n_q, 128)
+  float* q_descale;    // (b, h_k)
+  int num_seqs, q_len, h_k, h_r, n_q;
+};
+
+// Parameters of the decode kernels.
+struct DecodeParams {
+  const uint8_t* q8;
+  const float* q_descale;
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t k_sp, k_ss, k_sh;
+  int64_t v_sp, v_ss, v_sh;
+  int64_t num_pages;
+  const float* kd;
+  const float* vd;
+  int kd_kind, vd_kind;
+  const int32_t* bt;
+  int64_t bt_stride;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* work;         // plan + 0
+  const int32_t* n_splits;     // plan + 4*cap_max
+  const int32_t* split_begin;  // plan + 4*cap_max + max_num_seqs
+  float* o_part;               // (S_max, h_k, nqp, 128)
+  float* m_part;               // (S_max, h_k, nqp)   log2 domain
+  float* l_part;               // (S_max, h_k, nqp)
+  int nqp;                     // partial row stride = max_q_len * h_r
+  int part_items;              // S_max: items that may hold partials
+  float scale_log2;            // softmax_scale * log2(e)
+  const float* o_mul;          // nullable (h_q, 128)
+  uint16_t* out;               // bf16
+  int64_t out_ts, out_hs;
+  float* lse;                  // nullable
+  int num_seqs, q_len, h_q, h_k, h_r, n_q;
+  int page_size, page_shift, kv_tile;
+  int causal;
+  int num_work;
+};
+
+struct MergeParams {
+  const int32_t* n_splits;
+  const int32_t* split_begin;
+  const float* o_part;
+  const float* m_part;
+  const float* l_part;
+  int nqp;
+  int part_items;
+  uint16_t* out;
+  int64_t out_ts, out_hs;
+  float* lse;
+  int num_seqs, q_len, h_q, h_k, h_r, n_q;
+};
+
+struct GatherParams {
+  const uint8_t* pool;
+  int64_t sp, ss, sh;
+  int64_t num_pages;
+  const int32_t* bt;
+  int64_t bt_stride;
+  int seq, head, seq_len, row_bytes, page_shift;
+  uint8_t* out;
+};
+
+hipError_t launch_qquant(const QQuantParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);
+
+}  // namespace mj

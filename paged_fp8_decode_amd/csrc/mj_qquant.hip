@@ -1,0 +1,92 @@
+// Dynamic e4m3 quantization of Q per (sequence, KV head), one workgroup per
+// (sequence, KV head).
+//
+// Definition (mjolnir-kernel wheel page mjolnir/runner.py,
+// T5DecodeRunner.run, fp8-Q branch; README "What it does", step 2): over the
+// q_len tokens and h_r query heads of KV head g, x = fp32(q) [* q_mul],
+// amax = max(max|x|, 1e-6f), s = amax / 448, code = e4m3(x / s), rows packed
+// t*h_r + r.  Every operation is one IEEE fp32 operation: the amax is exact,
+// the divisions are correctly rounded (built with
+// -fhip-fp32-correctly-rounded-divide-sqrt, never a reciprocal multiply) and
+// the e4m3 rounding is done in integer arithmetic, so the codes are
+// bit-identical to any other correct evaluation of the definition.
+//
+// Q is tiny (n_q x 128 values per workgroup), so the kernel simply reads it
+// twice (amax pass, quantize pass) with 16-byte loads of 8 bf16 values.
+#include "mj_device.h"
+#include "mj_internal.h"
+
+namespace mj {
+
+namespace {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ void load8(const QQuantParams& p, int seq, int g, int v, float x[8], int& row, int& c0) {
+  row = v >> 4;
+  c0 = (v & 15) * 8;
+  const int t = row / p.h_r;
+  const int rr = row - t * p.h_r;
+  const int h = g * p.h_r + rr;
+  const uint16_t* src = p.q + ((int64_t)seq * p.q_len + t) * p.q_ts + (int64_t)h * p.q_hs + c0;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+  if (p.q_mul) {
+    const float4 m0 = *reinterpret_cast<const float4*>(p.q_mul + (int64_t)h * kHeadDim + c0);
+    const float4 m1 = *reinterpret_cast<const float4*>(p.q_mul + (int64_t)h * kHeadDim + c0 + 4);
+    x[0] *= m0.x; x[1] *= m0.y; x[2] *= m0.z; x[3] *= m0.w;
+    x[4] *= m1.x; x[5] *= m1.y; x[6] *= m1.z; x[7] *= m1.w;
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void qquant_kernel(QQuantParams p) {
+  const int seq = blockIdx.x;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nvec = p.n_q * 16;
+  __shared__ float red[kQThreads / 64];
+
+  float amax = 0.0f;
+  for (int v = tid; v < nvec; v += kQThreads) {
+    float x[8];
+    int row, c0;
+    load8(p, seq, g, v, x, row, c0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  }
+  // wave64 max, then across the four waves
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  const float s = fmaxf(amax, 1e-6f) / 448.0f;
+  uint8_t* dst = p.q8 + ((int64_t)seq * p.h_k + g) * p.n_q * kHeadDim;
+  for (int v = tid; v < nvec; v += kQThreads) {
+    float x[8];
+    int row, c0;
+    load8(p, seq, g, v, x, row, c0);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lo |= e4m3_rne(x[e] / s) << (8 * e);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hi |= e4m3_rne(x[4 + e] / s) << (8 * e);
+    *reinterpret_cast<uint2*>(dst + (int64_t)row * kHeadDim + c0) = make_uint2(lo, hi);
+  }
+  if (tid == 0) p.q_descale[(int64_t)seq * p.h_k + g] = s;
+}
+
+}  // namespace
+
+hipError_t launch_qquant(const QQuantParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(qquant_kernel, dim3(p.num_seqs, p.h_k), dim3(kQThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mj

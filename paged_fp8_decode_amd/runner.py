@@ -1,0 +1,129 @@
+"""``DecodeStep``: one decode site's configuration, its persistent device
+buffers, and the four C-ABI calls in order (plan -> quantize Q -> decode ->
+merge).  Buffers are allocated once with torch (plumbing) at fixed
+addresses, so a hipGraph that captured ``run`` replays any later ``plan``
+(mjolnir-kernel wheel page mjolnir/runner.py, module docstring and
+T5DecodeRunner.__init__: fixed-address plan buffers padded to a fixed grid).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, check, mj_config, mj_config_check, mj_merge_lse,
+               mj_paged_decode, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_quantize_q,
+               mj_workspace_bytes)
+
+
+class DecodeStep:
+    def __init__(self, *, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, kv_format="e4m3",
+                 num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, device="cuda"):
+        self.device = torch.device(device)
+        if num_cus == 0:
+            num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+        self.cfg = mj_config(h_q=h_q, h_k=h_k, page_size=page_size, max_num_seqs=max_num_seqs, max_q_len=max_q_len,
+                             max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
+                             kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, kv_format=kv_format)
+        check(mj_config_check(self.cfg), "mj_config_check")
+        self.h_q, self.h_k, self.h_r = h_q, h_k, h_q // h_k
+        self.max_q_len = max_q_len
+        n_plan = mj_plan_buffer_bytes(self.cfg) // 4
+        self.plan_dev = torch.zeros(n_plan, dtype=torch.int32, device=self.device)
+        # two pinned staging slots: a slot is rewritten only after its copy ran
+        self._staging = [torch.zeros(n_plan, dtype=torch.int32).pin_memory() for _ in range(2)]
+        self._staging_done = [None, None]
+        self._slot = 0
+        self.workspace = torch.empty(max(256, mj_workspace_bytes(self.cfg)), dtype=torch.uint8, device=self.device)
+        n_q_max = max_q_len * self.h_r
+        self.q8 = torch.empty(max_num_seqs * h_k * n_q_max * 128, dtype=torch.uint8, device=self.device)
+        self.q_descale = torch.empty(max_num_seqs * h_k, dtype=torch.float32, device=self.device)
+        self.info: PlanInfo | None = None
+
+    def capacity(self, q_len: int) -> int:
+        return mj_plan_capacity(self.cfg, q_len)
+
+    def plan(self, seq_lens_host, q_len: int, max_blocks_per_seq: int, margin: int = 0, stream=None) -> PlanInfo:
+        """Host plan + async copy into the fixed plan buffer (outside capture)."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        slot = self._slot
+        if self._staging_done[slot] is not None:
+            self._staging_done[slot].synchronize()
+        info = mj_plan_split_kv(self.cfg, seq_lens_host, q_len, margin, max_blocks_per_seq, self._staging[slot],
+                                self.plan_dev, stream)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        self._staging_done[slot] = ev
+        self._slot ^= 1
+        self.info = info
+        return info
+
+    def run(self, *, q, k_cache, v_cache, k_strides, v_strides, num_pages, block_table, seq_lens, k_descale,
+            v_descale, descale_kind, softmax_scale, out, lse=None, q_mul=None, o_mul=None, causal=True,
+            info: PlanInfo | None = None, stream=None, events=None):
+        """quantize Q -> decode -> merge (iff the plan split), all on ``stream``.
+
+        q: bf16 (b*q_len, h_q, 128) view; out: bf16 (b*q_len, h_q, 128) view;
+        k/v strides: bytes (page, slot, head); block_table: int32 (b, max_blocks).
+        ``events``: optional pair of events recorded right before and right
+        after the decode launch (decode-kernel timing on this stream).
+        """
+        info = info or self.info
+        assert info is not None, "plan() first"
+        b, ql = info.num_seqs, info.q_len
+        stream = stream or torch.cuda.current_stream(self.device)
+        mj_quantize_q(self.cfg, q, q_mul, b, ql, self.q8, self.q_descale, stream)
+        kind = SCALE_KINDS[descale_kind] if isinstance(descale_kind, str) else descale_kind
+        a = DecodeArgs(
+            q8=self.q8.data_ptr(), q_descale=self.q_descale.data_ptr(), num_seqs=b, q_len=ql, causal=int(causal),
+            k_cache=k_cache.data_ptr(), k_page_stride=k_strides[0], k_slot_stride=k_strides[1],
+            k_head_stride=k_strides[2],
+            v_cache=v_cache.data_ptr(), v_page_stride=v_strides[0], v_slot_stride=v_strides[1],
+            v_head_stride=v_strides[2], num_pages=num_pages,
+            k_descale=k_descale.data_ptr(), k_descale_kind=kind, v_descale=v_descale.data_ptr(), v_descale_kind=kind,
+            block_table=block_table.data_ptr(), bt_row_stride=block_table.stride(0),
+            max_blocks_per_seq=block_table.shape[1], seq_lens=seq_lens.data_ptr(),
+            plan=self.plan_dev.data_ptr(), num_work=info.num_work, with_reduction=info.with_reduction,
+            workspace=self.workspace.data_ptr(), workspace_bytes=self.workspace.numel(),
+            softmax_scale=float(softmax_scale), o_mul=o_mul.data_ptr() if o_mul is not None else None,
+            out=out.data_ptr(), out_tok_stride=out.stride(0), out_head_stride=out.stride(1),
+            lse=lse.data_ptr() if lse is not None else None,
+        )
+        if events:
+            events[0].record(stream)
+        mj_paged_decode(self.cfg, a, stream)
+        if events:
+            events[1].record(stream)
+        if info.with_reduction:
+            m = MergeArgs(plan=self.plan_dev.data_ptr(), num_seqs=b, q_len=ql, workspace=self.workspace.data_ptr(),
+                          workspace_bytes=self.workspace.numel(), out=out.data_ptr(), out_tok_stride=out.stride(0),
+                          out_head_stride=out.stride(1), lse=lse.data_ptr() if lse is not None else None)
+            mj_merge_lse(self.cfg, m, stream)
+        return out
+
+    # convenience for seeded workloads (tests, bench, smoke)
+    @classmethod
+    def for_workload(cls, wl, device=None, **overrides):
+        s = wl.spec
+        kw = dict(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, max_q_len=s.q_len,
+                  kv_format=s.kv_format, slots_override=s.slots_override, device=device or wl.q.device)
+        kw.update(overrides)
+        return cls(**kw)
+
+    def plan_workload(self, wl, margin=0, stream=None) -> PlanInfo:
+        return self.plan(wl.seq_lens, wl.spec.q_len, wl.block_table.shape[1], margin, stream)
+
+    def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None):
+        ks, vs = wl.kv_strides()
+        return self.run(q=wl.q, k_cache=wl.k_pool, v_cache=wl.v_pool, k_strides=ks, v_strides=vs,
+                        num_pages=wl.num_pages, block_table=wl.block_table, seq_lens=wl.seq_lens_dev,
+                        k_descale=wl.k_descale, v_descale=wl.v_descale, descale_kind=wl.descale_kind,
+                        softmax_scale=wl.softmax_scale, out=out, lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul,
+                        causal=wl.spec.causal, info=info, stream=stream, events=events)
+
+
+def new_output(wl, device=None):
+    s = wl.spec
+    dev = device or wl.q.device
+    out = torch.empty(s.b * s.q_len, s.h_q, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(s.b * s.q_len, s.h_q, dtype=torch.float32, device=dev)
+    return out, lse

@@ -1,0 +1,193 @@
+"""Host-side tests of the C-ABI library (no GPU needed): it loads and exports
+every symbol include/mj.h declares; the C++ planner equals the oracle's plan
+bit for bit; argument validation rejects bad calls before any device work."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import paged_fp8_decode_amd as mj
+from oracle import plan as oplan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="fake device pointers: host-validation tests run where no GPU is visible")
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "mj.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:[\w\*\s]+?)\b(mj_\w+)\(", hdr, flags=re.M)))
+    assert len(names) >= 12, names
+    lib = ctypes.CDLL(mj.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert mj.lib().mj_abi_version() == 1
+
+
+def _cfg(**kw):
+    base = dict(h_q=32, h_k=8, page_size=16, max_num_seqs=64, max_q_len=1, max_splits=16, num_cus=256,
+                wgs_per_cu=2, kv_tile_tokens=128)
+    base.update(kw)
+    return mj.mj_config(**base)
+
+
+def _oracle(cfg, lens, q_len, margin=0):
+    return oplan.plan_split_kv(lens, q_len=q_len, h_q=cfg.h_q, h_k=cfg.h_k, num_cus=cfg.num_cus,
+                               wgs_per_cu=cfg.wgs_per_cu or 2, kv_tile=cfg.kv_tile_tokens or 128,
+                               max_splits=cfg.max_splits, max_num_seqs=cfg.max_num_seqs,
+                               slots_override=cfg.slots_override, margin=margin)
+
+
+def _unpack(cfg, img, q_len):
+    cap_max = max(mj.mj_plan_capacity(cfg, ql) for ql in range(1, cfg.max_q_len + 1))
+    work = img[: 4 * cap_max].reshape(cap_max, 4)
+    ns = img[4 * cap_max: 4 * cap_max + cfg.max_num_seqs]
+    sb = img[4 * cap_max + cfg.max_num_seqs:]
+    return work, ns, sb
+
+
+def _compare(cfg, lens, q_len, margin=0):
+    img, info = mj.mj_plan_compute(cfg, lens, q_len, margin)
+    ref = _oracle(cfg, lens, q_len, margin)
+    work, ns, sb = _unpack(cfg, img, q_len)
+    cap = ref["num_work"]
+    assert info.num_work == cap
+    assert [tuple(int(x) for x in w) for w in work[:cap]] == [tuple(w) for w in ref["work"]]
+    assert np.all(work[cap:] == [-1, 0, 0, 0])
+    assert ns[: len(lens)].tolist() == ref["n_splits"]
+    assert sb[: len(lens)].tolist() == ref["split_begin"]
+    assert info.chunk_tiles == ref["chunk_tiles"]
+    assert info.slots == ref["slots"]
+    assert info.num_chunks == ref["num_chunks"]
+    assert bool(info.with_reduction) == ref["with_reduction"]
+
+
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "32k"])
+def test_planner_matches_oracle_on_workloads(key):
+    import synth
+    s = synth.spec_for(key)
+    lens = synth.workloads._lens(s, np.random.default_rng(s.seed))
+    cfg = _cfg(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, max_q_len=s.q_len,
+               slots_override=s.slots_override)
+    _compare(cfg, lens, s.q_len)
+
+
+def test_planner_matches_oracle_random():
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        h_k = int(rng.choice([1, 2, 4, 8]))
+        h_q = h_k * int(rng.choice([1, 2, 4, 8, 16]))
+        mq = int(rng.integers(1, 6))
+        cfg = _cfg(h_q=h_q, h_k=h_k, max_num_seqs=int(rng.integers(1, 100)), max_q_len=mq,
+                   max_splits=int(rng.choice([1, 2, 4, 16, 32])), num_cus=int(rng.choice([20, 80, 256, 304])),
+                   wgs_per_cu=int(rng.integers(1, 5)), kv_tile_tokens=int(rng.choice([16, 64, 128, 256])),
+                   slots_override=int(rng.choice([0, 0, 0, 7, 300])))
+        b = int(rng.integers(1, cfg.max_num_seqs + 1))
+        lens = rng.integers(0, int(rng.choice([100, 5000, 200000])), size=b).tolist()
+        _compare(cfg, lens, int(rng.integers(1, mq + 1)), int(rng.integers(0, 8)))
+
+
+def test_config_errors():
+    assert mj.mj_config_check(_cfg()) == mj.MJ_OK
+    assert mj.mj_config_check(_cfg(head_dim=64)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(page_size=24)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(page_size=256)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(h_q=30, h_k=8)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(kv_format=3)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(max_num_seqs=0)) == mj.MJ_EINVAL
+    assert mj.mj_config_check(_cfg(kv_tile_tokens=100)) == mj.MJ_EINVAL
+    assert mj.mj_plan_buffer_bytes(_cfg(head_dim=64)) == 0
+    assert mj.mj_workspace_bytes(_cfg(page_size=8)) == 0
+
+
+def test_plan_errors():
+    cfg = _cfg(max_num_seqs=4, max_q_len=2)
+    with pytest.raises(mj.MjError) as e:
+        mj.mj_plan_compute(cfg, [10] * 5, 1)
+    assert e.value.status == mj.MJ_ECAPACITY
+    with pytest.raises(mj.MjError) as e:
+        mj.mj_plan_compute(cfg, [10], 3)
+    assert e.value.status == mj.MJ_ECAPACITY
+    with pytest.raises(mj.MjError) as e:
+        mj.mj_plan_compute(cfg, [10, -1], 1)
+    assert e.value.status == mj.MJ_EINVAL
+    with pytest.raises(mj.MjError) as e:  # 33 tokens need 3 pages of 16
+        mj.mj_plan_compute(cfg, [33], 1, max_blocks_per_seq=2)
+    assert e.value.status == mj.MJ_ECAPACITY
+    mj.mj_plan_compute(cfg, [32], 1, max_blocks_per_seq=2)
+
+
+FAKE = 1 << 20  # a 16-byte (and 256-byte) aligned, never dereferenced address
+
+
+def _args(cfg, **kw):
+    cap = mj.mj_plan_capacity(cfg, 1)
+    a = dict(q8=FAKE, q_descale=FAKE, num_seqs=4, q_len=1, causal=1, k_cache=FAKE, k_page_stride=16 * 8 * 128,
+             k_slot_stride=128, k_head_stride=16 * 128, v_cache=FAKE, v_page_stride=16 * 8 * 128, v_slot_stride=128,
+             v_head_stride=16 * 128, num_pages=100, k_descale=FAKE, k_descale_kind=0, v_descale=FAKE,
+             v_descale_kind=0, block_table=FAKE, bt_row_stride=8, max_blocks_per_seq=8, seq_lens=FAKE, plan=FAKE,
+             num_work=cap, with_reduction=1, workspace=FAKE, workspace_bytes=mj.mj_workspace_bytes(cfg),
+             softmax_scale=0.088, o_mul=None, out=FAKE, out_tok_stride=32 * 128, out_head_stride=128, lse=None)
+    a.update(kw)
+    return mj.DecodeArgs(**a)
+
+
+def _decode_status(cfg, **kw):
+    return mj.lib().mj_paged_decode(ctypes.byref(cfg), ctypes.byref(_args(cfg, **kw)), None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(q8=None), mj.MJ_EINVAL),
+    (dict(out=None), mj.MJ_EINVAL),
+    (dict(plan=None), mj.MJ_EINVAL),
+    (dict(num_seqs=0), mj.MJ_EINVAL),
+    (dict(num_seqs=65), mj.MJ_ECAPACITY),
+    (dict(q_len=2), mj.MJ_ECAPACITY),
+    (dict(num_work=5), mj.MJ_EINVAL),
+    (dict(with_reduction=0), mj.MJ_EINVAL),
+    (dict(workspace_bytes=1024), mj.MJ_ECAPACITY),
+    (dict(workspace=None), mj.MJ_ECAPACITY),
+    (dict(k_cache=FAKE + 8), mj.MJ_EALIGN),
+    (dict(v_slot_stride=120), mj.MJ_EALIGN),
+    (dict(out=FAKE + 2), mj.MJ_EALIGN),
+    (dict(out_head_stride=129), mj.MJ_EALIGN),
+    (dict(k_descale_kind=3), mj.MJ_EINVAL),
+    (dict(num_pages=0), mj.MJ_EINVAL),
+    (dict(bt_row_stride=4), mj.MJ_EINVAL),
+    (dict(softmax_scale=float("nan")), mj.MJ_EINVAL),
+])
+def test_decode_argument_errors(kw, status):
+    assert _decode_status(_cfg(), **kw) == status
+
+
+@no_gpu
+def test_decode_config_errors_come_first():
+    assert _decode_status(_cfg(page_size=12)) == mj.MJ_EUNSUPPORTED
+    assert mj.lib().mj_paged_decode(ctypes.byref(_cfg()), None, None) == mj.MJ_EINVAL
+
+
+@no_gpu
+def test_quantize_and_merge_errors():
+    cfg = _cfg()
+    L = mj.lib()
+    assert L.mj_quantize_q(ctypes.byref(cfg), None, 4096, 128, None, 4, 1, FAKE, FAKE, None) == mj.MJ_EINVAL
+    assert L.mj_quantize_q(ctypes.byref(cfg), FAKE + 2, 4096, 128, None, 4, 1, FAKE, FAKE, None) == mj.MJ_EALIGN
+    assert L.mj_quantize_q(ctypes.byref(cfg), FAKE, 4096, 100, None, 4, 1, FAKE, FAKE, None) == mj.MJ_EALIGN
+    assert L.mj_quantize_q(ctypes.byref(cfg), FAKE, 4096, 128, None, 65, 1, FAKE, FAKE, None) == mj.MJ_ECAPACITY
+    assert L.mj_quantize_q(ctypes.byref(cfg), FAKE, 4096, 128, None, 4, 2, FAKE, FAKE, None) == mj.MJ_ECAPACITY
+    m = mj.MergeArgs(plan=FAKE, num_seqs=4, q_len=1, workspace=FAKE, workspace_bytes=10, out=FAKE,
+                     out_tok_stride=4096, out_head_stride=128, lse=None)
+    assert L.mj_merge_lse(ctypes.byref(cfg), ctypes.byref(m), None) == mj.MJ_ECAPACITY
+    m.workspace_bytes = mj.mj_workspace_bytes(cfg)
+    m.out = FAKE + 4
+    assert L.mj_merge_lse(ctypes.byref(cfg), ctypes.byref(m), None) == mj.MJ_EALIGN
+    m.out = FAKE
+    m.num_seqs = 0
+    assert L.mj_merge_lse(ctypes.byref(cfg), ctypes.byref(m), None) == mj.MJ_EINVAL
+    assert L.mj_debug_decode_codes(7, FAKE, 4, FAKE, None) == mj.MJ_EINVAL

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+* integer / byte work is bit-exact: the kernels' code decoders (all codes),
+  the Q codes and descales, the gather through block table and strides;
+* outputs match the fp64 oracle per element within 1e-2 + 2e-2*|ref| on all
+  five workloads (reduced sizes: every output; full sizes: sampled
+  (sequence, KV head) pairs, in the launch configuration bench.py times);
+* physical page permutation gives bit-identical outputs; forced splits and no
+  splits both match; hipGraph replay after re-planning new lengths is correct.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import compare_lse, compare_out, oracle_step, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mj(gpu):
+    import paged_fp8_decode_amd as m
+    return m
+
+
+def _run(mj, wl, **overrides):
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    step = DecodeStep.for_workload(wl, **overrides)
+    info = step.plan_workload(wl)
+    out, lse = new_output(wl)
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    step.run_workload(wl, out, lse, info=info)
+    torch.cuda.synchronize()
+    return out, lse, info
+
+
+def test_code_decoders_exhaustive(mj, gpu):
+    from oracle.formats import E4M3_TABLE, E2M3_TABLE
+    codes = torch.arange(256, dtype=torch.uint8, device=gpu)
+    out = torch.empty(256, dtype=torch.float32, device=gpu)
+    mj.mj_debug_decode_codes("e4m3", codes, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    fin = ~np.isnan(E4M3_TABLE)
+    assert np.array_equal(got[fin], E4M3_TABLE[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(E4M3_TABLE[fin]))
+    codes = torch.arange(64, dtype=torch.uint8, device=gpu)
+    out = torch.empty(64, dtype=torch.float32, device=gpu)
+    mj.mj_debug_decode_codes("e2m3", codes, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), E2M3_TABLE)
+
+
+@pytest.mark.parametrize("b,q_len,h_q,h_k,mul,extra", [(1, 1, 8, 2, False, 0), (32, 1, 32, 8, False, 0),
+                                                       (16, 4, 64, 8, False, 16), (4, 1, 32, 8, True, 0),
+                                                       (3, 3, 16, 2, True, 4), (64, 1, 32, 8, False, 0)])
+def test_quantize_q_bit_exact(mj, gpu, b, q_len, h_q, h_k, mul, extra):
+    from oracle.qquant import quantize_q
+    say(f"qquant b={b} q_len={q_len} h_q={h_q} h_k={h_k} mul={mul} extra_heads={extra}")
+    g = torch.Generator().manual_seed(b + 7 * q_len)
+    full = (torch.randn(b * q_len, h_q + extra, 128, generator=g) * 3).to(torch.bfloat16)
+    full[0, 0, :5] = 0  # exact zeros and a tiny group
+    q = full.to(gpu)[:, :h_q]
+    q_mul = (torch.rand(h_q, 128, generator=g) * 2 + 0.05) if mul else None
+    cfg = mj.mj_config(h_q=h_q, h_k=h_k, page_size=16, max_num_seqs=b, max_q_len=q_len, num_cus=256)
+    q8 = torch.empty(b * h_k * q_len * (h_q // h_k) * 128, dtype=torch.uint8, device=gpu)
+    qd = torch.empty(b * h_k, dtype=torch.float32, device=gpu)
+    mj.mj_quantize_q(cfg, q, None if q_mul is None else q_mul.to(gpu), b, q_len, q8, qd)
+    torch.cuda.synchronize()
+    ref_c, ref_s = quantize_q(full[:, :h_q].float().numpy(), b, q_len, h_k, None if q_mul is None else q_mul.numpy())
+    assert np.array_equal(qd.cpu().numpy().reshape(b, h_k), ref_s)
+    assert np.array_equal(q8.cpu().numpy().reshape(ref_c.shape), ref_c)
+
+
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5"])
+def test_gather_probe_bit_exact(mj, gpu, key):
+    from oracle.attention import gather_codes
+    from paged_fp8_decode_amd.runner import DecodeStep
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    s = wl.spec
+    say(f"gather {s.name}")
+    step = DecodeStep.for_workload(wl)
+    ks, vs = wl.kv_strides()
+    a = mj.DecodeArgs(k_cache=wl.k_pool.data_ptr(), k_page_stride=ks[0], k_slot_stride=ks[1], k_head_stride=ks[2],
+                      v_cache=wl.v_pool.data_ptr(), v_page_stride=vs[0], v_slot_stride=vs[1], v_head_stride=vs[2],
+                      num_pages=wl.num_pages, block_table=wl.block_table.data_ptr(),
+                      bt_row_stride=wl.block_table.stride(0), max_blocks_per_seq=wl.block_table.shape[1])
+    h = wl.host()
+    row = s.row_bytes
+    for i in range(s.b):
+        L = wl.seq_lens[i]
+        for g in {0, s.h_k - 1}:
+            for which, pool, st in ((0, h["k_pool"], h["k_strides"]), (1, h["v_pool"], h["v_strides"])):
+                dense = torch.empty(max(1, L * row), dtype=torch.uint8, device=gpu)
+                mj.mj_debug_gather_kv(step.cfg, a, i, g, L, which, dense)
+                torch.cuda.synchronize()
+                ref = gather_codes(pool, st, s.page_size, h["block_table"][i], L, g, row)
+                assert np.array_equal(dense.cpu().numpy()[: L * row].reshape(L, row), ref)
+
+
+SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "32k"]
+
+
+@pytest.mark.parametrize("key", SMALL_KEYS)
+def test_parity_small_all_outputs(mj, gpu, key):
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    say(f"parity {wl.spec.name} lens={wl.seq_lens}")
+    out, lse, info = _run(mj, wl)
+    say(f"  plan: work={info.num_work} slots={info.slots} chunk_tiles={info.chunk_tiles} "
+        f"reduction={info.with_reduction}")
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, wl.spec.name)
+    compare_lse(lse, LSE, wl.spec.name)
+
+
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5"])
+def test_split_and_unsplit_agree(mj, gpu, key):
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    say(f"splits {wl.spec.name}")
+    O, LSE = oracle_step(wl)
+    for ms, ovr in ((1, 0), (16, 0), (16, 64), (4, 200)):
+        out, lse, info = _run(mj, wl, max_splits=ms, slots_override=ovr)
+        say(f"  max_splits={ms} slots_override={ovr}: reduction={info.with_reduction} chunks={info.num_chunks}")
+        compare_out(out, O, f"{wl.spec.name} ms={ms}")
+        compare_lse(lse, LSE, f"{wl.spec.name} ms={ms}")
+
+
+def test_page_permutation_bit_identical(mj, gpu):
+    wl = synth.build(synth.spec_for("cfg3", small=True), gpu)
+    say(f"permutation {wl.spec.name}")
+    out1, lse1, _ = _run(mj, wl)
+    perm = torch.randperm(wl.num_pages, generator=torch.Generator().manual_seed(3)).to(gpu)
+    inv = torch.argsort(perm)
+    wl.k_pool = wl.k_pool[perm].contiguous()
+    wl.v_pool = wl.v_pool[perm].contiguous()
+    wl.block_table = inv[wl.block_table.long()].to(torch.int32).contiguous()
+    out2, lse2, _ = _run(mj, wl)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
+
+
+def test_edge_lengths(mj, gpu):
+    # empty (padding) request, a single token, a length inside the first
+    # page, tile boundaries +-1, and causal rows that see no key (L < q_len)
+    wl = synth.build(synth.spec_for("cfg4c", small=True, b=7, lens=(0, 1, 2, 127, 128, 129, 3001)), gpu)
+    say(f"edges {wl.spec.name} lens={wl.seq_lens}")
+    out, lse, _ = _run(mj, wl)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, "edges")
+    compare_lse(lse, LSE, "edges")
+    assert torch.all(out[:4].float() == 0)  # L = 0: every row empty
+    wl = synth.build(synth.spec_for("cfg2", small=True, b=3, lens=(0, 1, 17)), gpu)
+    out, lse, _ = _run(mj, wl)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, "edges q_len=1")
+    compare_lse(lse, LSE, "edges q_len=1")
+
+
+def test_strided_q_view(mj, gpu):
+    wl = synth.build(synth.spec_for("cfg2", small=True, q_extra_heads=16), gpu)
+    say(f"strided Q {wl.spec.name} q.stride={wl.q.stride()}")
+    out, lse, _ = _run(mj, wl)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, "strided q")
+
+
+def test_graph_replay_after_replanning(mj, gpu):
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for("cfg4c", small=True), gpu)
+    say(f"graph replay {wl.spec.name}")
+    step = DecodeStep.for_workload(wl)
+    info = step.plan_workload(wl)
+    out, lse = new_output(wl)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run_workload(wl, out, lse, info=info)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run_workload(wl, out, lse, info=info)
+    torch.cuda.synchronize()
+    orig = list(wl.seq_lens)
+    rng = np.random.default_rng(5)
+    for trial in range(4):
+        lens = [int(x) for x in rng.integers(1, np.array(orig) + 1)]
+        wl.seq_lens = lens
+        wl.seq_lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        new_info = step.plan_workload(wl)
+        assert new_info.num_work == info.num_work and new_info.with_reduction == info.with_reduction
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        O, LSE = oracle_step(wl)
+        compare_out(out, O, f"replay {trial} lens={lens}")
+        compare_lse(lse, LSE, f"replay {trial}")
+
+
+FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "32k": 2}
+
+
+@pytest.mark.parametrize("key", list(FULL))
+def test_parity_full_size_sampled(mj, gpu, key):
+    """Full-size workloads in the bench's launch configuration; the oracle
+    checks every output row of a few sampled (sequence, KV head) pairs."""
+    wl = synth.build(synth.spec_for(key), gpu)
+    s = wl.spec
+    say(f"full {s.name}: b={s.b} kv_bytes={wl.kv_bytes()}")
+    out, lse, info = _run(mj, wl)
+    say(f"  plan: work={info.num_work} slots={info.slots} chunk_tiles={info.chunk_tiles} "
+        f"reduction={info.with_reduction}")
+    rng = np.random.default_rng(17)
+    lens = np.array(wl.seq_lens)
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), *rng.choice(s.b, size=min(s.b, FULL[key]) , replace=False).tolist()})
+    heads = sorted({0, s.h_k - 1})
+    O, LSE = oracle_step(wl, seqs=seqs, heads=heads)
+    compare_out(out, O, f"{s.name} seqs={seqs} heads={heads}")
+    compare_lse(lse, LSE, s.name)
