@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--extra", default="32k", help="comma list of extra workloads reported under 'extra' ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--variant", type=int, default=0,
+                    help="decode kernel: 0 automatic, 1 generic, 2 VALU-PV streaming (A/B runs)")
+    ap.add_argument("--no-nt", action="store_true", help="plain (not non-temporal) KV loads (A/B runs)")
     return ap.parse_args()
 
 
@@ -168,7 +171,9 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    import paged_fp8_decode_amd  # noqa: F401  (fails loudly if libmj.so is missing)
+    import paged_fp8_decode_amd
+
+    paged_fp8_decode_amd.mj_debug_set_decode_variant(args.variant, 0 if args.no_nt else 1)
 
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     main_res = measure(args.workload, args.steps, args.warmup, flush_buf)
@@ -195,7 +200,8 @@ def main():
         vs_baseline=None,
         dtype="e4m3" if "e2m3" not in main_res["workload"] else "e2m3",
         data="synthetic",
-        config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"]),
+        config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"], kernel_variant=args.variant,
+                    nontemporal=not args.no_nt),
         roofline=roof,
         cpu_baseline=cpu,
         detail=main_res,

@@ -247,6 +247,15 @@ mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* args, hipStrea
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, int32_t seq, int32_t head,
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream);
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);
+/* Process-wide choice of decode kernel, for A/B measurements and for testing
+ * every kernel on the same inputs: variant 0 = automatic (q_len*h_r <= 4:
+ * the matrix-core kernel for e4m3 KV, the VALU-PV streaming kernel for
+ * e2m3; otherwise the generic LDS-tiled kernel), 1 = always the generic
+ * kernel, 2 = the VALU-PV streaming kernel wherever q_len*h_r <= 4, 3 = same
+ * as 0.  nontemporal 1 (default) marks the streaming kernels' KV loads
+ * non-temporal.  Not thread-safe; set it before launching.  EINVAL on other
+ * values. */
+mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal);
 
 #ifdef __cplusplus
 }

@@ -4,8 +4,9 @@ packed-e2m3 KV cache on MI355X).
 The functions below carry the C names and only marshal arguments: every step
 of the decode path runs in the HIP kernels of ``libmj.so``.  PyTorch supplies
 device memory and the current HIP stream.  Importing works without a GPU
-(host-only entry points such as ``mj_plan_compute`` run on the CPU); a missing
-library raises ImportError -- there is no fallback implementation.
+(host-only entry points such as ``mj_plan_compute`` run on the CPU).  The
+library is loaded on first use; a missing or stale ``libmj.so`` raises
+ImportError there -- there is no fallback implementation.
 """
 
 from __future__ import annotations
@@ -18,8 +19,6 @@ from ._abi import (  # noqa: F401
     Config, PlanInfo, DecodeArgs, MergeArgs, MjError, KV_FORMATS, SCALE_KINDS,
     MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
 )
-
-lib()  # fail loudly at import if the library is missing
 
 
 def _stream(stream):
@@ -114,6 +113,10 @@ def mj_debug_decode_codes(kv_format, codes, out, stream=None):
     fmt = KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format
     check(lib().mj_debug_decode_codes(fmt, _ptr(codes), codes.numel(), _ptr(out), _stream(stream)),
           "mj_debug_decode_codes")
+
+
+def mj_debug_set_decode_variant(variant: int, nontemporal: int = 1):
+    check(lib().mj_debug_set_decode_variant(variant, nontemporal), "mj_debug_set_decode_variant")
 
 
 from .runner import DecodeStep  # noqa: E402,F401

@@ -78,8 +78,11 @@ def _load():
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
+        "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),
     }
     for name, (res, args) in sigs.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{LIB_PATH} is stale (no {name}): rebuild it (python paged_fp8_decode_amd/build.py)")
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args

@@ -1,0 +1,484 @@
+// Paged decode for GQA groups of up to 4 query rows (q_len * h_r <= 4) with
+// both products on the gfx950 matrix cores; e4m3 or packed-e2m3 KV.
+//
+// Method: mjolnir-kernel README "What it does", step 3 (stream KV pages,
+// online softmax) and the partials step 4 merges.  The pages' Thor design
+// (TMA ring into shared memory, TMEM accumulators, fp8 P) is not followed;
+// P stays in bf16 here.
+//
+// Work split: one workgroup (4 waves) per (plan item, KV head); 32-token
+// granules are dealt round-robin to the waves, which stream 4 adjacent
+// granules at a time and merge their softmax states through LDS at the end.
+// Lane l = 16*jj + n.
+//
+// QK^T (v_mfma_f32_16x16x128_f8f6f4 on e4m3 bytes): A = 16 tokens of K
+// (lane (n, jj): token n, codes [32jj, 32jj+32)), B = the Q rows (column n =
+// Q row n % 4, i.e. the <= 4 rows replicated four times).  The result puts
+// the logits of tokens 4jj..4jj+3 of the tile for Q row n % 4 in lane
+// (n, jj).  e4m3 K goes in as loaded; e2m3 K (24 bytes per lane) is expanded
+// exactly to e4m3 bytes first (hardware 32-code fp6 -> fp32 convert, then
+// fp32 -> fp8 packs; every e2m3 value is an e4m3 value).
+//
+// PV (v_mfma_f32_16x16x32_bf16): over one granule, lane (n, jj) holds p for
+// the 8 tokens tau(jj, e) = 16*(e/4) + 4*jj + e%4, e = 0..7, of row n % 4.
+// Taking e as the contraction index of lane group jj makes these 8 values
+// exactly the A operand (row n = P of Q row n % 4) -- no data movement.  The
+// B operand needs V[tau(jj, e)][channel] for the lane's column: lane (n, jj)
+// loads channels 8n..8n+7 of its 8 tokens (one 8-byte load per token; 4
+// tokens x whole rows per load instruction), converts them to fp32 and packs
+// token pairs of one channel into bf16 words, giving 8 B operands (channel
+// 8n + q, q = 0..7).  Eight MFMAs per granule leave O for all 4 rows and
+// channel 8n + q in every lane: the sum over tokens happens in the matrix
+// core and the accumulators are only 32 values per lane.
+//
+// Loads run one granule ahead (K and V double-buffered in registers) through
+// buffer resources built per tile in scalar registers: the per-lane offsets
+// are loop-invariant, and a dead tile (past the range end, invalid page) has
+// zero records, so its loads return zeros without a branch and the wait
+// before each use only covers the granule being computed.  KV bytes are
+// read once, non-temporally.  The softmax max per row is raised lazily (only
+// when a granule exceeds it by more than 8 in log2 units), which is exact.
+#include "mj_device.h"
+#include "mj_internal.h"
+
+namespace mj {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGran = 32;
+constexpr float kLazyMax = 8.0f;
+constexpr int kE8m0One = 127;
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<0> {                     // e4m3: 128-byte rows
+  static constexpr int kKDw = 8;    // K dwords per lane per tile (32 codes)
+  static constexpr int kKOff = 32;  // K bytes per lane group
+};
+template <>
+struct Fmt<1> {                     // e2m3: 96-byte rows, 4 codes per 3 bytes
+  static constexpr int kKDw = 6;
+  static constexpr int kKOff = 24;
+};
+
+template <int FMT>
+struct KRows {  // tile k: this lane's codes [32jj, 32jj+32) of token n
+  uint32_t d[2][Fmt<FMT>::kKDw];
+};
+struct VRows {  // element e: 8 bytes holding channels 8n..8n+7 of token tau(jj, e)
+  uint32_t d[8][2];
+};
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// reduce over the 4 lane groups jj (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max_jj(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_jj(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// two fp32 -> one word of two bf16 (round to nearest even; exact for KV values)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const v2bf v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+struct Ctx {
+  const int32_t* bt_row;
+  const uint8_t* kpool;  // pool + head offset (wave-uniform)
+  const uint8_t* vpool;
+  int64_t k_sp, v_sp;
+  uint32_t k_ss, v_ss;
+  uint32_t k_rec, v_rec; // bytes a 16-token tile spans from its first row
+  uint32_t k_lane;       // n * k_ss + codes offset of lane group jj
+  uint32_t v_lane;       // 4 * jj * v_ss + byte offset of channel 8n (4-aligned)
+  uint32_t num_pages;    // clamped to 2^31 - 1
+  int j0, j1, page_shift, pmask, lim0, causal, n, jj;
+  int v_shift;           // e2m3: bit offset of channel 8n in the loaded 8 bytes
+  float cscale;
+  int my_row_tok;        // token (within the q_len block) of this lane's Q row n % 4
+};
+
+// Page of the tile starting at token tk (wave-uniform), or -1 if the tile is
+// past the range end or its block-table entry is out of range.
+__device__ __forceinline__ int tile_page(const Ctx& c, int tk) {
+  const int idx = min(tk, c.j1 - 1);  // a granule exists only when j1 > j0
+  const int pg = c.bt_row[idx >> c.page_shift];
+  // all-ones when the tile is live; bit operations keep the block-table
+  // load out of any branch
+  const int live = ((tk - c.j1) >> 31) & -(int)((uint32_t)pg < c.num_pages);
+  return (pg & live) | ~live;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* pool, int64_t sp, uint32_t ss, uint32_t rec,
+                                                            int pg, int tk, int pmask) {
+  const uint8_t* base = pool + (int64_t)max(pg, 0) * sp + (uint32_t)(tk & pmask) * ss;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, pg >= 0 ? (int)rec : 0, kRsrcWord3);
+}
+
+template <int FMT, bool NT>
+__device__ __forceinline__ KRows<FMT> load_k(const Ctx& c, int gi) {
+  KRows<FMT> R;
+  const int t0 = c.j0 + gi * kGran;
+  constexpr int aux = NT ? 2 : 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int tk = t0 + 16 * k;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.kpool, c.k_sp, c.k_ss, c.k_rec, tile_page(c, tk), tk, c.pmask);
+    if constexpr (FMT == 0) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 0, aux);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 16, aux);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        R.d[k][i] = a[i];
+        R.d[k][4 + i] = b[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, c.k_lane, 8 * i, aux);
+        R.d[k][2 * i] = a[0];
+        R.d[k][2 * i + 1] = a[1];
+      }
+    }
+  }
+  return R;
+}
+
+template <bool NT>
+__device__ __forceinline__ VRows load_v(const Ctx& c, int gi) {
+  VRows R;
+  const int t0 = c.j0 + gi * kGran;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int tk = t0 + 16 * t;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.vpool, c.v_sp, c.v_ss, c.v_rec, tile_page(c, tk), tk, c.pmask);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, c.v_lane, v * c.v_ss, NT ? 2 : 0);
+      R.d[4 * t + v][0] = x[0];
+      R.d[4 * t + v][1] = x[1];
+    }
+  }
+  return R;
+}
+
+// K tile k as the fp8 A operand of the QK^T MFMA.
+template <int FMT>
+__device__ __forceinline__ v8i k_operand(const KRows<FMT>& K, int k) {
+  v8i a;
+  if constexpr (FMT == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (int)K.d[k][i];
+  } else {
+    v6i src;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) src[i] = (int)K.d[k][i];
+    const v32f f = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(src, 1.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i], f[4 * i + 1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * i + 2], f[4 * i + 3], w, true);
+      a[i] = w;
+    }
+  }
+  return a;
+}
+
+// V of one granule as 8 bf16 B operands: vb[q] = channel 8n + q of the 8
+// tokens tau(jj, 0..7), as 4 words of token pairs (2i, 2i+1).
+template <int FMT>
+__device__ __forceinline__ void v_operands(const Ctx& c, const VRows& V, uint32_t vb[8][4]) {
+  if constexpr (FMT == 0) {
+    float f[8][8];  // [token e][channel q]
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int dw = 0; dw < 2; ++dw) {
+        const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][dw], 1.0f, false);
+        const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][dw], 1.0f, true);
+        f[e][4 * dw + 0] = lo[0];
+        f[e][4 * dw + 1] = lo[1];
+        f[e][4 * dw + 2] = hi[0];
+        f[e][4 * dw + 3] = hi[1];
+      }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vb[q][i] = pack_bf16(f[2 * i][q], f[2 * i + 1][q]);
+  } else {
+    // per tile t: the 48-bit channel groups of its 4 tokens form one
+    // 192-bit stream of 32 codes (token-major) for the hardware converter
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t d0 = V.d[4 * t + v][0], d1 = V.d[4 * t + v][1];
+        lo[v] = __builtin_amdgcn_alignbit(d1, d0, c.v_shift);      // codes 0..4 and 2 bits of 5
+        hi[v] = (d1 >> c.v_shift) & 0xFFFFu;                       // the rest of the 48 bits
+      }
+      v6i src;
+      src[0] = (int)lo[0];
+      src[1] = (int)(hi[0] | (lo[1] << 16));
+      src[2] = (int)((lo[1] >> 16) | (hi[1] << 16));
+      src[3] = (int)lo[2];
+      src[4] = (int)(hi[2] | (lo[3] << 16));
+      src[5] = (int)((lo[3] >> 16) | (hi[3] << 16));
+      const v32f f = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(src, 1.0f);  // f[8 * v + q]
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        vb[q][2 * t + 0] = pack_bf16(f[q], f[8 + q]);
+        vb[q][2 * t + 1] = pack_bf16(f[16 + q], f[24 + q]);
+      }
+    }
+  }
+}
+
+struct State {
+  float m[4];   // reference max per Q row, log2 units (wave-uniform)
+  float l;      // this lane's partial sum for Q row n % 4
+  v4f acc[8];   // O[row v][channel 8n + q] in acc[q][v]
+};
+
+template <int FMT>
+__device__ __forceinline__ void granule(const Ctx& c, const v8i& qb, int gi, const KRows<FMT>& K, const VRows& V,
+                                        State& st) {
+  const int t0 = c.j0 + gi * kGran;
+  // ---- logits: lane (n, jj) gets tokens t0 + 16k + 4jj + v for Q row n % 4
+  float s[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const v8i ka = k_operand<FMT>(K, k);
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, zero, 0, 0, 0, kE8m0One, 0, kE8m0One);
+    const int tk = t0 + 16 * k;
+    // tokens at or past `end` are masked; a dead tile masks all of them
+    const int end = tile_page(c, tk) >= 0 ? c.j1 : 0;  // scalar; the block-table entry is cached
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = tk + 4 * c.jj + v;
+      const bool vis = t < end && (!c.causal || t <= c.lim0 + c.my_row_tok);
+      s[k][v] = vis ? d[v] * c.cscale : -INFINITY;
+    }
+  }
+  // ---- online softmax: per-row max over the granule, lazily raised
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = max_jj(mx);  // lane (n, jj): max of Q row n % 4 over the granule
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float M = lane_f(mx, r);  // lane r holds Q row r
+    if (M > st.m[r] + kLazyMax) {   // wave-uniform
+      const float a = exp2f(st.m[r] - M);  // m = -inf -> 0
+      st.m[r] = M;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st.acc[q][r] *= a;
+      if ((c.n & 3) == r) st.l *= a;
+    }
+  }
+  const int myr = c.n & 3;
+  float ms = myr == 0 ? st.m[0] : myr == 1 ? st.m[1] : myr == 2 ? st.m[2] : st.m[3];
+  ms = ms == -INFINITY ? 0.0f : ms;
+  float p[8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[4 * k + v] = exp2f(s[k][v] - ms);
+      st.l += p[4 * k + v];
+    }
+  u32x4 pw;  // A operand: element e = 4k + v, token pairs per word
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+  const v8bf pa = __builtin_bit_cast(v8bf, pw);
+  // ---- PV
+  uint32_t vb[8][4];
+  v_operands<FMT>(c, V, vb);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const u32x4 w = {vb[q][0], vb[q][1], vb[q][2], vb[q][3]};
+    st.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(v8bf, w), st.acc[q], 0, 0, 0);
+  }
+}
+
+template <int FMT, bool NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_mfma_kernel(DecodeParams p) {
+  using F = Fmt<FMT>;
+  __shared__ float o_s[kWaves][4][kHeadDim];
+  __shared__ float m_s[kWaves][4], l_s[kWaves][4];
+
+  const int w = blockIdx.x;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, jj = lane >> 4;
+  const int seq = p.work[4 * w];
+  if (seq < 0 || seq >= p.num_seqs) return;
+
+  int L = p.seq_lens[seq];
+  L = max(0, min(L, p.max_blocks * p.page_size));
+  Ctx c;
+  c.j0 = p.work[4 * w + 1] * p.kv_tile;
+  c.j1 = min(p.work[4 * w + 2] * p.kv_tile, L);
+  c.causal = p.causal && p.q_len > 1;
+  c.lim0 = L - p.q_len;
+  c.n = n;
+  c.jj = jj;
+  c.bt_row = p.bt + (int64_t)seq * p.bt_stride;
+  c.kpool = p.k + (int64_t)g * p.k_sh;
+  c.vpool = p.v + (int64_t)g * p.v_sh;
+  c.k_sp = p.k_sp;
+  c.v_sp = p.v_sp;
+  c.k_ss = (uint32_t)p.k_ss;
+  c.v_ss = (uint32_t)p.v_ss;
+  constexpr uint32_t row = FMT == 0 ? 128u : 96u;
+  c.k_rec = 15u * c.k_ss + row;
+  c.v_rec = 15u * c.v_ss + row;
+  c.k_lane = (uint32_t)(n * p.k_ss + F::kKOff * jj);
+  const uint32_t vch = FMT == 0 ? 8u * n : (6u * n) & ~3u;  // 4-aligned byte offset holding channel 8n
+  c.v_lane = (uint32_t)(4 * jj * p.v_ss) + vch;
+  c.v_shift = FMT == 0 ? 0 : 16 * (n & 1);
+  c.num_pages = (uint32_t)min<int64_t>(p.num_pages, 0x7FFFFFFF);
+  c.page_shift = p.page_shift;
+  c.pmask = p.page_size - 1;
+  c.cscale = p.q_descale[(int64_t)seq * p.h_k + g] * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
+  c.my_row_tok = (n & 3) / p.h_r;
+  const bool single = p.n_splits[seq] <= 1;
+
+  // B operand of QK^T: column n = Q row n % 4 (zero if it does not exist)
+  v8i qb;
+  {
+    const int r = n & 3;
+    if (r < p.n_q) {
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim + 32 * jj);
+      const u32x4 a = src[0], b = src[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qb[i] = (int)a[i];
+        qb[4 + i] = (int)b[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qb[i] = 0;
+    }
+  }
+
+  State st;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st.m[r] = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) st.acc[q] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
+  int gi = wave;
+  if (gi < ngr) {
+    KRows<FMT> KA = load_k<FMT, NT>(c, gi);
+    VRows VA = load_v<NT>(c, gi);
+    while (true) {
+      KRows<FMT> KB = load_k<FMT, NT>(c, gi + kWaves);
+      VRows VB = load_v<NT>(c, gi + kWaves);
+      granule<FMT>(c, qb, gi, KA, VA, st);
+      gi += kWaves;
+      if (gi >= ngr) break;
+      KA = load_k<FMT, NT>(c, gi + kWaves);
+      VA = load_v<NT>(c, gi + kWaves);
+      granule<FMT>(c, qb, gi, KB, VB, st);
+      gi += kWaves;
+      if (gi >= ngr) break;
+    }
+  }
+
+  // per-wave results: O rows 0..3 x channels (lanes jj == 0), sums per row
+  const float lrow = sum_jj(st.l);  // lane (n, jj): sum of Q row n % 4
+  if (jj == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o_s[wave][v][8 * n + q] = st.acc[q][v];
+  }
+  if (lane < 4) {
+    l_s[wave][lane] = lrow;
+    m_s[wave][lane] = lane == 0 ? st.m[0] : lane == 1 ? st.m[1] : lane == 2 ? st.m[2] : st.m[3];
+  }
+  __syncthreads();
+
+  // combine the 4 waves; thread -> (row r, channel ch), r in {tid>>7, (tid>>7)+2}
+  const int ch = threadIdx.x & 127;
+  const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k);
+  for (int r = threadIdx.x >> 7; r < p.n_q; r += 2) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, m_s[ww][r]);
+    const float Ms = M == -INFINITY ? 0.0f : M;
+    float Lsum = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float wt = exp2f(m_s[ww][r] - Ms);
+      Lsum += wt * l_s[ww][r];
+      O += wt * o_s[ww][r][ch];
+    }
+    const int t = r / p.h_r;
+    const int h = g * p.h_r + (r - t * p.h_r);
+    const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vd;
+    if (single) {
+      const float o = Lsum > 0.0f ? O / Lsum * om : 0.0f;
+      p.out[((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + ch] = f32_to_bf16(o);
+      if (ch == 0 && p.lse)
+        p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+    } else if (w < p.part_items) {
+      const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + r;
+      p.o_part[idx * kHeadDim + ch] = O * om;
+      if (ch == 0) {
+        p.m_part[idx] = Lsum > 0.0f ? M : -INFINITY;
+        p.l_part[idx] = Lsum;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, hipStream_t s) {
+  const dim3 grid(p.num_work, p.h_k);
+  if (kv_format == 0) {
+    if (nontemporal)
+      hipLaunchKernelGGL((decode_mfma_kernel<0, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<0, false>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (nontemporal)
+      hipLaunchKernelGGL((decode_mfma_kernel<1, true>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<1, false>), grid, dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mj

@@ -392,6 +392,12 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
   return mj::launch_gather(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
+mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal) {
+  if (variant < 0 || variant > 3 || (nontemporal != 0 && nontemporal != 1)) return MJ_EINVAL;
+  mj::set_decode_variant(variant, nontemporal);
+  return MJ_OK;
+}
+
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream) {
   if (!codes || !out || n < 0 || (kv_format != MJ_KV_E4M3 && kv_format != MJ_KV_E2M3)) return MJ_EINVAL;
   return mj::launch_decode_codes(kv_format, codes, n, out, stream) == hipSuccess ? MJ_OK : MJ_EHIP;

@@ -80,6 +80,7 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hi
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+void set_decode_variant(int variant, int nontemporal);
 hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);
 
 }  // namespace mj

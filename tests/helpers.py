@@ -11,9 +11,13 @@ import numpy as np
 # element: |gpu - ref| <= ATOL + RTOL * |ref| (max-abs 1e-2, max-rel 2e-2).
 ATOL = 1e-2
 RTOL = 2e-2
-# LSE is a diagnostic of the softmax normaliser (fp32 accumulation over up
-# to 2^17 keys); it is held to a looser absolute bound.
+# LSE is a diagnostic of the softmax normaliser, held to an absolute bound
+# plus a part relative to its size: the matrix-core fp8 dot products that
+# produce the logits accumulate with a relative error near 2^-13 of the sum
+# of |products| (measured on the hardware), which shifts large logits (K
+# outlier channels) by a few 1e-3.
 LSE_ATOL = 2e-3
+LSE_RTOL = 2e-4
 
 
 def say(*a):
@@ -45,7 +49,7 @@ def compare_lse(lse_gpu, LSE_ref, what=""):
     if fin.any():
         d = np.abs(g[fin] - LSE_ref[fin])
         say(f"  {what} lse: max_abs={d.max():.3e}")
-        assert d.max() <= LSE_ATOL + 1e-5 * np.abs(LSE_ref[fin]).max(), f"{what}: lse max_abs {d.max()}"
+        assert np.all(d <= LSE_ATOL + LSE_RTOL * np.abs(LSE_ref[fin])), f"{what}: lse max_abs {d.max()}"
 
 
 def oracle_step(wl, seqs=None, heads=None, quantize=True):

@@ -103,12 +103,23 @@ def test_gather_probe_bit_exact(mj, gpu, key):
 
 
 SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "32k"]
+# 0 = automatic choice, 1 = generic LDS kernel, 2 = VALU-PV streaming kernel
+VARIANTS = [0, 1, 2]
 
 
+@pytest.fixture
+def variant(mj, request):
+    v = getattr(request, "param", 0)
+    mj.mj_debug_set_decode_variant(v, 1)
+    yield v
+    mj.mj_debug_set_decode_variant(0, 1)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
 @pytest.mark.parametrize("key", SMALL_KEYS)
-def test_parity_small_all_outputs(mj, gpu, key):
+def test_parity_small_all_outputs(mj, gpu, key, variant):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
-    say(f"parity {wl.spec.name} lens={wl.seq_lens}")
+    say(f"parity {wl.spec.name} variant={variant} lens={wl.seq_lens}")
     out, lse, info = _run(mj, wl)
     say(f"  plan: work={info.num_work} slots={info.slots} chunk_tiles={info.chunk_tiles} "
         f"reduction={info.with_reduction}")
@@ -118,7 +129,8 @@ def test_parity_small_all_outputs(mj, gpu, key):
 
 
 @pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5"])
-def test_split_and_unsplit_agree(mj, gpu, key):
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+def test_split_and_unsplit_agree(mj, gpu, key, variant):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
     say(f"splits {wl.spec.name}")
     O, LSE = oracle_step(wl)
@@ -129,7 +141,8 @@ def test_split_and_unsplit_agree(mj, gpu, key):
         compare_lse(lse, LSE, f"{wl.spec.name} ms={ms}")
 
 
-def test_page_permutation_bit_identical(mj, gpu):
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+def test_page_permutation_bit_identical(mj, gpu, variant):
     wl = synth.build(synth.spec_for("cfg3", small=True), gpu)
     say(f"permutation {wl.spec.name}")
     out1, lse1, _ = _run(mj, wl)
@@ -143,7 +156,8 @@ def test_page_permutation_bit_identical(mj, gpu):
     assert torch.equal(lse1, lse2)
 
 
-def test_edge_lengths(mj, gpu):
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+def test_edge_lengths(mj, gpu, variant):
     # empty (padding) request, a single token, a length inside the first
     # page, tile boundaries +-1, and causal rows that see no key (L < q_len)
     wl = synth.build(synth.spec_for("cfg4c", small=True, b=7, lens=(0, 1, 2, 127, 128, 129, 3001)), gpu)
@@ -158,6 +172,16 @@ def test_edge_lengths(mj, gpu):
     O, LSE = oracle_step(wl)
     compare_out(out, O, "edges q_len=1")
     compare_lse(lse, LSE, "edges q_len=1")
+    # speculative blocks small enough for the streaming kernels (q_len*h_r <= 4)
+    lens = (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, 1000)
+    for q_len, h_q, h_k, causal in ((2, 16, 8, True), (4, 8, 8, True), (4, 8, 8, False), (2, 4, 2, False)):
+        wl = synth.build(synth.spec_for("cfg2", small=True, b=len(lens), lens=lens, q_len=q_len, h_q=h_q, h_k=h_k,
+                                        causal=causal, k_outliers=0), gpu)
+        say(f"  edges q_len={q_len} h_q={h_q} h_k={h_k} causal={causal}")
+        out, lse, _ = _run(mj, wl)
+        O, LSE = oracle_step(wl)
+        compare_out(out, O, f"edges q_len={q_len} causal={causal}")
+        compare_lse(lse, LSE, f"edges q_len={q_len} causal={causal}")
 
 
 def test_strided_q_view(mj, gpu):
@@ -206,7 +230,7 @@ FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "32k
 
 
 @pytest.mark.parametrize("key", list(FULL))
-def test_parity_full_size_sampled(mj, gpu, key):
+def test_parity_full_size_sampled(mj, gpu, key, variant):
     """Full-size workloads in the bench's launch configuration; the oracle
     checks every output row of a few sampled (sequence, KV head) pairs."""
     wl = synth.build(synth.spec_for(key), gpu)
