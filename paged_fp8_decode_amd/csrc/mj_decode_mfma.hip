@@ -258,79 +258,134 @@ __device__ __forceinline__ void v_operands(const Ctx& c, const VRows& V, uint32_
   }
 }
 
+// Row layout of a GQA group of n_q <= 32 query rows: NRB blocks of 16 rows;
+// a group of NQB < 16 rows (one block) is replicated 16 / NQB times.
+//  - softmax layout (QK^T output): lane (n, jj) holds row 16R + n % NQB of
+//    block R for the 8 tokens tau(jj, e) of the granule;
+//  - O layout (PV output): lane (n, jj) holds rows 16R + (4jj + v) % NQB,
+//    v = 0..3, for channels 8n + q.
+// With NQB == 4 every lane holds all 4 rows in both layouts, the rows' max
+// is wave-uniform and rescaling needs no lane exchange.
+template <int NQB, int NRB>
 struct State {
-  float m[4];   // reference max per Q row, log2 units (wave-uniform)
-  float l;      // this lane's partial sum for Q row n % 4
-  v4f acc[8];   // O[row v][channel 8n + q] in acc[q][v]
+  float m[NRB];         // reference max of this lane's softmax row, log2 units
+  float l[NRB];         // this lane's partial sum of that row
+  v4f acc[NRB][8];      // O rows 16R + (4jj + v) % NQB, channel 8n + q: acc[R][q][v]
 };
 
-template <int FMT>
-__device__ __forceinline__ void granule(const Ctx& c, const v8i& qb, int gi, const KRows<FMT>& K, const VRows& V,
-                                        State& st) {
+template <int NQB, int NRB>
+__device__ __forceinline__ float row_of(const Ctx& c, int R) {  // softmax-layout row of this lane
+  return 16 * R + (c.n % NQB);
+}
+
+template <int FMT, int NQB, int NRB>
+__device__ __forceinline__ void granule(const Ctx& c, const v8i (&qb)[NRB], const int (&row_tok)[NRB], int gi,
+                                        const KRows<FMT>& K, const VRows& V, State<NQB, NRB>& st) {
   const int t0 = c.j0 + gi * kGran;
-  // ---- logits: lane (n, jj) gets tokens t0 + 16k + 4jj + v for Q row n % 4
-  float s[2][4];
+  // ---- logits: lane (n, jj) gets tokens t0 + 16k + 4jj + v of its rows
+  float s[NRB][2][4];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const v8i ka = k_operand<FMT>(K, k);
-    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, zero, 0, 0, 0, kE8m0One, 0, kE8m0One);
     const int tk = t0 + 16 * k;
     // tokens at or past `end` are masked; a dead tile masks all of them
     const int end = tile_page(c, tk) >= 0 ? c.j1 : 0;  // scalar; the block-table entry is cached
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = tk + 4 * c.jj + v;
-      const bool vis = t < end && (!c.causal || t <= c.lim0 + c.my_row_tok);
-      s[k][v] = vis ? d[v] * c.cscale : -INFINITY;
+    for (int R = 0; R < NRB; ++R) {
+      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[R], zero, 0, 0, 0, kE8m0One, 0,
+                                                                      kE8m0One);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = tk + 4 * c.jj + v;
+        const bool vis = t < end && (!c.causal || t <= c.lim0 + row_tok[R]);
+        s[R][k][v] = vis ? d[v] * c.cscale : -INFINITY;
+      }
     }
   }
-  // ---- online softmax: per-row max over the granule, lazily raised
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = max_jj(mx);  // lane (n, jj): max of Q row n % 4 over the granule
+  // ---- online softmax: max of each row over the granule, raised lazily
+  float M[NRB];
+  bool raise = false;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float M = lane_f(mx, r);  // lane r holds Q row r
-    if (M > st.m[r] + kLazyMax) {   // wave-uniform
-      const float a = exp2f(st.m[r] - M);  // m = -inf -> 0
-      st.m[r] = M;
+  for (int R = 0; R < NRB; ++R) {
+    float mx = fmaxf(fmaxf(fmaxf(s[R][0][0], s[R][0][1]), fmaxf(s[R][0][2], s[R][0][3])),
+                     fmaxf(fmaxf(s[R][1][0], s[R][1][1]), fmaxf(s[R][1][2], s[R][1][3])));
+    M[R] = max_jj(mx);
+    raise |= M[R] > st.m[R] + kLazyMax;
+  }
+  if constexpr (NQB == 4 && NRB == 1) {
+    // every lane holds rows 0..3 in the O layout: per-row uniform decisions
 #pragma unroll
-      for (int q = 0; q < 8; ++q) st.acc[q][r] *= a;
-      if ((c.n & 3) == r) st.l *= a;
+    for (int r = 0; r < 4; ++r) {
+      const float Mr = lane_f(M[0], r);       // lane r holds row r
+      const float mr = lane_f(st.m[0], r);
+      if (Mr > mr + kLazyMax) {               // wave-uniform
+        const float a = exp2f(mr - Mr);       // m = -inf -> 0
+#pragma unroll
+        for (int q = 0; q < 8; ++q) st.acc[0][q][r] *= a;
+        if ((c.n & 3) == r) {
+          st.m[0] = Mr;
+          st.l[0] *= a;
+        }
+      }
+    }
+  } else {
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // rare after the first granules
+#pragma unroll
+      for (int R = 0; R < NRB; ++R) {
+        const bool up = M[R] > st.m[R] + kLazyMax;
+        const float a = up ? exp2f(st.m[R] - M[R]) : 1.0f;
+        st.m[R] = up ? M[R] : st.m[R];
+        st.l[R] *= a;
+        // O-layout row 16R + (4jj + v) % NQB lives in softmax-layout lane
+        // (jj, (4jj + v) % NQB)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int src = (c.jj << 4) | ((4 * c.jj + v) % NQB);
+          const float av = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(a)));
+#pragma unroll
+          for (int q = 0; q < 8; ++q) st.acc[R][q][v] *= av;
+        }
+      }
     }
   }
-  const int myr = c.n & 3;
-  float ms = myr == 0 ? st.m[0] : myr == 1 ? st.m[1] : myr == 2 ? st.m[2] : st.m[3];
-  ms = ms == -INFINITY ? 0.0f : ms;
-  float p[8];
+  // ---- P (bf16 A operands) and the row sums
+  v8bf pa[NRB];
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+  for (int R = 0; R < NRB; ++R) {
+    const float ms = st.m[R] == -INFINITY ? 0.0f : st.m[R];
+    float p[8];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p[4 * k + v] = exp2f(s[k][v] - ms);
-      st.l += p[4 * k + v];
-    }
-  u32x4 pw;  // A operand: element e = 4k + v, token pairs per word
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pw[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
-  const v8bf pa = __builtin_bit_cast(v8bf, pw);
+      for (int v = 0; v < 4; ++v) {
+        p[4 * k + v] = exp2f(s[R][k][v] - ms);
+        st.l[R] += p[4 * k + v];
+      }
+    u32x4 pw;  // element e = 4k + v, token pairs per word
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+    pa[R] = __builtin_bit_cast(v8bf, pw);
+  }
   // ---- PV
   uint32_t vb[8][4];
   v_operands<FMT>(c, V, vb);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const u32x4 w = {vb[q][0], vb[q][1], vb[q][2], vb[q][3]};
-    st.acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(v8bf, w), st.acc[q], 0, 0, 0);
+    const v8bf b = __builtin_bit_cast(v8bf, w);
+#pragma unroll
+    for (int R = 0; R < NRB; ++R) st.acc[R][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], b, st.acc[R][q], 0, 0, 0);
   }
 }
 
-template <int FMT, bool NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int FMT, int NQB, int NRB, bool NT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1, 2)))
 void decode_mfma_kernel(DecodeParams p) {
   using F = Fmt<FMT>;
-  __shared__ float o_s[kWaves][4][kHeadDim];
-  __shared__ float m_s[kWaves][4], l_s[kWaves][4];
+  constexpr int kRows = NQB * NRB;  // rows of the GQA group this instance serves (padded)
+  __shared__ float o_s[kWaves][kRows][kHeadDim];
+  __shared__ float m_s[kWaves][kRows], l_s[kWaves][kRows];
 
   const int w = blockIdx.x;
   const int g = blockIdx.y;
@@ -367,34 +422,38 @@ void decode_mfma_kernel(DecodeParams p) {
   c.page_shift = p.page_shift;
   c.pmask = p.page_size - 1;
   c.cscale = p.q_descale[(int64_t)seq * p.h_k + g] * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
-  c.my_row_tok = (n & 3) / p.h_r;
   const bool single = p.n_splits[seq] <= 1;
 
-  // B operand of QK^T: column n = Q row n % 4 (zero if it does not exist)
-  v8i qb;
-  {
-    const int r = n & 3;
+  // B operands of QK^T: column n of block R = Q row 16R + n % NQB (zero past n_q)
+  v8i qb[NRB];
+  int row_tok[NRB];
+#pragma unroll
+  for (int R = 0; R < NRB; ++R) {
+    const int r = 16 * R + (n % NQB);
+    row_tok[R] = r / p.h_r;
     if (r < p.n_q) {
       const u32x4* src =
           reinterpret_cast<const u32x4*>(p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim + 32 * jj);
       const u32x4 a = src[0], b = src[1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qb[i] = (int)a[i];
-        qb[4 + i] = (int)b[i];
+        qb[R][i] = (int)a[i];
+        qb[R][4 + i] = (int)b[i];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[i] = 0;
+      for (int i = 0; i < 8; ++i) qb[R][i] = 0;
     }
   }
 
-  State st;
+  State<NQB, NRB> st;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) st.m[r] = -INFINITY;
-  st.l = 0.0f;
+  for (int R = 0; R < NRB; ++R) {
+    st.m[R] = -INFINITY;
+    st.l[R] = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) st.acc[q] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < 8; ++q) st.acc[R][q] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
   int gi = wave;
@@ -404,32 +463,36 @@ void decode_mfma_kernel(DecodeParams p) {
     while (true) {
       KRows<FMT> KB = load_k<FMT, NT>(c, gi + kWaves);
       VRows VB = load_v<NT>(c, gi + kWaves);
-      granule<FMT>(c, qb, gi, KA, VA, st);
+      granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KA, VA, st);
       gi += kWaves;
       if (gi >= ngr) break;
       KA = load_k<FMT, NT>(c, gi + kWaves);
       VA = load_v<NT>(c, gi + kWaves);
-      granule<FMT>(c, qb, gi, KB, VB, st);
+      granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KB, VB, st);
       gi += kWaves;
       if (gi >= ngr) break;
     }
   }
 
-  // per-wave results: O rows 0..3 x channels (lanes jj == 0), sums per row
-  const float lrow = sum_jj(st.l);  // lane (n, jj): sum of Q row n % 4
-  if (jj == 0) {
+  // per-wave results: O rows x channels from the lanes holding distinct rows,
+  // max and sum of each row from the softmax layout
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+  for (int R = 0; R < NRB; ++R) {
+    const float lrow = sum_jj(st.l[R]);  // lane (n, jj): sum of row 16R + n % NQB
+    if (4 * jj < NQB) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o_s[wave][v][8 * n + q] = st.acc[q][v];
-  }
-  if (lane < 4) {
-    l_s[wave][lane] = lrow;
-    m_s[wave][lane] = lane == 0 ? st.m[0] : lane == 1 ? st.m[1] : lane == 2 ? st.m[2] : st.m[3];
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o_s[wave][NQB * R + 4 * jj + v][8 * n + q] = st.acc[R][q][v];
+    }
+    if (jj == 0 && n < NQB) {
+      l_s[wave][NQB * R + n] = lrow;
+      m_s[wave][NQB * R + n] = st.m[R];
+    }
   }
   __syncthreads();
 
-  // combine the 4 waves; thread -> (row r, channel ch), r in {tid>>7, (tid>>7)+2}
+  // combine the 4 waves; thread -> (row r, channel ch), r in {tid>>7, (tid>>7)+2, ...}
   const int ch = threadIdx.x & 127;
   const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k);
   for (int r = threadIdx.x >> 7; r < p.n_q; r += 2) {
@@ -463,22 +526,30 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
+template <int FMT, int NQB, int NRB>
+hipError_t launch_shape(const DecodeParams& p, bool nt, hipStream_t s) {
+  const dim3 grid(p.num_work, p.h_k);
+  if (nt)
+    hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, true>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, false>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const DecodeParams& p, bool nt, hipStream_t s) {
+  if (p.n_q <= 4) return launch_shape<FMT, 4, 1>(p, nt, s);
+  if (p.n_q <= 8) return launch_shape<FMT, 8, 1>(p, nt, s);
+  if (p.n_q <= 16) return launch_shape<FMT, 16, 1>(p, nt, s);
+  return launch_shape<FMT, 16, 2>(p, nt, s);
+}
+
 }  // namespace
 
+bool decode_mfma_supports(int n_q) { return n_q >= 1 && n_q <= 32; }
+
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, hipStream_t s) {
-  const dim3 grid(p.num_work, p.h_k);
-  if (kv_format == 0) {
-    if (nontemporal)
-      hipLaunchKernelGGL((decode_mfma_kernel<0, true>), grid, dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<0, false>), grid, dim3(kThreads), 0, s, p);
-  } else {
-    if (nontemporal)
-      hipLaunchKernelGGL((decode_mfma_kernel<1, true>), grid, dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<1, false>), grid, dim3(kThreads), 0, s, p);
-  }
-  return hipGetLastError();
+  return kv_format == 0 ? launch_fmt<0>(p, nontemporal, s) : launch_fmt<1>(p, nontemporal, s);
 }
 
 }  // namespace mj

@@ -41,6 +41,7 @@ namespace mj {
 
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, hipStream_t s);
+bool decode_mfma_supports(int n_q);
 
 namespace {
 
@@ -409,9 +410,10 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hi
   // the streaming kernels address a page's rows with 32-bit lane offsets and
   // take whole 16-token tiles inside one page
   const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24);
-  const bool stream_ok = p.n_q <= 4 && row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
-  if (g_variant == 1 || !stream_ok) return launch_decode_generic(p, kv_format, row_tiles, s);
-  if (kv_format != 0 || g_variant != 2) return launch_decode_mfma(p, kv_format, g_nontemporal != 0, s);
+  const bool tiles_ok = row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
+  if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q))
+    return launch_decode_generic(p, kv_format, row_tiles, s);
+  if (kv_format != 0 || g_variant != 2 || p.n_q > 4) return launch_decode_mfma(p, kv_format, g_nontemporal != 0, s);
   const dim3 grid(p.num_work, p.h_k);
   if (g_nontemporal)
     hipLaunchKernelGGL((decode_stream_kernel<0, true>), grid, dim3(kThreads), 0, s, p);

@@ -172,9 +172,10 @@ def test_edge_lengths(mj, gpu, variant):
     O, LSE = oracle_step(wl)
     compare_out(out, O, "edges q_len=1")
     compare_lse(lse, LSE, "edges q_len=1")
-    # speculative blocks small enough for the streaming kernels (q_len*h_r <= 4)
+    # speculative blocks: q_len*h_r of 4 (replicated rows), 8, 16, 15 and 32
     lens = (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, 1000)
-    for q_len, h_q, h_k, causal in ((2, 16, 8, True), (4, 8, 8, True), (4, 8, 8, False), (2, 4, 2, False)):
+    for q_len, h_q, h_k, causal in ((2, 16, 8, True), (4, 8, 8, True), (4, 8, 8, False), (2, 4, 2, False),
+                                    (2, 32, 8, True), (4, 32, 8, True), (3, 40, 8, True), (4, 64, 8, False)):
         wl = synth.build(synth.spec_for("cfg2", small=True, b=len(lens), lens=lens, q_len=q_len, h_q=h_q, h_k=h_k,
                                         causal=causal, k_outliers=0), gpu)
         say(f"  edges q_len={q_len} h_q={h_q} h_k={h_k} causal={causal}")
