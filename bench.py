@@ -8,7 +8,9 @@ Infinity Cache is flushed (a 1 GiB write) before every step, outside that
 step's event pair, so KV bytes come from HBM.
 
 Prints one JSON line.  ``value`` is the achieved KV-read bandwidth of the
-step (KV bytes / step time); the decode kernel's own bandwidth against the
+step (KV bytes / step time) with the step replayed as one hipGraph (device
+planner + quantize + decode + merge); the eager step with the host planner
+is reported in ``detail``.  The decode kernel's own bandwidth against the
 8 TB/s HBM peak is the ``roofline`` object.  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
 
@@ -54,10 +56,12 @@ def parse():
     ap.add_argument("--variant", type=int, default=0,
                     help="decode kernel: 0 automatic, 1 generic, 2 VALU-PV streaming (A/B runs)")
     ap.add_argument("--no-nt", action="store_true", help="plain (not non-temporal) KV loads (A/B runs)")
+    ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner workgroups per CU (0 = library default)")
+    ap.add_argument("--stream-read", action="store_true", help="also time a plain streaming read of the KV pool")
     return ap.parse_args()
 
 
-def measure(key, steps, warmup, flush_buf):
+def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     import torch
     import synth
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
@@ -66,7 +70,7 @@ def measure(key, steps, warmup, flush_buf):
     wl = synth.build(synth.spec_for(key), "cuda")
     torch.cuda.synchronize()
     log(f"[bench] {key}: built {wl.spec.name} in {time.time() - t0:.1f}s, kv_bytes={wl.kv_bytes()}")
-    step = DecodeStep.for_workload(wl)
+    step = DecodeStep.for_workload(wl, wgs_per_cu=wgs_per_cu)
     out, lse = new_output(wl)
     stream = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -94,6 +98,33 @@ def measure(key, steps, warmup, flush_buf):
     torch.cuda.synchronize()
     t_wall = time.time() - t_wall
     info = step.info
+
+    # the same step as one hipGraph: device-side plan + quantize + decode + merge
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step.plan_workload_device(wl, stream=side)
+        step.run_workload(wl, out, lse, stream=side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gs = torch.cuda.current_stream()
+        ginfo = step.plan_workload_device(wl, stream=gs)
+        step.run_workload(wl, out, lse, info=ginfo, stream=gs)
+    torch.cuda.synchronize()
+    gev = [(E(), E()) for _ in range(steps)]
+    for _ in range(warmup):
+        flush_buf.add_(1)
+        graph.replay()
+    for k in range(steps):
+        flush_buf.add_(1)
+        gev[k][0].record(stream)
+        graph.replay()
+        gev[k][1].record(stream)
+    torch.cuda.synchronize()
+    graph_ms = np.array([a.elapsed_time(b) for a, b in gev])
+    del graph
     step_ms = np.array([e[0].elapsed_time(e[4]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
     plan_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
@@ -105,6 +136,9 @@ def measure(key, steps, warmup, flush_buf):
         us_per_step_p90=float(np.percentile(step_ms, 90) * 1e3),
         decode_us_mean=float(dec_ms.mean() * 1e3), decode_us_median=float(np.median(dec_ms) * 1e3),
         plan_us_median=float(np.median(plan_ms) * 1e3),
+        graph_us_per_step_median=float(np.median(graph_ms) * 1e3),
+        graph_us_per_step_mean=float(graph_ms.mean() * 1e3),
+        graph_step_kv_gbs=kvb / (graph_ms.mean() * 1e-3) / 1e9,
         step_kv_gbs=kvb / (step_ms.mean() * 1e-3) / 1e9,
         decode_kv_gbs=kvb / (dec_ms.mean() * 1e-3) / 1e9,
         plan=dict(num_work=info.num_work, slots=info.slots, chunk_tiles=info.chunk_tiles,
@@ -112,7 +146,25 @@ def measure(key, steps, warmup, flush_buf):
         timed_wall_s=t_wall,
     )
     res["decode_frac_of_hbm_peak"] = res["decode_kv_gbs"] / HBM_PEAK_GBS
-    log(f"[bench] {key}: step {res['us_per_step_median']:.1f} us (median), decode {res['decode_us_mean']:.1f} us, "
+    if stream_read:
+        # plain non-temporal streaming read of as many bytes as the KV the step reads
+        import paged_fp8_decode_amd as mjlib
+        nbytes = min(kvb, wl.k_pool.numel()) // 16 * 16
+        src = wl.k_pool.view(-1)[:nbytes]
+        chk = torch.empty(4096, dtype=torch.int32, device="cuda")
+        ms = []
+        for k in range(10):
+            flush_buf.add_(1)
+            e0, e1 = E(), E()
+            e0.record(stream)
+            mjlib.mj_debug_stream_read(src, chk, 2048, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        res["stream_read_gbs"] = nbytes / (np.median(ms[2:]) * 1e-3) / 1e9
+        log(f"[bench] {key}: plain streaming read of {nbytes} B: {res['stream_read_gbs']:.0f} GB/s")
+    log(f"[bench] {key}: step {res['us_per_step_median']:.1f} us eager / {res['graph_us_per_step_median']:.1f} us graph "
+        f"(median), decode {res['decode_us_mean']:.1f} us, "
         f"decode KV {res['decode_kv_gbs']:.0f} GB/s ({100 * res['decode_frac_of_hbm_peak']:.1f}% of 8 TB/s)")
     del wl
     torch.cuda.empty_cache()
@@ -176,10 +228,11 @@ def main():
     paged_fp8_decode_amd.mj_debug_set_decode_variant(args.variant, 0 if args.no_nt else 1)
 
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-    main_res = measure(args.workload, args.steps, args.warmup, flush_buf)
+    main_res = measure(args.workload, args.steps, args.warmup, flush_buf, args.wgs_per_cu, args.stream_read)
     extra = {}
     for k in [x for x in args.extra.split(",") if x]:
-        extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf)
+        extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu,
+                           args.stream_read)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     kvb = main_res["kv_bytes"]
     dec_s = main_res["decode_us_mean"] * 1e-6
@@ -188,13 +241,13 @@ def main():
                 kernel="mj_paged_decode", algorithmic_bytes_per_launch=kvb)
     line = dict(
         metric="paged decode us/step and achieved KV-read HBM GB/s (% of MI355X peak)",
-        value=round(main_res["step_kv_gbs"], 1),
+        value=round(main_res["graph_step_kv_gbs"], 1),
         unit="GB/s",
         n_gpus=1,
         steps=args.steps,
         warmup=args.warmup,
-        ms_per_step=round(main_res["us_per_step_mean"] / 1e3, 5),
-        us_per_step_median=round(main_res["us_per_step_median"], 2),
+        ms_per_step=round(main_res["graph_us_per_step_mean"] / 1e3, 5),
+        us_per_step_median=round(main_res["graph_us_per_step_median"], 2),
         higher_is_better=True,
         scaling="weak",
         vs_baseline=None,

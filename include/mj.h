@@ -200,6 +200,19 @@ mj_status mj_plan_split_kv(const mj_config* cfg, const int32_t* seq_lens_host, i
                            int32_t margin, int32_t max_blocks_per_seq, int32_t* host_staging, int32_t* plan_dev,
                            mj_plan_info* info, hipStream_t stream);
 
+/* The same plan computed on the device from device lengths (one workgroup):
+ * seq_lens_dev[i] is clamped to [0, max_blocks_per_seq * page_size] as the
+ * decode kernels clamp it, then the rule above applies unchanged, so the plan
+ * buffer is bit-identical to mj_plan_split_kv's for valid lengths.  It reads
+ * only device memory, so it may be captured in a hipGraph together with the
+ * other three calls; replays then re-plan from whatever lengths the device
+ * buffer holds.  `info` gets everything the host can know from num_seqs and
+ * q_len (num_work, slots, with_reduction; chunk_tiles = num_chunks = -1).
+ * plan_dev must be 16-byte aligned.  Errors: EINVAL, ECAPACITY, EALIGN, EHIP. */
+mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_dev, int32_t num_seqs, int32_t q_len,
+                                  int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev, mj_plan_info* info,
+                                  hipStream_t stream);
+
 /* Dynamic e4m3 quantization of Q per (sequence, KV head) (README "What it
  * does", step 2; runner.py T5DecodeRunner.run, fp8-Q branch): over the q_len
  * tokens and h_r heads of KV head g, x = fp32(q) [* q_mul], amax =
@@ -256,6 +269,11 @@ mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t
  * non-temporal.  Not thread-safe; set it before launching.  EINVAL on other
  * values. */
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal);
+/* Plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
+ * non-temporal 16-byte loads by `blocks` workgroups of 256 threads, each
+ * writing one xor checksum to out[block]: the practical HBM read ceiling the
+ * decode kernels are compared with.  EINVAL on bad arguments. */
+mj_status mj_debug_stream_read(const void* src, int64_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

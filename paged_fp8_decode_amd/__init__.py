@@ -86,6 +86,16 @@ def mj_plan_split_kv(cfg: Config, seq_lens, q_len: int, margin: int, max_blocks_
     return info
 
 
+def mj_plan_split_kv_device(cfg: Config, seq_lens_dev, num_seqs: int, q_len: int, margin: int,
+                            max_blocks_per_seq: int, plan_dev, stream=None) -> PlanInfo:
+    """Plan on the device from ``seq_lens_dev`` (torch int32 on the GPU) into ``plan_dev``."""
+    info = PlanInfo()
+    st = lib().mj_plan_split_kv_device(ctypes.byref(cfg), _ptr(seq_lens_dev), num_seqs, q_len, margin,
+                                       max_blocks_per_seq, _ptr(plan_dev), ctypes.byref(info), _stream(stream))
+    check(st, "mj_plan_split_kv_device")
+    return info
+
+
 def mj_quantize_q(cfg: Config, q, q_mul, num_seqs: int, q_len: int, q8, q_descale, stream=None):
     """q: bf16 torch view (tokens, h_q, 128) with unit channel stride."""
     assert q.stride(2) == 1
@@ -117,6 +127,12 @@ def mj_debug_decode_codes(kv_format, codes, out, stream=None):
 
 def mj_debug_set_decode_variant(variant: int, nontemporal: int = 1):
     check(lib().mj_debug_set_decode_variant(variant, nontemporal), "mj_debug_set_decode_variant")
+
+
+def mj_debug_stream_read(src, out, blocks: int, stream=None):
+    """src: any contiguous device tensor; out: uint32/int32 device tensor with >= blocks elements."""
+    nbytes = src.numel() * src.element_size()
+    check(lib().mj_debug_stream_read(_ptr(src), nbytes, _ptr(out), blocks, _stream(stream)), "mj_debug_stream_read")
 
 
 from .runner import DecodeStep  # noqa: E402,F401

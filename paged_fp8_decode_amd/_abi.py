@@ -73,12 +73,14 @@ def _load():
         "mj_plan_capacity": (_i32, [P(Config), _i32]),
         "mj_plan_compute": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo)]),
         "mj_plan_split_kv": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, _p, P(PlanInfo), _p]),
+        "mj_plan_split_kv_device": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo), _p]),
         "mj_quantize_q": (_i32, [P(Config), _p, _i64, _i64, _p, _i32, _i32, _p, _p, _p]),
         "mj_paged_decode": (_i32, [P(Config), P(DecodeArgs), _p]),
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
         "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),
+        "mj_debug_stream_read": (_i32, [_p, _i64, _p, _i32, _p]),
     }
     for name, (res, args) in sigs.items():
         if not hasattr(lib, name):

@@ -260,3 +260,33 @@ hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float
 }
 
 }  // namespace mj
+
+namespace mj {
+namespace {
+
+// Probe: read `n16` 16-byte words with non-temporal loads and fold them into
+// one xor checksum per workgroup (a plain HBM streaming read, the practical
+// bandwidth ceiling the decode kernels are compared with).
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* src, int64_t n16, uint32_t* out) {
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(src) + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(src), bytes / 16, out);
+  return hipGetLastError();
+}
+
+}  // namespace mj

@@ -379,16 +379,20 @@ __device__ __forceinline__ void granule(const Ctx& c, const v8i (&qb)[NRB], cons
   }
 }
 
-template <int FMT, int NQB, int NRB, bool NT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NRB == 1 ? 2 : 1, 2)))
+// PF: granules of loads in flight ahead of the one being computed (1 or 2);
+// OCC: waves per SIMD the register budget is fitted to.
+template <int FMT, int NQB, int NRB, bool NT, int PF, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_mfma_kernel(DecodeParams p) {
   using F = Fmt<FMT>;
   constexpr int kRows = NQB * NRB;  // rows of the GQA group this instance serves (padded)
   __shared__ float o_s[kWaves][kRows][kHeadDim];
   __shared__ float m_s[kWaves][kRows], l_s[kWaves][kRows];
 
-  const int w = blockIdx.x;
-  const int g = blockIdx.y;
+  // head-major grids put the KV heads of one work item in consecutive
+  // workgroups, so they are resident together
+  const int w = p.head_major ? blockIdx.y : blockIdx.x;
+  const int g = p.head_major ? blockIdx.x : blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, jj = lane >> 4;
@@ -458,19 +462,42 @@ void decode_mfma_kernel(DecodeParams p) {
   const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
   int gi = wave;
   if (gi < ngr) {
-    KRows<FMT> KA = load_k<FMT, NT>(c, gi);
-    VRows VA = load_v<NT>(c, gi);
-    while (true) {
-      KRows<FMT> KB = load_k<FMT, NT>(c, gi + kWaves);
-      VRows VB = load_v<NT>(c, gi + kWaves);
-      granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KA, VA, st);
-      gi += kWaves;
-      if (gi >= ngr) break;
-      KA = load_k<FMT, NT>(c, gi + kWaves);
-      VA = load_v<NT>(c, gi + kWaves);
-      granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KB, VB, st);
-      gi += kWaves;
-      if (gi >= ngr) break;
+    // register ring of PF + 1 granules, rotated by unrolling
+    if constexpr (PF == 1) {
+      KRows<FMT> KA = load_k<FMT, NT>(c, gi);
+      VRows VA = load_v<NT>(c, gi);
+      while (true) {
+        KRows<FMT> KB = load_k<FMT, NT>(c, gi + kWaves);
+        VRows VB = load_v<NT>(c, gi + kWaves);
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KA, VA, st);
+        gi += kWaves;
+        if (gi >= ngr) break;
+        KA = load_k<FMT, NT>(c, gi + kWaves);
+        VA = load_v<NT>(c, gi + kWaves);
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KB, VB, st);
+        gi += kWaves;
+        if (gi >= ngr) break;
+      }
+    } else {
+      KRows<FMT> K0 = load_k<FMT, NT>(c, gi), K1 = load_k<FMT, NT>(c, gi + kWaves);
+      VRows V0 = load_v<NT>(c, gi), V1 = load_v<NT>(c, gi + kWaves);
+      while (true) {
+        KRows<FMT> K2 = load_k<FMT, NT>(c, gi + 2 * kWaves);
+        VRows V2 = load_v<NT>(c, gi + 2 * kWaves);
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K0, V0, st);
+        gi += kWaves;
+        if (gi >= ngr) break;
+        K0 = load_k<FMT, NT>(c, gi + 2 * kWaves);
+        V0 = load_v<NT>(c, gi + 2 * kWaves);
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K1, V1, st);
+        gi += kWaves;
+        if (gi >= ngr) break;
+        K1 = load_k<FMT, NT>(c, gi + 2 * kWaves);
+        V1 = load_v<NT>(c, gi + 2 * kWaves);
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K2, V2, st);
+        gi += kWaves;
+        if (gi >= ngr) break;
+      }
     }
   }
 
@@ -526,30 +553,42 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <int FMT, int NQB, int NRB>
+template <int FMT, int NQB, int NRB, int PF, int OCC>
 hipError_t launch_shape(const DecodeParams& p, bool nt, hipStream_t s) {
-  const dim3 grid(p.num_work, p.h_k);
+  const dim3 grid = p.head_major ? dim3(p.h_k, p.num_work) : dim3(p.num_work, p.h_k);
   if (nt)
-    hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, true, PF, OCC>), grid, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, false, PF, OCC>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_fmt(const DecodeParams& p, bool nt, hipStream_t s) {
-  if (p.n_q <= 4) return launch_shape<FMT, 4, 1>(p, nt, s);
-  if (p.n_q <= 8) return launch_shape<FMT, 8, 1>(p, nt, s);
-  if (p.n_q <= 16) return launch_shape<FMT, 16, 1>(p, nt, s);
-  return launch_shape<FMT, 16, 2>(p, nt, s);
+hipError_t launch_fmt(const DecodeParams& p, bool nt, int tune, hipStream_t s) {
+  if (p.n_q <= 4) {
+    switch (tune) {  // prefetch depth x occupancy of the 4-row kernel
+      case 1: return launch_shape<FMT, 4, 1, 1, 3>(p, nt, s);
+      case 2: return launch_shape<FMT, 4, 1, 2, 2>(p, nt, s);
+      case 3: return launch_shape<FMT, 4, 1, 2, 3>(p, nt, s);
+      default: return launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
+    }
+  }
+  if (p.n_q <= 8) return launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
+  if (p.n_q <= 16) return launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
+  return launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
 }
 
 }  // namespace
 
 bool decode_mfma_supports(int n_q) { return n_q >= 1 && n_q <= 32; }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, hipStream_t s) {
-  return kv_format == 0 ? launch_fmt<0>(p, nontemporal, s) : launch_fmt<1>(p, nontemporal, s);
+// tune: 0 = defaults; 1..3 select prefetch depth / occupancy of the 4-row kernel
+hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, bool nontemporal, int tune, hipStream_t s) {
+  DecodeParams p = p_in;
+  p.head_major = (tune & 4) ? 1 : 0;
+  tune &= 3;
+  if (kv_format != 0 && (tune & 1)) tune &= ~1;  // the e2m3 kernel does not fit 3 waves per SIMD
+  return kv_format == 0 ? launch_fmt<0>(p, nontemporal, tune, s) : launch_fmt<1>(p, nontemporal, tune, s);
 }
 
 }  // namespace mj

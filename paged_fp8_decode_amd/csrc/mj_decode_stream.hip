@@ -40,7 +40,7 @@
 namespace mj {
 
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, int tune, hipStream_t s);
 bool decode_mfma_supports(int n_q);
 
 namespace {
@@ -397,7 +397,9 @@ void decode_stream_kernel(DecodeParams p) {
 }  // namespace
 
 // Kernel choice: 0 = automatic, 1 = always the generic kernel, 2 = the
-// VALU-PV streaming kernel wherever it applies, 3 = same as 0.
+// VALU-PV streaming kernel wherever it applies, 3 = same as 0, 10..17 = the
+// matrix-core kernel with tuning setting (variant - 10): bit 0 three waves per
+// SIMD, bit 1 two granules of prefetch (4-row groups), bit 2 head-major grid.
 static int g_variant = 0;
 static int g_nontemporal = 1;
 
@@ -413,7 +415,9 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hi
   const bool tiles_ok = row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
   if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q))
     return launch_decode_generic(p, kv_format, row_tiles, s);
-  if (kv_format != 0 || g_variant != 2 || p.n_q > 4) return launch_decode_mfma(p, kv_format, g_nontemporal != 0, s);
+  const int tune = g_variant >= 10 ? g_variant - 10 : 0;
+  if (kv_format != 0 || g_variant != 2 || p.n_q > 4)
+    return launch_decode_mfma(p, kv_format, g_nontemporal != 0, tune, s);
   const dim3 grid(p.num_work, p.h_k);
   if (g_nontemporal)
     hipLaunchKernelGGL((decode_stream_kernel<0, true>), grid, dim3(kThreads), 0, s, p);

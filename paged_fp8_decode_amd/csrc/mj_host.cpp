@@ -224,6 +224,45 @@ mj_status mj_plan_split_kv(const mj_config* cfg, const int32_t* seq_lens_host, i
   return MJ_OK;
 }
 
+mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_dev, int32_t num_seqs, int32_t q_len,
+                                  int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev, mj_plan_info* info,
+                                  hipStream_t stream) {
+  Derived d;
+  mj_status st = derive(cfg, &d);
+  if (st != MJ_OK) return st;
+  if (!seq_lens_dev || !plan_dev || !info || num_seqs < 1 || q_len < 1 || margin < 0 || max_blocks_per_seq < 1)
+    return MJ_EINVAL;
+  if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  if (!aligned(plan_dev, 16) || !aligned(seq_lens_dev, 4)) return MJ_EALIGN;
+  const int S = slots_for(cfg, d, q_len);
+  const bool split = cfg->max_splits > 1 && num_seqs < S;
+  mj::PlanParams p;
+  p.seq_lens = seq_lens_dev;
+  p.work = plan_dev;
+  p.n_splits = plan_dev + 4 * (size_t)d.cap_max;
+  p.split_begin = p.n_splits + cfg->max_num_seqs;
+  p.num_seqs = num_seqs;
+  p.max_num_seqs = cfg->max_num_seqs;
+  p.margin = margin;
+  p.kv_tile = d.kv_tile;
+  p.page_size = cfg->page_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_splits = cfg->max_splits;
+  p.slots = S;
+  p.split = split ? 1 : 0;
+  p.cap_max = d.cap_max;
+  if (mj::launch_plan(p, stream) != hipSuccess) return MJ_EHIP;
+  info->num_work = cap_for(cfg, d, q_len);
+  info->slots = S;
+  info->chunk_tiles = -1;  // decided on the device
+  info->num_chunks = -1;
+  info->with_reduction = split ? 1 : 0;
+  info->num_seqs = num_seqs;
+  info->q_len = q_len;
+  info->kv_tile_tokens = d.kv_tile;
+  return MJ_OK;
+}
+
 mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                         const float* q_mul, int32_t num_seqs, int32_t q_len, uint8_t* q8, float* q_descale,
                         hipStream_t stream) {
@@ -320,6 +359,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->kv_tile = d.kv_tile;
   p->causal = a->causal ? 1 : 0;
   p->num_work = a->num_work;
+  p->head_major = 0;
   return MJ_OK;
 }
 
@@ -393,9 +433,14 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
 }
 
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal) {
-  if (variant < 0 || variant > 3 || (nontemporal != 0 && nontemporal != 1)) return MJ_EINVAL;
+  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 17)) || (nontemporal != 0 && nontemporal != 1)) return MJ_EINVAL;
   mj::set_decode_variant(variant, nontemporal);
   return MJ_OK;
+}
+
+mj_status mj_debug_stream_read(const void* src, int64_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream) {
+  if (!src || !out || bytes < 16 || bytes % 16 || blocks < 1 || !aligned(src, 16)) return MJ_EINVAL;
+  return mj::launch_stream_read(src, bytes, out, blocks, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream) {

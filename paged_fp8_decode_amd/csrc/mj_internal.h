@@ -49,6 +49,7 @@ struct DecodeParams {
   int page_size, page_shift, kv_tile;
   int causal;
   int num_work;
+  int head_major;              // grid is (h_k, num_work) instead of (num_work, h_k)
 };
 
 struct MergeParams {
@@ -75,12 +76,22 @@ struct GatherParams {
   uint8_t* out;
 };
 
+struct PlanParams {
+  const int32_t* seq_lens;  // device
+  int32_t* work;            // plan buffer: [cap_max][4]
+  int32_t* n_splits;        // [max_num_seqs]
+  int32_t* split_begin;     // [max_num_seqs]
+  int num_seqs, max_num_seqs, margin, kv_tile, page_size, max_blocks, max_splits, slots, split, cap_max;
+};
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t s);
 hipError_t launch_qquant(const QQuantParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 void set_decode_variant(int variant, int nontemporal);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s);
 hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);
 
 }  // namespace mj

@@ -11,8 +11,8 @@ from __future__ import annotations
 import torch
 
 from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, check, mj_config, mj_config_check, mj_merge_lse,
-               mj_paged_decode, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_quantize_q,
-               mj_workspace_bytes)
+               mj_paged_decode, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
+               mj_quantize_q, mj_workspace_bytes)
 
 
 class DecodeStep:
@@ -54,6 +54,15 @@ class DecodeStep:
         ev.record(stream)
         self._staging_done[slot] = ev
         self._slot ^= 1
+        self.info = info
+        return info
+
+    def plan_device(self, seq_lens_dev, num_seqs: int, q_len: int, max_blocks_per_seq: int, margin: int = 0,
+                    stream=None) -> PlanInfo:
+        """Plan on the device from device lengths (capture-safe)."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        info = mj_plan_split_kv_device(self.cfg, seq_lens_dev, num_seqs, q_len, margin, max_blocks_per_seq,
+                                       self.plan_dev, stream)
         self.info = info
         return info
 
@@ -111,6 +120,9 @@ class DecodeStep:
 
     def plan_workload(self, wl, margin=0, stream=None) -> PlanInfo:
         return self.plan(wl.seq_lens, wl.spec.q_len, wl.block_table.shape[1], margin, stream)
+
+    def plan_workload_device(self, wl, margin=0, stream=None) -> PlanInfo:
+        return self.plan_device(wl.seq_lens_dev, wl.spec.b, wl.spec.q_len, wl.block_table.shape[1], margin, stream)
 
     def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None):
         ks, vs = wl.kv_strides()

@@ -247,3 +247,69 @@ def test_parity_full_size_sampled(mj, gpu, key, variant):
     O, LSE = oracle_step(wl, seqs=seqs, heads=heads)
     compare_out(out, O, f"{s.name} seqs={seqs} heads={heads}")
     compare_lse(lse, LSE, s.name)
+
+
+def test_device_plan_bit_exact(mj, gpu):
+    """The device planner writes the same plan image as the host planner."""
+    rng = np.random.default_rng(21)
+    cases = 0
+    for trial in range(40):
+        h_k = int(rng.choice([1, 2, 4, 8]))
+        h_q = h_k * int(rng.choice([1, 4, 8]))
+        mns = int(rng.choice([1, 8, 64, 300, 1500]))
+        cfg = mj.mj_config(h_q=h_q, h_k=h_k, page_size=int(rng.choice([16, 32, 64, 128])), max_num_seqs=mns,
+                           max_q_len=int(rng.integers(1, 5)), max_splits=int(rng.choice([1, 4, 16, 64])),
+                           num_cus=256, wgs_per_cu=int(rng.integers(1, 9)),
+                           kv_tile_tokens=int(rng.choice([16, 64, 128, 256])),
+                           slots_override=int(rng.choice([0, 0, 24, 700])))
+        b = int(rng.integers(1, mns + 1))
+        q_len = int(rng.integers(1, cfg.max_q_len + 1))
+        lens = rng.integers(0, int(rng.choice([50, 5000, 140000])), size=b).astype(np.int32)
+        if trial % 7 == 0:
+            lens[:] = 0
+        margin = int(rng.integers(0, 6))
+        max_blocks = int(-(-int(lens.max()) // cfg.page_size)) + 1
+        img, hinfo = mj.mj_plan_compute(cfg, lens, q_len, margin, max_blocks)
+        plan = torch.full((img.size,), -7, dtype=torch.int32, device=gpu)
+        dinfo = mj.mj_plan_split_kv_device(cfg, torch.from_numpy(lens).to(gpu), b, q_len, margin, max_blocks, plan)
+        torch.cuda.synchronize()
+        assert np.array_equal(plan.cpu().numpy(), img), f"trial {trial}: b={b} split={hinfo.with_reduction}"
+        assert (dinfo.num_work, dinfo.with_reduction, dinfo.slots) == (hinfo.num_work, hinfo.with_reduction,
+                                                                       hinfo.slots)
+        cases += hinfo.with_reduction
+    assert cases > 5
+
+
+def test_graph_replay_with_device_plan(mj, gpu):
+    """One graph holds plan + quantize + decode + merge; replays follow new
+    device lengths with no host planning."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for("cfg2", small=True), gpu)
+    say(f"graph+device plan {wl.spec.name}")
+    step = DecodeStep.for_workload(wl)
+    out, lse = new_output(wl)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        info = step.plan_workload_device(wl)
+        step.run_workload(wl, out, lse, info=info)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        info = step.plan_workload_device(wl)
+        step.run_workload(wl, out, lse, info=info)
+    torch.cuda.synchronize()
+    orig = list(wl.seq_lens)
+    rng = np.random.default_rng(8)
+    for trial in range(4):
+        lens = [int(x) for x in rng.integers(0, np.array(orig) + 1)]
+        wl.seq_lens = lens
+        wl.seq_lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        O, LSE = oracle_step(wl)
+        compare_out(out, O, f"device-plan replay {trial} lens={lens}")
+        compare_lse(lse, LSE, f"device-plan replay {trial}")
