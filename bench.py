@@ -1,18 +1,22 @@
 """Benchmark of one paged-decode step on one MI355X.
 
-A step is the whole hot path on one batch: the split-KV plan (host, copied
-into the fixed plan buffer), dynamic e4m3 Q quantization, the paged decode
-and the LSE merge (when the plan splits), enqueued back to back on one
-stream.  Inputs are seeded synthetic tensors already resident in HBM.  The
-Infinity Cache is flushed (a 1 GiB write) before every step, outside that
-step's event pair, so KV bytes come from HBM.
+A step is the whole hot path on one batch: the split-KV plan, dynamic e4m3
+Q quantization, the paged decode and the LSE merge of split partials.  The
+timed step is a hipGraph of two kernels, the device planner and
+``mj_decode_step`` (quantization, decode and merge fused into one launch).
+Inputs are seeded synthetic tensors already resident in HBM.  The Infinity
+Cache is flushed (a 1 GiB write) before every step, outside that step's
+event pair, so KV bytes come from HBM.
 
 Prints one JSON line.  ``value`` is the achieved KV-read bandwidth of the
-step (KV bytes / step time) with the step replayed as one hipGraph (device
-planner + quantize + decode + merge); the eager step with the host planner
-is reported in ``detail``.  The decode kernel's own bandwidth against the
-8 TB/s HBM peak is the ``roofline`` object.  ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload.
+step (KV bytes / mean graph step time); ``detail`` also has the eager step
+(host planner + fused step) and the eager three-call step (quantize, decode,
+merge as separate launches).  The ``roofline`` object is the fused decode
+kernel's own bandwidth against the 8 TB/s HBM peak, its duration taken with
+one event pair around back-to-back launches that rotate over copies of the
+KV pools (no launch reads KV the Infinity Cache still holds).
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--extra 32k,cfg3,...]
 """
@@ -74,44 +78,48 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     out, lse = new_output(wl)
     stream = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [(E(), E(), E(), E(), E()) for _ in range(steps)]
 
-    def one(e=None):
-        if e:
-            e[0].record(stream)
-        info = step.plan_workload(wl, stream=stream)
-        if e:
-            e[1].record(stream)
-        step.run_workload(wl, out, lse, info=info, stream=stream, events=(e[2], e[3]) if e else None)
-        if e:
-            e[4].record(stream)
-        return info
+    def eager(n, fused, with_events):
+        ev = [(E(), E(), E(), E()) for _ in range(n)] if with_events else None
+        for k in range(n):
+            flush_buf.add_(1)  # 1 GiB read + write: evicts the 256 MB Infinity Cache
+            e = ev[k] if ev else None
+            if e:
+                e[0].record(stream)
+            info = step.plan_workload(wl, stream=stream)
+            step.run_workload(wl, out, lse, info=info, stream=stream, events=(e[1], e[2]) if e else None,
+                              fused=fused)
+            if e:
+                e[3].record(stream)
+        torch.cuda.synchronize()
+        return ev
 
-    for _ in range(warmup):
-        flush_buf.add_(1)
-        one()
-    torch.cuda.synchronize()
+    # eager steps: host plan (async copy) + the fused step (one kernel)
+    eager(warmup, True, False)
     t_wall = time.time()
-    for k in range(steps):
-        flush_buf.add_(1)  # 1 GiB read + write: evicts the 256 MB Infinity Cache
-        one(ev[k])
-    torch.cuda.synchronize()
+    ev = eager(steps, True, True)
     t_wall = time.time() - t_wall
     info = step.info
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    # the same step as the pages' three calls (quantize, decode, merge), for comparison
+    eager(max(3, warmup // 2), False, False)
+    ev3 = eager(max(5, steps // 2), False, True)
+    step3_ms = np.array([e[0].elapsed_time(e[3]) for e in ev3])
 
-    # the same step as one hipGraph: device-side plan + quantize + decode + merge
+    # the step as one hipGraph: device-side plan + fused step
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
         step.plan_workload_device(wl, stream=side)
-        step.run_workload(wl, out, lse, stream=side)
+        step.run_workload(wl, out, lse, stream=side, fused=True)
     stream.wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         gs = torch.cuda.current_stream()
         ginfo = step.plan_workload_device(wl, stream=gs)
-        step.run_workload(wl, out, lse, info=ginfo, stream=gs)
+        step.run_workload(wl, out, lse, info=ginfo, stream=gs, fused=True)
     torch.cuda.synchronize()
     gev = [(E(), E()) for _ in range(steps)]
     for _ in range(warmup):
@@ -125,27 +133,58 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     torch.cuda.synchronize()
     graph_ms = np.array([a.elapsed_time(b) for a, b in gev])
     del graph
-    step_ms = np.array([e[0].elapsed_time(e[4]) for e in ev])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    plan_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+
+    # kernel duration for the roofline: the fused decode kernel launched back
+    # to back, rotating over copies of the KV pools so that no launch finds
+    # the previous one's KV in the 256 MB Infinity Cache (>= 1 GiB of
+    # distinct KV between reuses); one event pair over all launches
     kvb = wl.kv_bytes()
+    n_copies = max(1, -(-(1 << 30) // kvb))
+    pools = [(wl.k_pool, wl.v_pool)] + [(wl.k_pool.clone(), wl.v_pool.clone()) for _ in range(n_copies - 1)]
+    reps = max(8, 2 * n_copies, steps)
+    ks, vs = wl.kv_strides()
+
+    def launch(i):
+        kp, vp = pools[i % len(pools)]
+        step.run(q=wl.q, k_cache=kp, v_cache=vp, k_strides=ks, v_strides=vs, num_pages=wl.num_pages,
+                 block_table=wl.block_table, seq_lens=wl.seq_lens_dev, k_descale=wl.k_descale,
+                 v_descale=wl.v_descale, descale_kind=wl.descale_kind, softmax_scale=wl.softmax_scale, out=out,
+                 lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul, causal=wl.spec.causal, info=info, stream=stream,
+                 fused=True)
+
+    step.plan_workload(wl, stream=stream)
+    for i in range(len(pools)):
+        launch(i)
+    torch.cuda.synchronize()
+    k0, k1 = E(), E()
+    k0.record(stream)
+    for i in range(reps):
+        launch(i)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    kernel_us = k0.elapsed_time(k1) * 1e3 / reps
+    del pools
+
     res = dict(
         workload=wl.spec.name, kv_bytes=kvb, steps=steps,
         us_per_step_median=float(np.median(step_ms) * 1e3), us_per_step_mean=float(step_ms.mean() * 1e3),
         us_per_step_p10=float(np.percentile(step_ms, 10) * 1e3),
         us_per_step_p90=float(np.percentile(step_ms, 90) * 1e3),
-        decode_us_mean=float(dec_ms.mean() * 1e3), decode_us_median=float(np.median(dec_ms) * 1e3),
-        plan_us_median=float(np.median(plan_ms) * 1e3),
+        step_decode_us_mean=float(dec_ms.mean() * 1e3), step_decode_us_median=float(np.median(dec_ms) * 1e3),
+        three_call_us_per_step_median=float(np.median(step3_ms) * 1e3),
         graph_us_per_step_median=float(np.median(graph_ms) * 1e3),
         graph_us_per_step_mean=float(graph_ms.mean() * 1e3),
+        graph_us_per_step_p10=float(np.percentile(graph_ms, 10) * 1e3),
+        graph_us_per_step_p90=float(np.percentile(graph_ms, 90) * 1e3),
         graph_step_kv_gbs=kvb / (graph_ms.mean() * 1e-3) / 1e9,
         step_kv_gbs=kvb / (step_ms.mean() * 1e-3) / 1e9,
-        decode_kv_gbs=kvb / (dec_ms.mean() * 1e-3) / 1e9,
+        kernel_us_back_to_back=kernel_us, kernel_launches=reps, kv_pool_copies=n_copies,
+        kernel_kv_gbs=kvb / (kernel_us * 1e-6) / 1e9,
         plan=dict(num_work=info.num_work, slots=info.slots, chunk_tiles=info.chunk_tiles,
-                  with_reduction=info.with_reduction),
+                  min_chunk_tiles=info.min_chunk_tiles, with_reduction=info.with_reduction),
         timed_wall_s=t_wall,
     )
-    res["decode_frac_of_hbm_peak"] = res["decode_kv_gbs"] / HBM_PEAK_GBS
+    res["kernel_frac_of_hbm_peak"] = res["kernel_kv_gbs"] / HBM_PEAK_GBS
     if stream_read:
         # plain non-temporal streaming read of as many bytes as the KV the step reads
         import paged_fp8_decode_amd as mjlib
@@ -163,9 +202,10 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
             ms.append(e0.elapsed_time(e1))
         res["stream_read_gbs"] = nbytes / (np.median(ms[2:]) * 1e-3) / 1e9
         log(f"[bench] {key}: plain streaming read of {nbytes} B: {res['stream_read_gbs']:.0f} GB/s")
-    log(f"[bench] {key}: step {res['us_per_step_median']:.1f} us eager / {res['graph_us_per_step_median']:.1f} us graph "
-        f"(median), decode {res['decode_us_mean']:.1f} us, "
-        f"decode KV {res['decode_kv_gbs']:.0f} GB/s ({100 * res['decode_frac_of_hbm_peak']:.1f}% of 8 TB/s)")
+    log(f"[bench] {key}: step {res['graph_us_per_step_median']:.1f} us graph / {res['us_per_step_median']:.1f} us "
+        f"eager / {res['three_call_us_per_step_median']:.1f} us three calls (median); decode kernel "
+        f"{kernel_us:.1f} us = {res['kernel_kv_gbs']:.0f} GB/s KV ({100 * res['kernel_frac_of_hbm_peak']:.1f}% "
+        f"of 8 TB/s); in-step decode {res['step_decode_us_mean']:.1f} us")
     del wl
     torch.cuda.empty_cache()
     return res
@@ -235,10 +275,11 @@ def main():
                            args.stream_read)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     kvb = main_res["kv_bytes"]
-    dec_s = main_res["decode_us_mean"] * 1e-6
+    dec_s = main_res["kernel_us_back_to_back"] * 1e-6
     roof = dict(bound="hbm", achieved=round(kvb / dec_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(kvb / dec_s / 1e9 / HBM_PEAK_GBS, 4), traffic=TRAFFIC.get(args.workload),
-                kernel="mj_paged_decode", algorithmic_bytes_per_launch=kvb)
+                kernel="decode_mfma_kernel (mj_decode_step: Q quantization + paged decode + LSE merge)",
+                algorithmic_bytes_per_launch=kvb, kernel_us=round(main_res["kernel_us_back_to_back"], 2))
     line = dict(
         metric="paged decode us/step and achieved KV-read HBM GB/s (% of MI355X peak)",
         value=round(main_res["graph_step_kv_gbs"], 1),
@@ -254,7 +295,7 @@ def main():
         dtype="e4m3" if "e2m3" not in main_res["workload"] else "e2m3",
         data="synthetic",
         config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"], kernel_variant=args.variant,
-                    nontemporal=not args.no_nt),
+                    nontemporal=not args.no_nt, step="hipGraph: device plan + mj_decode_step"),
         roofline=roof,
         cpu_baseline=cpu,
         detail=main_res,

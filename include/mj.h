@@ -11,6 +11,10 @@
  *   mj_merge_lse       device: log-sum-exp merge of the split partials
  *                      (call it iff the plan says with_reduction)
  *
+ * or, after the plan, as one call: mj_decode_step (quantize + decode + merge
+ * fused into one kernel launch where the matrix-core kernel serves the
+ * shape; the same three launches otherwise, with identical results).
+ *
  * The method is the one the mjolnir-kernel 0.1.0 pages describe (PyPI project
  * page and sdist README, section "What it does", steps 1-4; wheel listing
  * mjolnir/runner.py, T5DecodeRunner.plan / .run / ._launch).  Their Thor
@@ -24,8 +28,8 @@
  *  - Errors: every call returns an mj_status; invalid arguments are rejected
  *    on the host before anything is enqueued (no partial launches).  Nothing
  *    aborts or throws across the ABI.
- *  - Graph capture: mj_quantize_q, mj_paged_decode and mj_merge_lse are
- *    capture-safe (their grids depend only on the config, q_len and
+ *  - Graph capture: mj_quantize_q, mj_paged_decode, mj_merge_lse,
+ *    mj_decode_step and mj_plan_split_kv_device are capture-safe (their grids depend only on the config, q_len and
  *    num_seqs; every per-step value is read from device memory).
  *    mj_plan_split_kv must run outside capture; a captured graph replays any
  *    later plan written to the same plan buffer.
@@ -44,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 1
+#define MJ_ABI_VERSION 2
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -83,11 +87,17 @@ typedef struct mj_config {
   int32_t max_q_len;       /* largest q_len (1 + speculative tokens), >= 1      */
   int32_t max_splits;      /* most KV chunks per sequence; 1 = never split      */
   int32_t num_cus;         /* compute units to plan for; 0 = ask the device     */
-  int32_t wgs_per_cu;      /* decode workgroups per CU in one wave; 0 = 2       */
+  int32_t wgs_per_cu;      /* planned workgroups per CU; 0 = default (below)    */
   int32_t kv_tile_tokens;  /* plan granularity in tokens (multiple of 16); 0=128*/
-  int32_t slots_override;  /* work items per wave; 0 = num_cus*wgs_per_cu/h_k   */
+  int32_t slots_override;  /* work items per plan; 0 = num_cus*wgs_per_cu/h_k   */
   int32_t kv_format;       /* mj_kv_format                                      */
+  int32_t min_chunk_tokens;/* floor of a split chunk; 0 = default (below)       */
 } mj_config;
+/* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):
+ * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
+ * workgroups per CU; four waves of items of >= 2048 tokens balance the tail
+ * across CUs and XCDs); 16 < n_q <= 32, or e2m3 -> 1 / 1 (one wave);
+ * n_q > 32 -> 2 / 1.  min_chunk_tokens is rounded up to whole KV tiles. */
 
 /* What a plan decided (runner.py, StepPlan). */
 typedef struct mj_plan_info {
@@ -99,6 +109,7 @@ typedef struct mj_plan_info {
   int32_t num_seqs;
   int32_t q_len;
   int32_t kv_tile_tokens;
+  int32_t min_chunk_tiles;  /* floor of the chunk for this q_len                */
 } mj_plan_info;
 
 /* Arguments of mj_paged_decode.  All strides are in BYTES for the KV cache and
@@ -169,7 +180,12 @@ mj_status mj_config_check(const mj_config* cfg);
  * Plan buffer: int32 [work: cap_max x 4][n_splits: max_num_seqs]
  * [split_begin: max_num_seqs], cap_max = the largest capacity over q_len.
  * Workspace: fp32 split partials sized by the largest slot count, not by the
- * batch (the plan splits only batches smaller than one wave). */
+ * batch (the plan splits only batches smaller than one wave), then
+ * mj_decode_step's arrival counters (int32, max_num_seqs x h_k) and its Q
+ * staging (e4m3 codes and scales, used when the step is not fused).  The
+ * counters must be zero before the first mj_decode_step on a workspace (zero
+ * the whole buffer once after allocating it); every completed mj_decode_step
+ * leaves them zero again.  The other calls never touch them. */
 size_t mj_plan_buffer_bytes(const mj_config* cfg);
 size_t mj_workspace_bytes(const mj_config* cfg);
 
@@ -183,8 +199,8 @@ int32_t mj_plan_capacity(const mj_config* cfg, int32_t q_len);
  *   override; capacity = max(S, max_num_seqs); tiles_i =
  *   ceil((seq_lens_host[i] + margin) / kv_tile_tokens).  A batch smaller
  *   than S (and max_splits > 1) is split with the smallest chunk c >=
- *   ceil(max tiles / max_splits) whose item count sum_i max(1,ceil(tiles_i/c))
- *   fits S; otherwise one item per sequence.  Items (seq, tile_begin,
+ *   max(ceil(max tiles / max_splits), min chunk tiles) whose item count
+ *   sum_i max(1,ceil(tiles_i/c)) fits S; otherwise one item per sequence.  Items (seq, tile_begin,
  *   tile_end, split) are sequence-major and padded with (-1,0,0,0).
  * mj_plan_compute writes the whole plan image into plan_host
  * (mj_plan_buffer_bytes bytes) without touching the device.
@@ -238,10 +254,11 @@ mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_strid
  * split sequence writes fp32 partials (unnormalized O, running max, sum) to
  * the workspace for mj_merge_lse.  A row that sees no key writes O = 0,
  * LSE = -inf.
- * Errors: EINVAL (nulls, num_work/with_reduction not those of a plan for
- * this config and q_len, causal q_len>1 with ... see docs), EALIGN
- * (k/v/q8/out bases or strides not 16-byte / 8-element aligned),
- * ECAPACITY (num_seqs, q_len, workspace), EUNSUPPORTED, EHIP. */
+ * Errors: EINVAL (nulls, negative strides, descale kind out of range,
+ * num_work / with_reduction not those of a plan for this config and q_len),
+ * EALIGN (k/v/q8/out bases or byte strides not 16-byte aligned, out strides
+ * not multiples of 8 elements), ECAPACITY (num_seqs, q_len, workspace
+ * missing or too small for a split plan), EUNSUPPORTED, EHIP. */
 mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* args, hipStream_t stream);
 
 /* Log-sum-exp merge of the split partials (README "What it does", step 4):
@@ -250,6 +267,32 @@ mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* args, hipS
  * LSE.  Sequences with a single item are left untouched (mj_paged_decode
  * already wrote them).  Errors: EINVAL, ECAPACITY, EALIGN, EHIP. */
 mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* args, hipStream_t stream);
+
+/* Arguments of one whole decode step after the plan: the decode arguments
+ * (decode.q8 and decode.q_descale are not read and may be NULL;
+ * decode.workspace is required, >= mj_workspace_bytes(cfg), 256-byte
+ * aligned, counters zeroed once as described above) plus bf16 Q as
+ * mj_quantize_q takes it. */
+typedef struct mj_step_args {
+  mj_decode_args decode;
+  const void* q;                /* bf16; see mj_quantize_q for layout       */
+  int64_t q_tok_stride;         /* elements                                  */
+  int64_t q_head_stride;        /* elements                                  */
+  const float* q_mul;           /* nullable (h_q, 128)                       */
+} mj_step_args;
+
+/* mj_quantize_q + mj_paged_decode + mj_merge_lse (README "What it does",
+ * steps 2-4) as one call with the same results bit for bit.  Where the
+ * matrix-core kernel serves the shape (q_len*h_r <= 32, whole 16-token
+ * tiles, slot strides < 2^24 bytes) it is ONE kernel launch: every
+ * workgroup quantizes its (sequence, KV head)'s Q rows in its prologue with
+ * the quantize kernel's arithmetic, and the last split item of a split
+ * (sequence, KV head) to finish merges the partials (agent-scope release /
+ * acquire around an arrival counter in the workspace).  Otherwise it
+ * enqueues the three kernels, staging Q codes in the workspace.  Calls that
+ * share a workspace must not overlap (one stream, or ordered streams).
+ * Errors: those of the three calls. */
+mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStream_t stream);
 
 /* Test probes (not part of a decode step).
  * mj_debug_gather_kv copies the codes of tokens 0..seq_len-1 of one
@@ -261,13 +304,15 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, i
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream);
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);
 /* Process-wide choice of decode kernel, for A/B measurements and for testing
- * every kernel on the same inputs: variant 0 = automatic (q_len*h_r <= 4:
- * the matrix-core kernel for e4m3 KV, the VALU-PV streaming kernel for
- * e2m3; otherwise the generic LDS-tiled kernel), 1 = always the generic
- * kernel, 2 = the VALU-PV streaming kernel wherever q_len*h_r <= 4, 3 = same
- * as 0.  nontemporal 1 (default) marks the streaming kernels' KV loads
- * non-temporal.  Not thread-safe; set it before launching.  EINVAL on other
- * values. */
+ * every kernel on the same inputs: variant 0 = automatic (the matrix-core
+ * kernel wherever q_len*h_r <= 32, whole 16-token tiles and slot strides
+ * < 2^24 bytes; otherwise the generic LDS-tiled kernel), 1 = always the
+ * generic kernel, 2 = the VALU-PV streaming kernel for e4m3 with
+ * q_len*h_r <= 4 (automatic otherwise), 3 = same as 0, 10..13 = the
+ * matrix-core kernel with tuning bits (variant - 10): bit 0 two granules of
+ * prefetch (4-row kernel), bit 1 head-major grid.  nontemporal 1 (default) marks the streaming
+ * kernels' KV loads non-temporal.  Not thread-safe; set it before
+ * launching.  EINVAL on other values. */
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal);
 /* Plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
  * non-temporal 16-byte loads by `blocks` workgroups of 256 threads, each

@@ -30,6 +30,14 @@ this project's reading (the plainest one consistent with them):
 * items are sequence-major, split-minor, padded to ``cap`` with
   ``(-1, 0, 0, 0)``; ``split_begin`` is the exclusive prefix sum of ``n``.
 
+One addition of this library, not in the pages: the chunk also has a floor
+``min_chunk_tiles`` (default 1, which is the rule above).  The pages size
+the split for one wave of 40 CTAs; on 256 CUs the library plans several
+waves of items (``wgs_per_cu`` above the residency) to balance the tail,
+and the floor keeps each item long enough to amortise its prologue and
+partial write.  ``default_shape`` is the library's table of defaults for
+``wgs_per_cu`` and the floor, by KV format and query rows per KV head.
+
 Row tiles here hold up to 64 query rows (one GQA group of up to 64 rows reads
 its KV once); the pages' Thor kernel used at most 32.
 """
@@ -54,6 +62,20 @@ def capacity(q_len, h_q, h_k, num_cus, wgs_per_cu, max_num_seqs, slots_override=
     return max(s, max_num_seqs)
 
 
+def default_shape(kv_format: str, n_q: int) -> tuple[int, int]:
+    """(wgs_per_cu, min_chunk_tokens) the library uses when the config leaves
+    them 0: the e4m3 matrix-core kernel for up to 16 rows runs two
+    workgroups per CU and is planned four waves deep with items of at least
+    2048 tokens; the 32-row kernel (one workgroup per CU) and the e2m3
+    kernel are planned one wave deep; wider groups (the generic kernel) two
+    per CU."""
+    if kv_format == "e4m3" and n_q <= 16:
+        return 8, 2048
+    if n_q <= 32:
+        return 1, 1
+    return 2, 1
+
+
 def plan_split_kv(
     lens,
     *,
@@ -68,6 +90,7 @@ def plan_split_kv(
     slots_override: int = 0,
     margin: int = 0,
     row_tile: int = ROW_TILE,
+    min_chunk_tiles: int = 1,
 ) -> dict:
     b = len(lens)
     assert 0 < b <= max_num_seqs
@@ -76,7 +99,7 @@ def plan_split_kv(
     tiles = [math.ceil((int(L) + margin) / kv_tile) for L in lens]
     split = max_splits > 1 and b < S
     if split:
-        c = max(1, math.ceil(max(tiles) / max_splits))
+        c = max(1, math.ceil(max(tiles) / max_splits), min_chunk_tiles)
         while sum(max(1, math.ceil(t / c)) for t in tiles) > S:
             c += 1
         n = [max(1, math.ceil(t / c)) for t in tiles]

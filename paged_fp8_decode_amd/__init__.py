@@ -16,7 +16,7 @@ import ctypes
 import numpy as np
 
 from ._abi import (  # noqa: F401
-    Config, PlanInfo, DecodeArgs, MergeArgs, MjError, KV_FORMATS, SCALE_KINDS,
+    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, MjError, KV_FORMATS, SCALE_KINDS,
     MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
 )
 
@@ -35,10 +35,10 @@ def _ptr(t):
 
 
 def mj_config(*, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, num_cus=0, wgs_per_cu=0,
-              kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128) -> Config:
+              kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128, min_chunk_tokens=0) -> Config:
     c = Config(h_q=h_q, h_k=h_k, head_dim=head_dim, page_size=page_size, max_num_seqs=max_num_seqs,
                max_q_len=max_q_len, max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
-               kv_tile_tokens=kv_tile_tokens, slots_override=slots_override,
+               kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, min_chunk_tokens=min_chunk_tokens,
                kv_format=KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format)
     return c
 
@@ -110,6 +110,10 @@ def mj_paged_decode(cfg: Config, args: DecodeArgs, stream=None):
 
 def mj_merge_lse(cfg: Config, args: MergeArgs, stream=None):
     check(lib().mj_merge_lse(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_merge_lse")
+
+
+def mj_decode_step(cfg: Config, args: StepArgs, stream=None):
+    check(lib().mj_decode_step(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_decode_step")
 
 
 def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_len: int, which: int, dense_out,

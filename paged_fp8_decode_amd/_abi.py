@@ -8,6 +8,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
+ABI_VERSION = 2  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
 KV_FORMATS = {"e4m3": 0, "e2m3": 1}
 SCALE_KINDS = {"tensor": 0, "head": 1, "seq_head": 2}
@@ -23,12 +24,13 @@ class MjError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "h_q", "h_k", "head_dim", "page_size", "max_num_seqs", "max_q_len", "max_splits", "num_cus",
-        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format")]
+        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens")]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_work", "slots", "chunk_tiles", "num_chunks", "with_reduction", "num_seqs", "q_len", "kv_tile_tokens")]
+        "num_work", "slots", "chunk_tiles", "num_chunks", "with_reduction", "num_seqs", "q_len", "kv_tile_tokens",
+        "min_chunk_tiles")]
 
 
 _p = ctypes.c_void_p
@@ -57,6 +59,12 @@ class MergeArgs(ctypes.Structure):
     ]
 
 
+class StepArgs(ctypes.Structure):
+    _fields_ = [
+        ("decode", DecodeArgs), ("q", _p), ("q_tok_stride", _i64), ("q_head_stride", _i64), ("q_mul", _p),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -77,6 +85,7 @@ def _load():
         "mj_quantize_q": (_i32, [P(Config), _p, _i64, _i64, _p, _i32, _i32, _p, _p, _p]),
         "mj_paged_decode": (_i32, [P(Config), P(DecodeArgs), _p]),
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
+        "mj_decode_step": (_i32, [P(Config), P(StepArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
         "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),
@@ -88,6 +97,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
+    if lib.mj_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI {lib.mj_abi_version()}, this binding expects {ABI_VERSION}: rebuild it")
     return lib
 
 

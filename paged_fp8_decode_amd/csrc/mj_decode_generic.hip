@@ -13,6 +13,7 @@
 // running max in log2 units, running sum) for the merge.
 #include "mj_device.h"
 #include "mj_internal.h"
+#include "mj_merge.h"
 
 namespace mj {
 
@@ -182,33 +183,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
 
 // Log-sum-exp merge of split partials: one workgroup per (sequence, KV head).
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
-  const int seq = blockIdx.x;
-  const int g = blockIdx.y;
-  const int n = p.n_splits[seq];
-  if (n <= 1) return;
-  const int w0 = p.split_begin[seq];
-  if (w0 < 0 || w0 + n > p.part_items) return;
-  const int c = threadIdx.x & 127;
-  for (int r = threadIdx.x >> 7; r < p.n_q; r += 2) {
-    float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, p.m_part[((int64_t)(w0 + s) * p.h_k + g) * p.nqp + r]);
-    float o = 0.0f, lse = -INFINITY;
-    if (M != -INFINITY) {
-      float num = 0.0f, den = 0.0f;
-      for (int s = 0; s < n; ++s) {
-        const int64_t idx = ((int64_t)(w0 + s) * p.h_k + g) * p.nqp + r;
-        const float wt = exp2f(p.m_part[idx] - M);
-        den += wt * p.l_part[idx];
-        num += wt * p.o_part[idx * kHeadDim + c];
-      }
-      o = num / den;
-      lse = (M + log2f(den)) * kLn2;
-    }
-    const int t = r / p.h_r;
-    const int h = g * p.h_r + (r - t * p.h_r);
-    p.out[((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c] = f32_to_bf16(o);
-    if (c == 0 && p.lse) p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = lse;
-  }
+  merge_one<false>(p, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // Probe: dense copy of one (sequence, head)'s codes through the same

@@ -40,6 +40,7 @@
 // when a granule exceeds it by more than 8 in log2 units), which is exact.
 #include "mj_device.h"
 #include "mj_internal.h"
+#include "mj_merge.h"
 
 namespace mj {
 
@@ -56,6 +57,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
+// s_waitcnt immediate (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]) that waits for vmcnt 0 only
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGran = 32;
 constexpr float kLazyMax = 8.0f;
@@ -388,6 +392,9 @@ void decode_mfma_kernel(DecodeParams p) {
   constexpr int kRows = NQB * NRB;  // rows of the GQA group this instance serves (padded)
   __shared__ float o_s[kWaves][kRows][kHeadDim];
   __shared__ float m_s[kWaves][kRows], l_s[kWaves][kRows];
+  __shared__ __align__(16) uint8_t q_s[kRows][kHeadDim];  // fused step: this item's e4m3 Q rows
+  __shared__ float red_s[kWaves];
+  __shared__ int last_s;
 
   // head-major grids put the KV heads of one work item in consecutive
   // workgroups, so they are resident together
@@ -425,7 +432,42 @@ void decode_mfma_kernel(DecodeParams p) {
   c.num_pages = (uint32_t)min<int64_t>(p.num_pages, 0x7FFFFFFF);
   c.page_shift = p.page_shift;
   c.pmask = p.page_size - 1;
-  c.cscale = p.q_descale[(int64_t)seq * p.h_k + g] * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
+  float qdesc;
+  if (p.qb) {
+    // fused step: quantize this (sequence, KV head)'s Q rows here, with the
+    // arithmetic of the stand-alone quantize kernel (every split item of the
+    // pair derives the same codes and scale)
+    constexpr int kQV = (kRows * 16 + kThreads - 1) / kThreads;  // 8-channel vectors per thread
+    const int nvec = p.n_q * 16;
+    float x[kQV][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kQV; ++k) {
+      const int v = threadIdx.x + k * kThreads;
+      if (v < nvec) {
+        q_load8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, v >> 4, (v & 15) * 8, x[k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if (lane == 0) red_s[wave] = amax;
+    __syncthreads();
+    amax = red_s[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red_s[i]);
+    qdesc = q_scale_from_amax(amax);
+#pragma unroll
+    for (int k = 0; k < kQV; ++k) {
+      const int v = threadIdx.x + k * kThreads;
+      if (v < nvec) *reinterpret_cast<uint2*>(&q_s[v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc);
+    }
+    __syncthreads();
+  } else {
+    qdesc = p.q_descale[(int64_t)seq * p.h_k + g];
+  }
+  c.cscale = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
   const bool single = p.n_splits[seq] <= 1;
 
   // B operands of QK^T: column n of block R = Q row 16R + n % NQB (zero past n_q)
@@ -437,7 +479,8 @@ void decode_mfma_kernel(DecodeParams p) {
     row_tok[R] = r / p.h_r;
     if (r < p.n_q) {
       const u32x4* src =
-          reinterpret_cast<const u32x4*>(p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim + 32 * jj);
+          p.qb ? reinterpret_cast<const u32x4*>(&q_s[r][32 * jj])
+               : reinterpret_cast<const u32x4*>(p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim + 32 * jj);
       const u32x4 a = src[0], b = src[1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -543,12 +586,52 @@ void decode_mfma_kernel(DecodeParams p) {
       if (ch == 0 && p.lse)
         p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
     } else if (w < p.part_items) {
+      // written through to device-coherent memory, for a merge on any XCD
       const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + r;
-      p.o_part[idx * kHeadDim + ch] = O * om;
+      store_coherent(&p.o_part[idx * kHeadDim + ch], O * om);
       if (ch == 0) {
-        p.m_part[idx] = Lsum > 0.0f ? M : -INFINITY;
-        p.l_part[idx] = Lsum;
+        store_coherent(&p.m_part[idx], Lsum > 0.0f ? M : -INFINITY);
+        store_coherent(&p.l_part[idx], Lsum);
       }
+    }
+  }
+
+  if (!single && p.counters) {
+    // fused merge: once every wave's write-through stores have completed
+    // (vmcnt 0) and the workgroup has met, the partials are visible to all
+    // XCDs; count the arrival, and the last split of the pair merges.  An
+    // agent-scope release fence would instead write back and invalidate the
+    // whole XCD L2 in every wave, which costs far more than the stores.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int32_t* cnt = p.counters + (int64_t)seq * p.h_k + g;
+      const int last = atomicAdd(cnt, 1) == p.n_splits[seq] - 1;
+      if (last) atomicExch(cnt, 0);  // every split of this launch has arrived
+      last_s = last;
+    }
+    __syncthreads();
+    if (last_s) {  // the partials are read with device-coherent loads
+      MergeParams mp;
+      mp.n_splits = p.n_splits;
+      mp.split_begin = p.split_begin;
+      mp.o_part = p.o_part;
+      mp.m_part = p.m_part;
+      mp.l_part = p.l_part;
+      mp.nqp = p.nqp;
+      mp.part_items = p.part_items;
+      mp.out = p.out;
+      mp.out_ts = p.out_ts;
+      mp.out_hs = p.out_hs;
+      mp.lse = p.lse;
+      mp.num_seqs = p.num_seqs;
+      mp.q_len = p.q_len;
+      mp.h_q = p.h_q;
+      mp.h_k = p.h_k;
+      mp.h_r = p.h_r;
+      mp.n_q = p.n_q;
+      merge_one<true>(mp, seq, g, threadIdx.x);
     }
   }
 }
@@ -565,14 +648,8 @@ hipError_t launch_shape(const DecodeParams& p, bool nt, hipStream_t s) {
 
 template <int FMT>
 hipError_t launch_fmt(const DecodeParams& p, bool nt, int tune, hipStream_t s) {
-  if (p.n_q <= 4) {
-    switch (tune) {  // prefetch depth x occupancy of the 4-row kernel
-      case 1: return launch_shape<FMT, 4, 1, 1, 3>(p, nt, s);
-      case 2: return launch_shape<FMT, 4, 1, 2, 2>(p, nt, s);
-      case 3: return launch_shape<FMT, 4, 1, 2, 3>(p, nt, s);
-      default: return launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
-    }
-  }
+  if (p.n_q <= 4)  // tune bit 1: two granules of prefetch instead of one
+    return (tune & 2) ? launch_shape<FMT, 4, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 8) return launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 16) return launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
   return launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
@@ -582,13 +659,12 @@ hipError_t launch_fmt(const DecodeParams& p, bool nt, int tune, hipStream_t s) {
 
 bool decode_mfma_supports(int n_q) { return n_q >= 1 && n_q <= 32; }
 
-// tune: 0 = defaults; 1..3 select prefetch depth / occupancy of the 4-row kernel
+// tune bits: 1 = two granules of prefetch (4-row groups), 2 = head-major grid
 hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, bool nontemporal, int tune, hipStream_t s) {
   DecodeParams p = p_in;
-  p.head_major = (tune & 4) ? 1 : 0;
-  tune &= 3;
-  if (kv_format != 0 && (tune & 1)) tune &= ~1;  // the e2m3 kernel does not fit 3 waves per SIMD
-  return kv_format == 0 ? launch_fmt<0>(p, nontemporal, tune, s) : launch_fmt<1>(p, nontemporal, tune, s);
+  p.head_major = (tune & 2) ? 1 : 0;
+  const int t = (tune & 1) ? 2 : 0;
+  return kv_format == 0 ? launch_fmt<0>(p, nontemporal, t, s) : launch_fmt<1>(p, nontemporal, t, s);
 }
 
 }  // namespace mj

@@ -397,9 +397,9 @@ void decode_stream_kernel(DecodeParams p) {
 }  // namespace
 
 // Kernel choice: 0 = automatic, 1 = always the generic kernel, 2 = the
-// VALU-PV streaming kernel wherever it applies, 3 = same as 0, 10..17 = the
-// matrix-core kernel with tuning setting (variant - 10): bit 0 three waves per
-// SIMD, bit 1 two granules of prefetch (4-row groups), bit 2 head-major grid.
+// VALU-PV streaming kernel wherever it applies, 3 = same as 0, 10..13 = the
+// matrix-core kernel with tuning setting (variant - 10): bit 0 two granules
+// of prefetch (4-row groups), bit 1 head-major grid.
 static int g_variant = 0;
 static int g_nontemporal = 1;
 
@@ -408,16 +408,26 @@ void set_decode_variant(int v, int nt) {
   g_nontemporal = nt;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s) {
+// 0 = generic kernel, 1 = matrix-core kernel, 2 = VALU-PV streaming kernel
+static int kernel_choice(const DecodeParams& p, int kv_format, int row_tiles) {
   // the streaming kernels address a page's rows with 32-bit lane offsets and
   // take whole 16-token tiles inside one page
   const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24);
   const bool tiles_ok = row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
-  if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q))
-    return launch_decode_generic(p, kv_format, row_tiles, s);
-  const int tune = g_variant >= 10 ? g_variant - 10 : 0;
-  if (kv_format != 0 || g_variant != 2 || p.n_q > 4)
-    return launch_decode_mfma(p, kv_format, g_nontemporal != 0, tune, s);
+  if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q)) return 0;
+  if (kv_format != 0 || g_variant != 2 || p.n_q > 4) return 1;
+  return 2;
+}
+
+bool decode_fuses_step(const DecodeParams& p, int kv_format, int row_tiles) {
+  return kernel_choice(p, kv_format, row_tiles) == 1;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s) {
+  const int k = kernel_choice(p, kv_format, row_tiles);
+  if (k != 1 && (p.qb || p.counters)) return hipErrorInvalidValue;  // only the matrix-core kernel fuses the step
+  if (k == 0) return launch_decode_generic(p, kv_format, row_tiles, s);
+  if (k == 1) return launch_decode_mfma(p, kv_format, g_nontemporal != 0, g_variant >= 10 ? g_variant - 10 : 0, s);
   const dim3 grid(p.num_work, p.h_k);
   if (g_nontemporal)
     hipLaunchKernelGGL((decode_stream_kernel<0, true>), grid, dim3(kThreads), 0, s, p);

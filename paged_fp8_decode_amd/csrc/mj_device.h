@@ -42,15 +42,12 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
   uint32_t u = __float_as_uint(x);
   const uint32_t sign = (u >> 24) & 0x80u;
   u &= 0x7FFFFFFFu;
-  uint32_t code;
-  if (u >= 0x3C800000u) {  // >= 2^-6: normal e4m3; keep 3 of 23 mantissa bits
-    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-    code = code > 0x7Eu ? 0x7Eu : code;
-  } else {  // subnormal range: multiples of 2^-9 (8 * 2^-9 is the min normal)
-    code = (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);
-  }
-  return sign | code;
+  // normal e4m3 (|x| >= 2^-6): keep 3 of 23 mantissa bits, ties to even
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t nrm = min(((r >> 23) << 3) - (120u << 3) + ((r >> 20) & 7u), 0x7Eu);
+  // subnormal range: multiples of 2^-9 (8 * 2^-9 is the min normal)
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);
+  return sign | (u >= 0x3C800000u ? nrm : sub);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
@@ -89,6 +86,53 @@ __device__ __forceinline__ void unpack16_e2m3(uint32_t w0, uint32_t w1, uint32_t
     const int b = 6 * k;
     out[k] = b + 6 <= 64 ? (uint32_t)((lo >> b) & 63u) : (uint32_t)((hi >> (b - 32)) & 63u);
   }
+}
+
+}  // namespace mj
+
+namespace mj {
+
+// Dynamic e4m3 quantization of Q per (sequence, KV head), the arithmetic
+// both the stand-alone quantize kernel and the fused decode step use, so the
+// two produce the same codes and scale bit for bit (mjolnir-kernel wheel page
+// mjolnir/runner.py, T5DecodeRunner.run, fp8-Q branch): over the q_len tokens
+// and h_r query heads of KV head g, x = fp32(q) [* q_mul], amax = max(max|x|,
+// 1e-6), s = amax / 448, code = e4m3(x / s), rows packed t*h_r + r.  The
+// division must be the correctly rounded one (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt).
+constexpr float kQAmaxFloor = 1e-6f;
+constexpr float kFp8Max = 448.0f;
+
+// Channels [c0, c0 + 8) of packed row `row` of (seq, g) as fp32.
+__device__ __forceinline__ void q_load8(const uint16_t* q, int64_t q_ts, int64_t q_hs, const float* q_mul, int q_len,
+                                        int h_r, int seq, int g, int row, int c0, float x[8]) {
+  const int t = row / h_r;
+  const int h = g * h_r + (row - t * h_r);
+  const uint4 raw = *reinterpret_cast<const uint4*>(q + ((int64_t)seq * q_len + t) * q_ts + (int64_t)h * q_hs + c0);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+  if (q_mul) {
+    const float4 m0 = *reinterpret_cast<const float4*>(q_mul + (int64_t)h * kHeadDim + c0);
+    const float4 m1 = *reinterpret_cast<const float4*>(q_mul + (int64_t)h * kHeadDim + c0 + 4);
+    x[0] *= m0.x; x[1] *= m0.y; x[2] *= m0.z; x[3] *= m0.w;
+    x[4] *= m1.x; x[5] *= m1.y; x[6] *= m1.z; x[7] *= m1.w;
+  }
+}
+
+__device__ __forceinline__ float q_scale_from_amax(float amax) { return fmaxf(amax, kQAmaxFloor) / kFp8Max; }
+
+// Eight e4m3 codes of x / s, little-endian in two dwords.
+__device__ __forceinline__ uint2 q_codes8(const float x[8], float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lo |= e4m3_rne(x[e] / s) << (8 * e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hi |= e4m3_rne(x[4 + e] / s) << (8 * e);
+  return make_uint2(lo, hi);
 }
 
 }  // namespace mj

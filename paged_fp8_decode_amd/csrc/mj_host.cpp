@@ -13,21 +13,47 @@
 namespace {
 
 constexpr int kRowTile = 64;      // query rows one decode workgroup covers
-constexpr int kDefaultWgsPerCu = 2;
 constexpr int kDefaultKvTile = 128;
 constexpr int kMaxRows = 1024;    // sanity bound on q_len * h_r
 
 struct Derived {
-  int num_cus, wgs_per_cu, kv_tile, h_r, nq_max;
+  int num_cus, kv_tile, h_r, nq_max;
   int cap_max, slots_max;
 };
+
+// Planned workgroups per CU and chunk floor (tokens) for a q_len: the config's
+// values, or the defaults of the kernel that serves n_q = q_len * h_r.  The
+// e4m3 matrix-core kernel for up to 16 rows holds two workgroups per CU;
+// planning it four waves deep lets CUs that stream faster take more items
+// (the tail of a single wave is set by the slowest CU), and the 2048-token
+// floor keeps items long enough to amortise the prologue and partial write.
+// The 32-row kernel (one workgroup per CU) and the e2m3 kernel measured
+// fastest planned one wave deep.
+struct PlanShape {
+  int wgs_per_cu, min_chunk_tokens;
+};
+
+PlanShape plan_shape(const mj_config* c, const Derived& d, int q_len) {
+  const int n_q = q_len * d.h_r;
+  const bool small_e4m3 = c->kv_format == MJ_KV_E4M3 && n_q <= 16;
+  PlanShape ps;
+  ps.wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : (small_e4m3 ? 8 : (n_q <= 32 ? 1 : 2));
+  ps.min_chunk_tokens = c->min_chunk_tokens ? c->min_chunk_tokens : (small_e4m3 ? 2048 : 1);
+  return ps;
+}
+
+int min_chunk_tiles(const mj_config* c, const Derived& d, int q_len) {
+  return (plan_shape(c, d, q_len).min_chunk_tokens + d.kv_tile - 1) / d.kv_tile;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 mj_status check_config(const mj_config* c) {
   if (!c) return MJ_EINVAL;
   if (c->h_q < 1 || c->h_k < 1 || c->max_num_seqs < 1 || c->max_q_len < 1 || c->max_splits < 1) return MJ_EINVAL;
-  if (c->num_cus < 0 || c->wgs_per_cu < 0 || c->kv_tile_tokens < 0 || c->slots_override < 0) return MJ_EINVAL;
+  if (c->num_cus < 0 || c->wgs_per_cu < 0 || c->kv_tile_tokens < 0 || c->slots_override < 0 ||
+      c->min_chunk_tokens < 0)
+    return MJ_EINVAL;
   if (c->kv_tile_tokens % 16 != 0) return MJ_EINVAL;
   if (c->h_q % c->h_k != 0) return MJ_EUNSUPPORTED;
   if (c->head_dim != 128) return MJ_EUNSUPPORTED;
@@ -42,7 +68,7 @@ int row_tiles(const mj_config* c, int q_len) { return (q_len * (c->h_q / c->h_k)
 int slots_for(const mj_config* c, const Derived& d, int q_len) {
   if (c->slots_override > 0) return c->slots_override;
   const int64_t denom = (int64_t)c->h_k * row_tiles(c, q_len);
-  return (int)std::max<int64_t>(1, ((int64_t)d.num_cus * d.wgs_per_cu) / denom);
+  return (int)std::max<int64_t>(1, ((int64_t)d.num_cus * plan_shape(c, d, q_len).wgs_per_cu) / denom);
 }
 
 int cap_for(const mj_config* c, const Derived& d, int q_len) { return std::max(slots_for(c, d, q_len), c->max_num_seqs); }
@@ -57,7 +83,6 @@ mj_status derive(const mj_config* c, Derived* d) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return MJ_EHIP;
     d->num_cus = n;
   }
-  d->wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : kDefaultWgsPerCu;
   d->kv_tile = c->kv_tile_tokens ? c->kv_tile_tokens : kDefaultKvTile;
   d->h_r = c->h_q / c->h_k;
   d->nq_max = c->max_q_len * d->h_r;
@@ -72,17 +97,24 @@ mj_status derive(const mj_config* c, Derived* d) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace: split partials (o | m | l) for the largest slot count, then the
+// step's arrival counters and its Q staging (codes, scales) for the unfused
+// fallback.
 struct WorkspaceLayout {
-  size_t o_off, m_off, l_off, total;
+  size_t o_off, m_off, l_off, cnt_off, q8_off, qd_off, total;
 };
 
 WorkspaceLayout workspace_layout(const mj_config* c, const Derived& d) {
   const size_t rows = (size_t)d.slots_max * c->h_k * d.nq_max;
+  const size_t pairs = (size_t)c->max_num_seqs * c->h_k;
   WorkspaceLayout w;
   w.o_off = 0;
   w.m_off = round256(rows * 128 * sizeof(float));
   w.l_off = w.m_off + round256(rows * sizeof(float));
-  w.total = w.l_off + round256(rows * sizeof(float));
+  w.cnt_off = w.l_off + round256(rows * sizeof(float));
+  w.q8_off = w.cnt_off + round256(pairs * sizeof(int32_t));
+  w.qd_off = w.q8_off + round256(pairs * d.nq_max * 128);
+  w.total = w.qd_off + round256(pairs * sizeof(float));
   return w;
 }
 
@@ -158,7 +190,7 @@ mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, in
     // smallest chunk >= ceil(max_tiles / max_splits) whose item count fits S;
     // the count only falls as the chunk grows, and at c = max_tiles it is
     // num_seqs < S, so a bisection finds it.
-    int64_t lo = std::max<int64_t>(1, ceil_div(max_tiles, cfg->max_splits));
+    int64_t lo = std::max<int64_t>({1, ceil_div(max_tiles, cfg->max_splits), min_chunk_tiles(cfg, d, q_len)});
     int64_t hi = std::max<int64_t>(lo, max_tiles);
     auto count = [&](int64_t ch) {
       int64_t n = 0;
@@ -210,6 +242,7 @@ mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, in
   info->num_seqs = num_seqs;
   info->q_len = q_len;
   info->kv_tile_tokens = d.kv_tile;
+  info->min_chunk_tiles = min_chunk_tiles(cfg, d, q_len);
   return MJ_OK;
 }
 
@@ -251,6 +284,7 @@ mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_
   p.slots = S;
   p.split = split ? 1 : 0;
   p.cap_max = d.cap_max;
+  p.min_chunk = min_chunk_tiles(cfg, d, q_len);
   if (mj::launch_plan(p, stream) != hipSuccess) return MJ_EHIP;
   info->num_work = cap_for(cfg, d, q_len);
   info->slots = S;
@@ -260,6 +294,7 @@ mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_
   info->num_seqs = num_seqs;
   info->q_len = q_len;
   info->kv_tile_tokens = d.kv_tile;
+  info->min_chunk_tiles = p.min_chunk;
   return MJ_OK;
 }
 
@@ -360,6 +395,10 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->causal = a->causal ? 1 : 0;
   p->num_work = a->num_work;
   p->head_major = 0;
+  p->qb = nullptr;
+  p->qb_ts = p->qb_hs = 0;
+  p->q_mul = nullptr;
+  p->counters = nullptr;
   return MJ_OK;
 }
 
@@ -372,6 +411,51 @@ mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* a, hipStre
   st = fill_decode(cfg, d, a, &p);
   if (st != MJ_OK) return st;
   return mj::launch_decode(p, cfg->kv_format, row_tiles(cfg, a->q_len), stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream_t stream) {
+  Derived d;
+  mj_status st = derive(cfg, &d);
+  if (st != MJ_OK) return st;
+  if (!sa || !sa->q || sa->q_tok_stride < 0 || sa->q_head_stride < 0) return MJ_EINVAL;
+  if (!aligned(sa->q, 16) || sa->q_tok_stride % 8 || sa->q_head_stride % 8 || (sa->q_mul && !aligned(sa->q_mul, 16)))
+    return MJ_EALIGN;
+  const WorkspaceLayout wl = workspace_layout(cfg, d);
+  if (!sa->decode.workspace || sa->decode.workspace_bytes < wl.total) return MJ_ECAPACITY;
+  if (!aligned(sa->decode.workspace, 256)) return MJ_EALIGN;
+  char* ws = static_cast<char*>(sa->decode.workspace);
+  uint8_t* q8 = reinterpret_cast<uint8_t*>(ws + wl.q8_off);
+  float* qd = reinterpret_cast<float*>(ws + wl.qd_off);
+  mj_decode_args a = sa->decode;
+  a.q8 = q8;
+  a.q_descale = qd;
+  mj::DecodeParams p;
+  st = fill_decode(cfg, d, &a, &p);
+  if (st != MJ_OK) return st;
+  const int rt = row_tiles(cfg, a.q_len);
+  if (mj::decode_fuses_step(p, cfg->kv_format, rt)) {
+    p.qb = static_cast<const uint16_t*>(sa->q);
+    p.qb_ts = sa->q_tok_stride;
+    p.qb_hs = sa->q_head_stride;
+    p.q_mul = sa->q_mul;
+    p.counters = a.with_reduction ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
+    return mj::launch_decode(p, cfg->kv_format, rt, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+  }
+  st = mj_quantize_q(cfg, sa->q, sa->q_tok_stride, sa->q_head_stride, sa->q_mul, a.num_seqs, a.q_len, q8, qd, stream);
+  if (st != MJ_OK) return st;
+  if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+  if (!a.with_reduction) return MJ_OK;
+  mj_merge_args m;
+  m.plan = a.plan;
+  m.num_seqs = a.num_seqs;
+  m.q_len = a.q_len;
+  m.workspace = a.workspace;
+  m.workspace_bytes = a.workspace_bytes;
+  m.out = a.out;
+  m.out_tok_stride = a.out_tok_stride;
+  m.out_head_stride = a.out_head_stride;
+  m.lse = a.lse;
+  return mj_merge_lse(cfg, &m, stream);
 }
 
 mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t stream) {
@@ -433,7 +517,7 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
 }
 
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal) {
-  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 17)) || (nontemporal != 0 && nontemporal != 1)) return MJ_EINVAL;
+  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 13)) || (nontemporal != 0 && nontemporal != 1)) return MJ_EINVAL;
   mj::set_decode_variant(variant, nontemporal);
   return MJ_OK;
 }

@@ -50,6 +50,15 @@ struct DecodeParams {
   int causal;
   int num_work;
   int head_major;              // grid is (h_k, num_work) instead of (num_work, h_k)
+  // Fused step (matrix-core kernel only; null otherwise).  qb: bf16 Q
+  // quantized in the prologue instead of reading q8 / q_descale.  counters:
+  // (max_num_seqs, h_k) zero-initialised arrival counters; the last split of
+  // a (sequence, KV head) to finish merges the partials and resets its
+  // counter to zero.
+  const uint16_t* qb;
+  int64_t qb_ts, qb_hs;        // elements
+  const float* q_mul;          // nullable (h_q, 128)
+  int32_t* counters;
 };
 
 struct MergeParams {
@@ -82,11 +91,13 @@ struct PlanParams {
   int32_t* n_splits;        // [max_num_seqs]
   int32_t* split_begin;     // [max_num_seqs]
   int num_seqs, max_num_seqs, margin, kv_tile, page_size, max_blocks, max_splits, slots, split, cap_max;
+  int min_chunk;            // floor of the chunk, KV tiles
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
 hipError_t launch_qquant(const QQuantParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
+bool decode_fuses_step(const DecodeParams& p, int kv_format, int row_tiles);
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);

@@ -22,28 +22,6 @@ namespace {
 
 constexpr int kQThreads = 256;
 
-__device__ __forceinline__ void load8(const QQuantParams& p, int seq, int g, int v, float x[8], int& row, int& c0) {
-  row = v >> 4;
-  c0 = (v & 15) * 8;
-  const int t = row / p.h_r;
-  const int rr = row - t * p.h_r;
-  const int h = g * p.h_r + rr;
-  const uint16_t* src = p.q + ((int64_t)seq * p.q_len + t) * p.q_ts + (int64_t)h * p.q_hs + c0;
-  const uint4 raw = *reinterpret_cast<const uint4*>(src);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(w[e] << 16);
-    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-  }
-  if (p.q_mul) {
-    const float4 m0 = *reinterpret_cast<const float4*>(p.q_mul + (int64_t)h * kHeadDim + c0);
-    const float4 m1 = *reinterpret_cast<const float4*>(p.q_mul + (int64_t)h * kHeadDim + c0 + 4);
-    x[0] *= m0.x; x[1] *= m0.y; x[2] *= m0.z; x[3] *= m0.w;
-    x[4] *= m1.x; x[5] *= m1.y; x[6] *= m1.z; x[7] *= m1.w;
-  }
-}
-
 __global__ __launch_bounds__(kQThreads) void qquant_kernel(QQuantParams p) {
   const int seq = blockIdx.x;
   const int g = blockIdx.y;
@@ -54,8 +32,7 @@ __global__ __launch_bounds__(kQThreads) void qquant_kernel(QQuantParams p) {
   float amax = 0.0f;
   for (int v = tid; v < nvec; v += kQThreads) {
     float x[8];
-    int row, c0;
-    load8(p, seq, g, v, x, row, c0);
+    q_load8(p.q, p.q_ts, p.q_hs, p.q_mul, p.q_len, p.h_r, seq, g, v >> 4, (v & 15) * 8, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
   }
@@ -66,18 +43,13 @@ __global__ __launch_bounds__(kQThreads) void qquant_kernel(QQuantParams p) {
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-  const float s = fmaxf(amax, 1e-6f) / 448.0f;
+  const float s = q_scale_from_amax(amax);
   uint8_t* dst = p.q8 + ((int64_t)seq * p.h_k + g) * p.n_q * kHeadDim;
   for (int v = tid; v < nvec; v += kQThreads) {
+    const int row = v >> 4, c0 = (v & 15) * 8;
     float x[8];
-    int row, c0;
-    load8(p, seq, g, v, x, row, c0);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lo |= e4m3_rne(x[e] / s) << (8 * e);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) hi |= e4m3_rne(x[4 + e] / s) << (8 * e);
-    *reinterpret_cast<uint2*>(dst + (int64_t)row * kHeadDim + c0) = make_uint2(lo, hi);
+    q_load8(p.q, p.q_ts, p.q_hs, p.q_mul, p.q_len, p.h_r, seq, g, row, c0, x);
+    *reinterpret_cast<uint2*>(dst + (int64_t)row * kHeadDim + c0) = q_codes8(x, s);
   }
   if (tid == 0) p.q_descale[(int64_t)seq * p.h_k + g] = s;
 }

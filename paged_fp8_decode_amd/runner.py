@@ -1,6 +1,6 @@
 """``DecodeStep``: one decode site's configuration, its persistent device
-buffers, and the four C-ABI calls in order (plan -> quantize Q -> decode ->
-merge).  Buffers are allocated once with torch (plumbing) at fixed
+buffers, and the C-ABI calls of a step in order: plan -> quantize Q ->
+decode -> merge, or plan -> ``mj_decode_step`` (the last three fused).  Buffers are allocated once with torch (plumbing) at fixed
 addresses, so a hipGraph that captured ``run`` replays any later ``plan``
 (mjolnir-kernel wheel page mjolnir/runner.py, module docstring and
 T5DecodeRunner.__init__: fixed-address plan buffers padded to a fixed grid).
@@ -10,20 +10,21 @@ from __future__ import annotations
 
 import torch
 
-from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, check, mj_config, mj_config_check, mj_merge_lse,
-               mj_paged_decode, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
+from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, StepArgs, check, mj_config, mj_config_check,
+               mj_decode_step, mj_merge_lse, mj_paged_decode, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
                mj_quantize_q, mj_workspace_bytes)
 
 
 class DecodeStep:
     def __init__(self, *, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, kv_format="e4m3",
-                 num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, device="cuda"):
+                 num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, min_chunk_tokens=0, device="cuda"):
         self.device = torch.device(device)
         if num_cus == 0:
             num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
         self.cfg = mj_config(h_q=h_q, h_k=h_k, page_size=page_size, max_num_seqs=max_num_seqs, max_q_len=max_q_len,
                              max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
-                             kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, kv_format=kv_format)
+                             kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, kv_format=kv_format,
+                             min_chunk_tokens=min_chunk_tokens)
         check(mj_config_check(self.cfg), "mj_config_check")
         self.h_q, self.h_k, self.h_r = h_q, h_k, h_q // h_k
         self.max_q_len = max_q_len
@@ -33,7 +34,8 @@ class DecodeStep:
         self._staging = [torch.zeros(n_plan, dtype=torch.int32).pin_memory() for _ in range(2)]
         self._staging_done = [None, None]
         self._slot = 0
-        self.workspace = torch.empty(max(256, mj_workspace_bytes(self.cfg)), dtype=torch.uint8, device=self.device)
+        # zeroed once: mj_decode_step's arrival counters start (and stay) zero
+        self.workspace = torch.zeros(max(256, mj_workspace_bytes(self.cfg)), dtype=torch.uint8, device=self.device)
         n_q_max = max_q_len * self.h_r
         self.q8 = torch.empty(max_num_seqs * h_k * n_q_max * 128, dtype=torch.uint8, device=self.device)
         self.q_descale = torch.empty(max_num_seqs * h_k, dtype=torch.float32, device=self.device)
@@ -68,19 +70,19 @@ class DecodeStep:
 
     def run(self, *, q, k_cache, v_cache, k_strides, v_strides, num_pages, block_table, seq_lens, k_descale,
             v_descale, descale_kind, softmax_scale, out, lse=None, q_mul=None, o_mul=None, causal=True,
-            info: PlanInfo | None = None, stream=None, events=None):
-        """quantize Q -> decode -> merge (iff the plan split), all on ``stream``.
+            info: PlanInfo | None = None, stream=None, events=None, fused=False):
+        """quantize Q -> decode -> merge (iff the plan split), all on ``stream``;
+        with ``fused`` one ``mj_decode_step`` call instead.
 
         q: bf16 (b*q_len, h_q, 128) view; out: bf16 (b*q_len, h_q, 128) view;
         k/v strides: bytes (page, slot, head); block_table: int32 (b, max_blocks).
         ``events``: optional pair of events recorded right before and right
-        after the decode launch (decode-kernel timing on this stream).
+        after the decode launch (the step call when fused).
         """
         info = info or self.info
         assert info is not None, "plan() first"
         b, ql = info.num_seqs, info.q_len
         stream = stream or torch.cuda.current_stream(self.device)
-        mj_quantize_q(self.cfg, q, q_mul, b, ql, self.q8, self.q_descale, stream)
         kind = SCALE_KINDS[descale_kind] if isinstance(descale_kind, str) else descale_kind
         a = DecodeArgs(
             q8=self.q8.data_ptr(), q_descale=self.q_descale.data_ptr(), num_seqs=b, q_len=ql, causal=int(causal),
@@ -97,6 +99,19 @@ class DecodeStep:
             out=out.data_ptr(), out_tok_stride=out.stride(0), out_head_stride=out.stride(1),
             lse=lse.data_ptr() if lse is not None else None,
         )
+        if fused:
+            assert q.stride(2) == 1
+            a.q8 = None
+            a.q_descale = None
+            sa = StepArgs(decode=a, q=q.data_ptr(), q_tok_stride=q.stride(0), q_head_stride=q.stride(1),
+                          q_mul=q_mul.data_ptr() if q_mul is not None else None)
+            if events:
+                events[0].record(stream)
+            mj_decode_step(self.cfg, sa, stream)
+            if events:
+                events[1].record(stream)
+            return out
+        mj_quantize_q(self.cfg, q, q_mul, b, ql, self.q8, self.q_descale, stream)
         if events:
             events[0].record(stream)
         mj_paged_decode(self.cfg, a, stream)
@@ -124,13 +139,13 @@ class DecodeStep:
     def plan_workload_device(self, wl, margin=0, stream=None) -> PlanInfo:
         return self.plan_device(wl.seq_lens_dev, wl.spec.b, wl.spec.q_len, wl.block_table.shape[1], margin, stream)
 
-    def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None):
+    def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None, fused=False):
         ks, vs = wl.kv_strides()
         return self.run(q=wl.q, k_cache=wl.k_pool, v_cache=wl.v_pool, k_strides=ks, v_strides=vs,
                         num_pages=wl.num_pages, block_table=wl.block_table, seq_lens=wl.seq_lens_dev,
                         k_descale=wl.k_descale, v_descale=wl.v_descale, descale_kind=wl.descale_kind,
                         softmax_scale=wl.softmax_scale, out=out, lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul,
-                        causal=wl.spec.causal, info=info, stream=stream, events=events)
+                        causal=wl.spec.causal, info=info, stream=stream, events=events, fused=fused)
 
 
 def new_output(wl, device=None):

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 1
+    assert mj.lib().mj_abi_version() == 2
 
 
 def _cfg(**kw):
@@ -37,10 +37,15 @@ def _cfg(**kw):
 
 
 def _oracle(cfg, lens, q_len, margin=0):
+    fmt = "e4m3" if cfg.kv_format == 0 else "e2m3"
+    wgs, mct = oplan.default_shape(fmt, q_len * (cfg.h_q // cfg.h_k))
+    kv_tile = cfg.kv_tile_tokens or 128
+    mct = cfg.min_chunk_tokens or mct
     return oplan.plan_split_kv(lens, q_len=q_len, h_q=cfg.h_q, h_k=cfg.h_k, num_cus=cfg.num_cus,
-                               wgs_per_cu=cfg.wgs_per_cu or 2, kv_tile=cfg.kv_tile_tokens or 128,
+                               wgs_per_cu=cfg.wgs_per_cu or wgs, kv_tile=kv_tile,
                                max_splits=cfg.max_splits, max_num_seqs=cfg.max_num_seqs,
-                               slots_override=cfg.slots_override, margin=margin)
+                               slots_override=cfg.slots_override, margin=margin,
+                               min_chunk_tiles=-(-mct // kv_tile))
 
 
 def _unpack(cfg, img, q_len):
@@ -65,6 +70,7 @@ def _compare(cfg, lens, q_len, margin=0):
     assert info.slots == ref["slots"]
     assert info.num_chunks == ref["num_chunks"]
     assert bool(info.with_reduction) == ref["with_reduction"]
+    return info
 
 
 @pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "32k"])
@@ -74,6 +80,10 @@ def test_planner_matches_oracle_on_workloads(key):
     lens = synth.workloads._lens(s, np.random.default_rng(s.seed))
     cfg = _cfg(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, max_q_len=s.q_len,
                slots_override=s.slots_override)
+    _compare(cfg, lens, s.q_len)
+    # the library's defaults (wgs_per_cu = min_chunk_tokens = 0)
+    cfg = _cfg(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, max_q_len=s.q_len,
+               slots_override=s.slots_override, wgs_per_cu=0, kv_format=s.kv_format)
     _compare(cfg, lens, s.q_len)
 
 
@@ -85,8 +95,10 @@ def test_planner_matches_oracle_random():
         mq = int(rng.integers(1, 6))
         cfg = _cfg(h_q=h_q, h_k=h_k, max_num_seqs=int(rng.integers(1, 100)), max_q_len=mq,
                    max_splits=int(rng.choice([1, 2, 4, 16, 32])), num_cus=int(rng.choice([20, 80, 256, 304])),
-                   wgs_per_cu=int(rng.integers(1, 5)), kv_tile_tokens=int(rng.choice([16, 64, 128, 256])),
-                   slots_override=int(rng.choice([0, 0, 0, 7, 300])))
+                   wgs_per_cu=int(rng.integers(0, 5)), kv_tile_tokens=int(rng.choice([16, 64, 128, 256])),
+                   slots_override=int(rng.choice([0, 0, 0, 7, 300])),
+                   min_chunk_tokens=int(rng.choice([0, 0, 1, 100, 2048, 9000])),
+                   kv_format=str(rng.choice(["e4m3", "e2m3"])))
         b = int(rng.integers(1, cfg.max_num_seqs + 1))
         lens = rng.integers(0, int(rng.choice([100, 5000, 200000])), size=b).tolist()
         _compare(cfg, lens, int(rng.integers(1, mq + 1)), int(rng.integers(0, 8)))

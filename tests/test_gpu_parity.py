@@ -26,16 +26,21 @@ def mj(gpu):
     return m
 
 
-def _run(mj, wl, **overrides):
+def _run(mj, wl, fused=False, **overrides):
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
     step = DecodeStep.for_workload(wl, **overrides)
     info = step.plan_workload(wl)
     out, lse = new_output(wl)
     out.fill_(float("nan"))
     lse.fill_(float("nan"))
-    step.run_workload(wl, out, lse, info=info)
+    step.run_workload(wl, out, lse, info=info, fused=fused)
     torch.cuda.synchronize()
     return out, lse, info
+
+
+# small workloads: KV-tile chunks (min_chunk_tokens=1) so that their short
+# sequences still split and every path of the merge runs
+FINE = dict(min_chunk_tokens=1)
 
 
 def test_code_decoders_exhaustive(mj, gpu):
@@ -120,7 +125,7 @@ def variant(mj, request):
 def test_parity_small_all_outputs(mj, gpu, key, variant):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
     say(f"parity {wl.spec.name} variant={variant} lens={wl.seq_lens}")
-    out, lse, info = _run(mj, wl)
+    out, lse, info = _run(mj, wl, **FINE)
     say(f"  plan: work={info.num_work} slots={info.slots} chunk_tiles={info.chunk_tiles} "
         f"reduction={info.with_reduction}")
     O, LSE = oracle_step(wl)
@@ -135,7 +140,7 @@ def test_split_and_unsplit_agree(mj, gpu, key, variant):
     say(f"splits {wl.spec.name}")
     O, LSE = oracle_step(wl)
     for ms, ovr in ((1, 0), (16, 0), (16, 64), (4, 200)):
-        out, lse, info = _run(mj, wl, max_splits=ms, slots_override=ovr)
+        out, lse, info = _run(mj, wl, max_splits=ms, slots_override=ovr, **FINE)
         say(f"  max_splits={ms} slots_override={ovr}: reduction={info.with_reduction} chunks={info.num_chunks}")
         compare_out(out, O, f"{wl.spec.name} ms={ms}")
         compare_lse(lse, LSE, f"{wl.spec.name} ms={ms}")
@@ -145,13 +150,13 @@ def test_split_and_unsplit_agree(mj, gpu, key, variant):
 def test_page_permutation_bit_identical(mj, gpu, variant):
     wl = synth.build(synth.spec_for("cfg3", small=True), gpu)
     say(f"permutation {wl.spec.name}")
-    out1, lse1, _ = _run(mj, wl)
+    out1, lse1, _ = _run(mj, wl, **FINE)
     perm = torch.randperm(wl.num_pages, generator=torch.Generator().manual_seed(3)).to(gpu)
     inv = torch.argsort(perm)
     wl.k_pool = wl.k_pool[perm].contiguous()
     wl.v_pool = wl.v_pool[perm].contiguous()
     wl.block_table = inv[wl.block_table.long()].to(torch.int32).contiguous()
-    out2, lse2, _ = _run(mj, wl)
+    out2, lse2, _ = _run(mj, wl, **FINE)
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse1, lse2)
 
@@ -162,13 +167,13 @@ def test_edge_lengths(mj, gpu, variant):
     # page, tile boundaries +-1, and causal rows that see no key (L < q_len)
     wl = synth.build(synth.spec_for("cfg4c", small=True, b=7, lens=(0, 1, 2, 127, 128, 129, 3001)), gpu)
     say(f"edges {wl.spec.name} lens={wl.seq_lens}")
-    out, lse, _ = _run(mj, wl)
+    out, lse, _ = _run(mj, wl, **FINE)
     O, LSE = oracle_step(wl)
     compare_out(out, O, "edges")
     compare_lse(lse, LSE, "edges")
     assert torch.all(out[:4].float() == 0)  # L = 0: every row empty
     wl = synth.build(synth.spec_for("cfg2", small=True, b=3, lens=(0, 1, 17)), gpu)
-    out, lse, _ = _run(mj, wl)
+    out, lse, _ = _run(mj, wl, **FINE)
     O, LSE = oracle_step(wl)
     compare_out(out, O, "edges q_len=1")
     compare_lse(lse, LSE, "edges q_len=1")
@@ -179,7 +184,7 @@ def test_edge_lengths(mj, gpu, variant):
         wl = synth.build(synth.spec_for("cfg2", small=True, b=len(lens), lens=lens, q_len=q_len, h_q=h_q, h_k=h_k,
                                         causal=causal, k_outliers=0), gpu)
         say(f"  edges q_len={q_len} h_q={h_q} h_k={h_k} causal={causal}")
-        out, lse, _ = _run(mj, wl)
+        out, lse, _ = _run(mj, wl, **FINE)
         O, LSE = oracle_step(wl)
         compare_out(out, O, f"edges q_len={q_len} causal={causal}")
         compare_lse(lse, LSE, f"edges q_len={q_len} causal={causal}")
@@ -188,7 +193,10 @@ def test_edge_lengths(mj, gpu, variant):
 def test_strided_q_view(mj, gpu):
     wl = synth.build(synth.spec_for("cfg2", small=True, q_extra_heads=16), gpu)
     say(f"strided Q {wl.spec.name} q.stride={wl.q.stride()}")
-    out, lse, _ = _run(mj, wl)
+    out, lse, _ = _run(mj, wl, **FINE)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, "strided q")
+    out, lse, _ = _run(mj, wl, fused=True, **FINE)
     O, LSE = oracle_step(wl)
     compare_out(out, O, "strided q")
 
@@ -197,7 +205,7 @@ def test_graph_replay_after_replanning(mj, gpu):
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
     wl = synth.build(synth.spec_for("cfg4c", small=True), gpu)
     say(f"graph replay {wl.spec.name}")
-    step = DecodeStep.for_workload(wl)
+    step = DecodeStep.for_workload(wl, **FINE)
     info = step.plan_workload(wl)
     out, lse = new_output(wl)
     s = torch.cuda.Stream()
@@ -232,12 +240,13 @@ FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "32k
 
 @pytest.mark.parametrize("key", list(FULL))
 def test_parity_full_size_sampled(mj, gpu, key, variant):
-    """Full-size workloads in the bench's launch configuration; the oracle
-    checks every output row of a few sampled (sequence, KV head) pairs."""
+    """Full-size workloads in the bench's launch configuration (default plan,
+    fused step); the oracle checks every output row of a few sampled
+    (sequence, KV head) pairs."""
     wl = synth.build(synth.spec_for(key), gpu)
     s = wl.spec
     say(f"full {s.name}: b={s.b} kv_bytes={wl.kv_bytes()}")
-    out, lse, info = _run(mj, wl)
+    out, lse, info = _run(mj, wl, fused=True)
     say(f"  plan: work={info.num_work} slots={info.slots} chunk_tiles={info.chunk_tiles} "
         f"reduction={info.with_reduction}")
     rng = np.random.default_rng(17)
@@ -286,7 +295,7 @@ def test_graph_replay_with_device_plan(mj, gpu):
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
     wl = synth.build(synth.spec_for("cfg2", small=True), gpu)
     say(f"graph+device plan {wl.spec.name}")
-    step = DecodeStep.for_workload(wl)
+    step = DecodeStep.for_workload(wl, **FINE)
     out, lse = new_output(wl)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -313,3 +322,74 @@ def test_graph_replay_with_device_plan(mj, gpu):
         O, LSE = oracle_step(wl)
         compare_out(out, O, f"device-plan replay {trial} lens={lens}")
         compare_lse(lse, LSE, f"device-plan replay {trial}")
+
+
+@pytest.mark.parametrize("variant", [0, 1], indirect=True)
+@pytest.mark.parametrize("key", SMALL_KEYS)
+def test_fused_step_matches_three_calls(mj, gpu, key, variant):
+    """mj_decode_step (one launch: in-kernel Q quantization, last-split merge)
+    gives the three-call path's outputs bit for bit, call after call (a
+    counter left non-zero would skip the next call's merge and leave NaN
+    rows), with default and fine splits; with the
+    generic kernel (variant 1) it is the three-call fallback."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    say(f"fused {wl.spec.name} variant={variant} lens={wl.seq_lens}")
+    for mct in (0, 1):
+        step = DecodeStep.for_workload(wl, min_chunk_tokens=mct)
+        info = step.plan_workload(wl)
+        say(f"  min_chunk_tokens={mct}: chunks={info.num_chunks} reduction={info.with_reduction}")
+        ref_o, ref_l = new_output(wl)
+        step.run_workload(wl, ref_o, ref_l, info=info)
+        out, lse = new_output(wl)
+        for rep in range(3):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            step.run_workload(wl, out, lse, info=info, fused=True)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"mct={mct} rep={rep}"
+            assert torch.equal(lse, ref_l), f"mct={mct} rep={rep}"
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, f"fused {wl.spec.name}")
+    compare_lse(lse, LSE, f"fused {wl.spec.name}")
+
+
+def test_fused_step_graph_replay(mj, gpu):
+    """plan (device) + fused step captured once; replays with new device
+    lengths match the oracle and the eager fused step, replay after replay."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for("cfg3", small=True), gpu)
+    say(f"fused graph {wl.spec.name}")
+    step = DecodeStep.for_workload(wl, **FINE)
+    out, lse = new_output(wl)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        info = step.plan_workload_device(wl)
+        step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        info = step.plan_workload_device(wl)
+        step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.synchronize()
+    orig = list(wl.seq_lens)
+    rng = np.random.default_rng(12)
+    eager_o, eager_l = new_output(wl)
+    for trial in range(5):
+        lens = [int(x) for x in rng.integers(0, np.array(orig) + 1)]
+        wl.seq_lens = lens
+        wl.seq_lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step.plan_workload_device(wl)
+        step.run_workload(wl, eager_o, eager_l, info=info, fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager_o.view(torch.int16)), f"replay {trial}"
+        assert torch.equal(lse, eager_l), f"replay {trial}"
+        O, LSE = oracle_step(wl)
+        compare_out(out, O, f"fused replay {trial} lens={lens}")
+        compare_lse(lse, LSE, f"fused replay {trial}")

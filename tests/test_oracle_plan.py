@@ -45,6 +45,21 @@ def test_mi355_workload_plans(args, expect):
     assert int(p["with_reduction"]) == expect[4], name
 
 
+@pytest.mark.parametrize("args,expect", _golden("mi355d"))
+def test_mi355_default_plans(args, expect):
+    name = args[0]
+    b, h_q, h_k, q_len, L = (int(x) for x in args[1:6])
+    fmt = args[6]
+    wgs, mct = P.default_shape(fmt, q_len * (h_q // h_k))
+    p = P.plan_split_kv([L] * b, q_len=q_len, h_q=h_q, h_k=h_k, num_cus=256, wgs_per_cu=wgs, kv_tile=128,
+                        max_splits=16, max_num_seqs=b, min_chunk_tiles=-(-mct // 128))
+    assert p["slots"] == expect[0], name
+    assert p["chunk_tiles"] == expect[1], name
+    assert p["n_splits"] == [expect[2]] * b, name
+    assert sum(1 for w in p["work"] if w[0] >= 0) == expect[3], name
+    assert int(p["with_reduction"]) == expect[4], name
+
+
 def _check_invariants(p, lens, kv_tile, max_splits, S, cap, margin=0):
     tiles = [math.ceil((L + margin) / kv_tile) for L in lens]
     assert p["num_work"] == cap == len(p["work"])
@@ -87,6 +102,15 @@ def test_brute_force_minimal_chunk():
                 if sum(max(1, math.ceil(t / c)) for t in tiles) <= S and max(math.ceil(t / c) for t in tiles) <= ms]
         assert p["chunk_tiles"] == min(feas)
         _check_invariants(p, lens, kv, ms, S, max(S, b))
+        # with a floor on the chunk: the smallest feasible chunk at or above it
+        floor = int(rng.integers(1, 40))
+        q = P.plan_split_kv(lens, q_len=1, h_q=8, h_k=1, num_cus=1, wgs_per_cu=1, kv_tile=kv, max_splits=ms,
+                            max_num_seqs=b, slots_override=S, min_chunk_tiles=floor)
+        top = max(floor, max(1, max(tiles)))
+        feas = [c for c in range(floor, top + 1)
+                if sum(max(1, math.ceil(t / c)) for t in tiles) <= S and max(math.ceil(t / c) for t in tiles) <= ms]
+        assert q["chunk_tiles"] == min(feas)
+        _check_invariants(q, lens, kv, ms, S, max(S, b))
 
 
 def test_invariants_and_fixed_grid():
