@@ -37,11 +37,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# HBM traffic of the decode kernel from rocprofv3 --pmc (FETCH_SIZE and
-# WRITE_SIZE per dispatch, KiB), scaled by the same counters on a plain copy
-# kernel of known size.  Filled in from the committed profile summaries when
-# they describe the kernel as it is now; None otherwise.
-TRAFFIC = {}
+# HBM traffic of the decode kernel per launch from rocprofv3 --pmc
+# (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what the same counters
+# read for a 256 MiB copy: fetch x 1.99980, write x 1.000), as recorded in
+# profiles/decode_mfma_kernel_hbm_traffic.md.  Reported only while the
+# kernel sources hash to the value the counters were taken with.
+TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
+TRAFFIC = {
+    "sources_sha256_16": "2615ad167cef8475",
+    "cfg2": dict(fetch_bytes=270358895, write_bytes=1391318),
+    "32k": dict(fetch_bytes=4306562111, write_bytes=5152162),
+}
+
+
+def traffic_for(key):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "paged_fp8_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != TRAFFIC["sources_sha256_16"] or key not in TRAFFIC:
+        return None
+    t = TRAFFIC[key]
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def log(*a):
@@ -62,7 +80,27 @@ def parse():
     ap.add_argument("--no-nt", action="store_true", help="plain (not non-temporal) KV loads (A/B runs)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner workgroups per CU (0 = library default)")
     ap.add_argument("--stream-read", action="store_true", help="also time a plain streaming read of the KV pool")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run the HBM-counter calibration kernels (256 MiB streaming read, 256 MiB copy) and exit")
     return ap.parse_args()
+
+
+def calibrate():
+    """Kernels of known traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE:
+    the library's plain streaming read of 256 MiB (reads 256 MiB, writes one
+    word per workgroup) and a torch copy of 256 MiB (reads and writes 256 MiB
+    each)."""
+    import torch
+    import paged_fp8_decode_amd as mjlib
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    chk = torch.empty(4096, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        mjlib.mj_debug_stream_read(src, chk, 2048)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(calibration=True, stream_read_bytes=n, copy_bytes=n)), flush=True)
 
 
 def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
@@ -265,6 +303,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import paged_fp8_decode_amd
 
+    if args.calibrate:
+        calibrate()
+        return
+
     paged_fp8_decode_amd.mj_debug_set_decode_variant(args.variant, 0 if args.no_nt else 1)
 
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
@@ -277,9 +319,10 @@ def main():
     kvb = main_res["kv_bytes"]
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6
     roof = dict(bound="hbm", achieved=round(kvb / dec_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(kvb / dec_s / 1e9 / HBM_PEAK_GBS, 4), traffic=TRAFFIC.get(args.workload),
+                frac=round(kvb / dec_s / 1e9 / HBM_PEAK_GBS, 4), traffic=traffic_for(args.workload),
                 kernel="decode_mfma_kernel (mj_decode_step: Q quantization + paged decode + LSE merge)",
-                algorithmic_bytes_per_launch=kvb, kernel_us=round(main_res["kernel_us_back_to_back"], 2))
+                algorithmic_bytes_per_launch=kvb, kernel_us=round(main_res["kernel_us_back_to_back"], 2),
+                traffic_unit="bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)")
     line = dict(
         metric="paged decode us/step and achieved KV-read HBM GB/s (% of MI355X peak)",
         value=round(main_res["graph_step_kv_gbs"], 1),
