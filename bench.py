@@ -44,19 +44,29 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "2615ad167cef8475",
+    "sources_sha256_16": "d935879d23604147",
     "cfg2": dict(fetch_bytes=270358895, write_bytes=1391318),
     "32k": dict(fetch_bytes=4306562111, write_bytes=5152162),
 }
 
 
-def traffic_for(key):
+def kernel_sources_hash():
+    """sha256[:16] of the decode kernel's sources with // comments and blank
+    lines removed (a comment edit does not change the kernel)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "paged_fp8_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest()[:16] != TRAFFIC["sources_sha256_16"] or key not in TRAFFIC:
+        with open(os.path.join(ROOT, "paged_fp8_decode_amd", "csrc", f)) as fh:
+            for line in fh:
+                line = re.sub(r"//.*", "", line).strip()
+                if line:
+                    h.update(line.encode() + b"\n")
+    return h.hexdigest()[:16]
+
+
+def traffic_for(key):
+    if kernel_sources_hash() != TRAFFIC["sources_sha256_16"] or key not in TRAFFIC:
         return None
     t = TRAFFIC[key]
     return t["fetch_bytes"] + t["write_bytes"]

@@ -1,5 +1,13 @@
-// Paged decode for GQA groups of up to 4 query rows (q_len * h_r <= 4) with
-// both products on the gfx950 matrix cores; e4m3 or packed-e2m3 KV.
+// Paged decode for GQA groups of up to 32 query rows (q_len * h_r <= 32)
+// with both products on the gfx950 matrix cores; e4m3 or packed-e2m3 KV.
+// The description below is for the 4-row instance; 8- and 16-row groups use
+// one 16-row block (column n = row n), 32-row groups two blocks, with the
+// same operand layouts per block and the max raised wave-uniformly.
+//
+// Fused step (mj_decode_step): the prologue quantizes the pair's Q rows into
+// LDS with the stand-alone quantize kernel's arithmetic, and after writing
+// its split partials (device-coherent stores) the last split item of a
+// (sequence, KV head) to arrive merges them (mj_merge.h).
 //
 // Method: mjolnir-kernel README "What it does", step 3 (stream KV pages,
 // online softmax) and the partials step 4 merges.  The pages' Thor design
