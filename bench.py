@@ -13,8 +13,9 @@ step (KV bytes / mean graph step time); ``detail`` also has the eager step
 (host planner + fused step) and the eager three-call step (quantize, decode,
 merge as separate launches).  The ``roofline`` object is the fused decode
 kernel's own bandwidth against the 8 TB/s HBM peak, its duration taken with
-one event pair around back-to-back launches that rotate over copies of the
-KV pools (no launch reads KV the Infinity Cache still holds).
+one event pair around back-to-back single-launch steps (merge in the decode
+kernel) that rotate over copies of the KV pools (no launch reads KV the
+Infinity Cache still holds).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.
 
@@ -33,6 +34,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+STEP_MERGE = 0  # mj_decode_step merge mode of the timed steps (--step-merge)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -44,9 +46,9 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "d935879d23604147",
-    "cfg2": dict(fetch_bytes=270358895, write_bytes=1391318),
-    "32k": dict(fetch_bytes=4306562111, write_bytes=5152162),
+    "sources_sha256_16": "77068e6439adafb5",
+    "cfg2": dict(fetch_bytes=269706413, write_bytes=1179648),
+    "32k": dict(fetch_bytes=4304903424, write_bytes=4718592),
 }
 
 
@@ -90,6 +92,8 @@ def parse():
     ap.add_argument("--no-nt", action="store_true", help="plain (not non-temporal) KV loads (A/B runs)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner workgroups per CU (0 = library default)")
     ap.add_argument("--stream-read", action="store_true", help="also time a plain streaming read of the KV pool")
+    ap.add_argument("--step-merge", type=int, default=0,
+                    help="mj_decode_step merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the HBM-counter calibration kernels (256 MiB streaming read, 256 MiB copy) and exit")
     return ap.parse_args()
@@ -154,6 +158,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     eager(max(3, warmup // 2), False, False)
     ev3 = eager(max(5, steps // 2), False, True)
     step3_ms = np.array([e[0].elapsed_time(e[3]) for e in ev3])
+    dec3_ms = np.array([e[1].elapsed_time(e[2]) for e in ev3])
 
     # the step as one hipGraph: device-side plan + fused step
     side = torch.cuda.Stream()
@@ -182,10 +187,11 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     graph_ms = np.array([a.elapsed_time(b) for a, b in gev])
     del graph
 
-    # kernel duration for the roofline: the fused decode kernel launched back
-    # to back, rotating over copies of the KV pools so that no launch finds
-    # the previous one's KV in the 256 MB Infinity Cache (>= 1 GiB of
-    # distinct KV between reuses); one event pair over all launches
+    # kernel duration for the roofline: the fused step as one launch (the
+    # split partials merged by the decode kernel's last split item), back to
+    # back, rotating over copies of the KV pools so that no launch finds the
+    # previous one's KV in the 256 MB Infinity Cache (>= 1 GiB of distinct KV
+    # between reuses); one event pair over all launches
     kvb = wl.kv_bytes()
     n_copies = max(1, -(-(1 << 30) // kvb))
     pools = [(wl.k_pool, wl.v_pool)] + [(wl.k_pool.clone(), wl.v_pool.clone()) for _ in range(n_copies - 1)]
@@ -200,16 +206,22 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
                  lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul, causal=wl.spec.causal, info=info, stream=stream,
                  fused=True)
 
+    import paged_fp8_decode_amd as mjlib
     step.plan_workload(wl, stream=stream)
-    for i in range(len(pools)):
-        launch(i)
     torch.cuda.synchronize()
-    k0, k1 = E(), E()
-    k0.record(stream)
-    for i in range(reps):
-        launch(i)
-    k1.record(stream)
-    torch.cuda.synchronize()
+    mjlib.mj_debug_set_step_merge(1)
+    try:
+        for i in range(len(pools)):
+            launch(i)
+        torch.cuda.synchronize()
+        k0, k1 = E(), E()
+        k0.record(stream)
+        for i in range(reps):
+            launch(i)
+        k1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        mjlib.mj_debug_set_step_merge(STEP_MERGE)
     kernel_us = k0.elapsed_time(k1) * 1e3 / reps
     del pools
 
@@ -220,6 +232,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
         us_per_step_p90=float(np.percentile(step_ms, 90) * 1e3),
         step_decode_us_mean=float(dec_ms.mean() * 1e3), step_decode_us_median=float(np.median(dec_ms) * 1e3),
         three_call_us_per_step_median=float(np.median(step3_ms) * 1e3),
+        three_call_decode_us_median=float(np.median(dec3_ms) * 1e3),
         graph_us_per_step_median=float(np.median(graph_ms) * 1e3),
         graph_us_per_step_mean=float(graph_ms.mean() * 1e3),
         graph_us_per_step_p10=float(np.percentile(graph_ms, 10) * 1e3),
@@ -253,7 +266,8 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     log(f"[bench] {key}: step {res['graph_us_per_step_median']:.1f} us graph / {res['us_per_step_median']:.1f} us "
         f"eager / {res['three_call_us_per_step_median']:.1f} us three calls (median); decode kernel "
         f"{kernel_us:.1f} us = {res['kernel_kv_gbs']:.0f} GB/s KV ({100 * res['kernel_frac_of_hbm_peak']:.1f}% "
-        f"of 8 TB/s); in-step decode {res['step_decode_us_mean']:.1f} us")
+        f"of 8 TB/s); in-step decode {res['step_decode_us_mean']:.1f} us fused / "
+        f"{res['three_call_decode_us_median']:.1f} us unfused")
     del wl
     torch.cuda.empty_cache()
     return res
@@ -318,6 +332,9 @@ def main():
         return
 
     paged_fp8_decode_amd.mj_debug_set_decode_variant(args.variant, 0 if args.no_nt else 1)
+    global STEP_MERGE
+    STEP_MERGE = args.step_merge
+    paged_fp8_decode_amd.mj_debug_set_step_merge(args.step_merge)
 
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
     main_res = measure(args.workload, args.steps, args.warmup, flush_buf, args.wgs_per_cu, args.stream_read)
@@ -330,7 +347,7 @@ def main():
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6
     roof = dict(bound="hbm", achieved=round(kvb / dec_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(kvb / dec_s / 1e9 / HBM_PEAK_GBS, 4), traffic=traffic_for(args.workload),
-                kernel="decode_mfma_kernel (mj_decode_step: Q quantization + paged decode + LSE merge)",
+                kernel="decode_mfma_kernel (mj_decode_step as one launch: Q quantization + paged decode + LSE merge)",
                 algorithmic_bytes_per_launch=kvb, kernel_us=round(main_res["kernel_us_back_to_back"], 2),
                 traffic_unit="bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)")
     line = dict(
@@ -348,7 +365,8 @@ def main():
         dtype="e4m3" if "e2m3" not in main_res["workload"] else "e2m3",
         data="synthetic",
         config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"], kernel_variant=args.variant,
-                    nontemporal=not args.no_nt, step="hipGraph: device plan + mj_decode_step"),
+                    nontemporal=not args.no_nt, step_merge=args.step_merge,
+                    step="hipGraph: device plan + mj_decode_step"),
         roofline=roof,
         cpu_baseline=cpu,
         detail=main_res,

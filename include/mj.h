@@ -284,12 +284,14 @@ typedef struct mj_step_args {
 /* mj_quantize_q + mj_paged_decode + mj_merge_lse (README "What it does",
  * steps 2-4) as one call with the same results bit for bit.  Where the
  * matrix-core kernel serves the shape (q_len*h_r <= 32, whole 16-token
- * tiles, slot strides < 2^24 bytes) it is ONE kernel launch: every
- * workgroup quantizes its (sequence, KV head)'s Q rows in its prologue with
- * the quantize kernel's arithmetic, and the last split item of a split
- * (sequence, KV head) to finish merges the partials (agent-scope release /
- * acquire around an arrival counter in the workspace).  Otherwise it
- * enqueues the three kernels, staging Q codes in the workspace.  Calls that
+ * tiles, slot strides < 2^24 bytes), every decode workgroup quantizes its
+ * (sequence, KV head)'s Q rows in its prologue with the quantize kernel's
+ * arithmetic, so the step is the decode launch plus, for a split plan, the
+ * merge launch; optionally (mj_debug_set_step_merge) the last split item of
+ * a pair to finish merges in the decode kernel itself (device-coherent
+ * partials, an arrival counter in the workspace) and the step is one
+ * launch.  Otherwise it enqueues the three kernels, staging Q codes in the
+ * workspace.  Calls that
  * share a workspace must not overlap (one stream, or ordered streams).
  * Errors: those of the three calls. */
 mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStream_t stream);
@@ -314,6 +316,11 @@ mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t
  * kernels' KV loads non-temporal.  Not thread-safe; set it before
  * launching.  EINVAL on other values. */
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal);
+/* Where mj_decode_step merges split partials when it fuses the step: 0 =
+ * automatic (currently the separate launch), 1 = in the decode kernel (last
+ * split item), 2 = a separate merge launch after it.  Results are
+ * identical.  Process-wide, not thread-safe.  EINVAL on other values. */
+mj_status mj_debug_set_step_merge(int32_t mode);
 /* Plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
  * non-temporal 16-byte loads by `blocks` workgroups of 256 threads, each
  * writing one xor checksum to out[block]: the practical HBM read ceiling the

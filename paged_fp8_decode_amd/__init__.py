@@ -133,6 +133,10 @@ def mj_debug_set_decode_variant(variant: int, nontemporal: int = 1):
     check(lib().mj_debug_set_decode_variant(variant, nontemporal), "mj_debug_set_decode_variant")
 
 
+def mj_debug_set_step_merge(mode: int):
+    check(lib().mj_debug_set_step_merge(mode), "mj_debug_set_step_merge")
+
+
 def mj_debug_stream_read(src, out, blocks: int, stream=None):
     """src: any contiguous device tensor; out: uint32/int32 device tensor with >= blocks elements."""
     nbytes = src.numel() * src.element_size()

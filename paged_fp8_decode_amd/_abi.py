@@ -90,6 +90,7 @@ def _load():
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
         "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),
         "mj_debug_stream_read": (_i32, [_p, _i64, _p, _i32, _p]),
+        "mj_debug_set_step_merge": (_i32, [_i32]),
     }
     for name, (res, args) in sigs.items():
         if not hasattr(lib, name):

@@ -112,6 +112,15 @@ __device__ __forceinline__ float sum_jj(float x) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Keeps the scheduler from hoisting the next granule's computation above the
+// loads just issued: the wait before that computation then leaves the new
+// loads in flight instead of draining every load.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// 2^x with the hardware instruction alone: arguments are <= 0 (a logit
+// minus a running max at least as large) or -inf, and results below the
+// smallest normal flush to 0, which no sum of probabilities can see.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // two fp32 -> one word of two bf16 (round to nearest even; exact for KV values)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const v2bf v = {(__bf16)lo, (__bf16)hi};
@@ -137,7 +146,9 @@ struct Ctx {
 // Page of the tile starting at token tk (wave-uniform), or -1 if the tile is
 // past the range end or its block-table entry is out of range.
 __device__ __forceinline__ int tile_page(const Ctx& c, int tk) {
-  const int idx = min(tk, c.j1 - 1);  // a granule exists only when j1 > j0
+  // clamped into [0, j1 - 1]; entry 0 of a block-table row always exists
+  // (at least one column), so an empty range reads it and stays dead
+  const int idx = max(min(tk, c.j1 - 1), 0);
   const int pg = c.bt_row[idx >> c.page_shift];
   // all-ones when the tile is live; bit operations keep the block-table
   // load out of any branch
@@ -302,16 +313,24 @@ __device__ __forceinline__ void granule(const Ctx& c, const v8i (&qb)[NRB], cons
     const int tk = t0 + 16 * k;
     // tokens at or past `end` are masked; a dead tile masks all of them
     const int end = tile_page(c, tk) >= 0 ? c.j1 : 0;  // scalar; the block-table entry is cached
+    // wave-uniform: every token of the tile visible to every row (row 0 of a
+    // causal block sees the fewest keys)
+    const bool full = tk + 16 <= end && (!c.causal || tk + 15 <= c.lim0);
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
       const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
       const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[R], zero, 0, 0, 0, kE8m0One, 0,
                                                                       kE8m0One);
+      if (full) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = tk + 4 * c.jj + v;
-        const bool vis = t < end && (!c.causal || t <= c.lim0 + row_tok[R]);
-        s[R][k][v] = vis ? d[v] * c.cscale : -INFINITY;
+        for (int v = 0; v < 4; ++v) s[R][k][v] = d[v] * c.cscale;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = tk + 4 * c.jj + v;
+          const bool vis = t < end && (!c.causal || t <= c.lim0 + row_tok[R]);
+          s[R][k][v] = vis ? d[v] * c.cscale : -INFINITY;
+        }
       }
     }
   }
@@ -371,7 +390,7 @@ __device__ __forceinline__ void granule(const Ctx& c, const v8i (&qb)[NRB], cons
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        p[4 * k + v] = exp2f(s[R][k][v] - ms);
+        p[4 * k + v] = exp2_fast(s[R][k][v] - ms);
         st.l[R] += p[4 * k + v];
       }
     u32x4 pw;  // element e = 4k + v, token pairs per word
@@ -440,23 +459,58 @@ void decode_mfma_kernel(DecodeParams p) {
   c.num_pages = (uint32_t)min<int64_t>(p.num_pages, 0x7FFFFFFF);
   c.page_shift = p.page_shift;
   c.pmask = p.page_size - 1;
+
+  // fused step: fetch this thread's Q words first, then issue the ring's
+  // first granules, so that the quantization below (two barriers) waits only
+  // on the Q loads (loads retire in issue order) while the KV loads fly
+  constexpr int kQV = (kRows * 16 + kThreads - 1) / kThreads;  // 8-channel vectors per thread
+  const int nvec = p.n_q * 16;
+  QRaw8 qr[kQV];
+  // unfused: the pre-quantized rows' words, fetched before the KV loads too
+  // (clamped rows load a valid row and are zeroed below)
+  u32x4 qg[NRB][2];
+  if (!p.qb) {
+#pragma unroll
+    for (int R = 0; R < NRB; ++R) {
+      const int r = min(16 * R + (n % NQB), p.n_q - 1);
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim + 32 * jj);
+      qg[R][0] = src[0];
+      qg[R][1] = src[1];
+    }
+  }
+  if (p.qb) {
+#pragma unroll
+    for (int k = 0; k < kQV; ++k) {
+      const int v = min((int)threadIdx.x + k * kThreads, nvec - 1);  // a repeat changes no max
+      qr[k] = q_fetch8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, v >> 4, (v & 15) * 8);
+    }
+  }
+
+  // the ring's first granules, issued unconditionally (a wave with no
+  // granule loads a dead tile, i.e. zeros) so that the wait counts stay static
+  const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
+  int gi = wave;
+  const bool run = gi < ngr;
+  KRows<FMT> K0 = load_k<FMT, NT>(c, gi), K1;
+  VRows V0 = load_v<NT>(c, gi), V1;
+  if constexpr (PF == 2) {
+    K1 = load_k<FMT, NT>(c, gi + kWaves);
+    V1 = load_v<NT>(c, gi + kWaves);
+  }
+
   float qdesc;
   if (p.qb) {
     // fused step: quantize this (sequence, KV head)'s Q rows here, with the
     // arithmetic of the stand-alone quantize kernel (every split item of the
     // pair derives the same codes and scale)
-    constexpr int kQV = (kRows * 16 + kThreads - 1) / kThreads;  // 8-channel vectors per thread
-    const int nvec = p.n_q * 16;
     float x[kQV][8];
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
-      const int v = threadIdx.x + k * kThreads;
-      if (v < nvec) {
-        q_load8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, v >> 4, (v & 15) * 8, x[k]);
+      q_convert8(qr[k], p.q_mul != nullptr, x[k]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
-      }
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -486,10 +540,14 @@ void decode_mfma_kernel(DecodeParams p) {
     const int r = 16 * R + (n % NQB);
     row_tok[R] = r / p.h_r;
     if (r < p.n_q) {
-      const u32x4* src =
-          p.qb ? reinterpret_cast<const u32x4*>(&q_s[r][32 * jj])
-               : reinterpret_cast<const u32x4*>(p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim + 32 * jj);
-      const u32x4 a = src[0], b = src[1];
+      u32x4 a, b;
+      if (p.qb) {  // LDS reads of the codes quantized above
+        a = *reinterpret_cast<const u32x4*>(&q_s[r][32 * jj]);
+        b = *reinterpret_cast<const u32x4*>(&q_s[r][32 * jj + 16]);
+      } else {
+        a = qg[R][0];
+        b = qg[R][1];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         qb[R][i] = (int)a[i];
@@ -510,41 +568,40 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int q = 0; q < 8; ++q) st.acc[R][q] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
-  int gi = wave;
-  if (gi < ngr) {
+  if (run) {
     // register ring of PF + 1 granules, rotated by unrolling
     if constexpr (PF == 1) {
-      KRows<FMT> KA = load_k<FMT, NT>(c, gi);
-      VRows VA = load_v<NT>(c, gi);
       while (true) {
-        KRows<FMT> KB = load_k<FMT, NT>(c, gi + kWaves);
-        VRows VB = load_v<NT>(c, gi + kWaves);
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KA, VA, st);
+        K1 = load_k<FMT, NT>(c, gi + kWaves);
+        V1 = load_v<NT>(c, gi + kWaves);
+        issue_fence();
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K0, V0, st);
         gi += kWaves;
         if (gi >= ngr) break;
-        KA = load_k<FMT, NT>(c, gi + kWaves);
-        VA = load_v<NT>(c, gi + kWaves);
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, KB, VB, st);
+        K0 = load_k<FMT, NT>(c, gi + kWaves);
+        V0 = load_v<NT>(c, gi + kWaves);
+        issue_fence();
+        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K1, V1, st);
         gi += kWaves;
         if (gi >= ngr) break;
       }
     } else {
-      KRows<FMT> K0 = load_k<FMT, NT>(c, gi), K1 = load_k<FMT, NT>(c, gi + kWaves);
-      VRows V0 = load_v<NT>(c, gi), V1 = load_v<NT>(c, gi + kWaves);
       while (true) {
         KRows<FMT> K2 = load_k<FMT, NT>(c, gi + 2 * kWaves);
         VRows V2 = load_v<NT>(c, gi + 2 * kWaves);
+        issue_fence();
         granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K0, V0, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K0 = load_k<FMT, NT>(c, gi + 2 * kWaves);
         V0 = load_v<NT>(c, gi + 2 * kWaves);
+        issue_fence();
         granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K1, V1, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K1 = load_k<FMT, NT>(c, gi + 2 * kWaves);
         V1 = load_v<NT>(c, gi + 2 * kWaves);
+        issue_fence();
         granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K2, V2, st);
         gi += kWaves;
         if (gi >= ngr) break;
@@ -656,18 +713,18 @@ hipError_t launch_shape(const DecodeParams& p, bool nt, hipStream_t s) {
 
 template <int FMT>
 hipError_t launch_fmt(const DecodeParams& p, bool nt, int tune, hipStream_t s) {
-  if (p.n_q <= 4)  // tune bit 1: two granules of prefetch instead of one
-    return (tune & 2) ? launch_shape<FMT, 4, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
-  if (p.n_q <= 8) return launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
-  if (p.n_q <= 16) return launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
-  return launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
+  const bool pf2 = tune & 2;  // two granules of prefetch instead of one
+  if (p.n_q <= 4) return pf2 ? launch_shape<FMT, 4, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
+  if (p.n_q <= 8) return pf2 ? launch_shape<FMT, 8, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
+  if (p.n_q <= 16) return pf2 ? launch_shape<FMT, 16, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
+  return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
 }
 
 }  // namespace
 
 bool decode_mfma_supports(int n_q) { return n_q >= 1 && n_q <= 32; }
 
-// tune bits: 1 = two granules of prefetch (4-row groups), 2 = head-major grid
+// tune bits: 1 = two granules of prefetch, 2 = head-major grid
 hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, bool nontemporal, int tune, hipStream_t s) {
   DecodeParams p = p_in;
   p.head_major = (tune & 2) ? 1 : 0;

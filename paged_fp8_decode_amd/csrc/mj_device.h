@@ -103,24 +103,45 @@ namespace mj {
 constexpr float kQAmaxFloor = 1e-6f;
 constexpr float kFp8Max = 448.0f;
 
-// Channels [c0, c0 + 8) of packed row `row` of (seq, g) as fp32.
-__device__ __forceinline__ void q_load8(const uint16_t* q, int64_t q_ts, int64_t q_hs, const float* q_mul, int q_len,
-                                        int h_r, int seq, int g, int row, int c0, float x[8]) {
+// Raw bf16 words and multipliers of channels [c0, c0 + 8) of packed row
+// `row` of (seq, g); without q_mul the multiplier words are read from Q
+// itself (a valid address) and ignored, so the fetch has no branch.
+struct QRaw8 {
+  uint4 q;
+  float4 m0, m1;
+};
+
+__device__ __forceinline__ QRaw8 q_fetch8(const uint16_t* q, int64_t q_ts, int64_t q_hs, const float* q_mul,
+                                          int q_len, int h_r, int seq, int g, int row, int c0) {
   const int t = row / h_r;
   const int h = g * h_r + (row - t * h_r);
-  const uint4 raw = *reinterpret_cast<const uint4*>(q + ((int64_t)seq * q_len + t) * q_ts + (int64_t)h * q_hs + c0);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  const uint16_t* src = q + ((int64_t)seq * q_len + t) * q_ts + (int64_t)h * q_hs + c0;
+  QRaw8 r;
+  r.q = *reinterpret_cast<const uint4*>(src);
+  const float* m = q_mul ? q_mul + (int64_t)h * kHeadDim + c0 : reinterpret_cast<const float*>(src);
+  r.m0 = *reinterpret_cast<const float4*>(m);
+  r.m1 = *reinterpret_cast<const float4*>(q_mul ? m + 4 : m);
+  return r;
+}
+
+// The eight values as fp32: x = fp32(q) [* q_mul] (one multiply each).
+__device__ __forceinline__ void q_convert8(const QRaw8& r, bool has_mul, float x[8]) {
+  const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     x[2 * e] = __uint_as_float(w[e] << 16);
     x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
   }
-  if (q_mul) {
-    const float4 m0 = *reinterpret_cast<const float4*>(q_mul + (int64_t)h * kHeadDim + c0);
-    const float4 m1 = *reinterpret_cast<const float4*>(q_mul + (int64_t)h * kHeadDim + c0 + 4);
-    x[0] *= m0.x; x[1] *= m0.y; x[2] *= m0.z; x[3] *= m0.w;
-    x[4] *= m1.x; x[5] *= m1.y; x[6] *= m1.z; x[7] *= m1.w;
+  if (has_mul) {
+    x[0] *= r.m0.x; x[1] *= r.m0.y; x[2] *= r.m0.z; x[3] *= r.m0.w;
+    x[4] *= r.m1.x; x[5] *= r.m1.y; x[6] *= r.m1.z; x[7] *= r.m1.w;
   }
+}
+
+// Channels [c0, c0 + 8) of packed row `row` of (seq, g) as fp32.
+__device__ __forceinline__ void q_load8(const uint16_t* q, int64_t q_ts, int64_t q_hs, const float* q_mul, int q_len,
+                                        int h_r, int seq, int g, int row, int c0, float x[8]) {
+  q_convert8(q_fetch8(q, q_ts, q_hs, q_mul, q_len, h_r, seq, g, row, c0), q_mul != nullptr, x);
 }
 
 __device__ __forceinline__ float q_scale_from_amax(float amax) { return fmaxf(amax, kQAmaxFloor) / kFp8Max; }

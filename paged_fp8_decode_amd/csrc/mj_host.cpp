@@ -413,6 +413,15 @@ mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* a, hipStre
   return mj::launch_decode(p, cfg->kv_format, row_tiles(cfg, a->q_len), stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
+// Where a fused step merges: 0 automatic, 1 in the decode kernel (the last
+// split item of a pair), 2 a separate merge launch.  Automatic is the
+// separate launch: the in-kernel merge makes every split workgroup wait for
+// its write-through stores and a returning atomic before it retires, which
+// costs more than the launch once a plan takes several rounds of workgroups
+// (measured: 32k context -10 us, ragged batch -12 us per step; a single
+// short sequence +1.4 us).
+static int g_step_merge = 0;
+
 mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream_t stream) {
   Derived d;
   mj_status st = derive(cfg, &d);
@@ -433,18 +442,6 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   st = fill_decode(cfg, d, &a, &p);
   if (st != MJ_OK) return st;
   const int rt = row_tiles(cfg, a.q_len);
-  if (mj::decode_fuses_step(p, cfg->kv_format, rt)) {
-    p.qb = static_cast<const uint16_t*>(sa->q);
-    p.qb_ts = sa->q_tok_stride;
-    p.qb_hs = sa->q_head_stride;
-    p.q_mul = sa->q_mul;
-    p.counters = a.with_reduction ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
-    return mj::launch_decode(p, cfg->kv_format, rt, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
-  }
-  st = mj_quantize_q(cfg, sa->q, sa->q_tok_stride, sa->q_head_stride, sa->q_mul, a.num_seqs, a.q_len, q8, qd, stream);
-  if (st != MJ_OK) return st;
-  if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
-  if (!a.with_reduction) return MJ_OK;
   mj_merge_args m;
   m.plan = a.plan;
   m.num_seqs = a.num_seqs;
@@ -455,7 +452,26 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   m.out_tok_stride = a.out_tok_stride;
   m.out_head_stride = a.out_head_stride;
   m.lse = a.lse;
-  return mj_merge_lse(cfg, &m, stream);
+  if (mj::decode_fuses_step(p, cfg->kv_format, rt)) {
+    p.qb = static_cast<const uint16_t*>(sa->q);
+    p.qb_ts = sa->q_tok_stride;
+    p.qb_hs = sa->q_head_stride;
+    p.q_mul = sa->q_mul;
+    const bool merge_in_kernel = g_step_merge == 1;
+    p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
+    if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+    return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
+  }
+  st = mj_quantize_q(cfg, sa->q, sa->q_tok_stride, sa->q_head_stride, sa->q_mul, a.num_seqs, a.q_len, q8, qd, stream);
+  if (st != MJ_OK) return st;
+  if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+  return a.with_reduction ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
+}
+
+mj_status mj_debug_set_step_merge(int32_t mode) {
+  if (mode < 0 || mode > 2) return MJ_EINVAL;
+  g_step_merge = mode;
+  return MJ_OK;
 }
 
 mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t stream) {

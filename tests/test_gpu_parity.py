@@ -324,9 +324,18 @@ def test_graph_replay_with_device_plan(mj, gpu):
         compare_lse(lse, LSE, f"device-plan replay {trial}")
 
 
+@pytest.fixture
+def step_merge(mj, request):
+    m = getattr(request, "param", 0)
+    mj.mj_debug_set_step_merge(m)
+    yield m
+    mj.mj_debug_set_step_merge(0)
+
+
+@pytest.mark.parametrize("step_merge", [1, 2], indirect=True)
 @pytest.mark.parametrize("variant", [0, 1], indirect=True)
 @pytest.mark.parametrize("key", SMALL_KEYS)
-def test_fused_step_matches_three_calls(mj, gpu, key, variant):
+def test_fused_step_matches_three_calls(mj, gpu, key, variant, step_merge):
     """mj_decode_step (one launch: in-kernel Q quantization, last-split merge)
     gives the three-call path's outputs bit for bit, call after call (a
     counter left non-zero would skip the next call's merge and leave NaN
@@ -334,7 +343,7 @@ def test_fused_step_matches_three_calls(mj, gpu, key, variant):
     generic kernel (variant 1) it is the three-call fallback."""
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
     wl = synth.build(synth.spec_for(key, small=True), gpu)
-    say(f"fused {wl.spec.name} variant={variant} lens={wl.seq_lens}")
+    say(f"fused {wl.spec.name} variant={variant} step_merge={step_merge} lens={wl.seq_lens}")
     for mct in (0, 1):
         step = DecodeStep.for_workload(wl, min_chunk_tokens=mct)
         info = step.plan_workload(wl)
@@ -354,7 +363,8 @@ def test_fused_step_matches_three_calls(mj, gpu, key, variant):
     compare_lse(lse, LSE, f"fused {wl.spec.name}")
 
 
-def test_fused_step_graph_replay(mj, gpu):
+@pytest.mark.parametrize("step_merge", [1, 2], indirect=True)
+def test_fused_step_graph_replay(mj, gpu, step_merge):
     """plan (device) + fused step captured once; replays with new device
     lengths match the oracle and the eager fused step, replay after replay."""
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
