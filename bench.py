@@ -84,14 +84,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="cfg2")
-    ap.add_argument("--extra", default="32k", help="comma list of extra workloads reported under 'extra' ('' = none)")
+    ap.add_argument("--extra", default="32k,32k_b16",
+                    help="comma list of extra workloads reported under 'extra' ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--variant", type=int, default=0,
                     help="decode kernel: 0 automatic, 1 generic, 2 VALU-PV streaming (A/B runs)")
     ap.add_argument("--no-nt", action="store_true", help="plain (not non-temporal) KV loads (A/B runs)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner workgroups per CU (0 = library default)")
-    ap.add_argument("--stream-read", action="store_true", help="also time a plain streaming read of the KV pool")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the plain streaming read of the main workload's KV pool (HBM context figure)")
     ap.add_argument("--step-merge", type=int, default=0,
                     help="mj_decode_step merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
     ap.add_argument("--calibrate", action="store_true",
@@ -337,11 +339,10 @@ def main():
     paged_fp8_decode_amd.mj_debug_set_step_merge(args.step_merge)
 
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-    main_res = measure(args.workload, args.steps, args.warmup, flush_buf, args.wgs_per_cu, args.stream_read)
+    main_res = measure(args.workload, args.steps, args.warmup, flush_buf, args.wgs_per_cu, not args.no_stream_read)
     extra = {}
     for k in [x for x in args.extra.split(",") if x]:
-        extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu,
-                           args.stream_read)
+        extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu, False)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     kvb = main_res["kv_bytes"]
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6

@@ -89,6 +89,49 @@ def e4m3_encode(x) -> np.ndarray:
     return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
 
 
+def e4m3_encode_sat(x) -> np.ndarray:
+    """The cache write's e4m3 rounding: saturate to +-448, then round to the
+    nearest code, ties to even (finite inputs only)."""
+    x = np.asarray(x, dtype=np.float32)
+    if np.any(~np.isfinite(x)):
+        raise ValueError("e4m3_encode_sat: non-finite input")
+    return e4m3_encode(np.clip(x, -E4M3_MAX, E4M3_MAX))
+
+
+# non-negative e2m3 values in code order 0x00..0x1F (strictly increasing)
+_E2M3_POS = E2M3_TABLE[:0x20]
+
+
+def e2m3_encode(x) -> np.ndarray:
+    """Round fp32 values to the nearest e2m3 code (6 bits), ties to the even
+    code, saturating at +-7.5; the sign is kept (negative zero gives 0x20)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(x)):
+        raise ValueError("e2m3_encode: non-finite input")
+    a = np.minimum(np.abs(x), E2M3_MAX)
+    hi = np.minimum(np.searchsorted(_E2M3_POS, a, side="left"), 0x1F)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E2M3_POS[hi] - a
+    d_lo = a - _E2M3_POS[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return (code | (np.signbit(x).astype(np.int64) << 5)).astype(np.uint8)
+
+
+def pack_6bit(codes: np.ndarray) -> np.ndarray:
+    """(..., n) 6-bit codes -> (..., 3n/4) bytes of the little-endian stream,
+    bit by bit: bit j of code k goes to stream bit 6k+j."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n = codes.shape[-1]
+    assert n % 4 == 0
+    out = np.zeros(codes.shape[:-1] + (n * 6 // 8,), dtype=np.uint8)
+    for k in range(n):
+        for j in range(6):
+            bit = 6 * k + j
+            out[..., bit // 8] |= (((codes[..., k] >> j) & 1) << (bit % 8)).astype(np.uint8)
+    return out
+
+
 def unpack_6bit(rows: np.ndarray, n: int) -> np.ndarray:
     """(..., 3n/4) bytes -> (..., n) codes of the little-endian 6-bit stream.
 

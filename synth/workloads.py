@@ -97,6 +97,9 @@ SPECS = {
                  seed=1005),
     "32k": Spec("b64_L32768_p64_nhd_e4m3", b=64, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
                 kv_format="e4m3", scale_kind="tensor", lens=(32768,) * 64, seed=1006),
+    # the 32k point at batch 16: the split path (several splits per sequence)
+    "32k_b16": Spec("b16_L32768_p64_nhd_e4m3", b=16, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
+                    kv_format="e4m3", scale_kind="tensor", lens=(32768,) * 16, seed=1007),
 }
 
 # Reduced sizes with the same heads, page size, layout, format and scales: the
@@ -110,6 +113,7 @@ SMALL = {
     "cfg4n": dict(b=3, lens=(1031, 517, 2000), pool_pages=0),
     "cfg5": dict(b=2, lens=(3001, 1290), pool_pages=0),
     "32k": dict(b=3, lens=(2048, 1985, 64), pool_pages=0),
+    "32k_b16": dict(b=2, lens=(4096, 3000), pool_pages=0),
 }
 
 

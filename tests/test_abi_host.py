@@ -73,7 +73,7 @@ def _compare(cfg, lens, q_len, margin=0):
     return info
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "32k"])
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "32k", "32k_b16"])
 def test_planner_matches_oracle_on_workloads(key):
     import synth
     s = synth.spec_for(key)

@@ -107,7 +107,7 @@ def test_gather_probe_bit_exact(mj, gpu, key):
                 assert np.array_equal(dense.cpu().numpy()[: L * row].reshape(L, row), ref)
 
 
-SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "32k"]
+SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "32k", "32k_b16"]
 # 0 = automatic choice, 1 = generic LDS kernel, 2 = VALU-PV streaming kernel
 VARIANTS = [0, 1, 2]
 
@@ -235,7 +235,7 @@ def test_graph_replay_after_replanning(mj, gpu):
         compare_lse(lse, LSE, f"replay {trial}")
 
 
-FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "32k": 2}
+FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "32k": 2, "32k_b16": 2}
 
 
 @pytest.mark.parametrize("key", list(FULL))

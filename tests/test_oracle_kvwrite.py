@@ -1,0 +1,151 @@
+"""Pins of the KV-cache write oracle (oracle/kvwrite.py) and its encoders:
+closed forms over every code, tie points and saturation, the hand-worked fp6
+packing examples, torch's e4m3 cast, a hand-worked write, and round trips
+through the decoders."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import kvwrite as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_e2m3_encode_every_code_maps_to_itself():
+    codes = np.arange(64, dtype=np.uint8)
+    vals = F.e2m3_decode(codes).astype(np.float32)
+    got = F.e2m3_encode(vals)
+    # +0 and -0 are distinct codes (0x00, 0x20) and both round-trip
+    assert np.array_equal(got, codes)
+
+
+def test_e2m3_encode_midpoints_tie_to_even_and_neighbours_round_to_nearest():
+    pos = F.E2M3_TABLE[:32]
+    for k in range(31):
+        lo, hi = pos[k], pos[k + 1]
+        mid = np.float32((lo + hi) / 2)  # exact in fp32: the grid has 3 mantissa bits
+        assert float(mid) == (lo + hi) / 2
+        want = k if k % 2 == 0 else k + 1
+        assert F.e2m3_encode(mid) == want, (k, lo, hi)
+        assert F.e2m3_encode(-mid) == want | 0x20
+        assert F.e2m3_encode(np.nextafter(mid, np.float32(0))) == k
+        assert F.e2m3_encode(np.nextafter(mid, np.float32(10))) == k + 1
+
+
+def test_e2m3_encode_saturates():
+    x = np.array([7.5, 7.74, 7.75, 8.0, 100.0, 3e38, -7.75, -1e9], dtype=np.float32)
+    assert F.e2m3_encode(x).tolist() == [0x1F] * 6 + [0x3F] * 2
+    with pytest.raises(ValueError):
+        F.e2m3_encode(np.array([np.inf], dtype=np.float32))
+
+
+def test_e4m3_encode_sat_matches_torch_cast_in_range_and_saturates_above():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.uniform(-448, 448, 200_000), rng.standard_normal(100_000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(F.e4m3_encode_sat(x), ref)
+    big = np.array([449.0, 464.0, 465.0, 1e6, -500.0, -3e38], dtype=np.float32)
+    assert F.e4m3_encode_sat(big).tolist() == [0x7E] * 4 + [0xFE] * 2
+
+
+def _golden_fp6():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "fp6_pack_example.txt")):
+        if line.startswith("#") or "->" not in line:
+            continue
+        a, b = line.split("->")
+        rows.append(([int(x) for x in a.split()], [int(x, 16) for x in b.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("codes,packed", _golden_fp6())
+def test_pack_6bit_worked_examples(codes, packed):
+    assert F.pack_6bit(np.array(codes, dtype=np.uint8)).tolist() == packed
+
+
+def test_pack_unpack_round_trip():
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 64, size=(33, 128), dtype=np.uint8)
+    assert np.array_equal(F.unpack_6bit(F.pack_6bit(codes), 128), codes)
+
+
+def _pools(kv_format, layout, pages, page_size, h_k):
+    row = 128 if kv_format == "e4m3" else 96
+    if layout == "HND":
+        st = (h_k * page_size * row, row, page_size * row)
+    else:
+        st = (page_size * h_k * row, h_k * row, row)
+    return pages * page_size * h_k * row, (st, st), row
+
+
+def test_write_hand_worked_example():
+    # one token, two KV heads, page size 16, per-head scales 2 and 0.5, slot
+    # 17 = page 1, row 1, HND: head g of row 1 of page 1 starts at byte
+    # 1*(2*16*128) + g*(16*128) + 1*128
+    size, strides, row = _pools("e4m3", "HND", 2, 16, 2)
+    x = np.zeros((1, 2, 128), dtype=np.float32)
+    x[0, 0, :4] = [3.0, -1.0, 896.0, 0.0078125]  # / 2 -> 1.5, -0.5, 448, 2^-8
+    x[0, 1, :3] = [0.75, 1000.0, -0.001953125]  # / 0.5 -> 1.5, 2000 (saturates), -2^-8
+    scale = np.array([2.0, 0.5], dtype=np.float32)
+    k, v = W.write_kv((np.full(size, 0xAA, np.uint8), np.zeros(size, np.uint8)), strides, 16, "e4m3",
+                      x, x, np.array([17]), scale, scale, "head")
+    b0 = 1 * 2 * 16 * 128 + 0 * 16 * 128 + 1 * 128
+    b1 = 1 * 2 * 16 * 128 + 1 * 16 * 128 + 1 * 128
+    # e4m3: 1.5 = 0x3C, -0.5 = 0xB0, 448 = 0x7E, 2^-8 = subnormal 2/8 * 2^-6 = 0x02
+    assert k[b0:b0 + 4].tolist() == [0x3C, 0xB0, 0x7E, 0x02]
+    assert k[b1:b1 + 3].tolist() == [0x3C, 0x7E, 0x82]
+    assert np.all(k[b0 + 4:b0 + 128] == 0) and np.all(k[b1 + 3:b1 + 128] == 0)
+    touched = np.zeros(size, bool)
+    touched[b0:b0 + 128] = touched[b1:b1 + 128] = True
+    assert np.all(k[~touched] == 0xAA)  # nothing else written
+    assert np.array_equal(k, v | (~touched * 0xAA).astype(np.uint8))
+
+
+def test_padding_slots_write_nothing():
+    size, strides, _ = _pools("e2m3", "NHD", 4, 16, 2)
+    x = np.ones((3, 2, 128), dtype=np.float32)
+    pools = (np.full(size, 7, np.uint8), np.full(size, 9, np.uint8))
+    k, v = W.write_kv(pools, strides, 16, "e2m3", x, x, np.array([-1, -1, -1]), np.ones((2, 128), np.float32),
+                      np.ones((2, 128), np.float32), "channel")
+    assert np.all(k == 7) and np.all(v == 9)
+
+
+@pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e2m3", "channel")])
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_write_round_trip_through_decoders(kv_format, kind, layout):
+    rng = np.random.default_rng(11)
+    h_k, P, pages, n = 2, 16, 8, 40
+    size, strides, row = _pools(kv_format, layout, pages, P, h_k)
+    x = torch.from_numpy(rng.standard_normal((n, h_k, 128)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    amax = np.abs(x).max()
+    if kind == "tensor":
+        sc = np.array([amax / 448], np.float32)
+    elif kind == "head":
+        sc = (np.abs(x).max(axis=(0, 2)) / 448).astype(np.float32)
+    else:
+        sc = (np.abs(x).max(axis=0) / 7.5).astype(np.float32)  # (h_k, 128)
+    slots = rng.permutation(pages * P)[:n]
+    slots[5] = -1
+    k, _ = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), strides, P, kv_format, x, x, slots,
+                      sc, sc, kind)
+    for t in range(n):
+        if slots[t] < 0:
+            continue
+        page, off = divmod(int(slots[t]), P)
+        for g in range(h_k):
+            b = page * strides[0][0] + off * strides[0][1] + g * strides[0][2]
+            raw = k[b:b + row]
+            dec = F.e4m3_decode(raw) if kv_format == "e4m3" else F.e2m3_decode(F.unpack_6bit(raw, 128))
+            s = W.scale_of(sc, kind, g)
+            y = x[t, g] / s
+            got = dec
+            # nearest-value rounding: the error is at most half the local grid
+            # step (3 mantissa bits: 2^-4 relative in the normal range, the
+            # subnormal step below it)
+            sub = 2.0 ** -9 if kv_format == "e4m3" else 1.0 / 8
+            bound = np.maximum(np.abs(y) * 2.0 ** -4, sub / 2)
+            assert np.all(np.abs(got - y) <= bound + 1e-12)
