@@ -96,6 +96,7 @@ def parse():
                     help="skip the plain streaming read of the main workload's KV pool (HBM context figure)")
     ap.add_argument("--step-merge", type=int, default=0,
                     help="mj_decode_step merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
+    ap.add_argument("--no-write", action="store_true", help="skip the KV-cache write measurement")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the HBM-counter calibration kernels (256 MiB streaming read, 256 MiB copy) and exit")
     return ap.parse_args()
@@ -275,6 +276,52 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     return res
 
 
+def measure_write(kv_format, n_tokens, reps, flush_buf, h_k=8, page_size=64):
+    """mj_write_kv of n_tokens new rows (bf16 K and V, h_k heads) into a paged
+    cache at scattered slots: time per call (one event pair around reps
+    back-to-back calls, cache flushed first) and algorithmic bytes (bf16 in,
+    codes out, 8-byte slots) against the HBM peak."""
+    import torch
+    import paged_fp8_decode_amd as mjlib
+    row = 128 if kv_format == "e4m3" else 96
+    pages = max(16, -(-2 * n_tokens // page_size))
+    g = torch.Generator(device="cuda").manual_seed(77)
+    key = torch.randn(n_tokens, h_k, 128, generator=g, device="cuda").to(torch.bfloat16)
+    value = torch.randn(n_tokens, h_k, 128, generator=g, device="cuda").to(torch.bfloat16)
+    slots = torch.randperm(pages * page_size, generator=g, device="cuda")[:n_tokens].to(torch.int64)
+    k_pool = torch.zeros(pages * page_size * h_k * row, dtype=torch.uint8, device="cuda")
+    v_pool = torch.zeros_like(k_pool)
+    st = (h_k * page_size * row, row, page_size * row)  # HND
+    kind = "head" if kv_format == "e4m3" else "channel"
+    n_sc = h_k if kind == "head" else h_k * 128
+    k_sc = torch.full((n_sc,), 4.0 / (448.0 if kv_format == "e4m3" else 7.5), device="cuda")
+    v_sc = k_sc.clone()
+    cfg = mjlib.mj_config(h_q=h_k, h_k=h_k, page_size=page_size, max_num_seqs=1, kv_format=kv_format)
+    kk = mjlib.SCALE_KINDS[kind]
+    a = mjlib.WriteArgs(key=key.data_ptr(), key_tok_stride=key.stride(0), key_head_stride=key.stride(1),
+                        value=value.data_ptr(), value_tok_stride=value.stride(0),
+                        value_head_stride=value.stride(1), num_tokens=n_tokens, slot_mapping=slots.data_ptr(),
+                        k_cache=k_pool.data_ptr(), k_page_stride=st[0], k_slot_stride=st[1], k_head_stride=st[2],
+                        v_cache=v_pool.data_ptr(), v_page_stride=st[0], v_slot_stride=st[1], v_head_stride=st[2],
+                        num_pages=pages, k_scale=k_sc.data_ptr(), k_scale_kind=kk, v_scale=v_sc.data_ptr(),
+                        v_scale_kind=kk)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        mjlib.mj_write_kv(cfg, a, stream)
+    flush_buf.add_(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        mjlib.mj_write_kv(cfg, a, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = n_tokens * h_k * 2 * (2 * 128 + row) + 8 * n_tokens
+    return dict(kv_format=kv_format, tokens=n_tokens, h_k=h_k, us_per_call=round(us, 2),
+                algorithmic_bytes=nbytes, gbs=round(nbytes / us / 1e3, 1),
+                frac_of_hbm_peak=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4))
+
+
 def cpu_baseline(key, budget_s):
     """The oracle as it stands, single-threaded BLAS, on whole (sequence, KV
     head) pairs of the same workload until ~budget_s seconds of CPU work."""
@@ -343,6 +390,13 @@ def main():
     extra = {}
     for k in [x for x in args.extra.split(",") if x]:
         extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu, False)
+    writes = []
+    if not args.no_write:
+        for fmt in ("e4m3", "e2m3"):
+            for n_tok, reps in ((16384, 20), (32, 200)):
+                w = measure_write(fmt, n_tok, reps, flush_buf)
+                log(f"[bench] mj_write_kv {fmt} {n_tok} tokens x 8 heads: {w['us_per_call']} us, {w['gbs']} GB/s")
+                writes.append(w)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     kvb = main_res["kv_bytes"]
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6
@@ -372,6 +426,7 @@ def main():
         cpu_baseline=cpu,
         detail=main_res,
         extra=extra,
+        write_kv=writes,
     )
     print(json.dumps(line), flush=True)
 

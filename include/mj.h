@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 2
+#define MJ_ABI_VERSION 3
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -72,7 +72,9 @@ typedef enum mj_kv_format {
 typedef enum mj_scale_kind {
   MJ_SCALE_TENSOR = 0,   /* descale[0]                       */
   MJ_SCALE_HEAD = 1,     /* descale[g], g = KV head          */
-  MJ_SCALE_SEQ_HEAD = 2  /* descale[i * h_k + g]             */
+  MJ_SCALE_SEQ_HEAD = 2, /* descale[i * h_k + g]             */
+  MJ_SCALE_CHANNEL = 3   /* scale[g * 128 + c] (cache write only; backend.py
+                            _install_fp6_scales: per (KV head, channel))     */
 } mj_scale_kind;
 
 /* Static configuration of one decode site (one KV-cache group).  Every size a
@@ -267,6 +269,42 @@ mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* args, hipS
  * LSE.  Sequences with a single item are left untouched (mj_paged_decode
  * already wrote them).  Errors: EINVAL, ECAPACITY, EALIGN, EHIP. */
 mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* args, hipStream_t stream);
+
+/* Arguments of mj_write_kv.  Strides of key/value in ELEMENTS (bf16), of
+ * the caches in BYTES (the same pools and strides mj_paged_decode reads). */
+typedef struct mj_write_args {
+  const void* key;              /* bf16 (num_tokens, h_k, 128), channel stride 1 */
+  int64_t key_tok_stride, key_head_stride;
+  const void* value;
+  int64_t value_tok_stride, value_head_stride;
+  int32_t num_tokens;
+  const int64_t* slot_mapping;  /* device (num_tokens): page * page_size + row;
+                                   negative = padding token, not written     */
+  void* k_cache;
+  int64_t k_page_stride, k_slot_stride, k_head_stride;
+  void* v_cache;
+  int64_t v_page_stride, v_slot_stride, v_head_stride;
+  int64_t num_pages;            /* slots in pages >= num_pages are skipped   */
+  const float* k_scale;         /* divisor(s) of the write                   */
+  int32_t k_scale_kind;         /* TENSOR, HEAD or CHANNEL                   */
+  const float* v_scale;
+  int32_t v_scale_kind;
+} mj_write_args;
+
+/* The KV-cache write of a step's new rows (wheel listing
+ * mjolnir/backend.py, do_kv_cache_update: an fp8 cache written with the
+ * layer's per-tensor or per-head scale, the fp6 cache with per-(KV head,
+ * channel) scales, _install_fp6_scales).  Every value becomes
+ * RNE(x / scale) in the config's KV format, saturated at 448 (e4m3) or 7.5
+ * (e2m3), x the fp32 value of the bf16 input and the division correctly
+ * rounded; e2m3 rows are packed as mj_paged_decode reads them.  Tokens are
+ * independent; two tokens mapped to one slot race (the caller's contract,
+ * as in any slot-mapped write).  num_tokens == 0 enqueues nothing.
+ * Errors: EINVAL (nulls, negative strides or counts, scale kind), EALIGN
+ * (key/value/cache bases not 16-byte aligned, key/value strides not
+ * multiples of 8 elements, cache strides not multiples of 16 bytes),
+ * EUNSUPPORTED (SEQ_HEAD scales), EHIP. */
+mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* args, hipStream_t stream);
 
 /* Arguments of one whole decode step after the plan: the decode arguments
  * (decode.q8 and decode.q_descale are not read and may be NULL;

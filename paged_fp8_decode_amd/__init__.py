@@ -16,7 +16,7 @@ import ctypes
 import numpy as np
 
 from ._abi import (  # noqa: F401
-    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, MjError, KV_FORMATS, SCALE_KINDS,
+    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, MjError, KV_FORMATS, SCALE_KINDS,
     MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
 )
 
@@ -114,6 +114,10 @@ def mj_merge_lse(cfg: Config, args: MergeArgs, stream=None):
 
 def mj_decode_step(cfg: Config, args: StepArgs, stream=None):
     check(lib().mj_decode_step(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_decode_step")
+
+
+def mj_write_kv(cfg: Config, args: WriteArgs, stream=None):
+    check(lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_write_kv")
 
 
 def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_len: int, which: int, dense_out,

@@ -8,10 +8,10 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 2  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 3  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
 KV_FORMATS = {"e4m3": 0, "e2m3": 1}
-SCALE_KINDS = {"tensor": 0, "head": 1, "seq_head": 2}
+SCALE_KINDS = {"tensor": 0, "head": 1, "seq_head": 2, "channel": 3}
 
 
 class MjError(RuntimeError):
@@ -59,6 +59,17 @@ class MergeArgs(ctypes.Structure):
     ]
 
 
+class WriteArgs(ctypes.Structure):
+    _fields_ = [
+        ("key", _p), ("key_tok_stride", _i64), ("key_head_stride", _i64),
+        ("value", _p), ("value_tok_stride", _i64), ("value_head_stride", _i64),
+        ("num_tokens", _i32), ("slot_mapping", _p),
+        ("k_cache", _p), ("k_page_stride", _i64), ("k_slot_stride", _i64), ("k_head_stride", _i64),
+        ("v_cache", _p), ("v_page_stride", _i64), ("v_slot_stride", _i64), ("v_head_stride", _i64),
+        ("num_pages", _i64), ("k_scale", _p), ("k_scale_kind", _i32), ("v_scale", _p), ("v_scale_kind", _i32),
+    ]
+
+
 class StepArgs(ctypes.Structure):
     _fields_ = [
         ("decode", DecodeArgs), ("q", _p), ("q_tok_stride", _i64), ("q_head_stride", _i64), ("q_mul", _p),
@@ -86,6 +97,7 @@ def _load():
         "mj_paged_decode": (_i32, [P(Config), P(DecodeArgs), _p]),
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
         "mj_decode_step": (_i32, [P(Config), P(StepArgs), _p]),
+        "mj_write_kv": (_i32, [P(Config), P(WriteArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
         "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),

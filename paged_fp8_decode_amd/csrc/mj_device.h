@@ -50,6 +50,20 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
   return sign | (u >= 0x3C800000u ? nrm : sub);
 }
 
+// Round an fp32 to the nearest e2m3 code (6 bits), ties to even, saturating
+// at 7.5 (any magnitude, infinities included).  Normal range (|x| >= 1): keep
+// 3 of 23 mantissa bits with the carry running into the exponent; below it,
+// multiples of 1/8 (8/8 is the smallest normal, code 8).
+__device__ __forceinline__ uint32_t e2m3_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 26) & 0x20u;
+  u &= 0x7FFFFFFFu;
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t nrm = min(((r >> 23) << 3) - (126u << 3) + ((r >> 20) & 7u), 0x1Fu);
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(u) * 8.0f);
+  return sign | (u >= 0x3F800000u ? nrm : sub);
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

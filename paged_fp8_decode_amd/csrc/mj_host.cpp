@@ -507,6 +507,56 @@ mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t
   return mj::launch_merge(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
+mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* a, hipStream_t stream) {
+  mj_status st = check_config(cfg);
+  if (st != MJ_OK) return st;
+  if (!a || a->num_tokens < 0) return MJ_EINVAL;
+  if (a->num_tokens == 0) return MJ_OK;
+  if (!a->key || !a->value || !a->slot_mapping || !a->k_cache || !a->v_cache || !a->k_scale || !a->v_scale ||
+      a->num_pages < 1)
+    return MJ_EINVAL;
+  if (a->key_tok_stride < 0 || a->key_head_stride < 0 || a->value_tok_stride < 0 || a->value_head_stride < 0 ||
+      a->k_page_stride < 0 || a->k_slot_stride < 0 || a->k_head_stride < 0 || a->v_page_stride < 0 ||
+      a->v_slot_stride < 0 || a->v_head_stride < 0)
+    return MJ_EINVAL;
+  for (int kind : {a->k_scale_kind, a->v_scale_kind}) {
+    if (kind == MJ_SCALE_SEQ_HEAD) return MJ_EUNSUPPORTED;
+    if (kind != MJ_SCALE_TENSOR && kind != MJ_SCALE_HEAD && kind != MJ_SCALE_CHANNEL) return MJ_EINVAL;
+  }
+  if (!aligned(a->key, 16) || !aligned(a->value, 16) || a->key_tok_stride % 8 || a->key_head_stride % 8 ||
+      a->value_tok_stride % 8 || a->value_head_stride % 8 || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
+      a->k_page_stride % 16 || a->k_slot_stride % 16 || a->k_head_stride % 16 || a->v_page_stride % 16 ||
+      a->v_slot_stride % 16 || a->v_head_stride % 16 || !aligned(a->slot_mapping, 8) || !aligned(a->k_scale, 4) ||
+      !aligned(a->v_scale, 4))
+    return MJ_EALIGN;
+  mj::WriteParams p;
+  p.key = static_cast<const uint16_t*>(a->key);
+  p.value = static_cast<const uint16_t*>(a->value);
+  p.k_ts = a->key_tok_stride;
+  p.k_hs = a->key_head_stride;
+  p.v_ts = a->value_tok_stride;
+  p.v_hs = a->value_head_stride;
+  p.slots = a->slot_mapping;
+  p.kc = static_cast<uint8_t*>(a->k_cache);
+  p.vc = static_cast<uint8_t*>(a->v_cache);
+  p.kc_sp = a->k_page_stride;
+  p.kc_ss = a->k_slot_stride;
+  p.kc_sh = a->k_head_stride;
+  p.vc_sp = a->v_page_stride;
+  p.vc_ss = a->v_slot_stride;
+  p.vc_sh = a->v_head_stride;
+  p.num_pages = a->num_pages;
+  p.ks = a->k_scale;
+  p.vs = a->v_scale;
+  p.ks_kind = a->k_scale_kind;
+  p.vs_kind = a->v_scale_kind;
+  p.num_tokens = a->num_tokens;
+  p.h_k = cfg->h_k;
+  p.page_shift = ilog2(cfg->page_size);
+  p.kv_format = cfg->kv_format;
+  return mj::launch_write_kv(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int32_t seq, int32_t head,
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream) {
   mj_status st = check_config(cfg);

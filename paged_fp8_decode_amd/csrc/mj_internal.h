@@ -75,6 +75,23 @@ struct MergeParams {
   int num_seqs, q_len, h_q, h_k, h_r, n_q;
 };
 
+// Parameters of the KV-cache write kernel.
+struct WriteParams {
+  const uint16_t* key;      // bf16
+  const uint16_t* value;
+  int64_t k_ts, k_hs, v_ts, v_hs;   // elements
+  const int64_t* slots;
+  uint8_t* kc;
+  uint8_t* vc;
+  int64_t kc_sp, kc_ss, kc_sh, vc_sp, vc_ss, vc_sh;  // bytes
+  int64_t num_pages;
+  const float* ks;
+  const float* vs;
+  int ks_kind, vs_kind;     // 0 tensor, 1 head, 3 channel
+  int num_tokens, h_k, page_shift, kv_format;
+  int tokens_per_thread;    // set by the launcher
+};
+
 struct GatherParams {
   const uint8_t* pool;
   int64_t sp, ss, sh;
@@ -101,6 +118,7 @@ bool decode_fuses_step(const DecodeParams& p, int kv_format, int row_tiles);
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_write_kv(const WriteParams& p, hipStream_t s);
 void set_decode_variant(int variant, int nontemporal);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s);
 hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);

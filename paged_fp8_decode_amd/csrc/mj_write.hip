@@ -1,0 +1,136 @@
+// KV-cache write: the step's new key / value rows quantized into the paged
+// cache through a slot mapping.
+//
+// Method (wheel listing mjolnir/backend.py, do_kv_cache_update, _write_kv
+// and _install_fp6_scales): an e4m3 cache is written with a per-tensor or
+// per-KV-head scale, a packed e2m3 cache with per-(KV head, channel) scales
+// s_c.  Each value becomes round-to-nearest-even(x / s) in the cache format,
+// saturated at its largest magnitude (448 / 7.5), from one correctly rounded
+// fp32 division (built with -fhip-fp32-correctly-rounded-divide-sqrt) of
+// the exact fp32 value of the bf16 input (computed from the correctly rounded
+// reciprocal with one FMA correction), so the bytes are the same as any other
+// correct evaluation.  e2m3 rows are the little-endian 6-bit stream
+// the decode kernels read (code k at stream bits [6k, 6k+6)).  Slot s is
+// page s / page_size, row s % page_size; a negative slot (padding) or one
+// past the pool is skipped.
+//
+// One thread per (KV head, 16 channels) of 8 tokens: 32 bytes of bf16 in
+// per side and token, 16 bytes (e4m3) or 12 bytes (e2m3) of codes out.  The
+// write touches every byte once.
+#include "mj_device.h"
+#include "mj_internal.h"
+
+namespace mj {
+
+namespace {
+
+constexpr int kWThreads = 256;
+
+// x / s rounded to nearest from y = RN(1/s): q = RN(x y) is a faithful
+// quotient, the residual x - q s is exact in one FMA, and RN(q + r y) is the
+// correctly rounded quotient (Markstein's theorem; Muller et al., Handbook of
+// Floating-Point Arithmetic, on division by FMA).  Quotients that underflow
+// into fp32 subnormals or overflow lie far below or above every rounding
+// boundary of e4m3 / e2m3, so their codes are those of the exact quotient.
+// Scales are positive and finite.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-q, s, x);
+  // a zero quotient keeps its sign (-0 / s = -0; the correction would give +0)
+  return x == 0.0f ? x : __builtin_fmaf(r, y, q);
+}
+
+template <int FMT>
+__device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc)[16], const float (&rc)[16], int c0,
+                                           uint8_t* dst_row) {
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
+    const float q = div_rn(__uint_as_float(bits), sc[i], rc[i]);
+    code[i] = FMT == 0 ? e4m3_rne(q) : e2m3_rne(q);
+  }
+  if constexpr (FMT == 0) {
+    uint4 o;
+    o.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    o.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
+    o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
+    *reinterpret_cast<uint4*>(dst_row + c0) = o;
+  } else {
+    uint32_t o[3] = {0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int bit = 6 * k;
+      o[bit >> 5] |= code[k] << (bit & 31);
+      if ((bit & 31) > 26) o[(bit >> 5) + 1] |= code[k] >> (32 - (bit & 31));
+    }
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst_row + (c0 / 16) * 12);
+    d[0] = o[0];
+    d[1] = o[1];
+    d[2] = o[2];
+  }
+}
+
+__device__ __forceinline__ void load_divisors(const float* s, int kind, int g, int c0, float (&sc)[16],
+                                              float (&rc)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sc[i] = kind == 0 ? s[0] : (kind == 1 ? s[g] : s[g * kHeadDim + c0 + i]);
+    rc[i] = 1.0f / sc[i];  // correctly rounded
+  }
+}
+
+// Thread -> (KV head g, channel group grp) of p.tokens_per_thread
+// consecutive tokens (the divisors are set up once per thread); the 8 h_k threads of one token's rows are adjacent, so each token's
+// bf16 rows are read with coalesced 16-byte loads.
+template <int FMT>
+__global__ __launch_bounds__(kWThreads) void write_kv_kernel(WriteParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * kWThreads + threadIdx.x;
+  const int row_threads = p.h_k * 8;
+  const int tpt = p.tokens_per_thread;
+  const int64_t blocks = ((int64_t)p.num_tokens + tpt - 1) / tpt;
+  if (gid >= blocks * row_threads) return;
+  const int r = (int)(gid % row_threads);
+  const int64_t tb = gid / row_threads;
+  const int grp = r & 7, g = r >> 3;
+  const int c0 = grp * 16;
+  float ks[16], kr[16], vs[16], vr[16];
+  load_divisors(p.ks, p.ks_kind, g, c0, ks, kr);
+  load_divisors(p.vs, p.vs_kind, g, c0, vs, vr);
+  const int t_end = (int)min<int64_t>(p.num_tokens, (tb + 1) * tpt);
+  for (int t = (int)(tb * tpt); t < t_end; ++t) {
+    const int64_t slot = p.slots[t];
+    if (slot < 0) continue;
+    const int64_t page = slot >> p.page_shift;
+    if (page >= p.num_pages) continue;
+    const int64_t row = slot & ((1 << p.page_shift) - 1);
+    write_side<FMT>(p.key + (int64_t)t * p.k_ts + (int64_t)g * p.k_hs + c0, ks, kr, c0,
+                    p.kc + page * p.kc_sp + row * p.kc_ss + (int64_t)g * p.kc_sh);
+    write_side<FMT>(p.value + (int64_t)t * p.v_ts + (int64_t)g * p.v_hs + c0, vs, vr, c0,
+                    p.vc + page * p.vc_sp + row * p.vc_ss + (int64_t)g * p.vc_sh);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const WriteParams& p_in, hipStream_t s) {
+  // a few tokens per thread amortize the divisors once the grid is large;
+  // a small write (a decode step's new rows) keeps one token per thread
+  WriteParams p = p_in;
+  const int64_t rows = (int64_t)p.num_tokens * p.h_k;
+  p.tokens_per_thread = rows >= (1 << 17) ? 8 : (rows >= (1 << 14) ? 2 : 1);
+  const int64_t threads = ((int64_t)p.num_tokens + p.tokens_per_thread - 1) / p.tokens_per_thread * p.h_k * 8;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + kWThreads - 1) / kWThreads));
+  if (p.kv_format == 0)
+    hipLaunchKernelGGL(write_kv_kernel<0>, grid, dim3(kWThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(write_kv_kernel<1>, grid, dim3(kWThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace mj

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 2
+    assert mj.lib().mj_abi_version() == 3
 
 
 def _cfg(**kw):
@@ -203,3 +203,42 @@ def test_quantize_and_merge_errors():
     m.num_seqs = 0
     assert L.mj_merge_lse(ctypes.byref(cfg), ctypes.byref(m), None) == mj.MJ_EINVAL
     assert L.mj_debug_decode_codes(7, FAKE, 4, FAKE, None) == mj.MJ_EINVAL
+
+
+def _wargs(**kw):
+    a = dict(key=FAKE, key_tok_stride=8 * 128, key_head_stride=128, value=FAKE, value_tok_stride=8 * 128,
+             value_head_stride=128, num_tokens=4, slot_mapping=FAKE, k_cache=FAKE, k_page_stride=16 * 8 * 128,
+             k_slot_stride=128, k_head_stride=16 * 128, v_cache=FAKE, v_page_stride=16 * 8 * 128, v_slot_stride=128,
+             v_head_stride=16 * 128, num_pages=10, k_scale=FAKE, k_scale_kind=0, v_scale=FAKE, v_scale_kind=0)
+    a.update(kw)
+    return mj.WriteArgs(**a)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(key=None), mj.MJ_EINVAL),
+    (dict(slot_mapping=None), mj.MJ_EINVAL),
+    (dict(num_tokens=-1), mj.MJ_EINVAL),
+    (dict(num_pages=0), mj.MJ_EINVAL),
+    (dict(k_scale_kind=7), mj.MJ_EINVAL),
+    (dict(v_scale_kind=2), mj.MJ_EUNSUPPORTED),
+    (dict(key=FAKE + 2), mj.MJ_EALIGN),
+    (dict(value_head_stride=100), mj.MJ_EALIGN),
+    (dict(k_slot_stride=120), mj.MJ_EALIGN),
+    (dict(v_cache=FAKE + 4), mj.MJ_EALIGN),
+    (dict(k_head_stride=-16), mj.MJ_EINVAL),
+])
+def test_write_argument_errors(kw, status):
+    cfg = _cfg(max_num_seqs=64)
+    assert mj.lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(_wargs(**kw)), None) == status
+
+
+def test_write_zero_tokens_needs_no_buffers():
+    cfg = _cfg()
+    assert mj.lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(mj.WriteArgs(num_tokens=0)), None) == mj.MJ_OK
+
+
+def test_debug_knob_errors():
+    assert mj.lib().mj_debug_set_step_merge(3) == mj.MJ_EINVAL
+    assert mj.lib().mj_debug_set_step_merge(-1) == mj.MJ_EINVAL
+    assert mj.lib().mj_debug_set_decode_variant(14, 1) == mj.MJ_EINVAL

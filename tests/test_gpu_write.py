@@ -1,0 +1,174 @@
+"""GPU parity of the KV-cache write (mj_write_kv) against the oracle: whole
+pools compared byte for byte after the write (both formats, every scale
+kind, HND and NHD, strided K/V views, padding and out-of-pool slots,
+saturating values), and a written cache decoded end to end."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import compare_lse, compare_out, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mj(gpu):
+    import paged_fp8_decode_amd as m
+    return m
+
+
+def _strides(layout, P, h_k, row):
+    if layout == "HND":
+        return (h_k * P * row, row, P * row)
+    return (P * h_k * row, h_k * row, row)
+
+
+def _write(mj, gpu, cfg, key, value, slots, k_pool, v_pool, ks, vs, k_scale, v_scale, kind, num_pages):
+    # the kernel trusts these sizes: check them before the launch
+    assert slots.numel() == key.shape[0] == value.shape[0]
+    assert key.shape[1:] == value.shape[1:] == (cfg.h_k, 128)
+    row = 128 if cfg.kv_format == 0 else 96
+    last = (num_pages - 1) * ks[0] + (cfg.page_size - 1) * ks[1] + (cfg.h_k - 1) * ks[2] + row
+    assert last <= k_pool.numel() and last <= v_pool.numel()
+    need = {"tensor": 1, "head": cfg.h_k, "channel": cfg.h_k * 128}[kind]
+    assert k_scale.numel() >= need and v_scale.numel() >= need
+    kk = mj.SCALE_KINDS[kind]
+    a = mj.WriteArgs(key=key.data_ptr(), key_tok_stride=key.stride(0), key_head_stride=key.stride(1),
+                     value=value.data_ptr(), value_tok_stride=value.stride(0), value_head_stride=value.stride(1),
+                     num_tokens=key.shape[0], slot_mapping=slots.data_ptr(),
+                     k_cache=k_pool.data_ptr(), k_page_stride=ks[0], k_slot_stride=ks[1], k_head_stride=ks[2],
+                     v_cache=v_pool.data_ptr(), v_page_stride=vs[0], v_slot_stride=vs[1], v_head_stride=vs[2],
+                     num_pages=num_pages, k_scale=k_scale.data_ptr(), k_scale_kind=kk, v_scale=v_scale.data_ptr(),
+                     v_scale_kind=kk)
+    mj.mj_write_kv(cfg, a)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e4m3", "channel"),
+                                            ("e2m3", "channel"), ("e2m3", "head")])
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+@pytest.mark.parametrize("P", [16, 128])
+def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
+    from oracle.kvwrite import write_kv
+    say(f"write {kv_format} {kind} {layout} P={P}")
+    rng = np.random.default_rng(zlib.crc32(f"{kv_format}{kind}{layout}{P}".encode()))
+    h_k, n = 4, 300
+    pages = max(9, -(-2 * n // P))  # at least two slots per token
+    row = 128 if kv_format == "e4m3" else 96
+    ks = vs = _strides(layout, P, h_k, row)
+    size = pages * P * h_k * row
+    init_k = rng.integers(0, 256, size, dtype=np.uint8)
+    init_v = rng.integers(0, 256, size, dtype=np.uint8)
+    # K and V as strided views of one fused buffer (token stride 3 heads wider)
+    fused = torch.from_numpy(rng.standard_normal((n, 2 * h_k + 2, 128)).astype(np.float32) * 2).to(torch.bfloat16)
+    special = torch.tensor([0, -0.0, 1e4, -1e4, 1e-30, -1e-30, 3.0, -2.5, 0.1, -0.0])  # zeros, saturation, tiny
+    fused[1, 0, :10] = special  # token 1 of K and token 2 of V are written (not padding)
+    fused[2, h_k + 1, 118:] = special
+    key, value = fused[:, :h_k], fused[:, h_k + 1:2 * h_k + 1]
+    fmax = 448.0 if kv_format == "e4m3" else 7.5
+    amax_k = key.float().abs().amax(dim=0).numpy()  # (h_k, 128); saturating rows stay rare
+    amax_v = value.float().abs().amax(dim=0).numpy()
+    if kind == "tensor":
+        k_sc = np.array([np.median(amax_k) / fmax], np.float32)
+        v_sc = np.array([np.median(amax_v) / fmax], np.float32)
+    elif kind == "head":
+        k_sc = (np.median(amax_k, axis=1) / fmax).astype(np.float32)
+        v_sc = (np.median(amax_v, axis=1) / fmax).astype(np.float32)
+    else:
+        k_sc = (amax_k / fmax * 0.9).astype(np.float32)
+        v_sc = (amax_v / fmax * 0.9).astype(np.float32)
+    slots = rng.permutation(pages * P)[:n].astype(np.int64)
+    assert slots.shape == (n,)  # one slot per token: the kernel reads num_tokens entries
+    slots[::17] = -1  # padding tokens (not tokens 1 and 2)
+    num_pages = pages - 1
+    slots[3] = (pages - 1) * P + 2  # in the last page: past num_pages, skipped
+    k_pool = torch.from_numpy(init_k.copy()).to(gpu)
+    v_pool = torch.from_numpy(init_v.copy()).to(gpu)
+    cfg = mj.mj_config(h_q=h_k, h_k=h_k, page_size=P, max_num_seqs=1, kv_format=kv_format, num_cus=256)
+    _write(mj, gpu, cfg, key.to(gpu), value.to(gpu), torch.from_numpy(slots).to(gpu), k_pool, v_pool, ks, vs,
+           torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, num_pages)
+    oslots = slots.copy()
+    oslots[oslots >= num_pages * P] = -1  # the oracle's pool has every page; the kernel skips past num_pages
+    ref_k, ref_v = write_kv((init_k, init_v), (ks, vs), P, kv_format, key.float().numpy(), value.float().numpy(),
+                            oslots, k_sc, v_sc, kind)
+    assert np.array_equal(k_pool.cpu().numpy(), ref_k)
+    assert np.array_equal(v_pool.cpu().numpy(), ref_v)
+
+
+def test_write_zero_tokens_is_a_noop(mj, gpu):
+    cfg = mj.mj_config(h_q=8, h_k=2, page_size=16, max_num_seqs=1, num_cus=256)
+    a = mj.WriteArgs(num_tokens=0)
+    mj.mj_write_kv(cfg, a)
+
+
+@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg5"])
+def test_written_cache_decodes(mj, gpu, key):
+    """Blank every token row of a seeded workload's cache, re-write them with
+    mj_write_kv from the dequantized K/V (code * scale in bf16: dividing by
+    the scale lands within 2^-9 of the code, which rounds back to it), and
+    check the pools are byte-identical to the generator's; then decode."""
+    import synth
+    from helpers import oracle_step
+    from oracle import formats as F
+    from oracle.attention import gather_codes
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    s = wl.spec
+    say(f"write+decode {s.name}")
+    h = wl.host()
+    ks, vs = wl.kv_strides()
+    row = s.row_bytes
+    if s.kv_format == "e4m3":
+        kind = "head" if wl.descale_kind == "head" else ("tensor" if wl.descale_kind == "tensor" else None)
+        if kind is None:  # per-(sequence, head) descales have no slot-mapped write form
+            pytest.skip("per-(sequence, head) scales are a decode-side shape only")
+        k_sc = wl.k_descale.cpu().numpy().astype(np.float32).reshape(-1)
+        v_sc = wl.v_descale.cpu().numpy().astype(np.float32).reshape(-1)
+    else:
+        kind = "channel"
+        k_sc = wl.k_channel_scale.cpu().numpy().astype(np.float32).reshape(-1)
+        v_sc = wl.v_channel_scale.cpu().numpy().astype(np.float32).reshape(-1)
+    n = sum(wl.seq_lens)
+    kx = np.zeros((n, s.h_k, 128), np.float32)
+    vx = np.zeros((n, s.h_k, 128), np.float32)
+    slots = np.zeros(n, np.int64)
+    mask = torch.zeros(wl.k_pool.numel(), dtype=torch.bool)
+    base = 0
+    for i in range(s.b):
+        L = wl.seq_lens[i]
+        bt = h["block_table"][i]
+        for j in range(L):
+            page = int(bt[j // s.page_size])
+            slots[base + j] = page * s.page_size + j % s.page_size
+            for g in range(s.h_k):
+                b = page * ks[0] + (j % s.page_size) * ks[1] + g * ks[2]
+                mask[b:b + row] = True
+        for g in range(s.h_k):
+            for pool, st, dst, sc in ((h["k_pool"], h["k_strides"], kx, k_sc), (h["v_pool"], h["v_strides"], vx, v_sc)):
+                codes = gather_codes(pool, st, s.page_size, bt, L, g, row)
+                vals = F.e4m3_decode(codes) if s.kv_format == "e4m3" else F.e2m3_decode(F.unpack_6bit(codes, 128))
+                div = sc[0] if kind == "tensor" else (sc[g] if kind == "head" else sc.reshape(-1, 128)[g])
+                dst[base:base + L, g] = vals * div
+        base += L
+    assert ks == vs
+    before_k, before_v = wl.k_pool.clone(), wl.v_pool.clone()
+    m = mask.to(gpu)
+    wl.k_pool.view(-1)[m] = 0
+    wl.v_pool.view(-1)[m] = 0
+    cfg = mj.mj_config(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, kv_format=s.kv_format,
+                       num_cus=256)
+    _write(mj, gpu, cfg, torch.from_numpy(kx).to(torch.bfloat16).to(gpu),
+           torch.from_numpy(vx).to(torch.bfloat16).to(gpu), torch.from_numpy(slots).to(gpu), wl.k_pool, wl.v_pool,
+           ks, vs, torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, wl.num_pages)
+    assert torch.equal(wl.k_pool, before_k) and torch.equal(wl.v_pool, before_v)
+    step = DecodeStep.for_workload(wl, min_chunk_tokens=1)
+    info = step.plan_workload(wl)
+    out, lse = new_output(wl)
+    step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.synchronize()
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, f"written {s.name}")
+    compare_lse(lse, LSE, f"written {s.name}")
