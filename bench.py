@@ -2,8 +2,9 @@
 
 A step is the whole hot path on one batch: the split-KV plan, dynamic e4m3
 Q quantization, the paged decode and the LSE merge of split partials.  The
-timed step is a hipGraph of two kernels, the device planner and
-``mj_decode_step`` (quantization, decode and merge fused into one launch).
+timed step is a hipGraph of ``mj_decode_step`` planning from the device
+lengths itself: the decode kernel (each workgroup derives its plan item and
+quantizes its Q rows) and, when the plan splits, the merge kernel.
 Inputs are seeded synthetic tensors already resident in HBM.  The Infinity
 Cache is flushed (a 1 GiB write) before every step, outside that step's
 event pair, so KV bytes come from HBM.
@@ -163,31 +164,47 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     step3_ms = np.array([e[0].elapsed_time(e[3]) for e in ev3])
     dec3_ms = np.array([e[1].elapsed_time(e[2]) for e in ev3])
 
-    # the step as one hipGraph: device-side plan + fused step
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step.plan_workload_device(wl, stream=side)
-        step.run_workload(wl, out, lse, stream=side, fused=True)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        gs = torch.cuda.current_stream()
-        ginfo = step.plan_workload_device(wl, stream=gs)
-        step.run_workload(wl, out, lse, info=ginfo, stream=gs, fused=True)
-    torch.cuda.synchronize()
-    gev = [(E(), E()) for _ in range(steps)]
-    for _ in range(warmup):
-        flush_buf.add_(1)
-        graph.replay()
-    for k in range(steps):
-        flush_buf.add_(1)
-        gev[k][0].record(stream)
-        graph.replay()
-        gev[k][1].record(stream)
-    torch.cuda.synchronize()
-    graph_ms = np.array([a.elapsed_time(b) for a, b in gev])
+    # the step as one hipGraph of mj_decode_step planning from the device
+    # lengths itself; for comparison, a graph of the device planner kernel
+    # followed by the step on its plan
+    def capture(planner_kernel):
+        def body(st):
+            if planner_kernel:
+                gi = step.plan_workload_device(wl, stream=st)
+                step.run_workload(wl, out, lse, info=gi, stream=st, fused=True)
+            else:
+                gi = step.plan_workload_shape(wl)
+                step.run_workload(wl, out, lse, info=gi, stream=st, fused=True, plan_on_device=True)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            body(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            body(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return gr
+
+    def time_graph(gr, n):
+        gev = [(E(), E()) for _ in range(n)]
+        for _ in range(warmup):
+            flush_buf.add_(1)
+            gr.replay()
+        for k in range(n):
+            flush_buf.add_(1)
+            gev[k][0].record(stream)
+            gr.replay()
+            gev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in gev])
+
+    graph = capture(False)
+    graph_ms = time_graph(graph, steps)
+    del graph
+    graph = capture(True)
+    graph_pk_ms = time_graph(graph, max(5, steps // 2))
     del graph
 
     # kernel duration for the roofline: the fused step as one launch (the
@@ -241,6 +258,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
         graph_us_per_step_p10=float(np.percentile(graph_ms, 10) * 1e3),
         graph_us_per_step_p90=float(np.percentile(graph_ms, 90) * 1e3),
         graph_step_kv_gbs=kvb / (graph_ms.mean() * 1e-3) / 1e9,
+        graph_with_planner_kernel_us_per_step_median=float(np.median(graph_pk_ms) * 1e3),
         step_kv_gbs=kvb / (step_ms.mean() * 1e-3) / 1e9,
         kernel_us_back_to_back=kernel_us, kernel_launches=reps, kv_pool_copies=n_copies,
         kernel_kv_gbs=kvb / (kernel_us * 1e-6) / 1e9,
@@ -266,7 +284,9 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
             ms.append(e0.elapsed_time(e1))
         res["stream_read_gbs"] = nbytes / (np.median(ms[2:]) * 1e-3) / 1e9
         log(f"[bench] {key}: plain streaming read of {nbytes} B: {res['stream_read_gbs']:.0f} GB/s")
-    log(f"[bench] {key}: step {res['graph_us_per_step_median']:.1f} us graph / {res['us_per_step_median']:.1f} us "
+    log(f"[bench] {key}: step {res['graph_us_per_step_median']:.1f} us graph "
+        f"({res['graph_with_planner_kernel_us_per_step_median']:.1f} with the planner kernel) / "
+        f"{res['us_per_step_median']:.1f} us "
         f"eager / {res['three_call_us_per_step_median']:.1f} us three calls (median); decode kernel "
         f"{kernel_us:.1f} us = {res['kernel_kv_gbs']:.0f} GB/s KV ({100 * res['kernel_frac_of_hbm_peak']:.1f}% "
         f"of 8 TB/s); in-step decode {res['step_decode_us_mean']:.1f} us fused / "
@@ -421,7 +441,7 @@ def main():
         data="synthetic",
         config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"], kernel_variant=args.variant,
                     nontemporal=not args.no_nt, step_merge=args.step_merge,
-                    step="hipGraph: device plan + mj_decode_step"),
+                    step="hipGraph: mj_decode_step with plan_on_device (decode + merge launches)"),
         roofline=roof,
         cpu_baseline=cpu,
         detail=main_res,

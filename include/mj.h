@@ -231,6 +231,11 @@ mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_
                                   int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev, mj_plan_info* info,
                                   hipStream_t stream);
 
+/* What a plan for (num_seqs, q_len) has regardless of the lengths: num_work,
+ * slots, with_reduction, kv_tile_tokens, min_chunk_tiles (chunk_tiles =
+ * num_chunks = -1).  Host only.  Errors: EINVAL, ECAPACITY. */
+mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, mj_plan_info* info);
+
 /* Dynamic e4m3 quantization of Q per (sequence, KV head) (README "What it
  * does", step 2; runner.py T5DecodeRunner.run, fp8-Q branch): over the q_len
  * tokens and h_r heads of KV head g, x = fp32(q) [* q_mul], amax =
@@ -317,6 +322,12 @@ typedef struct mj_step_args {
   int64_t q_tok_stride;         /* elements                                  */
   int64_t q_head_stride;        /* elements                                  */
   const float* q_mul;           /* nullable (h_q, 128)                       */
+  int32_t plan_on_device;       /* 1: plan this step from decode.seq_lens
+                                   (as mj_plan_split_kv_device, with margin
+                                   below) instead of reading a prepared plan;
+                                   decode.plan still receives the plan's
+                                   n_splits / split_begin                    */
+  int32_t margin;               /* plan margin when plan_on_device           */
 } mj_step_args;
 
 /* mj_quantize_q + mj_paged_decode + mj_merge_lse (README "What it does",
@@ -329,7 +340,12 @@ typedef struct mj_step_args {
  * a pair to finish merges in the decode kernel itself (device-coherent
  * partials, an arrival counter in the workspace) and the step is one
  * launch.  Otherwise it enqueues the three kernels, staging Q codes in the
- * workspace.  Calls that
+ * workspace.  With plan_on_device the step also plans: where the matrix-core
+ * kernel serves the shape and num_seqs <= 256, every decode workgroup
+ * derives its own work item from the device lengths (the planner's rule,
+ * no plan launch, the separate merge launch); otherwise the device planner
+ * runs first.  The result is bit-identical to planning with
+ * mj_plan_split_kv_device and calling the step on that plan.  Calls that
  * share a workspace must not overlap (one stream, or ordered streams).
  * Errors: those of the three calls. */
 mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStream_t stream);

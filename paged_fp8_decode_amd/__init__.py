@@ -96,6 +96,12 @@ def mj_plan_split_kv_device(cfg: Config, seq_lens_dev, num_seqs: int, q_len: int
     return info
 
 
+def mj_plan_shape(cfg: Config, num_seqs: int, q_len: int) -> PlanInfo:
+    info = PlanInfo()
+    check(lib().mj_plan_shape(ctypes.byref(cfg), num_seqs, q_len, ctypes.byref(info)), "mj_plan_shape")
+    return info
+
+
 def mj_quantize_q(cfg: Config, q, q_mul, num_seqs: int, q_len: int, q8, q_descale, stream=None):
     """q: bf16 torch view (tokens, h_q, 128) with unit channel stride."""
     assert q.stride(2) == 1

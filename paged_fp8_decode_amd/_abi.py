@@ -73,6 +73,7 @@ class WriteArgs(ctypes.Structure):
 class StepArgs(ctypes.Structure):
     _fields_ = [
         ("decode", DecodeArgs), ("q", _p), ("q_tok_stride", _i64), ("q_head_stride", _i64), ("q_mul", _p),
+        ("plan_on_device", _i32), ("margin", _i32),
     ]
 
 
@@ -93,6 +94,7 @@ def _load():
         "mj_plan_compute": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo)]),
         "mj_plan_split_kv": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, _p, P(PlanInfo), _p]),
         "mj_plan_split_kv_device": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo), _p]),
+        "mj_plan_shape": (_i32, [P(Config), _i32, _i32, P(PlanInfo)]),
         "mj_quantize_q": (_i32, [P(Config), _p, _i64, _i64, _p, _i32, _i32, _p, _p, _p]),
         "mj_paged_decode": (_i32, [P(Config), P(DecodeArgs), _p]),
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),

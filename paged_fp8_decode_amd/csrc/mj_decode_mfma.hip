@@ -49,6 +49,7 @@
 #include "mj_device.h"
 #include "mj_internal.h"
 #include "mj_merge.h"
+#include "mj_plan_item.h"
 
 namespace mj {
 
@@ -430,14 +431,37 @@ void decode_mfma_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, jj = lane >> 4;
-  const int seq = p.work[4 * w];
+  int seq, tb, te;
+  bool single;
+  int plan_n = 0, plan_begin = 0;
+  bool plan_writer = false;  // this workgroup publishes its sequence's split count (in the epilogue)
+  if (p.plan_in_kernel) {
+    const PlanItem it = plan_item_wave(p.seq_lens, p.num_seqs, w, p.plan_margin, p.kv_tile,
+                                       (int64_t)p.max_blocks * p.page_size, p.plan_max_splits, p.plan_slots,
+                                       p.plan_split != 0, p.plan_min_chunk);
+    // wave-uniform by construction; said so, so that everything addressed
+    // through them (block-table entries above all) stays scalar
+    seq = __builtin_amdgcn_readfirstlane(it.seq);
+    tb = __builtin_amdgcn_readfirstlane(it.tb);
+    te = __builtin_amdgcn_readfirstlane(it.te);
+    single = __builtin_amdgcn_readfirstlane(it.n) <= 1;
+    plan_n = it.n;
+    plan_begin = it.begin;
+    plan_writer = it.split == 0 && g == 0;
+  } else {
+    seq = p.work[4 * w];
+    tb = p.work[4 * w + 1];
+    te = p.work[4 * w + 2];
+    single = true;  // read below, once seq is known to be valid
+  }
   if (seq < 0 || seq >= p.num_seqs) return;
+  if (!p.plan_in_kernel) single = p.n_splits[seq] <= 1;
 
   int L = p.seq_lens[seq];
   L = max(0, min(L, p.max_blocks * p.page_size));
   Ctx c;
-  c.j0 = p.work[4 * w + 1] * p.kv_tile;
-  c.j1 = min(p.work[4 * w + 2] * p.kv_tile, L);
+  c.j0 = tb * p.kv_tile;
+  c.j1 = min(te * p.kv_tile, L);
   c.causal = p.causal && p.q_len > 1;
   c.lim0 = L - p.q_len;
   c.n = n;
@@ -530,7 +554,6 @@ void decode_mfma_kernel(DecodeParams p) {
     qdesc = p.q_descale[(int64_t)seq * p.h_k + g];
   }
   c.cscale = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
-  const bool single = p.n_splits[seq] <= 1;
 
   // B operands of QK^T: column n of block R = Q row 16R + n % NQB (zero past n_q)
   v8i qb[NRB];
@@ -659,6 +682,15 @@ void decode_mfma_kernel(DecodeParams p) {
         store_coherent(&p.l_part[idx], Lsum);
       }
     }
+  }
+
+  // the in-kernel plan's split count and first item of this sequence, for
+  // the merge launch that follows; stored after the main loop so that no
+  // integer store precedes the block-table reads (which then stay scalar
+  // loads of memory the kernel provably does not write before them)
+  if (plan_writer && threadIdx.x == 0) {
+    p.ns_out[seq] = plan_n;
+    p.sb_out[seq] = plan_begin;
   }
 
   if (!single && p.counters) {

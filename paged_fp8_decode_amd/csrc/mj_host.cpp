@@ -257,13 +257,43 @@ mj_status mj_plan_split_kv(const mj_config* cfg, const int32_t* seq_lens_host, i
   return MJ_OK;
 }
 
+static mj_status plan_device(const mj_config* cfg, const Derived& d, const int32_t* seq_lens_dev, int32_t num_seqs,
+                             int32_t q_len, int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev,
+                             mj_plan_info* info, hipStream_t stream);
+
+mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, mj_plan_info* info) {
+  Derived d;
+  mj_status st = derive(cfg, &d);
+  if (st != MJ_OK) return st;
+  if (!info || num_seqs < 1 || q_len < 1) return MJ_EINVAL;
+  if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  const int S = slots_for(cfg, d, q_len);
+  info->num_work = cap_for(cfg, d, q_len);
+  info->slots = S;
+  info->chunk_tiles = -1;
+  info->num_chunks = -1;
+  info->with_reduction = cfg->max_splits > 1 && num_seqs < S ? 1 : 0;
+  info->num_seqs = num_seqs;
+  info->q_len = q_len;
+  info->kv_tile_tokens = d.kv_tile;
+  info->min_chunk_tiles = min_chunk_tiles(cfg, d, q_len);
+  return MJ_OK;
+}
+
 mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_dev, int32_t num_seqs, int32_t q_len,
                                   int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev, mj_plan_info* info,
                                   hipStream_t stream) {
   Derived d;
   mj_status st = derive(cfg, &d);
   if (st != MJ_OK) return st;
-  if (!seq_lens_dev || !plan_dev || !info || num_seqs < 1 || q_len < 1 || margin < 0 || max_blocks_per_seq < 1)
+  if (!info) return MJ_EINVAL;
+  return plan_device(cfg, d, seq_lens_dev, num_seqs, q_len, margin, max_blocks_per_seq, plan_dev, info, stream);
+}
+
+static mj_status plan_device(const mj_config* cfg, const Derived& d, const int32_t* seq_lens_dev, int32_t num_seqs,
+                             int32_t q_len, int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev,
+                             mj_plan_info* info, hipStream_t stream) {
+  if (!seq_lens_dev || !plan_dev || num_seqs < 1 || q_len < 1 || margin < 0 || max_blocks_per_seq < 1)
     return MJ_EINVAL;
   if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
   if (!aligned(plan_dev, 16) || !aligned(seq_lens_dev, 4)) return MJ_EALIGN;
@@ -286,6 +316,7 @@ mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_
   p.cap_max = d.cap_max;
   p.min_chunk = min_chunk_tiles(cfg, d, q_len);
   if (mj::launch_plan(p, stream) != hipSuccess) return MJ_EHIP;
+  if (!info) return MJ_OK;
   info->num_work = cap_for(cfg, d, q_len);
   info->slots = S;
   info->chunk_tiles = -1;  // decided on the device
@@ -399,6 +430,9 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->qb_ts = p->qb_hs = 0;
   p->q_mul = nullptr;
   p->counters = nullptr;
+  p->plan_in_kernel = 0;
+  p->plan_margin = p->plan_max_splits = p->plan_slots = p->plan_split = p->plan_min_chunk = 0;
+  p->ns_out = p->sb_out = nullptr;
   return MJ_OK;
 }
 
@@ -438,10 +472,31 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   mj_decode_args a = sa->decode;
   a.q8 = q8;
   a.q_descale = qd;
+  if (sa->plan_on_device && sa->margin < 0) return MJ_EINVAL;
   mj::DecodeParams p;
   st = fill_decode(cfg, d, &a, &p);
   if (st != MJ_OK) return st;
   const int rt = row_tiles(cfg, a.q_len);
+  // plan in the decode kernel: matrix-core kernel, a batch the wave-level
+  // planner covers, tile counts small enough for its float quotients
+  const int64_t max_tiles = ((int64_t)a.max_blocks_per_seq * cfg->page_size + sa->margin + d.kv_tile - 1) / d.kv_tile;
+  const bool plan_in_kernel = sa->plan_on_device && mj::decode_fuses_step(p, cfg->kv_format, rt) &&
+                              a.num_seqs <= mj::kPlanMaxSeqs && 2 * max_tiles < (1 << 22);
+  if (sa->plan_on_device && !plan_in_kernel) {
+    st = plan_device(cfg, d, a.seq_lens, a.num_seqs, a.q_len, sa->margin, a.max_blocks_per_seq,
+                     const_cast<int32_t*>(a.plan), nullptr, stream);
+    if (st != MJ_OK) return st;
+  }
+  if (plan_in_kernel) {
+    p.plan_in_kernel = 1;
+    p.plan_margin = sa->margin;
+    p.plan_max_splits = cfg->max_splits;
+    p.plan_slots = slots_for(cfg, d, a.q_len);
+    p.plan_split = a.with_reduction ? 1 : 0;
+    p.plan_min_chunk = min_chunk_tiles(cfg, d, a.q_len);
+    p.ns_out = const_cast<int32_t*>(p.n_splits);
+    p.sb_out = const_cast<int32_t*>(p.split_begin);
+  }
   mj_merge_args m;
   m.plan = a.plan;
   m.num_seqs = a.num_seqs;
@@ -457,7 +512,7 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
     p.qb_ts = sa->q_tok_stride;
     p.qb_hs = sa->q_head_stride;
     p.q_mul = sa->q_mul;
-    const bool merge_in_kernel = g_step_merge == 1;
+    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel;  // its merge reads this launch's plan
     p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
     if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
     return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;

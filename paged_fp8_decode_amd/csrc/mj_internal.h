@@ -59,6 +59,14 @@ struct DecodeParams {
   int64_t qb_ts, qb_hs;        // elements
   const float* q_mul;          // nullable (h_q, 128)
   int32_t* counters;
+  // Plan in the kernel (matrix-core kernel, fused step): every workgroup
+  // derives its item from seq_lens with the planner's rule, and the split-0
+  // workgroup of KV head 0 writes n_splits / split_begin of its sequence for
+  // the merge launch.  `work` is not read then.
+  int plan_in_kernel;
+  int plan_margin, plan_max_splits, plan_slots, plan_split, plan_min_chunk;
+  int32_t* ns_out;
+  int32_t* sb_out;
 };
 
 struct MergeParams {
@@ -112,6 +120,7 @@ struct PlanParams {
 };
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+constexpr int kPlanMaxSeqs = 256;  // batches the decode kernel plans itself (mj_plan_item.h)
 hipError_t launch_qquant(const QQuantParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
 bool decode_fuses_step(const DecodeParams& p, int kv_format, int row_tiles);

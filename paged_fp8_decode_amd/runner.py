@@ -11,7 +11,7 @@ from __future__ import annotations
 import torch
 
 from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, StepArgs, check, mj_config, mj_config_check,
-               mj_decode_step, mj_merge_lse, mj_paged_decode, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
+               mj_decode_step, mj_merge_lse, mj_paged_decode, mj_plan_shape, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
                mj_quantize_q, mj_workspace_bytes)
 
 
@@ -68,17 +68,26 @@ class DecodeStep:
         self.info = info
         return info
 
+    def plan_shape(self, num_seqs: int, q_len: int) -> PlanInfo:
+        """The plan's size fields for a batch (no planning, no device work)."""
+        info = mj_plan_shape(self.cfg, num_seqs, q_len)
+        self.info = info
+        return info
+
     def run(self, *, q, k_cache, v_cache, k_strides, v_strides, num_pages, block_table, seq_lens, k_descale,
             v_descale, descale_kind, softmax_scale, out, lse=None, q_mul=None, o_mul=None, causal=True,
-            info: PlanInfo | None = None, stream=None, events=None, fused=False):
+            info: PlanInfo | None = None, stream=None, events=None, fused=False, plan_on_device=False, margin=0):
         """quantize Q -> decode -> merge (iff the plan split), all on ``stream``;
         with ``fused`` one ``mj_decode_step`` call instead.
 
         q: bf16 (b*q_len, h_q, 128) view; out: bf16 (b*q_len, h_q, 128) view;
         k/v strides: bytes (page, slot, head); block_table: int32 (b, max_blocks).
         ``events``: optional pair of events recorded right before and right
-        after the decode launch (the step call when fused).
+        after the decode launch (the step call when fused).  ``plan_on_device``
+        (fused only): the step plans from ``seq_lens`` itself (``info`` from
+        ``plan_shape``).
         """
+        assert fused or not plan_on_device
         info = info or self.info
         assert info is not None, "plan() first"
         b, ql = info.num_seqs, info.q_len
@@ -104,7 +113,8 @@ class DecodeStep:
             a.q8 = None
             a.q_descale = None
             sa = StepArgs(decode=a, q=q.data_ptr(), q_tok_stride=q.stride(0), q_head_stride=q.stride(1),
-                          q_mul=q_mul.data_ptr() if q_mul is not None else None)
+                          q_mul=q_mul.data_ptr() if q_mul is not None else None,
+                          plan_on_device=int(plan_on_device), margin=margin)
             if events:
                 events[0].record(stream)
             mj_decode_step(self.cfg, sa, stream)
@@ -139,13 +149,18 @@ class DecodeStep:
     def plan_workload_device(self, wl, margin=0, stream=None) -> PlanInfo:
         return self.plan_device(wl.seq_lens_dev, wl.spec.b, wl.spec.q_len, wl.block_table.shape[1], margin, stream)
 
-    def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None, fused=False):
+    def plan_workload_shape(self, wl) -> PlanInfo:
+        return self.plan_shape(wl.spec.b, wl.spec.q_len)
+
+    def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None, fused=False,
+                     plan_on_device=False):
         ks, vs = wl.kv_strides()
         return self.run(q=wl.q, k_cache=wl.k_pool, v_cache=wl.v_pool, k_strides=ks, v_strides=vs,
                         num_pages=wl.num_pages, block_table=wl.block_table, seq_lens=wl.seq_lens_dev,
                         k_descale=wl.k_descale, v_descale=wl.v_descale, descale_kind=wl.descale_kind,
                         softmax_scale=wl.softmax_scale, out=out, lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul,
-                        causal=wl.spec.causal, info=info, stream=stream, events=events, fused=fused)
+                        causal=wl.spec.causal, info=info, stream=stream, events=events, fused=fused,
+                        plan_on_device=plan_on_device)
 
 
 def new_output(wl, device=None):

@@ -1,0 +1,70 @@
+"""Code-generation invariants of the decode kernel (host only: hipcc
+cross-compiles gfx950 here).  Each guards a regression that once cost tens
+of percent while every numeric test still passed:
+
+* no scratch (register spills) in the instances the library launches;
+* no agent-scope L2 writeback / invalidate (each one flushes an XCD's L2);
+* the main loop keeps the next granule's loads in flight: its first waits
+  on vector memory leave at least 8 loads outstanding (a wait for zero there
+  means the loop drains every load each granule -- seen when a pending load
+  of uncertain provenance reached the loop, and when block-table reads
+  turned into vector loads).
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "paged_fp8_decode_amd", "csrc", "mj_decode_mfma.hip")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# the instances the default dispatch launches: (format, rows per block,
+# row blocks, non-temporal, prefetch, waves per SIMD)
+DEFAULT = ["Li0ELi4ELi1ELb1ELi1ELi2E", "Li0ELi8ELi1ELb1ELi1ELi2E", "Li0ELi16ELi1ELb1ELi1ELi2E",
+           "Li0ELi16ELi2ELb1ELi1ELi1E", "Li1ELi4ELi1ELb1ELi1ELi2E", "Li1ELi8ELi1ELb1ELi1ELi2E",
+           "Li1ELi16ELi1ELb1ELi1ELi2E", "Li1ELi16ELi2ELb1ELi1ELi1E"]
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "mfma.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fhip-fp32-correctly-rounded-divide-sqrt",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics", "--cuda-device-only",
+           "-S", "-o", str(out), SRC]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    return out.read_text().splitlines()
+
+
+def _body(lines, inst):
+    name = f"_ZN2mj12_GLOBAL__N_118decode_mfma_kernelI{inst}EEvNS_12DecodeParamsE:"
+    i = next(j for j, l in enumerate(lines) if l.startswith(name))
+    e = next(j for j in range(i, len(lines)) if "s_endpgm" in lines[j])
+    meta = next(j for j in range(e, len(lines)) if lines[j].strip().startswith(".private_segment_fixed_size") or
+                ".private_segment_fixed_size" in lines[j])
+    return lines[i:e], lines[e:meta + 1]
+
+
+@pytest.mark.parametrize("inst", DEFAULT)
+def test_no_scratch_and_no_l2_flush(asm, inst):
+    body, meta = _body(asm, inst)
+    scratch = [l for l in meta if ".private_segment_fixed_size" in l]
+    assert scratch and int(scratch[-1].split()[-1]) == 0, scratch
+    text = "\n".join(body)
+    assert "buffer_wbl2" not in text and "buffer_inv" not in text
+    assert "scratch_" not in text
+
+
+@pytest.mark.parametrize("inst", DEFAULT)
+def test_main_loop_keeps_loads_in_flight(asm, inst):
+    body, _ = _body(asm, inst)
+    heads = [j for j, l in enumerate(body) if "Loop Header" in l]
+    loop = next(j for j in heads if any("v_mfma_scale" in x for x in body[j:j + 300]) and
+                any("buffer_load" in x for x in body[j:j + 300]))
+    waits = [int(re.search(r"vmcnt\((\d+)\)", x).group(1)) for x in body[loop:loop + 1500] if "vmcnt(" in x][:4]
+    assert len(waits) == 4 and min(waits) >= 8, waits

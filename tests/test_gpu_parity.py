@@ -403,3 +403,79 @@ def test_fused_step_graph_replay(mj, gpu, step_merge):
         O, LSE = oracle_step(wl)
         compare_out(out, O, f"fused replay {trial} lens={lens}")
         compare_lse(lse, LSE, f"fused replay {trial}")
+
+
+@pytest.mark.parametrize("shape", [dict(h_q=32, h_k=8, q_len=1), dict(h_q=64, h_k=8, q_len=4),
+                                   dict(h_q=8, h_k=2, q_len=1, kv_format="e2m3")])
+def test_plan_in_kernel_matches_host_plan(mj, gpu, shape):
+    """mj_decode_step with plan_on_device: the decode workgroups derive their
+    items from the device lengths.  Outputs are bit-identical to the step on
+    the host plan, and n_splits / split_begin in the plan buffer equal the
+    host plan's; batches beyond the in-kernel limit take the device
+    planner."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    key = "cfg5" if shape.get("kv_format") == "e2m3" else "cfg2"
+    rng = np.random.default_rng(31 + shape["q_len"])
+    for trial, b in enumerate([1, 3, 17, 64, 130, 256, 260]):
+        lens = tuple(int(x) for x in rng.integers(0, 700, size=b))
+        if trial == 2:
+            lens = (0,) * b
+        over = dict(b=b, lens=lens, h_q=shape["h_q"], h_k=shape["h_k"], q_len=shape["q_len"], k_outliers=0)
+        wl = synth.build(synth.spec_for(key, small=True, **over), gpu)
+        for mct in (0, 1):
+            step = DecodeStep.for_workload(wl, min_chunk_tokens=mct)
+            info = step.plan_workload(wl)
+            img, _ = mj.mj_plan_compute(step.cfg, np.array(wl.seq_lens, np.int32), shape["q_len"], 0,
+                                        wl.block_table.shape[1])
+            ref_o, ref_l = new_output(wl)
+            step.run_workload(wl, ref_o, ref_l, info=info, fused=True)
+            step.plan_dev.fill_(-5)
+            sinfo = step.plan_workload_shape(wl)
+            assert (sinfo.num_work, sinfo.with_reduction) == (info.num_work, info.with_reduction)
+            out, lse = new_output(wl)
+            out.fill_(float("nan"))
+            step.run_workload(wl, out, lse, info=sinfo, fused=True, plan_on_device=True)
+            torch.cuda.synchronize()
+            say(f"  plan-in-kernel {shape} b={b} mct={mct} splits={info.with_reduction} chunk={info.chunk_tiles}")
+            assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"b={b} mct={mct}"
+            assert torch.equal(lse, ref_l), f"b={b} mct={mct}"
+            if info.with_reduction:
+                cap_max = (img.size - 2 * step.cfg.max_num_seqs) // 4
+                got = step.plan_dev.cpu().numpy()
+                ns = slice(4 * cap_max, 4 * cap_max + b)
+                sb = slice(4 * cap_max + step.cfg.max_num_seqs, 4 * cap_max + step.cfg.max_num_seqs + b)
+                assert np.array_equal(got[ns], img[ns]) and np.array_equal(got[sb], img[sb]), f"b={b}"
+
+
+def test_plan_in_kernel_graph_replay(mj, gpu):
+    """One graph of just the step (planning included) follows new device
+    lengths replay after replay."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for("cfg3", small=True), gpu)
+    say(f"plan-in-kernel graph {wl.spec.name}")
+    step = DecodeStep.for_workload(wl, **FINE)
+    out, lse = new_output(wl)
+    info = step.plan_workload_shape(wl)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run_workload(wl, out, lse, info=info, fused=True, plan_on_device=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run_workload(wl, out, lse, info=info, fused=True, plan_on_device=True)
+    torch.cuda.synchronize()
+    orig = list(wl.seq_lens)
+    rng = np.random.default_rng(19)
+    for trial in range(5):
+        lens = [int(x) for x in rng.integers(0, np.array(orig) + 1)]
+        wl.seq_lens = lens
+        wl.seq_lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        O, LSE = oracle_step(wl)
+        compare_out(out, O, f"plan-in-kernel replay {trial} lens={lens}")
+        compare_lse(lse, LSE, f"plan-in-kernel replay {trial}")
