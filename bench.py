@@ -18,7 +18,9 @@ one event pair around back-to-back single-launch steps (merge in the decode
 kernel) that rotate over copies of the KV pools (no launch reads KV the
 Infinity Cache still holds).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.
+workload.  ``bf16_q`` measures the same step in the bf16-Q mode (Q used as
+given, no quantization; the KV codes converted to bf16 in the kernel) on the
+workloads ``--bf16q`` names.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--extra 32k,cfg3,...]
 """
@@ -88,6 +90,8 @@ def parse():
     ap.add_argument("--extra", default="32k,32k_b16",
                     help="comma list of extra workloads reported under 'extra' ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--bf16q", default="cfg2,32k",
+                    help="comma-separated workloads also measured in the bf16-Q mode ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--variant", type=int, default=0,
                     help="decode kernel: 0 automatic, 1 generic, 2 VALU-PV streaming (A/B runs)")
@@ -121,7 +125,7 @@ def calibrate():
     print(json.dumps(dict(calibration=True, stream_read_bytes=n, copy_bytes=n)), flush=True)
 
 
-def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
+def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mode="fp8"):
     import torch
     import synth
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
@@ -130,7 +134,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     wl = synth.build(synth.spec_for(key), "cuda")
     torch.cuda.synchronize()
     log(f"[bench] {key}: built {wl.spec.name} in {time.time() - t0:.1f}s, kv_bytes={wl.kv_bytes()}")
-    step = DecodeStep.for_workload(wl, wgs_per_cu=wgs_per_cu)
+    step = DecodeStep.for_workload(wl, wgs_per_cu=wgs_per_cu, q_mode=q_mode)
     out, lse = new_output(wl)
     stream = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -246,7 +250,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
     del pools
 
     res = dict(
-        workload=wl.spec.name, kv_bytes=kvb, steps=steps,
+        workload=wl.spec.name, q_mode=q_mode, kv_bytes=kvb, steps=steps,
         us_per_step_median=float(np.median(step_ms) * 1e3), us_per_step_mean=float(step_ms.mean() * 1e3),
         us_per_step_p10=float(np.percentile(step_ms, 10) * 1e3),
         us_per_step_p90=float(np.percentile(step_ms, 90) * 1e3),
@@ -284,7 +288,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False):
             ms.append(e0.elapsed_time(e1))
         res["stream_read_gbs"] = nbytes / (np.median(ms[2:]) * 1e-3) / 1e9
         log(f"[bench] {key}: plain streaming read of {nbytes} B: {res['stream_read_gbs']:.0f} GB/s")
-    log(f"[bench] {key}: step {res['graph_us_per_step_median']:.1f} us graph "
+    log(f"[bench] {key} ({q_mode} Q): step {res['graph_us_per_step_median']:.1f} us graph "
         f"({res['graph_with_planner_kernel_us_per_step_median']:.1f} with the planner kernel) / "
         f"{res['us_per_step_median']:.1f} us "
         f"eager / {res['three_call_us_per_step_median']:.1f} us three calls (median); decode kernel "
@@ -410,6 +414,10 @@ def main():
     extra = {}
     for k in [x for x in args.extra.split(",") if x]:
         extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu, False)
+    bf16q = {}
+    for k in [x for x in args.bf16q.split(",") if x]:
+        bf16q[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu, False,
+                           q_mode="bf16")
     writes = []
     if not args.no_write:
         for fmt in ("e4m3", "e2m3"):
@@ -446,6 +454,7 @@ def main():
         cpu_baseline=cpu,
         detail=main_res,
         extra=extra,
+        bf16_q=bf16q,
         write_kv=writes,
     )
     print(json.dumps(line), flush=True)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 3
+#define MJ_ABI_VERSION 4
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -66,6 +66,17 @@ typedef enum mj_kv_format {
                       being bit j of byte B (runner.py, comment above
                       RUNNER_KV_FORMATS: "little-endian bitstream")             */
 } mj_kv_format;
+
+/* How the decode takes Q (runner.py, T5DecodeRunner.__init__ `q_mode`, and
+ * the backend's MJOLNIR_ATTN_Q_DTYPE): quantized per (sequence, KV head) to
+ * e4m3 by mj_quantize_q, or used as is in bf16 with the KV codes converted
+ * to bf16 inside the decode kernel (e4m3 KV only: the packed e2m3 cache
+ * takes fp8 Q only, per the runner's kv_format comment). */
+typedef enum mj_q_mode {
+  MJ_Q_FP8 = 0,   /* dynamic e4m3 Q: mj_quantize_q, then q8 / q_descale        */
+  MJ_Q_BF16 = 1   /* bf16 Q as given: logit = softmax_scale * k_descale *
+                     sum_c q_c * dec(k_c); no Q quantization step           */
+} mj_q_mode;
 
 /* Shape of a K or V descale tensor (runner.py, T5DecodeRunner.run: k_scale /
  * v_scale are fp32 with 1 element, (h_k,) or (b, h_k)). */
@@ -94,6 +105,7 @@ typedef struct mj_config {
   int32_t slots_override;  /* work items per plan; 0 = num_cus*wgs_per_cu/h_k   */
   int32_t kv_format;       /* mj_kv_format                                      */
   int32_t min_chunk_tokens;/* floor of a split chunk; 0 = default (below)       */
+  int32_t q_mode;          /* mj_q_mode (0 = fp8)                               */
 } mj_config;
 /* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):
  * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
@@ -117,7 +129,7 @@ typedef struct mj_plan_info {
 /* Arguments of mj_paged_decode.  All strides are in BYTES for the KV cache and
  * in ELEMENTS (bf16) for the output. */
 typedef struct mj_decode_args {
-  /* Q from mj_quantize_q */
+  /* Q from mj_quantize_q (MJ_Q_FP8; not read in MJ_Q_BF16 mode)            */
   const uint8_t* q8;          /* (num_seqs, h_k, q_len*h_r, 128) e4m3, contiguous */
   const float* q_descale;     /* (num_seqs, h_k)                                  */
   int32_t num_seqs;
@@ -158,6 +170,11 @@ typedef struct mj_decode_args {
   void* out;                  /* bf16 (num_seqs*q_len, h_q, 128) through strides  */
   int64_t out_tok_stride, out_head_stride;
   float* lse;                 /* nullable (num_seqs*q_len, h_q) fp32, natural log */
+  /* bf16 Q (MJ_Q_BF16 mode only; not read in MJ_Q_FP8 mode): element
+     (token, head, c) at q_bf16[token*q_tok_stride + head*q_head_stride + c],
+     token = i*q_len + t; 16-byte aligned, strides multiples of 8 elements  */
+  const void* q_bf16;
+  int64_t q_tok_stride, q_head_stride;
 } mj_decode_args;
 
 typedef struct mj_merge_args {
@@ -247,6 +264,7 @@ mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, m
  *      fused QKV buffer works); 16-byte aligned, strides multiples of 8.
  *   q_mul: nullable (h_q, 128) fp32 (fp6 K channel scales folded into Q).
  *   q8: (num_seqs, h_k, q_len*h_r, 128) bytes; q_descale: (num_seqs, h_k).
+ * It does not depend on cfg->q_mode (a MJ_Q_BF16 step simply never calls it).
  * Errors: EINVAL, EALIGN, ECAPACITY, EHIP. */
 mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_stride, int64_t q_head_stride,
                         const float* q_mul, int32_t num_seqs, int32_t q_len, uint8_t* q8, float* q_descale,
@@ -254,7 +272,9 @@ mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_strid
 
 /* Paged decode attention (README "What it does", step 3): for every plan item
  * (sequence i, token range) and KV head g, logit = softmax_scale *
- * q_descale[i,g] * k_descale * sum_c dec(q8)*dec(k) over the keys the row may
+ * q_descale[i,g] * k_descale * sum_c dec(q8)*dec(k) (MJ_Q_FP8), or
+ * softmax_scale * k_descale * sum_c q*dec(k) with the bf16 q_bf16 rows
+ * (MJ_Q_BF16; the products are exact in fp32) over the keys the row may
  * see (causal token t of a q_len block sees keys 0 .. L-q_len+t; q_len == 1
  * or non-causal: 0 .. L-1), online softmax, O = v_descale * sum_j p_j dec(v_j)
  * [* o_mul].  A sequence with one item writes bf16 O and LSE directly; a
@@ -263,8 +283,8 @@ mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_strid
  * LSE = -inf.
  * Errors: EINVAL (nulls, negative strides, descale kind out of range,
  * num_work / with_reduction not those of a plan for this config and q_len),
- * EALIGN (k/v/q8/out bases or byte strides not 16-byte aligned, out strides
- * not multiples of 8 elements), ECAPACITY (num_seqs, q_len, workspace
+ * EALIGN (k/v/q8/q_bf16/out bases or byte strides not 16-byte aligned, out
+ * and q_bf16 strides not multiples of 8 elements), ECAPACITY (num_seqs, q_len, workspace
  * missing or too small for a split plan), EUNSUPPORTED, EHIP. */
 mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* args, hipStream_t stream);
 
@@ -312,7 +332,8 @@ typedef struct mj_write_args {
 mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* args, hipStream_t stream);
 
 /* Arguments of one whole decode step after the plan: the decode arguments
- * (decode.q8 and decode.q_descale are not read and may be NULL;
+ * (decode.q8, decode.q_descale and decode.q_bf16 are not read and may be
+ * NULL;
  * decode.workspace is required, >= mj_workspace_bytes(cfg), 256-byte
  * aligned, counters zeroed once as described above) plus bf16 Q as
  * mj_quantize_q takes it. */
@@ -321,7 +342,8 @@ typedef struct mj_step_args {
   const void* q;                /* bf16; see mj_quantize_q for layout       */
   int64_t q_tok_stride;         /* elements                                  */
   int64_t q_head_stride;        /* elements                                  */
-  const float* q_mul;           /* nullable (h_q, 128)                       */
+  const float* q_mul;           /* nullable (h_q, 128); must be NULL in
+                                   MJ_Q_BF16 mode (EUNSUPPORTED)             */
   int32_t plan_on_device;       /* 1: plan this step from decode.seq_lens
                                    (as mj_plan_split_kv_device, with margin
                                    below) instead of reading a prepared plan;
@@ -345,7 +367,9 @@ typedef struct mj_step_args {
  * derives its own work item from the device lengths (the planner's rule,
  * no plan launch, the separate merge launch); otherwise the device planner
  * runs first.  The result is bit-identical to planning with
- * mj_plan_split_kv_device and calling the step on that plan.  Calls that
+ * mj_plan_split_kv_device and calling the step on that plan.  In MJ_Q_BF16
+ * mode there is nothing to quantize: the step is mj_paged_decode (+ merge)
+ * reading `q` as decode.q_bf16.  Calls that
  * share a workspace must not overlap (one stream, or ordered streams).
  * Errors: those of the three calls. */
 mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStream_t stream);
@@ -355,7 +379,9 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStre
  * (sequence, KV head) from the K (which = 0) or V (which = 1) pool into
  * dense_out (seq_len x row bytes), using the decode kernel's own address
  * computation.  mj_debug_decode_codes decodes n codes (one per byte; e2m3
- * codes in the low 6 bits) with the kernel's own decoder into fp32. */
+ * codes in the low 6 bits) with the kernel's own decoder into fp32;
+ * kv_format 2 decodes e4m3 codes through the bf16 operand converter of the
+ * MJ_Q_BF16 decode (fp32 of the bf16 it yields). */
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, int32_t seq, int32_t head,
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream);
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);

@@ -16,7 +16,7 @@ import ctypes
 import numpy as np
 
 from ._abi import (  # noqa: F401
-    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, MjError, KV_FORMATS, SCALE_KINDS,
+    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, MjError, KV_FORMATS, Q_MODES, SCALE_KINDS,
     MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
 )
 
@@ -35,11 +35,13 @@ def _ptr(t):
 
 
 def mj_config(*, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, num_cus=0, wgs_per_cu=0,
-              kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128, min_chunk_tokens=0) -> Config:
+              kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128, min_chunk_tokens=0,
+              q_mode="fp8") -> Config:
     c = Config(h_q=h_q, h_k=h_k, head_dim=head_dim, page_size=page_size, max_num_seqs=max_num_seqs,
                max_q_len=max_q_len, max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
                kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, min_chunk_tokens=min_chunk_tokens,
-               kv_format=KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format)
+               kv_format=KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format,
+               q_mode=Q_MODES[q_mode] if isinstance(q_mode, str) else q_mode)
     return c
 
 
@@ -134,7 +136,7 @@ def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_l
 
 
 def mj_debug_decode_codes(kv_format, codes, out, stream=None):
-    fmt = KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format
+    fmt = {**KV_FORMATS, "e4m3_bf16": 2}[kv_format] if isinstance(kv_format, str) else kv_format
     check(lib().mj_debug_decode_codes(fmt, _ptr(codes), codes.numel(), _ptr(out), _stream(stream)),
           "mj_debug_decode_codes")
 

@@ -8,9 +8,10 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 3  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 4  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
 KV_FORMATS = {"e4m3": 0, "e2m3": 1}
+Q_MODES = {"fp8": 0, "bf16": 1}
 SCALE_KINDS = {"tensor": 0, "head": 1, "seq_head": 2, "channel": 3}
 
 
@@ -24,7 +25,7 @@ class MjError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "h_q", "h_k", "head_dim", "page_size", "max_num_seqs", "max_q_len", "max_splits", "num_cus",
-        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens")]
+        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens", "q_mode")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -49,6 +50,7 @@ class DecodeArgs(ctypes.Structure):
         ("plan", _p), ("num_work", _i32), ("with_reduction", _i32), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
         ("softmax_scale", ctypes.c_float), ("o_mul", _p),
         ("out", _p), ("out_tok_stride", _i64), ("out_head_stride", _i64), ("lse", _p),
+        ("q_bf16", _p), ("q_tok_stride", _i64), ("q_head_stride", _i64),
     ]
 
 

@@ -67,11 +67,19 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const int lim0 = L - p.q_len;  // causal: token t sees keys j <= lim0 + t
 
   const float rescale = FMT == 0 ? kE4m3Rescale : kE2m3Rescale;
-  const float qs = p.q_descale[(int64_t)seq * p.h_k + g] * p.scale_log2;
+  const float qs = (p.q_bf16 ? 1.0f : p.q_descale[(int64_t)seq * p.h_k + g]) * p.scale_log2;
   const float kd = load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * rescale;
   const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k) * rescale;
-  const uint8_t* qsrc = p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + row0) * kHeadDim;
-  for (int e = tid; e < nr * kHeadDim; e += kThreads) q_s[e >> 7][e & 127] = e4m3_value(qsrc[e]) * qs;
+  if (p.q_bf16) {  // bf16 Q as is: packed row t*h_r + r is query head g*h_r + r of token t
+    for (int e = tid; e < nr * kHeadDim; e += kThreads) {
+      const int r = row0 + (e >> 7), t = r / p.h_r;
+      const int64_t tok = (int64_t)seq * p.q_len + t, h = (int64_t)g * p.h_r + (r - t * p.h_r);
+      q_s[e >> 7][e & 127] = __uint_as_float((uint32_t)p.qb[tok * p.qb_ts + h * p.qb_hs + (e & 127)] << 16) * qs;
+    }
+  } else {
+    const uint8_t* qsrc = p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + row0) * kHeadDim;
+    for (int e = tid; e < nr * kHeadDim; e += kThreads) q_s[e >> 7][e & 127] = e4m3_value(qsrc[e]) * qs;
+  }
   if (tid < kRT) {
     m_s[tid] = -INFINITY;
     l_s[tid] = 0.0f;
@@ -202,6 +210,12 @@ __global__ void gather_kernel(GatherParams p) {
 __global__ void decode_codes_kernel(int fmt, const uint8_t* codes, int n, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  if (fmt == 2) {  // e4m3 through the bf16 operand converter of the bf16-Q kernel
+    uint32_t h[2];
+    e4m3x4_to_bf16(codes[i], h);
+    out[i] = __uint_as_float(h[0] << 16);
+    return;
+  }
   out[i] = fmt == 0 ? e4m3_value(codes[i]) : e2m3_value(codes[i] & 63u);
 }
 

@@ -9,6 +9,14 @@
 // its split partials (device-coherent stores) the last split item of a
 // (sequence, KV head) to arrive merges them (mj_merge.h).
 //
+// bf16-Q mode (the runner's q_mode "bf16": Q as is, KV converted in the
+// kernel; FMT 2 below): the lane's 32 K codes of a tile become bf16 with the
+// hardware converter (exact) and QK^T is four v_mfma_f32_16x16x32_bf16 per
+// tile, the lane's codes [32jj + 8i, 32jj + 8i + 8) forming the contraction
+// slice of MFMA i; Q's B operands are the same channels of the bf16 rows,
+// loaded as they are.  Products of bf16 values are exact in fp32, so only
+// the accumulation rounds.
+//
 // Method: mjolnir-kernel README "What it does", step 3 (stream KV pages,
 // online softmax) and the partials step 4 merges.  The pages' Thor design
 // (TMA ring into shared memory, TMEM accumulators, fp8 P) is not followed;
@@ -88,6 +96,8 @@ struct Fmt<1> {                     // e2m3: 96-byte rows, 4 codes per 3 bytes
   static constexpr int kKDw = 6;
   static constexpr int kKOff = 24;
 };
+template <>
+struct Fmt<2> : Fmt<0> {};          // e4m3 KV with bf16 Q (bf16 MFMAs for QK^T)
 
 template <int FMT>
 struct KRows {  // tile k: this lane's codes [32jj, 32jj+32) of token n
@@ -172,7 +182,7 @@ __device__ __forceinline__ KRows<FMT> load_k(const Ctx& c, int gi) {
   for (int k = 0; k < 2; ++k) {
     const int tk = t0 + 16 * k;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.kpool, c.k_sp, c.k_ss, c.k_rec, tile_page(c, tk), tk, c.pmask);
-    if constexpr (FMT == 0) {
+    if constexpr (FMT != 1) {
       const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 0, aux);
       const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 16, aux);
 #pragma unroll
@@ -236,7 +246,7 @@ __device__ __forceinline__ v8i k_operand(const KRows<FMT>& K, int k) {
 // tokens tau(jj, 0..7), as 4 words of token pairs (2i, 2i+1).
 template <int FMT>
 __device__ __forceinline__ void v_operands(const Ctx& c, const VRows& V, uint32_t vb[8][4]) {
-  if constexpr (FMT == 0) {
+  if constexpr (FMT != 1) {
     float f[8][8];  // [token e][channel q]
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -282,6 +292,47 @@ __device__ __forceinline__ void v_operands(const Ctx& c, const VRows& V, uint32_
   }
 }
 
+// B operands of QK^T per 16-row block: fp8 codes (one MFMA per tile), or
+// bf16 Q channels [32jj + 8i, 32jj + 8i + 8) for MFMA i (bf16-Q mode).
+template <int FMT, int NRB>
+struct QOps {
+  v8i b[NRB];
+};
+template <int NRB>
+struct QOps<2, NRB> {
+  v8bf b[NRB][4];
+};
+
+// Unscaled Q.K dot products of tile k for every row block: lane (n, jj) gets
+// tokens 4jj + v of the tile against column n of the block.
+template <int FMT, int NRB>
+__device__ __forceinline__ void qk_tile(const KRows<FMT>& K, int k, const QOps<FMT, NRB>& q, v4f (&d)[NRB]) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (FMT == 2) {
+    v8bf ka[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h[4];
+      e4m3x4_to_bf16(K.d[k][2 * i], h);
+      e4m3x4_to_bf16(K.d[k][2 * i + 1], h + 2);
+      const u32x4 w = {h[0], h[1], h[2], h[3]};
+      ka[i] = __builtin_bit_cast(v8bf, w);
+    }
+#pragma unroll
+    for (int R = 0; R < NRB; ++R) {
+      v4f acc = zero;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i], q.b[R][i], acc, 0, 0, 0);
+      d[R] = acc;
+    }
+  } else {
+    const v8i ka = k_operand<FMT>(K, k);
+#pragma unroll
+    for (int R = 0; R < NRB; ++R)
+      d[R] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q.b[R], zero, 0, 0, 0, kE8m0One, 0, kE8m0One);
+  }
+}
+
 // Row layout of a GQA group of n_q <= 32 query rows: NRB blocks of 16 rows;
 // a group of NQB < 16 rows (one block) is replicated 16 / NQB times.
 //  - softmax layout (QK^T output): lane (n, jj) holds row 16R + n % NQB of
@@ -303,14 +354,15 @@ __device__ __forceinline__ float row_of(const Ctx& c, int R) {  // softmax-layou
 }
 
 template <int FMT, int NQB, int NRB>
-__device__ __forceinline__ void granule(const Ctx& c, const v8i (&qb)[NRB], const int (&row_tok)[NRB], int gi,
+__device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, const int (&row_tok)[NRB], int gi,
                                         const KRows<FMT>& K, const VRows& V, State<NQB, NRB>& st) {
   const int t0 = c.j0 + gi * kGran;
   // ---- logits: lane (n, jj) gets tokens t0 + 16k + 4jj + v of its rows
   float s[NRB][2][4];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const v8i ka = k_operand<FMT>(K, k);
+    v4f dk[NRB];
+    qk_tile<FMT, NRB>(K, k, qo, dk);
     const int tk = t0 + 16 * k;
     // tokens at or past `end` are masked; a dead tile masks all of them
     const int end = tile_page(c, tk) >= 0 ? c.j1 : 0;  // scalar; the block-table entry is cached
@@ -319,9 +371,7 @@ __device__ __forceinline__ void granule(const Ctx& c, const v8i (&qb)[NRB], cons
     const bool full = tk + 16 <= end && (!c.causal || tk + 15 <= c.lim0);
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
-      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb[R], zero, 0, 0, 0, kE8m0One, 0,
-                                                                      kE8m0One);
+      const v4f d = dk[R];
       if (full) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) s[R][k][v] = d[v] * c.cscale;
@@ -473,13 +523,13 @@ void decode_mfma_kernel(DecodeParams p) {
   c.v_sp = p.v_sp;
   c.k_ss = (uint32_t)p.k_ss;
   c.v_ss = (uint32_t)p.v_ss;
-  constexpr uint32_t row = FMT == 0 ? 128u : 96u;
+  constexpr uint32_t row = FMT != 1 ? 128u : 96u;
   c.k_rec = 15u * c.k_ss + row;
   c.v_rec = 15u * c.v_ss + row;
   c.k_lane = (uint32_t)(n * p.k_ss + F::kKOff * jj);
-  const uint32_t vch = FMT == 0 ? 8u * n : (6u * n) & ~3u;  // 4-aligned byte offset holding channel 8n
+  const uint32_t vch = FMT != 1 ? 8u * n : (6u * n) & ~3u;  // 4-aligned byte offset holding channel 8n
   c.v_lane = (uint32_t)(4 * jj * p.v_ss) + vch;
-  c.v_shift = FMT == 0 ? 0 : 16 * (n & 1);
+  c.v_shift = FMT != 1 ? 0 : 16 * (n & 1);
   c.num_pages = (uint32_t)min<int64_t>(p.num_pages, 0x7FFFFFFF);
   c.page_shift = p.page_shift;
   c.pmask = p.page_size - 1;
@@ -493,7 +543,20 @@ void decode_mfma_kernel(DecodeParams p) {
   // unfused: the pre-quantized rows' words, fetched before the KV loads too
   // (clamped rows load a valid row and are zeroed below)
   u32x4 qg[NRB][2];
-  if (!p.qb) {
+  // bf16-Q mode: this lane's channels [32jj, 32jj + 32) of Q row 16R + n % NQB
+  // (clamped like the codes; zeroed below past n_q)
+  u32x4 qh[NRB][4];
+  if constexpr (FMT == 2) {
+#pragma unroll
+    for (int R = 0; R < NRB; ++R) {
+      const int r = min(16 * R + (n % NQB), p.n_q - 1);
+      const int t = r / p.h_r;
+      const int64_t tok = (int64_t)seq * p.q_len + t, h = (int64_t)g * p.h_r + (r - t * p.h_r);
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.qb + tok * p.qb_ts + h * p.qb_hs + 32 * jj);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qh[R][i] = src[i];
+    }
+  } else if (!p.qb) {
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
       const int r = min(16 * R + (n % NQB), p.n_q - 1);
@@ -503,7 +566,7 @@ void decode_mfma_kernel(DecodeParams p) {
       qg[R][1] = src[1];
     }
   }
-  if (p.qb) {
+  if (FMT != 2 && p.qb) {
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
       const int v = min((int)threadIdx.x + k * kThreads, nvec - 1);  // a repeat changes no max
@@ -523,8 +586,8 @@ void decode_mfma_kernel(DecodeParams p) {
     V1 = load_v<NT>(c, gi + kWaves);
   }
 
-  float qdesc;
-  if (p.qb) {
+  float qdesc = 1.0f;  // bf16-Q mode: no Q scale
+  if (FMT != 2 && p.qb) {
     // fused step: quantize this (sequence, KV head)'s Q rows here, with the
     // arithmetic of the stand-alone quantize kernel (every split item of the
     // pair derives the same codes and scale)
@@ -550,19 +613,23 @@ void decode_mfma_kernel(DecodeParams p) {
       if (v < nvec) *reinterpret_cast<uint2*>(&q_s[v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc);
     }
     __syncthreads();
-  } else {
+  } else if (FMT != 2) {
     qdesc = p.q_descale[(int64_t)seq * p.h_k + g];
   }
   c.cscale = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
 
   // B operands of QK^T: column n of block R = Q row 16R + n % NQB (zero past n_q)
-  v8i qb[NRB];
+  QOps<FMT, NRB> qo;
   int row_tok[NRB];
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     const int r = 16 * R + (n % NQB);
     row_tok[R] = r / p.h_r;
-    if (r < p.n_q) {
+    if constexpr (FMT == 2) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qo.b[R][i] = __builtin_bit_cast(v8bf, r < p.n_q ? qh[R][i] : z);
+    } else if (r < p.n_q) {
       u32x4 a, b;
       if (p.qb) {  // LDS reads of the codes quantized above
         a = *reinterpret_cast<const u32x4*>(&q_s[r][32 * jj]);
@@ -573,12 +640,12 @@ void decode_mfma_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qb[R][i] = (int)a[i];
-        qb[R][4 + i] = (int)b[i];
+        qo.b[R][i] = (int)a[i];
+        qo.b[R][4 + i] = (int)b[i];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[R][i] = 0;
+      for (int i = 0; i < 8; ++i) qo.b[R][i] = 0;
     }
   }
 
@@ -598,13 +665,13 @@ void decode_mfma_kernel(DecodeParams p) {
         K1 = load_k<FMT, NT>(c, gi + kWaves);
         V1 = load_v<NT>(c, gi + kWaves);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K0, V0, st);
+        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K0, V0, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K0 = load_k<FMT, NT>(c, gi + kWaves);
         V0 = load_v<NT>(c, gi + kWaves);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K1, V1, st);
+        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K1, V1, st);
         gi += kWaves;
         if (gi >= ngr) break;
       }
@@ -613,19 +680,19 @@ void decode_mfma_kernel(DecodeParams p) {
         KRows<FMT> K2 = load_k<FMT, NT>(c, gi + 2 * kWaves);
         VRows V2 = load_v<NT>(c, gi + 2 * kWaves);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K0, V0, st);
+        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K0, V0, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K0 = load_k<FMT, NT>(c, gi + 2 * kWaves);
         V0 = load_v<NT>(c, gi + 2 * kWaves);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K1, V1, st);
+        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K1, V1, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K1 = load_k<FMT, NT>(c, gi + 2 * kWaves);
         V1 = load_v<NT>(c, gi + 2 * kWaves);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qb, row_tok, gi, K2, V2, st);
+        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K2, V2, st);
         gi += kWaves;
         if (gi >= ngr) break;
       }
@@ -761,7 +828,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, bool nont
   DecodeParams p = p_in;
   p.head_major = (tune & 2) ? 1 : 0;
   const int t = (tune & 1) ? 2 : 0;
-  return kv_format == 0 ? launch_fmt<0>(p, nontemporal, t, s) : launch_fmt<1>(p, nontemporal, t, s);
+  if (kv_format == 0) return p.q_bf16 ? launch_fmt<2>(p, nontemporal, t, s) : launch_fmt<0>(p, nontemporal, t, s);
+  return launch_fmt<1>(p, nontemporal, t, s);
 }
 
 }  // namespace mj

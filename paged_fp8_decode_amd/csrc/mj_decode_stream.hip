@@ -415,7 +415,7 @@ static int kernel_choice(const DecodeParams& p, int kv_format, int row_tiles) {
   const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24);
   const bool tiles_ok = row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
   if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q)) return 0;
-  if (kv_format != 0 || g_variant != 2 || p.n_q > 4) return 1;
+  if (kv_format != 0 || g_variant != 2 || p.n_q > 4 || p.q_bf16) return 1;
   return 2;
 }
 
@@ -425,7 +425,8 @@ bool decode_fuses_step(const DecodeParams& p, int kv_format, int row_tiles) {
 
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s) {
   const int k = kernel_choice(p, kv_format, row_tiles);
-  if (k != 1 && (p.qb || p.counters)) return hipErrorInvalidValue;  // only the matrix-core kernel fuses the step
+  // only the matrix-core kernel fuses the step; bf16 Q is read by it and the generic kernel
+  if (k != 1 && ((p.qb && !p.q_bf16) || p.counters)) return hipErrorInvalidValue;
   if (k == 0) return launch_decode_generic(p, kv_format, row_tiles, s);
   if (k == 1) return launch_decode_mfma(p, kv_format, g_nontemporal != 0, g_variant >= 10 ? g_variant - 10 : 0, s);
   const dim3 grid(p.num_work, p.h_k);

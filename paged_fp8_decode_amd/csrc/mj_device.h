@@ -36,6 +36,16 @@ __device__ __forceinline__ float e2m3_raw(uint32_t c) {
 __device__ __forceinline__ float e4m3_value(uint32_t c) { return e4m3_raw(c) * kE4m3Rescale; }
 __device__ __forceinline__ float e2m3_value(uint32_t c) { return e2m3_raw(c) * kE2m3Rescale; }
 
+// Four e4m3 codes (one word, byte b = code b) -> four bf16 (two words, code
+// 2i + h in half h of word i) with gfx950's scaled converter at scale 1.
+// Exact: every e4m3 value, subnormals included, is a normal bf16 (8-bit
+// significand, exponent range far wider); the two NaN codes give NaN.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t out[2]) {
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  out[0] = __builtin_bit_cast(uint32_t, (v2bf_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  out[1] = __builtin_bit_cast(uint32_t, (v2bf_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
 // Round an fp32 to the nearest e4m3 code, ties to even.  Domain: finite
 // |x| <= 464 (the Q quantizer stays within 448 * (1 + 2^-23)).
 __device__ __forceinline__ uint32_t e4m3_rne(float x) {

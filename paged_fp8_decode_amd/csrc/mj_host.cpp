@@ -59,6 +59,8 @@ mj_status check_config(const mj_config* c) {
   if (c->head_dim != 128) return MJ_EUNSUPPORTED;
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64 && c->page_size != 128) return MJ_EUNSUPPORTED;
   if (c->kv_format != MJ_KV_E4M3 && c->kv_format != MJ_KV_E2M3) return MJ_EUNSUPPORTED;
+  if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
+  if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3) return MJ_EUNSUPPORTED;  // packed e2m3 takes fp8 Q only
   if ((int64_t)c->max_q_len * (c->h_q / c->h_k) > kMaxRows) return MJ_ECAPACITY;
   return MJ_OK;
 }
@@ -355,7 +357,11 @@ mj_status mj_quantize_q(const mj_config* cfg, const void* q, int64_t q_tok_strid
 }
 
 static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_decode_args* a, mj::DecodeParams* p) {
-  if (!a->q8 || !a->q_descale || !a->k_cache || !a->v_cache || !a->k_descale || !a->v_descale || !a->block_table ||
+  const bool qbf = cfg->q_mode == MJ_Q_BF16;
+  if (qbf ? !a->q_bf16 : (!a->q8 || !a->q_descale)) return MJ_EINVAL;
+  if (qbf && (a->q_tok_stride < 0 || a->q_head_stride < 0)) return MJ_EINVAL;
+  if (qbf && (!aligned(a->q_bf16, 16) || a->q_tok_stride % 8 || a->q_head_stride % 8)) return MJ_EALIGN;
+  if (!a->k_cache || !a->v_cache || !a->k_descale || !a->v_descale || !a->block_table ||
       !a->seq_lens || !a->plan || !a->out)
     return MJ_EINVAL;
   if (a->num_seqs < 1 || a->q_len < 1) return MJ_EINVAL;
@@ -367,7 +373,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   if (a->k_page_stride < 0 || a->k_slot_stride < 0 || a->k_head_stride < 0 || a->v_page_stride < 0 ||
       a->v_slot_stride < 0 || a->v_head_stride < 0 || a->out_tok_stride < 0 || a->out_head_stride < 0)
     return MJ_EINVAL;
-  if (!aligned(a->q8, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16) ||
+  if ((!qbf && !aligned(a->q8, 16)) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) || !aligned(a->out, 16) ||
       a->k_page_stride % 16 || a->k_slot_stride % 16 || a->k_head_stride % 16 || a->v_page_stride % 16 ||
       a->v_slot_stride % 16 || a->v_head_stride % 16 || a->out_tok_stride % 8 || a->out_head_stride % 8 ||
       (a->o_mul && !aligned(a->o_mul, 16)))
@@ -381,8 +387,8 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
 
   char* ws = static_cast<char*>(a->workspace);
   const bool has_ws = ws && a->workspace_bytes >= wl.total;
-  p->q8 = a->q8;
-  p->q_descale = a->q_descale;
+  p->q8 = qbf ? nullptr : a->q8;
+  p->q_descale = qbf ? nullptr : a->q_descale;
   p->k = static_cast<const uint8_t*>(a->k_cache);
   p->v = static_cast<const uint8_t*>(a->v_cache);
   p->k_sp = a->k_page_stride;
@@ -426,8 +432,10 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->causal = a->causal ? 1 : 0;
   p->num_work = a->num_work;
   p->head_major = 0;
-  p->qb = nullptr;
-  p->qb_ts = p->qb_hs = 0;
+  p->q_bf16 = qbf ? 1 : 0;
+  p->qb = qbf ? static_cast<const uint16_t*>(a->q_bf16) : nullptr;
+  p->qb_ts = qbf ? a->q_tok_stride : 0;
+  p->qb_hs = qbf ? a->q_head_stride : 0;
   p->q_mul = nullptr;
   p->counters = nullptr;
   p->plan_in_kernel = 0;
@@ -469,9 +477,14 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   char* ws = static_cast<char*>(sa->decode.workspace);
   uint8_t* q8 = reinterpret_cast<uint8_t*>(ws + wl.q8_off);
   float* qd = reinterpret_cast<float*>(ws + wl.qd_off);
+  const bool qbf = cfg->q_mode == MJ_Q_BF16;
+  if (qbf && sa->q_mul) return MJ_EUNSUPPORTED;  // q_mul folds fp6 K scales into quantized Q
   mj_decode_args a = sa->decode;
   a.q8 = q8;
   a.q_descale = qd;
+  a.q_bf16 = sa->q;
+  a.q_tok_stride = sa->q_tok_stride;
+  a.q_head_stride = sa->q_head_stride;
   if (sa->plan_on_device && sa->margin < 0) return MJ_EINVAL;
   mj::DecodeParams p;
   st = fill_decode(cfg, d, &a, &p);
@@ -507,6 +520,12 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   m.out_tok_stride = a.out_tok_stride;
   m.out_head_stride = a.out_head_stride;
   m.lse = a.lse;
+  if (qbf) {  // nothing to quantize: the decode reads bf16 Q itself
+    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel && mj::decode_fuses_step(p, cfg->kv_format, rt);
+    p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
+    if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+    return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
+  }
   if (mj::decode_fuses_step(p, cfg->kv_format, rt)) {
     p.qb = static_cast<const uint16_t*>(sa->q);
     p.qb_ts = sa->q_tok_stride;
@@ -649,7 +668,7 @@ mj_status mj_debug_stream_read(const void* src, int64_t bytes, uint32_t* out, in
 }
 
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream) {
-  if (!codes || !out || n < 0 || (kv_format != MJ_KV_E4M3 && kv_format != MJ_KV_E2M3)) return MJ_EINVAL;
+  if (!codes || !out || n < 0 || kv_format < 0 || kv_format > 2) return MJ_EINVAL;
   return mj::launch_decode_codes(kv_format, codes, n, out, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 

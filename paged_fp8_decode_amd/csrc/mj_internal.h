@@ -50,11 +50,14 @@ struct DecodeParams {
   int causal;
   int num_work;
   int head_major;              // grid is (h_k, num_work) instead of (num_work, h_k)
-  // Fused step (matrix-core kernel only; null otherwise).  qb: bf16 Q
-  // quantized in the prologue instead of reading q8 / q_descale.  counters:
+  // q_bf16 = 1: bf16-Q mode.  qb is then the bf16 Q the kernels use as is
+  // (q8 / q_descale unused), on every decode kernel but the VALU-PV one.
+  // Otherwise (fused step, matrix-core kernel only; null elsewhere) qb is the
+  // bf16 Q quantized in the prologue instead of reading q8 / q_descale.  counters:
   // (max_num_seqs, h_k) zero-initialised arrival counters; the last split of
   // a (sequence, KV head) to finish merges the partials and resets its
   // counter to zero.
+  int q_bf16;
   const uint16_t* qb;
   int64_t qb_ts, qb_hs;        // elements
   const float* q_mul;          // nullable (h_q, 128)

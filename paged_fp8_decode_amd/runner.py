@@ -1,6 +1,7 @@
 """``DecodeStep``: one decode site's configuration, its persistent device
 buffers, and the C-ABI calls of a step in order: plan -> quantize Q ->
-decode -> merge, or plan -> ``mj_decode_step`` (the last three fused).  Buffers are allocated once with torch (plumbing) at fixed
+decode -> merge, or plan -> ``mj_decode_step`` (the last three fused).  With
+``q_mode="bf16"`` there is no quantize call: the decode reads bf16 Q.  Buffers are allocated once with torch (plumbing) at fixed
 addresses, so a hipGraph that captured ``run`` replays any later ``plan``
 (mjolnir-kernel wheel page mjolnir/runner.py, module docstring and
 T5DecodeRunner.__init__: fixed-address plan buffers padded to a fixed grid).
@@ -17,17 +18,19 @@ from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, StepArgs, check, mj
 
 class DecodeStep:
     def __init__(self, *, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, kv_format="e4m3",
-                 num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, min_chunk_tokens=0, device="cuda"):
+                 num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, min_chunk_tokens=0, q_mode="fp8",
+                 device="cuda"):
         self.device = torch.device(device)
         if num_cus == 0:
             num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
         self.cfg = mj_config(h_q=h_q, h_k=h_k, page_size=page_size, max_num_seqs=max_num_seqs, max_q_len=max_q_len,
                              max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
                              kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, kv_format=kv_format,
-                             min_chunk_tokens=min_chunk_tokens)
+                             min_chunk_tokens=min_chunk_tokens, q_mode=q_mode)
         check(mj_config_check(self.cfg), "mj_config_check")
         self.h_q, self.h_k, self.h_r = h_q, h_k, h_q // h_k
         self.max_q_len = max_q_len
+        self.q_bf16 = q_mode == "bf16"
         n_plan = mj_plan_buffer_bytes(self.cfg) // 4
         self.plan_dev = torch.zeros(n_plan, dtype=torch.int32, device=self.device)
         # two pinned staging slots: a slot is rewritten only after its copy ran
@@ -108,6 +111,11 @@ class DecodeStep:
             out=out.data_ptr(), out_tok_stride=out.stride(0), out_head_stride=out.stride(1),
             lse=lse.data_ptr() if lse is not None else None,
         )
+        if self.q_bf16:
+            if q_mul is not None:
+                raise ValueError("q_mul folds fp6 K scales into quantized Q; bf16-Q mode takes e4m3 KV only")
+            assert q.stride(2) == 1
+            a.q_bf16, a.q_tok_stride, a.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
         if fused:
             assert q.stride(2) == 1
             a.q8 = None
@@ -121,7 +129,8 @@ class DecodeStep:
             if events:
                 events[1].record(stream)
             return out
-        mj_quantize_q(self.cfg, q, q_mul, b, ql, self.q8, self.q_descale, stream)
+        if not self.q_bf16:
+            mj_quantize_q(self.cfg, q, q_mul, b, ql, self.q8, self.q_descale, stream)
         if events:
             events[0].record(stream)
         mj_paged_decode(self.cfg, a, stream)

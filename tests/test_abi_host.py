@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 3
+    assert mj.lib().mj_abi_version() == 4
 
 
 def _cfg(**kw):
@@ -113,6 +113,10 @@ def test_config_errors():
     assert mj.mj_config_check(_cfg(kv_format=3)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_config_check(_cfg(max_num_seqs=0)) == mj.MJ_EINVAL
     assert mj.mj_config_check(_cfg(kv_tile_tokens=100)) == mj.MJ_EINVAL
+    assert mj.mj_config_check(_cfg(q_mode="bf16")) == mj.MJ_OK
+    assert mj.mj_config_check(_cfg(q_mode=2)) == mj.MJ_EINVAL
+    # the packed e2m3 cache takes fp8 Q only
+    assert mj.mj_config_check(_cfg(q_mode="bf16", kv_format="e2m3")) == mj.MJ_EUNSUPPORTED
     assert mj.mj_plan_buffer_bytes(_cfg(head_dim=64)) == 0
     assert mj.mj_workspace_bytes(_cfg(page_size=8)) == 0
 
@@ -179,6 +183,29 @@ def test_decode_argument_errors(kw, status):
 
 
 @no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_bf16=None), mj.MJ_EINVAL),
+    (dict(q_head_stride=-128), mj.MJ_EINVAL),
+    (dict(q_bf16=FAKE + 2), mj.MJ_EALIGN),
+    (dict(q_tok_stride=4100), mj.MJ_EALIGN),
+    (dict(q_head_stride=130), mj.MJ_EALIGN),
+    (dict(out=None), mj.MJ_EINVAL),
+])
+def test_decode_bf16_q_argument_errors(kw, status):
+    base = dict(q8=None, q_descale=None, q_bf16=FAKE, q_tok_stride=32 * 128, q_head_stride=128)
+    base.update(kw)
+    assert _decode_status(_cfg(q_mode="bf16"), **base) == status
+
+
+@no_gpu
+def test_step_rejects_q_mul_in_bf16_q_mode():
+    cfg = _cfg(q_mode="bf16")
+    sa = mj.StepArgs(decode=_args(cfg, q8=None, q_descale=None), q=FAKE, q_tok_stride=32 * 128, q_head_stride=128,
+                     q_mul=FAKE)
+    assert mj.lib().mj_decode_step(ctypes.byref(cfg), ctypes.byref(sa), None) == mj.MJ_EUNSUPPORTED
+
+
+@no_gpu
 def test_decode_config_errors_come_first():
     assert _decode_status(_cfg(page_size=12)) == mj.MJ_EUNSUPPORTED
     assert mj.lib().mj_paged_decode(ctypes.byref(_cfg()), None, None) == mj.MJ_EINVAL
@@ -203,6 +230,7 @@ def test_quantize_and_merge_errors():
     m.num_seqs = 0
     assert L.mj_merge_lse(ctypes.byref(cfg), ctypes.byref(m), None) == mj.MJ_EINVAL
     assert L.mj_debug_decode_codes(7, FAKE, 4, FAKE, None) == mj.MJ_EINVAL
+    assert L.mj_debug_decode_codes(3, FAKE, 4, FAKE, None) == mj.MJ_EINVAL
 
 
 def _wargs(**kw):

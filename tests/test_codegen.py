@@ -22,11 +22,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "paged_fp8_decode_amd", "csrc", "mj_decode_mfma.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# the instances the default dispatch launches: (format, rows per block,
+# the instances the default dispatch launches: (operand format, rows per block,
 # row blocks, non-temporal, prefetch, waves per SIMD)
 DEFAULT = ["Li0ELi4ELi1ELb1ELi1ELi2E", "Li0ELi8ELi1ELb1ELi1ELi2E", "Li0ELi16ELi1ELb1ELi1ELi2E",
            "Li0ELi16ELi2ELb1ELi1ELi1E", "Li1ELi4ELi1ELb1ELi1ELi2E", "Li1ELi8ELi1ELb1ELi1ELi2E",
-           "Li1ELi16ELi1ELb1ELi1ELi2E", "Li1ELi16ELi2ELb1ELi1ELi1E"]
+           "Li1ELi16ELi1ELb1ELi1ELi2E", "Li1ELi16ELi2ELb1ELi1ELi1E",
+           # e4m3 KV with bf16 Q
+           "Li2ELi4ELi1ELb1ELi1ELi2E", "Li2ELi8ELi1ELb1ELi1ELi2E", "Li2ELi16ELi1ELb1ELi1ELi2E",
+           "Li2ELi16ELi2ELb1ELi1ELi1E"]
 
 
 @pytest.fixture(scope="module")
@@ -64,7 +67,7 @@ def test_no_scratch_and_no_l2_flush(asm, inst):
 def test_main_loop_keeps_loads_in_flight(asm, inst):
     body, _ = _body(asm, inst)
     heads = [j for j, l in enumerate(body) if "Loop Header" in l]
-    loop = next(j for j in heads if any("v_mfma_scale" in x for x in body[j:j + 300]) and
+    loop = next(j for j in heads if any("v_mfma" in x for x in body[j:j + 300]) and
                 any("buffer_load" in x for x in body[j:j + 300]))
     waits = [int(re.search(r"vmcnt\((\d+)\)", x).group(1)) for x in body[loop:loop + 1500] if "vmcnt(" in x][:4]
     assert len(waits) == 4 and min(waits) >= 8, waits

@@ -57,6 +57,36 @@ def test_matches_sdpa_per_head(key):
                                  - lse)) < 1e-12
 
 
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n"])
+def test_unquantized_q_matches_sdpa(key):
+    """The bf16-Q reading (Q used as given, no quantization): each (sequence,
+    KV head) equals torch SDPA in fp64 on Q rows gathered here by query head
+    and token, the dequantized K/V and the step's mask."""
+    wl, h = _small(key)
+    s = wl.spec
+    O, LSE = A.decode_step(h, causal=s.causal, quantize=False, **_args(wl))
+    q = wl.q.float().numpy().astype(np.float64).reshape(s.b, s.q_len, s.h_q, s.d)
+    for i in range(s.b):
+        for g in range(s.h_k):
+            _, K, V = A.head_inputs(h, i, g, quantize=False, **_args(wl))
+            L = K.shape[0]
+            for t in range(s.q_len):
+                for r in range(s.h_r):
+                    seen = L if not (s.causal and s.q_len > 1) else L - s.q_len + t + 1
+                    allowed = np.zeros((1, L), bool)
+                    allowed[0, :max(seen, 0)] = True
+                    h_idx = g * s.h_r + r
+                    got = O[i * s.q_len + t, h_idx]
+                    if seen <= 0:
+                        assert np.all(got == 0) and np.isneginf(LSE[i * s.q_len + t, h_idx])
+                        continue
+                    ref = _ref_sdpa(q[i, t, h_idx][None], K, V, allowed, h["softmax_scale"])[0]
+                    assert np.max(np.abs(got - ref)) < 1e-12
+                    sc = h["softmax_scale"] * (K[:seen] @ q[i, t, h_idx])
+                    lse = sc.max() + math.log(np.sum(np.exp(sc - sc.max())))
+                    assert abs(LSE[i * s.q_len + t, h_idx] - lse) < 1e-12
+
+
 def test_gather_identity_table_is_dense_slice():
     # one page holding the whole sequence, identity block table: the gather is a plain slice
     rng = np.random.default_rng(0)
