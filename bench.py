@@ -5,18 +5,21 @@ Q quantization, the paged decode and the LSE merge of split partials.  The
 timed step is a hipGraph of ``mj_decode_step`` planning from the device
 lengths itself: the decode kernel (each workgroup derives its plan item and
 quantizes its Q rows) and, when the plan splits, the merge kernel.
-Inputs are seeded synthetic tensors already resident in HBM.  The Infinity
-Cache is flushed (a 1 GiB write) before every step, outside that step's
-event pair, so KV bytes come from HBM.
+Inputs are seeded synthetic tensors already resident in HBM.  Before every
+step, outside that step's event pair, a 1 GiB read evicts the 256 MB
+Infinity Cache, so KV bytes come from HBM.  (A 1 GiB write would evict it
+too but leave it full of dirty lines whose write-back then competes with the
+step's loads -- a state no serving step starts from; the graph step after
+such a write is reported as well, ``graph_us_per_step_median_after_write``.)
 
 Prints one JSON line.  ``value`` is the achieved KV-read bandwidth of the
 step (KV bytes / mean graph step time); ``detail`` also has the eager step
 (host planner + fused step) and the eager three-call step (quantize, decode,
-merge as separate launches).  The ``roofline`` object is the fused decode
-kernel's own bandwidth against the 8 TB/s HBM peak, its duration taken with
-one event pair around back-to-back single-launch steps (merge in the decode
-kernel) that rotate over copies of the KV pools (no launch reads KV the
-Infinity Cache still holds).
+merge as separate launches).  The ``roofline`` object is the decode
+kernel's own bandwidth against the 8 TB/s HBM peak: one event pair around
+back-to-back steps that rotate over copies of the KV pools (no launch reads
+KV the Infinity Cache still holds), minus one event pair around as many
+back-to-back launches of the merge kernel alone, per launch.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.  ``bf16_q`` measures the same step in the bf16-Q mode (Q used as
 given, no quantization; the KV codes converted to bf16 in the kernel) on the
@@ -125,7 +128,24 @@ def calibrate():
     print(json.dumps(dict(calibration=True, stream_read_bytes=n, copy_bytes=n)), flush=True)
 
 
-def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mode="fp8"):
+class Flusher:
+    """Evicts the Infinity Cache between steps: reads 1 GiB (``__call__``), or
+    writes it (``dirty``) for the secondary after-write figure."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        self.acc = torch.zeros((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, 0, out=self.acc)
+
+    def dirty(self):
+        self.buf.add_(1)
+
+
+def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="fp8"):
     import torch
     import synth
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
@@ -142,7 +162,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
     def eager(n, fused, with_events):
         ev = [(E(), E(), E(), E()) for _ in range(n)] if with_events else None
         for k in range(n):
-            flush_buf.add_(1)  # 1 GiB read + write: evicts the 256 MB Infinity Cache
+            flush()
             e = ev[k] if ev else None
             if e:
                 e[0].record(stream)
@@ -191,13 +211,13 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
         torch.cuda.synchronize()
         return gr
 
-    def time_graph(gr, n):
+    def time_graph(gr, n, evict=flush):
         gev = [(E(), E()) for _ in range(n)]
         for _ in range(warmup):
-            flush_buf.add_(1)
+            evict()
             gr.replay()
         for k in range(n):
-            flush_buf.add_(1)
+            evict()
             gev[k][0].record(stream)
             gr.replay()
             gev[k][1].record(stream)
@@ -206,16 +226,17 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
 
     graph = capture(False)
     graph_ms = time_graph(graph, steps)
+    graph_dirty_ms = time_graph(graph, max(5, steps // 2), flush.dirty)
     del graph
     graph = capture(True)
     graph_pk_ms = time_graph(graph, max(5, steps // 2))
     del graph
 
-    # kernel duration for the roofline: the fused step as one launch (the
-    # split partials merged by the decode kernel's last split item), back to
-    # back, rotating over copies of the KV pools so that no launch finds the
-    # previous one's KV in the 256 MB Infinity Cache (>= 1 GiB of distinct KV
-    # between reuses); one event pair over all launches
+    # decode kernel duration for the roofline: steps (decode + merge
+    # launch) back to back, rotating over copies of the KV pools so that no
+    # launch finds the previous one's KV in the 256 MB Infinity Cache (>= 1 GiB
+    # of distinct KV between reuses), one event pair over all of them; minus
+    # the same number of merge launches alone, one event pair over those
     kvb = wl.kv_bytes()
     n_copies = max(1, -(-(1 << 30) // kvb))
     pools = [(wl.k_pool, wl.v_pool)] + [(wl.k_pool.clone(), wl.v_pool.clone()) for _ in range(n_copies - 1)]
@@ -233,7 +254,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
     import paged_fp8_decode_amd as mjlib
     step.plan_workload(wl, stream=stream)
     torch.cuda.synchronize()
-    mjlib.mj_debug_set_step_merge(1)
+    mjlib.mj_debug_set_step_merge(2)
     try:
         for i in range(len(pools)):
             launch(i)
@@ -243,10 +264,20 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
         for i in range(reps):
             launch(i)
         k1.record(stream)
+        merge_us = 0.0
+        if info.with_reduction:
+            m0, m1 = E(), E()
+            m0.record(stream)
+            for i in range(reps):
+                step.merge(out, lse, info, stream)
+            m1.record(stream)
         torch.cuda.synchronize()
+        if info.with_reduction:
+            merge_us = m0.elapsed_time(m1) * 1e3 / reps
     finally:
         mjlib.mj_debug_set_step_merge(STEP_MERGE)
-    kernel_us = k0.elapsed_time(k1) * 1e3 / reps
+    step_us_b2b = k0.elapsed_time(k1) * 1e3 / reps
+    kernel_us = step_us_b2b - merge_us
     del pools
 
     res = dict(
@@ -263,8 +294,10 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
         graph_us_per_step_p90=float(np.percentile(graph_ms, 90) * 1e3),
         graph_step_kv_gbs=kvb / (graph_ms.mean() * 1e-3) / 1e9,
         graph_with_planner_kernel_us_per_step_median=float(np.median(graph_pk_ms) * 1e3),
+        graph_us_per_step_median_after_write=float(np.median(graph_dirty_ms) * 1e3),
         step_kv_gbs=kvb / (step_ms.mean() * 1e-3) / 1e9,
-        kernel_us_back_to_back=kernel_us, kernel_launches=reps, kv_pool_copies=n_copies,
+        kernel_us_back_to_back=kernel_us, step_us_back_to_back=step_us_b2b, merge_us_back_to_back=merge_us,
+        kernel_launches=reps, kv_pool_copies=n_copies,
         kernel_kv_gbs=kvb / (kernel_us * 1e-6) / 1e9,
         plan=dict(num_work=info.num_work, slots=info.slots, chunk_tiles=info.chunk_tiles,
                   min_chunk_tiles=info.min_chunk_tiles, with_reduction=info.with_reduction),
@@ -279,7 +312,7 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
         chk = torch.empty(4096, dtype=torch.int32, device="cuda")
         ms = []
         for k in range(10):
-            flush_buf.add_(1)
+            flush()
             e0, e1 = E(), E()
             e0.record(stream)
             mjlib.mj_debug_stream_read(src, chk, 2048, stream)
@@ -294,13 +327,15 @@ def measure(key, steps, warmup, flush_buf, wgs_per_cu=0, stream_read=False, q_mo
         f"eager / {res['three_call_us_per_step_median']:.1f} us three calls (median); decode kernel "
         f"{kernel_us:.1f} us = {res['kernel_kv_gbs']:.0f} GB/s KV ({100 * res['kernel_frac_of_hbm_peak']:.1f}% "
         f"of 8 TB/s); in-step decode {res['step_decode_us_mean']:.1f} us fused / "
-        f"{res['three_call_decode_us_median']:.1f} us unfused")
+        f"{res['three_call_decode_us_median']:.1f} us unfused; graph step after a 1 GiB write "
+        f"{res['graph_us_per_step_median_after_write']:.1f} us; back-to-back step {step_us_b2b:.1f} us, "
+        f"merge alone {merge_us:.1f} us")
     del wl
     torch.cuda.empty_cache()
     return res
 
 
-def measure_write(kv_format, n_tokens, reps, flush_buf, h_k=8, page_size=64):
+def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
     """mj_write_kv of n_tokens new rows (bf16 K and V, h_k heads) into a paged
     cache at scattered slots: time per call (one event pair around reps
     back-to-back calls, cache flushed first) and algorithmic bytes (bf16 in,
@@ -332,7 +367,7 @@ def measure_write(kv_format, n_tokens, reps, flush_buf, h_k=8, page_size=64):
     stream = torch.cuda.current_stream()
     for _ in range(3):
         mjlib.mj_write_kv(cfg, a, stream)
-    flush_buf.add_(1)
+    flush()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -409,20 +444,20 @@ def main():
     STEP_MERGE = args.step_merge
     paged_fp8_decode_amd.mj_debug_set_step_merge(args.step_merge)
 
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-    main_res = measure(args.workload, args.steps, args.warmup, flush_buf, args.wgs_per_cu, not args.no_stream_read)
+    flush = Flusher()
+    main_res = measure(args.workload, args.steps, args.warmup, flush, args.wgs_per_cu, not args.no_stream_read)
     extra = {}
     for k in [x for x in args.extra.split(",") if x]:
-        extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu, False)
+        extra[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush, args.wgs_per_cu, False)
     bf16q = {}
     for k in [x for x in args.bf16q.split(",") if x]:
-        bf16q[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush_buf, args.wgs_per_cu, False,
+        bf16q[k] = measure(k, max(10, args.steps // 2), max(3, args.warmup // 2), flush, args.wgs_per_cu, False,
                            q_mode="bf16")
     writes = []
     if not args.no_write:
         for fmt in ("e4m3", "e2m3"):
             for n_tok, reps in ((16384, 20), (32, 200)):
-                w = measure_write(fmt, n_tok, reps, flush_buf)
+                w = measure_write(fmt, n_tok, reps, flush)
                 log(f"[bench] mj_write_kv {fmt} {n_tok} tokens x 8 heads: {w['us_per_call']} us, {w['gbs']} GB/s")
                 writes.append(w)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
@@ -430,7 +465,8 @@ def main():
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6
     roof = dict(bound="hbm", achieved=round(kvb / dec_s / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(kvb / dec_s / 1e9 / HBM_PEAK_GBS, 4), traffic=traffic_for(args.workload),
-                kernel="decode_mfma_kernel (mj_decode_step as one launch: Q quantization + paged decode + LSE merge)",
+                kernel="decode_mfma_kernel (fused Q quantization + paged decode; its steps' merge launches timed apart "
+                       "and subtracted)",
                 algorithmic_bytes_per_launch=kvb, kernel_us=round(main_res["kernel_us_back_to_back"], 2),
                 traffic_unit="bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)")
     line = dict(

@@ -392,8 +392,11 @@ mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t
  * generic kernel, 2 = the VALU-PV streaming kernel for e4m3 with
  * q_len*h_r <= 4 (automatic otherwise), 3 = same as 0, 10..13 = the
  * matrix-core kernel with tuning bits (variant - 10): bit 0 two granules of
- * prefetch (4-row kernel), bit 1 head-major grid.  nontemporal 1 (default) marks the streaming
- * kernels' KV loads non-temporal.  Not thread-safe; set it before
+ * prefetch (4-row kernel), bit 1 head-major grid.  nontemporal selects the
+ * streaming kernels' KV load cache policy: 1 (default) the library's choice
+ * per format, 0 every load cached, 2 every load non-temporal, 3 K cached and
+ * V non-temporal, 4 K non-temporal and V cached (the VALU-PV kernel: any
+ * value but 0 is non-temporal).  Not thread-safe; set it before
  * launching.  EINVAL on other values. */
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal);
 /* Where mj_decode_step merges split partials when it fuses the step: 0 =

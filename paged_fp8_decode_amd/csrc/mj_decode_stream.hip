@@ -40,7 +40,7 @@
 namespace mj {
 
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, bool nontemporal, int tune, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, int cache_policy, int tune, hipStream_t s);
 bool decode_mfma_supports(int n_q);
 
 namespace {
@@ -428,7 +428,11 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hi
   // only the matrix-core kernel fuses the step; bf16 Q is read by it and the generic kernel
   if (k != 1 && ((p.qb && !p.q_bf16) || p.counters)) return hipErrorInvalidValue;
   if (k == 0) return launch_decode_generic(p, kv_format, row_tiles, s);
-  if (k == 1) return launch_decode_mfma(p, kv_format, g_nontemporal != 0, g_variant >= 10 ? g_variant - 10 : 0, s);
+  if (k == 1) {
+    // debug setting -> matrix-core cache policy bits (K non-temporal, V non-temporal)
+    static const int kPolicy[5] = {0, -1, 3, 2, 1};
+    return launch_decode_mfma(p, kv_format, kPolicy[g_nontemporal], g_variant >= 10 ? g_variant - 10 : 0, s);
+  }
   const dim3 grid(p.num_work, p.h_k);
   if (g_nontemporal)
     hipLaunchKernelGGL((decode_stream_kernel<0, true>), grid, dim3(kThreads), 0, s, p);

@@ -657,7 +657,7 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
 }
 
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal) {
-  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 13)) || (nontemporal != 0 && nontemporal != 1)) return MJ_EINVAL;
+  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 13)) || nontemporal < 0 || nontemporal > 4) return MJ_EINVAL;
   mj::set_decode_variant(variant, nontemporal);
   return MJ_OK;
 }

@@ -137,10 +137,18 @@ class DecodeStep:
         if events:
             events[1].record(stream)
         if info.with_reduction:
-            m = MergeArgs(plan=self.plan_dev.data_ptr(), num_seqs=b, q_len=ql, workspace=self.workspace.data_ptr(),
-                          workspace_bytes=self.workspace.numel(), out=out.data_ptr(), out_tok_stride=out.stride(0),
-                          out_head_stride=out.stride(1), lse=lse.data_ptr() if lse is not None else None)
-            mj_merge_lse(self.cfg, m, stream)
+            self.merge(out, lse, info, stream)
+        return out
+
+    def merge(self, out, lse=None, info: PlanInfo | None = None, stream=None):
+        """mj_merge_lse of the partials in the workspace under the current plan."""
+        info = info or self.info
+        stream = stream or torch.cuda.current_stream(self.device)
+        m = MergeArgs(plan=self.plan_dev.data_ptr(), num_seqs=info.num_seqs, q_len=info.q_len,
+                      workspace=self.workspace.data_ptr(), workspace_bytes=self.workspace.numel(), out=out.data_ptr(),
+                      out_tok_stride=out.stride(0), out_head_stride=out.stride(1),
+                      lse=lse.data_ptr() if lse is not None else None)
+        mj_merge_lse(self.cfg, m, stream)
         return out
 
     # convenience for seeded workloads (tests, bench, smoke)

@@ -270,3 +270,4 @@ def test_debug_knob_errors():
     assert mj.lib().mj_debug_set_step_merge(3) == mj.MJ_EINVAL
     assert mj.lib().mj_debug_set_step_merge(-1) == mj.MJ_EINVAL
     assert mj.lib().mj_debug_set_decode_variant(14, 1) == mj.MJ_EINVAL
+    assert mj.lib().mj_debug_set_decode_variant(0, 5) == mj.MJ_EINVAL
