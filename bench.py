@@ -52,9 +52,10 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "1dc9da7ac06ed459",
-    "cfg2": dict(fetch_bytes=270172533, write_bytes=1277257),
-    "32k": dict(fetch_bytes=4306304070, write_bytes=4889147),
+    "sources_sha256_16": "b8d14a77409d3d6c",
+    "cfg2": dict(fetch_bytes=269285363, write_bytes=1179922),
+    "32k": dict(fetch_bytes=4297903582, write_bytes=4718905),
+    "cfg5": dict(fetch_bytes=806117880, write_bytes=589833),
 }
 
 
