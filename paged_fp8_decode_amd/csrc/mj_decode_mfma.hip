@@ -122,12 +122,18 @@ struct VRows {  // element e: 8 bytes holding channels 8n..8n+7 of token tau(jj,
 __device__ __forceinline__ float lane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
+// max(a, b) as the median of (a, b, inf) with inf = +inf: one instruction,
+// where fmaxf first quiets each operand it cannot prove came from
+// arithmetic (the logits reach the max through the masking branch),
+// doubling the count.  inf must be a run-time value (a kernel argument):
+// with the constant the median is folded back into fmaxf.
+__device__ __forceinline__ float fmax2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
 // reduce over the 4 lane groups jj (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float max_jj(float x) {
+__device__ __forceinline__ float max_jj(float x, float inf) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmax2(__uint_as_float(a[0]), __uint_as_float(a[1]), inf);
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax2(__uint_as_float(b[0]), __uint_as_float(b[1]), inf);
 }
 __device__ __forceinline__ float sum_jj(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -163,7 +169,7 @@ struct Ctx {
   int j0, j1, page_shift, pmask, lim0, causal, n, jj;
   int v_shift;           // e2m3: bit offset of channel 8n in the loaded 8 bytes
   float cscale;
-  int my_row_tok;        // token (within the q_len block) of this lane's Q row n % 4
+  float pos_inf;         // +inf (kernel argument; see fmax2)
 };
 
 // Page of the tile starting at token tk (wave-uniform), or -1 if the tile is
@@ -352,6 +358,27 @@ struct State {
   v4f acc[NRB][8];      // O rows 16R + (4jj + v) % NQB, channel 8n + q: acc[R][q][v]
 };
 
+// PV for channels 2PR and 2PR + 1 of the lane's 8-channel group (e4m3 V).
+template <int PR, int NQB, int NRB>
+__device__ __forceinline__ void pv_pair(const VRows& V, const v8bf (&pa)[NRB], State<NQB, NRB>& st) {
+  float a[8], b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const v2f x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][PR >> 1], 1.0f, (PR & 1) != 0);
+    a[e] = x[0];
+    b[e] = x[1];
+  }
+  const u32x4 wa = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(a[4], a[5]), pack_bf16(a[6], a[7])};
+  const u32x4 wb = {pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3]), pack_bf16(b[4], b[5]), pack_bf16(b[6], b[7])};
+#pragma unroll
+  for (int R = 0; R < NRB; ++R) {
+    st.acc[R][2 * PR] =
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], __builtin_bit_cast(v8bf, wa), st.acc[R][2 * PR], 0, 0, 0);
+    st.acc[R][2 * PR + 1] =
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], __builtin_bit_cast(v8bf, wb), st.acc[R][2 * PR + 1], 0, 0, 0);
+  }
+}
+
 template <int NQB, int NRB>
 __device__ __forceinline__ float row_of(const Ctx& c, int R) {  // softmax-layout row of this lane
   return 16 * R + (c.n % NQB);
@@ -394,9 +421,10 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
   bool raise = false;
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
-    float mx = fmaxf(fmaxf(fmaxf(s[R][0][0], s[R][0][1]), fmaxf(s[R][0][2], s[R][0][3])),
-                     fmaxf(fmaxf(s[R][1][0], s[R][1][1]), fmaxf(s[R][1][2], s[R][1][3])));
-    M[R] = max_jj(mx);
+    const float inf = c.pos_inf;
+    const float mx = fmax2(fmax2(fmax2(s[R][0][0], s[R][0][1], inf), fmax2(s[R][0][2], s[R][0][3], inf), inf),
+                           fmax2(fmax2(s[R][1][0], s[R][1][1], inf), fmax2(s[R][1][2], s[R][1][3], inf), inf), inf);
+    M[R] = max_jj(mx, inf);
     raise |= M[R] > st.m[R] + kLazyMax;
   }
   if constexpr (NQB == 4 && NRB == 1) {
@@ -454,14 +482,26 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
     pa[R] = __builtin_bit_cast(v8bf, pw);
   }
   // ---- PV
-  uint32_t vb[8][4];
-  v_operands<FMT>(c, V, vb);
+  if constexpr (FMT != 1) {
+    // e4m3 V, one channel pair at a time: converting a word's low or high
+    // two bytes gives channels (2pr, 2pr + 1) of one token, so the 8 tokens'
+    // words give both channels' B operands, used at once (16 floats live,
+    // not 64)
+    pv_pair<0, NQB, NRB>(V, pa, st);
+    pv_pair<1, NQB, NRB>(V, pa, st);
+    pv_pair<2, NQB, NRB>(V, pa, st);
+    pv_pair<3, NQB, NRB>(V, pa, st);
+  } else {
+    uint32_t vb[8][4];
+    v_operands<FMT>(c, V, vb);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const u32x4 w = {vb[q][0], vb[q][1], vb[q][2], vb[q][3]};
-    const v8bf b = __builtin_bit_cast(v8bf, w);
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 w = {vb[q][0], vb[q][1], vb[q][2], vb[q][3]};
+      const v8bf b = __builtin_bit_cast(v8bf, w);
 #pragma unroll
-    for (int R = 0; R < NRB; ++R) st.acc[R][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], b, st.acc[R][q], 0, 0, 0);
+      for (int R = 0; R < NRB; ++R)
+        st.acc[R][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], b, st.acc[R][q], 0, 0, 0);
+    }
   }
 }
 
@@ -537,6 +577,7 @@ void decode_mfma_kernel(DecodeParams p) {
   c.v_lane = (uint32_t)(4 * jj * p.v_ss) + vch;
   c.v_shift = FMT != 1 ? 0 : 16 * (n & 1);
   c.num_pages = (uint32_t)min<int64_t>(p.num_pages, 0x7FFFFFFF);
+  c.pos_inf = p.pos_inf;
   c.page_shift = p.page_shift;
   c.pmask = p.page_size - 1;
 
@@ -823,7 +864,13 @@ hipError_t launch_fmt(const DecodeParams& p, int nt, int tune, hipStream_t s) {
   if (p.n_q <= 4) return pf2 ? launch_shape<FMT, 4, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 8) return pf2 ? launch_shape<FMT, 8, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 16) return pf2 ? launch_shape<FMT, 16, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
-  return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
+  // 32 rows: two waves per SIMD fit the register budget (VGPR accumulators,
+  // no copies through AGPRs) except for e2m3, whose fp6 V expansion needs
+  // the one-wave budget
+  if constexpr (FMT == 1)
+    return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
+  else
+    return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 2>(p, nt, s);
 }
 
 }  // namespace

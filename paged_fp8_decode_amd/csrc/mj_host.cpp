@@ -415,6 +415,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->nqp = d.nq_max;
   p->part_items = has_ws ? d.slots_max : 0;
   p->scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p->pos_inf = INFINITY;
   p->o_mul = a->o_mul;
   p->out = static_cast<uint16_t*>(a->out);
   p->out_ts = a->out_tok_stride;

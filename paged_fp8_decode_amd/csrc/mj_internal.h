@@ -41,6 +41,9 @@ struct DecodeParams {
   int nqp;                     // partial row stride = max_q_len * h_r
   int part_items;              // S_max: items that may hold partials
   float scale_log2;            // softmax_scale * log2(e)
+  float pos_inf;               // +inf, as an argument: max(a, b) = med3(a, b, pos_inf)
+                               // is one instruction only while the compiler
+                               // cannot fold the third operand
   const float* o_mul;          // nullable (h_q, 128)
   uint16_t* out;               // bf16
   int64_t out_ts, out_hs;

@@ -25,11 +25,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # the instances the default dispatch launches: (operand format, rows per block,
 # row blocks, KV cache policy, prefetch, waves per SIMD)
 DEFAULT = ["Li0ELi4ELi1ELi2ELi1ELi2E", "Li0ELi8ELi1ELi2ELi1ELi2E", "Li0ELi16ELi1ELi2ELi1ELi2E",
-           "Li0ELi16ELi2ELi2ELi1ELi1E", "Li1ELi4ELi1ELi2ELi1ELi2E", "Li1ELi8ELi1ELi2ELi1ELi2E",
+           "Li0ELi16ELi2ELi2ELi1ELi2E", "Li1ELi4ELi1ELi2ELi1ELi2E", "Li1ELi8ELi1ELi2ELi1ELi2E",
            "Li1ELi16ELi1ELi2ELi1ELi2E", "Li1ELi16ELi2ELi2ELi1ELi1E",
            # e4m3 KV with bf16 Q
            "Li2ELi4ELi1ELi2ELi1ELi2E", "Li2ELi8ELi1ELi2ELi1ELi2E", "Li2ELi16ELi1ELi2ELi1ELi2E",
-           "Li2ELi16ELi2ELi2ELi1ELi1E"]
+           "Li2ELi16ELi2ELi2ELi1ELi2E"]
 
 
 @pytest.fixture(scope="module")
