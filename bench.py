@@ -225,13 +225,18 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in gev])
 
+    # the two graphs timed in alternating chunks, so that neither gains or
+    # loses from its place in the run
     graph = capture(False)
-    graph_ms = time_graph(graph, steps)
+    graph_pk = capture(True)
+    chunks = 4
+    parts, parts_pk = [], []
+    for i in range(chunks):
+        parts.append(time_graph(graph, max(2, steps // chunks)))
+        parts_pk.append(time_graph(graph_pk, max(2, steps // (2 * chunks))))
+    graph_ms, graph_pk_ms = np.concatenate(parts), np.concatenate(parts_pk)
     graph_dirty_ms = time_graph(graph, max(5, steps // 2), flush.dirty)
-    del graph
-    graph = capture(True)
-    graph_pk_ms = time_graph(graph, max(5, steps // 2))
-    del graph
+    del graph, graph_pk
 
     # decode kernel duration for the roofline: steps (decode + merge
     # launch) back to back, rotating over copies of the KV pools so that no

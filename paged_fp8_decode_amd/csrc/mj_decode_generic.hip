@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
 
 // Log-sum-exp merge of split partials: one workgroup per (sequence, KV head).
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
-  merge_one<false>(p, blockIdx.x, blockIdx.y, threadIdx.x);
+  merge_one<false, 4, 8>(p, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // Probe: dense copy of one (sequence, head)'s codes through the same

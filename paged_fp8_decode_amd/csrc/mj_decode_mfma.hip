@@ -841,7 +841,7 @@ void decode_mfma_kernel(DecodeParams p) {
       mp.h_k = p.h_k;
       mp.h_r = p.h_r;
       mp.n_q = p.n_q;
-      merge_one<true>(mp, seq, g, threadIdx.x);
+      merge_one<true, 1, 8>(mp, seq, g, threadIdx.x);  // same batches as the merge kernel: same rounding
     }
   }
 }

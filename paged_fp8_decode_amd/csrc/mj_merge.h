@@ -39,61 +39,84 @@ __device__ __forceinline__ float4 ld_part4(const float* p) {
   }
 }
 
-// Thread layout: 256 threads = 8 rows x 32 lanes of 4 channels; rows
-// (tid >> 5), (tid >> 5) + 8, ...  The splits are read in batches of kB with
-// every load of a batch in flight at once (the merge is latency-bound: a
-// loop that waits on each partial in turn costs a memory round trip per
-// split and row).  Batches combine with the usual running-max rescale; a
+// Thread layout: 256 threads = 8 rows x 32 lanes of 4 channels; a thread
+// takes rows (tid >> 5) + 8i, kRU of them at a time, and reads the splits in
+// batches of kB: every load of a batch, for all kRU rows, is in flight at
+// once (the merge is latency-bound: a memory round trip per row or split
+// would dominate; kRU * kB * 6 registers hold a batch).  kB fixes the
+// summation order, so every caller uses the same kB (bit-identical merges);
+// kRU only groups independent rows.  Batches combine with the usual running-max rescale; a
 // single batch (n <= kB) is exactly the two-pass formula above.
-template <bool kCoherent>
+template <bool kCoherent, int kRU, int kB>
 __device__ __forceinline__ void merge_one(const MergeParams& p, int seq, int g, int tid) {
-  constexpr int kB = 16;
   const int n = p.n_splits[seq];
   const int w0 = p.split_begin[seq];
   if (n <= 1 || w0 < 0 || w0 + n > p.part_items) return;
   const int c4 = (tid & 31) * 4;
-  for (int r = tid >> 5; r < p.n_q; r += 8) {
-    float M = -INFINITY, den = 0.0f;
-    float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int r0 = tid >> 5; r0 < p.n_q; r0 += 8 * kRU) {
+    float M[kRU], den[kRU];
+    float4 num[kRU];
+#pragma unroll
+    for (int u = 0; u < kRU; ++u) {
+      M[u] = -INFINITY;
+      den[u] = 0.0f;
+      num[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
     for (int s0 = 0; s0 < n; s0 += kB) {
-      float m[kB], l[kB];
-      float4 o[kB];
+      float m[kRU][kB], l[kRU][kB];
+      float4 o[kRU][kB];
 #pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        if (s0 + j < n) {
-          const int64_t idx = ((int64_t)(w0 + s0 + j) * p.h_k + g) * p.nqp + r;
-          m[j] = ld_part<kCoherent>(&p.m_part[idx]);
-          l[j] = ld_part<kCoherent>(&p.l_part[idx]);
-          o[j] = ld_part4<kCoherent>(&p.o_part[idx * kHeadDim + c4]);
-        }
-      }
-      float bm = M;
-#pragma unroll
-      for (int j = 0; j < kB; ++j)
-        if (s0 + j < n) bm = fmaxf(bm, m[j]);
-      if (bm != -INFINITY) {
-        const float sc = exp2f(M - bm);  // 0 while nothing was seen (M = -inf)
-        den *= sc;
-        num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
+      for (int u = 0; u < kRU; ++u) {
+        const int r = r0 + 8 * u;
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
-          if (s0 + j < n) {
-            const float wt = exp2f(m[j] - bm);
-            den += wt * l[j];
-            num.x += wt * o[j].x; num.y += wt * o[j].y; num.z += wt * o[j].z; num.w += wt * o[j].w;
+          if (r < p.n_q && s0 + j < n) {
+            const int64_t idx = ((int64_t)(w0 + s0 + j) * p.h_k + g) * p.nqp + r;
+            m[u][j] = ld_part<kCoherent>(&p.m_part[idx]);
+            l[u][j] = ld_part<kCoherent>(&p.l_part[idx]);
+            o[u][j] = ld_part4<kCoherent>(&p.o_part[idx * kHeadDim + c4]);
           }
         }
-        M = bm;
+      }
+#pragma unroll
+      for (int u = 0; u < kRU; ++u) {
+        if (r0 + 8 * u >= p.n_q) continue;
+        float bm = M[u];
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+          if (s0 + j < n) bm = fmaxf(bm, m[u][j]);
+        if (bm != -INFINITY) {
+          const float sc = exp2f(M[u] - bm);  // 0 while nothing was seen (M = -inf)
+          den[u] *= sc;
+          num[u].x *= sc; num[u].y *= sc; num[u].z *= sc; num[u].w *= sc;
+#pragma unroll
+          for (int j = 0; j < kB; ++j) {
+            if (s0 + j < n) {
+              const float wt = exp2f(m[u][j] - bm);
+              den[u] += wt * l[u][j];
+              num[u].x += wt * o[u][j].x; num[u].y += wt * o[u][j].y;
+              num[u].z += wt * o[u][j].z; num[u].w += wt * o[u][j].w;
+            }
+          }
+          M[u] = bm;
+        }
       }
     }
-    const bool seen = M != -INFINITY;
-    const int t = r / p.h_r;
-    const int h = g * p.h_r + (r - t * p.h_r);
-    const uint32_t b0 = f32_to_bf16(seen ? num.x / den : 0.0f), b1 = f32_to_bf16(seen ? num.y / den : 0.0f);
-    const uint32_t b2 = f32_to_bf16(seen ? num.z / den : 0.0f), b3 = f32_to_bf16(seen ? num.w / den : 0.0f);
-    *reinterpret_cast<uint2*>(p.out + ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c4) =
-        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-    if (c4 == 0 && p.lse) p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = seen ? (M + log2f(den)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kRU; ++u) {
+      const int r = r0 + 8 * u;
+      if (r >= p.n_q) continue;
+      const bool seen = M[u] != -INFINITY;
+      const int t = r / p.h_r;
+      const int h = g * p.h_r + (r - t * p.h_r);
+      const float dn = den[u];
+      const uint32_t b0 = f32_to_bf16(seen ? num[u].x / dn : 0.0f), b1 = f32_to_bf16(seen ? num[u].y / dn : 0.0f);
+      const uint32_t b2 = f32_to_bf16(seen ? num[u].z / dn : 0.0f), b3 = f32_to_bf16(seen ? num[u].w / dn : 0.0f);
+      *reinterpret_cast<uint2*>(p.out + ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c4) =
+          make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      if (c4 == 0 && p.lse)
+        p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = seen ? (M[u] + log2f(dn)) * kLn2 : -INFINITY;
+    }
   }
 }
 
