@@ -8,7 +8,11 @@ of percent while every numeric test still passed:
   on vector memory leave at least 8 loads outstanding (a wait for zero there
   means the loop drains every load each granule -- seen when a pending load
   of uncertain provenance reached the loop, and when block-table reads
-  turned into vector loads).
+  turned into vector loads);
+* no scaled MFMA has its E8M0 scale register rewritten within the next 24
+  instructions: the instruction still reads it after issue and the compiler
+  does not wait for that (a register-only probe whose scale register was
+  reused two instructions later got wrong products in 15 of 16 rows).
 """
 
 import os
@@ -71,3 +75,27 @@ def test_main_loop_keeps_loads_in_flight(asm, inst):
                 any("buffer_load" in x for x in body[j:j + 300]))
     waits = [int(re.search(r"vmcnt\((\d+)\)", x).group(1)) for x in body[loop:loop + 1500] if "vmcnt(" in x][:4]
     assert len(waits) == 4 and min(waits) >= 8, waits
+
+
+def _writes(line, reg):
+    t = line.strip().split(None, 1)
+    if len(t) < 2 or not t[0].startswith("v_"):
+        return False
+    dst = t[1].split(",")[0].strip()
+    m = re.match(r"v\[(\d+):(\d+)\]", dst)
+    if m:
+        return int(m.group(1)) <= int(reg[1:]) <= int(m.group(2))
+    return dst == reg
+
+
+def test_scale_registers_not_rewritten_after_scaled_mfma(asm):
+    n = 0
+    for i, line in enumerate(asm):
+        if "v_mfma_scale" not in line:
+            continue
+        ops = [x.strip() for x in line.split(None, 1)[1].split(",")]
+        regs = {ops[4].split()[0], ops[5].split()[0]}
+        n += 1
+        for later in asm[i + 1:i + 24]:
+            assert not any(_writes(later, r) for r in regs), (line.strip(), later.strip())
+    assert n > 0
