@@ -14,8 +14,8 @@ What it computes (mjolnir-kernel PyPI project page / sdist README, section
 * ``qquant``    dynamic e4m3 quantization of Q per (sequence, KV head), in
                 fp32 with IEEE round-to-nearest division, exactly as the pages
                 define it;
-* ``formats``   the e4m3 / e2m3 codecs and the 6-bit bitstream unpacker, each
-                from the published format definition;
+* ``formats``   the e4m3 / e2m3 / e3m2 / e2m1 codecs and the 6- and 4-bit
+                bitstream packers, each from the published format definition;
 * ``attention`` exact attention over the gathered, dequantized pages in fp64
                 (softmax(Q K^T * scale) V), its split partials and their
                 log-sum-exp merge;

@@ -37,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import e4m3_decode, e2m3_decode, unpack_6bit
+from .formats import ROW_BYTES, decode_row_codes, e4m3_decode
 from .qquant import quantize_q
 
 
@@ -57,9 +57,7 @@ def gather_codes(pool: np.ndarray, strides, page_size: int, bt_row: np.ndarray, 
 
 
 def dequant_rows(codes: np.ndarray, kv_format: str, d: int) -> np.ndarray:
-    if kv_format == "e4m3":
-        return e4m3_decode(codes)
-    return e2m3_decode(unpack_6bit(codes, d))
+    return decode_row_codes(codes, kv_format, d)
 
 
 def descale(values: np.ndarray, kind: str, i: int, g: int) -> float:
@@ -131,7 +129,7 @@ def head_inputs(h: dict, i: int, g: int, *, q_len: int, h_q: int, h_k: int, d: i
     """Dequantized (Q rows, K, V) of sequence i, KV head g, in fp64."""
     h_r = h_q // h_k
     L = int(h["seq_lens"][i])
-    row = d if kv_format == "e4m3" else d * 6 // 8
+    row = ROW_BYTES[kv_format] * d // 128
     kc = gather_codes(h["k_pool"], h["k_strides"], page_size, h["block_table"][i], L, g, row)
     vc = gather_codes(h["v_pool"], h["v_strides"], page_size, h["block_table"][i], L, g, row)
     K = dequant_rows(kc, kv_format, d) * descale(h["k_descale"], h["descale_kind"], i, g)

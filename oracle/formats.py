@@ -17,6 +17,16 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   bitstream)" (mjolnir/runner.py, the comment above ``RUNNER_KV_FORMATS``).
   Reading taken: code k of a row occupies stream bits [6k, 6k+6) and stream
   bit 8B+j is bit j of byte B.
+* e3m2 and e2m1, the other formats the pages' harness reads ("Beyond fp8:
+  the harness": fp6 e2m3/e3m2 and fp4 e2m1): OCP Microscaling FP6 E3M2 --
+  sign bit 5, exponent bits 4..2 with bias 3, mantissa bits 1..0, exponent
+  field 0 subnormal (m/4 * 2^-2), no NaN or infinity, largest magnitude 28 --
+  and OCP Microscaling FP4 E2M1 -- sign bit 3, exponent bits 2..1 with bias
+  1, mantissa bit 0, exponent field 0 subnormal (m/2), largest magnitude 6.
+  Packing (the pages give none for them; the plainest reading, the same
+  little-endian bitstream as e2m3): e3m2 rows exactly like e2m3 rows, e2m1
+  code k at stream bits [4k, 4k+4), i.e. the low nibble of byte k/2 for even
+  k and its high nibble for odd k (64-byte rows).
 """
 
 from __future__ import annotations
@@ -49,8 +59,32 @@ def e2m3_value(code: int) -> float:
     return s * (1.0 + m / 8.0) * 2.0 ** (e - 1)
 
 
+def e3m2_value(code: int) -> float:
+    """Value of one 6-bit e3m2 code from its bit fields."""
+    s = -1.0 if code & 0x20 else 1.0
+    e = (code >> 2) & 0x7
+    m = code & 0x3
+    if e == 0:
+        return s * (m / 4.0) * 2.0 ** -2
+    return s * (1.0 + m / 4.0) * 2.0 ** (e - 3)
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one 4-bit e2m1 code from its bit fields."""
+    s = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * (m / 2.0)
+    return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
 E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 E2M3_TABLE = np.array([e2m3_value(c) for c in range(64)], dtype=np.float64)
+E3M2_TABLE = np.array([e3m2_value(c) for c in range(64)], dtype=np.float64)
+E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+E3M2_MAX = 28.0
+E2M1_MAX = 6.0
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
@@ -59,6 +93,14 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 def e2m3_decode(codes: np.ndarray) -> np.ndarray:
     return E2M3_TABLE[np.asarray(codes, dtype=np.uint8) & 0x3F]
+
+
+def e3m2_decode(codes: np.ndarray) -> np.ndarray:
+    return E3M2_TABLE[np.asarray(codes, dtype=np.uint8) & 0x3F]
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    return E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
 
 
 # finite non-negative e4m3 values in code order 0x00..0x7E (strictly increasing)
@@ -116,6 +158,81 @@ def e2m3_encode(x) -> np.ndarray:
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo)
     return (code | (np.signbit(x).astype(np.int64) << 5)).astype(np.uint8)
+
+
+def _encode_small(x, table_pos: np.ndarray, vmax: float, sign_bit: int, name: str) -> np.ndarray:
+    """Nearest code of a small sign-magnitude format, ties to the even code,
+    saturating at +-vmax; table_pos: the non-negative values in code order
+    (strictly increasing); the sign is kept (negative zero sets the sign)."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    if np.any(~np.isfinite(x)):
+        raise ValueError(f"{name}: non-finite input")
+    a = np.minimum(np.abs(x), vmax)
+    hi = np.minimum(np.searchsorted(table_pos, a, side="left"), len(table_pos) - 1)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_hi = table_pos[hi] - a
+    d_lo = a - table_pos[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return (code | (np.signbit(x).astype(np.int64) << sign_bit)).astype(np.uint8)
+
+
+def e3m2_encode(x) -> np.ndarray:
+    """Round fp32 values to the nearest e3m2 code (6 bits), ties to the even
+    code, saturating at +-28."""
+    return _encode_small(x, E3M2_TABLE[:0x20], E3M2_MAX, 5, "e3m2_encode")
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Round fp32 values to the nearest e2m1 code (4 bits), ties to the even
+    code, saturating at +-6."""
+    return _encode_small(x, E2M1_TABLE[:0x8], E2M1_MAX, 3, "e2m1_encode")
+
+
+def pack_4bit(codes: np.ndarray) -> np.ndarray:
+    """(..., n) 4-bit codes -> (..., n/2) bytes: code k in stream bits
+    [4k, 4k+4), written bit by bit like pack_6bit."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n = codes.shape[-1]
+    assert n % 2 == 0
+    out = np.zeros(codes.shape[:-1] + (n // 2,), dtype=np.uint8)
+    for k in range(n):
+        for j in range(4):
+            bit = 4 * k + j
+            out[..., bit // 8] |= (((codes[..., k] >> j) & 1) << (bit % 8)).astype(np.uint8)
+    return out
+
+
+def unpack_4bit(rows: np.ndarray, n: int) -> np.ndarray:
+    """(..., n/2) bytes -> (..., n) codes of the little-endian 4-bit stream."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    assert rows.shape[-1] * 2 == n
+    out = np.zeros(rows.shape[:-1] + (n,), dtype=np.uint8)
+    k = np.arange(n)
+    for j in range(4):
+        bit = 4 * k + j
+        v = (rows[..., bit // 8] >> (bit % 8).astype(np.uint8)) & 1
+        out |= (v << j).astype(np.uint8)
+    return out
+
+
+# bytes of one 128-value row and the (decode, encode, pack, unpack) of each
+# KV format
+ROW_BYTES = {"e4m3": 128, "e2m3": 96, "e3m2": 96, "e2m1": 64}
+FMT_MAX = {"e4m3": E4M3_MAX, "e2m3": E2M3_MAX, "e3m2": E3M2_MAX, "e2m1": E2M1_MAX}
+
+
+def decode_row_codes(rows: np.ndarray, kv_format: str, n: int = 128) -> np.ndarray:
+    """Packed rows (..., ROW_BYTES) -> (..., n) values of the format."""
+    if kv_format == "e4m3":
+        return e4m3_decode(rows)
+    if kv_format == "e2m3":
+        return e2m3_decode(unpack_6bit(rows, n))
+    if kv_format == "e3m2":
+        return e3m2_decode(unpack_6bit(rows, n))
+    if kv_format == "e2m1":
+        return e2m1_decode(unpack_4bit(rows, n))
+    raise ValueError(kv_format)
 
 
 def pack_6bit(codes: np.ndarray) -> np.ndarray:

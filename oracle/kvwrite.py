@@ -15,16 +15,17 @@ the readings taken, the plainest the text supports:
   a negative slot (a padding token) writes nothing;
 * code = the format's round-to-nearest-even of ``x / scale`` in fp32 (one
   IEEE division, x = fp32 of the bf16 input), saturated at the format's
-  largest magnitude (448 for e4m3, 7.5 for e2m3);
-* e2m3 rows are packed 4 codes per 3 bytes as the decode reads them (the
-  little-endian bitstream of ``formats.pack_6bit``).
+  largest magnitude (448 for e4m3, 7.5 for e2m3, 28 for e3m2, 6 for e2m1);
+* 6-bit rows (e2m3, e3m2) are packed 4 codes per 3 bytes and e2m1 rows 2
+  codes per byte, as the decode reads them (the little-endian bitstreams of
+  ``formats.pack_6bit`` / ``pack_4bit``).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import e2m3_encode, e4m3_encode_sat, pack_6bit
+from .formats import ROW_BYTES, e2m1_encode, e2m3_encode, e3m2_encode, e4m3_encode_sat, pack_4bit, pack_6bit
 
 
 def scale_of(scale, kind: str, g: int, d: int = 128) -> np.ndarray:
@@ -45,7 +46,13 @@ def encode_row(x_bf16_as_f32: np.ndarray, divisor: np.ndarray, kv_format: str) -
     q = (np.asarray(x_bf16_as_f32, dtype=np.float32) / divisor).astype(np.float32)
     if kv_format == "e4m3":
         return e4m3_encode_sat(q)
-    return pack_6bit(e2m3_encode(q))
+    if kv_format == "e2m3":
+        return pack_6bit(e2m3_encode(q))
+    if kv_format == "e3m2":
+        return pack_6bit(e3m2_encode(q))
+    if kv_format == "e2m1":
+        return pack_4bit(e2m1_encode(q))
+    raise ValueError(kv_format)
 
 
 def write_kv(pools, strides, page_size: int, kv_format: str, key, value, slot_mapping, k_scale, v_scale,
@@ -57,7 +64,7 @@ def write_kv(pools, strides, page_size: int, kv_format: str, key, value, slot_ma
     (num_tokens, h_k, 128) holding the bf16 inputs exactly.
     """
     k_pool, v_pool = (np.array(p, dtype=np.uint8, copy=True).reshape(-1) for p in pools)
-    row = 128 if kv_format == "e4m3" else 96
+    row = ROW_BYTES[kv_format]
     n, h_k, d = key.shape
     for t in range(n):
         s = int(slot_mapping[t])

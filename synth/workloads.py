@@ -10,9 +10,10 @@ mjolnir/runner.py, ``T5DecodeRunner.run`` for the Q/K/V/scale shapes):
 * e4m3 caches use one fp32 scale ``amax / 448`` per tensor, per KV head or per
   (sequence, KV head), computed over the pages that group owns, and torch's
   own float8_e4m3fn cast.
-* The e2m3 cache uses static per-(KV head, channel) scales ``amax_c / 7.5``
-  from a separate seeded calibration draw; codes are packed four per three
-  bytes as a little-endian bitstream.
+* The sub-byte caches (e2m3, e3m2, e2m1) use static per-(KV head, channel)
+  scales ``amax_c / max`` (7.5, 28, 6) from a separate seeded calibration
+  draw; 6-bit codes are packed four per three bytes and 4-bit codes two per
+  byte, as little-endian bitstreams.
 * Physical pages are consecutive slices of one seeded permutation of the pool.
   Unused block-table entries and the unused tail slots of each sequence's last
   page hold a poison page (codes of value 448, or 7.5 for e2m3) so that any
@@ -33,6 +34,8 @@ import torch
 
 E4M3_MAX = 448.0
 E2M3_MAX = 7.5
+E3M2_MAX = 28.0
+E2M1_MAX = 6.0
 HEAD_DIM = 128
 OUTLIER_GAIN = 20.0
 CALIB_TOKENS = 8192
@@ -40,6 +43,8 @@ CALIB_TOKENS = 8192
 # poison codes: the largest finite magnitude of each format
 POISON_E4M3 = 0x7E
 POISON_E2M3 = 0x1F
+POISON_E3M2 = 0x1F
+POISON_E2M1 = 0x7
 
 
 @dataclass(frozen=True)
@@ -51,7 +56,7 @@ class Spec:
     h_k: int
     page_size: int
     layout: str  # "HND" | "NHD"
-    kv_format: str  # "e4m3" | "e2m3"
+    kv_format: str  # "e4m3" | "e2m3" | "e3m2" | "e2m1"
     scale_kind: str  # "tensor" | "head" | "seq_head" | "channel" (e2m3 only)
     lens: tuple = ()  # explicit context lengths (tokens, including the q_len new ones)
     lens_loguniform: tuple = ()  # (lo, hi): draw b lengths floor(exp(U(ln lo, ln hi)))
@@ -74,7 +79,8 @@ class Spec:
 
     @property
     def row_bytes(self) -> int:
-        return self.d if self.kv_format == "e4m3" else self.d * 6 // 8
+        bits = {"e4m3": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}[self.kv_format]
+        return self.d * bits // 8
 
 
 # The five workloads (full size) and the 32k-context target point.
@@ -100,6 +106,13 @@ SPECS = {
     # the 32k point at batch 16: the split path (several splits per sequence)
     "32k_b16": Spec("b16_L32768_p64_nhd_e4m3", b=16, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
                     kv_format="e4m3", scale_kind="tensor", lens=(32768,) * 16, seed=1007),
+    # the fp6 long-context point in the harness's other sub-byte formats
+    "cfg5_e3m2": Spec("b4_L131072_p128_hnd_e3m2", b=4, q_len=1, h_q=32, h_k=8, page_size=128, layout="HND",
+                      kv_format="e3m2", scale_kind="channel", lens=(131072,) * 4, k_outliers=4, pool_pages=8192,
+                      seed=1008),
+    "cfg5_e2m1": Spec("b4_L131072_p128_hnd_e2m1", b=4, q_len=1, h_q=32, h_k=8, page_size=128, layout="HND",
+                      kv_format="e2m1", scale_kind="channel", lens=(131072,) * 4, k_outliers=4, pool_pages=8192,
+                      seed=1009),
 }
 
 # Reduced sizes with the same heads, page size, layout, format and scales: the
@@ -114,6 +127,8 @@ SMALL = {
     "cfg5": dict(b=2, lens=(3001, 1290), pool_pages=0),
     "32k": dict(b=3, lens=(2048, 1985, 64), pool_pages=0),
     "32k_b16": dict(b=2, lens=(4096, 3000), pool_pages=0),
+    "cfg5_e3m2": dict(b=2, lens=(3001, 1290), pool_pages=0),
+    "cfg5_e2m1": dict(b=2, lens=(3001, 1290), pool_pages=0),
 }
 
 
@@ -226,16 +241,64 @@ def e2m3_magnitudes() -> list:
     return out
 
 
-def e2m3_encode_table(x: torch.Tensor) -> torch.Tensor:
-    """Nearest e2m3 code of each value (clamped to +-7.5), ties to the even code."""
-    mags = torch.tensor(e2m3_magnitudes(), dtype=torch.float32, device=x.device)
+def e3m2_magnitudes() -> list:
+    """The 32 non-negative e3m2 values in code order (OCP MX FP6 E3M2)."""
+    out = []
+    for m in range(32):
+        e, man = m >> 2, m & 3
+        out.append(man / 4.0 * 0.25 if e == 0 else (1.0 + man / 4.0) * 2.0 ** (e - 3))
+    return out
+
+
+def e2m1_magnitudes() -> list:
+    """The 8 non-negative e2m1 values in code order (OCP MX FP4 E2M1)."""
+    out = []
+    for m in range(8):
+        e, man = m >> 1, m & 1
+        out.append(man / 2.0 if e == 0 else (1.0 + man / 2.0) * 2.0 ** (e - 1))
+    return out
+
+
+def _encode_table(x: torch.Tensor, mags_list: list, sign_bit: int) -> torch.Tensor:
+    """Nearest code of each value of a small sign-magnitude format (clamped to
+    its largest magnitude), ties to the even code."""
+    mags = torch.tensor(mags_list, dtype=torch.float32, device=x.device)
+    n = len(mags_list)
     mids = (mags[1:] + mags[:-1]) * 0.5  # exact in fp32
-    a = x.abs().clamp_max(E2M3_MAX)
+    a = x.abs().clamp_max(mags_list[-1])
     idx = torch.bucketize(a, mids)  # mids[idx-1] < a <= mids[idx]
-    tie = (idx < 31) & (a == mids[idx.clamp_max(30)])
+    tie = (idx < n - 1) & (a == mids[idx.clamp_max(n - 2)])
     idx = torch.where(tie & (idx % 2 == 1), idx + 1, idx)
     sign = (x < 0) | ((x == 0) & torch.signbit(x))
-    return (idx | (sign.to(idx.dtype) << 5)).to(torch.uint8)
+    return (idx | (sign.to(idx.dtype) << sign_bit)).to(torch.uint8)
+
+
+def e2m3_encode_table(x: torch.Tensor) -> torch.Tensor:
+    """Nearest e2m3 code of each value (clamped to +-7.5), ties to the even code."""
+    return _encode_table(x, e2m3_magnitudes(), 5)
+
+
+def e3m2_encode_table(x: torch.Tensor) -> torch.Tensor:
+    return _encode_table(x, e3m2_magnitudes(), 5)
+
+
+def e2m1_encode_table(x: torch.Tensor) -> torch.Tensor:
+    return _encode_table(x, e2m1_magnitudes(), 3)
+
+
+def pack_codes_4bit(codes: torch.Tensor) -> torch.Tensor:
+    """(..., n) 4-bit codes -> (..., n/2) bytes: code 2k in the low nibble of
+    byte k, code 2k + 1 in its high nibble (little-endian bitstream)."""
+    c = codes.to(torch.int32).reshape(*codes.shape[:-1], codes.shape[-1] // 2, 2)
+    return (c[..., 0] | (c[..., 1] << 4)).to(torch.uint8)
+
+
+# per sub-byte format: (largest magnitude, encoder, packer, poison code)
+SUBBYTE = {
+    "e2m3": (E2M3_MAX, e2m3_encode_table, lambda c: pack_codes_6bit(c), POISON_E2M3),
+    "e3m2": (E3M2_MAX, e3m2_encode_table, lambda c: pack_codes_6bit(c), POISON_E3M2),
+    "e2m1": (E2M1_MAX, e2m1_encode_table, lambda c: pack_codes_4bit(c), POISON_E2M1),
+}
 
 
 def pack_codes_6bit(codes: torch.Tensor) -> torch.Tensor:
@@ -309,7 +372,8 @@ def build(spec: Spec, device="cpu") -> Workload:
         v_pool[poison] = POISON_E4M3
         poison_row = torch.full((row,), POISON_E4M3, dtype=torch.uint8, device=device)
     else:
-        poison_row = pack_codes_6bit(torch.full((d,), POISON_E2M3, dtype=torch.uint8, device=device))
+        fmax, enc_fn, pack_fn, pcode = SUBBYTE[s.kv_format]
+        poison_row = pack_fn(torch.full((d,), pcode, dtype=torch.uint8, device=device))
         k_pool[poison] = poison_row
         v_pool[poison] = poison_row
 
@@ -346,8 +410,8 @@ def build(spec: Spec, device="cpu") -> Workload:
         # calibration pass: a separate seeded draw, same outlier channels
         ck = _randn((CALIB_TOKENS, h_k, d), device, s.seed + 1) * gain_t
         cv = _randn((CALIB_TOKENS, h_k, d), device, s.seed + 2)
-        kcs = (ck.abs().amax(dim=0) / E2M3_MAX).contiguous()  # (h_k, d)
-        vcs = (cv.abs().amax(dim=0) / E2M3_MAX).contiguous()
+        kcs = (ck.abs().amax(dim=0) / fmax).contiguous()  # (h_k, d)
+        vcs = (cv.abs().amax(dim=0) / fmax).contiguous()
         del ck, cv
         q_mul = kcs.repeat_interleave(s.h_r, dim=0).contiguous()  # (h_q, d)
         o_mul = vcs.repeat_interleave(s.h_r, dim=0).contiguous()
@@ -357,7 +421,7 @@ def build(spec: Spec, device="cpu") -> Workload:
 
         def encode(i, side, x):
             scl = kcs if side == "k" else vcs
-            return pack_codes_6bit(e2m3_encode_table(x / scl.view(1, h_k, d)))
+            return pack_fn(enc_fn(x / scl.view(1, h_k, d)))
 
     bt_t = torch.from_numpy(bt).to(device)
     for i in range(s.b):

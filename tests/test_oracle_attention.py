@@ -11,7 +11,7 @@ import torch
 
 import synth
 from oracle import attention as A
-from oracle.formats import e4m3_decode, e2m3_decode, unpack_6bit
+from oracle.formats import e2m1_decode, e2m3_decode, e3m2_decode, e4m3_decode, unpack_4bit, unpack_6bit
 
 
 def _ref_sdpa(qrows, K, V, allowed, scale):
@@ -33,7 +33,7 @@ def _args(wl):
     return dict(q_len=s.q_len, h_q=s.h_q, h_k=s.h_k, d=s.d, page_size=s.page_size, kv_format=s.kv_format)
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5"])
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
 def test_matches_sdpa_per_head(key):
     wl, h = _small(key)
     s = wl.spec
@@ -172,10 +172,11 @@ def test_empty_sequence_in_a_batch():
     assert np.all(np.isfinite(O[1:]))
 
 
-def test_fp6_folding_identity():
+@pytest.mark.parametrize("key", ["cfg5", "cfg5_e3m2", "cfg5_e2m1"])
+def test_fp6_folding_identity(key):
     """Channel scales folded into Q and O equal attention on explicitly
     dequantized K/V (the identities in mjolnir/backend.py, _install_fp6_scales)."""
-    wl, h = _small("cfg5")
+    wl, h = _small(key)
     s = wl.spec
     O, _ = A.decode_step(h, causal=True, quantize=False, **_args(wl))
     ks = wl.k_channel_scale.numpy().astype(np.float64)
@@ -183,10 +184,12 @@ def test_fp6_folding_identity():
     for i in range(s.b):
         for g in (0, s.h_k - 1):
             L = int(h["seq_lens"][i])
-            kc = A.gather_codes(h["k_pool"], h["k_strides"], s.page_size, h["block_table"][i], L, g, 96)
-            vc = A.gather_codes(h["v_pool"], h["v_strides"], s.page_size, h["block_table"][i], L, g, 96)
-            K = e2m3_decode(unpack_6bit(kc, 128)) * ks[g]
-            V = e2m3_decode(unpack_6bit(vc, 128)) * vs[g]
+            kc = A.gather_codes(h["k_pool"], h["k_strides"], s.page_size, h["block_table"][i], L, g, s.row_bytes)
+            vc = A.gather_codes(h["v_pool"], h["v_strides"], s.page_size, h["block_table"][i], L, g, s.row_bytes)
+            unpack = (lambda r: unpack_4bit(r, 128)) if s.kv_format == "e2m1" else (lambda r: unpack_6bit(r, 128))
+            dec = {"e2m3": e2m3_decode, "e3m2": e3m2_decode, "e2m1": e2m1_decode}[s.kv_format]
+            K = dec(unpack(kc)) * ks[g]
+            V = dec(unpack(vc)) * vs[g]
             q = h["q"][i, g * s.h_r:(g + 1) * s.h_r].astype(np.float64)
             ref = _ref_sdpa(q, K, V, np.ones((s.h_r, L), bool), h["softmax_scale"])
             assert np.max(np.abs(O[i, g * s.h_r:(g + 1) * s.h_r] - ref)) < 1e-12

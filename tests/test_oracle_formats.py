@@ -120,3 +120,87 @@ def test_generator_e2m3_encoder_is_nearest_even():
     assert np.array_equal(err, best)
     tie = np.isin(np.abs(xs), mids)
     assert np.all((c[tie] & 1) == 0)
+
+
+# ---- e3m2 / e2m1 (the harness's other formats; OCP MX FP6 E3M2 and FP4 E2M1)
+
+def test_e3m2_landmarks():
+    T = F.E3M2_TABLE
+    assert T[0x1F] == 28.0                   # largest magnitude
+    assert T[0x04] == 0.25                   # smallest normal 2^-2
+    assert T[0x01] == 0.0625                 # smallest subnormal 2^-4
+    assert T[0x0C] == 1.0 and T[0x2C] == -1.0
+    assert T[0x20] == 0.0 and np.signbit(T[0x20])
+    assert np.all(np.diff(T[:0x20]) > 0)     # codes 0x00..0x1f increase
+    assert np.array_equal(T[0x20:], -T[:0x20])
+
+
+def test_e2m1_landmarks():
+    assert F.E2M1_TABLE[:8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(F.E2M1_TABLE[8:], -F.E2M1_TABLE[:8])
+    assert np.signbit(F.E2M1_TABLE[8])
+
+
+def test_small_formats_nest_inside_e4m3_per_torch():
+    """e2m1 c e3m2 c e4m3 and e2m1 c e2m3 c e4m3 as value sets, e4m3 taken
+    from torch's own decode of all 256 codes (independent of the tables)."""
+    e4 = set(torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().tolist())
+    assert set(F.E3M2_TABLE.tolist()) <= e4
+    assert set(F.E2M3_TABLE.tolist()) <= e4
+    assert set(F.E2M1_TABLE.tolist()) <= set(F.E3M2_TABLE.tolist())
+    assert set(F.E2M1_TABLE.tolist()) <= set(F.E2M3_TABLE.tolist())
+
+
+@pytest.mark.parametrize("enc,table,n,vmax", [(F.e3m2_encode, F.E3M2_TABLE, 32, 28.0),
+                                              (F.e2m1_encode, F.E2M1_TABLE, 8, 6.0)])
+def test_small_encoders_nearest_even_and_saturating(enc, table, n, vmax):
+    codes = np.arange(2 * n, dtype=np.uint8)
+    assert np.array_equal(enc(table.astype(np.float32)), codes)   # every code maps to itself
+    pos = table[:n]
+    for k in range(n - 1):
+        mid = np.float32((pos[k] + pos[k + 1]) / 2)                  # exact: few mantissa bits
+        want = k if k % 2 == 0 else k + 1
+        assert enc(mid) == want and enc(-mid) == want | n
+        assert enc(np.nextafter(mid, np.float32(0))) == k
+        assert enc(np.nextafter(mid, np.float32(100))) == k + 1
+    big = np.array([vmax, vmax * 1.01, 1e30, -vmax * 3], dtype=np.float32)
+    assert enc(big).tolist() == [n - 1, n - 1, n - 1, 2 * n - 1]
+
+
+def _golden_fp4():
+    rows = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "fp4_pack_example.txt")):
+        if line.startswith("#") or "->" not in line:
+            continue
+        a, b = line.split("->")
+        rows.append(([int(x) for x in a.split()], [int(x, 16) for x in b.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("codes,packed", _golden_fp4())
+def test_pack_4bit_worked_examples(codes, packed):
+    assert F.pack_4bit(np.array(codes, dtype=np.uint8)).tolist() == packed
+    assert F.unpack_4bit(np.array(packed, dtype=np.uint8), len(codes)).tolist() == codes
+
+
+def test_decode_row_codes_dispatch():
+    rng = np.random.default_rng(5)
+    c6 = rng.integers(0, 64, (3, 128), dtype=np.uint8)
+    c4 = rng.integers(0, 16, (3, 128), dtype=np.uint8)
+    assert np.array_equal(F.decode_row_codes(F.pack_6bit(c6), "e3m2"), F.E3M2_TABLE[c6])
+    assert np.array_equal(F.decode_row_codes(F.pack_6bit(c6), "e2m3"), F.E2M3_TABLE[c6])
+    assert np.array_equal(F.decode_row_codes(F.pack_4bit(c4), "e2m1"), F.E2M1_TABLE[c4])
+
+
+def test_generator_small_encoders_agree_with_the_oracle():
+    """The generator's table encoders (torch, used to fill the caches) give
+    the oracle encoders' codes on grid points, midpoints and random values."""
+    from synth.workloads import e2m1_encode_table, e3m2_encode_table
+    rng = np.random.default_rng(9)
+    for enc_t, enc_o, table, n in ((e3m2_encode_table, F.e3m2_encode, F.E3M2_TABLE, 32),
+                                   (e2m1_encode_table, F.e2m1_encode, F.E2M1_TABLE, 8)):
+        pos = table[:n]
+        mids = (pos[1:] + pos[:-1]) / 2
+        x = np.concatenate([pos, -pos, mids, -mids, rng.normal(0, pos[-1] / 3, 5000), [1e4, -1e4]])
+        x = x.astype(np.float32)
+        assert np.array_equal(enc_t(torch.from_numpy(x)).numpy(), enc_o(x))

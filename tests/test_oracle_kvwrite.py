@@ -74,7 +74,7 @@ def test_pack_unpack_round_trip():
 
 
 def _pools(kv_format, layout, pages, page_size, h_k):
-    row = 128 if kv_format == "e4m3" else 96
+    row = F.ROW_BYTES[kv_format]
     if layout == "HND":
         st = (h_k * page_size * row, row, page_size * row)
     else:
@@ -114,20 +114,22 @@ def test_padding_slots_write_nothing():
     assert np.all(k == 7) and np.all(v == 9)
 
 
-@pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e2m3", "channel")])
+@pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e2m3", "channel"),
+                                            ("e3m2", "channel"), ("e2m1", "channel"), ("e2m1", "head")])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 def test_write_round_trip_through_decoders(kv_format, kind, layout):
     rng = np.random.default_rng(11)
     h_k, P, pages, n = 2, 16, 8, 40
-    size, strides, row = _pools(kv_format, layout, pages, P, h_k)
+    size, strides, _ = _pools(kv_format, layout, pages, P, h_k)
+    row = F.ROW_BYTES[kv_format]
     x = torch.from_numpy(rng.standard_normal((n, h_k, 128)).astype(np.float32)).to(torch.bfloat16).float().numpy()
     amax = np.abs(x).max()
     if kind == "tensor":
-        sc = np.array([amax / 448], np.float32)
+        sc = np.array([amax / F.FMT_MAX[kv_format]], np.float32)
     elif kind == "head":
-        sc = (np.abs(x).max(axis=(0, 2)) / 448).astype(np.float32)
+        sc = (np.abs(x).max(axis=(0, 2)) / F.FMT_MAX[kv_format]).astype(np.float32)
     else:
-        sc = (np.abs(x).max(axis=0) / 7.5).astype(np.float32)  # (h_k, 128)
+        sc = (np.abs(x).max(axis=0) / F.FMT_MAX[kv_format]).astype(np.float32)  # (h_k, 128)
     slots = rng.permutation(pages * P)[:n]
     slots[5] = -1
     k, _ = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), strides, P, kv_format, x, x, slots,
@@ -139,13 +141,33 @@ def test_write_round_trip_through_decoders(kv_format, kind, layout):
         for g in range(h_k):
             b = page * strides[0][0] + off * strides[0][1] + g * strides[0][2]
             raw = k[b:b + row]
-            dec = F.e4m3_decode(raw) if kv_format == "e4m3" else F.e2m3_decode(F.unpack_6bit(raw, 128))
+            dec = F.decode_row_codes(raw, kv_format)
             s = W.scale_of(sc, kind, g)
             y = x[t, g] / s
             got = dec
             # nearest-value rounding: the error is at most half the local grid
-            # step (3 mantissa bits: 2^-4 relative in the normal range, the
-            # subnormal step below it)
-            sub = 2.0 ** -9 if kv_format == "e4m3" else 1.0 / 8
-            bound = np.maximum(np.abs(y) * 2.0 ** -4, sub / 2)
+            # step (m mantissa bits: 2^-(m+1) relative in the normal range,
+            # half the subnormal step below it)
+            mbits, sub = {"e4m3": (3, 2.0 ** -9), "e2m3": (3, 1.0 / 8), "e3m2": (2, 2.0 ** -4),
+                          "e2m1": (1, 0.5)}[kv_format]
+            bound = np.maximum(np.abs(y) * 2.0 ** -(mbits + 1), sub / 2)
             assert np.all(np.abs(got - y) <= bound + 1e-12)
+
+
+def test_write_hand_worked_e2m1_and_e3m2_rows():
+    # one token, one KV head, page size 16, per-tensor scale 1, slot 0, HND
+    x = np.zeros((1, 1, 128), dtype=np.float32)
+    x[0, 0, :4] = [3.0, -1.0, 100.0, 0.25]
+    # e2m1: 3 -> 0x5, -1 -> 0x8|0x2 = 0xA, 100 saturates to 6 -> 0x7, 0.25 is the
+    # midpoint of 0 and 0.5 -> the even code 0; bytes 0x5|0xA<<4 = 0xA5, 0x7|0<<4 = 0x07
+    size = 16 * 64
+    k, _ = W.write_kv((np.full(size, 0xEE, np.uint8), np.zeros(size, np.uint8)), ((16 * 64, 64, 16 * 64),) * 2,
+                      16, "e2m1", x, x, np.array([0]), np.ones(1, np.float32), np.ones(1, np.float32), "tensor")
+    assert k[:2].tolist() == [0xA5, 0x07] and np.all(k[2:64] == 0) and np.all(k[64:] == 0xEE)
+    # e3m2: 1 -> 0x0C, 30 saturates to 28 -> 0x1F, -0.0625 -> 0x21, 0.03125 (midpoint of
+    # 0 and 2^-4) -> 0; w = 0x0C | 0x1F<<6 | 0x21<<12 = 0x217CC -> bytes CC 17 02
+    x[0, 0, :4] = [1.0, 30.0, -0.0625, 0.03125]
+    size = 16 * 96
+    k, _ = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), ((16 * 96, 96, 16 * 96),) * 2,
+                      16, "e3m2", x, x, np.array([0]), np.ones(1, np.float32), np.ones(1, np.float32), "tensor")
+    assert k[:3].tolist() == [0xCC, 0x17, 0x02] and np.all(k[3:96] == 0)
