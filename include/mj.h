@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 4
+#define MJ_ABI_VERSION 5
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -61,17 +61,25 @@ typedef enum mj_status {
 
 typedef enum mj_kv_format {
   MJ_KV_E4M3 = 0,  /* one OCP e4m3 (float8_e4m3fn) byte per value, 128-byte rows  */
-  MJ_KV_E2M3 = 1   /* OCP MX e2m3 6-bit codes, 4 per 3 bytes, 96-byte rows:
+  MJ_KV_E2M3 = 1,  /* OCP MX e2m3 6-bit codes, 4 per 3 bytes, 96-byte rows:
                       code k of a row is stream bits [6k, 6k+6), stream bit 8B+j
                       being bit j of byte B (runner.py, comment above
                       RUNNER_KV_FORMATS: "little-endian bitstream")             */
+  MJ_KV_E3M2 = 2,  /* OCP MX e3m2 6-bit codes (bias 3, max 28), packed as e2m3
+                      (project page, "Beyond fp8: the harness" names fp6
+                      e3m2; the pages give no packing, the e2m3 bitstream is
+                      taken)                                                    */
+  MJ_KV_E2M1 = 3   /* OCP MX e2m1 4-bit codes (bias 1, max 6), 64-byte rows:
+                      code k is stream bits [4k, 4k+4), i.e. the low nibble of
+                      byte k/2 for even k, the high nibble for odd k (same
+                      section: fp4 e2m1; same bitstream reading)               */
 } mj_kv_format;
 
 /* How the decode takes Q (runner.py, T5DecodeRunner.__init__ `q_mode`, and
  * the backend's MJOLNIR_ATTN_Q_DTYPE): quantized per (sequence, KV head) to
  * e4m3 by mj_quantize_q, or used as is in bf16 with the KV codes converted
- * to bf16 inside the decode kernel (e4m3 KV only: the packed e2m3 cache
- * takes fp8 Q only, per the runner's kv_format comment). */
+ * to bf16 inside the decode kernel (e4m3 KV only: the packed sub-byte caches
+ * take fp8 Q only, per the runner's kv_format comment). */
 typedef enum mj_q_mode {
   MJ_Q_FP8 = 0,   /* dynamic e4m3 Q: mj_quantize_q, then q8 / q_descale        */
   MJ_Q_BF16 = 1   /* bf16 Q as given: logit = softmax_scale * k_descale *
@@ -110,8 +118,8 @@ typedef struct mj_config {
 /* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):
  * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
  * workgroups per CU; four waves of items of >= 2048 tokens balance the tail
- * across CUs and XCDs); 16 < n_q <= 32, or e2m3 -> 1 / 1 (one wave);
- * n_q > 32 -> 2 / 1.  min_chunk_tokens is rounded up to whole KV tiles. */
+ * across CUs and XCDs); 16 < n_q <= 32, or fp6 (e2m3 / e3m2) -> 1 / 1 (one
+ * wave); e2m1, or n_q > 32 -> 2 / 1.  min_chunk_tokens is rounded up to whole KV tiles. */
 
 /* What a plan decided (runner.py, StepPlan). */
 typedef struct mj_plan_info {
@@ -320,9 +328,10 @@ typedef struct mj_write_args {
  * mjolnir/backend.py, do_kv_cache_update: an fp8 cache written with the
  * layer's per-tensor or per-head scale, the fp6 cache with per-(KV head,
  * channel) scales, _install_fp6_scales).  Every value becomes
- * RNE(x / scale) in the config's KV format, saturated at 448 (e4m3) or 7.5
- * (e2m3), x the fp32 value of the bf16 input and the division correctly
- * rounded; e2m3 rows are packed as mj_paged_decode reads them.  Tokens are
+ * RNE(x / scale) in the config's KV format, saturated at its largest
+ * magnitude (448 e4m3, 7.5 e2m3, 28 e3m2, 6 e2m1), x the fp32 value of the
+ * bf16 input and the division correctly rounded; sub-byte rows are packed
+ * as mj_paged_decode reads them.  Tokens are
  * independent; two tokens mapped to one slot race (the caller's contract,
  * as in any slot-mapped write).  num_tokens == 0 enqueues nothing.
  * Errors: EINVAL (nulls, negative strides or counts, scale kind), EALIGN
@@ -378,10 +387,11 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStre
  * mj_debug_gather_kv copies the codes of tokens 0..seq_len-1 of one
  * (sequence, KV head) from the K (which = 0) or V (which = 1) pool into
  * dense_out (seq_len x row bytes), using the decode kernel's own address
- * computation.  mj_debug_decode_codes decodes n codes (one per byte; e2m3
- * codes in the low 6 bits) with the kernel's own decoder into fp32;
- * kv_format 2 decodes e4m3 codes through the bf16 operand converter of the
- * MJ_Q_BF16 decode (fp32 of the bf16 it yields). */
+ * computation.  mj_debug_decode_codes decodes n codes (one per byte; 6-
+ * and 4-bit codes in the low bits) with the kernel's own decoder of format
+ * kv_format (an mj_kv_format) into fp32; kv_format 16 decodes e4m3 codes
+ * through the bf16 operand converter of the MJ_Q_BF16 decode (fp32 of the
+ * bf16 it yields). */
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, int32_t seq, int32_t head,
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream);
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);

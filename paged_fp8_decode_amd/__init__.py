@@ -1,5 +1,5 @@
-"""Python binding of the mj C ABI (paged decode attention over an e4m3 /
-packed-e2m3 KV cache on MI355X).
+"""Python binding of the mj C ABI (paged decode attention over an e4m3 or
+packed fp6 (e2m3 / e3m2) or fp4 (e2m1) KV cache on MI355X).
 
 The functions below carry the C names and only marshal arguments: every step
 of the decode path runs in the HIP kernels of ``libmj.so``.  PyTorch supplies
@@ -136,7 +136,7 @@ def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_l
 
 
 def mj_debug_decode_codes(kv_format, codes, out, stream=None):
-    fmt = {**KV_FORMATS, "e4m3_bf16": 2}[kv_format] if isinstance(kv_format, str) else kv_format
+    fmt = {**KV_FORMATS, "e4m3_bf16": 16}[kv_format] if isinstance(kv_format, str) else kv_format
     check(lib().mj_debug_decode_codes(fmt, _ptr(codes), codes.numel(), _ptr(out), _stream(stream)),
           "mj_debug_decode_codes")
 

@@ -8,9 +8,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 4  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 5  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
-KV_FORMATS = {"e4m3": 0, "e2m3": 1}
+KV_FORMATS = {"e4m3": 0, "e2m3": 1, "e3m2": 2, "e2m1": 3}
 Q_MODES = {"fp8": 0, "bf16": 1}
 SCALE_KINDS = {"tensor": 0, "head": 1, "seq_head": 2, "channel": 3}
 

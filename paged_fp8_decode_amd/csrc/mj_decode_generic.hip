@@ -30,13 +30,23 @@ __device__ __forceinline__ void load_row16(const uint8_t* row, int chunk, float 
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 16; ++e) out[e] = e4m3_raw((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-  } else {  // e2m3: 12 bytes at chunk*12 hold codes 16*chunk .. 16*chunk+15
+  } else if constexpr (FMT == 3) {  // e2m1: 8 bytes at chunk*8, code e in nibble e
+    const uint2 raw = *reinterpret_cast<const uint2*>(row + chunk * 8);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[e] = e2m1_raw(((e < 8 ? raw.x : raw.y) >> (4 * (e & 7))) & 0xFu);
+  } else {  // e2m3 / e3m2: 12 bytes at chunk*12 hold codes 16*chunk .. 16*chunk+15
     const uint32_t* src = reinterpret_cast<const uint32_t*>(row + chunk * 12);
     uint32_t c[16];
-    unpack16_e2m3(src[0], src[1], src[2], c);
+    unpack16_6bit(src[0], src[1], src[2], c);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) out[e] = e2m3_raw(c[e]);
+    for (int e = 0; e < 16; ++e) out[e] = FMT == 1 ? e2m3_raw(c[e]) : e3m2_raw(c[e]);
   }
+}
+
+// Power of two that turns a format's raw decode into its value.
+template <int FMT>
+constexpr float fmt_rescale() {
+  return FMT == 0 ? kE4m3Rescale : FMT == 1 ? kE2m3Rescale : FMT == 2 ? kE3m2Rescale : kE2m1Rescale;
 }
 
 template <int FMT>
@@ -66,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const bool causal = p.causal && p.q_len > 1;
   const int lim0 = L - p.q_len;  // causal: token t sees keys j <= lim0 + t
 
-  const float rescale = FMT == 0 ? kE4m3Rescale : kE2m3Rescale;
+  const float rescale = fmt_rescale<FMT>();
   const float qs = (p.q_bf16 ? 1.0f : p.q_descale[(int64_t)seq * p.h_k + g]) * p.scale_log2;
   const float kd = load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * rescale;
   const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k) * rescale;
@@ -210,23 +220,26 @@ __global__ void gather_kernel(GatherParams p) {
 __global__ void decode_codes_kernel(int fmt, const uint8_t* codes, int n, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  if (fmt == 2) {  // e4m3 through the bf16 operand converter of the bf16-Q kernel
+  if (fmt == 16) {  // e4m3 through the bf16 operand converter of the bf16-Q kernel
     uint32_t h[2];
     e4m3x4_to_bf16(codes[i], h);
     out[i] = __uint_as_float(h[0] << 16);
     return;
   }
-  out[i] = fmt == 0 ? e4m3_value(codes[i]) : e2m3_value(codes[i] & 63u);
+  const uint32_t c = codes[i];
+  out[i] = fmt == 0 ? e4m3_value(c) : fmt == 1 ? e2m3_value(c & 63u) : fmt == 2 ? e3m2_value(c & 63u) : e2m1_value(c & 15u);
 }
 
 }  // namespace
 
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s) {
   const dim3 grid(p.num_work, p.h_k * row_tiles);
-  if (kv_format == 0)
-    hipLaunchKernelGGL(decode_generic_kernel<0>, grid, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(kThreads), 0, s, p);
+  switch (kv_format) {
+    case 0: hipLaunchKernelGGL(decode_generic_kernel<0>, grid, dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(decode_generic_kernel<2>, grid, dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL(decode_generic_kernel<3>, grid, dim3(kThreads), 0, s, p); break;
+  }
   return hipGetLastError();
 }
 

@@ -431,7 +431,7 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hi
   if (k == 1) {
     // debug setting -> matrix-core cache policy bits (K non-temporal, V non-temporal)
     static const int kPolicy[5] = {0, -1, 3, 2, 1};
-    return launch_decode_mfma(p, kv_format, kPolicy[g_nontemporal], g_variant >= 10 ? g_variant - 10 : 0, s);
+    return launch_decode_mfma(p, kv_format, kPolicy[g_nontemporal], g_variant >= 10 ? g_variant - 10 : -1, s);
   }
   const dim3 grid(p.num_work, p.h_k);
   if (g_nontemporal)

@@ -1,15 +1,18 @@
 // Device-side helpers shared by the mj kernels (gfx950, wave64).
 //
-// Formats (the e4m3 / e2m3 codes the mjolnir-kernel pages name; bit layouts
-// from the OCP OFP8 and OCP MX specifications):
+// Formats (the e4m3 / e2m3 / e3m2 / e2m1 codes the mjolnir-kernel pages name;
+// bit layouts from the OCP OFP8 and OCP MX specifications):
 //   e4m3: s.eeee.mmm, bias 7, subnormal at e == 0, max 448.
 //   e2m3: s.ee.mmm (6 bits), bias 1, subnormal at e == 0, max 7.5.
-// Both decode by moving the exponent/mantissa bits into an fp32 bit pattern
+//   e3m2: s.eee.mm (6 bits), bias 3, subnormal at e == 0, max 28.
+//   e2m1: s.ee.m (4 bits), bias 1, subnormal at e == 0, max 6.
+// All decode by moving the exponent/mantissa bits into an fp32 bit pattern
 // with the same mantissa alignment and rescaling by a power of two: an fp32
-// with exponent field e and mantissa m/8 is 2^(e-127)(1+m/8), and its
-// subnormals (e == 0) are 2^-126 (m/8), so one multiply by 2^120 (e4m3) or
-// 2^126 (e2m3) maps both normal and subnormal codes exactly.  Callers fold
-// that power of two into the descale they multiply by anyway.
+// with exponent field e and mantissa m/2^k is 2^(e-127)(1+m/2^k), and its
+// subnormals (e == 0) are 2^-126 (m/2^k), so one multiply by 2^(127 - bias)
+// -- 2^120 (e4m3), 2^126 (e2m3, e2m1), 2^124 (e3m2) -- maps both normal and
+// subnormal codes exactly.  Callers fold that power of two into the descale
+// they multiply by anyway.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,6 +25,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kE4m3Rescale = 1.329227995784916e+36f;  // 2^120
 constexpr float kE2m3Rescale = 8.507059173023462e+37f;  // 2^126
+constexpr float kE3m2Rescale = 2.1267647932558654e+37f;  // 2^124
+constexpr float kE2m1Rescale = 8.507059173023462e+37f;  // 2^126
 
 __device__ __forceinline__ float bits_to_float(uint32_t u) { return __uint_as_float(u); }
 
@@ -33,8 +38,18 @@ __device__ __forceinline__ float e4m3_raw(uint32_t c) {
 __device__ __forceinline__ float e2m3_raw(uint32_t c) {
   return bits_to_float(((c & 0x20u) << 26) | ((c & 0x1Fu) << 20));
 }
+// e3m2 code (low 6 bits) -> fp32 whose value is 2^-124 * value.
+__device__ __forceinline__ float e3m2_raw(uint32_t c) {
+  return bits_to_float(((c & 0x20u) << 26) | ((c & 0x1Fu) << 21));
+}
+// e2m1 code (low 4 bits) -> fp32 whose value is 2^-126 * value.
+__device__ __forceinline__ float e2m1_raw(uint32_t c) {
+  return bits_to_float(((c & 0x8u) << 28) | ((c & 0x7u) << 22));
+}
 __device__ __forceinline__ float e4m3_value(uint32_t c) { return e4m3_raw(c) * kE4m3Rescale; }
 __device__ __forceinline__ float e2m3_value(uint32_t c) { return e2m3_raw(c) * kE2m3Rescale; }
+__device__ __forceinline__ float e3m2_value(uint32_t c) { return e3m2_raw(c) * kE3m2Rescale; }
+__device__ __forceinline__ float e2m1_value(uint32_t c) { return e2m1_raw(c) * kE2m1Rescale; }
 
 // Four e4m3 codes (one word, byte b = code b) -> four bf16 (two words, code
 // 2i + h in half h of word i) with gfx950's scaled converter at scale 1.
@@ -74,6 +89,32 @@ __device__ __forceinline__ uint32_t e2m3_rne(float x) {
   return sign | (u >= 0x3F800000u ? nrm : sub);
 }
 
+// Round an fp32 to the nearest e3m2 code (6 bits), ties to even, saturating
+// at 28.  Normal range (|x| >= 2^-2): keep 2 of 23 mantissa bits with the
+// carry running into the exponent; below it, multiples of 2^-4.
+__device__ __forceinline__ uint32_t e3m2_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 26) & 0x20u;
+  u &= 0x7FFFFFFFu;
+  const uint32_t r = u + 0xFFFFFu + ((u >> 21) & 1u);
+  const uint32_t nrm = min(((r >> 23) << 2) - (124u << 2) + ((r >> 21) & 3u), 0x1Fu);
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(u) * 16.0f);
+  return sign | (u >= 0x3E800000u ? nrm : sub);
+}
+
+// Round an fp32 to the nearest e2m1 code (4 bits), ties to even, saturating
+// at 6.  Normal range (|x| >= 1): keep 1 of 23 mantissa bits; below it,
+// multiples of 1/2.
+__device__ __forceinline__ uint32_t e2m1_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 28) & 0x8u;
+  u &= 0x7FFFFFFFu;
+  const uint32_t r = u + 0x1FFFFFu + ((u >> 22) & 1u);
+  const uint32_t nrm = min(((r >> 23) << 1) - (126u << 1) + ((r >> 22) & 1u), 0x7u);
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(u) * 2.0f);
+  return sign | (u >= 0x3F800000u ? nrm : sub);
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -101,7 +142,7 @@ __device__ __forceinline__ int64_t kv_offset(int64_t page, int slot, int head, i
 }
 
 // 16 e2m3 codes from 12 packed bytes (three little-endian dwords).
-__device__ __forceinline__ void unpack16_e2m3(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t out[16]) {
+__device__ __forceinline__ void unpack16_6bit(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t out[16]) {
   // stream bit b of the 96-bit group is bit b%32 of word b/32
   const uint64_t lo = (uint64_t)w0 | ((uint64_t)w1 << 32);
   const uint64_t hi = (uint64_t)w1 | ((uint64_t)w2 << 32);  // starts at stream bit 32

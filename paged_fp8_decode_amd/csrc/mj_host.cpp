@@ -36,14 +36,20 @@ struct PlanShape {
 PlanShape plan_shape(const mj_config* c, const Derived& d, int q_len) {
   const int n_q = q_len * d.h_r;
   const bool small_e4m3 = c->kv_format == MJ_KV_E4M3 && n_q <= 16;
+  const bool fp4 = c->kv_format == MJ_KV_E2M1;
   PlanShape ps;
-  ps.wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : (small_e4m3 ? 8 : (n_q <= 32 ? 1 : 2));
+  ps.wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : (small_e4m3 ? 8 : (n_q <= 32 && !fp4 ? 1 : 2));
   ps.min_chunk_tokens = c->min_chunk_tokens ? c->min_chunk_tokens : (small_e4m3 ? 2048 : 1);
   return ps;
 }
 
 int min_chunk_tiles(const mj_config* c, const Derived& d, int q_len) {
   return (plan_shape(c, d, q_len).min_chunk_tokens + d.kv_tile - 1) / d.kv_tile;
+}
+
+// Bytes of one packed 128-channel K or V row of each format.
+int kv_row_bytes(int kv_format) {
+  return kv_format == MJ_KV_E4M3 ? 128 : (kv_format == MJ_KV_E2M1 ? 64 : 96);
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -58,9 +64,9 @@ mj_status check_config(const mj_config* c) {
   if (c->h_q % c->h_k != 0) return MJ_EUNSUPPORTED;
   if (c->head_dim != 128) return MJ_EUNSUPPORTED;
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64 && c->page_size != 128) return MJ_EUNSUPPORTED;
-  if (c->kv_format != MJ_KV_E4M3 && c->kv_format != MJ_KV_E2M3) return MJ_EUNSUPPORTED;
+  if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_E2M1) return MJ_EUNSUPPORTED;
   if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
-  if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3) return MJ_EUNSUPPORTED;  // packed e2m3 takes fp8 Q only
+  if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3) return MJ_EUNSUPPORTED;  // packed formats take fp8 Q only
   if ((int64_t)c->max_q_len * (c->h_q / c->h_k) > kMaxRows) return MJ_ECAPACITY;
   return MJ_OK;
 }
@@ -651,7 +657,7 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
   p.seq = seq;
   p.head = head;
   p.seq_len = seq_len;
-  p.row_bytes = cfg->kv_format == MJ_KV_E4M3 ? 128 : 96;
+  p.row_bytes = kv_row_bytes(cfg->kv_format);
   p.page_shift = ilog2(cfg->page_size);
   p.out = dense_out;
   return mj::launch_gather(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
@@ -669,7 +675,8 @@ mj_status mj_debug_stream_read(const void* src, int64_t bytes, uint32_t* out, in
 }
 
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream) {
-  if (!codes || !out || n < 0 || kv_format < 0 || kv_format > 2) return MJ_EINVAL;
+  if (!codes || !out || n < 0 || ((kv_format < MJ_KV_E4M3 || kv_format > MJ_KV_E2M1) && kv_format != 16))
+    return MJ_EINVAL;
   return mj::launch_decode_codes(kv_format, codes, n, out, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 

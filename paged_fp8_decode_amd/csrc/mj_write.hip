@@ -3,19 +3,22 @@
 //
 // Method (wheel listing mjolnir/backend.py, do_kv_cache_update, _write_kv
 // and _install_fp6_scales): an e4m3 cache is written with a per-tensor or
-// per-KV-head scale, a packed e2m3 cache with per-(KV head, channel) scales
-// s_c.  Each value becomes round-to-nearest-even(x / s) in the cache format,
-// saturated at its largest magnitude (448 / 7.5), from one correctly rounded
+// per-KV-head scale, a packed fp6 cache with per-(KV head, channel) scales
+// s_c (any scale kind is taken for any format).  Each value becomes
+// round-to-nearest-even(x / s) in the cache format, saturated at its largest
+// magnitude (448 e4m3, 7.5 e2m3, 28 e3m2, 6 e2m1), from one correctly rounded
 // fp32 division (built with -fhip-fp32-correctly-rounded-divide-sqrt) of
 // the exact fp32 value of the bf16 input (computed from the correctly rounded
 // reciprocal with one FMA correction), so the bytes are the same as any other
-// correct evaluation.  e2m3 rows are the little-endian 6-bit stream
-// the decode kernels read (code k at stream bits [6k, 6k+6)).  Slot s is
+// correct evaluation.  fp6 and fp4 rows are the little-endian 6- and 4-bit
+// streams the decode kernels read (code k at stream bits [6k, 6k+6) or
+// [4k, 4k+4)).  Slot s is
 // page s / page_size, row s % page_size; a negative slot (padding) or one
 // past the pool is skipped.
 //
 // One thread per (KV head, 16 channels) of 8 tokens: 32 bytes of bf16 in
-// per side and token, 16 bytes (e4m3) or 12 bytes (e2m3) of codes out.  The
+// per side and token, 16 bytes (e4m3), 12 bytes (fp6) or 8 bytes (fp4) of
+// codes out.  The
 // write touches every byte once.
 #include "mj_device.h"
 #include "mj_internal.h"
@@ -31,7 +34,8 @@ constexpr int kWThreads = 256;
 // correctly rounded quotient (Markstein's theorem; Muller et al., Handbook of
 // Floating-Point Arithmetic, on division by FMA).  Quotients that underflow
 // into fp32 subnormals or overflow lie far below or above every rounding
-// boundary of e4m3 / e2m3, so their codes are those of the exact quotient.
+// boundary of the four formats, so their codes are those of the exact
+// quotient.
 // Scales are positive and finite.
 __device__ __forceinline__ float div_rn(float x, float s, float y) {
   const float q = x * y;
@@ -51,7 +55,7 @@ __device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc
   for (int i = 0; i < 16; ++i) {
     const uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
     const float q = div_rn(__uint_as_float(bits), sc[i], rc[i]);
-    code[i] = FMT == 0 ? e4m3_rne(q) : e2m3_rne(q);
+    code[i] = FMT == 0 ? e4m3_rne(q) : FMT == 1 ? e2m3_rne(q) : FMT == 2 ? e3m2_rne(q) : e2m1_rne(q);
   }
   if constexpr (FMT == 0) {
     uint4 o;
@@ -60,6 +64,14 @@ __device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc
     o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
     o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
     *reinterpret_cast<uint4*>(dst_row + c0) = o;
+  } else if constexpr (FMT == 3) {
+    uint2 o = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o.x |= code[k] << (4 * k);
+      o.y |= code[k + 8] << (4 * k);
+    }
+    *reinterpret_cast<uint2*>(dst_row + (c0 / 16) * 8) = o;
   } else {
     uint32_t o[3] = {0u, 0u, 0u};
 #pragma unroll
@@ -126,10 +138,12 @@ hipError_t launch_write_kv(const WriteParams& p_in, hipStream_t s) {
   const int64_t threads = ((int64_t)p.num_tokens + p.tokens_per_thread - 1) / p.tokens_per_thread * p.h_k * 8;
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + kWThreads - 1) / kWThreads));
-  if (p.kv_format == 0)
-    hipLaunchKernelGGL(write_kv_kernel<0>, grid, dim3(kWThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(write_kv_kernel<1>, grid, dim3(kWThreads), 0, s, p);
+  switch (p.kv_format) {
+    case 0: hipLaunchKernelGGL(write_kv_kernel<0>, grid, dim3(kWThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL(write_kv_kernel<1>, grid, dim3(kWThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(write_kv_kernel<2>, grid, dim3(kWThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL(write_kv_kernel<3>, grid, dim3(kWThreads), 0, s, p); break;
+  }
   return hipGetLastError();
 }
 

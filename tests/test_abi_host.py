@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 4
+    assert mj.lib().mj_abi_version() == 5
 
 
 def _cfg(**kw):
@@ -37,7 +37,7 @@ def _cfg(**kw):
 
 
 def _oracle(cfg, lens, q_len, margin=0):
-    fmt = "e4m3" if cfg.kv_format == 0 else "e2m3"
+    fmt = {v: k for k, v in mj.KV_FORMATS.items()}[cfg.kv_format]
     wgs, mct = oplan.default_shape(fmt, q_len * (cfg.h_q // cfg.h_k))
     kv_tile = cfg.kv_tile_tokens or 128
     mct = cfg.min_chunk_tokens or mct
@@ -98,7 +98,7 @@ def test_planner_matches_oracle_random():
                    wgs_per_cu=int(rng.integers(0, 5)), kv_tile_tokens=int(rng.choice([16, 64, 128, 256])),
                    slots_override=int(rng.choice([0, 0, 0, 7, 300])),
                    min_chunk_tokens=int(rng.choice([0, 0, 1, 100, 2048, 9000])),
-                   kv_format=str(rng.choice(["e4m3", "e2m3"])))
+                   kv_format=str(rng.choice(["e4m3", "e2m3", "e3m2", "e2m1"])))
         b = int(rng.integers(1, cfg.max_num_seqs + 1))
         lens = rng.integers(0, int(rng.choice([100, 5000, 200000])), size=b).tolist()
         _compare(cfg, lens, int(rng.integers(1, mq + 1)), int(rng.integers(0, 8)))
@@ -110,13 +110,17 @@ def test_config_errors():
     assert mj.mj_config_check(_cfg(page_size=24)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_config_check(_cfg(page_size=256)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_config_check(_cfg(h_q=30, h_k=8)) == mj.MJ_EUNSUPPORTED
-    assert mj.mj_config_check(_cfg(kv_format=3)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(kv_format=4)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(kv_format=-1)) == mj.MJ_EUNSUPPORTED
+    for f in ("e2m3", "e3m2", "e2m1"):
+        assert mj.mj_config_check(_cfg(kv_format=f)) == mj.MJ_OK
     assert mj.mj_config_check(_cfg(max_num_seqs=0)) == mj.MJ_EINVAL
     assert mj.mj_config_check(_cfg(kv_tile_tokens=100)) == mj.MJ_EINVAL
     assert mj.mj_config_check(_cfg(q_mode="bf16")) == mj.MJ_OK
     assert mj.mj_config_check(_cfg(q_mode=2)) == mj.MJ_EINVAL
-    # the packed e2m3 cache takes fp8 Q only
-    assert mj.mj_config_check(_cfg(q_mode="bf16", kv_format="e2m3")) == mj.MJ_EUNSUPPORTED
+    # the packed sub-byte caches take fp8 Q only
+    for f in ("e2m3", "e3m2", "e2m1"):
+        assert mj.mj_config_check(_cfg(q_mode="bf16", kv_format=f)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_plan_buffer_bytes(_cfg(head_dim=64)) == 0
     assert mj.mj_workspace_bytes(_cfg(page_size=8)) == 0
 
@@ -229,8 +233,9 @@ def test_quantize_and_merge_errors():
     m.out = FAKE
     m.num_seqs = 0
     assert L.mj_merge_lse(ctypes.byref(cfg), ctypes.byref(m), None) == mj.MJ_EINVAL
-    assert L.mj_debug_decode_codes(7, FAKE, 4, FAKE, None) == mj.MJ_EINVAL
-    assert L.mj_debug_decode_codes(3, FAKE, 4, FAKE, None) == mj.MJ_EINVAL
+    for fmt in (-1, 4, 7, 15, 17):
+        assert L.mj_debug_decode_codes(fmt, FAKE, 4, FAKE, None) == mj.MJ_EINVAL
+    assert L.mj_debug_decode_codes(0, FAKE, -1, FAKE, None) == mj.MJ_EINVAL
 
 
 def _wargs(**kw):

@@ -44,7 +44,7 @@ FINE = dict(min_chunk_tokens=1)
 
 
 def test_code_decoders_exhaustive(mj, gpu):
-    from oracle.formats import E4M3_TABLE, E2M3_TABLE
+    from oracle.formats import E2M1_TABLE, E2M3_TABLE, E3M2_TABLE, E4M3_TABLE
     codes = torch.arange(256, dtype=torch.uint8, device=gpu)
     out = torch.empty(256, dtype=torch.float32, device=gpu)
     mj.mj_debug_decode_codes("e4m3", codes, out)
@@ -58,6 +58,14 @@ def test_code_decoders_exhaustive(mj, gpu):
     mj.mj_debug_decode_codes("e2m3", codes, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), E2M3_TABLE)
+    for fmt, table in (("e3m2", E3M2_TABLE), ("e2m1", E2M1_TABLE)):
+        codes = torch.arange(len(table), dtype=torch.uint8, device=gpu)
+        out = torch.empty(len(table), dtype=torch.float32, device=gpu)
+        mj.mj_debug_decode_codes(fmt, codes, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, table), fmt
+        assert np.array_equal(np.signbit(got), np.signbit(table)), fmt
 
 
 @pytest.mark.parametrize("b,q_len,h_q,h_k,mul,extra", [(1, 1, 8, 2, False, 0), (32, 1, 32, 8, False, 0),
@@ -81,7 +89,7 @@ def test_quantize_q_bit_exact(mj, gpu, b, q_len, h_q, h_k, mul, extra):
     assert np.array_equal(q8.cpu().numpy().reshape(ref_c.shape), ref_c)
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5"])
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
 def test_gather_probe_bit_exact(mj, gpu, key):
     from oracle.attention import gather_codes
     from paged_fp8_decode_amd.runner import DecodeStep
@@ -107,7 +115,7 @@ def test_gather_probe_bit_exact(mj, gpu, key):
                 assert np.array_equal(dense.cpu().numpy()[: L * row].reshape(L, row), ref)
 
 
-SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "32k", "32k_b16"]
+SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "32k", "32k_b16"]
 # 0 = automatic choice, 1 = generic LDS kernel, 2 = VALU-PV streaming kernel
 VARIANTS = [0, 1, 2]
 
@@ -133,7 +141,7 @@ def test_parity_small_all_outputs(mj, gpu, key, variant):
     compare_lse(lse, LSE, wl.spec.name)
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5"])
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
 def test_split_and_unsplit_agree(mj, gpu, key, variant):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
@@ -235,7 +243,8 @@ def test_graph_replay_after_replanning(mj, gpu):
         compare_lse(lse, LSE, f"replay {trial}")
 
 
-FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "32k": 2, "32k_b16": 2}
+FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "cfg5_e3m2": 1, "cfg5_e2m1": 1, "32k": 2,
+        "32k_b16": 2}
 
 
 @pytest.mark.parametrize("key", list(FULL))
@@ -406,7 +415,8 @@ def test_fused_step_graph_replay(mj, gpu, step_merge):
 
 
 @pytest.mark.parametrize("shape", [dict(h_q=32, h_k=8, q_len=1), dict(h_q=64, h_k=8, q_len=4),
-                                   dict(h_q=8, h_k=2, q_len=1, kv_format="e2m3")])
+                                   dict(h_q=8, h_k=2, q_len=1, kv_format="e2m3"),
+                                   dict(h_q=32, h_k=8, q_len=1, kv_format="e2m1")])
 def test_plan_in_kernel_matches_host_plan(mj, gpu, shape):
     """mj_decode_step with plan_on_device: the decode workgroups derive their
     items from the device lengths.  Outputs are bit-identical to the step on
@@ -414,7 +424,7 @@ def test_plan_in_kernel_matches_host_plan(mj, gpu, shape):
     host plan's; batches beyond the in-kernel limit take the device
     planner."""
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
-    key = "cfg5" if shape.get("kv_format") == "e2m3" else "cfg2"
+    key = {"e2m3": "cfg5", "e2m1": "cfg5_e2m1"}.get(shape.get("kv_format"), "cfg2")
     rng = np.random.default_rng(31 + shape["q_len"])
     for trial, b in enumerate([1, 3, 17, 64, 130, 256, 260]):
         lens = tuple(int(x) for x in rng.integers(0, 700, size=b))

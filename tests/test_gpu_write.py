@@ -1,5 +1,5 @@
 """GPU parity of the KV-cache write (mj_write_kv) against the oracle: whole
-pools compared byte for byte after the write (both formats, every scale
+pools compared byte for byte after the write (every KV format, every scale
 kind, HND and NHD, strided K/V views, padding and out-of-pool slots,
 saturating values), and a written cache decoded end to end."""
 
@@ -30,7 +30,7 @@ def _write(mj, gpu, cfg, key, value, slots, k_pool, v_pool, ks, vs, k_scale, v_s
     # the kernel trusts these sizes: check them before the launch
     assert slots.numel() == key.shape[0] == value.shape[0]
     assert key.shape[1:] == value.shape[1:] == (cfg.h_k, 128)
-    row = 128 if cfg.kv_format == 0 else 96
+    row = (128, 96, 96, 64)[cfg.kv_format]
     last = (num_pages - 1) * ks[0] + (cfg.page_size - 1) * ks[1] + (cfg.h_k - 1) * ks[2] + row
     assert last <= k_pool.numel() and last <= v_pool.numel()
     need = {"tensor": 1, "head": cfg.h_k, "channel": cfg.h_k * 128}[kind]
@@ -48,16 +48,18 @@ def _write(mj, gpu, cfg, key, value, slots, k_pool, v_pool, ks, vs, k_scale, v_s
 
 
 @pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e4m3", "channel"),
-                                            ("e2m3", "channel"), ("e2m3", "head")])
+                                            ("e2m3", "channel"), ("e2m3", "head"), ("e3m2", "channel"),
+                                            ("e3m2", "tensor"), ("e2m1", "channel"), ("e2m1", "head")])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 @pytest.mark.parametrize("P", [16, 128])
 def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
+    from oracle.formats import FMT_MAX, ROW_BYTES
     from oracle.kvwrite import write_kv
     say(f"write {kv_format} {kind} {layout} P={P}")
     rng = np.random.default_rng(zlib.crc32(f"{kv_format}{kind}{layout}{P}".encode()))
     h_k, n = 4, 300
     pages = max(9, -(-2 * n // P))  # at least two slots per token
-    row = 128 if kv_format == "e4m3" else 96
+    row = ROW_BYTES[kv_format]
     ks = vs = _strides(layout, P, h_k, row)
     size = pages * P * h_k * row
     init_k = rng.integers(0, 256, size, dtype=np.uint8)
@@ -68,7 +70,7 @@ def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
     fused[1, 0, :10] = special  # token 1 of K and token 2 of V are written (not padding)
     fused[2, h_k + 1, 118:] = special
     key, value = fused[:, :h_k], fused[:, h_k + 1:2 * h_k + 1]
-    fmax = 448.0 if kv_format == "e4m3" else 7.5
+    fmax = FMT_MAX[kv_format]
     amax_k = key.float().abs().amax(dim=0).numpy()  # (h_k, 128); saturating rows stay rare
     amax_v = value.float().abs().amax(dim=0).numpy()
     if kind == "tensor":
@@ -104,7 +106,7 @@ def test_write_zero_tokens_is_a_noop(mj, gpu):
     mj.mj_write_kv(cfg, a)
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg5"])
+@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
 def test_written_cache_decodes(mj, gpu, key):
     """Blank every token row of a seeded workload's cache, re-write them with
     mj_write_kv from the dequantized K/V (code * scale in bf16: dividing by
@@ -149,7 +151,7 @@ def test_written_cache_decodes(mj, gpu, key):
         for g in range(s.h_k):
             for pool, st, dst, sc in ((h["k_pool"], h["k_strides"], kx, k_sc), (h["v_pool"], h["v_strides"], vx, v_sc)):
                 codes = gather_codes(pool, st, s.page_size, bt, L, g, row)
-                vals = F.e4m3_decode(codes) if s.kv_format == "e4m3" else F.e2m3_decode(F.unpack_6bit(codes, 128))
+                vals = F.decode_row_codes(codes, s.kv_format)
                 div = sc[0] if kind == "tensor" else (sc[g] if kind == "head" else sc.reshape(-1, 128)[g])
                 dst[base:base + L, g] = vals * div
         base += L
