@@ -12,7 +12,8 @@ mjolnir/runner.py, ``T5DecodeRunner.run`` and ``split_kv_cache``):
    head-major or token-major pages differ only in the strides);
 2. dequantize: ``K = k_descale * dec(k_code)``, ``V = v_descale * dec(v_code)``
    with the descale per tensor, per KV head or per (sequence, KV head)
-   (``run``'s ``k_scale`` / ``v_scale`` shapes);
+   (``run``'s ``k_scale`` / ``v_scale`` shapes); for nvfp4, ``dec`` includes
+   the row's e4m3 block scale (``formats.nvfp4_decode``);
 3. quantize Q exactly as ``qquant.quantize_q`` and dequantize it,
    ``Q = q_descale * dec(q_code)`` (or skip this and use fp32 Q times q_mul);
 4. ``S = softmax_scale * Q K^T``; mask; ``P = softmax(S)``; ``O = P V``;
@@ -37,7 +38,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import ROW_BYTES, decode_row_codes, e4m3_decode
+from .formats import ROW_BYTES, SCALE_ROW_BYTES, decode_row_codes, e4m3_decode, nvfp4_decode
 from .qquant import quantize_q
 
 
@@ -132,8 +133,16 @@ def head_inputs(h: dict, i: int, g: int, *, q_len: int, h_q: int, h_k: int, d: i
     row = ROW_BYTES[kv_format] * d // 128
     kc = gather_codes(h["k_pool"], h["k_strides"], page_size, h["block_table"][i], L, g, row)
     vc = gather_codes(h["v_pool"], h["v_strides"], page_size, h["block_table"][i], L, g, row)
-    K = dequant_rows(kc, kv_format, d) * descale(h["k_descale"], h["descale_kind"], i, g)
-    V = dequant_rows(vc, kv_format, d) * descale(h["v_descale"], h["descale_kind"], i, g)
+    if kv_format == "nvfp4":
+        # the block scales of each row, gathered through their own pool's strides
+        srow = SCALE_ROW_BYTES[kv_format] * d // 128
+        ks = gather_codes(h["k_bs_pool"], h["k_bs_strides"], page_size, h["block_table"][i], L, g, srow)
+        vs = gather_codes(h["v_bs_pool"], h["v_bs_strides"], page_size, h["block_table"][i], L, g, srow)
+        Kc, Vc = nvfp4_decode(kc, ks, d), nvfp4_decode(vc, vs, d)
+    else:
+        Kc, Vc = dequant_rows(kc, kv_format, d), dequant_rows(vc, kv_format, d)
+    K = Kc * descale(h["k_descale"], h["descale_kind"], i, g)
+    V = Vc * descale(h["v_descale"], h["descale_kind"], i, g)
     if quantize:
         qrows = np.float64(q_descale[i, g]) * e4m3_decode(q_codes[i, g])
     else:

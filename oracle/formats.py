@@ -27,6 +27,16 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   little-endian bitstream as e2m3): e3m2 rows exactly like e2m3 rows, e2m1
   code k at stream bits [4k, 4k+4), i.e. the low nibble of byte k/2 for even
   k and its high nibble for odd k (64-byte rows).
+* nvfp4, the harness's remaining format ("Beyond fp8: the harness"; the
+  runner passes the kernel a K and a V "nvfp4 scale pointer", typed
+  float8_e4m3fn, mjolnir/runner.py ``dummy_scales``).  The pages give
+  neither its block size nor where the scales live; the reading taken is the
+  published NVFP4 format: e2m1 codes in blocks of 16 consecutive values that
+  share one e4m3 scale, value = e2m1(code) * e4m3(scale), times a per-tensor
+  (here also per-head or per-(sequence, head)) fp32 scale.  A 128-channel row
+  is then 64 code bytes (the e2m1 row) plus 8 scale bytes, scale b covering
+  channels [16b, 16b + 16); the scale rows live in a pool of their own, paged
+  like the codes.
 """
 
 from __future__ import annotations
@@ -216,10 +226,21 @@ def unpack_4bit(rows: np.ndarray, n: int) -> np.ndarray:
     return out
 
 
-# bytes of one 128-value row and the (decode, encode, pack, unpack) of each
-# KV format
-ROW_BYTES = {"e4m3": 128, "e2m3": 96, "e3m2": 96, "e2m1": 64}
+# bytes of one 128-value row (codes only; nvfp4 rows also have SCALE_ROW_BYTES
+# of block scales in their own pool) and the largest code magnitude
+ROW_BYTES = {"e4m3": 128, "e2m3": 96, "e3m2": 96, "e2m1": 64, "nvfp4": 64}
 FMT_MAX = {"e4m3": E4M3_MAX, "e2m3": E2M3_MAX, "e3m2": E3M2_MAX, "e2m1": E2M1_MAX}
+NVFP4_BLOCK = 16
+SCALE_ROW_BYTES = {"nvfp4": 128 // NVFP4_BLOCK}
+
+
+def nvfp4_decode(code_rows: np.ndarray, scale_rows: np.ndarray, n: int = 128) -> np.ndarray:
+    """(..., n/2) e2m1 code bytes and (..., n/16) e4m3 scale bytes -> (..., n)
+    values: value c = e2m1(code c) * e4m3(scale c // 16)."""
+    vals = e2m1_decode(unpack_4bit(code_rows, n))
+    scales = e4m3_decode(np.asarray(scale_rows, dtype=np.uint8))
+    assert scales.shape[-1] * NVFP4_BLOCK == n
+    return vals * np.repeat(scales, NVFP4_BLOCK, axis=-1)
 
 
 def decode_row_codes(rows: np.ndarray, kv_format: str, n: int = 128) -> np.ndarray:

@@ -14,6 +14,11 @@ mjolnir/runner.py, ``T5DecodeRunner.run`` for the Q/K/V/scale shapes):
   scales ``amax_c / max`` (7.5, 28, 6) from a separate seeded calibration
   draw; 6-bit codes are packed four per three bytes and 4-bit codes two per
   byte, as little-endian bitstreams.
+* nvfp4 caches: a per-tensor or per-KV-head fp32 scale ``amax / (6 * 448)``
+  (as the e4m3 caches), then per 16-channel block of each row an e4m3 block
+  scale (torch's float8_e4m3fn cast of ``amax_block / 6``) and e2m1 codes of
+  the values over it; the 8 scale bytes of a row sit in a second pool paged
+  like the codes.
 * Physical pages are consecutive slices of one seeded permutation of the pool.
   Unused block-table entries and the unused tail slots of each sequence's last
   page hold a poison page (codes of value 448, or 7.5 for e2m3) so that any
@@ -56,8 +61,8 @@ class Spec:
     h_k: int
     page_size: int
     layout: str  # "HND" | "NHD"
-    kv_format: str  # "e4m3" | "e2m3" | "e3m2" | "e2m1"
-    scale_kind: str  # "tensor" | "head" | "seq_head" | "channel" (e2m3 only)
+    kv_format: str  # "e4m3" | "e2m3" | "e3m2" | "e2m1" | "nvfp4"
+    scale_kind: str  # "tensor" | "head" | "seq_head" | "channel" (fp6 / e2m1 only)
     lens: tuple = ()  # explicit context lengths (tokens, including the q_len new ones)
     lens_loguniform: tuple = ()  # (lo, hi): draw b lengths floor(exp(U(ln lo, ln hi)))
     k_outliers: int = 0  # outlier K channels per KV head (x20 before quantization)
@@ -79,8 +84,13 @@ class Spec:
 
     @property
     def row_bytes(self) -> int:
-        bits = {"e4m3": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}[self.kv_format]
+        bits = {"e4m3": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4, "nvfp4": 4}[self.kv_format]
         return self.d * bits // 8
+
+    @property
+    def scale_row_bytes(self) -> int:
+        """Block-scale bytes per row (nvfp4: one e4m3 per 16 channels)."""
+        return self.d // 16 if self.kv_format == "nvfp4" else 0
 
 
 # The five workloads (full size) and the 32k-context target point.
@@ -113,6 +123,13 @@ SPECS = {
     "cfg5_e2m1": Spec("b4_L131072_p128_hnd_e2m1", b=4, q_len=1, h_q=32, h_k=8, page_size=128, layout="HND",
                       kv_format="e2m1", scale_kind="channel", lens=(131072,) * 4, k_outliers=4, pool_pages=8192,
                       seed=1009),
+    # block-scaled fp4 at the long-context point and at the ragged token-major point
+    "cfg5_nvfp4": Spec("b4_L131072_p128_hnd_nvfp4", b=4, q_len=1, h_q=32, h_k=8, page_size=128, layout="HND",
+                       kv_format="nvfp4", scale_kind="head", lens=(131072,) * 4, k_outliers=4, pool_pages=8192,
+                       seed=1010),
+    "cfg3_nvfp4": Spec("b64_ragged1k-32k_p64_nhd_nvfp4", b=64, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
+                       kv_format="nvfp4", scale_kind="tensor", lens_loguniform=(1024, 32768), slots_override=256,
+                       seed=1011),
 }
 
 # Reduced sizes with the same heads, page size, layout, format and scales: the
@@ -129,6 +146,8 @@ SMALL = {
     "32k_b16": dict(b=2, lens=(4096, 3000), pool_pages=0),
     "cfg5_e3m2": dict(b=2, lens=(3001, 1290), pool_pages=0),
     "cfg5_e2m1": dict(b=2, lens=(3001, 1290), pool_pages=0),
+    "cfg5_nvfp4": dict(b=2, lens=(3001, 1290), pool_pages=0),
+    "cfg3_nvfp4": dict(b=6, lens=(), lens_loguniform=(100, 3000), slots_override=24),
 }
 
 
@@ -158,6 +177,8 @@ class Workload:
     o_mul: torch.Tensor | None
     k_channel_scale: torch.Tensor | None = None  # (h_k, d) for e2m3
     v_channel_scale: torch.Tensor | None = None
+    k_bs_pool: torch.Tensor | None = None  # nvfp4: uint8 block scales, laid out like k_pool with 8-byte rows
+    v_bs_pool: torch.Tensor | None = None
     softmax_scale: float = 1.0 / math.sqrt(HEAD_DIM)
     extra: dict = field(default_factory=dict)
 
@@ -173,10 +194,19 @@ class Workload:
             return (p.stride(0), p.stride(1), p.stride(2))
         return st(self.k_pool), st(self.v_pool)
 
+    def bs_strides(self):
+        """Byte strides (page, slot, head) of the K and V block-scale pools."""
+        def st(p):
+            if self.spec.layout == "HND":
+                return (p.stride(0), p.stride(2), p.stride(1))
+            return (p.stride(0), p.stride(1), p.stride(2))
+        return st(self.k_bs_pool), st(self.v_bs_pool)
+
     def kv_bytes(self) -> int:
-        """K and V bytes one decode step must read: sum_i L_i * h_k * 2 * row."""
+        """K and V bytes one decode step must read: sum_i L_i * h_k * 2 * row
+        (row = codes plus block scales)."""
         s = self.spec
-        return int(sum(self.seq_lens)) * s.h_k * 2 * s.row_bytes
+        return int(sum(self.seq_lens)) * s.h_k * 2 * (s.row_bytes + s.scale_row_bytes)
 
     def host(self, seqs=None) -> dict:
         """NumPy copies for the oracle.  ``seqs`` restricts the copy to the
@@ -186,8 +216,12 @@ class Workload:
         bt = self.block_table.cpu().numpy()
         lens = np.asarray(self.seq_lens, dtype=np.int64)
         seqs = list(range(s.b)) if seqs is None else list(seqs)
+        nv = self.k_bs_pool is not None
+        kbp = vbp = None
         if len(seqs) == s.b and self.num_pages * self.k_pool[0].numel() <= (1 << 30):
             kp, vp, bt_sub = self.k_pool.cpu().numpy(), self.v_pool.cpu().numpy(), bt
+            if nv:
+                kbp, vbp = self.k_bs_pool.cpu().numpy(), self.v_bs_pool.cpu().numpy()
             bt_sub = bt_sub[seqs]
         else:
             used = []
@@ -198,6 +232,9 @@ class Workload:
             idx = torch.tensor(uniq, dtype=torch.long, device=self.k_pool.device)
             kp = self.k_pool.index_select(0, idx).cpu().numpy()
             vp = self.v_pool.index_select(0, idx).cpu().numpy()
+            if nv:
+                kbp = self.k_bs_pool.index_select(0, idx).cpu().numpy()
+                vbp = self.v_bs_pool.index_select(0, idx).cpu().numpy()
             bt_sub = np.zeros((len(seqs), bt.shape[1]), dtype=np.int32)
             for r, i in enumerate(seqs):
                 n = max(1, -(-int(lens[i]) // s.page_size))
@@ -212,7 +249,13 @@ class Workload:
         vd = self.v_descale.cpu().numpy()
         if self.descale_kind == "seq_head":
             kd, vd = kd[seqs], vd[seqs]
+        extra = {}
+        if nv:
+            extra = dict(k_bs_pool=np.ascontiguousarray(kbp).reshape(-1), v_bs_pool=np.ascontiguousarray(vbp).reshape(-1),
+                         k_bs_strides=strides(np.ascontiguousarray(kbp)),
+                         v_bs_strides=strides(np.ascontiguousarray(vbp)))
         return dict(
+            **extra,
             q=np.ascontiguousarray(qd),
             k_pool=np.ascontiguousarray(kp).reshape(-1),
             v_pool=np.ascontiguousarray(vp).reshape(-1),
@@ -301,6 +344,17 @@ SUBBYTE = {
 }
 
 
+def nvfp4_encode_blocks(y: torch.Tensor):
+    """(..., d) fp32 -> ((..., d/2) e2m1 code bytes, (..., d/16) e4m3 block
+    scales): per 16 values, scale = e4m3(min(amax / 6, 448)) by torch's cast,
+    codes the nearest e2m1 of y / scale (zero codes under a zero scale)."""
+    blk = y.reshape(*y.shape[:-1], y.shape[-1] // 16, 16)
+    sc8 = (blk.abs().amax(dim=-1) / 6.0).clamp_max(E4M3_MAX).to(torch.float8_e4m3fn)  # the cast does not saturate
+    sv = sc8.to(torch.float32).unsqueeze(-1)
+    codes = e2m1_encode_table(torch.where(sv > 0, blk / torch.where(sv > 0, sv, 1.0), 0.0))
+    return pack_codes_4bit(codes.reshape(y.shape)), sc8.view(torch.uint8)
+
+
 def pack_codes_6bit(codes: torch.Tensor) -> torch.Tensor:
     """(..., n) 6-bit codes -> (..., 3n/4) bytes: code k occupies stream bits
     [6k, 6k+6), stream bit 8B+j being bit j of byte B (little-endian)."""
@@ -367,10 +421,22 @@ def build(spec: Spec, device="cpu") -> Workload:
     shape = (pool, h_k, P, row) if s.layout == "HND" else (pool, P, h_k, row)
     k_pool = torch.randint(0, 256, shape, generator=_gen(device, s.seed + 11), device=device, dtype=torch.uint8)
     v_pool = torch.randint(0, 256, shape, generator=_gen(device, s.seed + 12), device=device, dtype=torch.uint8)
+    k_bs = v_bs = None
+    srow = s.scale_row_bytes
     if s.kv_format == "e4m3":
         k_pool[poison] = POISON_E4M3
         v_pool[poison] = POISON_E4M3
         poison_row = torch.full((row,), POISON_E4M3, dtype=torch.uint8, device=device)
+    elif s.kv_format == "nvfp4":
+        # poison: codes of 6 under scales of 448
+        bshape = shape[:-1] + (srow,)
+        k_bs = torch.randint(0, 256, bshape, generator=_gen(device, s.seed + 13), device=device, dtype=torch.uint8)
+        v_bs = torch.randint(0, 256, bshape, generator=_gen(device, s.seed + 14), device=device, dtype=torch.uint8)
+        poison_row = torch.full((row,), POISON_E2M1 * 0x11, dtype=torch.uint8, device=device)
+        poison_srow = torch.full((srow,), POISON_E4M3, dtype=torch.uint8, device=device)
+        for pool_t, bs_t in ((k_pool, k_bs), (v_pool, v_bs)):
+            pool_t[poison] = poison_row
+            bs_t[poison] = poison_srow
     else:
         fmax, enc_fn, pack_fn, pcode = SUBBYTE[s.kv_format]
         poison_row = pack_fn(torch.full((d,), pcode, dtype=torch.uint8, device=device))
@@ -378,19 +444,21 @@ def build(spec: Spec, device="cpu") -> Workload:
         v_pool[poison] = poison_row
 
     q_mul = o_mul = kcs = vcs = None
-    if s.kv_format == "e4m3":
-        # pass 1: amax per (sequence, KV head)
+    if s.kv_format in ("e4m3", "nvfp4"):
+        # pass 1: amax per (sequence, KV head); nvfp4's second-level scale
+        # leaves room for e2m1's 6 times e4m3's 448
+        top = E4M3_MAX if s.kv_format == "e4m3" else E2M1_MAX * E4M3_MAX
         amax = torch.zeros(2, s.b, h_k, dtype=torch.float32, device=device)
         for i in range(s.b):
             for j, side in enumerate("kv"):
                 if lens[i] > 0:
                     amax[j, i] = draw(i, side).abs().amax(dim=(0, 2))
         if s.scale_kind == "tensor":
-            sc = amax.amax(dim=(1, 2)).reshape(2, 1) / E4M3_MAX
+            sc = amax.amax(dim=(1, 2)).reshape(2, 1) / top
         elif s.scale_kind == "head":
-            sc = amax.amax(dim=1) / E4M3_MAX
+            sc = amax.amax(dim=1) / top
         elif s.scale_kind == "seq_head":
-            sc = torch.where(amax > 0, amax, torch.ones_like(amax)) / E4M3_MAX
+            sc = torch.where(amax > 0, amax, torch.ones_like(amax)) / top
         else:
             raise ValueError(s.scale_kind)
         k_desc, v_desc = sc[0].contiguous(), sc[1].contiguous()
@@ -404,7 +472,9 @@ def build(spec: Spec, device="cpu") -> Workload:
                 y = x / scl.view(1, h_k, 1)
             else:
                 y = x / scl[i].view(1, h_k, 1)
-            return y.to(torch.float8_e4m3fn).view(torch.uint8)
+            if s.kv_format == "e4m3":
+                return y.to(torch.float8_e4m3fn).view(torch.uint8)
+            return nvfp4_encode_blocks(y)
     else:
         assert s.scale_kind == "channel"
         # calibration pass: a separate seeded draw, same outlier channels
@@ -429,12 +499,23 @@ def build(spec: Spec, device="cpu") -> Workload:
         idx = bt_t[i, :n].long()
         for side, pool_t in (("k", k_pool), ("v", v_pool)):
             codes = encode(i, side, draw(i, side))  # (L, h_k, row)
+            scales = None
+            if s.kv_format == "nvfp4":
+                codes, scales = codes
             padded = poison_row.view(1, 1, row).expand(n * P, h_k, row).clone()
             padded[: lens[i]] = codes
             paged = padded.view(n, P, h_k, row)
             if s.layout == "HND":
                 paged = paged.permute(0, 2, 1, 3)
             pool_t[idx] = paged.contiguous()
+            if scales is not None:
+                bs_t = k_bs if side == "k" else v_bs
+                padded = poison_srow.view(1, 1, srow).expand(n * P, h_k, srow).clone()
+                padded[: lens[i]] = scales
+                paged = padded.view(n, P, h_k, srow)
+                if s.layout == "HND":
+                    paged = paged.permute(0, 2, 1, 3)
+                bs_t[idx] = paged.contiguous()
 
     # Q: bf16 N(0,1); optionally a strided view into a wider per-token buffer
     tokens = s.b * s.q_len
@@ -458,4 +539,6 @@ def build(spec: Spec, device="cpu") -> Workload:
         o_mul=o_mul,
         k_channel_scale=kcs,
         v_channel_scale=vcs,
+        k_bs_pool=k_bs,
+        v_bs_pool=v_bs,
     )

@@ -33,7 +33,8 @@ def _args(wl):
     return dict(q_len=s.q_len, h_q=s.h_q, h_k=s.h_k, d=s.d, page_size=s.page_size, kv_format=s.kv_format)
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
+                                 "cfg3_nvfp4"])
 def test_matches_sdpa_per_head(key):
     wl, h = _small(key)
     s = wl.spec
@@ -57,7 +58,7 @@ def test_matches_sdpa_per_head(key):
                                  - lse)) < 1e-12
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n"])
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5_nvfp4"])
 def test_unquantized_q_matches_sdpa(key):
     """The bf16-Q reading (Q used as given, no quantization): each (sequence,
     KV head) equals torch SDPA in fp64 on Q rows gathered here by query head
@@ -113,7 +114,7 @@ def test_physical_page_permutation_is_exactly_invariant():
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg4c"])
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg3_nvfp4"])
 def test_split_merge_invariance(key):
     wl, h = _small(key)
     s = wl.spec

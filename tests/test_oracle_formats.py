@@ -204,3 +204,21 @@ def test_generator_small_encoders_agree_with_the_oracle():
         x = np.concatenate([pos, -pos, mids, -mids, rng.normal(0, pos[-1] / 3, 5000), [1e4, -1e4]])
         x = x.astype(np.float32)
         assert np.array_equal(enc_t(torch.from_numpy(x)).numpy(), enc_o(x))
+
+
+def test_generator_nvfp4_encoder_agrees_with_the_oracle_write():
+    """The generator's nvfp4 block encoder (torch's e4m3 cast, table e2m1
+    codes) gives the oracle write's codes and scales, incl. zero blocks,
+    saturating blocks and tiny blocks whose scale rounds to zero."""
+    from oracle.kvwrite import nvfp4_encode_row
+    from synth.workloads import nvfp4_encode_blocks
+    rng = np.random.default_rng(29)
+    rows = (rng.standard_normal((300, 128)) * 10.0 ** rng.uniform(-4, 3, (300, 1))).astype(np.float32)
+    rows[0, :16] = 0.0
+    rows[1, 16:32] = 1e-7
+    rows[2, :16] *= 1e4
+    codes_t, sc_t = nvfp4_encode_blocks(torch.from_numpy(rows))
+    for r in range(rows.shape[0]):
+        codes_o, sc_o = nvfp4_encode_row(rows[r])
+        assert np.array_equal(sc_t[r].numpy(), sc_o), r
+        assert np.array_equal(codes_t[r].numpy(), codes_o), r

@@ -1,7 +1,9 @@
 """Pins of the KV-cache write oracle (oracle/kvwrite.py) and its encoders:
 closed forms over every code, tie points and saturation, the hand-worked fp6
 packing examples, torch's e4m3 cast, a hand-worked write, and round trips
-through the decoders."""
+through the decoders, and the nvfp4 block-scaled write (a hand-worked row,
+exact round trips, torch's e4m3 decode of the scales, and brute-force
+nearest-value checks)."""
 
 import os
 
@@ -171,3 +173,105 @@ def test_write_hand_worked_e2m1_and_e3m2_rows():
     k, _ = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), ((16 * 96, 96, 16 * 96),) * 2,
                       16, "e3m2", x, x, np.array([0]), np.ones(1, np.float32), np.ones(1, np.float32), "tensor")
     assert k[:3].tolist() == [0xCC, 0x17, 0x02] and np.all(k[3:96] == 0)
+
+
+def _nvfp4_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_row_example.txt")
+    x = np.zeros(128, np.float32)
+    codes = np.zeros(128, np.uint8)
+    dec = {}
+    scales = None
+    for line in open(path):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "x":
+            x[int(f[1])] = np.float32(float(f[2]))
+        elif f[0] == "scales":
+            scales = np.array([int(v, 16) for v in f[1:]], np.uint8)
+        elif f[0] == "codes":
+            c0 = int(f[1])
+            codes[c0:c0 + 16] = [int(v, 16) for v in f[2:]]
+        elif f[0] == "dec":
+            dec[int(f[1])] = float(f[2])
+    return x, scales, codes, dec
+
+
+def test_nvfp4_hand_worked_row():
+    x, scales, codes, dec = _nvfp4_golden()
+    assert np.array_equal(torch.from_numpy(x).to(torch.bfloat16).float().numpy(), x)  # bf16-exact inputs
+    got_codes, got_scales = W.nvfp4_encode_row(x)
+    assert got_scales.tolist() == scales.tolist()
+    assert np.array_equal(F.unpack_4bit(got_codes, 128), codes)
+    vals = F.nvfp4_decode(got_codes, got_scales)
+    for c, v in dec.items():
+        assert vals[c] == v, c
+    # through the slot-mapped write: codes to the e2m1 row, scales to the scale row of the same slot
+    size, (st, _), _ = _pools("e2m1", "HND", 2, 16, 1)
+    bst = (16 * 8, 8, 16 * 8)
+    xx = x.reshape(1, 1, 128)
+    k, v, kb, vb = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), (st, st), 16, "nvfp4", xx, xx,
+                              np.array([19]), np.ones(1, np.float32), np.ones(1, np.float32), "tensor",
+                              bs_pools=(np.full(2 * 16 * 8, 0xEE, np.uint8), np.zeros(2 * 16 * 8, np.uint8)),
+                              bs_strides=(bst, bst))
+    b = 1 * st[0] + 3 * st[1]
+    assert np.array_equal(k[b:b + 64], got_codes) and np.array_equal(v, k)
+    assert kb[8 * 19:8 * 20].tolist() == scales.tolist()
+    assert np.all(np.delete(kb, np.arange(8 * 19, 8 * 20)) == 0xEE)
+
+
+def test_nvfp4_decode_matches_torch_scales():
+    """The block-scale half of the decode through torch's float8_e4m3fn."""
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, 256, (50, 64), dtype=np.uint8)
+    sc = rng.integers(0, 0x7F, (50, 8), dtype=np.uint8)  # finite non-negative scales
+    ts = torch.from_numpy(sc).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    lo, hi = rows & 0xF, rows >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(50, 128)
+    ref = F.E2M1_TABLE[codes] * np.repeat(ts, 16, axis=1)
+    assert np.array_equal(F.nvfp4_decode(rows, sc), ref)
+
+
+def test_nvfp4_exact_inputs_round_trip():
+    """Rows whose every block holds a +-6 code are written back to the same
+    codes and scales: amax / 6 is then the block scale exactly."""
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        codes = rng.integers(0, 16, 128).astype(np.uint8)
+        for b in range(8):
+            codes[16 * b + rng.integers(0, 16)] = rng.choice([0x7, 0xF])
+        scales = rng.integers(0x01, 0x7F, 8).astype(np.uint8)  # positive, finite, incl. subnormals
+        packed = F.pack_4bit(codes)
+        y = F.nvfp4_decode(packed, scales).astype(np.float32)
+        assert np.array_equal(y.astype(np.float64), F.nvfp4_decode(packed, scales))  # exact in fp32
+        got_codes, got_scales = W.nvfp4_encode_row(y)
+        assert got_scales.tolist() == scales.tolist()
+        assert np.array_equal(got_codes, packed)
+
+
+def test_nvfp4_scale_and_codes_are_nearest_by_brute_force():
+    """Random rows: every block scale is the e4m3 value nearest amax / 6 and
+    every code the e2m1 value nearest y / scale (saturating), checked by
+    search over every value of the two formats."""
+    rng = np.random.default_rng(23)
+    e4 = F.E4M3_TABLE[:0x7F]  # non-negative finite, code order
+    e2 = F.E2M1_TABLE[:8]
+    for _ in range(100):
+        y = (rng.standard_normal(128) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        packed, scales = W.nvfp4_encode_row(y)
+        codes = F.unpack_4bit(packed, 128)
+        for b in range(8):
+            blk = y[16 * b:16 * b + 16].astype(np.float64)
+            t = np.float64(np.float32(np.abs(blk).max() / 6.0))  # the one fp32 division
+            best = np.min(np.abs(e4 - min(t, 448.0)))
+            assert abs(F.E4M3_TABLE[scales[b]] - min(t, 448.0)) == best
+            s = F.E4M3_TABLE[scales[b]]
+            if s == 0:
+                assert np.all(codes[16 * b:16 * b + 16] == 0)
+                continue
+            for c in range(16):
+                r = np.float64(np.float32(blk[c] / s))
+                a = min(abs(r), 6.0)
+                val = F.E2M1_TABLE[codes[16 * b + c]]
+                assert abs(abs(val) - a) == np.min(np.abs(e2 - a))
+                assert (val < 0) == (r < 0) or val == 0
