@@ -245,13 +245,17 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
     # the same number of merge launches alone, one event pair over those
     kvb = wl.kv_bytes()
     n_copies = max(1, -(-(1 << 30) // kvb))
-    pools = [(wl.k_pool, wl.v_pool)] + [(wl.k_pool.clone(), wl.v_pool.clone()) for _ in range(n_copies - 1)]
+    # (nvfp4: the block-scale pools rotate with the codes)
+    srcs = (wl.k_pool, wl.v_pool, wl.k_bs_pool, wl.v_bs_pool)
+    pools = [srcs] + [tuple(None if t is None else t.clone() for t in srcs) for _ in range(n_copies - 1)]
     reps = max(8, 2 * n_copies, steps)
     ks, vs = wl.kv_strides()
+    bss = wl.bs_strides() if wl.k_bs_pool is not None else (None, None)
 
     def launch(i):
-        kp, vp = pools[i % len(pools)]
-        step.run(q=wl.q, k_cache=kp, v_cache=vp, k_strides=ks, v_strides=vs, num_pages=wl.num_pages,
+        kp, vp, kb, vb = pools[i % len(pools)]
+        step.run(k_block_scale=kb, v_block_scale=vb, k_bs_strides=bss[0], v_bs_strides=bss[1],
+                 q=wl.q, k_cache=kp, v_cache=vp, k_strides=ks, v_strides=vs, num_pages=wl.num_pages,
                  block_table=wl.block_table, seq_lens=wl.seq_lens_dev, k_descale=wl.k_descale,
                  v_descale=wl.v_descale, descale_kind=wl.descale_kind, softmax_scale=wl.softmax_scale, out=out,
                  lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul, causal=wl.spec.causal, info=info, stream=stream,

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 5
+#define MJ_ABI_VERSION 6
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -69,17 +69,24 @@ typedef enum mj_kv_format {
                       (project page, "Beyond fp8: the harness" names fp6
                       e3m2; the pages give no packing, the e2m3 bitstream is
                       taken)                                                    */
-  MJ_KV_E2M1 = 3   /* OCP MX e2m1 4-bit codes (bias 1, max 6), 64-byte rows:
+  MJ_KV_E2M1 = 3,  /* OCP MX e2m1 4-bit codes (bias 1, max 6), 64-byte rows:
                       code k is stream bits [4k, 4k+4), i.e. the low nibble of
                       byte k/2 for even k, the high nibble for odd k (same
                       section: fp4 e2m1; same bitstream reading)               */
+  MJ_KV_NVFP4 = 4  /* block-scaled fp4 (same section: "nvfp4"; the runner
+                      passes K and V "nvfp4 scale pointers"): e2m1 rows as
+                      MJ_KV_E2M1, plus one e4m3 scale per 16 channels, i.e.
+                      an 8-byte row per (token, KV head) in a block-scale
+                      pool paged like the codes; value = e2m1(code c) *
+                      e4m3(scale c/16) * the fp32 descale.  The pages give no
+                      layout: this is the published NVFP4 block format.     */
 } mj_kv_format;
 
 /* How the decode takes Q (runner.py, T5DecodeRunner.__init__ `q_mode`, and
  * the backend's MJOLNIR_ATTN_Q_DTYPE): quantized per (sequence, KV head) to
  * e4m3 by mj_quantize_q, or used as is in bf16 with the KV codes converted
- * to bf16 inside the decode kernel (e4m3 KV only: the packed sub-byte caches
- * take fp8 Q only, per the runner's kv_format comment). */
+ * to bf16 inside the decode kernel (e4m3 and nvfp4 KV: the packed fp6 / fp4
+ * caches take fp8 Q only, per the runner's kv_format comment). */
 typedef enum mj_q_mode {
   MJ_Q_FP8 = 0,   /* dynamic e4m3 Q: mj_quantize_q, then q8 / q_descale        */
   MJ_Q_BF16 = 1   /* bf16 Q as given: logit = softmax_scale * k_descale *
@@ -119,7 +126,7 @@ typedef struct mj_config {
  * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
  * workgroups per CU; four waves of items of >= 2048 tokens balance the tail
  * across CUs and XCDs); 16 < n_q <= 32, or fp6 (e2m3 / e3m2) -> 1 / 1 (one
- * wave); e2m1, or n_q > 32 -> 2 / 1.  min_chunk_tokens is rounded up to whole KV tiles. */
+ * wave); e2m1 / nvfp4, or n_q > 32 -> 2 / 1.  min_chunk_tokens is rounded up to whole KV tiles. */
 
 /* What a plan decided (runner.py, StepPlan). */
 typedef struct mj_plan_info {
@@ -183,6 +190,16 @@ typedef struct mj_decode_args {
      token = i*q_len + t; 16-byte aligned, strides multiples of 8 elements  */
   const void* q_bf16;
   int64_t q_tok_stride, q_head_stride;
+  /* MJ_KV_NVFP4 only (not read otherwise): the 8-byte block-scale row of
+     token j, KV head g starts at byte page*page_stride + (j %
+     page_size)*slot_stride + g*head_stride of the block-scale pool, page
+     from the same block table (each block-scale pool holds num_pages pages
+     too); bases 8-byte aligned, strides multiples of 8 bytes (EALIGN),
+     non-null (EINVAL)                                                         */
+  const void* k_block_scale;
+  int64_t k_bs_page_stride, k_bs_slot_stride, k_bs_head_stride;
+  const void* v_block_scale;
+  int64_t v_bs_page_stride, v_bs_slot_stride, v_bs_head_stride;
 } mj_decode_args;
 
 typedef struct mj_merge_args {
@@ -322,6 +339,11 @@ typedef struct mj_write_args {
   int32_t k_scale_kind;         /* TENSOR, HEAD or CHANNEL                   */
   const float* v_scale;
   int32_t v_scale_kind;
+  /* MJ_KV_NVFP4 only: the block-scale pools, as in mj_decode_args */
+  void* k_block_scale;
+  int64_t k_bs_page_stride, k_bs_slot_stride, k_bs_head_stride;
+  void* v_block_scale;
+  int64_t v_bs_page_stride, v_bs_slot_stride, v_bs_head_stride;
 } mj_write_args;
 
 /* The KV-cache write of a step's new rows (wheel listing
@@ -331,7 +353,11 @@ typedef struct mj_write_args {
  * RNE(x / scale) in the config's KV format, saturated at its largest
  * magnitude (448 e4m3, 7.5 e2m3, 28 e3m2, 6 e2m1), x the fp32 value of the
  * bf16 input and the division correctly rounded; sub-byte rows are packed
- * as mj_paged_decode reads them.  Tokens are
+ * as mj_paged_decode reads them.  nvfp4 (the published NVFP4 recipe; the
+ * pages print no writer): with y = x / scale as above, each 16-channel
+ * block's e4m3 scale is RNE(amax|y| / 6) saturated at 448, each code
+ * RNE_e2m1(y / e4m3(block scale)) (both divisions correctly rounded), and a
+ * block whose scale is 0 stores zero codes.  Tokens are
  * independent; two tokens mapped to one slot race (the caller's contract,
  * as in any slot-mapped write).  num_tokens == 0 enqueues nothing.
  * Errors: EINVAL (nulls, negative strides or counts, scale kind), EALIGN
@@ -385,9 +411,10 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStre
 
 /* Test probes (not part of a decode step).
  * mj_debug_gather_kv copies the codes of tokens 0..seq_len-1 of one
- * (sequence, KV head) from the K (which = 0) or V (which = 1) pool into
- * dense_out (seq_len x row bytes), using the decode kernel's own address
- * computation.  mj_debug_decode_codes decodes n codes (one per byte; 6-
+ * (sequence, KV head) from the K (which = 0) or V (which = 1) pool, or for
+ * nvfp4 the block scales from the K (which = 2) or V (which = 3) block-scale
+ * pool, into dense_out (seq_len x row bytes), using the decode kernel's own
+ * address computation.  mj_debug_decode_codes decodes n codes (one per byte; 6-
  * and 4-bit codes in the low bits) with the kernel's own decoder of format
  * kv_format (an mj_kv_format) into fp32; kv_format 16 decodes e4m3 codes
  * through the bf16 operand converter of the MJ_Q_BF16 decode (fp32 of the
@@ -400,9 +427,10 @@ mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t
  * kernel wherever q_len*h_r <= 32, whole 16-token tiles and slot strides
  * < 2^24 bytes; otherwise the generic LDS-tiled kernel), 1 = always the
  * generic kernel, 2 = the VALU-PV streaming kernel for e4m3 with
- * q_len*h_r <= 4 (automatic otherwise), 3 = same as 0, 10..13 = the
+ * q_len*h_r <= 4 (automatic otherwise), 3 = same as 0, 10..17 = the
  * matrix-core kernel with tuning bits (variant - 10): bit 0 two granules of
- * prefetch (4-row kernel), bit 1 head-major grid.  nontemporal selects the
+ * prefetch, bit 1 head-major grid, bit 2 XCD-grouped grid (the KV heads of a
+ * work item on one XCD; takes precedence over bit 1).  nontemporal selects the
  * streaming kernels' KV load cache policy: 1 (default) the library's choice
  * per format, 0 every load cached, 2 every load non-temporal, 3 K cached and
  * V non-temporal, 4 K non-temporal and V cached (the VALU-PV kernel: any

@@ -67,11 +67,11 @@ def default_shape(kv_format: str, n_q: int) -> tuple[int, int]:
     them 0: the e4m3 matrix-core kernel for up to 16 rows runs two
     workgroups per CU and is planned four waves deep with items of at least
     2048 tokens; the 32-row kernel (one workgroup per CU) and the e2m3
-    kernel are planned one wave deep; the e2m1 kernel (half-size rows) and
-    wider groups (the generic kernel) two per CU."""
+    kernel are planned one wave deep; the e2m1 and nvfp4 kernels (half-size
+    rows) and wider groups (the generic kernel) two per CU."""
     if kv_format == "e4m3" and n_q <= 16:
         return 8, 2048
-    if n_q <= 32 and kv_format != "e2m1":
+    if n_q <= 32 and kv_format not in ("e2m1", "nvfp4"):
         return 1, 1
     return 2, 1
 

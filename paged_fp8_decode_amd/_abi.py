@@ -8,9 +8,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 5  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 6  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
-KV_FORMATS = {"e4m3": 0, "e2m3": 1, "e3m2": 2, "e2m1": 3}
+KV_FORMATS = {"e4m3": 0, "e2m3": 1, "e3m2": 2, "e2m1": 3, "nvfp4": 4}
 Q_MODES = {"fp8": 0, "bf16": 1}
 SCALE_KINDS = {"tensor": 0, "head": 1, "seq_head": 2, "channel": 3}
 
@@ -51,6 +51,8 @@ class DecodeArgs(ctypes.Structure):
         ("softmax_scale", ctypes.c_float), ("o_mul", _p),
         ("out", _p), ("out_tok_stride", _i64), ("out_head_stride", _i64), ("lse", _p),
         ("q_bf16", _p), ("q_tok_stride", _i64), ("q_head_stride", _i64),
+        ("k_block_scale", _p), ("k_bs_page_stride", _i64), ("k_bs_slot_stride", _i64), ("k_bs_head_stride", _i64),
+        ("v_block_scale", _p), ("v_bs_page_stride", _i64), ("v_bs_slot_stride", _i64), ("v_bs_head_stride", _i64),
     ]
 
 
@@ -69,6 +71,8 @@ class WriteArgs(ctypes.Structure):
         ("k_cache", _p), ("k_page_stride", _i64), ("k_slot_stride", _i64), ("k_head_stride", _i64),
         ("v_cache", _p), ("v_page_stride", _i64), ("v_slot_stride", _i64), ("v_head_stride", _i64),
         ("num_pages", _i64), ("k_scale", _p), ("k_scale_kind", _i32), ("v_scale", _p), ("v_scale_kind", _i32),
+        ("k_block_scale", _p), ("k_bs_page_stride", _i64), ("k_bs_slot_stride", _i64), ("k_bs_head_stride", _i64),
+        ("v_block_scale", _p), ("v_bs_page_stride", _i64), ("v_bs_slot_stride", _i64), ("v_bs_head_stride", _i64),
     ]
 
 

@@ -30,7 +30,7 @@ __device__ __forceinline__ void load_row16(const uint8_t* row, int chunk, float 
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 16; ++e) out[e] = e4m3_raw((w[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-  } else if constexpr (FMT == 3) {  // e2m1: 8 bytes at chunk*8, code e in nibble e
+  } else if constexpr (FMT >= 3) {  // e2m1 (nvfp4 codes): 8 bytes at chunk*8, code e in nibble e
     const uint2 raw = *reinterpret_cast<const uint2*>(row + chunk * 8);
 #pragma unroll
     for (int e = 0; e < 16; ++e) out[e] = e2m1_raw(((e < 8 ? raw.x : raw.y) >> (4 * (e & 7))) & 0xFu);
@@ -44,9 +44,10 @@ __device__ __forceinline__ void load_row16(const uint8_t* row, int chunk, float 
 }
 
 // Power of two that turns a format's raw decode into its value.
+// (nvfp4: applied per 16-channel chunk together with the block scale)
 template <int FMT>
 constexpr float fmt_rescale() {
-  return FMT == 0 ? kE4m3Rescale : FMT == 1 ? kE2m3Rescale : FMT == 2 ? kE3m2Rescale : kE2m1Rescale;
+  return FMT == 0 ? kE4m3Rescale : FMT == 1 ? kE2m3Rescale : FMT == 2 ? kE3m2Rescale : FMT == 3 ? kE2m1Rescale : 1.0f;
 }
 
 template <int FMT>
@@ -117,6 +118,15 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
         const int slot = j & (p.page_size - 1);
         load_row16<FMT>(p.k + kv_offset(pg, slot, g, p.k_sp, p.k_ss, p.k_sh), ch, kv);
         load_row16<FMT>(p.v + kv_offset(pg, slot, g, p.v_sp, p.v_ss, p.v_sh), ch, vv);
+        if constexpr (FMT == 4) {  // nvfp4: chunk ch is block ch; e2m1 value times its e4m3 scale (exact)
+          const float ksf = e4m3_value(p.ksb[kv_offset(pg, slot, g, p.ksb_sp, p.ksb_ss, p.ksb_sh) + ch]);
+          const float vsf = e4m3_value(p.vsb[kv_offset(pg, slot, g, p.vsb_sp, p.vsb_ss, p.vsb_sh) + ch]);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            kv[e] = kv[e] * kE2m1Rescale * ksf;
+            vv[e] = vv[e] * kE2m1Rescale * vsf;
+          }
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) kv[e] = vv[e] = 0.0f;
@@ -238,7 +248,8 @@ hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_t
     case 0: hipLaunchKernelGGL(decode_generic_kernel<0>, grid, dim3(kThreads), 0, s, p); break;
     case 1: hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(kThreads), 0, s, p); break;
     case 2: hipLaunchKernelGGL(decode_generic_kernel<2>, grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(decode_generic_kernel<3>, grid, dim3(kThreads), 0, s, p); break;
+    case 3: hipLaunchKernelGGL(decode_generic_kernel<3>, grid, dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL(decode_generic_kernel<4>, grid, dim3(kThreads), 0, s, p); break;
   }
   return hipGetLastError();
 }

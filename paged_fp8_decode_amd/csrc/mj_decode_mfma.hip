@@ -16,7 +16,9 @@
 // tile, the lane's codes [32jj + 8i, 32jj + 8i + 8) forming the contraction
 // slice of MFMA i; Q's B operands are the same channels of the bf16 rows,
 // loaded as they are.  Products of bf16 values are exact in fp32, so only
-// the accumulation rounds.
+// the accumulation rounds.  nvfp4 KV (FMT 5 with fp8 Q, FMT 6 with bf16 Q)
+// takes the same route: its fp4 codes times their e4m3 block scales are
+// bf16 values, and fp8 Q codes become bf16 B operands.
 //
 // Method: mjolnir-kernel README "What it does", step 3 (stream KV pages,
 // online softmax) and the partials step 4 merges.  The pages' Thor design
@@ -56,6 +58,8 @@
 // before each use only covers the granule being computed.  KV bytes are
 // read once, non-temporally.  The softmax max per row is raised lazily (only
 // when a granule exceeds it by more than 8 in log2 units), which is exact.
+#include <type_traits>
+
 #include "mj_device.h"
 #include "mj_internal.h"
 #include "mj_merge.h"
@@ -72,10 +76,14 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
+// XCDs of the part: consecutive workgroups of a launch go to them in turn
+constexpr int kXcds = 8;
 // s_waitcnt immediate (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]) that waits for vmcnt 0 only
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -96,6 +104,11 @@ struct Fmt<0> {                     // e4m3: 128-byte rows
   static constexpr uint32_t kRow = 128;  // bytes per 128-channel row
   static constexpr int kVDw = 2;    // V dwords per token per lane (channels 8n..8n+7)
   static constexpr bool kPacked6 = false;
+  static constexpr bool kQkBf16 = false;     // QK^T on bf16 MFMAs (K converted in registers)
+  static constexpr bool kQBf16 = false;      // Q given in bf16 (no Q quantization)
+  static constexpr bool kBlockScaled = false;  // nvfp4: an e4m3 scale per 16 channels
+  static constexpr bool kQkF16 = false;      // QK^T on fp16 MFMAs
+  static constexpr bool kPvF16 = false;      // PV on fp16 MFMAs (P and V in fp16)
 };
 template <>
 struct Fmt<1> {                     // e2m3: 96-byte rows, 4 codes per 3 bytes
@@ -105,9 +118,17 @@ struct Fmt<1> {                     // e2m3: 96-byte rows, 4 codes per 3 bytes
   static constexpr uint32_t kRow = 96;
   static constexpr int kVDw = 2;    // the 4-aligned 8 bytes holding the lane's 48 bits
   static constexpr bool kPacked6 = true;
+  static constexpr bool kQkBf16 = false;
+  static constexpr bool kQBf16 = false;
+  static constexpr bool kBlockScaled = false;
+  static constexpr bool kQkF16 = false;
+  static constexpr bool kPvF16 = false;
 };
 template <>
-struct Fmt<2> : Fmt<0> {};          // e4m3 KV with bf16 Q (bf16 MFMAs for QK^T)
+struct Fmt<2> : Fmt<0> {            // e4m3 KV with bf16 Q (bf16 MFMAs for QK^T)
+  static constexpr bool kQkBf16 = true;
+  static constexpr bool kQBf16 = true;
+};
 template <>
 struct Fmt<3> : Fmt<1> {            // e3m2: packed like e2m3
   static constexpr int kMfmaFmt = 3;  // bf6 e3m2, same operand layout as fp6
@@ -120,6 +141,35 @@ struct Fmt<4> {                     // e2m1: 64-byte rows, 2 codes per byte
   static constexpr uint32_t kRow = 64;
   static constexpr int kVDw = 1;
   static constexpr bool kPacked6 = false;
+  static constexpr bool kQkBf16 = false;
+  static constexpr bool kQBf16 = false;
+  static constexpr bool kBlockScaled = false;
+  static constexpr bool kQkF16 = false;
+  static constexpr bool kPvF16 = false;
+};
+// nvfp4: e2m1 rows as Fmt<4> plus an 8-byte row of e4m3 block scales.  The
+// matrix cores' block scales are powers of two per 32 values, so they cannot
+// carry e4m3 scales per 16: K and V are scaled in registers.  An e2m1 value
+// times an e4m3 scale has at most 6 significant bits and lies in [2^-10,
+// 2688], so it is exact in fp16 (and bf16).  The converters apply the power
+// of two of their fp32 scale operand only (measured on gfx950), so a block
+// scale s = 2^E * M is applied as the converter's 2^E and one packed fp16
+// multiply by M (3 fraction bits at most).  Fmt<5> (fp8 Q): QK^T on fp16
+// MFMAs with the Q codes converted to fp16 (exact); Fmt<6> (bf16 Q): QK^T on
+// bf16 MFMAs with K scaled in fp32.  PV runs on fp16 MFMAs in both, P
+// rounded to fp16.
+template <>
+struct Fmt<5> : Fmt<4> {
+  static constexpr int kMfmaFmt = 0;  // Q operands in the fp8 channel order
+  static constexpr bool kBlockScaled = true;
+  static constexpr bool kQkF16 = true;
+  static constexpr bool kPvF16 = true;
+};
+template <>
+struct Fmt<6> : Fmt<5> {
+  static constexpr bool kQBf16 = true;
+  static constexpr bool kQkBf16 = true;
+  static constexpr bool kQkF16 = false;
 };
 // Byte offsets in a Q row of the two 16-byte halves of lane group jj's fp8
 // B operand.  Against fp8 K the lane group's 32 bytes pair with the K codes
@@ -137,10 +187,12 @@ __device__ __forceinline__ int q_half_offset(int jj, int h) {
 template <int FMT>
 struct KRows {  // tile k: this lane's codes [32jj, 32jj+32) of token n
   uint32_t d[2][Fmt<FMT>::kKDw];
+  uint32_t s[Fmt<FMT>::kBlockScaled ? 2 : 1];  // nvfp4: scales of blocks 2jj, 2jj + 1 (low 16 bits)
 };
 template <int FMT>
 struct VRows {  // element e: the bytes holding channels 8n..8n+7 of token tau(jj, e)
   uint32_t d[8][Fmt<FMT>::kVDw];
+  uint32_t s[Fmt<FMT>::kBlockScaled ? 8 : 1];  // nvfp4: scale of block n / 2 (low byte)
 };
 
 __device__ __forceinline__ float lane_f(float x, int l) {
@@ -194,6 +246,13 @@ struct Ctx {
   int v_shift;           // e2m3: bit offset of channel 8n in the loaded 8 bytes
   float cscale;
   float pos_inf;         // +inf (kernel argument; see fmax2)
+  // nvfp4 block-scale pools, addressed like the codes (8-byte rows)
+  const uint8_t* ksbpool;
+  const uint8_t* vsbpool;
+  int64_t ksb_sp, vsb_sp;
+  uint32_t ksb_ss, vsb_ss, ksb_rec, vsb_rec;
+  uint32_t ksb_lane;     // n * ksb_ss + 2jj: the scales of blocks 2jj, 2jj + 1 of token n
+  uint32_t vsb_lane;     // 4jj * vsb_ss + n / 2: the scale of channel 8n's block
 };
 
 // Page of the tile starting at token tk (wave-uniform), or -1 if the tile is
@@ -225,7 +284,12 @@ __device__ __forceinline__ KRows<FMT> load_k(const Ctx& c, int gi) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int tk = t0 + 16 * k;
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.kpool, c.k_sp, c.k_ss, c.k_rec, tile_page(c, tk), tk, c.pmask);
+    const int pg = tile_page(c, tk);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.kpool, c.k_sp, c.k_ss, c.k_rec, pg, tk, c.pmask);
+    if constexpr (Fmt<FMT>::kBlockScaled) {
+      const __amdgpu_buffer_rsrc_t srs = tile_rsrc(c.ksbpool, c.ksb_sp, c.ksb_ss, c.ksb_rec, pg, tk, c.pmask);
+      R.s[k] = __builtin_amdgcn_raw_buffer_load_b16(srs, c.ksb_lane, 0, aux);
+    }
     if constexpr (Fmt<FMT>::kKDw == 8) {
       const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 0, aux);
       const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 16, aux);
@@ -257,7 +321,14 @@ __device__ __forceinline__ VRows<FMT> load_v(const Ctx& c, int gi) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int tk = t0 + 16 * t;
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.vpool, c.v_sp, c.v_ss, c.v_rec, tile_page(c, tk), tk, c.pmask);
+    const int pg = tile_page(c, tk);
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.vpool, c.v_sp, c.v_ss, c.v_rec, pg, tk, c.pmask);
+    if constexpr (Fmt<FMT>::kBlockScaled) {
+      const __amdgpu_buffer_rsrc_t srs = tile_rsrc(c.vsbpool, c.vsb_sp, c.vsb_ss, c.vsb_rec, pg, tk, c.pmask);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        R.s[4 * t + v] = __builtin_amdgcn_raw_buffer_load_b8(srs, c.vsb_lane, v * c.vsb_ss, NT ? 2 : 0);
+    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       if constexpr (Fmt<FMT>::kVDw == 1) {
@@ -320,29 +391,90 @@ __device__ __forceinline__ void v_operands(const Ctx& c, const VRows<FMT>& V, ui
 
 // B operands of QK^T per 16-row block: fp8 codes (one MFMA per tile), or
 // bf16 Q channels [32jj + 8i, 32jj + 8i + 8) for MFMA i (bf16-Q mode).
-template <int FMT, int NRB>
+template <int FMT, int NRB, int kKind = Fmt<FMT>::kQkF16 ? 2 : (Fmt<FMT>::kQkBf16 ? 1 : 0)>
 struct QOps {
   v8i b[NRB];
 };
-template <int NRB>
-struct QOps<2, NRB> {
+template <int FMT, int NRB>
+struct QOps<FMT, NRB, 1> {
   v8bf b[NRB][4];
 };
+template <int FMT, int NRB>
+struct QOps<FMT, NRB, 2> {
+  v8h b[NRB][4];
+};
+
+// the e2m1 values of byte B of w as fp16, times the power of two of s
+template <int B>
+__device__ __forceinline__ v2h fp4_f16(uint32_t w, float s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, B);
+}
+// fp16 bits of M for an fp32 s = 2^E * M, M in [1, 2) (0 -> 1: the
+// converter then yields 0 anyway); exact when s has at most 10 fraction bits
+__device__ __forceinline__ uint32_t scale_mantissa_h(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return 0x3C00u | ((b >> 13) & 0x3FFu) | ((b >> 16) & 0x8000u);
+}
+
+// the two e2m1 values of byte B of w, as fp32 (low nibble first)
+template <int B>
+__device__ __forceinline__ v2f fp4_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+}
 
 // Unscaled Q.K dot products of tile k for every row block: lane (n, jj) gets
 // tokens 4jj + v of the tile against column n of the block.
 template <int FMT, int NRB>
 __device__ __forceinline__ void qk_tile(const KRows<FMT>& K, int k, const QOps<FMT, NRB>& q, v4f (&d)[NRB]) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (FMT == 2) {
-    v8bf ka[4];
+  if constexpr (Fmt<FMT>::kQkF16) {
+    // nvfp4 with fp8 Q: dword i holds codes [8i, 8i + 8) of the lane's 32, in
+    // block 2jj + i / 2; the converter applies the scale's power of two, one
+    // packed multiply its mantissa
+    const v2f sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(K.s[k], 1.0f, false);
+    const uint32_t h0 = scale_mantissa_h(sc[0]), h1 = scale_mantissa_h(sc[1]);
+    const v2h m0 = __builtin_bit_cast(v2h, h0 | (h0 << 16)), m1 = __builtin_bit_cast(v2h, h1 | (h1 << 16));
+    v8h ka[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t h[4];
-      e4m3x4_to_bf16(K.d[k][2 * i], h);
-      e4m3x4_to_bf16(K.d[k][2 * i + 1], h + 2);
-      const u32x4 w = {h[0], h[1], h[2], h[3]};
-      ka[i] = __builtin_bit_cast(v8bf, w);
+      const float bs = i < 2 ? sc[0] : sc[1];
+      const v2h mm = i < 2 ? m0 : m1;
+      const uint32_t w = K.d[k][i];
+      const v2h x0 = fp4_f16<0>(w, bs) * mm, x1 = fp4_f16<1>(w, bs) * mm;
+      const v2h x2 = fp4_f16<2>(w, bs) * mm, x3 = fp4_f16<3>(w, bs) * mm;
+      ka[i] = (v8h){x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+    }
+#pragma unroll
+    for (int R = 0; R < NRB; ++R) {
+      v4f acc = zero;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i], q.b[R][i], acc, 0, 0, 0);
+      d[R] = acc;
+    }
+  } else if constexpr (Fmt<FMT>::kQkBf16) {
+    v8bf ka[4];
+    if constexpr (Fmt<FMT>::kBlockScaled) {
+      // nvfp4: dword i holds codes [8i, 8i + 8) of the lane's 32, in block
+      // 2jj + i / 2; value times its block scale, exact in bf16
+      const v2f sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(K.s[k], 1.0f, false);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bs = i < 2 ? sc[0] : sc[1];
+        const uint32_t w = K.d[k][i];
+        const v2f x0 = fp4_pair<0>(w), x1 = fp4_pair<1>(w), x2 = fp4_pair<2>(w), x3 = fp4_pair<3>(w);
+        const u32x4 h = {pack_bf16(x0[0] * bs, x0[1] * bs), pack_bf16(x1[0] * bs, x1[1] * bs),
+                         pack_bf16(x2[0] * bs, x2[1] * bs), pack_bf16(x3[0] * bs, x3[1] * bs)};
+        ka[i] = __builtin_bit_cast(v8bf, h);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h[4];
+        e4m3x4_to_bf16(K.d[k][2 * i], h);
+        e4m3x4_to_bf16(K.d[k][2 * i + 1], h + 2);
+        const u32x4 w = {h[0], h[1], h[2], h[3]};
+        ka[i] = __builtin_bit_cast(v8bf, w);
+      }
     }
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
@@ -384,8 +516,8 @@ __device__ __forceinline__ void pv_pair(const VRows<FMT>& V, const v8bf (&pa)[NR
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     v2f x;
-    if constexpr (FMT == 4)
-      x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(V.d[e][0], 1.0f, PR);
+    if constexpr (Fmt<FMT>::kVDw == 1)
+      x = fp4_pair<PR>(V.d[e][0]);
     else
       x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][PR >> 1], 1.0f, (PR & 1) != 0);
     a[e] = x[0];
@@ -399,6 +531,30 @@ __device__ __forceinline__ void pv_pair(const VRows<FMT>& V, const v8bf (&pa)[NR
         __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], __builtin_bit_cast(v8bf, wa), st.acc[R][2 * PR], 0, 0, 0);
     st.acc[R][2 * PR + 1] =
         __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], __builtin_bit_cast(v8bf, wb), st.acc[R][2 * PR + 1], 0, 0, 0);
+  }
+}
+
+// nvfp4 PV for channels 2PR and 2PR + 1, on fp16 MFMAs: token e's two values
+// times the power of two of its block scale vsc[e] (converter), the token
+// pairs' words times their scales' mantissas mm (one packed multiply each)
+template <int FMT, int PR, int NQB, int NRB>
+__device__ __forceinline__ void pv_pair_h(const VRows<FMT>& V, const float (&vsc)[8], const v2h (&mm)[4],
+                                          const v8h (&pa)[NRB], State<NQB, NRB>& st) {
+  v2h x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = fp4_f16<PR>(V.d[e][0], vsc[e]);
+  v2h a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (v2h){x[2 * i][0], x[2 * i + 1][0]} * mm[i];
+    b[i] = (v2h){x[2 * i][1], x[2 * i + 1][1]} * mm[i];
+  }
+  const v8h wa = {a[0][0], a[0][1], a[1][0], a[1][1], a[2][0], a[2][1], a[3][0], a[3][1]};
+  const v8h wb = {b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
+#pragma unroll
+  for (int R = 0; R < NRB; ++R) {
+    st.acc[R][2 * PR] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[R], wa, st.acc[R][2 * PR], 0, 0, 0);
+    st.acc[R][2 * PR + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[R], wb, st.acc[R][2 * PR + 1], 0, 0, 0);
   }
 }
 
@@ -486,8 +642,9 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
       }
     }
   }
-  // ---- P (bf16 A operands) and the row sums
-  v8bf pa[NRB];
+  // ---- P (bf16 A operands; fp16 for nvfp4) and the row sums
+  using PA = typename std::conditional<Fmt<FMT>::kPvF16, v8h, v8bf>::type;
+  PA pa[NRB];
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     const float ms = st.m[R] == -INFINITY ? 0.0f : st.m[R];
@@ -501,11 +658,31 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
       }
     u32x4 pw;  // element e = 4k + v, token pairs per word
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pw[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
-    pa[R] = __builtin_bit_cast(v8bf, pw);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (Fmt<FMT>::kPvF16)
+        pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(((v2f){p[2 * i], p[2 * i + 1]}), v2h));
+      else
+        pw[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+    }
+    pa[R] = __builtin_bit_cast(PA, pw);
   }
   // ---- PV
-  if constexpr (!Fmt<FMT>::kPacked6) {
+  if constexpr (Fmt<FMT>::kPvF16) {
+    float vsc[8];
+    uint32_t hm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vsc[e] = __builtin_amdgcn_cvt_f32_fp8((int)V.s[e], 0);
+      hm[e] = scale_mantissa_h(vsc[e]);
+    }
+    v2h mm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mm[i] = __builtin_bit_cast(v2h, hm[2 * i] | (hm[2 * i + 1] << 16));
+    pv_pair_h<FMT, 0, NQB, NRB>(V, vsc, mm, pa, st);
+    pv_pair_h<FMT, 1, NQB, NRB>(V, vsc, mm, pa, st);
+    pv_pair_h<FMT, 2, NQB, NRB>(V, vsc, mm, pa, st);
+    pv_pair_h<FMT, 3, NQB, NRB>(V, vsc, mm, pa, st);
+  } else if constexpr (!Fmt<FMT>::kPacked6) {
     // e4m3 / e2m1 V, one channel pair at a time: converting a word's low or
     // high two bytes (e2m1: one byte) gives channels (2pr, 2pr + 1) of one
     // token, so the 8 tokens' words give both channels' B operands, used at
@@ -545,8 +722,19 @@ void decode_mfma_kernel(DecodeParams p) {
 
   // head-major grids put the KV heads of one work item in consecutive
   // workgroups, so they are resident together
-  const int w = p.head_major ? blockIdx.y : blockIdx.x;
-  const int g = p.head_major ? blockIdx.x : blockIdx.y;
+  int w, g;
+  if (p.head_major == 2) {
+    // XCD-grouped: workgroup L runs on XCD L % 8; the heads of item w are
+    // L = (w / 8) * 8 h_k + 8 g + w % 8, one XCD, dispatched close together
+    const int L = blockIdx.x, per = kXcds * p.h_k;
+    const int chunk = L / per, r = L - chunk * per;
+    g = r / kXcds;
+    w = chunk * kXcds + (r - g * kXcds);
+    if (w >= p.num_work) return;  // padding of the last chunk
+  } else {
+    w = p.head_major ? blockIdx.y : blockIdx.x;
+    g = p.head_major ? blockIdx.x : blockIdx.y;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, jj = lane >> 4;
@@ -602,6 +790,18 @@ void decode_mfma_kernel(DecodeParams p) {
   c.v_shift = F::kPacked6 ? 16 * (n & 1) : 0;
   c.num_pages = (uint32_t)min<int64_t>(p.num_pages, 0x7FFFFFFF);
   c.pos_inf = p.pos_inf;
+  if constexpr (F::kBlockScaled) {
+    c.ksbpool = p.ksb + (int64_t)g * p.ksb_sh;
+    c.vsbpool = p.vsb + (int64_t)g * p.vsb_sh;
+    c.ksb_sp = p.ksb_sp;
+    c.vsb_sp = p.vsb_sp;
+    c.ksb_ss = (uint32_t)p.ksb_ss;
+    c.vsb_ss = (uint32_t)p.vsb_ss;
+    c.ksb_rec = 15u * c.ksb_ss + 8u;
+    c.vsb_rec = 15u * c.vsb_ss + 8u;
+    c.ksb_lane = (uint32_t)n * c.ksb_ss + 2u * jj;
+    c.vsb_lane = 4u * jj * c.vsb_ss + ((uint32_t)n >> 1);
+  }
   c.page_shift = p.page_shift;
   c.pmask = p.page_size - 1;
 
@@ -617,7 +817,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // bf16-Q mode: this lane's channels [32jj, 32jj + 32) of Q row 16R + n % NQB
   // (clamped like the codes; zeroed below past n_q)
   u32x4 qh[NRB][4];
-  if constexpr (FMT == 2) {
+  if constexpr (F::kQBf16) {
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
       const int r = min(16 * R + (n % NQB), p.n_q - 1);
@@ -636,7 +836,7 @@ void decode_mfma_kernel(DecodeParams p) {
       qg[R][1] = *reinterpret_cast<const u32x4*>(row_q + q_half_offset<FMT>(jj, 1));
     }
   }
-  if (FMT != 2 && p.qb) {
+  if (!F::kQBf16 && p.qb) {
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
       const int v = min((int)threadIdx.x + k * kThreads, nvec - 1);  // a repeat changes no max
@@ -657,7 +857,7 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 
   float qdesc = 1.0f;  // bf16-Q mode: no Q scale
-  if (FMT != 2 && p.qb) {
+  if (!F::kQBf16 && p.qb) {
     // fused step: quantize this (sequence, KV head)'s Q rows here, with the
     // arithmetic of the stand-alone quantize kernel (every split item of the
     // pair derives the same codes and scale)
@@ -683,7 +883,7 @@ void decode_mfma_kernel(DecodeParams p) {
       if (v < nvec) *reinterpret_cast<uint2*>(&q_s[v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc);
     }
     __syncthreads();
-  } else if (FMT != 2) {
+  } else if (!F::kQBf16) {
     qdesc = p.q_descale[(int64_t)seq * p.h_k + g];
   }
   c.cscale = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
@@ -695,8 +895,8 @@ void decode_mfma_kernel(DecodeParams p) {
   for (int R = 0; R < NRB; ++R) {
     const int r = 16 * R + (n % NQB);
     row_tok[R] = r / p.h_r;
-    if constexpr (FMT == 2) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if constexpr (F::kQBf16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) qo.b[R][i] = __builtin_bit_cast(v8bf, r < p.n_q ? qh[R][i] : z);
     } else if (r < p.n_q) {
@@ -708,14 +908,48 @@ void decode_mfma_kernel(DecodeParams p) {
         a = qg[R][0];
         b = qg[R][1];
       }
+      if constexpr (F::kQkF16) {
+        // fp8 codes of channels [32jj, 32jj + 32) as the fp16 operands of
+        // the four MFMAs (exact)
+        const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qo.b[R][i] = (int)a[i];
-        qo.b[R][4 + i] = (int)b[i];
+        for (int i = 0; i < 4; ++i) {
+          const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i], 1.0f, false);
+          const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i], 1.0f, true);
+          const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i + 1], 1.0f, false);
+          const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[2 * i + 1], 1.0f, true);
+          qo.b[R][i] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+        }
+      } else if constexpr (F::kQkBf16) {
+        // fp8 codes of channels [32jj, 32jj + 32) as the bf16 operands of
+        // the four MFMAs (exact)
+        const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t h[4];
+          e4m3x4_to_bf16(w[2 * i], h);
+          e4m3x4_to_bf16(w[2 * i + 1], h + 2);
+          const u32x4 hv = {h[0], h[1], h[2], h[3]};
+          qo.b[R][i] = __builtin_bit_cast(v8bf, hv);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qo.b[R][i] = (int)a[i];
+          qo.b[R][4 + i] = (int)b[i];
+        }
       }
     } else {
+      if constexpr (F::kQkF16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qo.b[R][i] = 0;
+        for (int i = 0; i < 4; ++i) qo.b[R][i] = __builtin_bit_cast(v8h, z);
+      } else if constexpr (F::kQkBf16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qo.b[R][i] = __builtin_bit_cast(v8bf, z);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qo.b[R][i] = 0;
+      }
     }
   }
 
@@ -872,7 +1106,8 @@ void decode_mfma_kernel(DecodeParams p) {
 
 template <int FMT, int NQB, int NRB, int PF, int OCC>
 hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
-  const dim3 grid = p.head_major ? dim3(p.h_k, p.num_work) : dim3(p.num_work, p.h_k);
+  const dim3 grid = p.head_major == 2 ? dim3((unsigned)((p.num_work + kXcds - 1) / kXcds * kXcds * p.h_k))
+                    : p.head_major ? dim3(p.h_k, p.num_work) : dim3(p.num_work, p.h_k);
   switch (cp) {
     case 0: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 0, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
     case 1: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 1, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
@@ -901,18 +1136,20 @@ hipError_t launch_fmt(const DecodeParams& p, int nt, int tune, hipStream_t s) {
 
 bool decode_mfma_supports(int n_q) { return n_q >= 1 && n_q <= 32; }
 
-// tune bits: 1 = two granules of prefetch, 2 = head-major grid; -1 = the
-// default for the format.  cache_policy: -1 = the default for the format,
+// tune bits: 1 = two granules of prefetch, 2 = head-major grid, 4 = XCD-
+// grouped grid (over 2); -1 = the default for the format.  cache_policy: -1 = the default for the format,
 // else the CP bits.
 hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache_policy, int tune, hipStream_t s) {
   DecodeParams p = p_in;
-  // e2m1 rows are half the bytes of e4m3 ones: its items are planned two
-  // workgroups per CU, and the KV heads of one item are launched next to
-  // each other, so that the pages' head rows (adjacent in a head-major
-  // page) are read at the same time.  Measured at 131K context, 4
-  // sequences: 117 -> 97 us.
-  if (tune < 0) tune = kv_format == 3 ? 2 : 0;
-  p.head_major = (tune & 2) ? 1 : 0;
+  // e2m1 and nvfp4 rows are half the bytes of e4m3 ones: their items are
+  // planned two workgroups per CU, and the KV heads of one item run on one
+  // XCD close together (XCD-grouped grid), so that rows of neighbouring
+  // heads (one 128-byte line in a token-major page) are fetched once into
+  // that XCD's L2 and head-major pages are read together.  Measured: 131K
+  // context, 4 sequences, head-major pages 117 -> 100 us; ragged batch,
+  // token-major pages 199 -> 169 us.
+  if (tune < 0) tune = kv_format >= 3 ? 4 : 0;
+  p.head_major = (tune & 4) ? 2 : ((tune & 2) ? 1 : 0);
   const int t = (tune & 1) ? 2 : 0;
   // default: K cached, V non-temporal.  A K tile's row lines are touched by
   // two (e4m3) or three (e2m3) load instructions, which the vector L1 then
@@ -924,7 +1161,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
     case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, s) : launch_fmt<0>(p, cp, t, s);
     case 1: return launch_fmt<1>(p, cp, t, s);
     case 2: return launch_fmt<3>(p, cp, t, s);
-    default: return launch_fmt<4>(p, cp, t, s);
+    case 3: return launch_fmt<4>(p, cp, t, s);
+    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, s) : launch_fmt<5>(p, cp, t, s);
   }
 }
 

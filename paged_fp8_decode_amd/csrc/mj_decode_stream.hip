@@ -397,9 +397,9 @@ void decode_stream_kernel(DecodeParams p) {
 }  // namespace
 
 // Kernel choice: 0 = automatic, 1 = always the generic kernel, 2 = the
-// VALU-PV streaming kernel wherever it applies, 3 = same as 0, 10..13 = the
+// VALU-PV streaming kernel wherever it applies, 3 = same as 0, 10..17 = the
 // matrix-core kernel with tuning setting (variant - 10): bit 0 two granules
-// of prefetch (4-row groups), bit 1 head-major grid.
+// of prefetch, bit 1 head-major grid, bit 2 XCD-grouped grid.
 static int g_variant = 0;
 static int g_nontemporal = 1;
 
@@ -412,7 +412,7 @@ void set_decode_variant(int v, int nt) {
 static int kernel_choice(const DecodeParams& p, int kv_format, int row_tiles) {
   // the streaming kernels address a page's rows with 32-bit lane offsets and
   // take whole 16-token tiles inside one page
-  const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24);
+  const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24) && p.ksb_ss < (1 << 24) && p.vsb_ss < (1 << 24);
   const bool tiles_ok = row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
   if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q)) return 0;
   if (kv_format != 0 || g_variant != 2 || p.n_q > 4 || p.q_bf16) return 1;

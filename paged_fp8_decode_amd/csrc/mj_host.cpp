@@ -36,7 +36,7 @@ struct PlanShape {
 PlanShape plan_shape(const mj_config* c, const Derived& d, int q_len) {
   const int n_q = q_len * d.h_r;
   const bool small_e4m3 = c->kv_format == MJ_KV_E4M3 && n_q <= 16;
-  const bool fp4 = c->kv_format == MJ_KV_E2M1;
+  const bool fp4 = c->kv_format == MJ_KV_E2M1 || c->kv_format == MJ_KV_NVFP4;
   PlanShape ps;
   ps.wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : (small_e4m3 ? 8 : (n_q <= 32 && !fp4 ? 1 : 2));
   ps.min_chunk_tokens = c->min_chunk_tokens ? c->min_chunk_tokens : (small_e4m3 ? 2048 : 1);
@@ -49,8 +49,9 @@ int min_chunk_tiles(const mj_config* c, const Derived& d, int q_len) {
 
 // Bytes of one packed 128-channel K or V row of each format.
 int kv_row_bytes(int kv_format) {
-  return kv_format == MJ_KV_E4M3 ? 128 : (kv_format == MJ_KV_E2M1 ? 64 : 96);
+  return kv_format == MJ_KV_E4M3 ? 128 : (kv_format == MJ_KV_E2M1 || kv_format == MJ_KV_NVFP4 ? 64 : 96);
 }
+constexpr int kBlockScaleRowBytes = 8;  // nvfp4: one e4m3 per 16 channels
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -64,9 +65,10 @@ mj_status check_config(const mj_config* c) {
   if (c->h_q % c->h_k != 0) return MJ_EUNSUPPORTED;
   if (c->head_dim != 128) return MJ_EUNSUPPORTED;
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64 && c->page_size != 128) return MJ_EUNSUPPORTED;
-  if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_E2M1) return MJ_EUNSUPPORTED;
+  if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
-  if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3) return MJ_EUNSUPPORTED;  // packed formats take fp8 Q only
+  // the packed fp6 / fp4 formats take fp8 Q only
+  if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3 && c->kv_format != MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if ((int64_t)c->max_q_len * (c->h_q / c->h_k) > kMaxRows) return MJ_ECAPACITY;
   return MJ_OK;
 }
@@ -384,6 +386,16 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
       a->v_slot_stride % 16 || a->v_head_stride % 16 || a->out_tok_stride % 8 || a->out_head_stride % 8 ||
       (a->o_mul && !aligned(a->o_mul, 16)))
     return MJ_EALIGN;
+  const bool nv = cfg->kv_format == MJ_KV_NVFP4;
+  if (nv) {
+    if (!a->k_block_scale || !a->v_block_scale || a->k_bs_page_stride < 0 || a->k_bs_slot_stride < 0 ||
+        a->k_bs_head_stride < 0 || a->v_bs_page_stride < 0 || a->v_bs_slot_stride < 0 || a->v_bs_head_stride < 0)
+      return MJ_EINVAL;
+    if (!aligned(a->k_block_scale, 8) || !aligned(a->v_block_scale, 8) || a->k_bs_page_stride % 8 ||
+        a->k_bs_slot_stride % 8 || a->k_bs_head_stride % 8 || a->v_bs_page_stride % 8 || a->v_bs_slot_stride % 8 ||
+        a->v_bs_head_stride % 8)
+      return MJ_EALIGN;
+  }
   if (a->num_work != cap_for(cfg, d, a->q_len)) return MJ_EINVAL;
   const bool split = cfg->max_splits > 1 && a->num_seqs < slots_for(cfg, d, a->q_len);
   if ((a->with_reduction != 0) != split) return MJ_EINVAL;
@@ -448,6 +460,14 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->plan_in_kernel = 0;
   p->plan_margin = p->plan_max_splits = p->plan_slots = p->plan_split = p->plan_min_chunk = 0;
   p->ns_out = p->sb_out = nullptr;
+  p->ksb = nv ? static_cast<const uint8_t*>(a->k_block_scale) : nullptr;
+  p->vsb = nv ? static_cast<const uint8_t*>(a->v_block_scale) : nullptr;
+  p->ksb_sp = nv ? a->k_bs_page_stride : 0;
+  p->ksb_ss = nv ? a->k_bs_slot_stride : 0;
+  p->ksb_sh = nv ? a->k_bs_head_stride : 0;
+  p->vsb_sp = nv ? a->v_bs_page_stride : 0;
+  p->vsb_ss = nv ? a->v_bs_slot_stride : 0;
+  p->vsb_sh = nv ? a->v_bs_head_stride : 0;
   return MJ_OK;
 }
 
@@ -610,6 +630,16 @@ mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* a, hipStream_t 
       a->v_slot_stride % 16 || a->v_head_stride % 16 || !aligned(a->slot_mapping, 8) || !aligned(a->k_scale, 4) ||
       !aligned(a->v_scale, 4))
     return MJ_EALIGN;
+  const bool nv = cfg->kv_format == MJ_KV_NVFP4;
+  if (nv) {
+    if (!a->k_block_scale || !a->v_block_scale || a->k_bs_page_stride < 0 || a->k_bs_slot_stride < 0 ||
+        a->k_bs_head_stride < 0 || a->v_bs_page_stride < 0 || a->v_bs_slot_stride < 0 || a->v_bs_head_stride < 0)
+      return MJ_EINVAL;
+    if (!aligned(a->k_block_scale, 8) || !aligned(a->v_block_scale, 8) || a->k_bs_page_stride % 8 ||
+        a->k_bs_slot_stride % 8 || a->k_bs_head_stride % 8 || a->v_bs_page_stride % 8 || a->v_bs_slot_stride % 8 ||
+        a->v_bs_head_stride % 8)
+      return MJ_EALIGN;
+  }
   mj::WriteParams p;
   p.key = static_cast<const uint16_t*>(a->key);
   p.value = static_cast<const uint16_t*>(a->value);
@@ -635,6 +665,14 @@ mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* a, hipStream_t 
   p.h_k = cfg->h_k;
   p.page_shift = ilog2(cfg->page_size);
   p.kv_format = cfg->kv_format;
+  p.kbs = nv ? static_cast<uint8_t*>(a->k_block_scale) : nullptr;
+  p.vbs = nv ? static_cast<uint8_t*>(a->v_block_scale) : nullptr;
+  p.kbs_sp = nv ? a->k_bs_page_stride : 0;
+  p.kbs_ss = nv ? a->k_bs_slot_stride : 0;
+  p.kbs_sh = nv ? a->k_bs_head_stride : 0;
+  p.vbs_sp = nv ? a->v_bs_page_stride : 0;
+  p.vbs_ss = nv ? a->v_bs_slot_stride : 0;
+  p.vbs_sh = nv ? a->v_bs_head_stride : 0;
   return mj::launch_write_kv(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
@@ -642,29 +680,35 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream) {
   mj_status st = check_config(cfg);
   if (st != MJ_OK) return st;
-  if (!a || !dense_out || !a->block_table || (which != 0 && which != 1)) return MJ_EINVAL;
+  const bool scales = which == 2 || which == 3;
+  if (!a || !dense_out || !a->block_table || which < 0 || which > 3) return MJ_EINVAL;
+  if (scales && cfg->kv_format != MJ_KV_NVFP4) return MJ_EINVAL;
   if (seq < 0 || head < 0 || head >= cfg->h_k || seq_len < 0 || a->num_pages < 1) return MJ_EINVAL;
   if ((int64_t)seq_len > (int64_t)a->max_blocks_per_seq * cfg->page_size) return MJ_ECAPACITY;
   mj::GatherParams p;
-  p.pool = static_cast<const uint8_t*>(which == 0 ? a->k_cache : a->v_cache);
+  const void* pools[4] = {a->k_cache, a->v_cache, a->k_block_scale, a->v_block_scale};
+  const int64_t sps[4] = {a->k_page_stride, a->v_page_stride, a->k_bs_page_stride, a->v_bs_page_stride};
+  const int64_t sss[4] = {a->k_slot_stride, a->v_slot_stride, a->k_bs_slot_stride, a->v_bs_slot_stride};
+  const int64_t shs[4] = {a->k_head_stride, a->v_head_stride, a->k_bs_head_stride, a->v_bs_head_stride};
+  p.pool = static_cast<const uint8_t*>(pools[which]);
   if (!p.pool) return MJ_EINVAL;
-  p.sp = which == 0 ? a->k_page_stride : a->v_page_stride;
-  p.ss = which == 0 ? a->k_slot_stride : a->v_slot_stride;
-  p.sh = which == 0 ? a->k_head_stride : a->v_head_stride;
+  p.sp = sps[which];
+  p.ss = sss[which];
+  p.sh = shs[which];
   p.num_pages = a->num_pages;
   p.bt = a->block_table;
   p.bt_stride = a->bt_row_stride;
   p.seq = seq;
   p.head = head;
   p.seq_len = seq_len;
-  p.row_bytes = kv_row_bytes(cfg->kv_format);
+  p.row_bytes = scales ? kBlockScaleRowBytes : kv_row_bytes(cfg->kv_format);
   p.page_shift = ilog2(cfg->page_size);
   p.out = dense_out;
   return mj::launch_gather(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
 mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal) {
-  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 13)) || nontemporal < 0 || nontemporal > 4) return MJ_EINVAL;
+  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 17)) || nontemporal < 0 || nontemporal > 4) return MJ_EINVAL;
   mj::set_decode_variant(variant, nontemporal);
   return MJ_OK;
 }

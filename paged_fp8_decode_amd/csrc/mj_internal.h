@@ -52,7 +52,10 @@ struct DecodeParams {
   int page_size, page_shift, kv_tile;
   int causal;
   int num_work;
-  int head_major;              // grid is (h_k, num_work) instead of (num_work, h_k)
+  // grid: 0 = (num_work, h_k); 1 = (h_k, num_work); 2 = XCD-grouped, one
+  // dimension of ceil(num_work / 8) * 8 * h_k workgroups numbered so that
+  // the h_k heads of a work item share an XCD (see the matrix-core launch)
+  int head_major;
   // q_bf16 = 1: bf16-Q mode.  qb is then the bf16 Q the kernels use as is
   // (q8 / q_descale unused), on every decode kernel but the VALU-PV one.
   // Otherwise (fused step, matrix-core kernel only; null elsewhere) qb is the
@@ -73,6 +76,12 @@ struct DecodeParams {
   int plan_margin, plan_max_splits, plan_slots, plan_split, plan_min_chunk;
   int32_t* ns_out;
   int32_t* sb_out;
+  // nvfp4: the e4m3 block-scale pools (8-byte rows, paged like the codes);
+  // null for the other formats
+  const uint8_t* ksb;
+  const uint8_t* vsb;
+  int64_t ksb_sp, ksb_ss, ksb_sh;
+  int64_t vsb_sp, vsb_ss, vsb_sh;
 };
 
 struct MergeParams {
@@ -104,6 +113,9 @@ struct WriteParams {
   int ks_kind, vs_kind;     // 0 tensor, 1 head, 3 channel
   int num_tokens, h_k, page_shift, kv_format;
   int tokens_per_thread;    // set by the launcher
+  uint8_t* kbs;             // nvfp4 block-scale pools (null otherwise)
+  uint8_t* vbs;
+  int64_t kbs_sp, kbs_ss, kbs_sh, vbs_sp, vbs_ss, vbs_sh;  // bytes
 };
 
 struct GatherParams {

@@ -12,13 +12,16 @@
 // reciprocal with one FMA correction), so the bytes are the same as any other
 // correct evaluation.  fp6 and fp4 rows are the little-endian 6- and 4-bit
 // streams the decode kernels read (code k at stream bits [6k, 6k+6) or
-// [4k, 4k+4)).  Slot s is
+// [4k, 4k+4)).  nvfp4 (the published NVFP4 recipe): per 16-channel block of
+// y = x / s, the e4m3 block scale RNE(amax|y| / 6), codes RNE_e2m1(y /
+// e4m3(scale)), both divisions correctly rounded, zero codes under a zero
+// scale; the scale byte goes to the block-scale row of the same slot.  Slot s is
 // page s / page_size, row s % page_size; a negative slot (padding) or one
 // past the pool is skipped.
 //
 // One thread per (KV head, 16 channels) of 8 tokens: 32 bytes of bf16 in
-// per side and token, 16 bytes (e4m3), 12 bytes (fp6) or 8 bytes (fp4) of
-// codes out.  The
+// per side and token, 16 bytes (e4m3), 12 bytes (fp6) or 8 bytes (fp4;
+// nvfp4 also the block's scale byte) of codes out.  The
 // write touches every byte once.
 #include "mj_device.h"
 #include "mj_internal.h"
@@ -44,18 +47,36 @@ __device__ __forceinline__ float div_rn(float x, float s, float y) {
   return x == 0.0f ? x : __builtin_fmaf(r, y, q);
 }
 
+// dst_bs (nvfp4 only): the row's block-scale byte of these 16 channels
 template <int FMT>
 __device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc)[16], const float (&rc)[16], int c0,
-                                           uint8_t* dst_row) {
+                                           uint8_t* dst_row, uint8_t* dst_bs) {
   const uint4 a = *reinterpret_cast<const uint4*>(src);
   const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t code[16];
+  float q[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t bits = (i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16);
-    const float q = div_rn(__uint_as_float(bits), sc[i], rc[i]);
-    code[i] = FMT == 0 ? e4m3_rne(q) : FMT == 1 ? e2m3_rne(q) : FMT == 2 ? e3m2_rne(q) : e2m1_rne(q);
+    q[i] = div_rn(__uint_as_float(bits), sc[i], rc[i]);
+  }
+  if constexpr (FMT == 4) {
+    // nvfp4: the 16 channels are one block; e4m3 scale of amax / 6, codes of
+    // q / scale (zero codes under a zero scale)
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(q[i]));
+    const uint32_t sc8 = e4m3_rne(div_rn(amax, 6.0f, 1.0f / 6.0f));
+    const float sv = e4m3_value(sc8);
+    const float rv = 1.0f / sv;  // correctly rounded; unused when sv == 0
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = sv > 0.0f ? e2m1_rne(div_rn(q[i], sv, rv)) : 0u;
+    *dst_bs = (uint8_t)sc8;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      code[i] = FMT == 0 ? e4m3_rne(q[i]) : FMT == 1 ? e2m3_rne(q[i]) : FMT == 2 ? e3m2_rne(q[i]) : e2m1_rne(q[i]);
   }
   if constexpr (FMT == 0) {
     uint4 o;
@@ -64,7 +85,7 @@ __device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc
     o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
     o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
     *reinterpret_cast<uint4*>(dst_row + c0) = o;
-  } else if constexpr (FMT == 3) {
+  } else if constexpr (FMT >= 3) {
     uint2 o = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -120,10 +141,12 @@ __global__ __launch_bounds__(kWThreads) void write_kv_kernel(WriteParams p) {
     const int64_t page = slot >> p.page_shift;
     if (page >= p.num_pages) continue;
     const int64_t row = slot & ((1 << p.page_shift) - 1);
+    uint8_t* kb = FMT == 4 ? p.kbs + page * p.kbs_sp + row * p.kbs_ss + (int64_t)g * p.kbs_sh + grp : nullptr;
+    uint8_t* vb = FMT == 4 ? p.vbs + page * p.vbs_sp + row * p.vbs_ss + (int64_t)g * p.vbs_sh + grp : nullptr;
     write_side<FMT>(p.key + (int64_t)t * p.k_ts + (int64_t)g * p.k_hs + c0, ks, kr, c0,
-                    p.kc + page * p.kc_sp + row * p.kc_ss + (int64_t)g * p.kc_sh);
+                    p.kc + page * p.kc_sp + row * p.kc_ss + (int64_t)g * p.kc_sh, kb);
     write_side<FMT>(p.value + (int64_t)t * p.v_ts + (int64_t)g * p.v_hs + c0, vs, vr, c0,
-                    p.vc + page * p.vc_sp + row * p.vc_ss + (int64_t)g * p.vc_sh);
+                    p.vc + page * p.vc_sp + row * p.vc_ss + (int64_t)g * p.vc_sh, vb);
   }
 }
 
@@ -142,7 +165,8 @@ hipError_t launch_write_kv(const WriteParams& p_in, hipStream_t s) {
     case 0: hipLaunchKernelGGL(write_kv_kernel<0>, grid, dim3(kWThreads), 0, s, p); break;
     case 1: hipLaunchKernelGGL(write_kv_kernel<1>, grid, dim3(kWThreads), 0, s, p); break;
     case 2: hipLaunchKernelGGL(write_kv_kernel<2>, grid, dim3(kWThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(write_kv_kernel<3>, grid, dim3(kWThreads), 0, s, p); break;
+    case 3: hipLaunchKernelGGL(write_kv_kernel<3>, grid, dim3(kWThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL(write_kv_kernel<4>, grid, dim3(kWThreads), 0, s, p); break;
   }
   return hipGetLastError();
 }

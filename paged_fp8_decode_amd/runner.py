@@ -79,7 +79,8 @@ class DecodeStep:
 
     def run(self, *, q, k_cache, v_cache, k_strides, v_strides, num_pages, block_table, seq_lens, k_descale,
             v_descale, descale_kind, softmax_scale, out, lse=None, q_mul=None, o_mul=None, causal=True,
-            info: PlanInfo | None = None, stream=None, events=None, fused=False, plan_on_device=False, margin=0):
+            info: PlanInfo | None = None, stream=None, events=None, fused=False, plan_on_device=False, margin=0,
+            k_block_scale=None, v_block_scale=None, k_bs_strides=None, v_bs_strides=None):
         """quantize Q -> decode -> merge (iff the plan split), all on ``stream``;
         with ``fused`` one ``mj_decode_step`` call instead.
 
@@ -88,7 +89,8 @@ class DecodeStep:
         ``events``: optional pair of events recorded right before and right
         after the decode launch (the step call when fused).  ``plan_on_device``
         (fused only): the step plans from ``seq_lens`` itself (``info`` from
-        ``plan_shape``).
+        ``plan_shape``).  nvfp4 caches also pass the two block-scale pools
+        (uint8) and their byte strides (page, slot, head).
         """
         assert fused or not plan_on_device
         info = info or self.info
@@ -111,9 +113,13 @@ class DecodeStep:
             out=out.data_ptr(), out_tok_stride=out.stride(0), out_head_stride=out.stride(1),
             lse=lse.data_ptr() if lse is not None else None,
         )
+        if k_block_scale is not None:
+            a.k_block_scale, a.v_block_scale = k_block_scale.data_ptr(), v_block_scale.data_ptr()
+            a.k_bs_page_stride, a.k_bs_slot_stride, a.k_bs_head_stride = k_bs_strides
+            a.v_bs_page_stride, a.v_bs_slot_stride, a.v_bs_head_stride = v_bs_strides
         if self.q_bf16:
             if q_mul is not None:
-                raise ValueError("q_mul folds fp6 K scales into quantized Q; bf16-Q mode takes e4m3 KV only")
+                raise ValueError("q_mul folds fp6 K scales into quantized Q; bf16-Q mode has no Q scale")
             assert q.stride(2) == 1
             a.q_bf16, a.q_tok_stride, a.q_head_stride = q.data_ptr(), q.stride(0), q.stride(1)
         if fused:
@@ -172,7 +178,11 @@ class DecodeStep:
     def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None, fused=False,
                      plan_on_device=False):
         ks, vs = wl.kv_strides()
-        return self.run(q=wl.q, k_cache=wl.k_pool, v_cache=wl.v_pool, k_strides=ks, v_strides=vs,
+        bs = {}
+        if wl.k_bs_pool is not None:
+            kbs, vbs = wl.bs_strides()
+            bs = dict(k_block_scale=wl.k_bs_pool, v_block_scale=wl.v_bs_pool, k_bs_strides=kbs, v_bs_strides=vbs)
+        return self.run(**bs, q=wl.q, k_cache=wl.k_pool, v_cache=wl.v_pool, k_strides=ks, v_strides=vs,
                         num_pages=wl.num_pages, block_table=wl.block_table, seq_lens=wl.seq_lens_dev,
                         k_descale=wl.k_descale, v_descale=wl.v_descale, descale_kind=wl.descale_kind,
                         softmax_scale=wl.softmax_scale, out=out, lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul,

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 5
+    assert mj.lib().mj_abi_version() == 6
 
 
 def _cfg(**kw):
@@ -98,7 +98,7 @@ def test_planner_matches_oracle_random():
                    wgs_per_cu=int(rng.integers(0, 5)), kv_tile_tokens=int(rng.choice([16, 64, 128, 256])),
                    slots_override=int(rng.choice([0, 0, 0, 7, 300])),
                    min_chunk_tokens=int(rng.choice([0, 0, 1, 100, 2048, 9000])),
-                   kv_format=str(rng.choice(["e4m3", "e2m3", "e3m2", "e2m1"])))
+                   kv_format=str(rng.choice(["e4m3", "e2m3", "e3m2", "e2m1", "nvfp4"])))
         b = int(rng.integers(1, cfg.max_num_seqs + 1))
         lens = rng.integers(0, int(rng.choice([100, 5000, 200000])), size=b).tolist()
         _compare(cfg, lens, int(rng.integers(1, mq + 1)), int(rng.integers(0, 8)))
@@ -110,10 +110,11 @@ def test_config_errors():
     assert mj.mj_config_check(_cfg(page_size=24)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_config_check(_cfg(page_size=256)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_config_check(_cfg(h_q=30, h_k=8)) == mj.MJ_EUNSUPPORTED
-    assert mj.mj_config_check(_cfg(kv_format=4)) == mj.MJ_EUNSUPPORTED
+    assert mj.mj_config_check(_cfg(kv_format=5)) == mj.MJ_EUNSUPPORTED
     assert mj.mj_config_check(_cfg(kv_format=-1)) == mj.MJ_EUNSUPPORTED
-    for f in ("e2m3", "e3m2", "e2m1"):
+    for f in ("e2m3", "e3m2", "e2m1", "nvfp4"):
         assert mj.mj_config_check(_cfg(kv_format=f)) == mj.MJ_OK
+    assert mj.mj_config_check(_cfg(kv_format="nvfp4", q_mode="bf16")) == mj.MJ_OK
     assert mj.mj_config_check(_cfg(max_num_seqs=0)) == mj.MJ_EINVAL
     assert mj.mj_config_check(_cfg(kv_tile_tokens=100)) == mj.MJ_EINVAL
     assert mj.mj_config_check(_cfg(q_mode="bf16")) == mj.MJ_OK
@@ -201,6 +202,34 @@ def test_decode_bf16_q_argument_errors(kw, status):
     assert _decode_status(_cfg(q_mode="bf16"), **base) == status
 
 
+_NV = dict(k_block_scale=FAKE, k_bs_page_stride=16 * 8 * 8, k_bs_slot_stride=8, k_bs_head_stride=16 * 8,
+           v_block_scale=FAKE, v_bs_page_stride=16 * 8 * 8, v_bs_slot_stride=8, v_bs_head_stride=16 * 8)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_block_scale=None), mj.MJ_EINVAL),
+    (dict(v_block_scale=None), mj.MJ_EINVAL),
+    (dict(k_bs_slot_stride=-8), mj.MJ_EINVAL),
+    (dict(k_block_scale=FAKE + 4), mj.MJ_EALIGN),
+    (dict(v_bs_head_stride=12), mj.MJ_EALIGN),
+    (dict(v_bs_page_stride=1020), mj.MJ_EALIGN),
+])
+def test_decode_nvfp4_block_scale_errors(kw, status):
+    a = dict(_NV, k_page_stride=16 * 8 * 64, k_slot_stride=64, k_head_stride=16 * 64, v_page_stride=16 * 8 * 64,
+             v_slot_stride=64, v_head_stride=16 * 64)
+    a.update(kw)
+    assert _decode_status(_cfg(kv_format="nvfp4"), **a) == status
+
+
+@no_gpu
+def test_block_scales_are_not_read_for_other_formats():
+    # null block-scale pools are fine outside nvfp4 (the decode then proceeds
+    # to its other checks: here a deliberately short workspace)
+    assert _decode_status(_cfg(kv_format="e2m1"), k_block_scale=None, workspace_bytes=16) == mj.MJ_ECAPACITY
+    assert _decode_status(_cfg(kv_format="nvfp4"), **_NV, workspace_bytes=16) == mj.MJ_ECAPACITY
+
+
 @no_gpu
 def test_step_rejects_q_mul_in_bf16_q_mode():
     cfg = _cfg(q_mode="bf16")
@@ -266,6 +295,19 @@ def test_write_argument_errors(kw, status):
     assert mj.lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(_wargs(**kw)), None) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_block_scale=None), mj.MJ_EINVAL),
+    (dict(v_bs_slot_stride=-8), mj.MJ_EINVAL),
+    (dict(v_block_scale=FAKE + 2), mj.MJ_EALIGN),
+    (dict(k_bs_head_stride=4), mj.MJ_EALIGN),
+])
+def test_write_nvfp4_block_scale_errors(kw, status):
+    cfg = _cfg(max_num_seqs=64, kv_format="nvfp4")
+    a = dict(_NV)
+    a.update(kw)
+    assert mj.lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(_wargs(**a)), None) == status
+
+
 def test_write_zero_tokens_needs_no_buffers():
     cfg = _cfg()
     assert mj.lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(mj.WriteArgs(num_tokens=0)), None) == mj.MJ_OK
@@ -274,5 +316,20 @@ def test_write_zero_tokens_needs_no_buffers():
 def test_debug_knob_errors():
     assert mj.lib().mj_debug_set_step_merge(3) == mj.MJ_EINVAL
     assert mj.lib().mj_debug_set_step_merge(-1) == mj.MJ_EINVAL
-    assert mj.lib().mj_debug_set_decode_variant(14, 1) == mj.MJ_EINVAL
+    assert mj.lib().mj_debug_set_decode_variant(18, 1) == mj.MJ_EINVAL
+    assert mj.lib().mj_debug_set_decode_variant(17, 1) == mj.MJ_OK
+    assert mj.lib().mj_debug_set_decode_variant(0, 1) == mj.MJ_OK
     assert mj.lib().mj_debug_set_decode_variant(0, 5) == mj.MJ_EINVAL
+
+
+@no_gpu
+def test_gather_probe_scale_pools_need_nvfp4():
+    L = mj.lib()
+    for fmt, which, status in (("e4m3", 2, mj.MJ_EINVAL), ("e2m1", 3, mj.MJ_EINVAL), ("nvfp4", 4, mj.MJ_EINVAL),
+                               ("e4m3", -1, mj.MJ_EINVAL)):
+        cfg = _cfg(kv_format=fmt)
+        a = _args(cfg, **_NV)
+        assert L.mj_debug_gather_kv(ctypes.byref(cfg), ctypes.byref(a), 0, 0, 16, which, FAKE, None) == status
+    cfg = _cfg(kv_format="nvfp4")
+    a = _args(cfg, **dict(_NV, k_block_scale=None))
+    assert L.mj_debug_gather_kv(ctypes.byref(cfg), ctypes.byref(a), 0, 0, 16, 2, FAKE, None) == mj.MJ_EINVAL

@@ -1,5 +1,5 @@
 """GPU parity of the bf16-Q mode (config q_mode = bf16: Q used as given, the
-e4m3 KV codes converted to bf16 in the kernel) against the oracle's
+e4m3 or nvfp4 KV codes converted to bf16 in the kernel) against the oracle's
 unquantized-Q attention, through the C ABI:
 
 * the in-kernel e4m3 -> bf16 operand converter on every code (bit-exact);
@@ -20,7 +20,7 @@ from helpers import compare_lse, compare_out, oracle_step, say
 
 pytestmark = pytest.mark.gpu
 
-E4M3_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "32k", "32k_b16"]
+E4M3_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "32k", "32k_b16", "cfg5_nvfp4", "cfg3_nvfp4"]
 FINE = dict(min_chunk_tokens=1)
 
 
@@ -128,7 +128,7 @@ def test_strided_q_view(mj, gpu):
         _check(wl, out, lse, f"strided q fused={fused}")
 
 
-FULL = {"cfg2": 2, "cfg3": 2, "cfg4c": 2, "32k": 2}
+FULL = {"cfg2": 2, "cfg3": 2, "cfg4c": 2, "32k": 2, "cfg5_nvfp4": 1}
 
 
 @pytest.mark.parametrize("key", list(FULL))

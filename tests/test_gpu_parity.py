@@ -89,7 +89,8 @@ def test_quantize_q_bit_exact(mj, gpu, b, q_len, h_q, h_k, mul, extra):
     assert np.array_equal(q8.cpu().numpy().reshape(ref_c.shape), ref_c)
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
+@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
+                                 "cfg3_nvfp4"])
 def test_gather_probe_bit_exact(mj, gpu, key):
     from oracle.attention import gather_codes
     from paged_fp8_decode_amd.runner import DecodeStep
@@ -103,11 +104,18 @@ def test_gather_probe_bit_exact(mj, gpu, key):
                       num_pages=wl.num_pages, block_table=wl.block_table.data_ptr(),
                       bt_row_stride=wl.block_table.stride(0), max_blocks_per_seq=wl.block_table.shape[1])
     h = wl.host()
-    row = s.row_bytes
+    pools = [(0, h["k_pool"], h["k_strides"], s.row_bytes), (1, h["v_pool"], h["v_strides"], s.row_bytes)]
+    if s.kv_format == "nvfp4":
+        kb, vb = wl.bs_strides()
+        a.k_block_scale, a.v_block_scale = wl.k_bs_pool.data_ptr(), wl.v_bs_pool.data_ptr()
+        a.k_bs_page_stride, a.k_bs_slot_stride, a.k_bs_head_stride = kb
+        a.v_bs_page_stride, a.v_bs_slot_stride, a.v_bs_head_stride = vb
+        pools += [(2, h["k_bs_pool"], h["k_bs_strides"], s.scale_row_bytes),
+                  (3, h["v_bs_pool"], h["v_bs_strides"], s.scale_row_bytes)]
     for i in range(s.b):
         L = wl.seq_lens[i]
         for g in {0, s.h_k - 1}:
-            for which, pool, st in ((0, h["k_pool"], h["k_strides"]), (1, h["v_pool"], h["v_strides"])):
+            for which, pool, st, row in pools:
                 dense = torch.empty(max(1, L * row), dtype=torch.uint8, device=gpu)
                 mj.mj_debug_gather_kv(step.cfg, a, i, g, L, which, dense)
                 torch.cuda.synchronize()
@@ -115,7 +123,8 @@ def test_gather_probe_bit_exact(mj, gpu, key):
                 assert np.array_equal(dense.cpu().numpy()[: L * row].reshape(L, row), ref)
 
 
-SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "32k", "32k_b16"]
+SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4",
+              "32k", "32k_b16"]
 # 0 = automatic choice, 1 = generic LDS kernel, 2 = VALU-PV streaming kernel
 VARIANTS = [0, 1, 2]
 
@@ -141,7 +150,7 @@ def test_parity_small_all_outputs(mj, gpu, key, variant):
     compare_lse(lse, LSE, wl.spec.name)
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4"])
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
 def test_split_and_unsplit_agree(mj, gpu, key, variant):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
@@ -167,6 +176,26 @@ def test_page_permutation_bit_identical(mj, gpu, variant):
     out2, lse2, _ = _run(mj, wl, **FINE)
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("variant", [0, 1], indirect=True)
+@pytest.mark.parametrize("key", ["cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4"])
+def test_sub_byte_edge_lengths_and_shapes(mj, gpu, key, variant):
+    """The fp4 formats at empty, single-token and tile-boundary lengths, and
+    in the speculative row shapes (replicated rows, 8, 16, 32 rows; > 32 rows
+    on the generic kernel)."""
+    lens = (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, 1000)
+    for q_len, h_q, h_k, causal in ((1, 32, 8, True), (2, 16, 8, True), (4, 8, 8, True), (2, 4, 2, False),
+                                    (2, 32, 8, True), (4, 32, 8, True), (3, 40, 8, True), (5, 64, 8, True)):
+        wl = synth.build(synth.spec_for(key, small=True, b=len(lens), lens=lens, lens_loguniform=(), q_len=q_len,
+                                        h_q=h_q, h_k=h_k, causal=causal, k_outliers=0, slots_override=0), gpu)
+        say(f"  {key} edges q_len={q_len} h_q={h_q} h_k={h_k} causal={causal} variant={variant}")
+        out, lse, _ = _run(mj, wl, **FINE)
+        O, LSE = oracle_step(wl)
+        compare_out(out, O, f"{key} edges q_len={q_len} h_q={h_q}")
+        compare_lse(lse, LSE, f"{key} edges q_len={q_len} h_q={h_q}")
+        if q_len == 1:
+            assert torch.all(out[:1].float() == 0)  # L = 0
 
 
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
@@ -243,8 +272,8 @@ def test_graph_replay_after_replanning(mj, gpu):
         compare_lse(lse, LSE, f"replay {trial}")
 
 
-FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "cfg5_e3m2": 1, "cfg5_e2m1": 1, "32k": 2,
-        "32k_b16": 2}
+FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "cfg5_e3m2": 1, "cfg5_e2m1": 1,
+        "cfg5_nvfp4": 1, "cfg3_nvfp4": 2, "32k": 2, "32k_b16": 2}
 
 
 @pytest.mark.parametrize("key", list(FULL))
@@ -489,3 +518,27 @@ def test_plan_in_kernel_graph_replay(mj, gpu):
         O, LSE = oracle_step(wl)
         compare_out(out, O, f"plan-in-kernel replay {trial} lens={lens}")
         compare_lse(lse, LSE, f"plan-in-kernel replay {trial}")
+
+
+@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e2m1", "cfg3_nvfp4"])
+def test_grid_orders_bit_identical(mj, gpu, key):
+    """The matrix-core kernel's three grid numberings (item-major, head-major,
+    XCD-grouped with a padded last group) and both prefetch depths give the
+    same bits: the order of workgroups changes no arithmetic."""
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    ref = None
+    for v in (10, 11, 12, 14, 15):
+        mj.mj_debug_set_decode_variant(v, 1)
+        try:
+            say(f"grid order {wl.spec.name} variant={v}")
+            out, lse, info = _run(mj, wl, fused=True, **FINE)
+        finally:
+            mj.mj_debug_set_decode_variant(0, 1)
+        if ref is None:
+            ref = (out, lse)
+            O, LSE = oracle_step(wl)
+            compare_out(out, O, f"{key} variant {v}")
+            compare_lse(lse, LSE, f"{key} variant {v}")
+        else:
+            assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), v
+            assert torch.equal(lse, ref[1]), v

@@ -26,13 +26,17 @@ def _strides(layout, P, h_k, row):
     return (P * h_k * row, h_k * row, row)
 
 
-def _write(mj, gpu, cfg, key, value, slots, k_pool, v_pool, ks, vs, k_scale, v_scale, kind, num_pages):
+def _write(mj, gpu, cfg, key, value, slots, k_pool, v_pool, ks, vs, k_scale, v_scale, kind, num_pages, bs=None):
     # the kernel trusts these sizes: check them before the launch
     assert slots.numel() == key.shape[0] == value.shape[0]
     assert key.shape[1:] == value.shape[1:] == (cfg.h_k, 128)
-    row = (128, 96, 96, 64)[cfg.kv_format]
+    row = (128, 96, 96, 64, 64)[cfg.kv_format]
     last = (num_pages - 1) * ks[0] + (cfg.page_size - 1) * ks[1] + (cfg.h_k - 1) * ks[2] + row
     assert last <= k_pool.numel() and last <= v_pool.numel()
+    assert (bs is not None) == (cfg.kv_format == mj.KV_FORMATS["nvfp4"])
+    if bs is not None:  # (k pool, v pool, k strides, v strides) of the block scales
+        for pool, st in ((bs[0], bs[2]), (bs[1], bs[3])):
+            assert (num_pages - 1) * st[0] + (cfg.page_size - 1) * st[1] + (cfg.h_k - 1) * st[2] + 8 <= pool.numel()
     need = {"tensor": 1, "head": cfg.h_k, "channel": cfg.h_k * 128}[kind]
     assert k_scale.numel() >= need and v_scale.numel() >= need
     kk = mj.SCALE_KINDS[kind]
@@ -43,13 +47,18 @@ def _write(mj, gpu, cfg, key, value, slots, k_pool, v_pool, ks, vs, k_scale, v_s
                      v_cache=v_pool.data_ptr(), v_page_stride=vs[0], v_slot_stride=vs[1], v_head_stride=vs[2],
                      num_pages=num_pages, k_scale=k_scale.data_ptr(), k_scale_kind=kk, v_scale=v_scale.data_ptr(),
                      v_scale_kind=kk)
+    if bs is not None:
+        a.k_block_scale, a.v_block_scale = bs[0].data_ptr(), bs[1].data_ptr()
+        a.k_bs_page_stride, a.k_bs_slot_stride, a.k_bs_head_stride = bs[2]
+        a.v_bs_page_stride, a.v_bs_slot_stride, a.v_bs_head_stride = bs[3]
     mj.mj_write_kv(cfg, a)
     torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e4m3", "channel"),
                                             ("e2m3", "channel"), ("e2m3", "head"), ("e3m2", "channel"),
-                                            ("e3m2", "tensor"), ("e2m1", "channel"), ("e2m1", "head")])
+                                            ("e3m2", "tensor"), ("e2m1", "channel"), ("e2m1", "head"),
+                                            ("nvfp4", "tensor"), ("nvfp4", "head"), ("nvfp4", "channel")])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])
 @pytest.mark.parametrize("P", [16, 128])
 def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
@@ -70,7 +79,7 @@ def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
     fused[1, 0, :10] = special  # token 1 of K and token 2 of V are written (not padding)
     fused[2, h_k + 1, 118:] = special
     key, value = fused[:, :h_k], fused[:, h_k + 1:2 * h_k + 1]
-    fmax = FMT_MAX[kv_format]
+    fmax = FMT_MAX.get(kv_format, 6.0 * 448.0)  # nvfp4: e2m1 max times e4m3 max
     amax_k = key.float().abs().amax(dim=0).numpy()  # (h_k, 128); saturating rows stay rare
     amax_v = value.float().abs().amax(dim=0).numpy()
     if kind == "tensor":
@@ -89,15 +98,25 @@ def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
     slots[3] = (pages - 1) * P + 2  # in the last page: past num_pages, skipped
     k_pool = torch.from_numpy(init_k.copy()).to(gpu)
     v_pool = torch.from_numpy(init_v.copy()).to(gpu)
+    bs = bs_np = None
+    if kv_format == "nvfp4":
+        bst = _strides(layout, P, h_k, 8)
+        init_kb = rng.integers(0, 256, pages * P * h_k * 8, dtype=np.uint8)
+        init_vb = rng.integers(0, 256, pages * P * h_k * 8, dtype=np.uint8)
+        bs = (torch.from_numpy(init_kb.copy()).to(gpu), torch.from_numpy(init_vb.copy()).to(gpu), bst, bst)
+        bs_np = dict(bs_pools=(init_kb, init_vb), bs_strides=(bst, bst))
     cfg = mj.mj_config(h_q=h_k, h_k=h_k, page_size=P, max_num_seqs=1, kv_format=kv_format, num_cus=256)
     _write(mj, gpu, cfg, key.to(gpu), value.to(gpu), torch.from_numpy(slots).to(gpu), k_pool, v_pool, ks, vs,
-           torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, num_pages)
+           torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, num_pages, bs)
     oslots = slots.copy()
     oslots[oslots >= num_pages * P] = -1  # the oracle's pool has every page; the kernel skips past num_pages
-    ref_k, ref_v = write_kv((init_k, init_v), (ks, vs), P, kv_format, key.float().numpy(), value.float().numpy(),
-                            oslots, k_sc, v_sc, kind)
-    assert np.array_equal(k_pool.cpu().numpy(), ref_k)
-    assert np.array_equal(v_pool.cpu().numpy(), ref_v)
+    ref = write_kv((init_k, init_v), (ks, vs), P, kv_format, key.float().numpy(), value.float().numpy(),
+                   oslots, k_sc, v_sc, kind, **(bs_np or {}))
+    assert np.array_equal(k_pool.cpu().numpy(), ref[0])
+    assert np.array_equal(v_pool.cpu().numpy(), ref[1])
+    if bs is not None:
+        assert np.array_equal(bs[0].cpu().numpy(), ref[2])
+        assert np.array_equal(bs[1].cpu().numpy(), ref[3])
 
 
 def test_write_zero_tokens_is_a_noop(mj, gpu):
@@ -106,12 +125,14 @@ def test_write_zero_tokens_is_a_noop(mj, gpu):
     mj.mj_write_kv(cfg, a)
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg5", "cfg5_e3m2", "cfg5_e2m1"])
+@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4"])
 def test_written_cache_decodes(mj, gpu, key):
     """Blank every token row of a seeded workload's cache, re-write them with
     mj_write_kv from the dequantized K/V (code * scale in bf16: dividing by
-    the scale lands within 2^-9 of the code, which rounds back to it), and
-    check the pools are byte-identical to the generator's; then decode."""
+    the scale lands within 2^-9 of the code, which rounds back to it; an
+    nvfp4 block holds a +-6 code, so its amax / 6 lands as close to its
+    block scale), and check the pools are byte-identical to the generator's;
+    then decode."""
     import synth
     from helpers import oracle_step
     from oracle import formats as F
@@ -123,7 +144,8 @@ def test_written_cache_decodes(mj, gpu, key):
     h = wl.host()
     ks, vs = wl.kv_strides()
     row = s.row_bytes
-    if s.kv_format == "e4m3":
+    nv = s.kv_format == "nvfp4"
+    if s.kv_format in ("e4m3", "nvfp4"):
         kind = "head" if wl.descale_kind == "head" else ("tensor" if wl.descale_kind == "tensor" else None)
         if kind is None:  # per-(sequence, head) descales have no slot-mapped write form
             pytest.skip("per-(sequence, head) scales are a decode-side shape only")
@@ -138,6 +160,8 @@ def test_written_cache_decodes(mj, gpu, key):
     vx = np.zeros((n, s.h_k, 128), np.float32)
     slots = np.zeros(n, np.int64)
     mask = torch.zeros(wl.k_pool.numel(), dtype=torch.bool)
+    bmask = torch.zeros(wl.k_bs_pool.numel() if nv else 1, dtype=torch.bool)
+    bss = wl.bs_strides() if nv else None
     base = 0
     for i in range(s.b):
         L = wl.seq_lens[i]
@@ -148,10 +172,18 @@ def test_written_cache_decodes(mj, gpu, key):
             for g in range(s.h_k):
                 b = page * ks[0] + (j % s.page_size) * ks[1] + g * ks[2]
                 mask[b:b + row] = True
+                if nv:
+                    b = page * bss[0][0] + (j % s.page_size) * bss[0][1] + g * bss[0][2]
+                    bmask[b:b + 8] = True
         for g in range(s.h_k):
-            for pool, st, dst, sc in ((h["k_pool"], h["k_strides"], kx, k_sc), (h["v_pool"], h["v_strides"], vx, v_sc)):
+            for side, pool, st, dst, sc in ((0, h["k_pool"], h["k_strides"], kx, k_sc),
+                                            (1, h["v_pool"], h["v_strides"], vx, v_sc)):
                 codes = gather_codes(pool, st, s.page_size, bt, L, g, row)
-                vals = F.decode_row_codes(codes, s.kv_format)
+                if nv:
+                    bp, bst = (h["k_bs_pool"], h["k_bs_strides"]) if side == 0 else (h["v_bs_pool"], h["v_bs_strides"])
+                    vals = F.nvfp4_decode(codes, gather_codes(bp, bst, s.page_size, bt, L, g, 8))
+                else:
+                    vals = F.decode_row_codes(codes, s.kv_format)
                 div = sc[0] if kind == "tensor" else (sc[g] if kind == "head" else sc.reshape(-1, 128)[g])
                 dst[base:base + L, g] = vals * div
         base += L
@@ -160,12 +192,22 @@ def test_written_cache_decodes(mj, gpu, key):
     m = mask.to(gpu)
     wl.k_pool.view(-1)[m] = 0
     wl.v_pool.view(-1)[m] = 0
+    bs = None
+    if nv:
+        assert bss[0] == bss[1]
+        before_kb, before_vb = wl.k_bs_pool.clone(), wl.v_bs_pool.clone()
+        bm = bmask.to(gpu)
+        wl.k_bs_pool.view(-1)[bm] = 0
+        wl.v_bs_pool.view(-1)[bm] = 0
+        bs = (wl.k_bs_pool, wl.v_bs_pool, bss[0], bss[1])
     cfg = mj.mj_config(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, kv_format=s.kv_format,
                        num_cus=256)
     _write(mj, gpu, cfg, torch.from_numpy(kx).to(torch.bfloat16).to(gpu),
            torch.from_numpy(vx).to(torch.bfloat16).to(gpu), torch.from_numpy(slots).to(gpu), wl.k_pool, wl.v_pool,
-           ks, vs, torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, wl.num_pages)
+           ks, vs, torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, wl.num_pages, bs)
     assert torch.equal(wl.k_pool, before_k) and torch.equal(wl.v_pool, before_v)
+    if nv:
+        assert torch.equal(wl.k_bs_pool, before_kb) and torch.equal(wl.v_bs_pool, before_vb)
     step = DecodeStep.for_workload(wl, min_chunk_tokens=1)
     info = step.plan_workload(wl)
     out, lse = new_output(wl)
