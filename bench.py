@@ -52,10 +52,12 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "b8d14a77409d3d6c",
-    "cfg2": dict(fetch_bytes=269285363, write_bytes=1179922),
-    "32k": dict(fetch_bytes=4297903582, write_bytes=4718905),
-    "cfg5": dict(fetch_bytes=806117880, write_bytes=589833),
+    "sources_sha256_16": "c9b8c3cdc9506ced",
+    "cfg2": dict(fetch_bytes=269311261, write_bytes=1180000),
+    "32k": dict(fetch_bytes=4297916945, write_bytes=4718974),
+    "cfg5": dict(fetch_bytes=806135702, write_bytes=589835),
+    "cfg5_e2m1": dict(fetch_bytes=538224434, write_bytes=1179671),
+    "cfg5_nvfp4": dict(fetch_bytes=604657040, write_bytes=1179671),
 }
 
 
@@ -91,7 +93,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="cfg2")
-    ap.add_argument("--extra", default="32k,32k_b16",
+    ap.add_argument("--extra", default="32k,32k_b16,cfg5,cfg5_e3m2,cfg5_e2m1,cfg5_nvfp4",
                     help="comma list of extra workloads reported under 'extra' ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--bf16q", default="cfg2,32k",
