@@ -565,7 +565,7 @@ __device__ __forceinline__ float row_of(const Ctx& c, int R) {  // softmax-layou
 
 template <int FMT, int NQB, int NRB>
 __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, const int (&row_tok)[NRB], int gi,
-                                        const KRows<FMT>& K, const VRows<FMT>& V, State<NQB, NRB>& st) {
+                                        const KRows<FMT>& K, VRows<FMT>& V, State<NQB, NRB>& st) {
   const int t0 = c.j0 + gi * kGran;
   // ---- logits: lane (n, jj) gets tokens t0 + 16k + 4jj + v of its rows
   float s[NRB][2][4];
@@ -576,6 +576,18 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
     const int tk = t0 + 16 * k;
     // tokens at or past `end` are masked; a dead tile masks all of them
     const int end = tile_page(c, tk) >= 0 ? c.j1 : 0;  // scalar; the block-table entry is cached
+    if (tk + 16 > end) {  // wave-uniform: the tile crosses the range end
+      // rows past the end hold whatever the page holds (NaN codes too):
+      // their V is zeroed so that their zero probabilities add exact zeros
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (tk + 4 * c.jj + v >= end) {
+#pragma unroll
+          for (int dw = 0; dw < Fmt<FMT>::kVDw; ++dw) V.d[4 * k + v][dw] = 0u;
+          if constexpr (Fmt<FMT>::kBlockScaled) V.s[4 * k + v] = 0u;
+        }
+      }
+    }
     // wave-uniform: every token of the tile visible to every row (row 0 of a
     // causal block sees the fewest keys)
     const bool full = tk + 16 <= end && (!c.causal || tk + 15 <= c.lim0);

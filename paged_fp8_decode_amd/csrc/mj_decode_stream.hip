@@ -214,8 +214,20 @@ __device__ __forceinline__ void qk_softmax(const Ctx& c, const v8i& qa, int gi, 
   }
 }
 
+// Rows past the range end hold whatever the page holds (NaN codes too): a
+// tile that crosses the end zeroes this lane's row if its token is past it,
+// so that its zero probabilities add exact zeros.
 template <int FMT>
-__device__ __forceinline__ void pv(const Rows<FMT>& V, const float pr[2][4], State& st) {
+__device__ __forceinline__ void pv(const Ctx& c, int gi, Rows<FMT>& V, const float pr[2][4], State& st) {
+  const int t0 = c.j0 + gi * kGran;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int tk = t0 + 16 * k;
+    if (tk + 16 > c.j1 && tk + c.n >= c.j1) {
+#pragma unroll
+      for (int i = 0; i < Fmt<FMT>::kDw; ++i) V.d[k][i] = 0u;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     if constexpr (FMT == 0) {
@@ -326,13 +338,13 @@ void decode_stream_kernel(DecodeParams p) {
       Rows<FMT> VB = load_rows<FMT, NT, true>(c, gi + kWaves);
       qk_softmax<FMT>(c, qa, gi, K, st, pr);
       K = load_rows<FMT, NT, false>(c, gi + kWaves);
-      pv<FMT>(VA, pr, st);
+      pv<FMT>(c, gi, VA, pr, st);
       gi += kWaves;
       if (gi >= ngr) break;
       VA = load_rows<FMT, NT, true>(c, gi + kWaves);
       qk_softmax<FMT>(c, qa, gi, K, st, pr);
       K = load_rows<FMT, NT, false>(c, gi + kWaves);
-      pv<FMT>(VB, pr, st);
+      pv<FMT>(c, gi, VB, pr, st);
       gi += kWaves;
       if (gi >= ngr) break;
     }

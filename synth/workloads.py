@@ -71,6 +71,7 @@ class Spec:
     pool_pages: int = 0  # 0 = round_up(2 * pages needed, 1024)
     extra_bt_cols: int = 2  # block-table columns beyond the longest sequence (poison)
     q_extra_heads: int = 0  # >0: Q is a strided view into a wider (fused-QKV-like) buffer
+    tail_nan: bool = False  # unused tail slots of each last page hold NaN codes (e4m3, nvfp4 scales), not poison
     seed: int = 1000
     d: int = HEAD_DIM
 
@@ -426,7 +427,8 @@ def build(spec: Spec, device="cpu") -> Workload:
     if s.kv_format == "e4m3":
         k_pool[poison] = POISON_E4M3
         v_pool[poison] = POISON_E4M3
-        poison_row = torch.full((row,), POISON_E4M3, dtype=torch.uint8, device=device)
+        # tail slots: the poison code, or e4m3's NaN code S.1111.111
+        poison_row = torch.full((row,), 0x7F if s.tail_nan else POISON_E4M3, dtype=torch.uint8, device=device)
     elif s.kv_format == "nvfp4":
         # poison: codes of 6 under scales of 448
         bshape = shape[:-1] + (srow,)
@@ -437,6 +439,8 @@ def build(spec: Spec, device="cpu") -> Workload:
         for pool_t, bs_t in ((k_pool, k_bs), (v_pool, v_bs)):
             pool_t[poison] = poison_row
             bs_t[poison] = poison_srow
+        if s.tail_nan:  # NaN block scales (S.1111.111) in the tail slots
+            poison_srow = torch.full((srow,), 0x7F, dtype=torch.uint8, device=device)
     else:
         fmax, enc_fn, pack_fn, pcode = SUBBYTE[s.kv_format]
         poison_row = pack_fn(torch.full((d,), pcode, dtype=torch.uint8, device=device))

@@ -542,3 +542,24 @@ def test_grid_orders_bit_identical(mj, gpu, key):
         else:
             assert torch.equal(out.view(torch.int16), ref[0].view(torch.int16)), v
             assert torch.equal(lse, ref[1]), v
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("key,q_mode", [("cfg2", "fp8"), ("cfg2", "bf16"), ("cfg4c", "fp8"), ("cfg3", "fp8"),
+                                        ("32k_b16", "fp8"), ("cfg5_nvfp4", "fp8"), ("cfg5_nvfp4", "bf16")])
+def test_nan_codes_past_the_sequence_end(mj, gpu, key, q_mode, variant):
+    """The unused slots of each sequence's last page hold NaN codes (e4m3
+    S.1111.111, NaN nvfp4 block scales): a tile that crosses the end must not
+    let them into the output (zero probabilities times NaN are NaN)."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for(key, small=True, tail_nan=True), gpu)
+    say(f"NaN tails {wl.spec.name} q_mode={q_mode} variant={variant} lens={wl.seq_lens}")
+    step = DecodeStep.for_workload(wl, q_mode=q_mode, **FINE)
+    info = step.plan_workload(wl)
+    out, lse = new_output(wl)
+    out.fill_(float("nan"))
+    step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.synchronize()
+    O, LSE = oracle_step(wl, quantize=q_mode == "fp8")
+    compare_out(out, O, f"{key} NaN tails")
+    compare_lse(lse, LSE, f"{key} NaN tails")
