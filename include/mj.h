@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 6
+#define MJ_ABI_VERSION 7
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -365,6 +365,35 @@ typedef struct mj_write_args {
  * multiples of 8 elements, cache strides not multiples of 16 bytes),
  * EUNSUPPORTED (SEQ_HEAD scales), EHIP. */
 mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* args, hipStream_t stream);
+
+/* Multi-step draft decode (runner.py, T5DecodeRunner.plan: a plan made
+ * `margin` tokens long stays valid while the device seq_lens grow by up to
+ * margin, since the kernels mask with the live lengths; backend.py: the
+ * speculator runs every draft step on one metadata build and advances the
+ * device seq_lens in place).  mj_draft_advance is that advance, on the
+ * device so that a whole draft loop (advance, mj_write_kv of the new rows,
+ * mj_decode_step on the margin plan) is one captured graph: for every
+ * sequence i < num_seqs with L = seq_lens[i] > 0, slot_mapping[i*q_len + t]
+ * = the cache slot of token position L + t (page block_table[i*bt_row_stride
+ * + (L+t)/page_size], as mj_write_kv takes it), for t < q_len, and then
+ * seq_lens[i] = min(L + q_len, max_blocks_per_seq * page_size).  A length-0
+ * sequence (graph padding) stays 0; slots of positions past the block table
+ * are -1 (not written).  One thread per sequence; the caller keeps the
+ * block table's pages for the new positions valid.
+ * Errors: EINVAL (nulls, num_seqs < 1, q_len < 1, bt_row_stride <
+ * max_blocks_per_seq, max_blocks_per_seq < 1), ECAPACITY (num_seqs >
+ * max_num_seqs, q_len > max_q_len), EALIGN (slot_mapping not 8-byte aligned),
+ * EHIP. */
+typedef struct mj_draft_args {
+  const int32_t* block_table;   /* device, row i at block_table + i*bt_row_stride */
+  int64_t bt_row_stride;        /* elements                                   */
+  int32_t max_blocks_per_seq;
+  int32_t* seq_lens;            /* device (num_seqs,), advanced in place        */
+  int32_t num_seqs;
+  int32_t q_len;                /* tokens appended per sequence                */
+  int64_t* slot_mapping;        /* device (num_seqs * q_len,), written          */
+} mj_draft_args;
+mj_status mj_draft_advance(const mj_config* cfg, const mj_draft_args* args, hipStream_t stream);
 
 /* Arguments of one whole decode step after the plan: the decode arguments
  * (decode.q8, decode.q_descale and decode.q_bf16 are not read and may be

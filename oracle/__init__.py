@@ -20,10 +20,12 @@ What it computes (mjolnir-kernel PyPI project page / sdist README, section
                 (softmax(Q K^T * scale) V), its split partials and their
                 log-sum-exp merge;
 * ``kvwrite``   the KV-cache write of new rows through a slot mapping
-                (wheel listing mjolnir/backend.py, ``do_kv_cache_update``).
+                (wheel listing mjolnir/backend.py, ``do_kv_cache_update``);
+* ``draft``     the draft-step advance (slots of the appended tokens, the
+                lengths grown in place) of multi-step draft decoding.
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``.
 """
 
-from . import formats, plan, qquant, attention, kvwrite  # noqa: F401
+from . import formats, plan, qquant, attention, kvwrite, draft  # noqa: F401

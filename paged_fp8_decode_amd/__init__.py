@@ -16,7 +16,7 @@ import ctypes
 import numpy as np
 
 from ._abi import (  # noqa: F401
-    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, MjError, KV_FORMATS, Q_MODES, SCALE_KINDS,
+    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, DraftArgs, MjError, KV_FORMATS, Q_MODES, SCALE_KINDS,
     MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
 )
 
@@ -126,6 +126,15 @@ def mj_decode_step(cfg: Config, args: StepArgs, stream=None):
 
 def mj_write_kv(cfg: Config, args: WriteArgs, stream=None):
     check(lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_write_kv")
+
+
+def mj_draft_advance(cfg: Config, block_table, seq_lens, num_seqs: int, q_len: int, slot_mapping, stream=None):
+    """Slots of the q_len tokens each sequence appends, then seq_lens += q_len
+    (device tensors: int32 block table and lengths, int64 slot mapping)."""
+    a = DraftArgs(block_table=block_table.data_ptr(), bt_row_stride=block_table.stride(0),
+                  max_blocks_per_seq=block_table.shape[1], seq_lens=seq_lens.data_ptr(), num_seqs=num_seqs,
+                  q_len=q_len, slot_mapping=slot_mapping.data_ptr())
+    check(lib().mj_draft_advance(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)), "mj_draft_advance")
 
 
 def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_len: int, which: int, dense_out,

@@ -8,7 +8,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 6  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 7  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
 KV_FORMATS = {"e4m3": 0, "e2m3": 1, "e3m2": 2, "e2m1": 3, "nvfp4": 4}
 Q_MODES = {"fp8": 0, "bf16": 1}
@@ -83,6 +83,13 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class DraftArgs(ctypes.Structure):
+    _fields_ = [
+        ("block_table", _p), ("bt_row_stride", _i64), ("max_blocks_per_seq", _i32), ("seq_lens", _p),
+        ("num_seqs", _i32), ("q_len", _i32), ("slot_mapping", _p),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -106,6 +113,7 @@ def _load():
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
         "mj_decode_step": (_i32, [P(Config), P(StepArgs), _p]),
         "mj_write_kv": (_i32, [P(Config), P(WriteArgs), _p]),
+        "mj_draft_advance": (_i32, [P(Config), P(DraftArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
         "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),

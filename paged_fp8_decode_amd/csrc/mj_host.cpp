@@ -676,6 +676,26 @@ mj_status mj_write_kv(const mj_config* cfg, const mj_write_args* a, hipStream_t 
   return mj::launch_write_kv(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
+mj_status mj_draft_advance(const mj_config* cfg, const mj_draft_args* a, hipStream_t stream) {
+  mj_status st = check_config(cfg);
+  if (st != MJ_OK) return st;
+  if (!a || !a->block_table || !a->seq_lens || !a->slot_mapping || a->num_seqs < 1 || a->q_len < 1 ||
+      a->max_blocks_per_seq < 1 || a->bt_row_stride < a->max_blocks_per_seq)
+    return MJ_EINVAL;
+  if (a->num_seqs > cfg->max_num_seqs || a->q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  if (!aligned(a->slot_mapping, 8)) return MJ_EALIGN;
+  mj::DraftParams p;
+  p.bt = a->block_table;
+  p.bt_stride = a->bt_row_stride;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.page_shift = ilog2(cfg->page_size);
+  p.seq_lens = a->seq_lens;
+  p.num_seqs = a->num_seqs;
+  p.q_len = a->q_len;
+  p.slots = a->slot_mapping;
+  return mj::launch_draft_advance(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int32_t seq, int32_t head,
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream) {
   mj_status st = check_config(cfg);

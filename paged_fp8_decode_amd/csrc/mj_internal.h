@@ -146,6 +146,18 @@ hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_t
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t s);
+
+// Parameters of the draft-step advance (slot mapping of the appended tokens,
+// seq_lens += q_len).
+struct DraftParams {
+  const int32_t* bt;
+  int64_t bt_stride;
+  int max_blocks, page_shift;
+  int32_t* seq_lens;
+  int num_seqs, q_len;
+  int64_t* slots;
+};
+hipError_t launch_draft_advance(const DraftParams& p, hipStream_t s);
 void set_decode_variant(int variant, int nontemporal);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s);
 hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);

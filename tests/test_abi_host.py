@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 6
+    assert mj.lib().mj_abi_version() == 7
 
 
 def _cfg(**kw):
@@ -333,3 +333,24 @@ def test_gather_probe_scale_pools_need_nvfp4():
     cfg = _cfg(kv_format="nvfp4")
     a = _args(cfg, **dict(_NV, k_block_scale=None))
     assert L.mj_debug_gather_kv(ctypes.byref(cfg), ctypes.byref(a), 0, 0, 16, 2, FAKE, None) == mj.MJ_EINVAL
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_table=None), mj.MJ_EINVAL),
+    (dict(seq_lens=None), mj.MJ_EINVAL),
+    (dict(slot_mapping=None), mj.MJ_EINVAL),
+    (dict(num_seqs=0), mj.MJ_EINVAL),
+    (dict(q_len=0), mj.MJ_EINVAL),
+    (dict(bt_row_stride=4), mj.MJ_EINVAL),
+    (dict(max_blocks_per_seq=0, bt_row_stride=0), mj.MJ_EINVAL),
+    (dict(num_seqs=65), mj.MJ_ECAPACITY),
+    (dict(q_len=3), mj.MJ_ECAPACITY),
+    (dict(slot_mapping=FAKE + 4), mj.MJ_EALIGN),
+])
+def test_draft_advance_errors(kw, status):
+    cfg = _cfg(max_q_len=2)
+    a = dict(block_table=FAKE, bt_row_stride=8, max_blocks_per_seq=8, seq_lens=FAKE, num_seqs=4, q_len=1,
+             slot_mapping=FAKE)
+    a.update(kw)
+    assert mj.lib().mj_draft_advance(ctypes.byref(cfg), ctypes.byref(mj.DraftArgs(**a)), None) == status
