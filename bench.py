@@ -108,6 +108,8 @@ def parse():
     ap.add_argument("--step-merge", type=int, default=0,
                     help="mj_decode_step merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
     ap.add_argument("--no-write", action="store_true", help="skip the KV-cache write measurement")
+    ap.add_argument("--draft", type=int, default=4,
+                    help="draft steps of the multi-step draft loop measured on the workload (0 = skip)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the HBM-counter calibration kernels (256 MiB streaming read, 256 MiB copy) and exit")
     return ap.parse_args()
@@ -293,7 +295,7 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
     del pools
 
     res = dict(
-        workload=wl.spec.name, q_mode=q_mode, kv_bytes=kvb, steps=steps,
+        workload=wl.spec.name, kv_format=wl.spec.kv_format, q_mode=q_mode, kv_bytes=kvb, steps=steps,
         us_per_step_median=float(np.median(step_ms) * 1e3), us_per_step_mean=float(step_ms.mean() * 1e3),
         us_per_step_p10=float(np.percentile(step_ms, 10) * 1e3),
         us_per_step_p90=float(np.percentile(step_ms, 90) * 1e3),
@@ -436,6 +438,104 @@ def cpu_baseline(key, budget_s):
                 seconds_per_step_extrapolated=t_used * len(order) / done)
 
 
+def measure_draft(key, k, reps, flush):
+    """Multi-step draft decode on the workload's shape: k steps of
+    (mj_draft_advance, mj_write_kv of one new K/V row per sequence,
+    mj_decode_step) captured as one hipGraph, timed per replay after the
+    cache eviction (the lengths reset outside the event pair).  Two plans:
+    the pages' host plan made k tokens long once, and each step planning
+    from the live lengths in its own decode launch."""
+    import torch
+    import synth
+    import paged_fp8_decode_amd as mjlib
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+
+    wl = synth.build(synth.spec_for(key), "cuda")
+    s = wl.spec
+    # real pages for the k new positions (the spare block-table columns point at the poison page)
+    bt = wl.block_table.cpu().numpy()
+    used = set(int(x) for x in bt.reshape(-1))
+    free = [p for p in range(wl.num_pages) if p not in used]
+    for i, L in enumerate(wl.seq_lens):
+        for c in range(-(-L // s.page_size), -(-(L + k * s.q_len) // s.page_size)):
+            bt[i, c] = free.pop()
+    wl.block_table.copy_(torch.from_numpy(bt))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    n = s.b * s.q_len
+    kn = torch.randn((k, n, s.h_k, 128), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((k, n, s.h_k, 128), generator=g, device="cuda").to(torch.bfloat16)
+    qn = torch.randn((k, n, s.h_q, 128), generator=g, device="cuda").to(torch.bfloat16)
+    slots = torch.zeros((k, n), dtype=torch.int64, device="cuda")
+    step = DecodeStep.for_workload(wl)
+    out, lse = new_output(wl)
+    lens0 = wl.seq_lens_dev.clone()
+    ks, vs = wl.kv_strides()
+    if s.kv_format in ("e4m3", "nvfp4"):
+        kind, k_sc, v_sc = wl.descale_kind, wl.k_descale, wl.v_descale
+    else:
+        kind, k_sc, v_sc = "channel", wl.k_channel_scale, wl.v_channel_scale
+    wa = []
+    for i in range(k):
+        a = mjlib.WriteArgs(key=kn[i].data_ptr(), key_tok_stride=kn[i].stride(0), key_head_stride=kn[i].stride(1),
+                            value=vn[i].data_ptr(), value_tok_stride=vn[i].stride(0),
+                            value_head_stride=vn[i].stride(1), num_tokens=n, slot_mapping=slots[i].data_ptr(),
+                            k_cache=wl.k_pool.data_ptr(), k_page_stride=ks[0], k_slot_stride=ks[1],
+                            k_head_stride=ks[2], v_cache=wl.v_pool.data_ptr(), v_page_stride=vs[0],
+                            v_slot_stride=vs[1], v_head_stride=vs[2], num_pages=wl.num_pages,
+                            k_scale=k_sc.data_ptr(), k_scale_kind=mjlib.SCALE_KINDS[kind], v_scale=v_sc.data_ptr(),
+                            v_scale_kind=mjlib.SCALE_KINDS[kind])
+        if wl.k_bs_pool is not None:
+            kb, vb = wl.bs_strides()
+            a.k_block_scale, a.v_block_scale = wl.k_bs_pool.data_ptr(), wl.v_bs_pool.data_ptr()
+            a.k_bs_page_stride, a.k_bs_slot_stride, a.k_bs_head_stride = kb
+            a.v_bs_page_stride, a.v_bs_slot_stride, a.v_bs_head_stride = vb
+        wa.append(a)
+
+    def loop(st, in_kernel):
+        for i in range(k):
+            mjlib.mj_draft_advance(step.cfg, wl.block_table, wl.seq_lens_dev, s.b, s.q_len, slots[i], st)
+            mjlib.mj_write_kv(step.cfg, wa[i], st)
+            wl.q = qn[i]
+            info = step.plan_workload_shape(wl) if in_kernel else step.info
+            step.run_workload(wl, out, lse, info=info, stream=st, fused=True, plan_on_device=in_kernel)
+
+    res = dict(k=k, workload=s.name)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for name, in_kernel in (("margin_plan", False), ("in_kernel_plan", True)):
+        if not in_kernel:
+            step.plan(list(wl.seq_lens), s.q_len, wl.block_table.shape[1], margin=k * s.q_len)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            loop(side, in_kernel)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            loop(torch.cuda.current_stream(), in_kernel)
+        stream = torch.cuda.current_stream()
+        ms = []
+        for r in range(reps + 3):
+            wl.seq_lens_dev.copy_(lens0)
+            flush()
+            e0, e1 = E(), E()
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if r >= 3:
+                ms.append(e0.elapsed_time(e1))
+        us = float(np.median(ms) * 1e3)
+        res[name] = dict(us_per_graph=round(us, 2), us_per_draft_step=round(us / k, 2))
+        del gr
+    log(f"[bench] {key}: {k}-step draft loop (advance + KV write + decode step per draft step) in one hipGraph: "
+        f"{res['margin_plan']['us_per_draft_step']:.1f} us per draft step on one margin plan, "
+        f"{res['in_kernel_plan']['us_per_draft_step']:.1f} us planning in the decode launch")
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -472,6 +572,9 @@ def main():
                 w = measure_write(fmt, n_tok, reps, flush)
                 log(f"[bench] mj_write_kv {fmt} {n_tok} tokens x 8 heads: {w['us_per_call']} us, {w['gbs']} GB/s")
                 writes.append(w)
+    draft = None
+    if args.draft > 0:
+        draft = measure_draft(args.workload, args.draft, max(10, args.steps // 2), flush)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     kvb = main_res["kv_bytes"]
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6
@@ -493,7 +596,7 @@ def main():
         higher_is_better=True,
         scaling="weak",
         vs_baseline=None,
-        dtype="e4m3" if "e2m3" not in main_res["workload"] else "e2m3",
+        dtype=main_res["kv_format"],
         data="synthetic",
         config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"], kernel_variant=args.variant,
                     nontemporal=not args.no_nt, step_merge=args.step_merge,
@@ -504,6 +607,7 @@ def main():
         extra=extra,
         bf16_q=bf16q,
         write_kv=writes,
+        draft=draft,
     )
     print(json.dumps(line), flush=True)
 
