@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 7
+#define MJ_ABI_VERSION 8
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -121,6 +121,9 @@ typedef struct mj_config {
   int32_t kv_format;       /* mj_kv_format                                      */
   int32_t min_chunk_tokens;/* floor of a split chunk; 0 = default (below)       */
   int32_t q_mode;          /* mj_q_mode (0 = fp8)                               */
+  int32_t out_f32;         /* 0: outputs `out` are bf16; 1: fp32 (a context-
+                              parallel slice's result, combined later by
+                              mj_combine_lse without rounding in between)    */
 } mj_config;
 /* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):
  * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
@@ -394,6 +397,36 @@ typedef struct mj_draft_args {
   int64_t* slot_mapping;        /* device (num_seqs * q_len,), written          */
 } mj_draft_args;
 mj_status mj_draft_advance(const mj_config* cfg, const mj_draft_args* args, hipStream_t stream);
+
+/* Context-parallel combine (the pages' split-KV reduction, README "What it
+ * does" step 4, across GPUs instead of within one): every GPU of a context-
+ * parallel group holds a slice of each sequence's pages and runs the decode
+ * on it (out_f32 = 1 in its config: fp32 O normalized over the slice, and
+ * its LSE); after one all-gather of those (the caller's collective), this
+ * merges the num_parts slices per (token, query head):
+ *   M = max_p lse_p,  w_p = exp(lse_p - M),
+ *   out = sum_p w_p o_p / sum_p w_p,  lse = M + ln sum_p w_p,
+ * a row no slice saw (every lse_p = -inf) giving out = 0, lse = -inf.  The
+ * slices must partition the context; with q_len > 1 and causal masking the
+ * last slice must hold each sequence's last q_len tokens (it runs causal,
+ * the others non-causal).  Output dtype per cfg->out_f32.
+ * Errors: EINVAL (nulls, num_parts < 1, num_rows < 1, negative strides),
+ * EALIGN (part_out / out not 16-byte aligned or strides not multiples of 4
+ * (fp32) / 8 (bf16) elements), EHIP. */
+typedef struct mj_combine_args {
+  int32_t num_parts;            /* slices (GPUs of the group)                  */
+  int32_t num_rows;             /* tokens: num_seqs * q_len                    */
+  const float* part_out;        /* fp32; slice p, token t, query head h,
+                                   channel c at part_out[p*part_stride +
+                                   t*part_tok_stride + h*part_head_stride + c] */
+  int64_t part_stride, part_tok_stride, part_head_stride;  /* elements         */
+  const float* part_lse;        /* fp32 [num_parts][num_rows][h_q], natural log */
+  void* out;                    /* bf16 or fp32 (cfg->out_f32), (num_rows, h_q,
+                                   128) through the strides                    */
+  int64_t out_tok_stride, out_head_stride;  /* elements                        */
+  float* lse;                   /* nullable [num_rows][h_q]                    */
+} mj_combine_args;
+mj_status mj_combine_lse(const mj_config* cfg, const mj_combine_args* args, hipStream_t stream);
 
 /* Arguments of one whole decode step after the plan: the decode arguments
  * (decode.q8, decode.q_descale and decode.q_bf16 are not read and may be

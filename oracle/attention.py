@@ -110,6 +110,13 @@ def merge(parts):
     return O, lse
 
 
+def combine(parts):
+    """Context-parallel combine of slices given as (O normalized over the
+    slice, LSE): the log-sum-exp merge above with m = LSE and l = 1 (l = 0
+    for a slice that saw no key of the row)."""
+    return merge([(o, lse, np.where(np.isfinite(lse), 1.0, 0.0)) for o, lse in parts])
+
+
 def attend(qrows, K, V, allowed, scale):
     """Textbook softmax attention for one (sequence, KV head): (O, LSE, P)."""
     s = scale * (qrows @ K.T)

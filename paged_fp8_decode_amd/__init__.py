@@ -16,7 +16,8 @@ import ctypes
 import numpy as np
 
 from ._abi import (  # noqa: F401
-    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, DraftArgs, MjError, KV_FORMATS, Q_MODES, SCALE_KINDS,
+    Config, PlanInfo, DecodeArgs, MergeArgs, StepArgs, WriteArgs, DraftArgs, CombineArgs, MjError, KV_FORMATS, Q_MODES,
+    SCALE_KINDS,
     MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP, lib, check, LIB_PATH,
 )
 
@@ -36,12 +37,12 @@ def _ptr(t):
 
 def mj_config(*, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, num_cus=0, wgs_per_cu=0,
               kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128, min_chunk_tokens=0,
-              q_mode="fp8") -> Config:
+              q_mode="fp8", out_f32=False) -> Config:
     c = Config(h_q=h_q, h_k=h_k, head_dim=head_dim, page_size=page_size, max_num_seqs=max_num_seqs,
                max_q_len=max_q_len, max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
                kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, min_chunk_tokens=min_chunk_tokens,
                kv_format=KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format,
-               q_mode=Q_MODES[q_mode] if isinstance(q_mode, str) else q_mode)
+               q_mode=Q_MODES[q_mode] if isinstance(q_mode, str) else q_mode, out_f32=int(bool(out_f32)))
     return c
 
 
@@ -135,6 +136,19 @@ def mj_draft_advance(cfg: Config, block_table, seq_lens, num_seqs: int, q_len: i
                   max_blocks_per_seq=block_table.shape[1], seq_lens=seq_lens.data_ptr(), num_seqs=num_seqs,
                   q_len=q_len, slot_mapping=slot_mapping.data_ptr())
     check(lib().mj_draft_advance(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)), "mj_draft_advance")
+
+
+def mj_combine_lse(cfg: Config, part_out, part_lse, out, lse=None, stream=None):
+    """Merge num_parts context slices: part_out fp32 (parts, rows, h_q, 128)
+    view, part_lse fp32 (parts, rows, h_q) contiguous, out (rows, h_q, 128)
+    in the config's output dtype."""
+    assert part_lse.is_contiguous() and part_out.shape[:3] == part_lse.shape
+    a = CombineArgs(num_parts=part_out.shape[0], num_rows=part_out.shape[1], part_out=part_out.data_ptr(),
+                    part_stride=part_out.stride(0), part_tok_stride=part_out.stride(1),
+                    part_head_stride=part_out.stride(2), part_lse=part_lse.data_ptr(), out=out.data_ptr(),
+                    out_tok_stride=out.stride(0), out_head_stride=out.stride(1),
+                    lse=lse.data_ptr() if lse is not None else None)
+    check(lib().mj_combine_lse(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)), "mj_combine_lse")
 
 
 def mj_debug_gather_kv(cfg: Config, args: DecodeArgs, seq: int, head: int, seq_len: int, which: int, dense_out,

@@ -8,7 +8,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 7  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 8  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
 KV_FORMATS = {"e4m3": 0, "e2m3": 1, "e3m2": 2, "e2m1": 3, "nvfp4": 4}
 Q_MODES = {"fp8": 0, "bf16": 1}
@@ -25,7 +25,7 @@ class MjError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "h_q", "h_k", "head_dim", "page_size", "max_num_seqs", "max_q_len", "max_splits", "num_cus",
-        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens", "q_mode")]
+        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens", "q_mode", "out_f32")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -90,6 +90,14 @@ class DraftArgs(ctypes.Structure):
     ]
 
 
+class CombineArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_parts", _i32), ("num_rows", _i32), ("part_out", _p), ("part_stride", _i64), ("part_tok_stride", _i64),
+        ("part_head_stride", _i64), ("part_lse", _p), ("out", _p), ("out_tok_stride", _i64),
+        ("out_head_stride", _i64), ("lse", _p),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -114,6 +122,7 @@ def _load():
         "mj_decode_step": (_i32, [P(Config), P(StepArgs), _p]),
         "mj_write_kv": (_i32, [P(Config), P(WriteArgs), _p]),
         "mj_draft_advance": (_i32, [P(Config), P(DraftArgs), _p]),
+        "mj_combine_lse": (_i32, [P(Config), P(CombineArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
         "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
     const float l = l_s[r];
     if (single) {
       const float o = l > 0.0f ? acc[k] / l * om : 0.0f;
-      p.out[((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c] = f32_to_bf16(o);
+      store_out(p.out, p.out_f32, ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c, o);
       if (c == 0 && p.lse) p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = l > 0.0f ? (m_s[r] + log2f(l)) * kLn2 : -INFINITY;
     } else if (w < p.part_items) {
       const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + row;

@@ -392,7 +392,7 @@ void decode_stream_kernel(DecodeParams p) {
     const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vd;
     if (single) {
       const float o = Lsum > 0.0f ? O / Lsum * om : 0.0f;
-      p.out[((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + ch] = f32_to_bf16(o);
+      store_out(p.out, p.out_f32, ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + ch, o);
       if (ch == 0 && p.lse)
         p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
     } else if (w < p.part_items) {

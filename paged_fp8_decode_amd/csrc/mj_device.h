@@ -116,6 +116,15 @@ __device__ __forceinline__ uint32_t e2m1_rne(float x) {
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
+// One output element: bf16 (round to nearest even), or fp32 when f32 is set
+// (the buffer is then fp32 with the same element strides).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f);
+__device__ __forceinline__ void store_out(uint16_t* out, int f32, int64_t idx, float v) {
+  if (f32)
+    reinterpret_cast<float*>(out)[idx] = v;
+  else
+    out[idx] = f32_to_bf16(v);
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);

@@ -67,6 +67,7 @@ mj_status check_config(const mj_config* c) {
   if (c->page_size != 16 && c->page_size != 32 && c->page_size != 64 && c->page_size != 128) return MJ_EUNSUPPORTED;
   if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
+  if (c->out_f32 != 0 && c->out_f32 != 1) return MJ_EINVAL;
   // the packed fp6 / fp4 formats take fp8 Q only
   if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3 && c->kv_format != MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if ((int64_t)c->max_q_len * (c->h_q / c->h_k) > kMaxRows) return MJ_ECAPACITY;
@@ -436,6 +437,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->pos_inf = INFINITY;
   p->o_mul = a->o_mul;
   p->out = static_cast<uint16_t*>(a->out);
+  p->out_f32 = cfg->out_f32;
   p->out_ts = a->out_tok_stride;
   p->out_hs = a->out_head_stride;
   p->lse = a->lse;
@@ -596,6 +598,7 @@ mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t
   p.nqp = d.nq_max;
   p.part_items = d.slots_max;
   p.out = static_cast<uint16_t*>(a->out);
+  p.out_f32 = cfg->out_f32;
   p.out_ts = a->out_tok_stride;
   p.out_hs = a->out_head_stride;
   p.lse = a->lse;
@@ -694,6 +697,34 @@ mj_status mj_draft_advance(const mj_config* cfg, const mj_draft_args* a, hipStre
   p.q_len = a->q_len;
   p.slots = a->slot_mapping;
   return mj::launch_draft_advance(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+}
+
+mj_status mj_combine_lse(const mj_config* cfg, const mj_combine_args* a, hipStream_t stream) {
+  mj_status st = check_config(cfg);
+  if (st != MJ_OK) return st;
+  if (!a || !a->part_out || !a->part_lse || !a->out || a->num_parts < 1 || a->num_rows < 1) return MJ_EINVAL;
+  if (a->part_stride < 0 || a->part_tok_stride < 0 || a->part_head_stride < 0 || a->out_tok_stride < 0 ||
+      a->out_head_stride < 0)
+    return MJ_EINVAL;
+  const int64_t om = cfg->out_f32 ? 4 : 8;
+  if (!aligned(a->part_out, 16) || a->part_stride % 4 || a->part_tok_stride % 4 || a->part_head_stride % 4 ||
+      !aligned(a->out, 16) || a->out_tok_stride % om || a->out_head_stride % om)
+    return MJ_EALIGN;
+  mj::CombineParams p;
+  p.po = a->part_out;
+  p.p_ps = a->part_stride;
+  p.p_ts = a->part_tok_stride;
+  p.p_hs = a->part_head_stride;
+  p.plse = a->part_lse;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.out_ts = a->out_tok_stride;
+  p.out_hs = a->out_head_stride;
+  p.out_f32 = cfg->out_f32;
+  p.lse = a->lse;
+  p.parts = a->num_parts;
+  p.rows = a->num_rows;
+  p.h_q = cfg->h_q;
+  return mj::launch_combine(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
 
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int32_t seq, int32_t head,

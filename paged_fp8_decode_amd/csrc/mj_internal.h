@@ -45,8 +45,9 @@ struct DecodeParams {
                                // is one instruction only while the compiler
                                // cannot fold the third operand
   const float* o_mul;          // nullable (h_q, 128)
-  uint16_t* out;               // bf16
+  uint16_t* out;               // bf16, or fp32 when out_f32 (strides in elements)
   int64_t out_ts, out_hs;
+  int out_f32;
   float* lse;                  // nullable
   int num_seqs, q_len, h_q, h_k, h_r, n_q;
   int page_size, page_shift, kv_tile;
@@ -94,6 +95,7 @@ struct MergeParams {
   int part_items;
   uint16_t* out;
   int64_t out_ts, out_hs;
+  int out_f32;
   float* lse;
   int num_seqs, q_len, h_q, h_k, h_r, n_q;
 };
@@ -158,6 +160,19 @@ struct DraftParams {
   int64_t* slots;
 };
 hipError_t launch_draft_advance(const DraftParams& p, hipStream_t s);
+
+// Parameters of the context-parallel combine.
+struct CombineParams {
+  const float* po;
+  int64_t p_ps, p_ts, p_hs;  // elements
+  const float* plse;         // [parts][rows][h_q]
+  uint16_t* out;             // bf16 or fp32 (out_f32)
+  int64_t out_ts, out_hs;
+  int out_f32;
+  float* lse;
+  int parts, rows, h_q;
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 void set_decode_variant(int variant, int nontemporal);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s);
 hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);

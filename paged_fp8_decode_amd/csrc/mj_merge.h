@@ -110,10 +110,15 @@ __device__ __forceinline__ void merge_one(const MergeParams& p, int seq, int g, 
       const int t = r / p.h_r;
       const int h = g * p.h_r + (r - t * p.h_r);
       const float dn = den[u];
-      const uint32_t b0 = f32_to_bf16(seen ? num[u].x / dn : 0.0f), b1 = f32_to_bf16(seen ? num[u].y / dn : 0.0f);
-      const uint32_t b2 = f32_to_bf16(seen ? num[u].z / dn : 0.0f), b3 = f32_to_bf16(seen ? num[u].w / dn : 0.0f);
-      *reinterpret_cast<uint2*>(p.out + ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c4) =
-          make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      const float o0 = seen ? num[u].x / dn : 0.0f, o1 = seen ? num[u].y / dn : 0.0f;
+      const float o2 = seen ? num[u].z / dn : 0.0f, o3 = seen ? num[u].w / dn : 0.0f;
+      const int64_t oi = ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + c4;
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + oi) = make_float4(o0, o1, o2, o3);
+      } else {
+        const uint32_t b0 = f32_to_bf16(o0), b1 = f32_to_bf16(o1), b2 = f32_to_bf16(o2), b3 = f32_to_bf16(o3);
+        *reinterpret_cast<uint2*>(p.out + oi) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      }
       if (c4 == 0 && p.lse)
         p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = seen ? (M[u] + log2f(dn)) * kLn2 : -INFINITY;
     }

@@ -19,6 +19,7 @@ from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, StepArgs, check, mj
 class DecodeStep:
     def __init__(self, *, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, kv_format="e4m3",
                  num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, min_chunk_tokens=0, q_mode="fp8",
+                 out_f32=False,
                  device="cuda"):
         self.device = torch.device(device)
         if num_cus == 0:
@@ -26,7 +27,7 @@ class DecodeStep:
         self.cfg = mj_config(h_q=h_q, h_k=h_k, page_size=page_size, max_num_seqs=max_num_seqs, max_q_len=max_q_len,
                              max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
                              kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, kv_format=kv_format,
-                             min_chunk_tokens=min_chunk_tokens, q_mode=q_mode)
+                             min_chunk_tokens=min_chunk_tokens, q_mode=q_mode, out_f32=out_f32)
         check(mj_config_check(self.cfg), "mj_config_check")
         self.h_q, self.h_k, self.h_r = h_q, h_k, h_q // h_k
         self.max_q_len = max_q_len
@@ -190,9 +191,9 @@ class DecodeStep:
                         plan_on_device=plan_on_device)
 
 
-def new_output(wl, device=None):
+def new_output(wl, device=None, out_f32=False):
     s = wl.spec
     dev = device or wl.q.device
-    out = torch.empty(s.b * s.q_len, s.h_q, 128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(s.b * s.q_len, s.h_q, 128, dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
     lse = torch.empty(s.b * s.q_len, s.h_q, dtype=torch.float32, device=dev)
     return out, lse

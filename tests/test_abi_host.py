@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 7
+    assert mj.lib().mj_abi_version() == 8
 
 
 def _cfg(**kw):
@@ -354,3 +354,31 @@ def test_draft_advance_errors(kw, status):
              slot_mapping=FAKE)
     a.update(kw)
     assert mj.lib().mj_draft_advance(ctypes.byref(cfg), ctypes.byref(mj.DraftArgs(**a)), None) == status
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,f32", [
+    (dict(part_out=None), mj.MJ_EINVAL, 0),
+    (dict(part_lse=None), mj.MJ_EINVAL, 0),
+    (dict(out=None), mj.MJ_EINVAL, 0),
+    (dict(num_parts=0), mj.MJ_EINVAL, 0),
+    (dict(num_rows=0), mj.MJ_EINVAL, 0),
+    (dict(part_tok_stride=-4), mj.MJ_EINVAL, 0),
+    (dict(part_out=FAKE + 4), mj.MJ_EALIGN, 0),
+    (dict(part_head_stride=130), mj.MJ_EALIGN, 0),
+    (dict(out_head_stride=132), mj.MJ_EALIGN, 0),
+    (dict(out_head_stride=130), mj.MJ_EALIGN, 1),
+])
+def test_combine_errors(kw, status, f32):
+    cfg = _cfg(out_f32=f32)
+    a = dict(num_parts=8, num_rows=4, part_out=FAKE, part_stride=4 * 32 * 128, part_tok_stride=32 * 128,
+             part_head_stride=128, part_lse=FAKE, out=FAKE, out_tok_stride=32 * 128, out_head_stride=128, lse=None)
+    a.update(kw)
+    assert mj.lib().mj_combine_lse(ctypes.byref(cfg), ctypes.byref(mj.CombineArgs(**a)), None) == status
+
+
+def test_out_f32_config_values():
+    assert mj.mj_config_check(_cfg(out_f32=1)) == mj.MJ_OK
+    c = _cfg()
+    c.out_f32 = 2
+    assert mj.mj_config_check(c) == mj.MJ_EINVAL

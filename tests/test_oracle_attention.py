@@ -217,3 +217,33 @@ def test_descale_kinds_scale_linearly():
     h2 = dict(h, v_descale=h["v_descale"] * 2.0)
     O2, _ = A.decode_step(h2, causal=True, **_args(wl))
     assert np.max(np.abs(O2 - 2.0 * O)) < 1e-12
+
+
+@pytest.mark.parametrize("G", [2, 3, 8])
+def test_context_parallel_combine_is_full_attention(G):
+    """Attention over contiguous slices of the context, each normalized with
+    its own LSE, combined by the LSE merge, equals attention over the whole
+    context (slices may be empty; the last slice holds the causal tail)."""
+    wl, h = _small("cfg4c")
+    s = wl.spec
+    from oracle.qquant import quantize_q
+    codes, qd = quantize_q(h["q"], s.b, s.q_len, s.h_k, h["q_mul"])
+    for i in range(s.b):
+        for g in range(s.h_k):
+            qrows, K, V = A.head_inputs(h, i, g, q_codes=codes, q_descale=qd, **_args(wl))
+            L = K.shape[0]
+            allowed = A.visible(L, s.q_len, s.h_r, s.causal)
+            O, LSE, _ = A.attend(qrows, K, V, allowed, h["softmax_scale"])
+            cuts = np.linspace(0, L - s.q_len, G).astype(int).tolist() + [L]  # last slice: the q_len tail and more
+            cuts[0] = 0
+            parts = []
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                o, lse, _ = A.attend(qrows, K[a:b], V[a:b], allowed[:, a:b], h["softmax_scale"])
+                parts.append((o, lse))
+            Oc, LSEc = A.combine(parts)
+            assert np.max(np.abs(Oc - O)) < 1e-12
+            assert np.max(np.abs(LSEc - LSE)) < 1e-12
+    # a row no slice saw: O = 0, LSE = -inf
+    e = np.zeros((2, 128))
+    Oc, LSEc = A.combine([(e, np.array([-np.inf, 0.0])), (e + 1.0, np.array([-np.inf, -np.inf]))])
+    assert np.all(Oc[0] == 0) and LSEc[0] == -np.inf and np.all(Oc[1] == 0) and LSEc[1] == 0.0
