@@ -108,6 +108,9 @@ def parse():
     ap.add_argument("--step-merge", type=int, default=0,
                     help="mj_decode_step merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
     ap.add_argument("--no-write", action="store_true", help="skip the KV-cache write measurement")
+    ap.add_argument("--cp", default="cfg3:8",
+                    help="context-parallel share measured as WORKLOAD:G (one GPU's slice of each context, "
+                         "and the combine of G slices); '' = skip")
     ap.add_argument("--draft", type=int, default=4,
                     help="draft steps of the multi-step draft loop measured on the workload (0 = skip)")
     ap.add_argument("--calibrate", action="store_true",
@@ -438,6 +441,90 @@ def cpu_baseline(key, budget_s):
                 seconds_per_step_extrapolated=t_used * len(order) / done)
 
 
+def measure_cp(key, G, reps, flush):
+    """Context parallelism on one GPU: the workload's pages cut into G
+    end-aligned slices (rank r's share of each context), each slice's fused
+    step (fp32 output and LSE) timed after the cache eviction, and
+    mj_combine_lse over the G results; the all-gather between them (RCCL)
+    is not run here: its bytes per GPU are reported."""
+    import torch
+    import synth
+    import paged_fp8_decode_amd as mjlib
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+
+    wl = synth.build(synth.spec_for(key), "cuda")
+    s = wl.spec
+    P = s.page_size
+    bt = wl.block_table.cpu().numpy()
+    lens = list(wl.seq_lens)
+    pages = [max(1, -(-L // P)) if L else 0 for L in lens]
+    chunk = [max(1, -(-p // G)) if p else 0 for p in pages]
+    cols = max(1, max(chunk))
+    rows = s.b * s.q_len
+    part_o = torch.empty((G, rows, s.h_q, 128), dtype=torch.float32, device="cuda")
+    part_l = torch.empty((G, rows, s.h_q), dtype=torch.float32, device="cuda")
+    step = DecodeStep.for_workload(wl, out_f32=True)
+    ks, vs = wl.kv_strides()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    stream = torch.cuda.current_stream()
+    rank_us, rank_kv = [], []
+    for r in range(G):
+        bt_r = np.tile(bt[:, :1], (1, cols)).astype(np.int32)
+        lens_r = np.zeros(s.b, dtype=np.int32)
+        for i, L in enumerate(lens):
+            hi = max(0, pages[i] - (G - 1 - r) * chunk[i]) if L else 0
+            lo = max(0, hi - chunk[i])
+            if hi > lo:
+                bt_r[i, :hi - lo] = bt[i, lo:hi]
+                lens_r[i] = min(hi * P, L) - lo * P
+        bt_d = torch.from_numpy(bt_r).to("cuda")
+        lens_d = torch.from_numpy(lens_r).to("cuda")
+        info = step.plan(lens_r.tolist(), s.q_len, cols)
+
+        def run():
+            step.run(q=wl.q, k_cache=wl.k_pool, v_cache=wl.v_pool, k_strides=ks, v_strides=vs, num_pages=wl.num_pages,
+                     block_table=bt_d, seq_lens=lens_d, k_descale=wl.k_descale, v_descale=wl.v_descale,
+                     descale_kind=wl.descale_kind, softmax_scale=wl.softmax_scale, out=part_o[r], lse=part_l[r],
+                     q_mul=wl.q_mul, o_mul=wl.o_mul, causal=s.causal and r == G - 1, info=info, stream=stream,
+                     fused=True)
+        ms = []
+        for k in range(reps + 2):
+            flush()
+            e0, e1 = E(), E()
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if k >= 2:
+                ms.append(e0.elapsed_time(e1))
+        rank_us.append(float(np.median(ms) * 1e3))
+        rank_kv.append(int(lens_r.sum()) * s.h_k * 2 * (s.row_bytes + s.scale_row_bytes))
+    cfg = mjlib.mj_config(h_q=s.h_q, h_k=s.h_k, page_size=P, max_num_seqs=s.b)
+    out, lse = new_output(wl)
+    ms = []
+    for k in range(reps + 2):
+        flush()
+        e0, e1 = E(), E()
+        e0.record(stream)
+        mjlib.mj_combine_lse(cfg, part_o, part_l, out, lse, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if k >= 2:
+            ms.append(e0.elapsed_time(e1))
+    comb = float(np.median(ms) * 1e3)
+    res = dict(workload=s.name, G=G, slice_step_us=[round(x, 1) for x in rank_us],
+               slice_step_us_max=round(max(rank_us), 1), slice_kv_bytes=rank_kv,
+               slice_kv_gbs_of_slowest=round(rank_kv[int(np.argmax(rank_us))] / max(rank_us) / 1e3, 1),
+               combine_us=round(comb, 1), allgather_bytes_per_gpu=rows * s.h_q * (128 + 1) * 4,
+               note="one GPU's share and the combine; the RCCL all-gather between them is not run")
+    log(f"[bench] {key} context-parallel share G={G}: slice steps {min(rank_us):.1f}-{max(rank_us):.1f} us "
+        f"(KV {min(rank_kv) / 1e6:.0f}-{max(rank_kv) / 1e6:.0f} MB per slice), combine of {G} slices "
+        f"{comb:.1f} us, all-gather {res['allgather_bytes_per_gpu'] / 1e6:.2f} MB per GPU")
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_draft(key, k, reps, flush):
     """Multi-step draft decode on the workload's shape: k steps of
     (mj_draft_advance, mj_write_kv of one new K/V row per sequence,
@@ -572,6 +659,10 @@ def main():
                 w = measure_write(fmt, n_tok, reps, flush)
                 log(f"[bench] mj_write_kv {fmt} {n_tok} tokens x 8 heads: {w['us_per_call']} us, {w['gbs']} GB/s")
                 writes.append(w)
+    cp = None
+    if args.cp:
+        cp_key, cp_g = args.cp.split(":")
+        cp = measure_cp(cp_key, int(cp_g), max(10, args.steps // 2), flush)
     draft = None
     if args.draft > 0:
         draft = measure_draft(args.workload, args.draft, max(10, args.steps // 2), flush)
@@ -608,6 +699,7 @@ def main():
         bf16_q=bf16q,
         write_kv=writes,
         draft=draft,
+        context_parallel=cp,
     )
     print(json.dumps(line), flush=True)
 

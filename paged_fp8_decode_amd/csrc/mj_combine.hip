@@ -16,8 +16,12 @@ namespace {
 
 constexpr int kCThreads = 256;
 
-
 // One thread per (token, query head, 4 channels): 32 threads cover a row.
+// Slices are taken kB at a time with all their loads issued together; a
+// running maximum rescales the sums between batches (one batch, every group
+// of up to kB GPUs, is exactly the formula above).
+constexpr int kB = 8;
+
 __global__ __launch_bounds__(kCThreads) void combine_kernel(CombineParams p) {
   const int64_t tid = (int64_t)blockIdx.x * kCThreads + threadIdx.x;
   const int64_t rows_h = (int64_t)p.rows * p.h_q;
@@ -25,22 +29,39 @@ __global__ __launch_bounds__(kCThreads) void combine_kernel(CombineParams p) {
   const int64_t rh = tid >> 5;
   const int c4 = (int)(tid & 31) * 4;
   const int t = (int)(rh / p.h_q), h = (int)(rh - (int64_t)t * p.h_q);
-  float M = -INFINITY;
-  for (int q = 0; q < p.parts; ++q) M = fmaxf(M, p.plse[((int64_t)q * p.rows + t) * p.h_q + h]);
+  float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  float den = 0.0f;
-  if (M != -INFINITY) {
-    for (int q = 0; q < p.parts; ++q) {
-      const float lq = p.plse[((int64_t)q * p.rows + t) * p.h_q + h];
-      if (lq == -INFINITY) continue;  // the slice saw no key of this row
-      const float w = expf(lq - M);
-      const float4 o = *reinterpret_cast<const float4*>(p.po + q * p.p_ps + t * p.p_ts + h * p.p_hs + c4);
-      den += w;
-      num.x += w * o.x;
-      num.y += w * o.y;
-      num.z += w * o.z;
-      num.w += w * o.w;
+  for (int q0 = 0; q0 < p.parts; q0 += kB) {
+    float l[kB];
+    float4 o[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int q = q0 + j;
+      l[j] = q < p.parts ? p.plse[((int64_t)q * p.rows + t) * p.h_q + h] : -INFINITY;
+      o[j] = q < p.parts ? *reinterpret_cast<const float4*>(p.po + q * p.p_ps + t * p.p_ts + h * p.p_hs + c4)
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) bm = fmaxf(bm, l[j]);
+    if (bm == -INFINITY) continue;  // no slice so far saw a key of this row
+    const float a = expf(M - bm);   // M = -inf -> 0
+    den *= a;
+    num.x *= a;
+    num.y *= a;
+    num.z *= a;
+    num.w *= a;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      if (l[j] == -INFINITY) continue;  // the slice saw no key of this row (its O is 0)
+      const float w = expf(l[j] - bm);
+      den += w;
+      num.x += w * o[j].x;
+      num.y += w * o[j].y;
+      num.z += w * o[j].z;
+      num.w += w * o[j].w;
+    }
+    M = bm;
   }
   const bool seen = M != -INFINITY;
   const float o0 = seen ? num.x / den : 0.0f, o1 = seen ? num.y / den : 0.0f;

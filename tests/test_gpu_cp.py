@@ -88,6 +88,18 @@ def test_context_parallel_slices_combine_to_full_attention(mj, gpu, key, G):
     compare_lse(lse, LSE, f"{key} G={G}")
 
 
+@pytest.mark.parametrize("key", ["cfg3", "cfg4c"])
+def test_more_slices_than_one_combine_batch(mj, gpu, key):
+    """11 slices: the combine takes them in two batches with a running
+    maximum between (several slices of a short sequence are empty)."""
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    say(f"context parallel {wl.spec.name} G=11")
+    out, lse, _, _ = run_cp(mj, wl, 11, gpu, min_chunk_tokens=1)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, f"{key} G=11")
+    compare_lse(lse, LSE, f"{key} G=11")
+
+
 def test_fp32_output_matches_bf16_output(mj, gpu):
     """out_f32 changes only the output rounding: the fp32 result rounded to
     bf16 is the bf16 result, on the matrix-core and generic kernels, split
