@@ -52,12 +52,12 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "c9b8c3cdc9506ced",
-    "cfg2": dict(fetch_bytes=269311261, write_bytes=1180000),
-    "32k": dict(fetch_bytes=4297916945, write_bytes=4718974),
-    "cfg5": dict(fetch_bytes=806135702, write_bytes=589835),
-    "cfg5_e2m1": dict(fetch_bytes=538224434, write_bytes=1179671),
-    "cfg5_nvfp4": dict(fetch_bytes=604657040, write_bytes=1179671),
+    "sources_sha256_16": "18479a67768f2ee6",
+    "cfg2": dict(fetch_bytes=269321405, write_bytes=1179995),
+    "32k": dict(fetch_bytes=4297924139, write_bytes=4718971),
+    "cfg5": dict(fetch_bytes=806134069, write_bytes=589835),
+    "cfg5_e2m1": dict(fetch_bytes=538135781, write_bytes=1179671),
+    "cfg5_nvfp4": dict(fetch_bytes=604685881, write_bytes=1179671),
 }
 
 
