@@ -86,22 +86,23 @@ def _write_args(mj, wl, key, value, slots):
     return a
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg5", "cfg5_nvfp4"])
-def test_draft_loop_graph_on_one_margin_plan(mj, gpu, key):
+@pytest.mark.parametrize("key,q_len", [("cfg2", 1), ("cfg5", 1), ("cfg5_nvfp4", 1), ("cfg2", 4)])
+def test_draft_loop_graph_on_one_margin_plan(mj, gpu, key, q_len):
+    """q_len = 4: each draft step appends a causal block of four tokens."""
     from oracle.attention import decode_step
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
     k = 4
     lens0 = (1000, 2048, 0, 777)  # a padding request stays empty
-    wl = synth.build(synth.spec_for(key, small=True, b=4, lens=lens0, extra_bt_cols=2), gpu)
+    wl = synth.build(synth.spec_for(key, small=True, b=4, lens=lens0, extra_bt_cols=2, q_len=q_len), gpu)
     s = wl.spec
-    assert s.q_len == 1 and (s.b * s.q_len) == 4
-    _grow_block_table(wl, k)
+    n = s.b * q_len
+    _grow_block_table(wl, k * q_len)
     g = torch.Generator(device=gpu)
     g.manual_seed(20260 + len(key))
-    kn = (torch.randn((k, s.b, s.h_k, 128), generator=g, device=gpu) * 1.5).to(torch.bfloat16)
-    vn = torch.randn((k, s.b, s.h_k, 128), generator=g, device=gpu).to(torch.bfloat16)
-    qn = torch.randn((k, s.b, s.h_q, 128), generator=g, device=gpu).to(torch.bfloat16)
-    slots = torch.zeros((k, s.b), dtype=torch.int64, device=gpu)
+    kn = (torch.randn((k, n, s.h_k, 128), generator=g, device=gpu) * 1.5).to(torch.bfloat16)
+    vn = torch.randn((k, n, s.h_k, 128), generator=g, device=gpu).to(torch.bfloat16)
+    qn = torch.randn((k, n, s.h_q, 128), generator=g, device=gpu).to(torch.bfloat16)
+    slots = torch.zeros((k, n), dtype=torch.int64, device=gpu)
     step = DecodeStep.for_workload(wl, min_chunk_tokens=1)
     pools0 = [t.clone() for t in (wl.k_pool, wl.v_pool, wl.k_bs_pool, wl.v_bs_pool) if t is not None]
     lens0_d = wl.seq_lens_dev.clone()
@@ -115,14 +116,14 @@ def test_draft_loop_graph_on_one_margin_plan(mj, gpu, key):
 
     def loop(stream, info_per_step=None):
         for st_i in range(k):
-            mj.mj_draft_advance(step.cfg, wl.block_table, wl.seq_lens_dev, s.b, 1, slots[st_i], stream)
+            mj.mj_draft_advance(step.cfg, wl.block_table, wl.seq_lens_dev, s.b, q_len, slots[st_i], stream)
             mj.mj_write_kv(step.cfg, _write_args(mj, wl, kn[st_i], vn[st_i], slots[st_i]), stream)
             wl.q = qn[st_i]
             info = info_per_step[st_i] if info_per_step else None
             step.run_workload(wl, outs[st_i][0], outs[st_i][1], info=info, stream=stream, fused=True)
 
     # one plan, k tokens long, before capture
-    margin_info = step.plan(list(lens0), 1, wl.block_table.shape[1], margin=k)
+    margin_info = step.plan(list(lens0), q_len, wl.block_table.shape[1], margin=k * q_len)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -145,7 +146,7 @@ def test_draft_loop_graph_on_one_margin_plan(mj, gpu, key):
         graph.replay()
         torch.cuda.synchronize()
         replays.append([(o.clone(), l.clone()) for o, l in outs])
-        assert wl.seq_lens_dev.cpu().tolist() == [L + k if L else 0 for L in lens0]
+        assert wl.seq_lens_dev.cpu().tolist() == [L + k * q_len if L else 0 for L in lens0]
     for r in (1, 2):
         for st_i in range(k):
             assert torch.equal(replays[r][st_i][0].view(torch.int16), replays[0][st_i][0].view(torch.int16))
@@ -156,9 +157,9 @@ def test_draft_loop_graph_on_one_margin_plan(mj, gpu, key):
     h = wl.host()
     for st_i in range(k):
         hi = dict(h)
-        hi["seq_lens"] = np.array([L + st_i + 1 if L else 0 for L in lens0], dtype=np.int64)
+        hi["seq_lens"] = np.array([L + (st_i + 1) * q_len if L else 0 for L in lens0], dtype=np.int64)
         hi["q"] = qn[st_i].float().cpu().numpy()
-        O, LSE = decode_step(hi, q_len=1, h_q=s.h_q, h_k=s.h_k, d=s.d, page_size=s.page_size, kv_format=s.kv_format,
+        O, LSE = decode_step(hi, q_len=q_len, h_q=s.h_q, h_k=s.h_k, d=s.d, page_size=s.page_size, kv_format=s.kv_format,
                              causal=s.causal)
         say(f"draft {key} step {st_i}: lens={hi['seq_lens'].tolist()} plan work={margin_info.num_work}")
         compare_out(replays[0][st_i][0], O, f"{key} graph step {st_i}")
@@ -169,10 +170,11 @@ def test_draft_loop_graph_on_one_margin_plan(mj, gpu, key):
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     for st_i in range(k):
-        mj.mj_draft_advance(step.cfg, wl.block_table, wl.seq_lens_dev, s.b, 1, slots[st_i], st)
+        mj.mj_draft_advance(step.cfg, wl.block_table, wl.seq_lens_dev, s.b, q_len, slots[st_i], st)
         mj.mj_write_kv(step.cfg, _write_args(mj, wl, kn[st_i], vn[st_i], slots[st_i]), st)
         wl.q = qn[st_i]
-        info = step.plan([L + st_i + 1 if L else 0 for L in lens0], 1, wl.block_table.shape[1], stream=st)
+        info = step.plan([L + (st_i + 1) * q_len if L else 0 for L in lens0], q_len, wl.block_table.shape[1],
+                         stream=st)
         step.run_workload(wl, outs[st_i][0], outs[st_i][1], info=info, stream=st, fused=True)
         torch.cuda.synchronize()
         compare_out(outs[st_i][0], replays[0][st_i][0].float().cpu().numpy().astype(np.float64),
