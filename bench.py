@@ -53,7 +53,7 @@ if ROOT not in sys.path:
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
     "sources_sha256_16": "18479a67768f2ee6",
-    "cfg2": dict(fetch_bytes=269321405, write_bytes=1179995),
+    "cfg2": dict(fetch_bytes=269323231, write_bytes=1179999),
     "32k": dict(fetch_bytes=4297924139, write_bytes=4718971),
     "cfg5": dict(fetch_bytes=806134069, write_bytes=589835),
     "cfg5_e2m1": dict(fetch_bytes=538135781, write_bytes=1179671),
@@ -359,7 +359,8 @@ def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
     codes out, 8-byte slots) against the HBM peak."""
     import torch
     import paged_fp8_decode_amd as mjlib
-    row = 128 if kv_format == "e4m3" else 96
+    row = {"e4m3": 128, "e2m3": 96, "e3m2": 96, "e2m1": 64, "nvfp4": 64}[kv_format]
+    srow = 8 if kv_format == "nvfp4" else 0  # nvfp4 block-scale bytes per row
     pages = max(16, -(-2 * n_tokens // page_size))
     g = torch.Generator(device="cuda").manual_seed(77)
     key = torch.randn(n_tokens, h_k, 128, generator=g, device="cuda").to(torch.bfloat16)
@@ -368,9 +369,10 @@ def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
     k_pool = torch.zeros(pages * page_size * h_k * row, dtype=torch.uint8, device="cuda")
     v_pool = torch.zeros_like(k_pool)
     st = (h_k * page_size * row, row, page_size * row)  # HND
-    kind = "head" if kv_format == "e4m3" else "channel"
+    kind = "head" if kv_format in ("e4m3", "nvfp4") else "channel"
     n_sc = h_k if kind == "head" else h_k * 128
-    k_sc = torch.full((n_sc,), 4.0 / (448.0 if kv_format == "e4m3" else 7.5), device="cuda")
+    fmax = {"e4m3": 448.0, "e2m3": 7.5, "e3m2": 28.0, "e2m1": 6.0, "nvfp4": 6.0 * 448.0}[kv_format]
+    k_sc = torch.full((n_sc,), 4.0 / fmax, device="cuda")
     v_sc = k_sc.clone()
     cfg = mjlib.mj_config(h_q=h_k, h_k=h_k, page_size=page_size, max_num_seqs=1, kv_format=kv_format)
     kk = mjlib.SCALE_KINDS[kind]
@@ -381,6 +383,13 @@ def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
                         v_cache=v_pool.data_ptr(), v_page_stride=st[0], v_slot_stride=st[1], v_head_stride=st[2],
                         num_pages=pages, k_scale=k_sc.data_ptr(), k_scale_kind=kk, v_scale=v_sc.data_ptr(),
                         v_scale_kind=kk)
+    if srow:
+        k_bs = torch.zeros(pages * page_size * h_k * srow, dtype=torch.uint8, device="cuda")
+        v_bs = torch.zeros_like(k_bs)
+        bst = (h_k * page_size * srow, srow, page_size * srow)
+        a.k_block_scale, a.v_block_scale = k_bs.data_ptr(), v_bs.data_ptr()
+        a.k_bs_page_stride, a.k_bs_slot_stride, a.k_bs_head_stride = bst
+        a.v_bs_page_stride, a.v_bs_slot_stride, a.v_bs_head_stride = bst
     stream = torch.cuda.current_stream()
     for _ in range(3):
         mjlib.mj_write_kv(cfg, a, stream)
@@ -392,7 +401,7 @@ def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    nbytes = n_tokens * h_k * 2 * (2 * 128 + row) + 8 * n_tokens
+    nbytes = n_tokens * h_k * 2 * (2 * 128 + row + srow) + 8 * n_tokens
     return dict(kv_format=kv_format, tokens=n_tokens, h_k=h_k, us_per_call=round(us, 2),
                 algorithmic_bytes=nbytes, gbs=round(nbytes / us / 1e3, 1),
                 frac_of_hbm_peak=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4))
@@ -654,7 +663,7 @@ def main():
                            q_mode="bf16")
     writes = []
     if not args.no_write:
-        for fmt in ("e4m3", "e2m3"):
+        for fmt in ("e4m3", "e2m3", "e3m2", "e2m1", "nvfp4"):
             for n_tok, reps in ((16384, 20), (32, 200)):
                 w = measure_write(fmt, n_tok, reps, flush)
                 log(f"[bench] mj_write_kv {fmt} {n_tok} tokens x 8 heads: {w['us_per_call']} us, {w['gbs']} GB/s")
