@@ -88,6 +88,18 @@ def test_context_parallel_slices_combine_to_full_attention(mj, gpu, key, G):
     compare_lse(lse, LSE, f"{key} G={G}")
 
 
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5_nvfp4"])
+def test_context_parallel_with_bf16_q(mj, gpu, key):
+    """The slices decoded in bf16-Q mode (Q as given, KV converted in the
+    kernel), fp32 output, combined."""
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    say(f"context parallel bf16 Q {wl.spec.name} G=4")
+    out, lse, _, _ = run_cp(mj, wl, 4, gpu, q_mode="bf16", min_chunk_tokens=1)
+    O, LSE = oracle_step(wl, quantize=False)
+    compare_out(out, O, f"{key} bf16 Q G=4")
+    compare_lse(lse, LSE, f"{key} bf16 Q G=4")
+
+
 @pytest.mark.parametrize("key", ["cfg3", "cfg4c"])
 def test_more_slices_than_one_combine_batch(mj, gpu, key):
     """11 slices: the combine takes them in two batches with a running
