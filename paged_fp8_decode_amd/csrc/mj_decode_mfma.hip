@@ -733,20 +733,31 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ int last_s;
 
   // head-major grids put the KV heads of one work item in consecutive
-  // workgroups, so they are resident together
-  int w, g;
+  // workgroups, so they are resident together.  The head index hc counts
+  // (KV head, row tile) pairs, row tiles innermost: every tile of a group
+  // reads the same KV rows
+  int w, hc;
   if (p.head_major == 2) {
     // XCD-grouped: workgroup L runs on XCD L % 8; the heads of item w are
-    // L = (w / 8) * 8 h_k + 8 g + w % 8, one XCD, dispatched close together
-    const int L = blockIdx.x, per = kXcds * p.h_k;
+    // L = (w / 8) * 8 H + 8 hc + w % 8 (H = h_k * row_tiles), one XCD,
+    // dispatched close together
+    const int L = blockIdx.x, per = kXcds * p.h_k * p.row_tiles;
     const int chunk = L / per, r = L - chunk * per;
-    g = r / kXcds;
-    w = chunk * kXcds + (r - g * kXcds);
+    hc = r / kXcds;
+    w = chunk * kXcds + (r - hc * kXcds);
     if (w >= p.num_work) return;  // padding of the last chunk
   } else {
     w = p.head_major ? blockIdx.y : blockIdx.x;
-    g = p.head_major ? blockIdx.x : blockIdx.y;
+    hc = p.head_major ? blockIdx.x : blockIdx.y;
   }
+  int g = hc, rt = 0;
+  if (p.row_tiles > 1) {
+    g = hc / p.row_tiles;
+    rt = hc - g * p.row_tiles;
+  }
+  // this workgroup's rows of the group: [row0, row0 + nq), nq >= 1
+  const int row0 = rt * kRows;
+  const int nq = min(kRows, p.n_q - row0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, jj = lane >> 4;
@@ -766,7 +777,7 @@ void decode_mfma_kernel(DecodeParams p) {
     single = __builtin_amdgcn_readfirstlane(it.n) <= 1;
     plan_n = it.n;
     plan_begin = it.begin;
-    plan_writer = it.split == 0 && g == 0;
+    plan_writer = it.split == 0 && g == 0 && rt == 0;
   } else {
     seq = p.work[4 * w];
     tb = p.work[4 * w + 1];
@@ -821,18 +832,18 @@ void decode_mfma_kernel(DecodeParams p) {
   // first granules, so that the quantization below (two barriers) waits only
   // on the Q loads (loads retire in issue order) while the KV loads fly
   constexpr int kQV = (kRows * 16 + kThreads - 1) / kThreads;  // 8-channel vectors per thread
-  const int nvec = p.n_q * 16;
+  const int nvec = nq * 16;
   QRaw8 qr[kQV];
   // unfused: the pre-quantized rows' words, fetched before the KV loads too
   // (clamped rows load a valid row and are zeroed below)
   u32x4 qg[NRB][2];
   // bf16-Q mode: this lane's channels [32jj, 32jj + 32) of Q row 16R + n % NQB
-  // (clamped like the codes; zeroed below past n_q)
+  // of the tile (clamped like the codes; zeroed below past the tile's rows)
   u32x4 qh[NRB][4];
   if constexpr (F::kQBf16) {
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
-      const int r = min(16 * R + (n % NQB), p.n_q - 1);
+      const int r = row0 + min(16 * R + (n % NQB), nq - 1);
       const int t = r / p.h_r;
       const int64_t tok = (int64_t)seq * p.q_len + t, h = (int64_t)g * p.h_r + (r - t * p.h_r);
       const u32x4* src = reinterpret_cast<const u32x4*>(p.qb + tok * p.qb_ts + h * p.qb_hs + 32 * jj);
@@ -842,7 +853,7 @@ void decode_mfma_kernel(DecodeParams p) {
   } else if (!p.qb) {
 #pragma unroll
     for (int R = 0; R < NRB; ++R) {
-      const int r = min(16 * R + (n % NQB), p.n_q - 1);
+      const int r = row0 + min(16 * R + (n % NQB), nq - 1);
       const uint8_t* row_q = p.q8 + (((int64_t)seq * p.h_k + g) * p.n_q + r) * kHeadDim;
       qg[R][0] = *reinterpret_cast<const u32x4*>(row_q + q_half_offset<FMT>(jj, 0));
       qg[R][1] = *reinterpret_cast<const u32x4*>(row_q + q_half_offset<FMT>(jj, 1));
@@ -852,7 +863,7 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
       const int v = min((int)threadIdx.x + k * kThreads, nvec - 1);  // a repeat changes no max
-      qr[k] = q_fetch8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, v >> 4, (v & 15) * 8);
+      qr[k] = q_fetch8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, row0 + (v >> 4), (v & 15) * 8);
     }
   }
 
@@ -881,6 +892,22 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
     }
+    if constexpr (kRows == 32) {
+      // row tiles: the scale covers every row of the pair, so the rows of
+      // the other tiles enter the maximum too (loaded after the ring's first
+      // granules, which they then wait for; once per workgroup)
+      if (p.row_tiles > 1) {
+        for (int v = threadIdx.x; v < p.n_q * 16; v += kThreads) {
+          const int r = v >> 4;
+          if (r >= row0 && r < row0 + nq) continue;  // in this tile: counted above
+          float y[8];
+          q_convert8(q_fetch8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, r, (v & 15) * 8),
+                     p.q_mul != nullptr, y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+        }
+      }
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if (lane == 0) red_s[wave] = amax;
@@ -900,18 +927,19 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   c.cscale = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
 
-  // B operands of QK^T: column n of block R = Q row 16R + n % NQB (zero past n_q)
+  // B operands of QK^T: column n of block R = Q row 16R + n % NQB of the
+  // tile (zero past its rows)
   QOps<FMT, NRB> qo;
   int row_tok[NRB];
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     const int r = 16 * R + (n % NQB);
-    row_tok[R] = r / p.h_r;
+    row_tok[R] = (row0 + r) / p.h_r;
     const u32x4 z = {0u, 0u, 0u, 0u};
     if constexpr (F::kQBf16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qo.b[R][i] = __builtin_bit_cast(v8bf, r < p.n_q ? qh[R][i] : z);
-    } else if (r < p.n_q) {
+      for (int i = 0; i < 4; ++i) qo.b[R][i] = __builtin_bit_cast(v8bf, r < nq ? qh[R][i] : z);
+    } else if (r < nq) {
       u32x4 a, b;
       if (p.qb) {  // LDS reads of the codes quantized above
         a = *reinterpret_cast<const u32x4*>(&q_s[r][q_half_offset<FMT>(jj, 0)]);
@@ -1036,7 +1064,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // combine the 4 waves; thread -> (row r, channel ch), r in {tid>>7, (tid>>7)+2, ...}
   const int ch = threadIdx.x & 127;
   const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k);
-  for (int r = threadIdx.x >> 7; r < p.n_q; r += 2) {
+  for (int r = threadIdx.x >> 7; r < nq; r += 2) {
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, m_s[ww][r]);
@@ -1048,8 +1076,9 @@ void decode_mfma_kernel(DecodeParams p) {
       Lsum += wt * l_s[ww][r];
       O += wt * o_s[ww][r][ch];
     }
-    const int t = r / p.h_r;
-    const int h = g * p.h_r + (r - t * p.h_r);
+    const int rg = row0 + r;  // row of the group
+    const int t = rg / p.h_r;
+    const int h = g * p.h_r + (rg - t * p.h_r);
     const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vd;
     if (single) {
       const float o = Lsum > 0.0f ? O / Lsum * om : 0.0f;
@@ -1058,7 +1087,7 @@ void decode_mfma_kernel(DecodeParams p) {
         p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
     } else if (w < p.part_items) {
       // written through to device-coherent memory, for a merge on any XCD
-      const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + r;
+      const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + rg;
       store_coherent(&p.o_part[idx * kHeadDim + ch], O * om);
       if (ch == 0) {
         store_coherent(&p.m_part[idx], Lsum > 0.0f ? M : -INFINITY);
@@ -1119,8 +1148,9 @@ void decode_mfma_kernel(DecodeParams p) {
 
 template <int FMT, int NQB, int NRB, int PF, int OCC>
 hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
-  const dim3 grid = p.head_major == 2 ? dim3((unsigned)((p.num_work + kXcds - 1) / kXcds * kXcds * p.h_k))
-                    : p.head_major ? dim3(p.h_k, p.num_work) : dim3(p.num_work, p.h_k);
+  const int heads = p.h_k * p.row_tiles;
+  const dim3 grid = p.head_major == 2 ? dim3((unsigned)((p.num_work + kXcds - 1) / kXcds * kXcds * heads))
+                    : p.head_major ? dim3(heads, p.num_work) : dim3(p.num_work, heads);
   switch (cp) {
     case 0: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 0, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
     case 1: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 1, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
@@ -1131,12 +1161,15 @@ hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
 }
 
 template <int FMT>
-hipError_t launch_fmt(const DecodeParams& p, int nt, int tune, hipStream_t s) {
+hipError_t launch_fmt(DecodeParams& p, int nt, int tune, hipStream_t s) {
   const bool pf2 = tune & 2;  // two granules of prefetch instead of one
+  // more than 32 rows: tiles of 32 rows (the 32-row instance), each
+  // workgroup one tile of one (item, KV head)
+  p.row_tiles = (p.n_q + kMfmaTileRows - 1) / kMfmaTileRows;
   if (p.n_q <= 4) return pf2 ? launch_shape<FMT, 4, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 8) return pf2 ? launch_shape<FMT, 8, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 16) return pf2 ? launch_shape<FMT, 16, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
-  // 32 rows: two waves per SIMD fit the register budget (VGPR accumulators,
+  // 32 rows (per tile): two waves per SIMD fit the register budget (VGPR accumulators,
   // no copies through AGPRs) except for packed fp6, whose V expansion needs
   // the one-wave budget
   if constexpr (Fmt<FMT>::kPacked6)
@@ -1147,7 +1180,7 @@ hipError_t launch_fmt(const DecodeParams& p, int nt, int tune, hipStream_t s) {
 
 }  // namespace
 
-bool decode_mfma_supports(int n_q) { return n_q >= 1 && n_q <= 32; }
+bool decode_mfma_supports(int n_q) { return n_q >= 1; }
 
 // tune bits: 1 = two granules of prefetch, 2 = head-major grid, 4 = XCD-
 // grouped grid (over 2); -1 = the default for the format.  cache_policy: -1 = the default for the format,

@@ -425,7 +425,7 @@ static int kernel_choice(const DecodeParams& p, int kv_format, int row_tiles) {
   // the streaming kernels address a page's rows with 32-bit lane offsets and
   // take whole 16-token tiles inside one page
   const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24) && p.ksb_ss < (1 << 24) && p.vsb_ss < (1 << 24);
-  const bool tiles_ok = row_tiles == 1 && (p.kv_tile % 16) == 0 && small_strides;
+  const bool tiles_ok = (p.kv_tile % 16) == 0 && small_strides;
   if (g_variant == 1 || !tiles_ok || !decode_mfma_supports(p.n_q)) return 0;
   if (kv_format != 0 || g_variant != 2 || p.n_q > 4 || p.q_bf16) return 1;
   return 2;
@@ -439,6 +439,8 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hi
   const int k = kernel_choice(p, kv_format, row_tiles);
   // only the matrix-core kernel fuses the step; bf16 Q is read by it and the generic kernel
   if (k != 1 && ((p.qb && !p.q_bf16) || p.counters)) return hipErrorInvalidValue;
+  // the fused merge counts one arrival per (item, KV head): one row tile
+  if (p.counters && p.n_q > kMfmaTileRows) return hipErrorInvalidValue;
   if (k == 0) return launch_decode_generic(p, kv_format, row_tiles, s);
   if (k == 1) {
     // debug setting -> matrix-core cache policy bits (K non-temporal, V non-temporal)

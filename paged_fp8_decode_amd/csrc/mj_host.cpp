@@ -453,6 +453,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->causal = a->causal ? 1 : 0;
   p->num_work = a->num_work;
   p->head_major = 0;
+  p->row_tiles = 1;
   p->q_bf16 = qbf ? 1 : 0;
   p->qb = qbf ? static_cast<const uint16_t*>(a->q_bf16) : nullptr;
   p->qb_ts = qbf ? a->q_tok_stride : 0;
@@ -550,7 +551,8 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   m.out_head_stride = a.out_head_stride;
   m.lse = a.lse;
   if (qbf) {  // nothing to quantize: the decode reads bf16 Q itself
-    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel && mj::decode_fuses_step(p, cfg->kv_format, rt);
+    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel && p.n_q <= mj::kMfmaTileRows &&
+                                 mj::decode_fuses_step(p, cfg->kv_format, rt);
     p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
     if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
     return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
@@ -560,7 +562,8 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
     p.qb_ts = sa->q_tok_stride;
     p.qb_hs = sa->q_head_stride;
     p.q_mul = sa->q_mul;
-    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel;  // its merge reads this launch's plan
+    // its merge reads this launch's plan, and covers a group of one row tile
+    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel && p.n_q <= mj::kMfmaTileRows;
     p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
     if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
     return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;

@@ -6,6 +6,10 @@
 
 namespace mj {
 
+// Query rows one matrix-core workgroup serves; groups of more rows run as
+// several such tiles, which the fused in-kernel merge does not cover.
+constexpr int kMfmaTileRows = 32;
+
 // Parameters of the Q quantization kernel.
 struct QQuantParams {
   const uint16_t* q;  // bf16
@@ -57,6 +61,11 @@ struct DecodeParams {
   // dimension of ceil(num_work / 8) * 8 * h_k workgroups numbered so that
   // the h_k heads of a work item share an XCD (see the matrix-core launch)
   int head_major;
+  // matrix-core kernel: workgroups per (item, KV head), each serving a tile
+  // of 32 of the group's n_q rows (the last one the remainder); the head
+  // dimension of the grid above then counts h_k * row_tiles (head-major
+  // order inside).  Set by the matrix-core launcher; 1 elsewhere.
+  int row_tiles;
   // q_bf16 = 1: bf16-Q mode.  qb is then the bf16 Q the kernels use as is
   // (q8 / q_descale unused), on every decode kernel but the VALU-PV one.
   // Otherwise (fused step, matrix-core kernel only; null elsewhere) qb is the
