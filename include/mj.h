@@ -128,8 +128,9 @@ typedef struct mj_config {
 /* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):
  * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
  * workgroups per CU; four waves of items of >= 2048 tokens balance the tail
- * across CUs and XCDs); 16 < n_q <= 32, or fp6 (e2m3 / e3m2) -> 1 / 1 (one
- * wave); e2m1 / nvfp4, or n_q > 32 -> 2 / 1.  min_chunk_tokens is rounded up to whole KV tiles. */
+ * across CUs and XCDs); e2m1 / nvfp4 with n_q <= 32 -> 2 / 1; everything
+ * else (16 < n_q <= 32, fp6 (e2m3 / e3m2), n_q > 32) -> 1 / 1 (one wave).
+ * min_chunk_tokens is rounded up to whole KV tiles. */
 
 /* What a plan decided (runner.py, StepPlan). */
 typedef struct mj_plan_info {
@@ -486,8 +487,9 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, i
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);
 /* Process-wide choice of decode kernel, for A/B measurements and for testing
  * every kernel on the same inputs: variant 0 = automatic (the matrix-core
- * kernel wherever q_len*h_r <= 32, whole 16-token tiles and slot strides
- * < 2^24 bytes; otherwise the generic LDS-tiled kernel), 1 = always the
+ * kernel wherever the plan's KV tiles are whole 16-token tiles and slot
+ * strides are < 2^24 bytes, groups of more than 32 rows as several 32-row
+ * tiles; otherwise the generic LDS-tiled kernel), 1 = always the
  * generic kernel, 2 = the VALU-PV streaming kernel for e4m3 with
  * q_len*h_r <= 4 (automatic otherwise), 3 = same as 0, 10..17 = the
  * matrix-core kernel with tuning bits (variant - 10): bit 0 two granules of

@@ -66,14 +66,16 @@ def default_shape(kv_format: str, n_q: int) -> tuple[int, int]:
     """(wgs_per_cu, min_chunk_tokens) the library uses when the config leaves
     them 0: the e4m3 matrix-core kernel for up to 16 rows runs two
     workgroups per CU and is planned four waves deep with items of at least
-    2048 tokens; the 32-row kernel (one workgroup per CU) and the e2m3
-    kernel are planned one wave deep; the e2m1 and nvfp4 kernels (half-size
-    rows) and wider groups (the generic kernel) two per CU."""
+    2048 tokens; the e2m1 and nvfp4 kernels (half-size rows) of up to 32
+    rows two per CU; everything else (the 32-row kernel, the fp6 kernels,
+    groups of more than 32 rows served as several 32-row tiles) one wave
+    deep.  A tuning choice of the library, mirrored here so that the plans
+    compare bit for bit; the pages fix no plan depth."""
     if kv_format == "e4m3" and n_q <= 16:
         return 8, 2048
-    if n_q <= 32 and kv_format not in ("e2m1", "nvfp4"):
-        return 1, 1
-    return 2, 1
+    if n_q <= 32 and kv_format in ("e2m1", "nvfp4"):
+        return 2, 1
+    return 1, 1
 
 
 def plan_split_kv(

@@ -28,7 +28,10 @@ struct Derived {
 // (the tail of a single wave is set by the slowest CU), and the 2048-token
 // floor keeps items long enough to amortise the prologue and partial write.
 // The 32-row kernel (one workgroup per CU) and the e2m3 kernel measured
-// fastest planned one wave deep.
+// fastest planned one wave deep, and so did groups of more than 32 rows (row
+// tiles: each item is already several workgroups; cfg4c's batch at 40 rows
+// 96 -> 79 us, 128 rows 157 -> 130 us against two per CU).  The e2m1 and
+// nvfp4 kernels of up to 32 rows plan two per CU.
 struct PlanShape {
   int wgs_per_cu, min_chunk_tokens;
 };
@@ -38,7 +41,7 @@ PlanShape plan_shape(const mj_config* c, const Derived& d, int q_len) {
   const bool small_e4m3 = c->kv_format == MJ_KV_E4M3 && n_q <= 16;
   const bool fp4 = c->kv_format == MJ_KV_E2M1 || c->kv_format == MJ_KV_NVFP4;
   PlanShape ps;
-  ps.wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : (small_e4m3 ? 8 : (n_q <= 32 && !fp4 ? 1 : 2));
+  ps.wgs_per_cu = c->wgs_per_cu ? c->wgs_per_cu : (small_e4m3 ? 8 : (fp4 && n_q <= 32 ? 2 : 1));
   ps.min_chunk_tokens = c->min_chunk_tokens ? c->min_chunk_tokens : (small_e4m3 ? 2048 : 1);
   return ps;
 }
