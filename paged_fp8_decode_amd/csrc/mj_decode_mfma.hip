@@ -492,7 +492,7 @@ __device__ __forceinline__ void qk_tile(const KRows<FMT>& K, int k, const QOps<F
   }
 }
 
-// Row layout of a GQA group of n_q <= 32 query rows: NRB blocks of 16 rows;
+// Row layout of a tile of up to 32 query rows of a GQA group: NRB blocks of 16 rows;
 // a group of NQB < 16 rows (one block) is replicated 16 / NQB times.
 //  - softmax layout (QK^T output): lane (n, jj) holds row 16R + n % NQB of
 //    block R for the 8 tokens tau(jj, e) of the granule;

@@ -6,8 +6,8 @@ unquantized-Q attention, through the C ABI:
 * every output of the reduced workloads, on the matrix-core kernel and the
   generic kernel, as four calls and as one mj_decode_step (with a host plan
   and planning from the device lengths);
-* edge lengths and speculative shapes (replicated rows, 32 rows, > 32 rows on
-  the generic kernel), forced splits, a strided Q view;
+* edge lengths and speculative shapes (replicated rows, 32 rows, > 32 rows as
+  32-row tiles), forced splits, a strided Q view;
 * sampled rows of the full-size workloads in the step the bench times.
 """
 
