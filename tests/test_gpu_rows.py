@@ -4,9 +4,10 @@ them as tiles of 32 rows, one workgroup per (item, KV head, tile), all tiles
 reading the same KV rows; the fused step's Q scale still covers every row of
 the (sequence, KV head) pair, as the stand-alone quantization does.
 
-* outputs and LSE of every format against the oracle at 40 (two tiles, the
-  second partial), 66, 128 and 576 rows, with causal blocks longer than some
-  sequences, empty sequences and forced splits;
+* outputs and LSE of every format (and the token-major layout) against the
+  oracle at 40 (two tiles, the second partial), 66, 128, 576 and 1024 rows,
+  with causal blocks longer than some sequences, empty sequences and forced
+  splits;
 * the fused step (in-kernel quantization) equals the three-call path bit for
   bit, also with the in-kernel merge asked for (which such groups leave to
   the merge launch) and with the plan made in the kernel;
@@ -24,9 +25,10 @@ from helpers import compare_lse, compare_out, oracle_step, say
 pytestmark = pytest.mark.gpu
 
 LENS = (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, 1000)
-# (q_len, h_q, h_k, causal): 40, 66, 128 and 576 rows per group
-SHAPES = [(5, 64, 8, True), (11, 48, 8, True), (16, 64, 8, False), (9, 64, 1, True)]
-KEYS = ["cfg2", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4"]
+# (q_len, h_q, h_k, causal): 40, 66, 128, 576 and 1024 rows per group (the
+# library's largest)
+SHAPES = [(5, 64, 8, True), (11, 48, 8, True), (16, 64, 8, False), (9, 64, 1, True), (16, 64, 1, True)]
+KEYS = ["cfg2", "cfg3", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4"]
 
 
 @pytest.fixture(scope="module")
