@@ -47,17 +47,17 @@ if ROOT not in sys.path:
 
 # HBM traffic of the decode kernel per launch from rocprofv3 --pmc
 # (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what the same counters
-# read for a 256 MiB copy: fetch x 1.99979, write x 1.000), as recorded in
+# read for a 256 MiB copy: fetch x 1.99980, write x 1.000), as recorded in
 # profiles/decode_mfma_kernel_hbm_traffic.md.  Reported only while the
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "0ab29a7dc90a414c",
-    "cfg2": dict(fetch_bytes=269320721, write_bytes=1179995),
-    "32k": dict(fetch_bytes=4297931685, write_bytes=4718970),
-    "cfg5": dict(fetch_bytes=806134000, write_bytes=589835),
-    "cfg5_e2m1": dict(fetch_bytes=538166224, write_bytes=1179673),
-    "cfg5_nvfp4": dict(fetch_bytes=604674026, write_bytes=1179671),
+    "sources_sha256_16": "f78a7c23e27f22f5",
+    "cfg2": dict(fetch_bytes=269319651, write_bytes=1179995),
+    "32k": dict(fetch_bytes=4297935229, write_bytes=4718959),
+    "cfg5": dict(fetch_bytes=806129201, write_bytes=589835),
+    "cfg5_e2m1": dict(fetch_bytes=538117560, write_bytes=1179671),
+    "cfg5_nvfp4": dict(fetch_bytes=604669234, write_bytes=1179671),
 }
 
 

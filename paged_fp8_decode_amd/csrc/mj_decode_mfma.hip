@@ -243,6 +243,7 @@ struct Ctx {
   uint32_t v_lane;       // 4 * jj * v_ss + byte offset of channel 8n (4-aligned)
   uint32_t num_pages;    // clamped to 2^31 - 1
   int j0, j1, page_shift, pmask, lim0, causal, n, jj;
+  int jcap;              // end of the item's range clamped to the block-table row, not to the length
   int v_shift;           // e2m3: bit offset of channel 8n in the loaded 8 bytes
   float cscale;
   float pos_inf;         // +inf (kernel argument; see fmax2)
@@ -258,9 +259,11 @@ struct Ctx {
 // Page of the tile starting at token tk (wave-uniform), or -1 if the tile is
 // past the range end or its block-table entry is out of range.
 __device__ __forceinline__ int tile_page(const Ctx& c, int tk) {
-  // clamped into [0, j1 - 1]; entry 0 of a block-table row always exists
-  // (at least one column), so an empty range reads it and stays dead
-  const int idx = max(min(tk, c.j1 - 1), 0);
+  // clamped into [0, jcap - 1], inside the block-table row; entry 0 of a row
+  // always exists (at least one column), so an empty range reads it and
+  // stays dead.  The clamp does not use the sequence length, so the entry's
+  // load does not wait for the length's: liveness (tk < j1) masks it after
+  const int idx = max(min(tk, c.jcap - 1), 0);
   const int pg = c.bt_row[idx >> c.page_shift];
   // all-ones when the tile is live; bit operations keep the block-table
   // load out of any branch
@@ -792,6 +795,7 @@ void decode_mfma_kernel(DecodeParams p) {
   Ctx c;
   c.j0 = tb * p.kv_tile;
   c.j1 = min(te * p.kv_tile, L);
+  c.jcap = min(te * p.kv_tile, p.max_blocks * p.page_size);
   c.causal = p.causal && p.q_len > 1;
   c.lim0 = L - p.q_len;
   c.n = n;
