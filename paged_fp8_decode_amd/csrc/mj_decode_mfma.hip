@@ -412,13 +412,6 @@ template <int B>
 __device__ __forceinline__ v2h fp4_f16(uint32_t w, float s) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, B);
 }
-// fp16 bits of M for an fp32 s = 2^E * M, M in [1, 2) (0 -> 1: the
-// converter then yields 0 anyway); exact when s has at most 10 fraction bits
-__device__ __forceinline__ uint32_t scale_mantissa_h(float s) {
-  const uint32_t b = __float_as_uint(s);
-  return 0x3C00u | ((b >> 13) & 0x3FFu) | ((b >> 16) & 0x8000u);
-}
-
 // the two e2m1 values of byte B of w, as fp32 (low nibble first)
 template <int B>
 __device__ __forceinline__ v2f fp4_pair(uint32_t w) {
@@ -432,19 +425,18 @@ __device__ __forceinline__ void qk_tile(const KRows<FMT>& K, int k, const QOps<F
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (Fmt<FMT>::kQkF16) {
     // nvfp4 with fp8 Q: dword i holds codes [8i, 8i + 8) of the lane's 32, in
-    // block 2jj + i / 2; the converter applies the scale's power of two, one
-    // packed multiply its mantissa
-    const v2f sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(K.s[k], 1.0f, false);
-    const uint32_t h0 = scale_mantissa_h(sc[0]), h1 = scale_mantissa_h(sc[1]);
-    const v2h m0 = __builtin_bit_cast(v2h, h0 | (h0 << 16)), m1 = __builtin_bit_cast(v2h, h1 | (h1 << 16));
+    // block 2jj + i / 2; codes and the two block scales become fp16 exactly,
+    // and one packed multiply per code pair applies the scale (exact: at
+    // most 6 significant bits, magnitudes in [2^-10, 2688], fp16 normals)
+    const v2h sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(K.s[k], 1.0f, false);
+    const v2h m0 = {sc[0], sc[0]}, m1 = {sc[1], sc[1]};
     v8h ka[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float bs = i < 2 ? sc[0] : sc[1];
       const v2h mm = i < 2 ? m0 : m1;
       const uint32_t w = K.d[k][i];
-      const v2h x0 = fp4_f16<0>(w, bs) * mm, x1 = fp4_f16<1>(w, bs) * mm;
-      const v2h x2 = fp4_f16<2>(w, bs) * mm, x3 = fp4_f16<3>(w, bs) * mm;
+      const v2h x0 = fp4_f16<0>(w, 1.0f) * mm, x1 = fp4_f16<1>(w, 1.0f) * mm;
+      const v2h x2 = fp4_f16<2>(w, 1.0f) * mm, x3 = fp4_f16<3>(w, 1.0f) * mm;
       ka[i] = (v8h){x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
     }
 #pragma unroll
@@ -537,20 +529,19 @@ __device__ __forceinline__ void pv_pair(const VRows<FMT>& V, const v8bf (&pa)[NR
   }
 }
 
-// nvfp4 PV for channels 2PR and 2PR + 1, on fp16 MFMAs: token e's two values
-// times the power of two of its block scale vsc[e] (converter), the token
-// pairs' words times their scales' mantissas mm (one packed multiply each)
+// nvfp4 PV for channels 2PR and 2PR + 1, on fp16 MFMAs.  lo[i] / hi[i]:
+// the codes of tokens (2i, 2i + 1) nibble-interleaved, so that byte PR holds
+// channel 2PR (lo) or 2PR + 1 (hi) of both tokens: one conversion gives a
+// B-operand word (a token pair of one channel) and one packed multiply by the
+// two tokens' block scales s[i] (fp16, exact) scales it, exactly as in QK^T
 template <int FMT, int PR, int NQB, int NRB>
-__device__ __forceinline__ void pv_pair_h(const VRows<FMT>& V, const float (&vsc)[8], const v2h (&mm)[4],
+__device__ __forceinline__ void pv_pair_h(const uint32_t (&lo)[4], const uint32_t (&hi)[4], const v2h (&s)[4],
                                           const v8h (&pa)[NRB], State<NQB, NRB>& st) {
-  v2h x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = fp4_f16<PR>(V.d[e][0], vsc[e]);
   v2h a[4], b[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a[i] = (v2h){x[2 * i][0], x[2 * i + 1][0]} * mm[i];
-    b[i] = (v2h){x[2 * i][1], x[2 * i + 1][1]} * mm[i];
+    a[i] = fp4_f16<PR>(lo[i], 1.0f) * s[i];
+    b[i] = fp4_f16<PR>(hi[i], 1.0f) * s[i];
   }
   const v8h wa = {a[0][0], a[0][1], a[1][0], a[1][1], a[2][0], a[2][1], a[3][0], a[3][1]};
   const v8h wb = {b[0][0], b[0][1], b[1][0], b[1][1], b[2][0], b[2][1], b[3][0], b[3][1]};
@@ -683,20 +674,21 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
   }
   // ---- PV
   if constexpr (Fmt<FMT>::kPvF16) {
-    float vsc[8];
-    uint32_t hm[8];
+    uint32_t lo[4], hi[4];
+    v2h sv[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      vsc[e] = __builtin_amdgcn_cvt_f32_fp8((int)V.s[e], 0);
-      hm[e] = scale_mantissa_h(vsc[e]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a = V.d[2 * i][0], b = V.d[2 * i + 1][0];
+      lo[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+      hi[i] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+      // the two tokens' scale bytes (low bytes) side by side, as fp16
+      sv[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(V.s[2 * i + 1], V.s[2 * i], 0x0C0C0400u),
+                                                       1.0f, false);
     }
-    v2h mm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mm[i] = __builtin_bit_cast(v2h, hm[2 * i] | (hm[2 * i + 1] << 16));
-    pv_pair_h<FMT, 0, NQB, NRB>(V, vsc, mm, pa, st);
-    pv_pair_h<FMT, 1, NQB, NRB>(V, vsc, mm, pa, st);
-    pv_pair_h<FMT, 2, NQB, NRB>(V, vsc, mm, pa, st);
-    pv_pair_h<FMT, 3, NQB, NRB>(V, vsc, mm, pa, st);
+    pv_pair_h<FMT, 0, NQB, NRB>(lo, hi, sv, pa, st);
+    pv_pair_h<FMT, 1, NQB, NRB>(lo, hi, sv, pa, st);
+    pv_pair_h<FMT, 2, NQB, NRB>(lo, hi, sv, pa, st);
+    pv_pair_h<FMT, 3, NQB, NRB>(lo, hi, sv, pa, st);
   } else if constexpr (!Fmt<FMT>::kPacked6) {
     // e4m3 / e2m1 V, one channel pair at a time: converting a word's low or
     // high two bytes (e2m1: one byte) gives channels (2pr, 2pr + 1) of one
