@@ -502,19 +502,14 @@ struct State {
   v4f acc[NRB][8];      // O rows 16R + (4jj + v) % NQB, channel 8n + q: acc[R][q][v]
 };
 
-// PV for channels 2PR and 2PR + 1 of the lane's 8-channel group (e4m3 V:
-// bytes 2PR % 4 and 2PR % 4 + 1 of dword PR / 2; e2m1 V: the two nibbles of
-// byte PR).
+// e4m3 PV for channels 2PR and 2PR + 1 of the lane's 8-channel group (bytes
+// 2PR % 4 and 2PR % 4 + 1 of dword PR / 2).
 template <int FMT, int PR, int NQB, int NRB>
 __device__ __forceinline__ void pv_pair(const VRows<FMT>& V, const v8bf (&pa)[NRB], State<NQB, NRB>& st) {
   float a[8], b[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    v2f x;
-    if constexpr (Fmt<FMT>::kVDw == 1)
-      x = fp4_pair<PR>(V.d[e][0]);
-    else
-      x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][PR >> 1], 1.0f, (PR & 1) != 0);
+    const v2f x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][PR >> 1], 1.0f, (PR & 1) != 0);
     a[e] = x[0];
     b[e] = x[1];
   }
@@ -550,6 +545,34 @@ __device__ __forceinline__ void pv_pair_h(const uint32_t (&lo)[4], const uint32_
     st.acc[R][2 * PR] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[R], wa, st.acc[R][2 * PR], 0, 0, 0);
     st.acc[R][2 * PR + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[R], wb, st.acc[R][2 * PR + 1], 0, 0, 0);
   }
+}
+
+// e2m1 PV for channels 2PR and 2PR + 1 from nibble-interleaved token pairs
+// (lo / hi as in the nvfp4 PV): one conversion per B-operand word, exact
+template <int FMT, int PR, int NQB, int NRB>
+__device__ __forceinline__ void pv_pair_fp4(const uint32_t (&lo)[4], const uint32_t (&hi)[4], const v8bf (&pa)[NRB],
+                                            State<NQB, NRB>& st) {
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  u32x4 wa, wb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wa[i] = __builtin_bit_cast(uint32_t, (v2bf_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(lo[i], 1.0f, PR));
+    wb[i] = __builtin_bit_cast(uint32_t, (v2bf_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(hi[i], 1.0f, PR));
+  }
+#pragma unroll
+  for (int R = 0; R < NRB; ++R) {
+    st.acc[R][2 * PR] =
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], __builtin_bit_cast(v8bf, wa), st.acc[R][2 * PR], 0, 0, 0);
+    st.acc[R][2 * PR + 1] =
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], __builtin_bit_cast(v8bf, wb), st.acc[R][2 * PR + 1], 0, 0, 0);
+  }
+}
+
+// the codes of tokens (2i, 2i + 1) nibble-interleaved: byte k of lo[i] holds
+// channel 2k of both tokens (low nibble: token 2i), byte k of hi[i] channel 2k + 1
+__device__ __forceinline__ void fp4_interleave(const uint32_t a, const uint32_t b, uint32_t& lo, uint32_t& hi) {
+  lo = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+  hi = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
 }
 
 template <int NQB, int NRB>
@@ -678,9 +701,7 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
     v2h sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t a = V.d[2 * i][0], b = V.d[2 * i + 1][0];
-      lo[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
-      hi[i] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+      fp4_interleave(V.d[2 * i][0], V.d[2 * i + 1][0], lo[i], hi[i]);
       // the two tokens' scale bytes (low bytes) side by side, as fp16
       sv[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(V.s[2 * i + 1], V.s[2 * i], 0x0C0C0400u),
                                                        1.0f, false);
@@ -689,9 +710,19 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
     pv_pair_h<FMT, 1, NQB, NRB>(lo, hi, sv, pa, st);
     pv_pair_h<FMT, 2, NQB, NRB>(lo, hi, sv, pa, st);
     pv_pair_h<FMT, 3, NQB, NRB>(lo, hi, sv, pa, st);
+  } else if constexpr (Fmt<FMT>::kVDw == 1) {
+    // e2m1 V: token pairs nibble-interleaved, then one bf16 conversion per
+    // B-operand word
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fp4_interleave(V.d[2 * i][0], V.d[2 * i + 1][0], lo[i], hi[i]);
+    pv_pair_fp4<FMT, 0, NQB, NRB>(lo, hi, pa, st);
+    pv_pair_fp4<FMT, 1, NQB, NRB>(lo, hi, pa, st);
+    pv_pair_fp4<FMT, 2, NQB, NRB>(lo, hi, pa, st);
+    pv_pair_fp4<FMT, 3, NQB, NRB>(lo, hi, pa, st);
   } else if constexpr (!Fmt<FMT>::kPacked6) {
-    // e4m3 / e2m1 V, one channel pair at a time: converting a word's low or
-    // high two bytes (e2m1: one byte) gives channels (2pr, 2pr + 1) of one
+    // e4m3 V, one channel pair at a time: converting a word's low or
+    // high two bytes gives channels (2pr, 2pr + 1) of one
     // token, so the 8 tokens' words give both channels' B operands, used at
     // once (16 floats live, not 64)
     pv_pair<FMT, 0, NQB, NRB>(V, pa, st);
