@@ -52,12 +52,12 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "f78a7c23e27f22f5",
-    "cfg2": dict(fetch_bytes=269319651, write_bytes=1179995),
-    "32k": dict(fetch_bytes=4297935229, write_bytes=4718959),
-    "cfg5": dict(fetch_bytes=806129201, write_bytes=589835),
-    "cfg5_e2m1": dict(fetch_bytes=538117560, write_bytes=1179671),
-    "cfg5_nvfp4": dict(fetch_bytes=604669234, write_bytes=1179671),
+    "sources_sha256_16": "2a48a770c1f6ea9a",
+    "cfg2": dict(fetch_bytes=269321213, write_bytes=1180002),
+    "32k": dict(fetch_bytes=4297924012, write_bytes=4718987),
+    "cfg5": dict(fetch_bytes=806126851, write_bytes=589835),
+    "cfg5_e2m1": dict(fetch_bytes=538199653, write_bytes=1179668),
+    "cfg5_nvfp4": dict(fetch_bytes=604645464, write_bytes=1179671),
 }
 
 
