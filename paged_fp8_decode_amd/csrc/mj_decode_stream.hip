@@ -420,8 +420,11 @@ void set_decode_variant(int v, int nt) {
   g_nontemporal = nt;
 }
 
-// 0 = generic kernel, 1 = matrix-core kernel, 2 = VALU-PV streaming kernel
+// 0 = generic kernel, 1 = matrix-core kernel, 2 = VALU-PV streaming kernel.
+// row_tiles (the plan's 64-row tiles) does not enter: the matrix-core kernel
+// serves any row count in 32-row tiles of its own.
 static int kernel_choice(const DecodeParams& p, int kv_format, int row_tiles) {
+  (void)row_tiles;
   // the streaming kernels address a page's rows with 32-bit lane offsets and
   // take whole 16-token tiles inside one page
   const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24) && p.ksb_ss < (1 << 24) && p.vsb_ss < (1 << 24);
