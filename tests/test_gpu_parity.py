@@ -563,3 +563,32 @@ def test_nan_codes_past_the_sequence_end(mj, gpu, key, q_mode, variant):
     O, LSE = oracle_step(wl, quantize=q_mode == "fp8")
     compare_out(out, O, f"{key} NaN tails")
     compare_lse(lse, LSE, f"{key} NaN tails")
+
+
+@pytest.mark.parametrize("variant", [0, 1], indirect=True)
+@pytest.mark.parametrize("key,q_mode", [("cfg5_nvfp4", "fp8"), ("cfg5_nvfp4", "bf16"), ("cfg3_nvfp4", "fp8")])
+def test_nvfp4_full_scale_range(mj, gpu, key, q_mode, variant):
+    """Block scales drawn over every finite non-negative e4m3 code (the
+    subnormals 2^-9 .. 7 * 2^-9 up to 448) and codes over all 16 e2m1 values
+    of both signs: the kernel's fp16 products code x scale must be exact over
+    the whole range (smallest 2^-10, largest 2688).  The fp32 descales bring
+    logits and outputs back to O(1)."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    g = torch.Generator().manual_seed(91)
+    for pool in (wl.k_bs_pool, wl.v_bs_pool):
+        pool.copy_(torch.randint(0, 0x7F, pool.shape, generator=g, dtype=torch.uint8))
+    for pool in (wl.k_pool, wl.v_pool):
+        pool.copy_(torch.randint(0, 256, pool.shape, generator=g, dtype=torch.uint8))
+    wl.k_descale.fill_(1.0 / 300.0)
+    wl.v_descale.fill_(1.0 / 200.0)
+    say(f"nvfp4 full scale range {wl.spec.name} q_mode={q_mode} variant={variant}")
+    step = DecodeStep.for_workload(wl, q_mode=q_mode, **FINE)
+    info = step.plan_workload(wl)
+    out, lse = new_output(wl)
+    out.fill_(float("nan"))
+    step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.synchronize()
+    O, LSE = oracle_step(wl, quantize=q_mode == "fp8")
+    compare_out(out, O, f"{key} full scale range")
+    compare_lse(lse, LSE, f"{key} full scale range")
