@@ -592,3 +592,22 @@ def test_nvfp4_full_scale_range(mj, gpu, key, q_mode, variant):
     O, LSE = oracle_step(wl, quantize=q_mode == "fp8")
     compare_out(out, O, f"{key} full scale range")
     compare_lse(lse, LSE, f"{key} full scale range")
+
+
+@pytest.mark.parametrize("variant", [0, 1], indirect=True)
+@pytest.mark.parametrize("key", ["cfg5", "cfg5_e3m2", "cfg5_e2m1"])
+def test_packed_codes_full_range(mj, gpu, key, variant):
+    """Every 6-bit (e2m3, e3m2) or 4-bit (e2m1) code, both signs and the
+    largest magnitudes (7.5, 28, 6), as random cache bytes through the
+    matrix-core operands and the generic kernel's decoders; the K descale
+    keeps the logits moderate."""
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    g = torch.Generator().manual_seed(92)
+    for pool in (wl.k_pool, wl.v_pool):
+        pool.copy_(torch.randint(0, 256, pool.shape, generator=g, dtype=torch.uint8))
+    wl.k_descale.fill_(0.25)
+    say(f"full code range {wl.spec.name} variant={variant}")
+    out, lse, _ = _run(mj, wl, fused=True, **FINE)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, f"{key} full code range")
+    compare_lse(lse, LSE, f"{key} full code range")
