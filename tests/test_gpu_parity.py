@@ -611,3 +611,29 @@ def test_packed_codes_full_range(mj, gpu, key, variant):
     O, LSE = oracle_step(wl)
     compare_out(out, O, f"{key} full code range")
     compare_lse(lse, LSE, f"{key} full code range")
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("key,q_mode", [("cfg2", "fp8"), ("cfg2", "bf16"), ("cfg4c", "fp8")])
+def test_e4m3_codes_full_range(mj, gpu, key, q_mode, variant):
+    """Every finite e4m3 code (subnormals, both signs, +-448) as random cache
+    bytes (the NaN codes replaced by zero), through every decode kernel."""
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    g = torch.Generator().manual_seed(93)
+    for pool in (wl.k_pool, wl.v_pool):
+        r = torch.randint(0, 256, pool.shape, generator=g, dtype=torch.uint8)
+        r[(r & 0x7F) == 0x7F] = 0
+        pool.copy_(r)
+    wl.k_descale.fill_(0.01)
+    wl.v_descale.fill_(0.01)
+    say(f"e4m3 full code range {wl.spec.name} q_mode={q_mode} variant={variant}")
+    step = DecodeStep.for_workload(wl, q_mode=q_mode, **FINE)
+    info = step.plan_workload(wl)
+    out, lse = new_output(wl)
+    out.fill_(float("nan"))
+    step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.synchronize()
+    O, LSE = oracle_step(wl, quantize=q_mode == "fp8")
+    compare_out(out, O, f"{key} e4m3 full code range")
+    compare_lse(lse, LSE, f"{key} e4m3 full code range")
