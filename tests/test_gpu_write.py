@@ -216,3 +216,53 @@ def test_written_cache_decodes(mj, gpu, key):
     O, LSE = oracle_step(wl)
     compare_out(out, O, f"written {s.name}")
     compare_lse(lse, LSE, f"written {s.name}")
+
+
+@pytest.mark.parametrize("kv_format", ["e4m3", "e2m3", "e3m2", "e2m1"])
+def test_write_ties_and_grid_points(mj, gpu, kv_format):
+    """Every value of the format's grid, every midpoint between neighbours
+    (ties to even) and values just inside and outside each midpoint, both
+    signs, through the write at unit scale: the stored bytes equal the
+    oracle's (all these inputs are exact in bf16)."""
+    from oracle import formats as F
+    from oracle.kvwrite import write_kv
+    table = {"e4m3": F.E4M3_TABLE[:0x7F], "e2m3": F.E2M3_TABLE[:0x20], "e3m2": F.E3M2_TABLE[:0x20],
+             "e2m1": F.E2M1_TABLE[:0x8]}[kv_format]
+    grid = np.unique(table)
+    mids = (grid[:-1] + grid[1:]) / 2
+    near = np.concatenate([np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(np.inf))])
+    vals = np.concatenate([grid, mids, grid[-1:] * 1.25])  # the last: saturates
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    bf = torch.from_numpy(vals).to(torch.bfloat16)
+    assert torch.equal(bf.float(), torch.from_numpy(vals)), "grid points and midpoints are exact in bf16"
+    # nextafter of a midpoint is not a bf16 value: round it to bf16 and keep the ones still off the midpoint
+    nb = torch.from_numpy(near).to(torch.bfloat16).float().numpy()
+    nb = nb[~np.isin(nb, mids)]
+    allv = torch.cat([bf, torch.from_numpy(np.concatenate([nb, -nb])).to(torch.bfloat16)])
+    h_k, d = 2, 128
+    n = -(-allv.numel() // (h_k * d)) + 1
+    flat = torch.zeros(n * h_k * d, dtype=torch.bfloat16)
+    flat[: allv.numel()] = allv
+    key = flat.view(n, h_k, d)
+    value = flat.flip(0).view(n, h_k, d).contiguous()
+    P, layout = 16, "HND"
+    pages = -(-n // P) + 1
+    row = F.ROW_BYTES[kv_format]
+    ks = vs = _strides(layout, P, h_k, row)
+    size = pages * P * h_k * row
+    rng = np.random.default_rng(5)
+    init_k = rng.integers(0, 256, size, dtype=np.uint8)
+    init_v = rng.integers(0, 256, size, dtype=np.uint8)
+    slots = np.arange(n, dtype=np.int64)
+    ones = np.ones((h_k, d), np.float32)
+    k_pool = torch.from_numpy(init_k.copy()).to(gpu)
+    v_pool = torch.from_numpy(init_v.copy()).to(gpu)
+    say(f"write ties {kv_format}: {allv.numel()} values over {n} tokens")
+    cfg = mj.mj_config(h_q=h_k, h_k=h_k, page_size=P, max_num_seqs=1, kv_format=kv_format, num_cus=256)
+    _write(mj, gpu, cfg, key.to(gpu), value.to(gpu), torch.from_numpy(slots).to(gpu), k_pool, v_pool, ks, vs,
+           torch.from_numpy(ones).to(gpu), torch.from_numpy(ones).to(gpu), "channel", pages)
+    ref = write_kv((init_k, init_v), (ks, vs), P, kv_format, key.float().numpy(), value.float().numpy(),
+                   slots, ones, ones, "channel")
+    assert np.array_equal(k_pool.cpu().numpy(), ref[0])
+    assert np.array_equal(v_pool.cpu().numpy(), ref[1])
