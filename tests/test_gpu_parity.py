@@ -89,6 +89,39 @@ def test_quantize_q_bit_exact(mj, gpu, b, q_len, h_q, h_k, mul, extra):
     assert np.array_equal(q8.cpu().numpy().reshape(ref_c.shape), ref_c)
 
 
+def test_quantize_q_ties(mj, gpu):
+    """Q rows holding every e4m3 grid value and every midpoint between
+    neighbours (both signs), with 448 in each (sequence, KV head) group so the
+    scale is exactly 1: the stand-alone kernel's codes (ties to even) and
+    descales equal the oracle's.  (The fused step's prologue repeats this
+    arithmetic; its outputs equal the three-call path's bit for bit.)"""
+    from oracle.formats import E4M3_TABLE
+    from oracle.qquant import quantize_q
+    grid = np.unique(E4M3_TABLE[:0x7F])
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([grid, mids])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    b, q_len, h_q, h_k = 2, 1, 8, 2
+    n_grp = q_len * (h_q // h_k) * 128
+    q = np.zeros((b * q_len, h_q, 128), np.float32)
+    for i in range(b):
+        for g in range(h_k):
+            blk = np.resize(np.roll(vals, 37 * (2 * i + g)), n_grp)
+            blk[0] = 448.0
+            q[i * q_len:(i + 1) * q_len, g * (h_q // h_k):(g + 1) * (h_q // h_k)] = blk.reshape(q_len, h_q // h_k, 128)
+    qt = torch.from_numpy(q).to(torch.bfloat16)
+    assert torch.equal(qt.float(), torch.from_numpy(q))
+    cfg = mj.mj_config(h_q=h_q, h_k=h_k, page_size=16, max_num_seqs=b, max_q_len=q_len, num_cus=256)
+    q8 = torch.empty(b * h_k * n_grp, dtype=torch.uint8, device=gpu)
+    qd = torch.empty(b * h_k, dtype=torch.float32, device=gpu)
+    mj.mj_quantize_q(cfg, qt.to(gpu), None, b, q_len, q8, qd)
+    torch.cuda.synchronize()
+    ref_c, ref_s = quantize_q(q, b, q_len, h_k, None)
+    assert np.all(ref_s == 1.0)
+    assert np.array_equal(qd.cpu().numpy().reshape(b, h_k), ref_s)
+    assert np.array_equal(q8.cpu().numpy().reshape(ref_c.shape), ref_c)
+
+
 @pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
                                  "cfg3_nvfp4"])
 def test_gather_probe_bit_exact(mj, gpu, key):
