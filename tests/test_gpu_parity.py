@@ -122,6 +122,42 @@ def test_quantize_q_ties(mj, gpu):
     assert np.array_equal(q8.cpu().numpy().reshape(ref_c.shape), ref_c)
 
 
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c"])
+def test_fused_quantization_ties(mj, gpu, key):
+    """The fused step's in-kernel Q quantization on tie values (every e4m3
+    midpoint at unit scale, 448 in each group) gives the stand-alone kernel's
+    codes: the fused step's outputs equal the three-call path's bit for bit."""
+    from oracle.formats import E4M3_TABLE
+    from paged_fp8_decode_amd.runner import DecodeStep, new_output
+    wl = synth.build(synth.spec_for(key, small=True), gpu)
+    s = wl.spec
+    grid = np.unique(E4M3_TABLE[:0x7F])
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([mids, -mids]).astype(np.float32)
+    h_r = s.h_q // s.h_k
+    n_grp = s.q_len * h_r * 128
+    q = np.zeros((s.b * s.q_len, s.h_q, 128), np.float32)
+    for i in range(s.b):
+        for g in range(s.h_k):
+            blk = np.resize(np.roll(vals, 29 * (i + 3 * g)), n_grp) / 64.0  # midpoints / 64: still ties after x / s
+            blk[0] = 448.0 / 64.0
+            q[i * s.q_len:(i + 1) * s.q_len, g * h_r:(g + 1) * h_r] = blk.reshape(s.q_len, h_r, 128)
+    wl.q.copy_(torch.from_numpy(q).to(torch.bfloat16).to(gpu))
+    say(f"fused quantization ties {wl.spec.name}")
+    step = DecodeStep.for_workload(wl, **FINE)
+    info = step.plan_workload(wl)
+    ref_o, ref_l = new_output(wl)
+    step.run_workload(wl, ref_o, ref_l, info=info)
+    out, lse = new_output(wl)
+    step.run_workload(wl, out, lse, info=info, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+    assert torch.equal(lse, ref_l)
+    O, LSE = oracle_step(wl)
+    compare_out(out, O, f"{key} Q ties")
+    compare_lse(lse, LSE, f"{key} Q ties")
+
+
 @pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
                                  "cfg3_nvfp4"])
 def test_gather_probe_bit_exact(mj, gpu, key):
