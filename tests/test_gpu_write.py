@@ -266,3 +266,63 @@ def test_write_ties_and_grid_points(mj, gpu, kv_format):
                    slots, ones, ones, "channel")
     assert np.array_equal(k_pool.cpu().numpy(), ref[0])
     assert np.array_equal(v_pool.cpu().numpy(), ref[1])
+
+
+def test_write_nvfp4_ties(mj, gpu):
+    """nvfp4 blocks whose amax is 6 (block scale exactly 1) holding every
+    e2m1 grid value and every midpoint (ties to even), both signs, and blocks
+    whose amax / 6 is itself an e4m3 midpoint (the scale's own tie): codes
+    and scale bytes equal the oracle's."""
+    from oracle import formats as F
+    from oracle.kvwrite import write_kv
+    grid = np.unique(F.E2M1_TABLE[:0x8])
+    mids = (grid[:-1] + grid[1:]) / 2
+    body = np.concatenate([grid, mids, -grid, -mids]).astype(np.float32)  # 28 values
+    e4 = np.unique(F.E4M3_TABLE[:0x7F])
+    e4mid = (e4[:-1] + e4[1:]) / 2  # amax = 6 * e4mid: the block scale ties
+    h_k, d, P = 2, 128, 16
+    blocks = []
+    for k in range(0, len(body), 15):
+        b = np.zeros(16, np.float32)
+        b[0] = 6.0
+        chunk = body[k:k + 15]
+        b[1:1 + len(chunk)] = chunk
+        blocks.append(b)
+    for m in e4mid[::5]:
+        b = np.zeros(16, np.float32)
+        b[0] = 6.0 * m
+        b[1:8] = np.float32(m) * grid[1:]
+        blocks.append(b)
+    flat = np.concatenate(blocks)
+    n = -(-flat.size // (h_k * d)) + 1
+    buf = np.zeros(n * h_k * d, np.float32)
+    buf[:flat.size] = flat
+    kt = torch.from_numpy(buf).to(torch.bfloat16)
+    keep = kt.float().numpy() == buf  # values not exact in bf16 would not be ties: drop them
+    buf[~keep] = 0.0
+    key = torch.from_numpy(buf).to(torch.bfloat16).view(n, h_k, d)
+    value = key.flip(0).contiguous()
+    pages = -(-n // P) + 1
+    row = F.ROW_BYTES["nvfp4"]
+    ks = vs = _strides("HND", P, h_k, row)
+    bst = _strides("HND", P, h_k, 8)
+    rng = np.random.default_rng(6)
+    init_k = rng.integers(0, 256, pages * P * h_k * row, dtype=np.uint8)
+    init_v = rng.integers(0, 256, pages * P * h_k * row, dtype=np.uint8)
+    init_kb = rng.integers(0, 256, pages * P * h_k * 8, dtype=np.uint8)
+    init_vb = rng.integers(0, 256, pages * P * h_k * 8, dtype=np.uint8)
+    k_pool = torch.from_numpy(init_k.copy()).to(gpu)
+    v_pool = torch.from_numpy(init_v.copy()).to(gpu)
+    bs = (torch.from_numpy(init_kb.copy()).to(gpu), torch.from_numpy(init_vb.copy()).to(gpu), bst, bst)
+    slots = np.arange(n, dtype=np.int64)
+    ones = np.ones((h_k, d), np.float32)
+    say(f"write nvfp4 ties: {len(blocks)} blocks over {n} tokens")
+    cfg = mj.mj_config(h_q=h_k, h_k=h_k, page_size=P, max_num_seqs=1, kv_format="nvfp4", num_cus=256)
+    _write(mj, gpu, cfg, key.to(gpu), value.to(gpu), torch.from_numpy(slots).to(gpu), k_pool, v_pool, ks, vs,
+           torch.from_numpy(ones).to(gpu), torch.from_numpy(ones).to(gpu), "channel", pages, bs)
+    ref = write_kv((init_k, init_v), (ks, vs), P, "nvfp4", key.float().numpy(), value.float().numpy(), slots,
+                   ones, ones, "channel", bs_pools=(init_kb, init_vb), bs_strides=(bst, bst))
+    assert np.array_equal(k_pool.cpu().numpy(), ref[0])
+    assert np.array_equal(v_pool.cpu().numpy(), ref[1])
+    assert np.array_equal(bs[0].cpu().numpy(), ref[2])
+    assert np.array_equal(bs[1].cpu().numpy(), ref[3])
