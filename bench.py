@@ -12,6 +12,12 @@ too but leave it full of dirty lines whose write-back then competes with the
 step's loads -- a state no serving step starts from; the graph step after
 such a write is reported as well, ``graph_us_per_step_median_after_write``.)
 
+The headline workload is 64 sequences of 32768 tokens each (32/8 heads,
+token-major pages of 64, e4m3 KV); every other workload is measured the
+same way under ``extra`` and summarised under ``configs``.  Before any
+timing, one replay of each captured graph must give the eager step's output
+(host planner, same kernels) bit for bit, or the run stops.
+
 Prints one JSON line.  ``value`` is the achieved KV-read bandwidth of the
 step (KV bytes / mean graph step time); ``detail`` also has the eager step
 (host planner + fused step) and the eager three-call step (quantize, decode,
@@ -25,7 +31,7 @@ workload.  ``bf16_q`` measures the same step in the bf16-Q mode (Q used as
 given, no quantization; the KV codes converted to bf16 in the kernel) on the
 workloads ``--bf16q`` names.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--extra 32k,cfg3,...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 32k] [--extra cfg2,cfg3,...]
 """
 
 from __future__ import annotations
@@ -40,7 +46,9 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
-STEP_MERGE = 0  # mj_decode_step merge mode of the timed steps (--step-merge)
+# kernel selection of every measured step (mj_config fields; --variant,
+# --cache-policy, --step-merge): 0 = the library's choice
+KSEL = dict(decode_kernel=0, kv_cache_policy=0, step_merge=0)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -92,27 +100,30 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="cfg2")
-    ap.add_argument("--extra", default="32k,32k_b16,cfg5,cfg5_e3m2,cfg5_e2m1,cfg5_nvfp4",
+    ap.add_argument("--workload", default="32k",
+                    help="the headline workload: 64 sequences of 32768 tokens, token-major pages of 64, e4m3 KV")
+    ap.add_argument("--extra", default="cfg1,cfg2,cfg3,cfg4c,cfg4n,cfg5,32k_b16,cfg5_e3m2,cfg5_e2m1,cfg5_nvfp4",
                     help="comma list of extra workloads reported under 'extra' ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--bf16q", default="cfg2,32k",
                     help="comma-separated workloads also measured in the bf16-Q mode ('' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--variant", type=int, default=0,
-                    help="decode kernel: 0 automatic, 1 generic, 2 VALU-PV streaming (A/B runs)")
-    ap.add_argument("--no-nt", action="store_true", help="plain (not non-temporal) KV loads (A/B runs)")
+                    help="mj_config.decode_kernel: 0 automatic, 1 generic, 10..17 matrix-core tuning (A/B runs)")
+    ap.add_argument("--cache-policy", type=int, default=0,
+                    help="mj_config.kv_cache_policy: 0 the library's choice, 1..4 (A/B runs)")
     ap.add_argument("--wgs-per-cu", type=int, default=0, help="planner workgroups per CU (0 = library default)")
     ap.add_argument("--no-stream-read", action="store_true",
                     help="skip the plain streaming read of the main workload's KV pool (HBM context figure)")
     ap.add_argument("--step-merge", type=int, default=0,
-                    help="mj_decode_step merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
+                    help="mj_config.step_merge: 0 automatic, 1 in the decode kernel, 2 separate launch (A/B runs)")
     ap.add_argument("--no-write", action="store_true", help="skip the KV-cache write measurement")
     ap.add_argument("--cp", default="cfg3:8",
                     help="context-parallel share measured as WORKLOAD:G (one GPU's slice of each context, "
                          "and the combine of G slices); '' = skip")
     ap.add_argument("--draft", type=int, default=4,
-                    help="draft steps of the multi-step draft loop measured on the workload (0 = skip)")
+                    help="draft steps of the multi-step draft loop (0 = skip)")
+    ap.add_argument("--draft-workload", default="cfg2", help="workload of the draft loop")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run the HBM-counter calibration kernels (256 MiB streaming read, 256 MiB copy) and exit")
     return ap.parse_args()
@@ -162,7 +173,7 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
     wl = synth.build(synth.spec_for(key), "cuda")
     torch.cuda.synchronize()
     log(f"[bench] {key}: built {wl.spec.name} in {time.time() - t0:.1f}s, kv_bytes={wl.kv_bytes()}")
-    step = DecodeStep.for_workload(wl, wgs_per_cu=wgs_per_cu, q_mode=q_mode)
+    step = DecodeStep.for_workload(wl, wgs_per_cu=wgs_per_cu, q_mode=q_mode, **KSEL)
     out, lse = new_output(wl)
     stream = torch.cuda.current_stream()
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -232,10 +243,25 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in gev])
 
-    # the two graphs timed in alternating chunks, so that neither gains or
-    # loses from its place in the run
+    # the timed graph's result, before any timing: bit for bit the eager
+    # step on the host planner's plan (same kernels, same plan)
     graph = capture(False)
     graph_pk = capture(True)
+    ref_out, ref_lse = torch.empty_like(out), torch.empty_like(lse)
+    step.plan_workload(wl, stream=stream)
+    step.run_workload(wl, ref_out, ref_lse, info=step.info, stream=stream, fused=True)
+    torch.cuda.synchronize()
+    for gr_chk in (graph, graph_pk):
+        out.fill_(float("nan"))
+        gr_chk.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                            ref_out.view(torch.int16) if out.dtype == torch.bfloat16 else ref_out)
+                and torch.equal(lse, ref_lse)):
+            raise RuntimeError(f"{key}: the graph step's output differs from the eager host-plan step")
+    del ref_out, ref_lse
+    # the two graphs timed in alternating chunks, so that neither gains or
+    # loses from its place in the run
     chunks = 4
     parts, parts_pk = [], []
     for i in range(chunks):
@@ -259,40 +285,39 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
     ks, vs = wl.kv_strides()
     bss = wl.bs_strides() if wl.k_bs_pool is not None else (None, None)
 
+    # the same step with the merge as a launch of its own (step_merge 2), so
+    # that the merge launches can be timed alone and subtracted
+    step2 = DecodeStep.for_workload(wl, wgs_per_cu=wgs_per_cu, q_mode=q_mode, **dict(KSEL, step_merge=2))
+
     def launch(i):
         kp, vp, kb, vb = pools[i % len(pools)]
-        step.run(k_block_scale=kb, v_block_scale=vb, k_bs_strides=bss[0], v_bs_strides=bss[1],
+        step2.run(k_block_scale=kb, v_block_scale=vb, k_bs_strides=bss[0], v_bs_strides=bss[1],
                  q=wl.q, k_cache=kp, v_cache=vp, k_strides=ks, v_strides=vs, num_pages=wl.num_pages,
                  block_table=wl.block_table, seq_lens=wl.seq_lens_dev, k_descale=wl.k_descale,
                  v_descale=wl.v_descale, descale_kind=wl.descale_kind, softmax_scale=wl.softmax_scale, out=out,
                  lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul, causal=wl.spec.causal, info=info, stream=stream,
                  fused=True)
 
-    import paged_fp8_decode_amd as mjlib
-    step.plan_workload(wl, stream=stream)
+    info = step2.plan_workload(wl, stream=stream)
     torch.cuda.synchronize()
-    mjlib.mj_debug_set_step_merge(2)
-    try:
-        for i in range(len(pools)):
-            launch(i)
-        torch.cuda.synchronize()
-        k0, k1 = E(), E()
-        k0.record(stream)
+    for i in range(len(pools)):
+        launch(i)
+    torch.cuda.synchronize()
+    k0, k1 = E(), E()
+    k0.record(stream)
+    for i in range(reps):
+        launch(i)
+    k1.record(stream)
+    merge_us = 0.0
+    if info.with_reduction:
+        m0, m1 = E(), E()
+        m0.record(stream)
         for i in range(reps):
-            launch(i)
-        k1.record(stream)
-        merge_us = 0.0
-        if info.with_reduction:
-            m0, m1 = E(), E()
-            m0.record(stream)
-            for i in range(reps):
-                step.merge(out, lse, info, stream)
-            m1.record(stream)
-        torch.cuda.synchronize()
-        if info.with_reduction:
-            merge_us = m0.elapsed_time(m1) * 1e3 / reps
-    finally:
-        mjlib.mj_debug_set_step_merge(STEP_MERGE)
+            step2.merge(out, lse, info, stream)
+        m1.record(stream)
+    torch.cuda.synchronize()
+    if info.with_reduction:
+        merge_us = m0.elapsed_time(m1) * 1e3 / reps
     step_us_b2b = k0.elapsed_time(k1) * 1e3 / reps
     kernel_us = step_us_b2b - merge_us
     del pools
@@ -317,7 +342,9 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
         kernel_launches=reps, kv_pool_copies=n_copies,
         kernel_kv_gbs=kvb / (kernel_us * 1e-6) / 1e9,
         plan=dict(num_work=info.num_work, slots=info.slots, chunk_tiles=info.chunk_tiles,
-                  min_chunk_tiles=info.min_chunk_tiles, with_reduction=info.with_reduction),
+                  min_chunk_tiles=info.min_chunk_tiles, wgs_per_cu=info.wgs_per_cu,
+                  with_reduction=info.with_reduction),
+        graph_step_equals_host_plan_step=True,
         timed_wall_s=t_wall,
     )
     res["kernel_frac_of_hbm_peak"] = res["kernel_kv_gbs"] / HBM_PEAK_GBS
@@ -407,9 +434,25 @@ def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
                 frac_of_hbm_peak=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4))
 
 
+def host_cpu():
+    """(cores this process may run on, CPU model name) of the host."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
 def cpu_baseline(key, budget_s):
-    """The oracle as it stands, single-threaded BLAS, on whole (sequence, KV
-    head) pairs of the same workload until ~budget_s seconds of CPU work."""
+    """The oracle as it stands on whole (sequence, KV head) pairs of the same
+    workload until ~budget_s seconds of wall time, with BLAS threads = the
+    cores this process may use."""
     import torch
     import synth
     from oracle.attention import decode_step
@@ -418,12 +461,13 @@ def cpu_baseline(key, budget_s):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
 
+    cores, model = host_cpu()
     spec = synth.spec_for(key)
     wl = synth.build(spec, "cuda")
     s = wl.spec
     order = [(i, g) for i in range(s.b) for g in range(s.h_k)]
     done, nbytes, t_used = 0, 0, 0.0
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
     try:
         for i in np.random.default_rng(0).permutation(s.b).tolist():
             h = wl.host([i])
@@ -433,7 +477,7 @@ def cpu_baseline(key, budget_s):
                             kv_format=s.kv_format, causal=s.causal, pairs=[(0, g)])
                 t_used += time.perf_counter() - t0
                 done += 1
-                nbytes += wl.seq_lens[i] * 2 * s.row_bytes
+                nbytes += wl.seq_lens[i] * 2 * (s.row_bytes + s.scale_row_bytes)
                 if t_used >= budget_s:
                     break
             if t_used >= budget_s:
@@ -443,10 +487,11 @@ def cpu_baseline(key, budget_s):
             ctx.restore_original_limits()
     del wl
     torch.cuda.empty_cache()
-    return dict(value=nbytes / t_used / 1e9, unit="GB/s", cores=1, kind="oracle",
+    return dict(value=nbytes / t_used / 1e9, unit="GB/s", cores=cores, cpu_model=model, kind="oracle",
+                blas_threads=cores,
                 sample=f"{done} of {len(order)} (sequence, KV head) pairs of {spec.name} "
-                       f"(each a full Q quantization + gather + fp64 attention), {t_used:.1f} s of CPU time, "
-                       f"single-threaded NumPy/BLAS",
+                       f"(each a full Q quantization + gather + fp64 attention), {t_used:.1f} s wall, "
+                       f"NumPy with {cores} BLAS threads on {model}",
                 seconds_per_step_extrapolated=t_used * len(order) / done)
 
 
@@ -647,10 +692,7 @@ def main():
         calibrate()
         return
 
-    paged_fp8_decode_amd.mj_debug_set_decode_variant(args.variant, 0 if args.no_nt else 1)
-    global STEP_MERGE
-    STEP_MERGE = args.step_merge
-    paged_fp8_decode_amd.mj_debug_set_step_merge(args.step_merge)
+    KSEL.update(decode_kernel=args.variant, kv_cache_policy=args.cache_policy, step_merge=args.step_merge)
 
     flush = Flusher()
     main_res = measure(args.workload, args.steps, args.warmup, flush, args.wgs_per_cu, not args.no_stream_read)
@@ -674,7 +716,7 @@ def main():
         cp = measure_cp(cp_key, int(cp_g), max(10, args.steps // 2), flush)
     draft = None
     if args.draft > 0:
-        draft = measure_draft(args.workload, args.draft, max(10, args.steps // 2), flush)
+        draft = measure_draft(args.draft_workload, args.draft, max(10, args.steps // 2), flush)
     cpu = None if args.no_cpu else cpu_baseline(args.workload, args.cpu_seconds)
     kvb = main_res["kv_bytes"]
     dec_s = main_res["kernel_us_back_to_back"] * 1e-6
@@ -684,6 +726,13 @@ def main():
                        "and subtracted)",
                 algorithmic_bytes_per_launch=kvb, kernel_us=round(main_res["kernel_us_back_to_back"], 2),
                 traffic_unit="bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)")
+    # every workload at a glance: graph step, decode kernel and its share of the HBM peak
+    configs = {k: dict(workload=r["workload"], kv_bytes=r["kv_bytes"],
+                       graph_us_per_step_median=round(r["graph_us_per_step_median"], 2),
+                       decode_kernel_us=round(r["kernel_us_back_to_back"], 2),
+                       kernel_frac_of_hbm_peak=round(r["kernel_frac_of_hbm_peak"], 4),
+                       with_reduction=r["plan"]["with_reduction"])
+               for k, r in [(args.workload, main_res)] + list(extra.items())}
     line = dict(
         metric="paged decode us/step and achieved KV-read HBM GB/s (% of MI355X peak)",
         value=round(main_res["graph_step_kv_gbs"], 1),
@@ -699,10 +748,11 @@ def main():
         dtype=main_res["kv_format"],
         data="synthetic",
         config=dict(workload=main_res["workload"], kv_bytes=kvb, plan=main_res["plan"], kernel_variant=args.variant,
-                    nontemporal=not args.no_nt, step_merge=args.step_merge,
+                    kv_cache_policy=args.cache_policy, step_merge=args.step_merge,
                     step="hipGraph: mj_decode_step with plan_on_device (decode + merge launches)"),
         roofline=roof,
         cpu_baseline=cpu,
+        configs=configs,
         detail=main_res,
         extra=extra,
         bf16_q=bf16q,

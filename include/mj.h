@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MJ_ABI_VERSION 8
+#define MJ_ABI_VERSION 9
 
 typedef enum mj_status {
   MJ_OK = 0,
@@ -124,6 +124,29 @@ typedef struct mj_config {
   int32_t out_f32;         /* 0: outputs `out` are bf16; 1: fp32 (a context-
                               parallel slice's result, combined later by
                               mj_combine_lse without rounding in between)    */
+  /* Kernel selection of this decode site (0 = the library's choice; the
+     other values exist for A/B measurements and for testing every kernel
+     on the same inputs; results agree within the output tolerance, plans
+     and codes bit for bit):                                               */
+  int32_t decode_kernel;   /* 0 automatic (the matrix-core kernel wherever the
+                              plan's KV tiles are whole 16-token tiles and
+                              slot strides are < 2^24 bytes, else the generic
+                              kernel); 1 always the generic LDS-tiled kernel;
+                              10..17 the matrix-core kernel with tuning bits
+                              (value - 10): bit 0 two granules of prefetch,
+                              bit 1 head-major grid, bit 2 XCD-grouped grid
+                              (the KV heads of a work item on one XCD; takes
+                              precedence over bit 1)                         */
+  int32_t kv_cache_policy; /* matrix-core kernel KV loads: 0 the library's
+                              choice (K cached, V non-temporal), 1 every load
+                              cached, 2 every load non-temporal, 3 K cached
+                              and V non-temporal, 4 K non-temporal and V
+                              cached                                         */
+  int32_t step_merge;      /* where mj_decode_step merges split partials when
+                              it fuses the step: 0 automatic (the separate
+                              merge launch), 1 in the decode kernel (the last
+                              split item of a (sequence, KV head) to finish),
+                              2 the separate merge launch                    */
 } mj_config;
 /* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):
  * e4m3 with n_q <= 16 -> 8 / 2048 (the matrix-core kernel runs two
@@ -143,6 +166,8 @@ typedef struct mj_plan_info {
   int32_t q_len;
   int32_t kv_tile_tokens;
   int32_t min_chunk_tiles;  /* floor of the chunk for this q_len                */
+  int32_t wgs_per_cu;       /* workgroups per CU the slot count was sized with
+                               (the config's value or the default above)      */
 } mj_plan_info;
 
 /* Arguments of mj_paged_decode.  All strides are in BYTES for the KV cache and
@@ -237,19 +262,29 @@ mj_status mj_config_check(const mj_config* cfg);
 size_t mj_plan_buffer_bytes(const mj_config* cfg);
 size_t mj_workspace_bytes(const mj_config* cfg);
 
-/* Capacity (= decode grid size) for q_len; -1 on error.  Host only (queries
- * the current device when cfg->num_cus == 0). */
+/* Largest decode grid (work items) any plan for q_len can have: max(S,
+ * max_num_seqs), S as below; -1 on error.  Host only (queries the current
+ * device when cfg->num_cus == 0).  A plan's own grid is mj_plan_info.num_work,
+ * which is never larger. */
 int32_t mj_plan_capacity(const mj_config* cfg, int32_t q_len);
 
 /* The split-KV plan (README "What it does", step 1; runner.py
  * T5DecodeRunner.plan and __init__ "Capacity per q_len"):
  *   slots S = max(1, num_cus*wgs_per_cu / (h_k*ceil(q_len*h_r/64))), or the
- *   override; capacity = max(S, max_num_seqs); tiles_i =
- *   ceil((seq_lens_host[i] + margin) / kv_tile_tokens).  A batch smaller
- *   than S (and max_splits > 1) is split with the smallest chunk c >=
- *   max(ceil(max tiles / max_splits), min chunk tiles) whose item count
- *   sum_i max(1,ceil(tiles_i/c)) fits S; otherwise one item per sequence.  Items (seq, tile_begin,
- *   tile_end, split) are sequence-major and padded with (-1,0,0,0).
+ *   override; with T = max_blocks_per_seq * page_size (the tokens a block-table
+ *   row addresses; nothing past them is ever read), tiles_i =
+ *   ceil(min(seq_lens_host[i] + margin, T) / kv_tile_tokens).  The plan
+ *   splits iff max_splits > 1, num_seqs < S and ceil(T / kv_tile_tokens) >
+ *   min chunk tiles (a sequence filling its row could be cut in two; else
+ *   every sequence is one item whatever the lengths and no merge is
+ *   needed).  A split plan takes the smallest chunk c >= max(ceil(max tiles
+ *   / max_splits), min chunk tiles) whose item count sum_i
+ *   max(1,ceil(tiles_i/c)) fits S; otherwise one item per sequence.  Items
+ *   (seq, tile_begin, tile_end, split) are sequence-major and padded with
+ *   (-1,0,0,0).  The grid num_work is max(S, max_num_seqs) for a plan that
+ *   may split and max_num_seqs for one that cannot: it depends on the
+ *   config, q_len, num_seqs and max_blocks_per_seq only, never on the
+ *   lengths, so a captured step replays later plans of that batch.
  * mj_plan_compute writes the whole plan image into plan_host
  * (mj_plan_buffer_bytes bytes) without touching the device.
  * mj_plan_split_kv does the same into `host_staging` (pinned, caller-owned;
@@ -277,10 +312,12 @@ mj_status mj_plan_split_kv_device(const mj_config* cfg, const int32_t* seq_lens_
                                   int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev, mj_plan_info* info,
                                   hipStream_t stream);
 
-/* What a plan for (num_seqs, q_len) has regardless of the lengths: num_work,
- * slots, with_reduction, kv_tile_tokens, min_chunk_tiles (chunk_tiles =
+/* What a plan for (num_seqs, q_len) over block-table rows of
+ * max_blocks_per_seq pages has regardless of the lengths: num_work, slots,
+ * with_reduction, kv_tile_tokens, min_chunk_tiles, wgs_per_cu (chunk_tiles =
  * num_chunks = -1).  Host only.  Errors: EINVAL, ECAPACITY. */
-mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, mj_plan_info* info);
+mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, int32_t max_blocks_per_seq,
+                        mj_plan_info* info);
 
 /* Dynamic e4m3 quantization of Q per (sequence, KV head) (README "What it
  * does", step 2; runner.py T5DecodeRunner.run, fp8-Q branch): over the q_len
@@ -456,7 +493,7 @@ typedef struct mj_step_args {
  * tiles, slot strides < 2^24 bytes), every decode workgroup quantizes its
  * (sequence, KV head)'s Q rows in its prologue with the quantize kernel's
  * arithmetic, so the step is the decode launch plus, for a split plan, the
- * merge launch; optionally (mj_debug_set_step_merge) the last split item of
+ * merge launch; optionally (cfg->step_merge = 1) the last split item of
  * a pair to finish merges in the decode kernel itself (device-coherent
  * partials, an arrival counter in the workspace) and the step is one
  * launch.  Otherwise it enqueues the three kernels, staging Q codes in the
@@ -485,27 +522,6 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStre
 mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* args, int32_t seq, int32_t head,
                              int32_t seq_len, int32_t which, uint8_t* dense_out, hipStream_t stream);
 mj_status mj_debug_decode_codes(int32_t kv_format, const uint8_t* codes, int32_t n, float* out, hipStream_t stream);
-/* Process-wide choice of decode kernel, for A/B measurements and for testing
- * every kernel on the same inputs: variant 0 = automatic (the matrix-core
- * kernel wherever the plan's KV tiles are whole 16-token tiles and slot
- * strides are < 2^24 bytes, groups of more than 32 rows as several 32-row
- * tiles; otherwise the generic LDS-tiled kernel), 1 = always the
- * generic kernel, 2 = the VALU-PV streaming kernel for e4m3 with
- * q_len*h_r <= 4 (automatic otherwise), 3 = same as 0, 10..17 = the
- * matrix-core kernel with tuning bits (variant - 10): bit 0 two granules of
- * prefetch, bit 1 head-major grid, bit 2 XCD-grouped grid (the KV heads of a
- * work item on one XCD; takes precedence over bit 1).  nontemporal selects the
- * streaming kernels' KV load cache policy: 1 (default) the library's choice
- * per format, 0 every load cached, 2 every load non-temporal, 3 K cached and
- * V non-temporal, 4 K non-temporal and V cached (the VALU-PV kernel: any
- * value but 0 is non-temporal).  Not thread-safe; set it before
- * launching.  EINVAL on other values. */
-mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal);
-/* Where mj_decode_step merges split partials when it fuses the step: 0 =
- * automatic (currently the separate launch), 1 = in the decode kernel (last
- * split item), 2 = a separate merge launch after it.  Results are
- * identical.  Process-wide, not thread-safe.  EINVAL on other values. */
-mj_status mj_debug_set_step_merge(int32_t mode);
 /* Plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
  * non-temporal 16-byte loads by `blocks` workgroups of 256 threads, each
  * writing one xor checksum to out[block]: the practical HBM read ceiling the

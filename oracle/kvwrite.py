@@ -12,7 +12,9 @@ scales s_c (h_k, d) quantize the cache write").  Neither kernel is printed;
 the readings taken, the plainest the text supports:
 
 * slot ``s`` of token ``t`` is page ``s // page_size``, row ``s % page_size``;
-  a negative slot (a padding token) writes nothing;
+  a negative slot (a padding token) writes nothing, and neither does a slot
+  in a page at or past ``num_pages`` (the pool's size: such a slot addresses
+  no row of the cache);
 * code = the format's round-to-nearest-even of ``x / scale`` in fp32 (one
   IEEE division, x = fp32 of the bf16 input), saturated at the format's
   largest magnitude (448 for e4m3, 7.5 for e2m3, 28 for e3m2, 6 for e2m1);
@@ -82,14 +84,15 @@ def encode_row(x_bf16_as_f32: np.ndarray, divisor: np.ndarray, kv_format: str):
 
 
 def write_kv(pools, strides, page_size: int, kv_format: str, key, value, slot_mapping, k_scale, v_scale,
-             scale_kind: str, bs_pools=None, bs_strides=None):
+             scale_kind: str, bs_pools=None, bs_strides=None, num_pages=None):
     """Apply the write to copies of the two byte pools and return them.
 
     pools: (k_pool, v_pool) flat uint8 arrays; strides: ((page, slot, head)
     byte strides of K), (same for V)); key/value: float32 arrays
     (num_tokens, h_k, 128) holding the bf16 inputs exactly.  nvfp4 also takes
     the two block-scale pools and their strides, and returns four pools
-    (k, v, k block scales, v block scales).
+    (k, v, k block scales, v block scales).  ``num_pages``: pages in each
+    pool (None: every page the strides reach).
     """
     k_pool, v_pool = (np.array(p, dtype=np.uint8, copy=True).reshape(-1) for p in pools)
     nv = kv_format == "nvfp4"
@@ -103,6 +106,8 @@ def write_kv(pools, strides, page_size: int, kv_format: str, key, value, slot_ma
         if s < 0:
             continue
         page, off = divmod(s, page_size)
+        if num_pages is not None and page >= num_pages:
+            continue
         for g in range(h_k):
             for side in range(2):
                 pool, st, x, sc = ((k_pool, strides[0], key, k_scale), (v_pool, strides[1], value, v_scale))[side]

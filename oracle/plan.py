@@ -30,13 +30,23 @@ this project's reading (the plainest one consistent with them):
 * items are sequence-major, split-minor, padded to ``cap`` with
   ``(-1, 0, 0, 0)``; ``split_begin`` is the exclusive prefix sum of ``n``.
 
-One addition of this library, not in the pages: the chunk also has a floor
-``min_chunk_tiles`` (default 1, which is the rule above).  The pages size
-the split for one wave of 40 CTAs; on 256 CUs the library plans several
-waves of items (``wgs_per_cu`` above the residency) to balance the tail,
-and the floor keeps each item long enough to amortise its prologue and
-partial write.  ``default_shape`` is the library's table of defaults for
-``wgs_per_cu`` and the floor, by KV format and query rows per KV head.
+Two parameters of the rule are not on the pages, and the rule takes them as
+given rather than choosing them: the chunk floor ``min_chunk_tiles`` (1 is
+the rule above) and the workgroups per CU behind ``slots``.  A caller that
+compares a library's plans with this rule passes the values that library
+reports for the plan.
+
+Block-table width (``max_len``, tokens; ``None`` = unbounded).  A sequence
+never holds more tokens than its block-table row can address, and nothing
+past that is read, so a plan made ``margin`` tokens long covers at most
+``max_len``: ``tiles_i = ceil(min(L_i + margin, max_len) / kv_tile)``.  And
+when even a sequence that fills the row is no longer than the chunk floor
+(``ceil(max_len / kv_tile) <= min_chunk_tiles``) every sequence is one item
+whatever the lengths, so the plan does not split and needs no merge: the
+pages' "never split, no merge kernel" case of ``max_splits == 1``, reached
+here from the table width instead.  Such a plan has only ``max_num_seqs``
+possible items, and its grid (``num_work``) is that; the decision and the
+grid depend on the configuration and the table width, never on the lengths.
 
 Row tiles here hold up to 64 query rows (one GQA group of up to 64 rows reads
 its KV once); the pages' Thor kernel used at most 32.
@@ -62,22 +72,6 @@ def capacity(q_len, h_q, h_k, num_cus, wgs_per_cu, max_num_seqs, slots_override=
     return max(s, max_num_seqs)
 
 
-def default_shape(kv_format: str, n_q: int) -> tuple[int, int]:
-    """(wgs_per_cu, min_chunk_tokens) the library uses when the config leaves
-    them 0: the e4m3 matrix-core kernel for up to 16 rows runs two
-    workgroups per CU and is planned four waves deep with items of at least
-    2048 tokens; the e2m1 and nvfp4 kernels (half-size rows) of up to 32
-    rows two per CU; everything else (the 32-row kernel, the fp6 kernels,
-    groups of more than 32 rows served as several 32-row tiles) one wave
-    deep.  A tuning choice of the library, mirrored here so that the plans
-    compare bit for bit; the pages fix no plan depth."""
-    if kv_format == "e4m3" and n_q <= 16:
-        return 8, 2048
-    if n_q <= 32 and kv_format in ("e2m1", "nvfp4"):
-        return 2, 1
-    return 1, 1
-
-
 def plan_split_kv(
     lens,
     *,
@@ -93,13 +87,18 @@ def plan_split_kv(
     margin: int = 0,
     row_tile: int = ROW_TILE,
     min_chunk_tiles: int = 1,
+    max_len: int | None = None,
 ) -> dict:
     b = len(lens)
     assert 0 < b <= max_num_seqs
     S = slots_override if slots_override > 0 else slots(q_len, h_q, h_k, num_cus, wgs_per_cu, row_tile)
-    cap = max(S, max_num_seqs)
-    tiles = [math.ceil((int(L) + margin) / kv_tile) for L in lens]
-    split = max_splits > 1 and b < S
+    if max_len is not None:
+        assert all(0 <= int(L) <= max_len for L in lens)
+    splittable = max_len is None or math.ceil(max_len / kv_tile) > min_chunk_tiles
+    cap = max(S, max_num_seqs) if splittable else max_num_seqs
+    reach = [int(L) + margin if max_len is None else min(int(L) + margin, max_len) for L in lens]
+    tiles = [math.ceil(x / kv_tile) for x in reach]
+    split = max_splits > 1 and b < S and splittable
     if split:
         c = max(1, math.ceil(max(tiles) / max_splits), min_chunk_tiles)
         while sum(max(1, math.ceil(t / c)) for t in tiles) > S:

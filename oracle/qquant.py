@@ -2,11 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-Source: mjolnir-kernel 0.1.0 wheel, mjolnir/runner.py, ``T5DecodeRunner.run``
-(the fp8-Q branch) and the ``FP8_MAX = 448`` constant; PyPI project page,
-"What it does", step 2 ("dynamic e4m3 per (sequence, KV head)").  Per
-sequence i and KV head g, over the q_len tokens and the h_r query heads of
-that group:
+Source: the mjolnir-kernel 0.1.0 PyPI project page, section "What it does",
+step 2 (Q is quantized to e4m3 dynamically, one scale for each sequence and
+KV head), and the wheel listing mjolnir/runner.py, the fp8-Q branch of
+``T5DecodeRunner.run`` with its ``FP8_MAX`` constant of 448.  For sequence i
+and KV head g, over the q_len tokens and the h_r query heads that share g:
 
     x     = fp32(q)                      (times the fp32 q_mul, if given:
                                           one fp32 multiply, before the amax)
@@ -15,9 +15,10 @@ that group:
     code  = e4m3(x / scale)              (fp32 IEEE division, then RNE)
     q_descale[i, g] = scale
 
-and the rows are packed ``t * h_r + r`` for token t and query head
-``g * h_r + r`` (the ``reshape(b, ql, h_k, h_r, d).permute(0, 2, 1, 3, 4)``
-of that branch).  Every step is fp32 as on the pages; the division is a true
+The codes of one pair form n_q = q_len * h_r rows, token-major: row
+t * h_r + r holds token t of query head g * h_r + r (the runner groups the
+query heads by KV head and puts the tokens of each group in front of its
+heads).  Every step is fp32 as on the pages; the division is a true
 division, not a multiply by a reciprocal.
 """
 

@@ -37,12 +37,13 @@ def _ptr(t):
 
 def mj_config(*, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, num_cus=0, wgs_per_cu=0,
               kv_tile_tokens=0, slots_override=0, kv_format="e4m3", head_dim=128, min_chunk_tokens=0,
-              q_mode="fp8", out_f32=False) -> Config:
+              q_mode="fp8", out_f32=False, decode_kernel=0, kv_cache_policy=0, step_merge=0) -> Config:
     c = Config(h_q=h_q, h_k=h_k, head_dim=head_dim, page_size=page_size, max_num_seqs=max_num_seqs,
                max_q_len=max_q_len, max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
                kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, min_chunk_tokens=min_chunk_tokens,
                kv_format=KV_FORMATS[kv_format] if isinstance(kv_format, str) else kv_format,
-               q_mode=Q_MODES[q_mode] if isinstance(q_mode, str) else q_mode, out_f32=int(bool(out_f32)))
+               q_mode=Q_MODES[q_mode] if isinstance(q_mode, str) else q_mode, out_f32=int(bool(out_f32)),
+               decode_kernel=decode_kernel, kv_cache_policy=kv_cache_policy, step_merge=step_merge)
     return c
 
 
@@ -99,9 +100,10 @@ def mj_plan_split_kv_device(cfg: Config, seq_lens_dev, num_seqs: int, q_len: int
     return info
 
 
-def mj_plan_shape(cfg: Config, num_seqs: int, q_len: int) -> PlanInfo:
+def mj_plan_shape(cfg: Config, num_seqs: int, q_len: int, max_blocks_per_seq: int) -> PlanInfo:
     info = PlanInfo()
-    check(lib().mj_plan_shape(ctypes.byref(cfg), num_seqs, q_len, ctypes.byref(info)), "mj_plan_shape")
+    check(lib().mj_plan_shape(ctypes.byref(cfg), num_seqs, q_len, max_blocks_per_seq, ctypes.byref(info)),
+          "mj_plan_shape")
     return info
 
 
@@ -162,14 +164,6 @@ def mj_debug_decode_codes(kv_format, codes, out, stream=None):
     fmt = {**KV_FORMATS, "e4m3_bf16": 16}[kv_format] if isinstance(kv_format, str) else kv_format
     check(lib().mj_debug_decode_codes(fmt, _ptr(codes), codes.numel(), _ptr(out), _stream(stream)),
           "mj_debug_decode_codes")
-
-
-def mj_debug_set_decode_variant(variant: int, nontemporal: int = 1):
-    check(lib().mj_debug_set_decode_variant(variant, nontemporal), "mj_debug_set_decode_variant")
-
-
-def mj_debug_set_step_merge(mode: int):
-    check(lib().mj_debug_set_step_merge(mode), "mj_debug_set_step_merge")
 
 
 def mj_debug_stream_read(src, out, blocks: int, stream=None):

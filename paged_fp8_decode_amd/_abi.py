@@ -8,7 +8,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmj.so")
 
-ABI_VERSION = 8  # MJ_ABI_VERSION of include/mj.h this binding matches
+ABI_VERSION = 9  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
 KV_FORMATS = {"e4m3": 0, "e2m3": 1, "e3m2": 2, "e2m1": 3, "nvfp4": 4}
 Q_MODES = {"fp8": 0, "bf16": 1}
@@ -25,13 +25,14 @@ class MjError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "h_q", "h_k", "head_dim", "page_size", "max_num_seqs", "max_q_len", "max_splits", "num_cus",
-        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens", "q_mode", "out_f32")]
+        "wgs_per_cu", "kv_tile_tokens", "slots_override", "kv_format", "min_chunk_tokens", "q_mode", "out_f32",
+        "decode_kernel", "kv_cache_policy", "step_merge")]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_work", "slots", "chunk_tiles", "num_chunks", "with_reduction", "num_seqs", "q_len", "kv_tile_tokens",
-        "min_chunk_tiles")]
+        "min_chunk_tiles", "wgs_per_cu")]
 
 
 _p = ctypes.c_void_p
@@ -115,7 +116,7 @@ def _load():
         "mj_plan_compute": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo)]),
         "mj_plan_split_kv": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, _p, P(PlanInfo), _p]),
         "mj_plan_split_kv_device": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo), _p]),
-        "mj_plan_shape": (_i32, [P(Config), _i32, _i32, P(PlanInfo)]),
+        "mj_plan_shape": (_i32, [P(Config), _i32, _i32, _i32, P(PlanInfo)]),
         "mj_quantize_q": (_i32, [P(Config), _p, _i64, _i64, _p, _i32, _i32, _p, _p, _p]),
         "mj_paged_decode": (_i32, [P(Config), P(DecodeArgs), _p]),
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
@@ -125,9 +126,7 @@ def _load():
         "mj_combine_lse": (_i32, [P(Config), P(CombineArgs), _p]),
         "mj_debug_gather_kv": (_i32, [P(Config), P(DecodeArgs), _i32, _i32, _i32, _i32, _p, _p]),
         "mj_debug_decode_codes": (_i32, [_i32, _p, _i32, _p, _p]),
-        "mj_debug_set_decode_variant": (_i32, [_i32, _i32]),
         "mj_debug_stream_read": (_i32, [_p, _i64, _p, _i32, _p]),
-        "mj_debug_set_step_merge": (_i32, [_i32]),
     }
     for name, (res, args) in sigs.items():
         if not hasattr(lib, name):

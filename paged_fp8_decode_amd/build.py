@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmj.so")
 
-HIP_SOURCES = ["mj_qquant.hip", "mj_decode_generic.hip", "mj_decode_stream.hip", "mj_decode_mfma.hip", "mj_plan.hip", "mj_write.hip",
+HIP_SOURCES = ["mj_qquant.hip", "mj_decode_generic.hip", "mj_decode_mfma.hip", "mj_plan.hip", "mj_write.hip",
                "mj_draft.hip", "mj_combine.hip"]
 HOST_SOURCES = ["mj_host.cpp"]
 

@@ -1207,8 +1207,6 @@ hipError_t launch_fmt(DecodeParams& p, int nt, int tune, hipStream_t s) {
 
 }  // namespace
 
-bool decode_mfma_supports(int n_q) { return n_q >= 1; }
-
 // tune bits: 1 = two granules of prefetch, 2 = head-major grid, 4 = XCD-
 // grouped grid (over 2); -1 = the default for the format.  cache_policy: -1 = the default for the format,
 // else the CP bits.

@@ -71,6 +71,9 @@ mj_status check_config(const mj_config* c) {
   if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
   if (c->out_f32 != 0 && c->out_f32 != 1) return MJ_EINVAL;
+  if (c->decode_kernel < 0 || (c->decode_kernel > 1 && (c->decode_kernel < 10 || c->decode_kernel > 17)))
+    return MJ_EINVAL;
+  if (c->kv_cache_policy < 0 || c->kv_cache_policy > 4 || c->step_merge < 0 || c->step_merge > 2) return MJ_EINVAL;
   // the packed fp6 / fp4 formats take fp8 Q only
   if (c->q_mode == MJ_Q_BF16 && c->kv_format != MJ_KV_E4M3 && c->kv_format != MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if ((int64_t)c->max_q_len * (c->h_q / c->h_k) > kMaxRows) return MJ_ECAPACITY;
@@ -85,7 +88,40 @@ int slots_for(const mj_config* c, const Derived& d, int q_len) {
   return (int)std::max<int64_t>(1, ((int64_t)d.num_cus * plan_shape(c, d, q_len).wgs_per_cu) / denom);
 }
 
+// Largest grid of any plan for q_len (the plan buffer is laid out for it).
 int cap_for(const mj_config* c, const Derived& d, int q_len) { return std::max(slots_for(c, d, q_len), c->max_num_seqs); }
+
+// Tokens a block-table row of max_blocks pages addresses: no plan covers more.
+int64_t table_tokens(const mj_config* c, int max_blocks) { return (int64_t)max_blocks * c->page_size; }
+
+// Can a plan over such rows split at all: a sequence that fills its row must
+// be longer than the chunk floor.  Otherwise every sequence is one item
+// whatever the lengths (no merge), and the grid needs max_num_seqs items.
+bool splittable(const mj_config* c, const Derived& d, int q_len, int max_blocks) {
+  return (table_tokens(c, max_blocks) + d.kv_tile - 1) / d.kv_tile > min_chunk_tiles(c, d, q_len);
+}
+
+bool plan_splits(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
+  return c->max_splits > 1 && num_seqs < slots_for(c, d, q_len) && splittable(c, d, q_len, max_blocks);
+}
+
+// The grid of a plan: fixed by the config, q_len and the table width.
+int work_for(const mj_config* c, const Derived& d, int q_len, int max_blocks) {
+  return splittable(c, d, q_len, max_blocks) ? cap_for(c, d, q_len) : c->max_num_seqs;
+}
+
+void shape_info(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks, mj_plan_info* info) {
+  info->num_work = work_for(c, d, q_len, max_blocks);
+  info->slots = slots_for(c, d, q_len);
+  info->chunk_tiles = -1;
+  info->num_chunks = -1;
+  info->with_reduction = plan_splits(c, d, num_seqs, q_len, max_blocks) ? 1 : 0;
+  info->num_seqs = num_seqs;
+  info->q_len = q_len;
+  info->kv_tile_tokens = d.kv_tile;
+  info->min_chunk_tiles = min_chunk_tiles(c, d, q_len);
+  info->wgs_per_cu = plan_shape(c, d, q_len).wgs_per_cu;
+}
 
 mj_status derive(const mj_config* c, Derived* d) {
   mj_status st = check_config(c);
@@ -140,6 +176,32 @@ int ilog2(int x) {
   return s;
 }
 
+// Decode kernel choice: 0 = the generic kernel, 1 = the matrix-core kernel.
+// The matrix-core kernel addresses a page's rows with 32-bit lane offsets and
+// takes whole 16-token tiles inside one page; it serves any row count (tiles
+// of 32 rows).  decode_kernel 1 forces the generic kernel.
+int kernel_choice(const mj::DecodeParams& p) {
+  const bool small_strides = p.k_ss < (1 << 24) && p.v_ss < (1 << 24) && p.ksb_ss < (1 << 24) && p.vsb_ss < (1 << 24);
+  const bool tiles_ok = (p.kv_tile % 16) == 0 && small_strides;
+  return p.kernel_variant == 1 || !tiles_ok || p.n_q < 1 ? 0 : 1;
+}
+
+bool decode_fuses_step(const mj::DecodeParams& p) { return kernel_choice(p) == 1; }
+
+hipError_t launch_decode(const mj::DecodeParams& p, int kv_format, int row_tiles, hipStream_t s) {
+  const int k = kernel_choice(p);
+  // only the matrix-core kernel fuses the step; bf16 Q is read by it and the generic kernel
+  if (k != 1 && ((p.qb && !p.q_bf16) || p.counters)) return hipErrorInvalidValue;
+  // the fused merge counts one arrival per (item, KV head): one row tile
+  if (p.counters && p.n_q > mj::kMfmaTileRows) return hipErrorInvalidValue;
+  if (k == 0) return mj::launch_decode_generic(p, kv_format, row_tiles, s);
+  // kv_cache_policy -> the matrix-core kernel's policy bits (bit 0 K
+  // non-temporal, bit 1 V non-temporal; -1 the kernel's default)
+  static const int kPolicy[5] = {-1, 0, 3, 2, 1};
+  return mj::launch_decode_mfma(p, kv_format, kPolicy[p.cache_policy],
+                                p.kernel_variant >= 10 ? p.kernel_variant - 10 : -1, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,19 +248,23 @@ mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, in
   if (!seq_lens_host || !plan_host || !info || num_seqs < 1 || q_len < 1 || margin < 0 || max_blocks_per_seq < 1)
     return MJ_EINVAL;
   if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
+  const int64_t T = table_tokens(cfg, max_blocks_per_seq);
+  // tokens the plan covers: the length plus the margin, never past the table row
+  auto tiles = [&](int i) -> int64_t {
+    return (std::min<int64_t>((int64_t)seq_lens_host[i] + margin, T) + d.kv_tile - 1) / d.kv_tile;
+  };
   int64_t max_tiles = 0;
   for (int i = 0; i < num_seqs; ++i) {
     const int64_t L = seq_lens_host[i];
     if (L < 0) return MJ_EINVAL;
     if ((L + cfg->page_size - 1) / cfg->page_size > max_blocks_per_seq) return MJ_ECAPACITY;
-    max_tiles = std::max(max_tiles, (L + margin + d.kv_tile - 1) / d.kv_tile);
+    max_tiles = std::max(max_tiles, tiles(i));
   }
-  auto tiles = [&](int i) -> int64_t { return ((int64_t)seq_lens_host[i] + margin + d.kv_tile - 1) / d.kv_tile; };
   auto ceil_div = [](int64_t a, int64_t b) -> int64_t { return (a + b - 1) / b; };
 
   const int S = slots_for(cfg, d, q_len);
-  const int cap = cap_for(cfg, d, q_len);
-  const bool split = cfg->max_splits > 1 && num_seqs < S;
+  const int cap = work_for(cfg, d, q_len, max_blocks_per_seq);
+  const bool split = plan_splits(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   int64_t c = std::max<int64_t>(1, max_tiles);
   if (split) {
     // smallest chunk >= ceil(max_tiles / max_splits) whose item count fits S;
@@ -257,6 +323,7 @@ mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, in
   info->q_len = q_len;
   info->kv_tile_tokens = d.kv_tile;
   info->min_chunk_tiles = min_chunk_tiles(cfg, d, q_len);
+  info->wgs_per_cu = plan_shape(cfg, d, q_len).wgs_per_cu;
   return MJ_OK;
 }
 
@@ -275,22 +342,14 @@ static mj_status plan_device(const mj_config* cfg, const Derived& d, const int32
                              int32_t q_len, int32_t margin, int32_t max_blocks_per_seq, int32_t* plan_dev,
                              mj_plan_info* info, hipStream_t stream);
 
-mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, mj_plan_info* info) {
+mj_status mj_plan_shape(const mj_config* cfg, int32_t num_seqs, int32_t q_len, int32_t max_blocks_per_seq,
+                        mj_plan_info* info) {
   Derived d;
   mj_status st = derive(cfg, &d);
   if (st != MJ_OK) return st;
-  if (!info || num_seqs < 1 || q_len < 1) return MJ_EINVAL;
+  if (!info || num_seqs < 1 || q_len < 1 || max_blocks_per_seq < 1) return MJ_EINVAL;
   if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
-  const int S = slots_for(cfg, d, q_len);
-  info->num_work = cap_for(cfg, d, q_len);
-  info->slots = S;
-  info->chunk_tiles = -1;
-  info->num_chunks = -1;
-  info->with_reduction = cfg->max_splits > 1 && num_seqs < S ? 1 : 0;
-  info->num_seqs = num_seqs;
-  info->q_len = q_len;
-  info->kv_tile_tokens = d.kv_tile;
-  info->min_chunk_tiles = min_chunk_tiles(cfg, d, q_len);
+  shape_info(cfg, d, num_seqs, q_len, max_blocks_per_seq, info);
   return MJ_OK;
 }
 
@@ -312,7 +371,7 @@ static mj_status plan_device(const mj_config* cfg, const Derived& d, const int32
   if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
   if (!aligned(plan_dev, 16) || !aligned(seq_lens_dev, 4)) return MJ_EALIGN;
   const int S = slots_for(cfg, d, q_len);
-  const bool split = cfg->max_splits > 1 && num_seqs < S;
+  const bool split = plan_splits(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   mj::PlanParams p;
   p.seq_lens = seq_lens_dev;
   p.work = plan_dev;
@@ -330,16 +389,7 @@ static mj_status plan_device(const mj_config* cfg, const Derived& d, const int32
   p.cap_max = d.cap_max;
   p.min_chunk = min_chunk_tiles(cfg, d, q_len);
   if (mj::launch_plan(p, stream) != hipSuccess) return MJ_EHIP;
-  if (!info) return MJ_OK;
-  info->num_work = cap_for(cfg, d, q_len);
-  info->slots = S;
-  info->chunk_tiles = -1;  // decided on the device
-  info->num_chunks = -1;
-  info->with_reduction = split ? 1 : 0;
-  info->num_seqs = num_seqs;
-  info->q_len = q_len;
-  info->kv_tile_tokens = d.kv_tile;
-  info->min_chunk_tiles = p.min_chunk;
+  if (info) shape_info(cfg, d, num_seqs, q_len, max_blocks_per_seq, info);  // chunk decided on the device
   return MJ_OK;
 }
 
@@ -400,8 +450,8 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
         a->v_bs_head_stride % 8)
       return MJ_EALIGN;
   }
-  if (a->num_work != cap_for(cfg, d, a->q_len)) return MJ_EINVAL;
-  const bool split = cfg->max_splits > 1 && a->num_seqs < slots_for(cfg, d, a->q_len);
+  if (a->num_work != work_for(cfg, d, a->q_len, a->max_blocks_per_seq)) return MJ_EINVAL;
+  const bool split = plan_splits(cfg, d, a->num_seqs, a->q_len, a->max_blocks_per_seq);
   if ((a->with_reduction != 0) != split) return MJ_EINVAL;
   const WorkspaceLayout wl = workspace_layout(cfg, d);
   if (split && (!a->workspace || a->workspace_bytes < wl.total)) return MJ_ECAPACITY;
@@ -466,6 +516,8 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->plan_in_kernel = 0;
   p->plan_margin = p->plan_max_splits = p->plan_slots = p->plan_split = p->plan_min_chunk = 0;
   p->ns_out = p->sb_out = nullptr;
+  p->kernel_variant = cfg->decode_kernel;
+  p->cache_policy = cfg->kv_cache_policy;
   p->ksb = nv ? static_cast<const uint8_t*>(a->k_block_scale) : nullptr;
   p->vsb = nv ? static_cast<const uint8_t*>(a->v_block_scale) : nullptr;
   p->ksb_sp = nv ? a->k_bs_page_stride : 0;
@@ -485,17 +537,8 @@ mj_status mj_paged_decode(const mj_config* cfg, const mj_decode_args* a, hipStre
   mj::DecodeParams p;
   st = fill_decode(cfg, d, a, &p);
   if (st != MJ_OK) return st;
-  return mj::launch_decode(p, cfg->kv_format, row_tiles(cfg, a->q_len), stream) == hipSuccess ? MJ_OK : MJ_EHIP;
+  return launch_decode(p, cfg->kv_format, row_tiles(cfg, a->q_len), stream) == hipSuccess ? MJ_OK : MJ_EHIP;
 }
-
-// Where a fused step merges: 0 automatic, 1 in the decode kernel (the last
-// split item of a pair), 2 a separate merge launch.  Automatic is the
-// separate launch: the in-kernel merge makes every split workgroup wait for
-// its write-through stores and a returning atomic before it retires, which
-// costs more than the launch once a plan takes several rounds of workgroups
-// (measured: 32k context -10 us, ragged batch -12 us per step; a single
-// short sequence +1.4 us).
-static int g_step_merge = 0;
 
 mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream_t stream) {
   Derived d;
@@ -523,10 +566,18 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   st = fill_decode(cfg, d, &a, &p);
   if (st != MJ_OK) return st;
   const int rt = row_tiles(cfg, a.q_len);
+  // Where a fused step merges (cfg->step_merge): 0 automatic, 1 in the decode
+  // kernel (the last split item of a pair), 2 a separate merge launch.
+  // Automatic is the separate launch: the in-kernel merge makes every split
+  // workgroup wait for its write-through stores and a returning atomic
+  // before it retires, which costs more than the launch once a plan takes
+  // several rounds of workgroups (measured: 32k context -10 us, ragged batch
+  // -12 us per step; a single short sequence +1.4 us).
+  const bool want_merge_in_kernel = cfg->step_merge == 1;
   // plan in the decode kernel: matrix-core kernel, a batch the wave-level
   // planner covers, tile counts small enough for its float quotients
   const int64_t max_tiles = ((int64_t)a.max_blocks_per_seq * cfg->page_size + sa->margin + d.kv_tile - 1) / d.kv_tile;
-  const bool plan_in_kernel = sa->plan_on_device && mj::decode_fuses_step(p, cfg->kv_format, rt) &&
+  const bool plan_in_kernel = sa->plan_on_device && decode_fuses_step(p) &&
                               a.num_seqs <= mj::kPlanMaxSeqs && 2 * max_tiles < (1 << 22);
   if (sa->plan_on_device && !plan_in_kernel) {
     st = plan_device(cfg, d, a.seq_lens, a.num_seqs, a.q_len, sa->margin, a.max_blocks_per_seq,
@@ -554,33 +605,27 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
   m.out_head_stride = a.out_head_stride;
   m.lse = a.lse;
   if (qbf) {  // nothing to quantize: the decode reads bf16 Q itself
-    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel && p.n_q <= mj::kMfmaTileRows &&
-                                 mj::decode_fuses_step(p, cfg->kv_format, rt);
+    const bool merge_in_kernel = want_merge_in_kernel && !plan_in_kernel && p.n_q <= mj::kMfmaTileRows &&
+                                 decode_fuses_step(p);
     p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
-    if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+    if (launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
     return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
   }
-  if (mj::decode_fuses_step(p, cfg->kv_format, rt)) {
+  if (decode_fuses_step(p)) {
     p.qb = static_cast<const uint16_t*>(sa->q);
     p.qb_ts = sa->q_tok_stride;
     p.qb_hs = sa->q_head_stride;
     p.q_mul = sa->q_mul;
     // its merge reads this launch's plan, and covers a group of one row tile
-    const bool merge_in_kernel = g_step_merge == 1 && !plan_in_kernel && p.n_q <= mj::kMfmaTileRows;
+    const bool merge_in_kernel = want_merge_in_kernel && !plan_in_kernel && p.n_q <= mj::kMfmaTileRows;
     p.counters = a.with_reduction && merge_in_kernel ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
-    if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+    if (launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
     return a.with_reduction && !merge_in_kernel ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
   }
   st = mj_quantize_q(cfg, sa->q, sa->q_tok_stride, sa->q_head_stride, sa->q_mul, a.num_seqs, a.q_len, q8, qd, stream);
   if (st != MJ_OK) return st;
-  if (mj::launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
+  if (launch_decode(p, cfg->kv_format, rt, stream) != hipSuccess) return MJ_EHIP;
   return a.with_reduction ? mj_merge_lse(cfg, &m, stream) : MJ_OK;
-}
-
-mj_status mj_debug_set_step_merge(int32_t mode) {
-  if (mode < 0 || mode > 2) return MJ_EINVAL;
-  g_step_merge = mode;
-  return MJ_OK;
 }
 
 mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t stream) {
@@ -762,12 +807,6 @@ mj_status mj_debug_gather_kv(const mj_config* cfg, const mj_decode_args* a, int3
   p.page_shift = ilog2(cfg->page_size);
   p.out = dense_out;
   return mj::launch_gather(p, stream) == hipSuccess ? MJ_OK : MJ_EHIP;
-}
-
-mj_status mj_debug_set_decode_variant(int32_t variant, int32_t nontemporal) {
-  if (variant < 0 || (variant > 3 && (variant < 10 || variant > 17)) || nontemporal < 0 || nontemporal > 4) return MJ_EINVAL;
-  mj::set_decode_variant(variant, nontemporal);
-  return MJ_OK;
 }
 
 mj_status mj_debug_stream_read(const void* src, int64_t bytes, uint32_t* out, int32_t blocks, hipStream_t stream) {

@@ -67,7 +67,7 @@ struct DecodeParams {
   // order inside).  Set by the matrix-core launcher; 1 elsewhere.
   int row_tiles;
   // q_bf16 = 1: bf16-Q mode.  qb is then the bf16 Q the kernels use as is
-  // (q8 / q_descale unused), on every decode kernel but the VALU-PV one.
+  // (q8 / q_descale unused), on every decode kernel.
   // Otherwise (fused step, matrix-core kernel only; null elsewhere) qb is the
   // bf16 Q quantized in the prologue instead of reading q8 / q_descale.  counters:
   // (max_num_seqs, h_k) zero-initialised arrival counters; the last split of
@@ -86,6 +86,9 @@ struct DecodeParams {
   int plan_margin, plan_max_splits, plan_slots, plan_split, plan_min_chunk;
   int32_t* ns_out;
   int32_t* sb_out;
+  // kernel selection of the config (mj_config.decode_kernel and
+  // kv_cache_policy; 0 = the library's choice)
+  int kernel_variant, cache_policy;
   // nvfp4: the e4m3 block-scale pools (8-byte rows, paged like the codes);
   // null for the other formats
   const uint8_t* ksb;
@@ -151,9 +154,11 @@ struct PlanParams {
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
 constexpr int kPlanMaxSeqs = 256;  // batches the decode kernel plans itself (mj_plan_item.h)
 hipError_t launch_qquant(const QQuantParams& p, hipStream_t s);
-hipError_t launch_decode(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
-bool decode_fuses_step(const DecodeParams& p, int kv_format, int row_tiles);
 hipError_t launch_decode_generic(const DecodeParams& p, int kv_format, int row_tiles, hipStream_t s);
+// cache_policy: -1 the default for the format, else bits (0 K non-temporal,
+// 1 V non-temporal); tune: -1 the default, else bits (0 two granules of
+// prefetch, 1 head-major grid, 2 XCD-grouped grid)
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_format, int cache_policy, int tune, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t s);
@@ -182,7 +187,6 @@ struct CombineParams {
   int parts, rows, h_q;
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
-void set_decode_variant(int variant, int nontemporal);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int blocks, hipStream_t s);
 hipError_t launch_decode_codes(int kv_format, const uint8_t* codes, int n, float* out, hipStream_t s);
 

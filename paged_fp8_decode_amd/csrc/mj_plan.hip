@@ -5,9 +5,9 @@
 // that captured [plan, decode step] replays later steps with new lengths and
 // no host work at all (the host planner must run outside capture).
 //
-// Rule (identical to mj_plan_compute): tiles_i = ceil((L_i + margin) /
-// kv_tile) with L_i clamped to [0, max_blocks * page_size] as the decode
-// kernels clamp it; without a split each sequence is one item; with a split
+// Rule (identical to mj_plan_compute): tiles_i = ceil(min(L_i + margin,
+// lmax) / kv_tile) with L_i clamped to [0, lmax], lmax = max_blocks *
+// page_size, as the decode kernels clamp it; without a split each sequence is one item; with a split
 // the chunk c is the smallest integer >= max(1, ceil(max tiles / max_splits),
 // min_chunk) whose item count sum_i max(1, ceil(tiles_i / c)) fits the slots (a
 // bisection over the monotone count); items are sequence-major, padded with
@@ -70,9 +70,9 @@ __global__ __launch_bounds__(kPT) void plan_kernel(PlanParams p) {
   const int lane = tid & 63, wv = tid >> 6;
   const int64_t lmax = (int64_t)p.max_blocks * p.page_size;
   const bool cached = p.num_seqs <= kCache;
-  auto tiles_mem = [&](int i) -> int {
+  auto tiles_mem = [&](int i) -> int {  // the length plus the margin, never past the table row
     const int64_t L = min<int64_t>(max<int64_t>(p.seq_lens[i], 0), lmax);
-    return (int)((L + p.margin + p.kv_tile - 1) / p.kv_tile);
+    return (int)((min<int64_t>(L + p.margin, lmax) + p.kv_tile - 1) / p.kv_tile);
   };
   auto tiles = [&](int i) -> int { return cached ? tl[i] : tiles_mem(i); };
 

@@ -1,8 +1,8 @@
 // One wave's view of the split-KV plan: the item a decode workgroup serves,
 // derived from the device lengths by the same rule as the host and device
 // planners (mjolnir-kernel README "What it does", step 1; wheel listing
-// mjolnir/runner.py, T5DecodeRunner.plan): tiles_i = ceil((clamped L_i +
-// margin) / kv_tile); without a split, item w is sequence w; with a split the
+// mjolnir/runner.py, T5DecodeRunner.plan): tiles_i = ceil(min(clamped L_i +
+// margin, lmax) / kv_tile); without a split, item w is sequence w; with a split the
 // chunk c is the smallest integer >= max(1, ceil(max tiles / max_splits),
 // min_chunk) whose item count sum_i max(1, ceil(tiles_i / c)) fits the slots,
 // and items run sequence-major.  Wave-level only (shuffles, ballots, no LDS
@@ -64,9 +64,9 @@ __device__ __forceinline__ PlanItem plan_item_wave(const int32_t* seq_lens, int 
                                                    int kv_tile, int64_t lmax, int max_splits, int slots, bool split,
                                                    int min_chunk) {
   const int lane = threadIdx.x & 63;
-  auto tiles_of = [&](int i) -> int {
+  auto tiles_of = [&](int i) -> int {  // the length plus the margin, never past the table row
     const int64_t L = min<int64_t>(max<int64_t>(seq_lens[i], 0), lmax);
-    return (int)((L + margin + kv_tile - 1) / kv_tile);
+    return (int)((min<int64_t>(L + margin, lmax) + kv_tile - 1) / kv_tile);
   };
   PlanItem it;
   if (!split) {

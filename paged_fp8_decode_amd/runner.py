@@ -19,15 +19,15 @@ from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, StepArgs, check, mj
 class DecodeStep:
     def __init__(self, *, h_q, h_k, page_size, max_num_seqs, max_q_len=1, max_splits=16, kv_format="e4m3",
                  num_cus=0, wgs_per_cu=0, kv_tile_tokens=0, slots_override=0, min_chunk_tokens=0, q_mode="fp8",
-                 out_f32=False,
-                 device="cuda"):
+                 out_f32=False, decode_kernel=0, kv_cache_policy=0, step_merge=0, device="cuda"):
         self.device = torch.device(device)
         if num_cus == 0:
             num_cus = torch.cuda.get_device_properties(self.device).multi_processor_count
         self.cfg = mj_config(h_q=h_q, h_k=h_k, page_size=page_size, max_num_seqs=max_num_seqs, max_q_len=max_q_len,
                              max_splits=max_splits, num_cus=num_cus, wgs_per_cu=wgs_per_cu,
                              kv_tile_tokens=kv_tile_tokens, slots_override=slots_override, kv_format=kv_format,
-                             min_chunk_tokens=min_chunk_tokens, q_mode=q_mode, out_f32=out_f32)
+                             min_chunk_tokens=min_chunk_tokens, q_mode=q_mode, out_f32=out_f32,
+                             decode_kernel=decode_kernel, kv_cache_policy=kv_cache_policy, step_merge=step_merge)
         check(mj_config_check(self.cfg), "mj_config_check")
         self.h_q, self.h_k, self.h_r = h_q, h_k, h_q // h_k
         self.max_q_len = max_q_len
@@ -72,9 +72,9 @@ class DecodeStep:
         self.info = info
         return info
 
-    def plan_shape(self, num_seqs: int, q_len: int) -> PlanInfo:
+    def plan_shape(self, num_seqs: int, q_len: int, max_blocks_per_seq: int) -> PlanInfo:
         """The plan's size fields for a batch (no planning, no device work)."""
-        info = mj_plan_shape(self.cfg, num_seqs, q_len)
+        info = mj_plan_shape(self.cfg, num_seqs, q_len, max_blocks_per_seq)
         self.info = info
         return info
 
@@ -174,7 +174,7 @@ class DecodeStep:
         return self.plan_device(wl.seq_lens_dev, wl.spec.b, wl.spec.q_len, wl.block_table.shape[1], margin, stream)
 
     def plan_workload_shape(self, wl) -> PlanInfo:
-        return self.plan_shape(wl.spec.b, wl.spec.q_len)
+        return self.plan_shape(wl.spec.b, wl.spec.q_len, wl.block_table.shape[1])
 
     def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None, fused=False,
                      plan_on_device=False):

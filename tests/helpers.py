@@ -3,6 +3,7 @@ with the oracle under the stated tolerance."""
 
 from __future__ import annotations
 
+import contextlib
 import sys
 
 import numpy as np
@@ -70,3 +71,23 @@ def oracle_step(wl, seqs=None, heads=None, quantize=True):
         O[i * s.q_len:(i + 1) * s.q_len] = O_sub[r * s.q_len:(r + 1) * s.q_len]
         LSE[i * s.q_len:(i + 1) * s.q_len] = L_sub[r * s.q_len:(r + 1) * s.q_len]
     return O, LSE
+
+
+@contextlib.contextmanager
+def step_overrides(**kw):
+    """Config fields (kernel selection: decode_kernel, kv_cache_policy,
+    step_merge) that every DecodeStep built inside the block takes unless its
+    caller passes them: the A/B and every-kernel tests run one test body on
+    each kernel.  Test-side only; the library keeps no such state."""
+    from paged_fp8_decode_amd import runner
+
+    orig = runner.DecodeStep.__init__
+
+    def init(self, **a):
+        orig(self, **{**kw, **a})
+
+    runner.DecodeStep.__init__ = init
+    try:
+        yield
+    finally:
+        runner.DecodeStep.__init__ = orig

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(mj.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert mj.lib().mj_abi_version() == 8
+    assert mj.lib().mj_abi_version() == 9
 
 
 def _cfg(**kw):
@@ -36,16 +36,16 @@ def _cfg(**kw):
     return mj.mj_config(**base)
 
 
-def _oracle(cfg, lens, q_len, margin=0):
-    fmt = {v: k for k, v in mj.KV_FORMATS.items()}[cfg.kv_format]
-    wgs, mct = oplan.default_shape(fmt, q_len * (cfg.h_q // cfg.h_k))
+def _oracle(cfg, lens, q_len, margin, max_blocks, info):
+    """The oracle's plan rule with the parameters the library reports for
+    this plan (workgroups per CU, chunk floor): the rule is the pages', the
+    two parameters are the library's tuning, checked on their own below."""
     kv_tile = cfg.kv_tile_tokens or 128
-    mct = cfg.min_chunk_tokens or mct
     return oplan.plan_split_kv(lens, q_len=q_len, h_q=cfg.h_q, h_k=cfg.h_k, num_cus=cfg.num_cus,
-                               wgs_per_cu=cfg.wgs_per_cu or wgs, kv_tile=kv_tile,
+                               wgs_per_cu=info.wgs_per_cu, kv_tile=kv_tile,
                                max_splits=cfg.max_splits, max_num_seqs=cfg.max_num_seqs,
                                slots_override=cfg.slots_override, margin=margin,
-                               min_chunk_tiles=-(-mct // kv_tile))
+                               min_chunk_tiles=info.min_chunk_tiles, max_len=max_blocks * cfg.page_size)
 
 
 def _unpack(cfg, img, q_len):
@@ -56,9 +56,13 @@ def _unpack(cfg, img, q_len):
     return work, ns, sb
 
 
-def _compare(cfg, lens, q_len, margin=0):
-    img, info = mj.mj_plan_compute(cfg, lens, q_len, margin)
-    ref = _oracle(cfg, lens, q_len, margin)
+def _compare(cfg, lens, q_len, margin=0, max_blocks=1 << 24):
+    img, info = mj.mj_plan_compute(cfg, lens, q_len, margin, max_blocks)
+    if cfg.wgs_per_cu:
+        assert info.wgs_per_cu == cfg.wgs_per_cu
+    if cfg.min_chunk_tokens:
+        assert info.min_chunk_tiles == -(-cfg.min_chunk_tokens // (cfg.kv_tile_tokens or 128))
+    ref = _oracle(cfg, lens, q_len, margin, max_blocks, info)
     work, ns, sb = _unpack(cfg, img, q_len)
     cap = ref["num_work"]
     assert info.num_work == cap
@@ -70,6 +74,10 @@ def _compare(cfg, lens, q_len, margin=0):
     assert info.slots == ref["slots"]
     assert info.num_chunks == ref["num_chunks"]
     assert bool(info.with_reduction) == ref["with_reduction"]
+    # the plan's size fields, known before any length
+    shp = mj.mj_plan_shape(cfg, len(lens), q_len, max_blocks)
+    assert (shp.num_work, shp.slots, shp.with_reduction, shp.min_chunk_tiles, shp.wgs_per_cu) == \
+        (info.num_work, info.slots, info.with_reduction, info.min_chunk_tiles, info.wgs_per_cu)
     return info
 
 
@@ -78,13 +86,14 @@ def test_planner_matches_oracle_on_workloads(key):
     import synth
     s = synth.spec_for(key)
     lens = synth.workloads._lens(s, np.random.default_rng(s.seed))
+    mb = -(-max(lens) // s.page_size) + 3  # a block table a little wider than the longest sequence
     cfg = _cfg(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, max_q_len=s.q_len,
                slots_override=s.slots_override)
-    _compare(cfg, lens, s.q_len)
+    _compare(cfg, lens, s.q_len, max_blocks=mb)
     # the library's defaults (wgs_per_cu = min_chunk_tokens = 0)
     cfg = _cfg(h_q=s.h_q, h_k=s.h_k, page_size=s.page_size, max_num_seqs=s.b, max_q_len=s.q_len,
                slots_override=s.slots_override, wgs_per_cu=0, kv_format=s.kv_format)
-    _compare(cfg, lens, s.q_len)
+    _compare(cfg, lens, s.q_len, max_blocks=mb)
 
 
 def test_planner_matches_oracle_random():
@@ -101,7 +110,11 @@ def test_planner_matches_oracle_random():
                    kv_format=str(rng.choice(["e4m3", "e2m3", "e3m2", "e2m1", "nvfp4"])))
         b = int(rng.integers(1, cfg.max_num_seqs + 1))
         lens = rng.integers(0, int(rng.choice([100, 5000, 200000])), size=b).tolist()
-        _compare(cfg, lens, int(rng.integers(1, mq + 1)), int(rng.integers(0, 8)))
+        # block tables from exactly the longest sequence's pages (the margin
+        # then reaches past the row) to far wider than any sequence
+        need = max(1, -(-max(lens) // cfg.page_size))
+        mb = need + int(rng.choice([0, 0, 1, 7, 1000, 1 << 20]))
+        _compare(cfg, lens, int(rng.integers(1, mq + 1)), int(rng.integers(0, 300)), mb)
 
 
 def test_config_errors():
@@ -147,12 +160,14 @@ FAKE = 1 << 20  # a 16-byte (and 256-byte) aligned, never dereferenced address
 
 
 def _args(cfg, **kw):
-    cap = mj.mj_plan_capacity(cfg, 1)
+    # rows of 256 pages (4096 tokens): long enough for a split plan (an
+    # invalid config has no plan: any grid, the config check comes first)
+    shp = mj.mj_plan_shape(cfg, 4, 1, 256) if mj.mj_config_check(cfg) == mj.MJ_OK else mj.PlanInfo(num_work=1)
     a = dict(q8=FAKE, q_descale=FAKE, num_seqs=4, q_len=1, causal=1, k_cache=FAKE, k_page_stride=16 * 8 * 128,
              k_slot_stride=128, k_head_stride=16 * 128, v_cache=FAKE, v_page_stride=16 * 8 * 128, v_slot_stride=128,
              v_head_stride=16 * 128, num_pages=100, k_descale=FAKE, k_descale_kind=0, v_descale=FAKE,
-             v_descale_kind=0, block_table=FAKE, bt_row_stride=8, max_blocks_per_seq=8, seq_lens=FAKE, plan=FAKE,
-             num_work=cap, with_reduction=1, workspace=FAKE, workspace_bytes=mj.mj_workspace_bytes(cfg),
+             v_descale_kind=0, block_table=FAKE, bt_row_stride=256, max_blocks_per_seq=256, seq_lens=FAKE, plan=FAKE,
+             num_work=shp.num_work, with_reduction=1, workspace=FAKE, workspace_bytes=mj.mj_workspace_bytes(cfg),
              softmax_scale=0.088, o_mul=None, out=FAKE, out_tok_stride=32 * 128, out_head_stride=128, lse=None)
     a.update(kw)
     return mj.DecodeArgs(**a)
@@ -313,13 +328,15 @@ def test_write_zero_tokens_needs_no_buffers():
     assert mj.lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(mj.WriteArgs(num_tokens=0)), None) == mj.MJ_OK
 
 
-def test_debug_knob_errors():
-    assert mj.lib().mj_debug_set_step_merge(3) == mj.MJ_EINVAL
-    assert mj.lib().mj_debug_set_step_merge(-1) == mj.MJ_EINVAL
-    assert mj.lib().mj_debug_set_decode_variant(18, 1) == mj.MJ_EINVAL
-    assert mj.lib().mj_debug_set_decode_variant(17, 1) == mj.MJ_OK
-    assert mj.lib().mj_debug_set_decode_variant(0, 1) == mj.MJ_OK
-    assert mj.lib().mj_debug_set_decode_variant(0, 5) == mj.MJ_EINVAL
+def test_kernel_selection_config_values():
+    for kw, status in ((dict(decode_kernel=0), mj.MJ_OK), (dict(decode_kernel=1), mj.MJ_OK),
+                       (dict(decode_kernel=2), mj.MJ_EINVAL), (dict(decode_kernel=9), mj.MJ_EINVAL),
+                       (dict(decode_kernel=10), mj.MJ_OK), (dict(decode_kernel=17), mj.MJ_OK),
+                       (dict(decode_kernel=18), mj.MJ_EINVAL), (dict(decode_kernel=-1), mj.MJ_EINVAL),
+                       (dict(kv_cache_policy=4), mj.MJ_OK), (dict(kv_cache_policy=5), mj.MJ_EINVAL),
+                       (dict(kv_cache_policy=-1), mj.MJ_EINVAL), (dict(step_merge=2), mj.MJ_OK),
+                       (dict(step_merge=3), mj.MJ_EINVAL), (dict(step_merge=-1), mj.MJ_EINVAL)):
+        assert mj.mj_config_check(_cfg(**kw)) == status, kw
 
 
 @no_gpu
@@ -382,3 +399,46 @@ def test_out_f32_config_values():
     c = _cfg()
     c.out_f32 = 2
     assert mj.mj_config_check(c) == mj.MJ_EINVAL
+
+
+# The library's plan parameters when the config leaves wgs_per_cu and
+# min_chunk_tokens at 0 (the defaults documented under mj_config in
+# include/mj.h).  A tuning choice of the library, not part of the pages'
+# method: checked here as a regression of that table, never through the oracle.
+@pytest.mark.parametrize("fmt,n_q,wgs,floor_tiles", [
+    ("e4m3", 1, 8, 16), ("e4m3", 4, 8, 16), ("e4m3", 16, 8, 16), ("e4m3", 32, 1, 1), ("e4m3", 64, 1, 1),
+    ("e2m3", 4, 1, 1), ("e3m2", 16, 1, 1), ("e2m1", 4, 2, 1), ("e2m1", 32, 2, 1), ("e2m1", 40, 1, 1),
+    ("nvfp4", 8, 2, 1), ("nvfp4", 64, 1, 1),
+])
+def test_library_default_plan_parameters(fmt, n_q, wgs, floor_tiles):
+    h_k = 8
+    q_len = 4 if n_q % 4 == 0 and n_q >= 16 else 1
+    cfg = _cfg(h_q=h_k * n_q // q_len, h_k=h_k, max_q_len=q_len, wgs_per_cu=0, kv_format=fmt)
+    info = mj.mj_plan_shape(cfg, 1, q_len, 4096)
+    assert (info.wgs_per_cu, info.min_chunk_tiles) == (wgs, floor_tiles)
+
+
+# The default plans of the workloads, worked by hand from the table above
+# (256 CUs, 128-token tiles, max 16 splits, block-table rows exactly as long
+# as the sequences):
+#   cfg1: e4m3 4 rows: S = 256*8/2 = 1024; the 32-page row is 4 tiles <= the
+#         16-tile floor: never split, one item, no merge, grid max_num_seqs = 1.
+#   cfg2: S = 256*8/8 = 256; 32 tiles > 16; c = max(ceil(32/16), 16) = 16 ->
+#         2 items x 32 = 64 <= 256; grid 256.
+#   cfg4: 32 rows: S = 256/8 = 32; 64 tiles; 16*ceil(64/c) <= 32 -> c = 32,
+#         2 x 16 = 32 items; grid 32.
+#   cfg5: e2m3: S = 32; 1024 tiles; 4*ceil(1024/c) <= 32 -> c = 128, 8 x 4.
+#   32k:  S = 256; 256 tiles; 64*ceil(256/c) <= 256 -> c = 64, 4 x 64 = 256.
+@pytest.mark.parametrize("b,h_q,h_k,q_len,L,P_,fmt,expect", [
+    (1, 8, 2, 1, 512, 16, "e4m3", (1024, 4, 1, 1, 0, 1)),
+    (32, 32, 8, 1, 4096, 16, "e4m3", (256, 16, 2, 64, 1, 256)),
+    (16, 64, 8, 4, 8192, 32, "e4m3", (32, 32, 2, 32, 1, 32)),
+    (4, 32, 8, 1, 131072, 128, "e2m3", (32, 128, 8, 32, 1, 32)),
+    (64, 32, 8, 1, 32768, 64, "e4m3", (256, 64, 4, 256, 1, 256)),
+])
+def test_library_default_workload_plans(b, h_q, h_k, q_len, L, P_, fmt, expect):
+    cfg = _cfg(h_q=h_q, h_k=h_k, page_size=P_, max_num_seqs=b, max_q_len=q_len, wgs_per_cu=0, kv_format=fmt)
+    img, info = mj.mj_plan_compute(cfg, [L] * b, q_len, 0, L // P_)
+    work, ns, _ = _unpack(cfg, img, q_len)
+    items = int(np.sum(work[:, 0] >= 0))
+    assert (info.slots, info.chunk_tiles, int(ns[0]), items, info.with_reduction, info.num_work) == expect

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from helpers import compare_lse, compare_out, oracle_step, say
+from helpers import compare_lse, compare_out, oracle_step, say, step_overrides
 
 pytestmark = pytest.mark.gpu
 
@@ -33,9 +33,8 @@ def mj(gpu):
 @pytest.fixture
 def variant(mj, request):
     v = getattr(request, "param", 0)
-    mj.mj_debug_set_decode_variant(v, 1)
-    yield v
-    mj.mj_debug_set_decode_variant(0, 1)
+    with step_overrides(decode_kernel=v):
+        yield v
 
 
 def _run(wl, fused=False, plan_on_device=False, **overrides):

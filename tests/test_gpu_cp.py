@@ -119,21 +119,18 @@ def test_fp32_output_matches_bf16_output(mj, gpu):
     from paged_fp8_decode_amd.runner import DecodeStep, new_output
     wl = synth.build(synth.spec_for("cfg4c", small=True), gpu)
     for variant in (0, 1):
-        mj.mj_debug_set_decode_variant(variant, 1)
-        try:
-            for ms in (1, 16):
-                res = []
-                for f32 in (False, True):
-                    step = DecodeStep.for_workload(wl, out_f32=f32, max_splits=ms, min_chunk_tokens=1)
-                    info = step.plan_workload(wl)
-                    out, lse = new_output(wl, out_f32=f32)
-                    step.run_workload(wl, out, lse, info=info, fused=True)
-                    torch.cuda.synchronize()
-                    res.append((out, lse))
-                assert torch.equal(res[1][0].to(torch.bfloat16).view(torch.int16), res[0][0].view(torch.int16))
-                assert torch.equal(res[1][1], res[0][1])
-        finally:
-            mj.mj_debug_set_decode_variant(0, 1)
+        for ms in (1, 16):
+            res = []
+            for f32 in (False, True):
+                step = DecodeStep.for_workload(wl, out_f32=f32, max_splits=ms, min_chunk_tokens=1,
+                                               decode_kernel=variant)
+                info = step.plan_workload(wl)
+                out, lse = new_output(wl, out_f32=f32)
+                step.run_workload(wl, out, lse, info=info, fused=True)
+                torch.cuda.synchronize()
+                res.append((out, lse))
+            assert torch.equal(res[1][0].to(torch.bfloat16).view(torch.int16), res[0][0].view(torch.int16))
+            assert torch.equal(res[1][1], res[0][1])
 
 
 def test_context_parallel_full_size_sampled(mj, gpu):

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import synth
-from helpers import compare_lse, compare_out, oracle_step, say
+from helpers import compare_lse, compare_out, oracle_step, say, step_overrides
 
 pytestmark = pytest.mark.gpu
 
@@ -194,16 +194,15 @@ def test_gather_probe_bit_exact(mj, gpu, key):
 
 SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4",
               "32k", "32k_b16"]
-# 0 = automatic choice, 1 = generic LDS kernel, 2 = VALU-PV streaming kernel
-VARIANTS = [0, 1, 2]
+# mj_config.decode_kernel: 0 = automatic choice, 1 = generic LDS kernel
+VARIANTS = [0, 1]
 
 
 @pytest.fixture
 def variant(mj, request):
     v = getattr(request, "param", 0)
-    mj.mj_debug_set_decode_variant(v, 1)
-    yield v
-    mj.mj_debug_set_decode_variant(0, 1)
+    with step_overrides(decode_kernel=v):
+        yield v
 
 
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
@@ -434,9 +433,8 @@ def test_graph_replay_with_device_plan(mj, gpu):
 @pytest.fixture
 def step_merge(mj, request):
     m = getattr(request, "param", 0)
-    mj.mj_debug_set_step_merge(m)
-    yield m
-    mj.mj_debug_set_step_merge(0)
+    with step_overrides(step_merge=m):
+        yield m
 
 
 @pytest.mark.parametrize("step_merge", [1, 2], indirect=True)
@@ -597,12 +595,8 @@ def test_grid_orders_bit_identical(mj, gpu, key):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
     ref = None
     for v in (10, 11, 12, 14, 15):
-        mj.mj_debug_set_decode_variant(v, 1)
-        try:
-            say(f"grid order {wl.spec.name} variant={v}")
-            out, lse, info = _run(mj, wl, fused=True, **FINE)
-        finally:
-            mj.mj_debug_set_decode_variant(0, 1)
+        say(f"grid order {wl.spec.name} variant={v}")
+        out, lse, info = _run(mj, wl, fused=True, decode_kernel=v, **FINE)
         if ref is None:
             ref = (out, lse)
             O, LSE = oracle_step(wl)

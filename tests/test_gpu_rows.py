@@ -86,13 +86,9 @@ def test_many_rows_in_kernel_merge_request_and_plan(mj, gpu, key):
     the in-kernel plan gives the host plan's bits."""
     wl = _wl(key, (5, 64, 8, True), gpu)
     ref = _run(mj, wl, fused=False, min_chunk_tokens=1)
-    mj.mj_debug_set_step_merge(1)
-    try:
-        for rep in range(3):
-            say(f"rows {wl.spec.name} step_merge=1 rep={rep}")
-            _same(_run(mj, wl, fused=True, min_chunk_tokens=1), ref[:2], f"merge request rep={rep}")
-    finally:
-        mj.mj_debug_set_step_merge(0)
+    for rep in range(3):
+        say(f"rows {wl.spec.name} step_merge=1 rep={rep}")
+        _same(_run(mj, wl, fused=True, min_chunk_tokens=1, step_merge=1), ref[:2], f"merge request rep={rep}")
     for mct in (0, 1):
         host = _run(mj, wl, fused=True, min_chunk_tokens=mct)
         say(f"rows {wl.spec.name} plan in kernel mct={mct}")
@@ -104,12 +100,8 @@ def test_many_rows_grid_orders_bit_identical(mj, gpu, key):
     wl = _wl(key, (11, 48, 8, True), gpu)
     ref = None
     for v in (10, 11, 12, 14, 15):
-        mj.mj_debug_set_decode_variant(v, 1)
-        try:
-            say(f"rows grid order {wl.spec.name} variant={v}")
-            got = _run(mj, wl, fused=True, min_chunk_tokens=1)
-        finally:
-            mj.mj_debug_set_decode_variant(0, 1)
+        say(f"rows grid order {wl.spec.name} variant={v}")
+        got = _run(mj, wl, fused=True, min_chunk_tokens=1, decode_kernel=v)
         if ref is None:
             ref = got
             O, LSE = oracle_step(wl)

@@ -108,10 +108,8 @@ def test_write_bytes_match_oracle(mj, gpu, kv_format, kind, layout, P):
     cfg = mj.mj_config(h_q=h_k, h_k=h_k, page_size=P, max_num_seqs=1, kv_format=kv_format, num_cus=256)
     _write(mj, gpu, cfg, key.to(gpu), value.to(gpu), torch.from_numpy(slots).to(gpu), k_pool, v_pool, ks, vs,
            torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, num_pages, bs)
-    oslots = slots.copy()
-    oslots[oslots >= num_pages * P] = -1  # the oracle's pool has every page; the kernel skips past num_pages
     ref = write_kv((init_k, init_v), (ks, vs), P, kv_format, key.float().numpy(), value.float().numpy(),
-                   oslots, k_sc, v_sc, kind, **(bs_np or {}))
+                   slots, k_sc, v_sc, kind, num_pages=num_pages, **(bs_np or {}))
     assert np.array_equal(k_pool.cpu().numpy(), ref[0])
     assert np.array_equal(v_pool.cpu().numpy(), ref[1])
     if bs is not None:

@@ -247,3 +247,106 @@ def test_context_parallel_combine_is_full_attention(G):
     e = np.zeros((2, 128))
     Oc, LSEc = A.combine([(e, np.array([-np.inf, 0.0])), (e + 1.0, np.array([-np.inf, -np.inf]))])
     assert np.all(Oc[0] == 0) and LSEc[0] == -np.inf and np.all(Oc[1] == 0) and LSEc[1] == 0.0
+
+
+def _descale_case(kind, seed=23):
+    """Three sequences of two KV heads (b != h_k, so a transposed index
+    reads another pair), two query heads each, q_len 2, HND pages of 16
+    through a permuted block table.  Each (sequence, KV head) pair's true K
+    and V are e4m3 values times that pair's own scale: per tensor one scale (0.625),
+    per head 0.75*(g+1), per (sequence, head) 2^i * 3^g / 8, all distinct and
+    exact in fp32 (V: times 1.25).
+    The descale array is filled from those scales in the layout of its kind;
+    the reference below never reads it."""
+    rng = np.random.default_rng(seed)
+    b, h_k, h_r, q_len, d, P = 3, 2, 2, 2, 128, 16
+    lens = [37, 20, 50]
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+
+    def scale(i, g, side):
+        base = {"tensor": 0.625, "head": 0.75 * (g + 1), "seq_head": 2.0 ** i * 3.0 ** g / 8}[kind]
+        return base * (1.0 if side == 0 else 1.25)
+
+    pages = [-(-L // P) for L in lens]
+    perm = rng.permutation(sum(pages) + 3)
+    bt = np.zeros((b, max(pages)), dtype=np.int32)
+    k = 0
+    for i, n in enumerate(pages):
+        bt[i, :n] = perm[k:k + n]
+        k += n
+    n_pages = len(perm)
+    pools = [np.zeros((n_pages, h_k, P, d), dtype=np.uint8) for _ in range(2)]
+    true = {}  # (i, g, side) -> fp64 values
+    for i, L in enumerate(lens):
+        for g in range(h_k):
+            for side in range(2):
+                codes = rng.choice(finite, size=(L, d))
+                vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                true[i, g, side] = vals * scale(i, g, side)
+                for j in range(L):
+                    pools[side][bt[i, j // P], g, j % P] = codes[j]
+    if kind == "tensor":
+        kd, vd = np.array([scale(0, 0, 0)]), np.array([scale(0, 0, 1)])
+    elif kind == "head":
+        kd = np.array([scale(0, g, 0) for g in range(h_k)])
+        vd = np.array([scale(0, g, 1) for g in range(h_k)])
+    else:
+        kd = np.array([[scale(i, g, 0) for g in range(h_k)] for i in range(b)])
+        vd = np.array([[scale(i, g, 1) for g in range(h_k)] for i in range(b)])
+    q = torch.randn(b * q_len, h_k * h_r, d, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    st = (h_k * P * d, d, P * d)
+    h = dict(q=q.float().numpy(), k_pool=pools[0].reshape(-1), v_pool=pools[1].reshape(-1), k_strides=st,
+             v_strides=st, block_table=bt, seq_lens=np.array(lens), k_descale=kd.astype(np.float32),
+             v_descale=vd.astype(np.float32), descale_kind=kind, softmax_scale=1 / math.sqrt(d), q_mul=None,
+             o_mul=None)
+    args = dict(q_len=q_len, h_q=h_k * h_r, h_k=h_k, d=d, page_size=P, kv_format="e4m3")
+    return h, args, true, q
+
+
+def _descale_reference(h, args, true, q):
+    """torch SDPA in fp64 on the pairs' true K and V, Q as given, the causal
+    block's mask built here."""
+    q_len, h_q, h_k, d = args["q_len"], args["h_q"], args["h_k"], args["d"]
+    h_r = h_q // h_k
+    b = len(h["seq_lens"])
+    O = np.zeros((b * q_len, h_q, d))
+    qq = q.float().numpy().astype(np.float64)
+    for i, L in enumerate(h["seq_lens"]):
+        for g in range(h_k):
+            for t in range(q_len):
+                allowed = np.zeros((h_r, L), bool)
+                allowed[:, :L - q_len + t + 1] = True
+                rows = qq[i * q_len + t, g * h_r:(g + 1) * h_r]
+                O[i * q_len + t, g * h_r:(g + 1) * h_r] = _ref_sdpa(rows, true[i, g, 0], true[i, g, 1], allowed,
+                                                                    h["softmax_scale"])
+    return O
+
+
+@pytest.mark.parametrize("kind", ["tensor", "head", "seq_head"])
+def test_descale_kinds_against_true_values(kind):
+    h, args, true, q = _descale_case(kind)
+    O, _ = A.decode_step(h, causal=True, quantize=False, **args)
+    assert np.max(np.abs(O - _descale_reference(h, args, true, q))) < 1e-12
+
+
+@pytest.mark.parametrize("wrong", ["transposed", "head_by_seq", "seq_head_by_head"])
+def test_descale_pin_catches_wrong_indexing(wrong, monkeypatch):
+    """Mistakes planted in the oracle (on the CPU): each one changes the
+    result, so the pin above would fail on it."""
+    real = A.descale
+
+    def planted(values, kind, i, g):
+        v = np.asarray(values, dtype=np.float64)
+        if wrong == "transposed" and kind == "seq_head":
+            return float(v.reshape(-1)[g * v.shape[0] + i])  # the (b, h_k) array read as (h_k, b)
+        if wrong == "head_by_seq" and kind == "head":
+            return float(v.reshape(-1)[i % v.size])
+        if wrong == "seq_head_by_head" and kind == "seq_head":
+            return float(v.reshape(-1)[g])
+        return real(values, kind, i, g)
+
+    kind = "head" if wrong == "head_by_seq" else "seq_head"
+    h, args, true, q = _descale_case(kind)
+    monkeypatch.setattr(A, "descale", planted)
+    O, _ = A.decode_step(h, causal=True, quantize=False, **args)
+    assert np.max(np.abs(O - _descale_reference(h, args, true, q))) > 1e-3

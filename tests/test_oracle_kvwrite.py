@@ -116,6 +116,27 @@ def test_padding_slots_write_nothing():
     assert np.all(k == 7) and np.all(v == 9)
 
 
+def test_slots_past_num_pages_write_nothing():
+    """A 4-page pool of which the cache owns 3 pages: slot 50 (page 3, row 2)
+    addresses no row of the cache and leaves every byte alone; slot 33 (page
+    2, row 1) is written, by hand at byte 2*(2*16*128) + g*(16*128) + 128."""
+    size, strides, _ = _pools("e4m3", "HND", 4, 16, 2)
+    x = np.full((2, 2, 128), 1.5, dtype=np.float32)  # e4m3 1.5 = 0x3C at scale 1
+    one = np.ones(1, np.float32)
+    k, v = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), strides, 16, "e4m3", x, x,
+                      np.array([50, 33]), one, one, "tensor", num_pages=3)
+    written = np.zeros(size, bool)
+    for g in range(2):
+        b = 2 * 2 * 16 * 128 + g * 16 * 128 + 128
+        written[b:b + 128] = True
+    assert np.all(k[written] == 0x3C) and np.all(k[~written] == 0)
+    assert np.array_equal(k, v)
+    # without the pool size, page 3 exists and slot 50 is written too
+    k2, _ = W.write_kv((np.zeros(size, np.uint8), np.zeros(size, np.uint8)), strides, 16, "e4m3", x, x,
+                       np.array([50, 33]), one, one, "tensor")
+    assert np.count_nonzero(k2) == 2 * np.count_nonzero(k)
+
+
 @pytest.mark.parametrize("kv_format,kind", [("e4m3", "tensor"), ("e4m3", "head"), ("e2m3", "channel"),
                                             ("e3m2", "channel"), ("e2m1", "channel"), ("e2m1", "head")])
 @pytest.mark.parametrize("layout", ["HND", "NHD"])

@@ -45,19 +45,60 @@ def test_mi355_workload_plans(args, expect):
     assert int(p["with_reduction"]) == expect[4], name
 
 
-@pytest.mark.parametrize("args,expect", _golden("mi355d"))
-def test_mi355_default_plans(args, expect):
-    name = args[0]
-    b, h_q, h_k, q_len, L = (int(x) for x in args[1:6])
-    fmt = args[6]
-    wgs, mct = P.default_shape(fmt, q_len * (h_q // h_k))
-    p = P.plan_split_kv([L] * b, q_len=q_len, h_q=h_q, h_k=h_k, num_cus=256, wgs_per_cu=wgs, kv_tile=128,
-                        max_splits=16, max_num_seqs=b, min_chunk_tiles=-(-mct // 128))
-    assert p["slots"] == expect[0], name
-    assert p["chunk_tiles"] == expect[1], name
-    assert p["n_splits"] == [expect[2]] * b, name
-    assert sum(1 for w in p["work"] if w[0] >= 0) == expect[3], name
-    assert int(p["with_reduction"]) == expect[4], name
+def _golden_table():
+    out = []
+    with open(os.path.join(GOLDEN, "plan_examples.txt")) as f:
+        for line in f:
+            if line.startswith("table "):
+                a, b = line.split("->")
+                tiles, rest = b.split("|")
+                out.append(([int(x) for x in a.split()[2:]], [int(x) for x in tiles.split()],
+                            [int(x) for x in rest.split()]))
+    return out
+
+
+@pytest.mark.parametrize("args,tiles,expect", _golden_table())
+def test_block_table_width_examples(args, tiles, expect):
+    P_, mb, mct, S, mns, margin, *lens = args
+    p = P.plan_split_kv(lens, q_len=1, h_q=8, h_k=1, num_cus=1, wgs_per_cu=1, kv_tile=128, max_splits=16,
+                        max_num_seqs=mns, slots_override=S, margin=margin, min_chunk_tiles=mct,
+                        max_len=mb * P_)
+    real = [w for w in p["work"] if w[0] >= 0]
+    assert [max(w[2] for w in real if w[0] == i) for i in range(len(lens))] == tiles
+    assert [len(real), int(p["with_reduction"]), p["num_work"]] == expect
+
+
+def test_table_width_clamps_and_unsplittable_loses_nothing():
+    """Brute force: with a table width, the plan covers exactly the clamped
+    tiles; where the rule declines to split (rows too short for the floor),
+    the split rule would have given every sequence one item anyway."""
+    rng = np.random.default_rng(17)
+    for _ in range(500):
+        b = int(rng.integers(1, 6))
+        P_ = int(rng.choice([16, 64]))
+        mb = int(rng.integers(1, 40))
+        T = mb * P_
+        lens = [int(x) for x in rng.integers(0, T + 1, size=b)]
+        margin = int(rng.integers(0, 300))
+        kv = int(rng.choice([16, 64, 128]))
+        mct = int(rng.integers(1, 12))
+        S = int(rng.integers(b + 1, 30))
+        p = P.plan_split_kv(lens, q_len=1, h_q=8, h_k=1, num_cus=1, wgs_per_cu=1, kv_tile=kv, max_splits=8,
+                            max_num_seqs=b, slots_override=S, margin=margin, min_chunk_tiles=mct, max_len=T)
+        tiles = [math.ceil(min(L + margin, T) / kv) for L in lens]
+        real = [w for w in p["work"] if w[0] >= 0]
+        for i in range(b):
+            assert sorted(t for w in real if w[0] == i for t in range(w[1], w[2])) == list(range(tiles[i]))
+        splittable = math.ceil(T / kv) > mct
+        assert p["with_reduction"] == splittable
+        assert p["num_work"] == (max(S, b) if splittable else b)
+        if not splittable:
+            # the smallest feasible chunk at or above the floor covers every sequence whole
+            c = min(c for c in range(mct, mct + max(tiles) + 2)
+                    if sum(max(1, math.ceil(t / c)) for t in tiles) <= S and
+                    max(math.ceil(t / c) for t in tiles) <= 8)
+            assert all(math.ceil(t / c) <= 1 for t in tiles)
+            assert p["n_splits"] == [1] * b
 
 
 def _check_invariants(p, lens, kv_tile, max_splits, S, cap, margin=0):
