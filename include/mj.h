@@ -252,8 +252,9 @@ mj_status mj_config_check(const mj_config* cfg);
 /* Byte sizes of the caller-allocated buffers; 0 for an invalid config.
  * Plan buffer: int32 [work: cap_max x 4][n_splits: max_num_seqs]
  * [split_begin: max_num_seqs], cap_max = the largest capacity over q_len.
- * Workspace: fp32 split partials sized by the largest slot count, not by the
- * batch (the plan splits only batches smaller than one wave), then
+ * Workspace: fp32 split partials for the largest slots(q_len) * q_len * h_r
+ * rows per KV head over q_len, not sized by the batch (the plan splits only
+ * batches smaller than one wave), then
  * mj_decode_step's arrival counters (int32, max_num_seqs x h_k) and its Q
  * staging (e4m3 codes and scales, used when the step is not fused).  The
  * counters must be zero before the first mj_decode_step on a workspace (zero

@@ -19,6 +19,7 @@ constexpr int kMaxRows = 1024;    // sanity bound on q_len * h_r
 struct Derived {
   int num_cus, kv_tile, h_r, nq_max;
   int cap_max, slots_max;
+  int64_t part_rows_max;  // max over q_len of slots(q_len) * q_len * h_r
 };
 
 // Planned workgroups per CU and chunk floor (tokens) for a q_len: the config's
@@ -138,24 +139,28 @@ mj_status derive(const mj_config* c, Derived* d) {
   d->nq_max = c->max_q_len * d->h_r;
   d->cap_max = 0;
   d->slots_max = 0;
+  d->part_rows_max = 0;
   for (int ql = 1; ql <= c->max_q_len; ++ql) {
     d->cap_max = std::max(d->cap_max, cap_for(c, *d, ql));
     d->slots_max = std::max(d->slots_max, slots_for(c, *d, ql));
+    d->part_rows_max = std::max<int64_t>(d->part_rows_max, (int64_t)slots_for(c, *d, ql) * ql * d->h_r);
   }
   return MJ_OK;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: split partials (o | m | l) for the largest slot count, then the
-// step's arrival counters and its Q staging (codes, scales) for the unfused
-// fallback.
+// Workspace: split partials (o | m | l), then the step's arrival counters
+// and its Q staging (codes, scales) for the unfused fallback.  A plan for
+// q_len has at most slots(q_len) split items of q_len * h_r rows per KV head,
+// laid out [item][KV head][row] with the row stride of that q_len, so the
+// partials take the largest slots(q_len) * q_len * h_r over q_len.
 struct WorkspaceLayout {
   size_t o_off, m_off, l_off, cnt_off, q8_off, qd_off, total;
 };
 
 WorkspaceLayout workspace_layout(const mj_config* c, const Derived& d) {
-  const size_t rows = (size_t)d.slots_max * c->h_k * d.nq_max;
+  const size_t rows = (size_t)d.part_rows_max * c->h_k;
   const size_t pairs = (size_t)c->max_num_seqs * c->h_k;
   WorkspaceLayout w;
   w.o_off = 0;
@@ -484,8 +489,8 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->o_part = has_ws ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
   p->m_part = has_ws ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
   p->l_part = has_ws ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
-  p->nqp = d.nq_max;
-  p->part_items = has_ws ? d.slots_max : 0;
+  p->nqp = a->q_len * d.h_r;
+  p->part_items = has_ws ? slots_for(cfg, d, a->q_len) : 0;
   p->scale_log2 = a->softmax_scale * 1.4426950408889634f;
   p->pos_inf = INFINITY;
   p->o_mul = a->o_mul;
@@ -646,8 +651,8 @@ mj_status mj_merge_lse(const mj_config* cfg, const mj_merge_args* a, hipStream_t
   p.o_part = reinterpret_cast<const float*>(ws + wl.o_off);
   p.m_part = reinterpret_cast<const float*>(ws + wl.m_off);
   p.l_part = reinterpret_cast<const float*>(ws + wl.l_off);
-  p.nqp = d.nq_max;
-  p.part_items = d.slots_max;
+  p.nqp = a->q_len * d.h_r;
+  p.part_items = slots_for(cfg, d, a->q_len);
   p.out = static_cast<uint16_t*>(a->out);
   p.out_f32 = cfg->out_f32;
   p.out_ts = a->out_tok_stride;

@@ -39,11 +39,11 @@ struct DecodeParams {
   const int32_t* work;         // plan + 0
   const int32_t* n_splits;     // plan + 4*cap_max
   const int32_t* split_begin;  // plan + 4*cap_max + max_num_seqs
-  float* o_part;               // (S_max, h_k, nqp, 128)
-  float* m_part;               // (S_max, h_k, nqp)   log2 domain
-  float* l_part;               // (S_max, h_k, nqp)
-  int nqp;                     // partial row stride = max_q_len * h_r
-  int part_items;              // S_max: items that may hold partials
+  float* o_part;               // (S, h_k, nqp, 128)
+  float* m_part;               // (S, h_k, nqp)   log2 domain
+  float* l_part;               // (S, h_k, nqp)
+  int nqp;                     // partial row stride = q_len * h_r of this call
+  int part_items;              // S = slots for this q_len: items that may hold partials
   float scale_log2;            // softmax_scale * log2(e)
   float pos_inf;               // +inf, as an argument: max(a, b) = med3(a, b, pos_inf)
                                // is one instruction only while the compiler
