@@ -510,6 +510,27 @@ typedef struct mj_step_args {
  * Errors: those of the three calls. */
 mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* args, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): mj_decode_step
+ * with the plan buffer and the workspace taken from a static device array of
+ * the library instead of the caller's buffers.  The array holds
+ * MJ_NOALLOC_SCRATCH_BYTES per GPU the library runs on, from the first call
+ * on that GPU until the process ends; a config needing more
+ * (mj_noalloc_scratch_bytes: the plan buffer rounded up to 256 bytes plus
+ * the workspace) is rejected with ECAPACITY before anything is enqueued.
+ * args->decode.plan and args->decode.workspace must be NULL and
+ * args->plan_on_device 1 (the step plans from the device lengths; num_work
+ * and with_reduction come from mj_plan_shape); cfg->step_merge 1 is
+ * EUNSUPPORTED.  The call allocates and frees nothing.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (streams with
+ * no ordering between them) race.  Results are those of mj_decode_step on
+ * caller-owned buffers, bit for bit.  Errors: those of mj_decode_step,
+ * EINVAL (a plan or workspace pointer given, plan_on_device 0), ECAPACITY,
+ * EUNSUPPORTED, EHIP. */
+#define MJ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+size_t mj_noalloc_scratch_bytes(const mj_config* cfg);
+mj_status mj_decode_step_noalloc(const mj_config* cfg, const mj_step_args* args, hipStream_t stream);
+
 /* Test probes (not part of a decode step).
  * mj_debug_gather_kv copies the codes of tokens 0..seq_len-1 of one
  * (sequence, KV head) from the K (which = 0) or V (which = 1) pool, or for

@@ -127,6 +127,17 @@ def mj_decode_step(cfg: Config, args: StepArgs, stream=None):
     check(lib().mj_decode_step(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_decode_step")
 
 
+def mj_decode_step_noalloc(cfg: Config, args: StepArgs, stream=None):
+    """mj_decode_step with the library's static per-GPU plan buffer and
+    workspace (args.decode.plan / .workspace None, plan_on_device 1)."""
+    check(lib().mj_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)),
+          "mj_decode_step_noalloc")
+
+
+def mj_noalloc_scratch_bytes(cfg: Config) -> int:
+    return lib().mj_noalloc_scratch_bytes(ctypes.byref(cfg))
+
+
 def mj_write_kv(cfg: Config, args: WriteArgs, stream=None):
     check(lib().mj_write_kv(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)), "mj_write_kv")
 

@@ -117,10 +117,12 @@ def _load():
         "mj_plan_split_kv": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, _p, P(PlanInfo), _p]),
         "mj_plan_split_kv_device": (_i32, [P(Config), _p, _i32, _i32, _i32, _i32, _p, P(PlanInfo), _p]),
         "mj_plan_shape": (_i32, [P(Config), _i32, _i32, _i32, P(PlanInfo)]),
+        "mj_noalloc_scratch_bytes": (ctypes.c_size_t, [P(Config)]),
         "mj_quantize_q": (_i32, [P(Config), _p, _i64, _i64, _p, _i32, _i32, _p, _p, _p]),
         "mj_paged_decode": (_i32, [P(Config), P(DecodeArgs), _p]),
         "mj_merge_lse": (_i32, [P(Config), P(MergeArgs), _p]),
         "mj_decode_step": (_i32, [P(Config), P(StepArgs), _p]),
+        "mj_decode_step_noalloc": (_i32, [P(Config), P(StepArgs), _p]),
         "mj_write_kv": (_i32, [P(Config), P(WriteArgs), _p]),
         "mj_draft_advance": (_i32, [P(Config), P(DraftArgs), _p]),
         "mj_combine_lse": (_i32, [P(Config), P(CombineArgs), _p]),

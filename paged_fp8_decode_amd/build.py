@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmj.so")
 
 HIP_SOURCES = ["mj_qquant.hip", "mj_decode_generic.hip", "mj_decode_mfma.hip", "mj_plan.hip", "mj_write.hip",
-               "mj_draft.hip", "mj_combine.hip"]
+               "mj_draft.hip", "mj_combine.hip", "mj_noalloc.hip"]
 HOST_SOURCES = ["mj_host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

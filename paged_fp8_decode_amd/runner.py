@@ -12,7 +12,7 @@ from __future__ import annotations
 import torch
 
 from . import (DecodeArgs, MergeArgs, PlanInfo, SCALE_KINDS, StepArgs, check, mj_config, mj_config_check,
-               mj_decode_step, mj_merge_lse, mj_paged_decode, mj_plan_shape, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
+               mj_decode_step, mj_decode_step_noalloc, mj_merge_lse, mj_paged_decode, mj_plan_shape, mj_plan_buffer_bytes, mj_plan_capacity, mj_plan_split_kv, mj_plan_split_kv_device,
                mj_quantize_q, mj_workspace_bytes)
 
 
@@ -81,7 +81,7 @@ class DecodeStep:
     def run(self, *, q, k_cache, v_cache, k_strides, v_strides, num_pages, block_table, seq_lens, k_descale,
             v_descale, descale_kind, softmax_scale, out, lse=None, q_mul=None, o_mul=None, causal=True,
             info: PlanInfo | None = None, stream=None, events=None, fused=False, plan_on_device=False, margin=0,
-            k_block_scale=None, v_block_scale=None, k_bs_strides=None, v_bs_strides=None):
+            k_block_scale=None, v_block_scale=None, k_bs_strides=None, v_bs_strides=None, noalloc=False):
         """quantize Q -> decode -> merge (iff the plan split), all on ``stream``;
         with ``fused`` one ``mj_decode_step`` call instead.
 
@@ -91,9 +91,12 @@ class DecodeStep:
         after the decode launch (the step call when fused).  ``plan_on_device``
         (fused only): the step plans from ``seq_lens`` itself (``info`` from
         ``plan_shape``).  nvfp4 caches also pass the two block-scale pools
-        (uint8) and their byte strides (page, slot, head).
+        (uint8) and their byte strides (page, slot, head).  ``noalloc``
+        (with ``fused`` and ``plan_on_device``): ``mj_decode_step_noalloc``,
+        the library's own plan buffer and workspace instead of this object's.
         """
         assert fused or not plan_on_device
+        assert not noalloc or (fused and plan_on_device)
         info = info or self.info
         assert info is not None, "plan() first"
         b, ql = info.num_seqs, info.q_len
@@ -130,9 +133,13 @@ class DecodeStep:
             sa = StepArgs(decode=a, q=q.data_ptr(), q_tok_stride=q.stride(0), q_head_stride=q.stride(1),
                           q_mul=q_mul.data_ptr() if q_mul is not None else None,
                           plan_on_device=int(plan_on_device), margin=margin)
+            if noalloc:
+                sa.decode.plan = None
+                sa.decode.workspace = None
+                sa.decode.workspace_bytes = 0
             if events:
                 events[0].record(stream)
-            mj_decode_step(self.cfg, sa, stream)
+            (mj_decode_step_noalloc if noalloc else mj_decode_step)(self.cfg, sa, stream)
             if events:
                 events[1].record(stream)
             return out
@@ -177,7 +184,7 @@ class DecodeStep:
         return self.plan_shape(wl.spec.b, wl.spec.q_len, wl.block_table.shape[1])
 
     def run_workload(self, wl, out, lse=None, info=None, stream=None, events=None, fused=False,
-                     plan_on_device=False):
+                     plan_on_device=False, noalloc=False):
         ks, vs = wl.kv_strides()
         bs = {}
         if wl.k_bs_pool is not None:
@@ -188,7 +195,7 @@ class DecodeStep:
                         k_descale=wl.k_descale, v_descale=wl.v_descale, descale_kind=wl.descale_kind,
                         softmax_scale=wl.softmax_scale, out=out, lse=lse, q_mul=wl.q_mul, o_mul=wl.o_mul,
                         causal=wl.spec.causal, info=info, stream=stream, events=events, fused=fused,
-                        plan_on_device=plan_on_device)
+                        plan_on_device=plan_on_device, noalloc=noalloc)
 
 
 def new_output(wl, device=None, out_f32=False):

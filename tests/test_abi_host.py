@@ -442,3 +442,26 @@ def test_library_default_workload_plans(b, h_q, h_k, q_len, L, P_, fmt, expect):
     work, ns, _ = _unpack(cfg, img, q_len)
     items = int(np.sum(work[:, 0] >= 0))
     assert (info.slots, info.chunk_tiles, int(ns[0]), items, info.with_reduction, info.num_work) == expect
+
+
+@no_gpu
+def test_noalloc_step_errors_come_before_any_device_work():
+    """mj_decode_step_noalloc rejects caller buffers, a host plan, the
+    in-kernel merge and configs beyond its static array on the host."""
+    L = mj.lib()
+    cfg = _cfg()
+    need = mj.mj_noalloc_scratch_bytes(cfg)
+    assert 0 < need == -(-mj.mj_plan_buffer_bytes(cfg) // 256) * 256 + mj.mj_workspace_bytes(cfg)
+    assert need <= 32 << 20
+    ok = dict(plan_on_device=1)
+    for kw, status in ((dict(plan_on_device=0), mj.MJ_EINVAL),
+                       (dict(ok, decode=mj.DecodeArgs(plan=FAKE)), mj.MJ_EINVAL),
+                       (dict(ok, decode=mj.DecodeArgs(workspace=FAKE)), mj.MJ_EINVAL)):
+        assert L.mj_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(mj.StepArgs(**kw)), None) == status, kw
+    assert L.mj_decode_step_noalloc(ctypes.byref(_cfg(step_merge=1)), ctypes.byref(mj.StepArgs(**ok)),
+                                    None) == mj.MJ_EUNSUPPORTED
+    big = _cfg(h_q=64, h_k=1, max_num_seqs=4096, max_q_len=16)
+    assert mj.mj_noalloc_scratch_bytes(big) > 32 << 20
+    assert L.mj_decode_step_noalloc(ctypes.byref(big), ctypes.byref(mj.StepArgs(**ok)), None) == mj.MJ_ECAPACITY
+    assert L.mj_decode_step_noalloc(ctypes.byref(_cfg(head_dim=64)), ctypes.byref(mj.StepArgs(**ok)),
+                                    None) == mj.MJ_EUNSUPPORTED
