@@ -204,18 +204,18 @@ __device__ __forceinline__ float lane_f(float x, int l) {
 // doubling the count.  inf must be a run-time value (a kernel argument):
 // with the constant the median is folded back into fmaxf.
 __device__ __forceinline__ float fmax2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
+// max(a, b, c) in one instruction (the inputs are finite logits or -inf)
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 // reduce over the 4 lane groups jj (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float max_jj(float x, float inf) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmax2(__uint_as_float(a[0]), __uint_as_float(a[1]), inf);
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmax2(__uint_as_float(b[0]), __uint_as_float(b[1]), inf);
-}
-__device__ __forceinline__ float sum_jj(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 // Keeps the scheduler from hoisting the next granule's computation above the
 // loads just issued: the wait before that computation then leaves the new
@@ -498,23 +498,28 @@ __device__ __forceinline__ void qk_tile(const KRows<FMT>& K, int k, const QOps<F
 template <int NQB, int NRB>
 struct State {
   float m[NRB];         // reference max of this lane's softmax row, log2 units
-  float l[NRB];         // this lane's partial sum of that row
+  v4f l[NRB];           // sums of the rounded P of O rows 16R + (4jj + v) % NQB (a
+                        // matrix-core product of P with ones: the PV numerator's own P)
   v4f acc[NRB][8];      // O rows 16R + (4jj + v) % NQB, channel 8n + q: acc[R][q][v]
 };
 
 // e4m3 PV for channels 2PR and 2PR + 1 of the lane's 8-channel group (bytes
-// 2PR % 4 and 2PR % 4 + 1 of dword PR / 2).
+// 2(PR % 2) and 2(PR % 2) + 1 of dword PR / 2).  One byte permute per token
+// pair (2i, 2i + 1) puts each channel's two codes side by side, so one packed
+// e4m3 -> bf16 conversion (exact) gives a whole B-operand word: the pair's
+// two tokens of one channel.
 template <int FMT, int PR, int NQB, int NRB>
 __device__ __forceinline__ void pv_pair(const VRows<FMT>& V, const v8bf (&pa)[NRB], State<NQB, NRB>& st) {
-  float a[8], b[8];
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  // bytes [t0 c, t1 c, t0 c+1, t1 c+1] of channel bytes c = 2(PR % 2)
+  constexpr uint32_t sel = (PR & 1) ? 0x07030602u : 0x05010400u;
+  u32x4 wa, wb;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const v2f x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(V.d[e][PR >> 1], 1.0f, (PR & 1) != 0);
-    a[e] = x[0];
-    b[e] = x[1];
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = __builtin_amdgcn_perm(V.d[2 * i + 1][PR >> 1], V.d[2 * i][PR >> 1], sel);
+    wa[i] = __builtin_bit_cast(uint32_t, (v2bf_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+    wb[i] = __builtin_bit_cast(uint32_t, (v2bf_t)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
   }
-  const u32x4 wa = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(a[4], a[5]), pack_bf16(a[6], a[7])};
-  const u32x4 wb = {pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3]), pack_bf16(b[4], b[5]), pack_bf16(b[6], b[7])};
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     st.acc[R][2 * PR] =
@@ -613,26 +618,28 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
       const v4f d = dk[R];
       if (full) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[R][k][v] = d[v] * c.cscale;
+        for (int v = 0; v < 4; ++v) s[R][k][v] = d[v];
       } else {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = tk + 4 * c.jj + v;
           const bool vis = t < end && (!c.causal || t <= c.lim0 + row_tok[R]);
-          s[R][k][v] = vis ? d[v] * c.cscale : -INFINITY;
+          s[R][k][v] = vis ? d[v] : -INFINITY;
         }
       }
     }
   }
-  // ---- online softmax: max of each row over the granule, raised lazily
+  // ---- online softmax: max of each row over the granule, raised lazily.
+  // The logits stay unscaled dot products; cscale > 0 (its sign is folded
+  // into the Q operand), so the scaled maximum is cscale times the raw one.
   float M[NRB];
   bool raise = false;
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     const float inf = c.pos_inf;
-    const float mx = fmax2(fmax2(fmax2(s[R][0][0], s[R][0][1], inf), fmax2(s[R][0][2], s[R][0][3], inf), inf),
-                           fmax2(fmax2(s[R][1][0], s[R][1][1], inf), fmax2(s[R][1][2], s[R][1][3], inf), inf), inf);
-    M[R] = max_jj(mx, inf);
+    const float mx = fmax3(fmax3(s[R][0][0], s[R][0][1], s[R][0][2]), fmax3(s[R][0][3], s[R][1][0], s[R][1][1]),
+                           fmax2(s[R][1][2], s[R][1][3], inf));
+    M[R] = max_jj(mx, inf) * c.cscale;
     raise |= M[R] > st.m[R] + kLazyMax;
   }
   if constexpr (NQB == 4 && NRB == 1) {
@@ -645,10 +652,8 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
         const float a = exp2f(mr - Mr);       // m = -inf -> 0
 #pragma unroll
         for (int q = 0; q < 8; ++q) st.acc[0][q][r] *= a;
-        if ((c.n & 3) == r) {
-          st.m[0] = Mr;
-          st.l[0] *= a;
-        }
+        st.l[0][r] *= a;
+        if ((c.n & 3) == r) st.m[0] = Mr;
       }
     }
   } else {
@@ -658,7 +663,6 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
         const bool up = M[R] > st.m[R] + kLazyMax;
         const float a = up ? exp2f(st.m[R] - M[R]) : 1.0f;
         st.m[R] = up ? M[R] : st.m[R];
-        st.l[R] *= a;
         // O-layout row 16R + (4jj + v) % NQB lives in softmax-layout lane
         // (jj, (4jj + v) % NQB)
 #pragma unroll
@@ -667,13 +671,19 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
           const float av = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(a)));
 #pragma unroll
           for (int q = 0; q < 8; ++q) st.acc[R][q][v] *= av;
+          st.l[R][v] *= av;
         }
       }
     }
   }
-  // ---- P (bf16 A operands; fp16 for nvfp4) and the row sums
+  // ---- P (bf16 A operands; fp16 for nvfp4): p = 2^(cscale * s - m), the
+  // scale folded into one fma; and the row sums of the rounded P, as the
+  // product of P with a ones operand on the matrix core
   using PA = typename std::conditional<Fmt<FMT>::kPvF16, v8h, v8bf>::type;
   PA pa[NRB];
+  const u32x4 ones_w = Fmt<FMT>::kPvF16 ? (u32x4){0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                                        : (u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const PA ones = __builtin_bit_cast(PA, ones_w);
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     const float ms = st.m[R] == -INFINITY ? 0.0f : st.m[R];
@@ -681,10 +691,7 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        p[4 * k + v] = exp2_fast(s[R][k][v] - ms);
-        st.l[R] += p[4 * k + v];
-      }
+      for (int v = 0; v < 4; ++v) p[4 * k + v] = exp2_fast(__builtin_fmaf(s[R][k][v], c.cscale, -ms));
     u32x4 pw;  // element e = 4k + v, token pairs per word
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -694,6 +701,10 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
         pw[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
     }
     pa[R] = __builtin_bit_cast(PA, pw);
+    if constexpr (Fmt<FMT>::kPvF16)
+      st.l[R] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[R], ones, st.l[R], 0, 0, 0);
+    else
+      st.l[R] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[R], ones, st.l[R], 0, 0, 0);
   }
   // ---- PV
   if constexpr (Fmt<FMT>::kPvF16) {
@@ -753,7 +764,7 @@ void decode_mfma_kernel(DecodeParams p) {
   using F = Fmt<FMT>;
   constexpr int kRows = NQB * NRB;  // rows of the GQA group this instance serves (padded)
   __shared__ float o_s[kWaves][kRows][kHeadDim];
-  __shared__ float m_s[kWaves][kRows], l_s[kWaves][kRows];
+  __shared__ float m_s[kWaves][kRows], l_s[kWaves][kRows], f_s[kWaves][kRows];
   __shared__ __align__(16) uint8_t q_s[kRows][kHeadDim];  // fused step: this item's e4m3 Q rows
   __shared__ float red_s[kWaves];
   __shared__ int last_s;
@@ -943,16 +954,22 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red_s[i]);
     qdesc = q_scale_from_amax(amax);
+    const float rq = 1.0f / qdesc;
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
       const int v = threadIdx.x + k * kThreads;
-      if (v < nvec) *reinterpret_cast<uint2*>(&q_s[v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc);
+      if (v < nvec) *reinterpret_cast<uint2*>(&q_s[v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc, rq);
     }
     __syncthreads();
   } else if (!F::kQBf16) {
     qdesc = p.q_descale[(int64_t)seq * p.h_k + g];
   }
-  c.cscale = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
+  // the logit scale (log2 units) applied to raw dot products; its sign goes
+  // into the Q operand below, so that the scale the softmax multiplies by is
+  // positive (a zero scale becomes the smallest normal: every logit ~ 0)
+  const float craw = qdesc * load_descale(p.kd, p.kd_kind, seq, g, p.h_k) * p.scale_log2;
+  const bool qneg = craw < 0.0f;  // wave-uniform
+  c.cscale = craw != craw ? craw : fmaxf(fabsf(craw), 1.17549435e-38f);
 
   // B operands of QK^T: column n of block R = Q row 16R + n % NQB of the
   // tile (zero past its rows)
@@ -1020,11 +1037,28 @@ void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
+  if (qneg) {  // negate Q exactly: flip the sign bit of every element
+#pragma unroll
+    for (int R = 0; R < NRB; ++R) {
+      if constexpr (Fmt<FMT>::kQkF16 || Fmt<FMT>::kQkBf16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 w = __builtin_bit_cast(u32x4, qo.b[R][i]);
+          w ^= 0x80008000u;
+          qo.b[R][i] = __builtin_bit_cast(std::remove_reference_t<decltype(qo.b[R][i])>, w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qo.b[R][i] ^= (int)0x80808080u;
+      }
+    }
+  }
+
   State<NQB, NRB> st;
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     st.m[R] = -INFINITY;
-    st.l[R] = 0.0f;
+    st.l[R] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 8; ++q) st.acc[R][q] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -1070,55 +1104,80 @@ void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
-  // per-wave results: O rows x channels from the lanes holding distinct rows,
-  // max and sum of each row from the softmax layout
+  // per-wave results: O rows x channels and the row sums (both in the O
+  // layout) from the lanes holding distinct rows, the max of each row from the
+  // softmax layout
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
-    const float lrow = sum_jj(st.l[R]);  // lane (n, jj): sum of row 16R + n % NQB
     if (4 * jj < NQB) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o_s[wave][NQB * R + 4 * jj + v][8 * n + q] = st.acc[R][q][v];
+      if (n == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) l_s[wave][NQB * R + 4 * jj + v] = st.l[R][v];
+      }
     }
-    if (jj == 0 && n < NQB) {
-      l_s[wave][NQB * R + n] = lrow;
-      m_s[wave][NQB * R + n] = st.m[R];
-    }
+    if (jj == 0 && n < NQB) m_s[wave][NQB * R + n] = st.m[R];
   }
   __syncthreads();
 
-  // combine the 4 waves; thread -> (row r, channel ch), r in {tid>>7, (tid>>7)+2, ...}
-  const int ch = threadIdx.x & 127;
+  // per row (thread r): the four waves' weights 2^(m_w - M), divided by the
+  // row sum when the item is the sequence's only one; the row's LSE, or its
+  // split partial's max and sum
   const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k);
-  for (int r = threadIdx.x >> 7; r < nq; r += 2) {
+  if (threadIdx.x < kRows) {
+    const int r = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, m_s[ww][r]);
     const float Ms = M == -INFINITY ? 0.0f : M;
-    float Lsum = 0.0f, O = 0.0f;
+    float wt[kWaves], Lsum = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float wt = exp2f(m_s[ww][r] - Ms);
-      Lsum += wt * l_s[ww][r];
-      O += wt * o_s[ww][r][ch];
+      wt[ww] = exp2f(m_s[ww][r] - Ms);
+      Lsum += wt[ww] * l_s[ww][r];
     }
-    const int rg = row0 + r;  // row of the group
-    const int t = rg / p.h_r;
-    const int h = g * p.h_r + (rg - t * p.h_r);
-    const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vd;
-    if (single) {
-      const float o = Lsum > 0.0f ? O / Lsum * om : 0.0f;
-      store_out(p.out, p.out_f32, ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + ch, o);
-      if (ch == 0 && p.lse)
-        p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
-    } else if (w < p.part_items) {
-      // written through to device-coherent memory, for a merge on any XCD
-      const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + rg;
-      store_coherent(&p.o_part[idx * kHeadDim + ch], O * om);
-      if (ch == 0) {
+    const float f = single ? (Lsum > 0.0f ? 1.0f / Lsum : 0.0f) : 1.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) f_s[ww][r] = wt[ww] * f;
+    if (r < nq) {
+      const int rg = row0 + r;
+      const int t = rg / p.h_r;
+      const int h = g * p.h_r + (rg - t * p.h_r);
+      if (single) {
+        if (p.lse)
+          p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+      } else if (w < p.part_items) {
+        // written through to device-coherent memory, for a merge on any XCD
+        const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + rg;
         store_coherent(&p.m_part[idx], Lsum > 0.0f ? M : -INFINITY);
         store_coherent(&p.l_part[idx], Lsum);
+      }
+    }
+  }
+  __syncthreads();
+
+  // combine the 4 waves: thread -> channel ch of rows tid / 128 + 2k, every
+  // row's LDS reads issued together (a compile-time row count)
+  const int ch = threadIdx.x & 127;
+#pragma unroll
+  for (int k = 0; k < (kRows + 1) / 2; ++k) {
+    const int r = (threadIdx.x >> 7) + 2 * k;
+    if (r < nq) {
+      float O = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) O += f_s[ww][r] * o_s[ww][r][ch];
+      const int rg = row0 + r;  // row of the group
+      const int t = rg / p.h_r;
+      const int h = g * p.h_r + (rg - t * p.h_r);
+      const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vd;
+      if (single) {
+        store_out(p.out, p.out_f32, ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + ch, O * om);
+      } else if (w < p.part_items) {
+        const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + rg;
+        store_coherent(&p.o_part[idx * kHeadDim + ch], O * om);
       }
     }
   }
@@ -1198,8 +1257,10 @@ hipError_t launch_fmt(DecodeParams& p, int nt, int tune, hipStream_t s) {
   if (p.n_q <= 16) return pf2 ? launch_shape<FMT, 16, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
   // 32 rows (per tile): two waves per SIMD fit the register budget (VGPR accumulators,
   // no copies through AGPRs) except for packed fp6, whose V expansion needs
-  // the one-wave budget
-  if constexpr (Fmt<FMT>::kPacked6)
+  // the one-wave budget, and 16-bit Q operands (bf16 Q; nvfp4), which take
+  // 32 more registers (the default plan runs 32-row groups one workgroup per
+  // CU either way)
+  if constexpr (Fmt<FMT>::kPacked6 || Fmt<FMT>::kQkBf16 || Fmt<FMT>::kQkF16)
     return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
   else
     return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 2>(p, nt, s);

@@ -166,6 +166,22 @@ __device__ __forceinline__ void unpack16_6bit(uint32_t w0, uint32_t w1, uint32_t
 
 namespace mj {
 
+// x / s rounded to nearest from y = RN(1/s): q = RN(x y) is a faithful
+// quotient, the residual x - q s is exact in one FMA, and RN(q + r y) is the
+// correctly rounded quotient (Markstein's theorem; Muller et al., Handbook of
+// Floating-Point Arithmetic, on division by FMA).  Quotients that underflow
+// into fp32 subnormals or overflow lie far below or above every rounding
+// boundary of the four formats, so their codes are those of the exact
+// quotient.
+// Scales are positive and finite; y = 1 / s computed with the (correctly
+// rounded) division.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-q, s, x);
+  // a zero quotient keeps its sign (-0 / s = -0; the correction would give +0)
+  return x == 0.0f ? x : __builtin_fmaf(r, y, q);
+}
+
 // Dynamic e4m3 quantization of Q per (sequence, KV head), the arithmetic
 // both the stand-alone quantize kernel and the fused decode step use, so the
 // two produce the same codes and scale bit for bit (mjolnir-kernel wheel page
@@ -220,13 +236,15 @@ __device__ __forceinline__ void q_load8(const uint16_t* q, int64_t q_ts, int64_t
 
 __device__ __forceinline__ float q_scale_from_amax(float amax) { return fmaxf(amax, kQAmaxFloor) / kFp8Max; }
 
-// Eight e4m3 codes of x / s, little-endian in two dwords.
-__device__ __forceinline__ uint2 q_codes8(const float x[8], float s) {
+// Eight e4m3 codes of x / s, little-endian in two dwords; rs = 1 / s (the
+// correctly rounded reciprocal), so each quotient is div_rn's correctly
+// rounded one without a division per value.
+__device__ __forceinline__ uint2 q_codes8(const float x[8], float s, float rs) {
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) lo |= e4m3_rne(x[e] / s) << (8 * e);
+  for (int e = 0; e < 4; ++e) lo |= e4m3_rne(div_rn(x[e], s, rs)) << (8 * e);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) hi |= e4m3_rne(x[4 + e] / s) << (8 * e);
+  for (int e = 0; e < 4; ++e) hi |= e4m3_rne(div_rn(x[4 + e], s, rs)) << (8 * e);
   return make_uint2(lo, hi);
 }
 

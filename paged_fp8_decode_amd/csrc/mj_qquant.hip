@@ -44,12 +44,13 @@ __global__ __launch_bounds__(kQThreads) void qquant_kernel(QQuantParams p) {
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   const float s = q_scale_from_amax(amax);
+  const float rs = 1.0f / s;
   uint8_t* dst = p.q8 + ((int64_t)seq * p.h_k + g) * p.n_q * kHeadDim;
   for (int v = tid; v < nvec; v += kQThreads) {
     const int row = v >> 4, c0 = (v & 15) * 8;
     float x[8];
     q_load8(p.q, p.q_ts, p.q_hs, p.q_mul, p.q_len, p.h_r, seq, g, row, c0, x);
-    *reinterpret_cast<uint2*>(dst + (int64_t)row * kHeadDim + c0) = q_codes8(x, s);
+    *reinterpret_cast<uint2*>(dst + (int64_t)row * kHeadDim + c0) = q_codes8(x, s, rs);
   }
   if (tid == 0) p.q_descale[(int64_t)seq * p.h_k + g] = s;
 }

@@ -32,21 +32,6 @@ namespace {
 
 constexpr int kWThreads = 256;
 
-// x / s rounded to nearest from y = RN(1/s): q = RN(x y) is a faithful
-// quotient, the residual x - q s is exact in one FMA, and RN(q + r y) is the
-// correctly rounded quotient (Markstein's theorem; Muller et al., Handbook of
-// Floating-Point Arithmetic, on division by FMA).  Quotients that underflow
-// into fp32 subnormals or overflow lie far below or above every rounding
-// boundary of the four formats, so their codes are those of the exact
-// quotient.
-// Scales are positive and finite.
-__device__ __forceinline__ float div_rn(float x, float s, float y) {
-  const float q = x * y;
-  const float r = __builtin_fmaf(-q, s, x);
-  // a zero quotient keeps its sign (-0 / s = -0; the correction would give +0)
-  return x == 0.0f ? x : __builtin_fmaf(r, y, q);
-}
-
 // dst_bs (nvfp4 only): the row's block-scale byte of these 16 channels
 template <int FMT>
 __device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc)[16], const float (&rc)[16], int c0,

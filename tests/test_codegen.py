@@ -33,15 +33,15 @@ DEFAULT = ["Li0ELi4ELi1ELi2ELi1ELi2E", "Li0ELi8ELi1ELi2ELi1ELi2E", "Li0ELi16ELi1
            "Li1ELi16ELi1ELi2ELi1ELi2E", "Li1ELi16ELi2ELi2ELi1ELi1E",
            # e4m3 KV with bf16 Q
            "Li2ELi4ELi1ELi2ELi1ELi2E", "Li2ELi8ELi1ELi2ELi1ELi2E", "Li2ELi16ELi1ELi2ELi1ELi2E",
-           "Li2ELi16ELi2ELi2ELi1ELi2E",
+           "Li2ELi16ELi2ELi2ELi1ELi1E",
            # e3m2 (bf6) and e2m1 (fp4) KV
            "Li3ELi4ELi1ELi2ELi1ELi2E", "Li3ELi8ELi1ELi2ELi1ELi2E", "Li3ELi16ELi1ELi2ELi1ELi2E",
            "Li3ELi16ELi2ELi2ELi1ELi1E", "Li4ELi4ELi1ELi2ELi1ELi2E", "Li4ELi8ELi1ELi2ELi1ELi2E",
            "Li4ELi16ELi1ELi2ELi1ELi2E", "Li4ELi16ELi2ELi2ELi1ELi2E",
            # nvfp4 KV with fp8 Q and with bf16 Q
            "Li5ELi4ELi1ELi2ELi1ELi2E", "Li5ELi8ELi1ELi2ELi1ELi2E", "Li5ELi16ELi1ELi2ELi1ELi2E",
-           "Li5ELi16ELi2ELi2ELi1ELi2E", "Li6ELi4ELi1ELi2ELi1ELi2E", "Li6ELi8ELi1ELi2ELi1ELi2E",
-           "Li6ELi16ELi1ELi2ELi1ELi2E", "Li6ELi16ELi2ELi2ELi1ELi2E"]
+           "Li5ELi16ELi2ELi2ELi1ELi1E", "Li6ELi4ELi1ELi2ELi1ELi2E", "Li6ELi8ELi1ELi2ELi1ELi2E",
+           "Li6ELi16ELi1ELi2ELi1ELi2E", "Li6ELi16ELi2ELi2ELi1ELi1E"]
 
 
 @pytest.fixture(scope="module")
