@@ -132,11 +132,14 @@ typedef struct mj_config {
                               plan's KV tiles are whole 16-token tiles and
                               slot strides are < 2^24 bytes, else the generic
                               kernel); 1 always the generic LDS-tiled kernel;
-                              10..17 the matrix-core kernel with tuning bits
+                              10..25 the matrix-core kernel with tuning bits
                               (value - 10): bit 0 two granules of prefetch,
                               bit 1 head-major grid, bit 2 XCD-grouped grid
                               (the KV heads of a work item on one XCD; takes
-                              precedence over bit 1)                         */
+                              precedence over bit 1), bit 3 four waves per
+                              workgroup where the default runs eight (a
+                              group of exactly one 32-row tile, e4m3 with
+                              fp8 Q or e2m1)                                 */
   int32_t kv_cache_policy; /* matrix-core kernel KV loads: 0 the library's
                               choice (K cached, V non-temporal), 1 every load
                               cached, 2 every load non-temporal, 3 K cached

@@ -186,6 +186,7 @@ __device__ __forceinline__ int q_half_offset(int jj, int h) {
 
 template <int FMT>
 struct KRows {  // tile k: this lane's codes [32jj, 32jj+32) of token n
+  int pg[2];    // the two tiles' pages (-1: dead), wave-uniform: found once, at the loads
   uint32_t d[2][Fmt<FMT>::kKDw];
   uint32_t s[Fmt<FMT>::kBlockScaled ? 2 : 1];  // nvfp4: scales of blocks 2jj, 2jj + 1 (low 16 bits)
 };
@@ -204,12 +205,7 @@ __device__ __forceinline__ float lane_f(float x, int l) {
 // doubling the count.  inf must be a run-time value (a kernel argument):
 // with the constant the median is folded back into fmaxf.
 __device__ __forceinline__ float fmax2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
-// max(a, b, c) in one instruction (the inputs are finite logits or -inf)
-__device__ __forceinline__ float fmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+
 // reduce over the 4 lane groups jj (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float max_jj(float x, float inf) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -287,7 +283,8 @@ __device__ __forceinline__ KRows<FMT> load_k(const Ctx& c, int gi) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int tk = t0 + 16 * k;
-    const int pg = tile_page(c, tk);
+    const int pg = __builtin_amdgcn_readfirstlane(tile_page(c, tk));  // wave-uniform: keep it scalar
+    R.pg[k] = pg;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.kpool, c.k_sp, c.k_ss, c.k_rec, pg, tk, c.pmask);
     if constexpr (Fmt<FMT>::kBlockScaled) {
       const __amdgpu_buffer_rsrc_t srs = tile_rsrc(c.ksbpool, c.ksb_sp, c.ksb_ss, c.ksb_rec, pg, tk, c.pmask);
@@ -317,14 +314,15 @@ __device__ __forceinline__ KRows<FMT> load_k(const Ctx& c, int gi) {
   return R;
 }
 
+// pgs: the tiles' pages as load_k found them for the same granule
 template <int FMT, bool NT>
-__device__ __forceinline__ VRows<FMT> load_v(const Ctx& c, int gi) {
+__device__ __forceinline__ VRows<FMT> load_v(const Ctx& c, int gi, const int (&pgs)[2]) {
   VRows<FMT> R;
   const int t0 = c.j0 + gi * kGran;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int tk = t0 + 16 * t;
-    const int pg = tile_page(c, tk);
+    const int pg = pgs[t];
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(c.vpool, c.v_sp, c.v_ss, c.v_rec, pg, tk, c.pmask);
     if constexpr (Fmt<FMT>::kBlockScaled) {
       const __amdgpu_buffer_rsrc_t srs = tile_rsrc(c.vsbpool, c.vsb_sp, c.vsb_ss, c.vsb_rec, pg, tk, c.pmask);
@@ -585,7 +583,9 @@ __device__ __forceinline__ float row_of(const Ctx& c, int R) {  // softmax-layou
   return 16 * R + (c.n % NQB);
 }
 
-template <int FMT, int NQB, int NRB>
+// MASK: the granule has a dead tile, tokens past the range end or (causal)
+// keys some row may not see; without it every logit is kept as is.
+template <int FMT, int NQB, int NRB, bool MASK>
 __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, const int (&row_tok)[NRB], int gi,
                                         const KRows<FMT>& K, VRows<FMT>& V, State<NQB, NRB>& st) {
   const int t0 = c.j0 + gi * kGran;
@@ -595,9 +595,16 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
   for (int k = 0; k < 2; ++k) {
     v4f dk[NRB];
     qk_tile<FMT, NRB>(K, k, qo, dk);
+    if constexpr (!MASK) {
+#pragma unroll
+      for (int R = 0; R < NRB; ++R)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[R][k][v] = dk[R][v];
+      continue;
+    }
     const int tk = t0 + 16 * k;
     // tokens at or past `end` are masked; a dead tile masks all of them
-    const int end = tile_page(c, tk) >= 0 ? c.j1 : 0;  // scalar; the block-table entry is cached
+    const int end = K.pg[k] >= 0 ? c.j1 : 0;
     if (tk + 16 > end) {  // wave-uniform: the tile crosses the range end
       // rows past the end hold whatever the page holds (NaN codes too):
       // their V is zeroed so that their zero probabilities add exact zeros
@@ -637,8 +644,8 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
 #pragma unroll
   for (int R = 0; R < NRB; ++R) {
     const float inf = c.pos_inf;
-    const float mx = fmax3(fmax3(s[R][0][0], s[R][0][1], s[R][0][2]), fmax3(s[R][0][3], s[R][1][0], s[R][1][1]),
-                           fmax2(s[R][1][2], s[R][1][3], inf));
+    const float mx = fmax2(fmax2(fmax2(s[R][0][0], s[R][0][1], inf), fmax2(s[R][0][2], s[R][0][3], inf), inf),
+                           fmax2(fmax2(s[R][1][0], s[R][1][1], inf), fmax2(s[R][1][2], s[R][1][3], inf), inf), inf);
     M[R] = max_jj(mx, inf) * c.cscale;
     raise |= M[R] > st.m[R] + kLazyMax;
   }
@@ -754,13 +761,37 @@ __device__ __forceinline__ void granule(const Ctx& c, const QOps<FMT, NRB>& qo, 
   }
 }
 
+// One granule, masked only where it has to be: wave-uniform, a granule whose
+// two tiles are live, end before the range end and (causal) hold only keys
+// every row may see -- row 0 of the block sees the fewest -- takes the body
+// without masking (groups of up to 16 rows).
+template <int FMT, int NQB, int NRB, int PF>
+__device__ __forceinline__ void granule_any(const Ctx& c, const QOps<FMT, NRB>& qo, const int (&row_tok)[NRB], int gi,
+                                            const KRows<FMT>& K, VRows<FMT>& V, State<NQB, NRB>& st) {
+  const int t0 = c.j0 + gi * kGran;
+  const bool full = (K.pg[0] | K.pg[1]) >= 0 && t0 + kGran <= c.j1 && (!c.causal || t0 + kGran - 1 <= c.lim0);
+  // (32-row tiles and the two-granule prefetch: a second copy of the body
+  // does not fit their register budget; nvfp4: with two bodies the byte
+  // loads of its V block scales get their zero-extension hoisted to the loop
+  // head, which then waits for most of the granule's loads.  The masked body
+  // alone, whose tile checks are wave-uniform branches, serves those.)
+  if (NRB == 1 && PF == 1 && !Fmt<FMT>::kBlockScaled && full)
+    granule<FMT, NQB, NRB, false>(c, qo, row_tok, gi, K, V, st);
+  else
+    granule<FMT, NQB, NRB, true>(c, qo, row_tok, gi, K, V, st);
+}
+
 // PF: granules of loads in flight ahead of the one being computed (1 or 2);
 // OCC: waves per SIMD the register budget is fitted to.
 // CP: cache policy of the KV loads, bit 0 = K non-temporal, bit 1 = V
 // non-temporal.
-template <int FMT, int NQB, int NRB, int CP, int PF, int OCC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+// W: waves per workgroup (4, or 8 for a 32-row tile that runs alone on its
+// CU: two waves per SIMD without cutting the item into more splits).
+template <int FMT, int NQB, int NRB, int CP, int PF, int OCC, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_mfma_kernel(DecodeParams p) {
+  constexpr int kWaves = W;
+  constexpr int kThreads = 64 * W;
   using F = Fmt<FMT>;
   constexpr int kRows = NQB * NRB;  // rows of the GQA group this instance serves (padded)
   __shared__ float o_s[kWaves][kRows][kHeadDim];
@@ -911,10 +942,10 @@ void decode_mfma_kernel(DecodeParams p) {
   int gi = wave;
   const bool run = gi < ngr;
   KRows<FMT> K0 = load_k<FMT, (CP & 1) != 0>(c, gi), K1;
-  VRows<FMT> V0 = load_v<FMT, (CP & 2) != 0>(c, gi), V1;
+  VRows<FMT> V0 = load_v<FMT, (CP & 2) != 0>(c, gi, K0.pg), V1;
   if constexpr (PF == 2) {
     K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWaves);
-    V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves);
+    V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves, K1.pg);
   }
 
   float qdesc = 1.0f;  // bf16-Q mode: no Q scale
@@ -1068,36 +1099,36 @@ void decode_mfma_kernel(DecodeParams p) {
     if constexpr (PF == 1) {
       while (true) {
         K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWaves);
-        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves);
+        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves, K1.pg);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K0, V0, st);
+        granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K0, V0, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K0 = load_k<FMT, (CP & 1) != 0>(c, gi + kWaves);
-        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves);
+        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves, K0.pg);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K1, V1, st);
+        granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K1, V1, st);
         gi += kWaves;
         if (gi >= ngr) break;
       }
     } else {
       while (true) {
         KRows<FMT> K2 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWaves);
-        VRows<FMT> V2 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves);
+        VRows<FMT> V2 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves, K2.pg);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K0, V0, st);
+        granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K0, V0, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K0 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWaves);
-        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves);
+        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves, K0.pg);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K1, V1, st);
+        granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K1, V1, st);
         gi += kWaves;
         if (gi >= ngr) break;
         K1 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWaves);
-        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves);
+        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves, K1.pg);
         issue_fence();
-        granule<FMT, NQB, NRB>(c, qo, row_tok, gi, K2, V2, st);
+        granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K2, V2, st);
         gi += kWaves;
         if (gi >= ngr) break;
       }
@@ -1159,12 +1190,13 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // combine the 4 waves: thread -> channel ch of rows tid / 128 + 2k, every
-  // row's LDS reads issued together (a compile-time row count)
+  // combine the waves: thread -> channel ch of rows tid / 128 + (W / 2) k,
+  // every row's LDS reads issued together (a compile-time row count)
   const int ch = threadIdx.x & 127;
+  constexpr int kRowStep = kThreads / 128;
 #pragma unroll
-  for (int k = 0; k < (kRows + 1) / 2; ++k) {
-    const int r = (threadIdx.x >> 7) + 2 * k;
+  for (int k = 0; k < (kRows + kRowStep - 1) / kRowStep; ++k) {
+    const int r = (threadIdx.x >> 7) + kRowStep * k;
     if (r < nq) {
       float O = 0.0f;
 #pragma unroll
@@ -1227,27 +1259,29 @@ void decode_mfma_kernel(DecodeParams p) {
       mp.h_k = p.h_k;
       mp.h_r = p.h_r;
       mp.n_q = p.n_q;
-      merge_one<true, 1, 8>(mp, seq, g, threadIdx.x);  // same batches as the merge kernel: same rounding
+      // same batches as the merge kernel: same rounding (its 256-thread layout)
+      if (threadIdx.x < 256) merge_one<true, 1, 8>(mp, seq, g, threadIdx.x);
     }
   }
 }
 
-template <int FMT, int NQB, int NRB, int PF, int OCC>
+template <int FMT, int NQB, int NRB, int PF, int OCC, int W = 4>
 hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
+  constexpr int kThreads = 64 * W;
   const int heads = p.h_k * p.row_tiles;
   const dim3 grid = p.head_major == 2 ? dim3((unsigned)((p.num_work + kXcds - 1) / kXcds * kXcds * heads))
                     : p.head_major ? dim3(heads, p.num_work) : dim3(p.num_work, heads);
   switch (cp) {
-    case 0: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 0, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 1, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 2, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 3, PF, OCC>), grid, dim3(kThreads), 0, s, p); break;
+    case 0: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 0, PF, OCC, W>), grid, dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 1, PF, OCC, W>), grid, dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 2, PF, OCC, W>), grid, dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 3, PF, OCC, W>), grid, dim3(kThreads), 0, s, p); break;
   }
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_fmt(DecodeParams& p, int nt, int tune, hipStream_t s) {
+hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide32, hipStream_t s) {
   const bool pf2 = tune & 2;  // two granules of prefetch instead of one
   // more than 32 rows: tiles of 32 rows (the 32-row instance), each
   // workgroup one tile of one (item, KV head)
@@ -1262,14 +1296,22 @@ hipError_t launch_fmt(DecodeParams& p, int nt, int tune, hipStream_t s) {
   // CU either way)
   if constexpr (Fmt<FMT>::kPacked6 || Fmt<FMT>::kQkBf16 || Fmt<FMT>::kQkF16)
     return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 1>(p, nt, s);
+  else if (pf2)
+    return launch_shape<FMT, 16, 2, 2, 1>(p, nt, s);
+  // a group of one 32-row tile is planned one workgroup per CU: eight waves
+  // (two per SIMD) share its item; row tiles of larger groups keep four waves
+  // so that two of their workgroups fit a CU
+  else if (p.row_tiles == 1 && wide32)
+    return launch_shape<FMT, 16, 2, 1, 2, 8>(p, nt, s);
   else
-    return pf2 ? launch_shape<FMT, 16, 2, 2, 1>(p, nt, s) : launch_shape<FMT, 16, 2, 1, 2>(p, nt, s);
+    return launch_shape<FMT, 16, 2, 1, 2>(p, nt, s);
 }
 
 }  // namespace
 
 // tune bits: 1 = two granules of prefetch, 2 = head-major grid, 4 = XCD-
-// grouped grid (over 2); -1 = the default for the format.  cache_policy: -1 = the default for the format,
+// grouped grid (over 2), 8 = four waves (not eight) for a lone 32-row tile;
+// -1 = the default for the format.  cache_policy: -1 = the default for the format,
 // else the CP bits.
 hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache_policy, int tune, hipStream_t s) {
   DecodeParams p = p_in;
@@ -1283,6 +1325,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
   if (tune < 0) tune = kv_format >= 3 ? 4 : 0;
   p.head_major = (tune & 4) ? 2 : ((tune & 2) ? 1 : 0);
   const int t = (tune & 1) ? 2 : 0;
+  const bool wide32 = (tune & 8) == 0;  // eight waves for a lone 32-row tile (bit 3: four)
   // default: K cached, V non-temporal.  A K tile's row lines are touched by
   // two (e4m3) or three (e2m3) load instructions, which the vector L1 then
   // serves after the first; V loads cover whole rows (e4m3) and stream.
@@ -1290,11 +1333,11 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
   // e4m3 at 32K 657 -> 647 us, ragged batch 225 -> 219 us.
   const int cp = cache_policy >= 0 ? cache_policy : 2;
   switch (kv_format) {
-    case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, s) : launch_fmt<0>(p, cp, t, s);
-    case 1: return launch_fmt<1>(p, cp, t, s);
-    case 2: return launch_fmt<3>(p, cp, t, s);
-    case 3: return launch_fmt<4>(p, cp, t, s);
-    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, s) : launch_fmt<5>(p, cp, t, s);
+    case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, wide32, s) : launch_fmt<0>(p, cp, t, wide32, s);
+    case 1: return launch_fmt<1>(p, cp, t, wide32, s);
+    case 2: return launch_fmt<3>(p, cp, t, wide32, s);
+    case 3: return launch_fmt<4>(p, cp, t, wide32, s);
+    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, wide32, s) : launch_fmt<5>(p, cp, t, wide32, s);
   }
 }
 

@@ -72,7 +72,7 @@ mj_status check_config(const mj_config* c) {
   if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
   if (c->out_f32 != 0 && c->out_f32 != 1) return MJ_EINVAL;
-  if (c->decode_kernel < 0 || (c->decode_kernel > 1 && (c->decode_kernel < 10 || c->decode_kernel > 17)))
+  if (c->decode_kernel < 0 || (c->decode_kernel > 1 && (c->decode_kernel < 10 || c->decode_kernel > 25)))
     return MJ_EINVAL;
   if (c->kv_cache_policy < 0 || c->kv_cache_policy > 4 || c->step_merge < 0 || c->step_merge > 2) return MJ_EINVAL;
   // the packed fp6 / fp4 formats take fp8 Q only

@@ -194,8 +194,9 @@ def test_gather_probe_bit_exact(mj, gpu, key):
 
 SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4",
               "32k", "32k_b16"]
-# mj_config.decode_kernel: 0 = automatic choice, 1 = generic LDS kernel
-VARIANTS = [0, 1]
+# mj_config.decode_kernel: 0 = automatic choice, 1 = generic LDS kernel, 18 =
+# the matrix-core kernel with four waves where the default runs eight
+VARIANTS = [0, 1, 18]
 
 
 @pytest.fixture
