@@ -19,7 +19,7 @@
 // page s / page_size, row s % page_size; a negative slot (padding) or one
 // past the pool is skipped.
 //
-// One thread per (KV head, 16 channels) of 8 tokens: 32 bytes of bf16 in
+// One thread per (KV head, 16 channels) of 1-4 tokens: 32 bytes of bf16 in
 // per side and token, 16 bytes (e4m3), 12 bytes (fp6) or 8 bytes (fp4;
 // nvfp4 also the block's scale byte) of codes out.  The
 // write touches every byte once.
@@ -32,12 +32,16 @@ namespace {
 
 constexpr int kWThreads = 256;
 
+// The 16 bf16 values of one (token, KV head, channel group) as loaded.
+struct Raw16 {
+  uint4 a, b;
+};
+
 // dst_bs (nvfp4 only): the row's block-scale byte of these 16 channels
 template <int FMT>
-__device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc)[16], const float (&rc)[16], int c0,
+__device__ __forceinline__ void write_side(const Raw16& in, const float (&sc)[16], const float (&rc)[16], int c0,
                                            uint8_t* dst_row, uint8_t* dst_bs) {
-  const uint4 a = *reinterpret_cast<const uint4*>(src);
-  const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+  const uint4 a = in.a, b = in.b;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t code[16];
   float q[16];
@@ -93,67 +97,107 @@ __device__ __forceinline__ void write_side(const uint16_t* src, const float (&sc
   }
 }
 
+// The 16 divisors of channels [c0, c0 + 16) of KV head g and their
+// correctly rounded reciprocals: one of each for a per-tensor or per-head
+// scale, sixteen for per-channel scales.
 __device__ __forceinline__ void load_divisors(const float* s, int kind, int g, int c0, float (&sc)[16],
                                               float (&rc)[16]) {
+  if (kind == 3) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    sc[i] = kind == 0 ? s[0] : (kind == 1 ? s[g] : s[g * kHeadDim + c0 + i]);
-    rc[i] = 1.0f / sc[i];  // correctly rounded
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = s[g * kHeadDim + c0 + i];
+      rc[i] = 1.0f / sc[i];
+    }
+  } else {
+    const float d = kind == 0 ? s[0] : s[g];
+    const float r = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = d;
+      rc[i] = r;
+    }
   }
 }
 
-// Thread -> (KV head g, channel group grp) of p.tokens_per_thread
-// consecutive tokens (the divisors are set up once per thread); the 8 h_k threads of one token's rows are adjacent, so each token's
-// bf16 rows are read with coalesced 16-byte loads.
-template <int FMT>
+// Thread -> (KV head g, channel group grp) of TPT consecutive tokens (the
+// divisors are set up once per thread); the 8 h_k threads of one token's
+// rows are adjacent, so each token's bf16 rows are read with coalesced
+// 16-byte loads.  Every slot and every input row of the thread's tokens is
+// loaded before any is encoded: the rows do not depend on the slots, so the
+// loads are in flight together instead of one token's chain at a time.
+template <int FMT, int TPT>
 __global__ __launch_bounds__(kWThreads) void write_kv_kernel(WriteParams p) {
   const int64_t gid = (int64_t)blockIdx.x * kWThreads + threadIdx.x;
   const int row_threads = p.h_k * 8;
-  const int tpt = p.tokens_per_thread;
-  const int64_t blocks = ((int64_t)p.num_tokens + tpt - 1) / tpt;
+  const int64_t blocks = ((int64_t)p.num_tokens + TPT - 1) / TPT;
   if (gid >= blocks * row_threads) return;
   const int r = (int)(gid % row_threads);
   const int64_t tb = gid / row_threads;
   const int grp = r & 7, g = r >> 3;
   const int c0 = grp * 16;
+  int64_t slot[TPT];
+  Raw16 kin[TPT], vin[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int64_t t = tb * TPT + u;
+    const bool ok = t < p.num_tokens;
+    const int64_t tc = ok ? t : tb * TPT;  // past the end: repeat the first token (loaded, never stored)
+    slot[u] = ok ? p.slots[tc] : -1;
+    const uint16_t* ks = p.key + tc * p.k_ts + (int64_t)g * p.k_hs + c0;
+    const uint16_t* vs = p.value + tc * p.v_ts + (int64_t)g * p.v_hs + c0;
+    kin[u].a = *reinterpret_cast<const uint4*>(ks);
+    kin[u].b = *reinterpret_cast<const uint4*>(ks + 8);
+    vin[u].a = *reinterpret_cast<const uint4*>(vs);
+    vin[u].b = *reinterpret_cast<const uint4*>(vs + 8);
+  }
   float ks[16], kr[16], vs[16], vr[16];
   load_divisors(p.ks, p.ks_kind, g, c0, ks, kr);
   load_divisors(p.vs, p.vs_kind, g, c0, vs, vr);
-  const int t_end = (int)min<int64_t>(p.num_tokens, (tb + 1) * tpt);
-  for (int t = (int)(tb * tpt); t < t_end; ++t) {
-    const int64_t slot = p.slots[t];
-    if (slot < 0) continue;
-    const int64_t page = slot >> p.page_shift;
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    if (slot[u] < 0) continue;
+    const int64_t page = slot[u] >> p.page_shift;
     if (page >= p.num_pages) continue;
-    const int64_t row = slot & ((1 << p.page_shift) - 1);
+    const int64_t row = slot[u] & ((1 << p.page_shift) - 1);
     uint8_t* kb = FMT == 4 ? p.kbs + page * p.kbs_sp + row * p.kbs_ss + (int64_t)g * p.kbs_sh + grp : nullptr;
     uint8_t* vb = FMT == 4 ? p.vbs + page * p.vbs_sp + row * p.vbs_ss + (int64_t)g * p.vbs_sh + grp : nullptr;
-    write_side<FMT>(p.key + (int64_t)t * p.k_ts + (int64_t)g * p.k_hs + c0, ks, kr, c0,
-                    p.kc + page * p.kc_sp + row * p.kc_ss + (int64_t)g * p.kc_sh, kb);
-    write_side<FMT>(p.value + (int64_t)t * p.v_ts + (int64_t)g * p.v_hs + c0, vs, vr, c0,
-                    p.vc + page * p.vc_sp + row * p.vc_ss + (int64_t)g * p.vc_sh, vb);
+    write_side<FMT>(kin[u], ks, kr, c0, p.kc + page * p.kc_sp + row * p.kc_ss + (int64_t)g * p.kc_sh, kb);
+    write_side<FMT>(vin[u], vs, vr, c0, p.vc + page * p.vc_sp + row * p.vc_ss + (int64_t)g * p.vc_sh, vb);
   }
+}
+
+template <int TPT>
+hipError_t launch_tpt(const WriteParams& p, hipStream_t s) {
+  const int64_t threads = ((int64_t)p.num_tokens + TPT - 1) / TPT * p.h_k * 8;
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + kWThreads - 1) / kWThreads));
+  switch (p.kv_format) {
+    case 0: hipLaunchKernelGGL((write_kv_kernel<0, TPT>), grid, dim3(kWThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((write_kv_kernel<1, TPT>), grid, dim3(kWThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((write_kv_kernel<2, TPT>), grid, dim3(kWThreads), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((write_kv_kernel<3, TPT>), grid, dim3(kWThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((write_kv_kernel<4, TPT>), grid, dim3(kWThreads), 0, s, p); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_write_kv(const WriteParams& p_in, hipStream_t s) {
-  // a few tokens per thread amortize the divisors once the grid is large;
-  // a small write (a decode step's new rows) keeps one token per thread
+  // per-channel scales: a few tokens per thread amortize the sixteen
+  // reciprocals per side once the grid is large (measured at 16K tokens x 8
+  // heads: e2m3 34.2 us at one token per thread, 29.8 us at four); per-tensor
+  // or per-head scales (one reciprocal) and small writes (a decode step's new
+  // rows) take one token per thread (e4m3 29.1 -> 26.9 us, nvfp4 36.3 -> 30.4)
   WriteParams p = p_in;
   const int64_t rows = (int64_t)p.num_tokens * p.h_k;
-  p.tokens_per_thread = rows >= (1 << 17) ? 8 : (rows >= (1 << 14) ? 2 : 1);
-  const int64_t threads = ((int64_t)p.num_tokens + p.tokens_per_thread - 1) / p.tokens_per_thread * p.h_k * 8;
-  if (threads == 0) return hipSuccess;
-  const dim3 grid((unsigned)((threads + kWThreads - 1) / kWThreads));
-  switch (p.kv_format) {
-    case 0: hipLaunchKernelGGL(write_kv_kernel<0>, grid, dim3(kWThreads), 0, s, p); break;
-    case 1: hipLaunchKernelGGL(write_kv_kernel<1>, grid, dim3(kWThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(write_kv_kernel<2>, grid, dim3(kWThreads), 0, s, p); break;
-    case 3: hipLaunchKernelGGL(write_kv_kernel<3>, grid, dim3(kWThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL(write_kv_kernel<4>, grid, dim3(kWThreads), 0, s, p); break;
+  const bool channel = p.ks_kind == 3 || p.vs_kind == 3;
+  p.tokens_per_thread = !channel ? 1 : (rows >= (1 << 17) ? 4 : (rows >= (1 << 14) ? 2 : 1));
+  switch (p.tokens_per_thread) {
+    case 4: return launch_tpt<4>(p, s);
+    case 2: return launch_tpt<2>(p, s);
+    default: return launch_tpt<1>(p, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace mj

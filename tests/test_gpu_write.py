@@ -324,3 +324,70 @@ def test_write_nvfp4_ties(mj, gpu):
     assert np.array_equal(v_pool.cpu().numpy(), ref[1])
     assert np.array_equal(bs[0].cpu().numpy(), ref[2])
     assert np.array_equal(bs[1].cpu().numpy(), ref[3])
+
+
+@pytest.mark.parametrize("kv_format,kind,n", [("e2m3", "channel", 16387), ("e4m3", "channel", 16386),
+                                              ("e2m1", "channel", 2049), ("nvfp4", "channel", 2051),
+                                              ("e3m2", "head", 16385)])
+def test_large_write_matches_oracle_on_sampled_tokens(mj, gpu, kv_format, kind, n):
+    """A write large enough to give each thread several tokens (8 KV heads,
+    thousands of tokens, a token count that leaves a ragged last group),
+    with padding and out-of-pool slots: the rows of a sample of tokens (the
+    first, the last group and random ones) equal the oracle's bytes, and
+    every row no token maps to is untouched."""
+    from oracle.formats import FMT_MAX, ROW_BYTES
+    from oracle.kvwrite import write_kv
+    say(f"large write {kv_format} {kind} n={n}")
+    rng = np.random.default_rng(zlib.crc32(f"large{kv_format}{kind}{n}".encode()))
+    h_k, P = 8, 16
+    pages = -(-(n + n // 4) // P) + 1
+    row = ROW_BYTES[kv_format]
+    ks = vs = _strides("NHD", P, h_k, row)
+    size = pages * P * h_k * row
+    init_k = rng.integers(0, 256, size, dtype=np.uint8)
+    init_v = rng.integers(0, 256, size, dtype=np.uint8)
+    key = torch.from_numpy(rng.standard_normal((n, h_k, 128)).astype(np.float32)).to(torch.bfloat16)
+    value = torch.from_numpy(rng.standard_normal((n, h_k, 128)).astype(np.float32) * 3).to(torch.bfloat16)
+    fmax = FMT_MAX.get(kv_format, 6.0 * 448.0)
+    if kind == "channel":
+        k_sc = (rng.uniform(2.0, 4.0, (h_k, 128)) / fmax).astype(np.float32)
+        v_sc = (rng.uniform(6.0, 12.0, (h_k, 128)) / fmax).astype(np.float32)
+    else:
+        k_sc = (rng.uniform(2.0, 4.0, h_k) / fmax).astype(np.float32)
+        v_sc = (rng.uniform(6.0, 12.0, h_k) / fmax).astype(np.float32)
+    slots = rng.permutation(pages * P)[:n].astype(np.int64)
+    slots[5::23] = -1
+    num_pages = pages - 1
+    slots[n - 2] = (pages - 1) * P + 1  # in the last group, past num_pages: skipped
+    bs = bs_np = None
+    if kv_format == "nvfp4":
+        bst = _strides("NHD", P, h_k, 8)
+        init_kb = rng.integers(0, 256, pages * P * h_k * 8, dtype=np.uint8)
+        init_vb = rng.integers(0, 256, pages * P * h_k * 8, dtype=np.uint8)
+        bs = (torch.from_numpy(init_kb.copy()).to(gpu), torch.from_numpy(init_vb.copy()).to(gpu), bst, bst)
+    k_pool = torch.from_numpy(init_k.copy()).to(gpu)
+    v_pool = torch.from_numpy(init_v.copy()).to(gpu)
+    cfg = mj.mj_config(h_q=h_k, h_k=h_k, page_size=P, max_num_seqs=1, kv_format=kv_format, num_cus=256)
+    _write(mj, gpu, cfg, key.to(gpu), value.to(gpu), torch.from_numpy(slots).to(gpu), k_pool, v_pool, ks, vs,
+           torch.from_numpy(k_sc).to(gpu), torch.from_numpy(v_sc).to(gpu), kind, num_pages, bs)
+    got = [k_pool.cpu().numpy(), v_pool.cpu().numpy()]
+    if bs is not None:
+        got += [bs[0].cpu().numpy(), bs[1].cpu().numpy()]
+    sample = np.unique(np.concatenate([np.arange(8), np.arange(n - 9, n), rng.choice(n, 120, replace=False)]))
+    if bs is not None:
+        bs_np = dict(bs_pools=(init_kb, init_vb), bs_strides=(bst, bst))
+    ref = write_kv((init_k, init_v), (ks, vs), P, kv_format, key[sample].float().numpy(),
+                   value[sample].float().numpy(), slots[sample], k_sc, v_sc, kind, num_pages=num_pages,
+                   **(bs_np or {}))
+    inits = [init_k, init_v] + ([init_kb, init_vb] if bs is not None else [])
+    others = np.setdiff1d(np.arange(n), sample)
+    others = others[(slots[others] >= 0) & (slots[others] // P < num_pages)]
+    # the row bytes of the tokens outside the sample are not compared; every other byte is
+    for which, (g_, r_, i_) in enumerate(zip(got, ref, inits)):
+        st, nb = ((ks, row), (vs, row), (bs[2], 8) if bs else None, (bs[3], 8) if bs else None)[which]
+        base = (slots[others] // P) * st[0] + (slots[others] % P) * st[1]
+        idx = base[:, None, None] + np.arange(h_k)[None, :, None] * st[2] + np.arange(nb)[None, None, :]
+        skip = np.zeros(g_.size, bool)
+        skip[idx.reshape(-1)] = True
+        assert np.array_equal(g_[~skip], r_[~skip]), f"pool {which}"
+        assert not np.array_equal(g_[skip], i_[skip]), f"pool {which}: rows outside the sample were not written"
