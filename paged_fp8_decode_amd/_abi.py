@@ -6,7 +6,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmj.so")
+# PAGED_FP8_DECODE_LIB names another build of the same library (the
+# host-sanitizer build the CPU tests load); unset, the in-tree libmj.so
+LIB_PATH = os.environ.get("PAGED_FP8_DECODE_LIB") or os.path.join(_HERE, "libmj.so")
 
 ABI_VERSION = 9  # MJ_ABI_VERSION of include/mj.h this binding matches
 MJ_OK, MJ_EINVAL, MJ_EUNSUPPORTED, MJ_EALIGN, MJ_ECAPACITY, MJ_EHIP = 0, -1, -2, -3, -4, -5
