@@ -132,14 +132,18 @@ typedef struct mj_config {
                               plan's KV tiles are whole 16-token tiles and
                               slot strides are < 2^24 bytes, else the generic
                               kernel); 1 always the generic LDS-tiled kernel;
-                              10..25 the matrix-core kernel with tuning bits
+                              10..73 the matrix-core kernel with tuning bits
                               (value - 10): bit 0 two granules of prefetch,
                               bit 1 head-major grid, bit 2 XCD-grouped grid
                               (the KV heads of a work item on one XCD; takes
                               precedence over bit 1), bit 3 four waves per
                               workgroup where the default runs eight (a
                               group of exactly one 32-row tile, e4m3 with
-                              fp8 Q or e2m1)                                 */
+                              fp8 Q or e2m1), bits 4-5 KV heads per
+                              workgroup (0 the library's choice, 1 one, 2
+                              two, 3 four; more than one only for the packed
+                              formats at up to 16 query rows per KV head,
+                              h_k a multiple, no in-kernel merge)            */
   int32_t kv_cache_policy; /* matrix-core kernel KV loads: 0 the library's
                               choice (K cached, V non-temporal), 1 every load
                               cached, 2 every load non-temporal, 3 K cached

@@ -81,13 +81,11 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
 // XCDs of the part: consecutive workgroups of a launch go to them in turn
 constexpr int kXcds = 8;
 // s_waitcnt immediate (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]) that waits for vmcnt 0 only
 constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kGran = 32;
 constexpr float kLazyMax = 8.0f;
 constexpr int kE8m0One = 127;
@@ -787,16 +785,25 @@ __device__ __forceinline__ void granule_any(const Ctx& c, const QOps<FMT, NRB>& 
 // non-temporal.
 // W: waves per workgroup (4, or 8 for a 32-row tile that runs alone on its
 // CU: two waves per SIMD without cutting the item into more splits).
-template <int FMT, int NQB, int NRB, int CP, int PF, int OCC, int W>
+// HG: KV heads per workgroup (1; 2 or 4 for token-major pages of packed
+// rows): head h of the group gets waves [h W / HG, (h + 1) W / HG), which
+// share its granules as the W waves of a one-head workgroup do.  The heads'
+// rows of one token are adjacent in such pages and fill whole 128-byte
+// lines together (4 x 96 bytes, 2 x 64), so that each line is fetched once,
+// by one CU, instead of once for each of the heads whose rows it holds.
+template <int FMT, int NQB, int NRB, int CP, int PF, int OCC, int W, int HG = 1>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_mfma_kernel(DecodeParams p) {
   constexpr int kWaves = W;
   constexpr int kThreads = 64 * W;
+  constexpr int kWph = W / HG;     // waves per KV head
+  constexpr int kTh = 64 * kWph;   // threads per KV head
+  static_assert(W % HG == 0 && (HG == 1 || NRB == 1), "head groups: whole waves per head, one row block");
   using F = Fmt<FMT>;
   constexpr int kRows = NQB * NRB;  // rows of the GQA group this instance serves (padded)
   __shared__ float o_s[kWaves][kRows][kHeadDim];
   __shared__ float m_s[kWaves][kRows], l_s[kWaves][kRows], f_s[kWaves][kRows];
-  __shared__ __align__(16) uint8_t q_s[kRows][kHeadDim];  // fused step: this item's e4m3 Q rows
+  __shared__ __align__(16) uint8_t q_s[HG][kRows][kHeadDim];  // fused step: this item's e4m3 Q rows per head
   __shared__ float red_s[kWaves];
   __shared__ int last_s;
 
@@ -807,9 +814,9 @@ void decode_mfma_kernel(DecodeParams p) {
   int w, hc;
   if (p.head_major == 2) {
     // XCD-grouped: workgroup L runs on XCD L % 8; the heads of item w are
-    // L = (w / 8) * 8 H + 8 hc + w % 8 (H = h_k * row_tiles), one XCD,
+    // L = (w / 8) * 8 H + 8 hc + w % 8 (H = h_k / HG * row_tiles), one XCD,
     // dispatched close together
-    const int L = blockIdx.x, per = kXcds * p.h_k * p.row_tiles;
+    const int L = blockIdx.x, per = kXcds * (p.h_k / HG) * p.row_tiles;
     const int chunk = L / per, r = L - chunk * per;
     hc = r / kXcds;
     w = chunk * kXcds + (r - hc * kXcds);
@@ -828,6 +835,10 @@ void decode_mfma_kernel(DecodeParams p) {
   const int nq = min(kRows, p.n_q - row0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // head groups: this wave's KV head (wave-uniform) and its index in the group
+  const int hw = HG > 1 ? wave / kWph : 0;
+  const int hc0 = g;  // the group's (first) head index, over HG
+  g = g * HG + hw;
   const int n = lane & 15, jj = lane >> 4;
   int seq, tb, te;
   bool single;
@@ -900,7 +911,8 @@ void decode_mfma_kernel(DecodeParams p) {
   // fused step: fetch this thread's Q words first, then issue the ring's
   // first granules, so that the quantization below (two barriers) waits only
   // on the Q loads (loads retire in issue order) while the KV loads fly
-  constexpr int kQV = (kRows * 16 + kThreads - 1) / kThreads;  // 8-channel vectors per thread
+  constexpr int kQV = (kRows * 16 + kTh - 1) / kTh;  // 8-channel vectors per thread (of its head)
+  const int th = threadIdx.x % kTh;                  // thread index among its head's
   const int nvec = nq * 16;
   QRaw8 qr[kQV];
   // unfused: the pre-quantized rows' words, fetched before the KV loads too
@@ -931,7 +943,7 @@ void decode_mfma_kernel(DecodeParams p) {
   if (!F::kQBf16 && p.qb) {
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
-      const int v = min((int)threadIdx.x + k * kThreads, nvec - 1);  // a repeat changes no max
+      const int v = min(th + k * kTh, nvec - 1);  // a repeat changes no max
       qr[k] = q_fetch8(p.qb, p.qb_ts, p.qb_hs, p.q_mul, p.q_len, p.h_r, seq, g, row0 + (v >> 4), (v & 15) * 8);
     }
   }
@@ -939,13 +951,13 @@ void decode_mfma_kernel(DecodeParams p) {
   // the ring's first granules, issued unconditionally (a wave with no
   // granule loads a dead tile, i.e. zeros) so that the wait counts stay static
   const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
-  int gi = wave;
+  int gi = wave % kWph;
   const bool run = gi < ngr;
   KRows<FMT> K0 = load_k<FMT, (CP & 1) != 0>(c, gi), K1;
   VRows<FMT> V0 = load_v<FMT, (CP & 2) != 0>(c, gi, K0.pg), V1;
   if constexpr (PF == 2) {
-    K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWaves);
-    V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves, K1.pg);
+    K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWph);
+    V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWph, K1.pg);
   }
 
   float qdesc = 1.0f;  // bf16-Q mode: no Q scale
@@ -961,7 +973,7 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
     }
-    if constexpr (kRows == 32) {
+    if constexpr (kRows == 32 && HG == 1) {
       // row tiles: the scale covers every row of the pair, so the rows of
       // the other tiles enter the maximum too (loaded after the ring's first
       // granules, which they then wait for; once per workgroup)
@@ -981,15 +993,15 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if (lane == 0) red_s[wave] = amax;
     __syncthreads();
-    amax = red_s[0];
+    amax = red_s[hw * kWph];
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) amax = fmaxf(amax, red_s[i]);
+    for (int i = 1; i < kWph; ++i) amax = fmaxf(amax, red_s[hw * kWph + i]);
     qdesc = q_scale_from_amax(amax);
     const float rq = 1.0f / qdesc;
 #pragma unroll
     for (int k = 0; k < kQV; ++k) {
-      const int v = threadIdx.x + k * kThreads;
-      if (v < nvec) *reinterpret_cast<uint2*>(&q_s[v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc, rq);
+      const int v = th + k * kTh;
+      if (v < nvec) *reinterpret_cast<uint2*>(&q_s[hw][v >> 4][(v & 15) * 8]) = q_codes8(x[k], qdesc, rq);
     }
     __syncthreads();
   } else if (!F::kQBf16) {
@@ -1017,8 +1029,8 @@ void decode_mfma_kernel(DecodeParams p) {
     } else if (r < nq) {
       u32x4 a, b;
       if (p.qb) {  // LDS reads of the codes quantized above
-        a = *reinterpret_cast<const u32x4*>(&q_s[r][q_half_offset<FMT>(jj, 0)]);
-        b = *reinterpret_cast<const u32x4*>(&q_s[r][q_half_offset<FMT>(jj, 1)]);
+        a = *reinterpret_cast<const u32x4*>(&q_s[hw][r][q_half_offset<FMT>(jj, 0)]);
+        b = *reinterpret_cast<const u32x4*>(&q_s[hw][r][q_half_offset<FMT>(jj, 1)]);
       } else {
         a = qg[R][0];
         b = qg[R][1];
@@ -1098,38 +1110,38 @@ void decode_mfma_kernel(DecodeParams p) {
     // register ring of PF + 1 granules, rotated by unrolling
     if constexpr (PF == 1) {
       while (true) {
-        K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWaves);
-        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves, K1.pg);
+        K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWph);
+        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWph, K1.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K0, V0, st);
-        gi += kWaves;
+        gi += kWph;
         if (gi >= ngr) break;
-        K0 = load_k<FMT, (CP & 1) != 0>(c, gi + kWaves);
-        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + kWaves, K0.pg);
+        K0 = load_k<FMT, (CP & 1) != 0>(c, gi + kWph);
+        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + kWph, K0.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K1, V1, st);
-        gi += kWaves;
+        gi += kWph;
         if (gi >= ngr) break;
       }
     } else {
       while (true) {
-        KRows<FMT> K2 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWaves);
-        VRows<FMT> V2 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves, K2.pg);
+        KRows<FMT> K2 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWph);
+        VRows<FMT> V2 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWph, K2.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K0, V0, st);
-        gi += kWaves;
+        gi += kWph;
         if (gi >= ngr) break;
-        K0 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWaves);
-        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves, K0.pg);
+        K0 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWph);
+        V0 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWph, K0.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K1, V1, st);
-        gi += kWaves;
+        gi += kWph;
         if (gi >= ngr) break;
-        K1 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWaves);
-        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWaves, K1.pg);
+        K1 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWph);
+        V1 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWph, K1.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K2, V2, st);
-        gi += kWaves;
+        gi += kWph;
         if (gi >= ngr) break;
       }
     }
@@ -1154,35 +1166,37 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // per row (thread r): the four waves' weights 2^(m_w - M), divided by the
-  // row sum when the item is the sequence's only one; the row's LSE, or its
-  // split partial's max and sum
-  const float vd = load_descale(p.vd, p.vd_kind, seq, g, p.h_k);
-  if (threadIdx.x < kRows) {
-    const int r = threadIdx.x;
+  const float vd = HG == 1 ? load_descale(p.vd, p.vd_kind, seq, g, p.h_k) : 0.0f;
+  // per row (thread r of head hr of the group): the weights 2^(m_w - M) of
+  // the head's waves, divided by the row sum when the item is the
+  // sequence's only one; the row's LSE, or its split partial's max and sum
+  if (threadIdx.x < kRows * HG) {
+    const int hr = threadIdx.x / kRows, r = threadIdx.x - hr * kRows;
+    const int w0 = hr * kWph;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, m_s[ww][r]);
+    for (int ww = 0; ww < kWph; ++ww) M = fmaxf(M, m_s[w0 + ww][r]);
     const float Ms = M == -INFINITY ? 0.0f : M;
-    float wt[kWaves], Lsum = 0.0f;
+    float wt[kWph], Lsum = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      wt[ww] = exp2f(m_s[ww][r] - Ms);
-      Lsum += wt[ww] * l_s[ww][r];
+    for (int ww = 0; ww < kWph; ++ww) {
+      wt[ww] = exp2f(m_s[w0 + ww][r] - Ms);
+      Lsum += wt[ww] * l_s[w0 + ww][r];
     }
     const float f = single ? (Lsum > 0.0f ? 1.0f / Lsum : 0.0f) : 1.0f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) f_s[ww][r] = wt[ww] * f;
+    for (int ww = 0; ww < kWph; ++ww) f_s[w0 + ww][r] = wt[ww] * f;
     if (r < nq) {
+      const int gr = hc0 * HG + hr;  // the row's KV head
       const int rg = row0 + r;
       const int t = rg / p.h_r;
-      const int h = g * p.h_r + (rg - t * p.h_r);
+      const int h = gr * p.h_r + (rg - t * p.h_r);
       if (single) {
         if (p.lse)
           p.lse[((int64_t)seq * p.q_len + t) * p.h_q + h] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
       } else if (w < p.part_items) {
         // written through to device-coherent memory, for a merge on any XCD
-        const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + rg;
+        const int64_t idx = ((int64_t)w * p.h_k + gr) * p.nqp + rg;
         store_coherent(&p.m_part[idx], Lsum > 0.0f ? M : -INFINITY);
         store_coherent(&p.l_part[idx], Lsum);
       }
@@ -1190,25 +1204,29 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // combine the waves: thread -> channel ch of rows tid / 128 + (W / 2) k,
-  // every row's LDS reads issued together (a compile-time row count)
+  // combine the waves: thread -> channel ch of rows tid / 128 + (W / 2) k
+  // (rows of head r / kRows of the group), every row's LDS reads issued
+  // together (a compile-time row count)
   const int ch = threadIdx.x & 127;
   constexpr int kRowStep = kThreads / 128;
 #pragma unroll
-  for (int k = 0; k < (kRows + kRowStep - 1) / kRowStep; ++k) {
-    const int r = (threadIdx.x >> 7) + kRowStep * k;
-    if (r < nq) {
+  for (int k = 0; k < (kRows * HG + kRowStep - 1) / kRowStep; ++k) {
+    const int rr = (threadIdx.x >> 7) + kRowStep * k;
+    const int hr = HG == 1 ? 0 : rr / kRows, r = rr - hr * kRows;
+    if (hr < HG && r < nq) {
       float O = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) O += f_s[ww][r] * o_s[ww][r][ch];
-      const int rg = row0 + r;  // row of the group
+      for (int ww = 0; ww < kWph; ++ww) O += f_s[hr * kWph + ww][r] * o_s[hr * kWph + ww][r][ch];
+      const int gr = hc0 * HG + hr;  // the row's KV head
+      const int rg = row0 + r;       // row of the group
       const int t = rg / p.h_r;
-      const int h = g * p.h_r + (rg - t * p.h_r);
-      const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vd;
+      const int h = gr * p.h_r + (rg - t * p.h_r);
+      const float vdr = HG == 1 ? vd : load_descale(p.vd, p.vd_kind, seq, gr, p.h_k);
+      const float om = (p.o_mul ? p.o_mul[(int64_t)h * kHeadDim + ch] : 1.0f) * vdr;
       if (single) {
         store_out(p.out, p.out_f32, ((int64_t)seq * p.q_len + t) * p.out_ts + (int64_t)h * p.out_hs + ch, O * om);
       } else if (w < p.part_items) {
-        const int64_t idx = ((int64_t)w * p.h_k + g) * p.nqp + rg;
+        const int64_t idx = ((int64_t)w * p.h_k + gr) * p.nqp + rg;
         store_coherent(&p.o_part[idx * kHeadDim + ch], O * om);
       }
     }
@@ -1223,7 +1241,7 @@ void decode_mfma_kernel(DecodeParams p) {
     p.sb_out[seq] = plan_begin;
   }
 
-  if (!single && p.counters) {
+  if (HG == 1 && !single && p.counters) {
     // fused merge: once every wave's write-through stores have completed
     // (vmcnt 0) and the workgroup has met, the partials are visible to all
     // XCDs; count the arrival, and the last split of the pair merges.  An
@@ -1265,12 +1283,21 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <int FMT, int NQB, int NRB, int PF, int OCC, int W = 4>
+template <int FMT, int NQB, int NRB, int PF, int OCC, int W = 4, int HG = 1>
 hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
   constexpr int kThreads = 64 * W;
-  const int heads = p.h_k * p.row_tiles;
+  const int heads = p.h_k / HG * p.row_tiles;
   const dim3 grid = p.head_major == 2 ? dim3((unsigned)((p.num_work + kXcds - 1) / kXcds * kXcds * heads))
                     : p.head_major ? dim3(heads, p.num_work) : dim3(p.num_work, heads);
+  if constexpr (HG > 1) {
+    // head groups: all KV loads cached (the group's waves share lines
+    // through the vector L1) or V streamed
+    if (cp == 0)
+      hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 0, PF, OCC, W, HG>), grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 2, PF, OCC, W, HG>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+  }
   switch (cp) {
     case 0: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 0, PF, OCC, W>), grid, dim3(kThreads), 0, s, p); break;
     case 1: hipLaunchKernelGGL((decode_mfma_kernel<FMT, NQB, NRB, 1, PF, OCC, W>), grid, dim3(kThreads), 0, s, p); break;
@@ -1280,12 +1307,28 @@ hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Head groups (hg = 2 or 4 KV heads per workgroup, eight waves) for the
+// packed formats at up to 16 rows.
+template <int FMT, int NQB>
+hipError_t launch_groups(const DecodeParams& p, int cp, int hg, hipStream_t s) {
+  if constexpr (Fmt<FMT>::kPacked6 || FMT == 4 || FMT == 5 || FMT == 6) {
+    return hg == 4 ? launch_shape<FMT, NQB, 1, 1, 2, 8, 4>(p, cp, s) : launch_shape<FMT, NQB, 1, 1, 2, 8, 2>(p, cp, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <int FMT>
-hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide32, hipStream_t s) {
+hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide32, int hg, hipStream_t s) {
   const bool pf2 = tune & 2;  // two granules of prefetch instead of one
   // more than 32 rows: tiles of 32 rows (the 32-row instance), each
   // workgroup one tile of one (item, KV head)
   p.row_tiles = (p.n_q + kMfmaTileRows - 1) / kMfmaTileRows;
+  if (hg > 1) {
+    if (p.n_q > 16 || p.h_k % hg || p.counters) return hipErrorInvalidValue;
+    return p.n_q <= 4 ? launch_groups<FMT, 4>(p, nt, hg, s)
+                      : (p.n_q <= 8 ? launch_groups<FMT, 8>(p, nt, hg, s) : launch_groups<FMT, 16>(p, nt, hg, s));
+  }
   if (p.n_q <= 4) return pf2 ? launch_shape<FMT, 4, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 4, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 8) return pf2 ? launch_shape<FMT, 8, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 8, 1, 1, 2>(p, nt, s);
   if (p.n_q <= 16) return pf2 ? launch_shape<FMT, 16, 1, 2, 2>(p, nt, s) : launch_shape<FMT, 16, 1, 1, 2>(p, nt, s);
@@ -1310,9 +1353,12 @@ hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide32, hipStream_
 }  // namespace
 
 // tune bits: 1 = two granules of prefetch, 2 = head-major grid, 4 = XCD-
-// grouped grid (over 2), 8 = four waves (not eight) for a lone 32-row tile;
-// -1 = the default for the format.  cache_policy: -1 = the default for the format,
-// else the CP bits.
+// grouped grid (over 2), 8 = four waves (not eight) for a lone 32-row tile,
+// 16-48 = KV heads per workgroup (0: the library's choice, 16: one, 32: two,
+// 48: four; more than one where it applies: packed formats, up to 16 rows,
+// no in-kernel merge, h_k a multiple); -1 = the default for the format.  cache_policy:
+// -1 = the default for the format, else the CP bits (head groups: 0, or V
+// non-temporal for any other).
 hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache_policy, int tune, hipStream_t s) {
   DecodeParams p = p_in;
   // e2m1 and nvfp4 rows are half the bytes of e4m3 ones: their items are
@@ -1322,7 +1368,29 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
   // that XCD's L2 and head-major pages are read together.  Measured: 131K
   // context, 4 sequences, head-major pages 117 -> 100 us; ragged batch,
   // token-major pages 199 -> 169 us.
-  if (tune < 0) tune = kv_format >= 3 ? 4 : 0;
+  const bool auto_tune = tune < 0;
+  if (auto_tune) tune = kv_format >= 3 ? 4 : 0;
+  // Head groups: packed rows (96 or 64 bytes) of adjacent KV heads in
+  // token-major pages share 128-byte lines; a workgroup of 4 heads (fp6:
+  // 384 bytes, three whole lines; fp4: 256 bytes, two) reads each line once.
+  // Chosen where the grid still gives every CU a workgroup.  Measured on the
+  // ragged batch in token-major pages: e2m3 230 -> 215 us, e2m1 149 -> 136.5,
+  // nvfp4 174 -> 168 (against one head per workgroup with every load
+  // cached); HBM bytes fetched per KV byte 1.95 -> 1.36, 1.20 -> 1.01 and
+  // 1.43 -> 1.11.  Two heads per workgroup were slower than one (192-252 us).
+  const int hsel = (tune >> 4) & 3;
+  int hg = hsel >= 2 ? (hsel == 2 ? 2 : 4) : 1;
+  if (hsel == 0 && kv_format >= 1) {
+    const int64_t row = kv_format <= 2 ? 96 : 64;
+    const int want = 4;
+    const bool adjacent = p.k_sh == row && p.v_sh == row;
+    const bool cp_ok = cache_policy < 0 || cache_policy == 0 || cache_policy == 2;
+    if (adjacent && cp_ok && (int64_t)p.num_work * (p.h_k / want) >= p.num_cus) hg = want;
+  }
+  if (kv_format == 0 || p.n_q > 16 || p.counters || p.h_k % hg) hg = 1;
+  // head groups share no lines across workgroups: the plain grid (measured:
+  // e2m1 143.6 -> 136.5 us, nvfp4 169.5 -> 168.3)
+  if (auto_tune && hg > 1) tune &= ~4;
   p.head_major = (tune & 4) ? 2 : ((tune & 2) ? 1 : 0);
   const int t = (tune & 1) ? 2 : 0;
   const bool wide32 = (tune & 8) == 0;  // eight waves for a lone 32-row tile (bit 3: four)
@@ -1330,14 +1398,15 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
   // two (e4m3) or three (e2m3) load instructions, which the vector L1 then
   // serves after the first; V loads cover whole rows (e4m3) and stream.
   // Measured against all-non-temporal: e2m3 at 131K context 169 -> 144 us,
-  // e4m3 at 32K 657 -> 647 us, ragged batch 225 -> 219 us.
-  const int cp = cache_policy >= 0 ? cache_policy : 2;
+  // e4m3 at 32K 657 -> 647 us, ragged batch 225 -> 219 us.  Head groups
+  // share V lines too: every load cached.
+  const int cp = cache_policy >= 0 ? cache_policy : (hg > 1 ? 0 : 2);
   switch (kv_format) {
-    case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, wide32, s) : launch_fmt<0>(p, cp, t, wide32, s);
-    case 1: return launch_fmt<1>(p, cp, t, wide32, s);
-    case 2: return launch_fmt<3>(p, cp, t, wide32, s);
-    case 3: return launch_fmt<4>(p, cp, t, wide32, s);
-    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, wide32, s) : launch_fmt<5>(p, cp, t, wide32, s);
+    case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, wide32, hg, s) : launch_fmt<0>(p, cp, t, wide32, hg, s);
+    case 1: return launch_fmt<1>(p, cp, t, wide32, hg, s);
+    case 2: return launch_fmt<3>(p, cp, t, wide32, hg, s);
+    case 3: return launch_fmt<4>(p, cp, t, wide32, hg, s);
+    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, wide32, hg, s) : launch_fmt<5>(p, cp, t, wide32, hg, s);
   }
 }
 

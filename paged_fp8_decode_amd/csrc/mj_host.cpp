@@ -72,7 +72,7 @@ mj_status check_config(const mj_config* c) {
   if (c->kv_format < MJ_KV_E4M3 || c->kv_format > MJ_KV_NVFP4) return MJ_EUNSUPPORTED;
   if (c->q_mode != MJ_Q_FP8 && c->q_mode != MJ_Q_BF16) return MJ_EINVAL;
   if (c->out_f32 != 0 && c->out_f32 != 1) return MJ_EINVAL;
-  if (c->decode_kernel < 0 || (c->decode_kernel > 1 && (c->decode_kernel < 10 || c->decode_kernel > 25)))
+  if (c->decode_kernel < 0 || (c->decode_kernel > 1 && (c->decode_kernel < 10 || c->decode_kernel > 73)))
     return MJ_EINVAL;
   if (c->kv_cache_policy < 0 || c->kv_cache_policy > 4 || c->step_merge < 0 || c->step_merge > 2) return MJ_EINVAL;
   // the packed fp6 / fp4 formats take fp8 Q only
@@ -522,6 +522,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->plan_margin = p->plan_max_splits = p->plan_slots = p->plan_split = p->plan_min_chunk = 0;
   p->ns_out = p->sb_out = nullptr;
   p->kernel_variant = cfg->decode_kernel;
+  p->num_cus = d.num_cus;
   p->cache_policy = cfg->kv_cache_policy;
   p->ksb = nv ? static_cast<const uint8_t*>(a->k_block_scale) : nullptr;
   p->vsb = nv ? static_cast<const uint8_t*>(a->v_block_scale) : nullptr;

@@ -57,6 +57,7 @@ struct DecodeParams {
   int page_size, page_shift, kv_tile;
   int causal;
   int num_work;
+  int num_cus;                 // of the config (the matrix-core launch's grid choices)
   // grid: 0 = (num_work, h_k); 1 = (h_k, num_work); 2 = XCD-grouped, one
   // dimension of ceil(num_work / 8) * 8 * h_k workgroups numbered so that
   // the h_k heads of a work item share an XCD (see the matrix-core launch)

@@ -131,6 +131,13 @@ SPECS = {
     "cfg3_nvfp4": Spec("b64_ragged1k-32k_p64_nhd_nvfp4", b=64, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
                        kv_format="nvfp4", scale_kind="tensor", lens_loguniform=(1024, 32768), slots_override=256,
                        seed=1011),
+    # the packed fp6 and fp4 caches at the ragged token-major point
+    "cfg3_e2m3": Spec("b64_ragged1k-32k_p64_nhd_e2m3", b=64, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
+                      kv_format="e2m3", scale_kind="channel", lens_loguniform=(1024, 32768), slots_override=256,
+                      seed=1012),
+    "cfg3_e2m1": Spec("b64_ragged1k-32k_p64_nhd_e2m1", b=64, q_len=1, h_q=32, h_k=8, page_size=64, layout="NHD",
+                      kv_format="e2m1", scale_kind="channel", lens_loguniform=(1024, 32768), slots_override=256,
+                      seed=1013),
 }
 
 # Reduced sizes with the same heads, page size, layout, format and scales: the
@@ -149,6 +156,8 @@ SMALL = {
     "cfg5_e2m1": dict(b=2, lens=(3001, 1290), pool_pages=0),
     "cfg5_nvfp4": dict(b=2, lens=(3001, 1290), pool_pages=0),
     "cfg3_nvfp4": dict(b=6, lens=(), lens_loguniform=(100, 3000), slots_override=24),
+    "cfg3_e2m3": dict(b=6, lens=(), lens_loguniform=(100, 3000), slots_override=24),
+    "cfg3_e2m1": dict(b=6, lens=(), lens_loguniform=(100, 3000), slots_override=24),
 }
 
 

@@ -331,8 +331,8 @@ def test_write_zero_tokens_needs_no_buffers():
 def test_kernel_selection_config_values():
     for kw, status in ((dict(decode_kernel=0), mj.MJ_OK), (dict(decode_kernel=1), mj.MJ_OK),
                        (dict(decode_kernel=2), mj.MJ_EINVAL), (dict(decode_kernel=9), mj.MJ_EINVAL),
-                       (dict(decode_kernel=10), mj.MJ_OK), (dict(decode_kernel=25), mj.MJ_OK),
-                       (dict(decode_kernel=26), mj.MJ_EINVAL), (dict(decode_kernel=-1), mj.MJ_EINVAL),
+                       (dict(decode_kernel=10), mj.MJ_OK), (dict(decode_kernel=25), mj.MJ_OK), (dict(decode_kernel=73), mj.MJ_OK),
+                       (dict(decode_kernel=74), mj.MJ_EINVAL), (dict(decode_kernel=-1), mj.MJ_EINVAL),
                        (dict(kv_cache_policy=4), mj.MJ_OK), (dict(kv_cache_policy=5), mj.MJ_EINVAL),
                        (dict(kv_cache_policy=-1), mj.MJ_EINVAL), (dict(step_merge=2), mj.MJ_OK),
                        (dict(step_merge=3), mj.MJ_EINVAL), (dict(step_merge=-1), mj.MJ_EINVAL)):

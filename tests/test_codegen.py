@@ -27,18 +27,24 @@ SRC = os.path.join(ROOT, "paged_fp8_decode_amd", "csrc", "mj_decode_mfma.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # the instances the default dispatch launches: (operand format, rows per block,
-# row blocks, KV cache policy, prefetch, waves per SIMD, waves per workgroup)
+# row blocks, KV cache policy, prefetch, waves per SIMD, waves per workgroup,
+# KV heads per workgroup)
 DEFAULT = [
-           "Li0ELi4ELi1ELi2ELi1ELi2ELi4E", "Li0ELi8ELi1ELi2ELi1ELi2ELi4E", "Li0ELi16ELi1ELi2ELi1ELi2ELi4E",
-           "Li0ELi16ELi2ELi2ELi1ELi2ELi4E", "Li0ELi16ELi2ELi2ELi1ELi2ELi8E", "Li1ELi4ELi1ELi2ELi1ELi2ELi4E",
-           "Li1ELi8ELi1ELi2ELi1ELi2ELi4E", "Li1ELi16ELi1ELi2ELi1ELi2ELi4E", "Li1ELi16ELi2ELi2ELi1ELi1ELi4E",
-           "Li2ELi4ELi1ELi2ELi1ELi2ELi4E", "Li2ELi8ELi1ELi2ELi1ELi2ELi4E", "Li2ELi16ELi1ELi2ELi1ELi2ELi4E",
-           "Li2ELi16ELi2ELi2ELi1ELi1ELi4E", "Li3ELi4ELi1ELi2ELi1ELi2ELi4E", "Li3ELi8ELi1ELi2ELi1ELi2ELi4E",
-           "Li3ELi16ELi1ELi2ELi1ELi2ELi4E", "Li3ELi16ELi2ELi2ELi1ELi1ELi4E", "Li4ELi4ELi1ELi2ELi1ELi2ELi4E",
-           "Li4ELi8ELi1ELi2ELi1ELi2ELi4E", "Li4ELi16ELi1ELi2ELi1ELi2ELi4E", "Li4ELi16ELi2ELi2ELi1ELi2ELi4E",
-           "Li4ELi16ELi2ELi2ELi1ELi2ELi8E", "Li5ELi4ELi1ELi2ELi1ELi2ELi4E", "Li5ELi8ELi1ELi2ELi1ELi2ELi4E",
-           "Li5ELi16ELi1ELi2ELi1ELi2ELi4E", "Li5ELi16ELi2ELi2ELi1ELi1ELi4E", "Li6ELi4ELi1ELi2ELi1ELi2ELi4E",
-           "Li6ELi8ELi1ELi2ELi1ELi2ELi4E", "Li6ELi16ELi1ELi2ELi1ELi2ELi4E", "Li6ELi16ELi2ELi2ELi1ELi1ELi4E"]
+           "Li0ELi4ELi1ELi2ELi1ELi2ELi4ELi1E", "Li0ELi8ELi1ELi2ELi1ELi2ELi4ELi1E", "Li0ELi16ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li0ELi16ELi2ELi2ELi1ELi2ELi4ELi1E", "Li0ELi16ELi2ELi2ELi1ELi2ELi8ELi1E", "Li1ELi4ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li1ELi8ELi1ELi2ELi1ELi2ELi4ELi1E", "Li1ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li1ELi16ELi2ELi2ELi1ELi1ELi4ELi1E",
+           "Li2ELi4ELi1ELi2ELi1ELi2ELi4ELi1E", "Li2ELi8ELi1ELi2ELi1ELi2ELi4ELi1E", "Li2ELi16ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li2ELi16ELi2ELi2ELi1ELi1ELi4ELi1E", "Li3ELi4ELi1ELi2ELi1ELi2ELi4ELi1E", "Li3ELi8ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li3ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li3ELi16ELi2ELi2ELi1ELi1ELi4ELi1E", "Li4ELi4ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li4ELi8ELi1ELi2ELi1ELi2ELi4ELi1E", "Li4ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li4ELi16ELi2ELi2ELi1ELi2ELi4ELi1E",
+           "Li4ELi16ELi2ELi2ELi1ELi2ELi8ELi1E", "Li5ELi4ELi1ELi2ELi1ELi2ELi4ELi1E", "Li5ELi8ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li5ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li5ELi16ELi2ELi2ELi1ELi1ELi4ELi1E", "Li6ELi4ELi1ELi2ELi1ELi2ELi4ELi1E",
+           "Li6ELi8ELi1ELi2ELi1ELi2ELi4ELi1E", "Li6ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li6ELi16ELi2ELi2ELi1ELi1ELi4ELi1E",
+           "Li1ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li1ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li1ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
+           "Li3ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li3ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li3ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
+           "Li4ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li4ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li4ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
+           "Li5ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li5ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li5ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
+           "Li6ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li6ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li6ELi16ELi1ELi0ELi1ELi2ELi8ELi4E"]
 
 
 @pytest.fixture(scope="module")

@@ -159,7 +159,7 @@ def test_fused_quantization_ties(mj, gpu, key):
 
 
 @pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
-                                 "cfg3_nvfp4"])
+                                 "cfg3_nvfp4", "cfg3_e2m3", "cfg3_e2m1"])
 def test_gather_probe_bit_exact(mj, gpu, key):
     from oracle.attention import gather_codes
     from paged_fp8_decode_amd.runner import DecodeStep
@@ -193,10 +193,13 @@ def test_gather_probe_bit_exact(mj, gpu, key):
 
 
 SMALL_KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4",
-              "32k", "32k_b16"]
+              "cfg3_e2m3", "cfg3_e2m1", "32k", "32k_b16"]
 # mj_config.decode_kernel: 0 = automatic choice, 1 = generic LDS kernel, 18 =
-# the matrix-core kernel with four waves where the default runs eight
-VARIANTS = [0, 1, 18]
+# the matrix-core kernel with four waves where the default runs eight, 58 =
+# four KV heads per workgroup and 46 = two on the XCD-grouped grid (packed
+# formats; the small workloads have too few items for the automatic choice
+# to take head groups)
+VARIANTS = [0, 1, 18, 58, 46]
 
 
 @pytest.fixture
@@ -219,7 +222,7 @@ def test_parity_small_all_outputs(mj, gpu, key, variant):
     compare_lse(lse, LSE, wl.spec.name)
 
 
-@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4"])
+@pytest.mark.parametrize("key", ["cfg2", "cfg4c", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4", "cfg3_e2m3"])
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
 def test_split_and_unsplit_agree(mj, gpu, key, variant):
     wl = synth.build(synth.spec_for(key, small=True), gpu)
@@ -247,8 +250,8 @@ def test_page_permutation_bit_identical(mj, gpu, variant):
     assert torch.equal(lse1, lse2)
 
 
-@pytest.mark.parametrize("variant", [0, 1], indirect=True)
-@pytest.mark.parametrize("key", ["cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4"])
+@pytest.mark.parametrize("variant", [0, 1, 46], indirect=True)
+@pytest.mark.parametrize("key", ["cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4", "cfg3_e2m3"])
 def test_sub_byte_edge_lengths_and_shapes(mj, gpu, key, variant):
     """The fp4 formats at empty, single-token and tile-boundary lengths, and
     in the speculative row shapes (replicated rows, 8, 16, 32 rows; 40 rows as
@@ -342,7 +345,7 @@ def test_graph_replay_after_replanning(mj, gpu):
 
 
 FULL = {"cfg1": 1, "cfg2": 2, "cfg3": 2, "cfg4c": 2, "cfg4n": 2, "cfg5": 2, "cfg5_e3m2": 1, "cfg5_e2m1": 1,
-        "cfg5_nvfp4": 1, "cfg3_nvfp4": 2, "32k": 2, "32k_b16": 2}
+        "cfg5_nvfp4": 1, "cfg3_nvfp4": 2, "cfg3_e2m3": 2, "cfg3_e2m1": 2, "32k": 2, "32k_b16": 2}
 
 
 @pytest.mark.parametrize("key", list(FULL))

@@ -17,7 +17,7 @@ from helpers import compare_lse, compare_out, oracle_step, say
 pytestmark = pytest.mark.gpu
 
 KEYS = ["cfg1", "cfg2", "cfg3", "cfg4c", "cfg4n", "cfg5", "32k", "32k_b16", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
-        "cfg3_nvfp4"]
+        "cfg3_nvfp4", "cfg3_e2m3", "cfg3_e2m1"]
 # bf16 Q is the runner's other mode for the e4m3 and nvfp4 caches (the packed
 # fp6 / fp4 caches take fp8 Q only)
 CASES = [(k, "fp8") for k in KEYS] + [(k, "bf16") for k in KEYS

@@ -34,7 +34,7 @@ def _args(wl):
 
 
 @pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg4c", "cfg4n", "cfg5", "cfg5_e3m2", "cfg5_e2m1", "cfg5_nvfp4",
-                                 "cfg3_nvfp4"])
+                                 "cfg3_nvfp4", "cfg3_e2m3", "cfg3_e2m1"])
 def test_matches_sdpa_per_head(key):
     wl, h = _small(key)
     s = wl.spec
