@@ -379,6 +379,46 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
     return res
 
 
+def measure_launch_floor(steps, warmup, flush):
+    """What launching costs by itself, timed like the steps (events around
+    the launch after the same Infinity Cache eviction): a hipGraph holding
+    one trivial kernel (torch's add on one element), and that kernel
+    launched alone.  A graph step can be no faster than the first."""
+    import torch
+    stream = torch.cuda.current_stream()
+    x = torch.zeros(1, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        x.add_(1)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        x.add_(1)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for _ in range(warmup):
+            flush()
+            fn()
+        for a, b in ev:
+            flush()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]) * 1e3)
+
+    res = dict(one_kernel_graph_us_median=round(timed(gr.replay), 2),
+               one_kernel_eager_us_median=round(timed(lambda: x.add_(1)), 2))
+    log(f"[bench] launch floor after eviction: graph of one trivial kernel {res['one_kernel_graph_us_median']} us, "
+        f"the kernel launched alone {res['one_kernel_eager_us_median']} us")
+    del gr
+    return res
+
+
 def measure_write(kv_format, n_tokens, reps, flush, h_k=8, page_size=64):
     """mj_write_kv of n_tokens new rows (bf16 K and V, h_k heads) into a paged
     cache at scattered slots: time per call (one event pair around reps
@@ -695,6 +735,7 @@ def main():
     KSEL.update(decode_kernel=args.variant, kv_cache_policy=args.cache_policy, step_merge=args.step_merge)
 
     flush = Flusher()
+    floor = measure_launch_floor(max(20, args.steps), max(5, args.warmup), flush)
     main_res = measure(args.workload, args.steps, args.warmup, flush, args.wgs_per_cu, not args.no_stream_read)
     extra = {}
     for k in [x for x in args.extra.split(",") if x]:
@@ -731,6 +772,7 @@ def main():
                        graph_us_per_step_median=round(r["graph_us_per_step_median"], 2),
                        decode_kernel_us=round(r["kernel_us_back_to_back"], 2),
                        kernel_frac_of_hbm_peak=round(r["kernel_frac_of_hbm_peak"], 4),
+                       graph_step_over_kernel_us=round(r["graph_us_per_step_median"] - r["kernel_us_back_to_back"], 2),
                        with_reduction=r["plan"]["with_reduction"])
                for k, r in [(args.workload, main_res)] + list(extra.items())}
     line = dict(
@@ -753,6 +795,7 @@ def main():
         roofline=roof,
         cpu_baseline=cpu,
         configs=configs,
+        launch_floor=floor,
         detail=main_res,
         extra=extra,
         bf16_q=bf16q,

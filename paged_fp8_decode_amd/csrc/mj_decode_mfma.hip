@@ -301,12 +301,14 @@ __device__ __forceinline__ KRows<FMT> load_k(const Ctx& c, int gi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) R.d[k][i] = a[i];
     } else {
+      // packed fp6: the lane's 24 bytes (8-byte aligned) as a 16- and an
+      // 8-byte load
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, c.k_lane, 0, aux);
+      const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rs, c.k_lane, 16, aux);
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, c.k_lane, 8 * i, aux);
-        R.d[k][2 * i] = a[0];
-        R.d[k][2 * i + 1] = a[1];
-      }
+      for (int i = 0; i < 4; ++i) R.d[k][i] = a[i];
+      R.d[k][4] = b[0];
+      R.d[k][5] = b[1];
     }
   }
   return R;
