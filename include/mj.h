@@ -139,7 +139,8 @@ typedef struct mj_config {
                               precedence over bit 1), bit 3 four waves per
                               workgroup where the default runs eight (a
                               group of exactly one 32-row tile, e4m3 with
-                              fp8 Q or e2m1), bits 4-5 KV heads per
+                              fp8 Q or e2m1; two granules of prefetch
+                              always run four), bits 4-5 KV heads per
                               workgroup (0 the library's choice, 1 one, 2
                               two, 3 four; more than one only for the packed
                               formats at up to 16 query rows per KV head,

@@ -1321,7 +1321,7 @@ hipError_t launch_groups(const DecodeParams& p, int cp, int hg, hipStream_t s) {
 }
 
 template <int FMT>
-hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide32, int hg, hipStream_t s) {
+hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide, int hg, hipStream_t s) {
   const bool pf2 = tune & 2;  // two granules of prefetch instead of one
   // more than 32 rows: tiles of 32 rows (the 32-row instance), each
   // workgroup one tile of one (item, KV head)
@@ -1346,7 +1346,7 @@ hipError_t launch_fmt(DecodeParams& p, int nt, int tune, bool wide32, int hg, hi
   // a group of one 32-row tile is planned one workgroup per CU: eight waves
   // (two per SIMD) share its item; row tiles of larger groups keep four waves
   // so that two of their workgroups fit a CU
-  else if (p.row_tiles == 1 && wide32)
+  else if (p.row_tiles == 1 && wide)
     return launch_shape<FMT, 16, 2, 1, 2, 8>(p, nt, s);
   else
     return launch_shape<FMT, 16, 2, 1, 2>(p, nt, s);
@@ -1395,7 +1395,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
   if (auto_tune && hg > 1) tune &= ~4;
   p.head_major = (tune & 4) ? 2 : ((tune & 2) ? 1 : 0);
   const int t = (tune & 1) ? 2 : 0;
-  const bool wide32 = (tune & 8) == 0;  // eight waves for a lone 32-row tile (bit 3: four)
+  const bool wide = (tune & 8) == 0;  // eight waves for a lone 32-row tile (bit 3: four)
   // default: K cached, V non-temporal.  A K tile's row lines are touched by
   // two (e4m3) or three (e2m3) load instructions, which the vector L1 then
   // serves after the first; V loads cover whole rows (e4m3) and stream.
@@ -1404,11 +1404,11 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
   // share V lines too: every load cached.
   const int cp = cache_policy >= 0 ? cache_policy : (hg > 1 ? 0 : 2);
   switch (kv_format) {
-    case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, wide32, hg, s) : launch_fmt<0>(p, cp, t, wide32, hg, s);
-    case 1: return launch_fmt<1>(p, cp, t, wide32, hg, s);
-    case 2: return launch_fmt<3>(p, cp, t, wide32, hg, s);
-    case 3: return launch_fmt<4>(p, cp, t, wide32, hg, s);
-    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, wide32, hg, s) : launch_fmt<5>(p, cp, t, wide32, hg, s);
+    case 0: return p.q_bf16 ? launch_fmt<2>(p, cp, t, wide, hg, s) : launch_fmt<0>(p, cp, t, wide, hg, s);
+    case 1: return launch_fmt<1>(p, cp, t, wide, hg, s);
+    case 2: return launch_fmt<3>(p, cp, t, wide, hg, s);
+    case 3: return launch_fmt<4>(p, cp, t, wide, hg, s);
+    default: return p.q_bf16 ? launch_fmt<6>(p, cp, t, wide, hg, s) : launch_fmt<5>(p, cp, t, wide, hg, s);
   }
 }
 

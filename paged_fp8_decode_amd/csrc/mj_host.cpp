@@ -509,7 +509,12 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
   p->page_shift = ilog2(cfg->page_size);
   p->kv_tile = d.kv_tile;
   p->causal = a->causal ? 1 : 0;
-  p->num_work = a->num_work;
+  // the launch covers the plan's items: at most max_splits per sequence, so
+  // a grid of max_num_seqs * max_splits item slots when that is below the
+  // plan's capacity (small batches of long sequences: 16 workgroups per KV
+  // head instead of 256 for one sequence on 256 CUs); like the capacity it
+  // depends on the config only, so a captured step stays valid
+  p->num_work = (int)std::min<int64_t>(a->num_work, (int64_t)cfg->max_num_seqs * cfg->max_splits);
   p->head_major = 0;
   p->row_tiles = 1;
   p->q_bf16 = qbf ? 1 : 0;
