@@ -60,12 +60,17 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "2a48a770c1f6ea9a",
-    "cfg2": dict(fetch_bytes=269321213, write_bytes=1180002),
-    "32k": dict(fetch_bytes=4297924012, write_bytes=4718987),
-    "cfg5": dict(fetch_bytes=806126851, write_bytes=589835),
-    "cfg5_e2m1": dict(fetch_bytes=538199653, write_bytes=1179668),
-    "cfg5_nvfp4": dict(fetch_bytes=604645464, write_bytes=1179671),
+    "sources_sha256_16": "231d268772cb2b31",
+    "32k": dict(fetch_bytes=4297974081, write_bytes=4325751),
+    "cfg2": dict(fetch_bytes=269359247, write_bytes=1081691),
+    "cfg3": dict(fetch_bytes=1284594265, write_bytes=4183089),
+    "cfg4c": dict(fetch_bytes=270856237, write_bytes=4260014),
+    "cfg5": dict(fetch_bytes=806217331, write_bytes=540683),
+    "cfg5_e2m1": dict(fetch_bytes=538442495, write_bytes=1081368),
+    "cfg5_nvfp4": dict(fetch_bytes=604678857, write_bytes=1081368),
+    "cfg3_e2m3": dict(fetch_bytes=1158887649, write_bytes=4011421),
+    "cfg3_e2m1": dict(fetch_bytes=658094110, write_bytes=4103085),
+    "cfg3_nvfp4": dict(fetch_bytes=784835738, write_bytes=4094701),
 }
 
 
