@@ -107,7 +107,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="32k",
                     help="the headline workload: 64 sequences of 32768 tokens, token-major pages of 64, e4m3 KV")
-    ap.add_argument("--extra", default="cfg1,cfg2,cfg3,cfg4c,cfg4n,cfg5,32k_b16,cfg5_e3m2,cfg5_e2m1,cfg5_nvfp4",
+    ap.add_argument("--extra", default="cfg1,cfg2,cfg3,cfg4c,cfg4n,cfg5,32k_b16,cfg5_e3m2,cfg5_e2m1,cfg5_nvfp4,cfg3_e2m3,cfg3_e2m1,cfg3_nvfp4",
                     help="comma list of extra workloads reported under 'extra' ('' = none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--bf16q", default="cfg2,32k",
