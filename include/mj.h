@@ -153,7 +153,11 @@ typedef struct mj_config {
   int32_t step_merge;      /* where mj_decode_step merges split partials when
                               it fuses the step: 0 automatic (the separate
                               merge launch), 1 in the decode kernel (the last
-                              split item of a (sequence, KV head) to finish),
+                              split item of a (sequence, KV head) to finish;
+                              host-planned steps with at most 32 rows per KV
+                              head, else the merge launch; every split
+                              workgroup then issues an agent-scope release,
+                              which costs more than the launch on gfx950),
                               2 the separate merge launch                    */
 } mj_config;
 /* Defaults of wgs_per_cu / min_chunk_tokens, per q_len (n_q = q_len*h_r):

@@ -250,12 +250,14 @@ def test_page_permutation_bit_identical(mj, gpu, variant):
     assert torch.equal(lse1, lse2)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 46], indirect=True)
+@pytest.mark.parametrize("variant", [0, 1, 46, 58], indirect=True)
 @pytest.mark.parametrize("key", ["cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4", "cfg3_e2m3"])
 def test_sub_byte_edge_lengths_and_shapes(mj, gpu, key, variant):
-    """The fp4 formats at empty, single-token and tile-boundary lengths, and
-    in the speculative row shapes (replicated rows, 8, 16, 32 rows; 40 rows as
-    two 32-row tiles, or on the generic kernel as variant 1)."""
+    """The packed formats at empty, single-token and tile-boundary lengths,
+    and in the speculative row shapes (replicated rows, 8, 16, 32 rows; 40
+    rows as two 32-row tiles, or on the generic kernel as variant 1), with
+    one, two (46) and four (58) KV heads per workgroup where the shape
+    allows it (up to 16 rows, h_k a multiple)."""
     lens = (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, 1000)
     for q_len, h_q, h_k, causal in ((1, 32, 8, True), (2, 16, 8, True), (4, 8, 8, True), (2, 4, 2, False),
                                     (2, 32, 8, True), (4, 32, 8, True), (3, 40, 8, True), (5, 64, 8, True)):
