@@ -251,7 +251,7 @@ def test_page_permutation_bit_identical(mj, gpu, variant):
 
 
 @pytest.mark.parametrize("variant", [0, 1, 46, 58], indirect=True)
-@pytest.mark.parametrize("key", ["cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4", "cfg3_e2m3"])
+@pytest.mark.parametrize("key", ["cfg5_e2m1", "cfg5_nvfp4", "cfg3_nvfp4", "cfg3_e2m3", "cfg3_e2m1"])
 def test_sub_byte_edge_lengths_and_shapes(mj, gpu, key, variant):
     """The packed formats at empty, single-token and tile-boundary lengths,
     and in the speculative row shapes (replicated rows, 8, 16, 32 rows; 40
