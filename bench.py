@@ -60,17 +60,17 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "231d268772cb2b31",
-    "32k": dict(fetch_bytes=4297974081, write_bytes=4325751),
-    "cfg2": dict(fetch_bytes=269359247, write_bytes=1081691),
-    "cfg3": dict(fetch_bytes=1284594265, write_bytes=4183089),
-    "cfg4c": dict(fetch_bytes=270856237, write_bytes=4260014),
-    "cfg5": dict(fetch_bytes=806217331, write_bytes=540683),
-    "cfg5_e2m1": dict(fetch_bytes=538442495, write_bytes=1081368),
-    "cfg5_nvfp4": dict(fetch_bytes=604678857, write_bytes=1081368),
-    "cfg3_e2m3": dict(fetch_bytes=1158887649, write_bytes=4011421),
-    "cfg3_e2m1": dict(fetch_bytes=658094110, write_bytes=4103085),
-    "cfg3_nvfp4": dict(fetch_bytes=784835738, write_bytes=4094701),
+    "sources_sha256_16": "c8240530deadf256",
+    "32k": dict(fetch_bytes=4297995464, write_bytes=4325676),
+    "cfg2": dict(fetch_bytes=269360985, write_bytes=1081620),
+    "cfg3": dict(fetch_bytes=1284624024, write_bytes=4182780),
+    "cfg4c": dict(fetch_bytes=270888223, write_bytes=4259977),
+    "cfg5": dict(fetch_bytes=806206338, write_bytes=540681),
+    "cfg5_e2m1": dict(fetch_bytes=538434012, write_bytes=1081363),
+    "cfg5_nvfp4": dict(fetch_bytes=604671791, write_bytes=1081362),
+    "cfg3_e2m3": dict(fetch_bytes=1158248455, write_bytes=4011172),
+    "cfg3_e2m1": dict(fetch_bytes=657845728, write_bytes=4102795),
+    "cfg3_nvfp4": dict(fetch_bytes=784736756, write_bytes=4094412),
 }
 
 
@@ -308,22 +308,26 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
     for i in range(len(pools)):
         launch(i)
     torch.cuda.synchronize()
-    k0, k1 = E(), E()
-    k0.record(stream)
-    for i in range(reps):
-        launch(i)
-    k1.record(stream)
-    merge_us = 0.0
-    if info.with_reduction:
-        m0, m1 = E(), E()
-        m0.record(stream)
+    # three series of each, medians: one stalled series (seen under the
+    # profiler: a merge series at 5x its usual time) moves nothing
+    step_series, merge_series = [], []
+    for _ in range(3):
+        k0, k1 = E(), E()
+        k0.record(stream)
         for i in range(reps):
-            step2.merge(out, lse, info, stream)
-        m1.record(stream)
-    torch.cuda.synchronize()
-    if info.with_reduction:
-        merge_us = m0.elapsed_time(m1) * 1e3 / reps
-    step_us_b2b = k0.elapsed_time(k1) * 1e3 / reps
+            launch(i)
+        k1.record(stream)
+        if info.with_reduction:
+            m0, m1 = E(), E()
+            m0.record(stream)
+            for i in range(reps):
+                step2.merge(out, lse, info, stream)
+            m1.record(stream)
+        torch.cuda.synchronize()
+        step_series.append(k0.elapsed_time(k1) * 1e3 / reps)
+        merge_series.append(m0.elapsed_time(m1) * 1e3 / reps if info.with_reduction else 0.0)
+    merge_us = float(np.median(merge_series))
+    step_us_b2b = float(np.median(step_series))
     kernel_us = step_us_b2b - merge_us
     del pools
 
@@ -344,6 +348,7 @@ def measure(key, steps, warmup, flush, wgs_per_cu=0, stream_read=False, q_mode="
         graph_us_per_step_median_after_write=float(np.median(graph_dirty_ms) * 1e3),
         step_kv_gbs=kvb / (step_ms.mean() * 1e-3) / 1e9,
         kernel_us_back_to_back=kernel_us, step_us_back_to_back=step_us_b2b, merge_us_back_to_back=merge_us,
+        back_to_back_series_us=dict(step=[round(x, 2) for x in step_series], merge=[round(x, 2) for x in merge_series]),
         kernel_launches=reps, kv_pool_copies=n_copies,
         kernel_kv_gbs=kvb / (kernel_us * 1e-6) / 1e9,
         plan=dict(num_work=info.num_work, slots=info.slots, chunk_tiles=info.chunk_tiles,
