@@ -37,13 +37,40 @@ struct Raw16 {
   uint4 a, b;
 };
 
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+
+// The encoders are gfx950's converters at unit scale on the correctly
+// rounded quotient: round to nearest, ties to even, the sign kept (a
+// negative value that rounds to zero gives the negative zero code), e2m3,
+// e3m2 and e2m1 saturating at their largest magnitude (all measured against
+// the format tables at every grid point, midpoint and its neighbours).  The
+// fp8 converter turns values past 448 into the NaN code instead, so e4m3
+// inputs are clamped to +-448 first.
+// e4m3 codes of a and b in the low and high byte of the low half-word
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  const float lo = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f), hi = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  v2s r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, lo, hi, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r) & 0xFFFFu;
+}
+// e2m1 codes of v[0..7], code k in bits [4k, 4k + 4)
+__device__ __forceinline__ uint32_t e2m1_word(const float* v) {
+  uint32_t r = 0u;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
+  return r;
+}
+
 // dst_bs (nvfp4 only): the row's block-scale byte of these 16 channels
 template <int FMT>
 __device__ __forceinline__ void write_side(const Raw16& in, const float (&sc)[16], const float (&rc)[16], int c0,
                                            uint8_t* dst_row, uint8_t* dst_bs) {
   const uint4 a = in.a, b = in.b;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t code[16];
   float q[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -56,44 +83,44 @@ __device__ __forceinline__ void write_side(const Raw16& in, const float (&sc)[16
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(q[i]));
-    const uint32_t sc8 = e4m3_rne(div_rn(amax, 6.0f, 1.0f / 6.0f));
+    const uint32_t sc8 = e4m3_pair(div_rn(amax, 6.0f, 1.0f / 6.0f), 0.0f) & 0xFFu;
     const float sv = e4m3_value(sc8);
     const float rv = 1.0f / sv;  // correctly rounded; unused when sv == 0
+    float y[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) code[i] = sv > 0.0f ? e2m1_rne(div_rn(q[i], sv, rv)) : 0u;
-    *dst_bs = (uint8_t)sc8;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      code[i] = FMT == 0 ? e4m3_rne(q[i]) : FMT == 1 ? e2m3_rne(q[i]) : FMT == 2 ? e3m2_rne(q[i]) : e2m1_rne(q[i]);
-  }
-  if constexpr (FMT == 0) {
-    uint4 o;
-    o.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    o.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-    o.z = code[8] | (code[9] << 8) | (code[10] << 16) | (code[11] << 24);
-    o.w = code[12] | (code[13] << 8) | (code[14] << 16) | (code[15] << 24);
-    *reinterpret_cast<uint4*>(dst_row + c0) = o;
-  } else if constexpr (FMT >= 3) {
-    uint2 o = {0u, 0u};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      o.x |= code[k] << (4 * k);
-      o.y |= code[k + 8] << (4 * k);
-    }
+    for (int i = 0; i < 16; ++i) y[i] = div_rn(q[i], sv, rv);
+    uint2 o = {e2m1_word(y), e2m1_word(y + 8)};
+    if (!(sv > 0.0f)) o = make_uint2(0u, 0u);
     *reinterpret_cast<uint2*>(dst_row + (c0 / 16) * 8) = o;
+    *dst_bs = (uint8_t)sc8;
+  } else if constexpr (FMT == 0) {
+    uint4 o;
+    o.x = e4m3_pair(q[0], q[1]) | (e4m3_pair(q[2], q[3]) << 16);
+    o.y = e4m3_pair(q[4], q[5]) | (e4m3_pair(q[6], q[7]) << 16);
+    o.z = e4m3_pair(q[8], q[9]) | (e4m3_pair(q[10], q[11]) << 16);
+    o.w = e4m3_pair(q[12], q[13]) | (e4m3_pair(q[14], q[15]) << 16);
+    *reinterpret_cast<uint4*>(dst_row + c0) = o;
+  } else if constexpr (FMT == 3) {
+    *reinterpret_cast<uint2*>(dst_row + (c0 / 16) * 8) = make_uint2(e2m1_word(q), e2m1_word(q + 8));
   } else {
-    uint32_t o[3] = {0u, 0u, 0u};
+    // e2m3 / e3m2: the converter's output slot 2i takes element i of its
+    // first operand, slot 2i + 1 element i of its second (measured), so the
+    // even channels go first and the odd second; its upper 16 slots are
+    // unused here
+    v16f ev, od;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int bit = 6 * k;
-      o[bit >> 5] |= code[k] << (bit & 31);
-      if ((bit & 31) > 26) o[(bit >> 5) + 1] |= code[k] >> (32 - (bit & 31));
+    for (int i = 0; i < 8; ++i) {
+      ev[i] = q[2 * i];
+      od[i] = q[2 * i + 1];
+      ev[8 + i] = 0.0f;
+      od[8 + i] = 0.0f;
     }
+    const v6i pk = FMT == 1 ? __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f)
+                            : __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
     uint32_t* d = reinterpret_cast<uint32_t*>(dst_row + (c0 / 16) * 12);
-    d[0] = o[0];
-    d[1] = o[1];
-    d[2] = o[2];
+    d[0] = (uint32_t)pk[0];
+    d[1] = (uint32_t)pk[1];
+    d[2] = (uint32_t)pk[2];
   }
 }
 
