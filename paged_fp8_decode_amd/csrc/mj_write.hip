@@ -19,7 +19,7 @@
 // page s / page_size, row s % page_size; a negative slot (padding) or one
 // past the pool is skipped.
 //
-// One thread per (KV head, 16 channels) of 1-4 tokens: 32 bytes of bf16 in
+// One thread per (KV head, 16 channels) of 1 or 2 tokens: 32 bytes of bf16 in
 // per side and token, 16 bytes (e4m3), 12 bytes (fp6) or 8 bytes (fp4;
 // nvfp4 also the block's scale byte) of codes out.  The
 // write touches every byte once.
@@ -211,20 +211,17 @@ hipError_t launch_tpt(const WriteParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_write_kv(const WriteParams& p_in, hipStream_t s) {
-  // per-channel scales: a few tokens per thread amortize the sixteen
+  // per-channel scales: two tokens per thread amortize the sixteen
   // reciprocals per side once the grid is large (measured at 16K tokens x 8
-  // heads: e2m3 34.2 us at one token per thread, 29.8 us at four); per-tensor
-  // or per-head scales (one reciprocal) and small writes (a decode step's new
-  // rows) take one token per thread (e4m3 29.1 -> 26.9 us, nvfp4 36.3 -> 30.4)
+  // heads with the hardware encoders: e2m3 24.3 us at one or four tokens per
+  // thread, 22.1 at two; e2m1 unchanged); per-tensor or per-head scales (one
+  // reciprocal) and small writes (a decode step's new rows) take one token
+  // per thread
   WriteParams p = p_in;
   const int64_t rows = (int64_t)p.num_tokens * p.h_k;
   const bool channel = p.ks_kind == 3 || p.vs_kind == 3;
-  p.tokens_per_thread = !channel ? 1 : (rows >= (1 << 17) ? 4 : (rows >= (1 << 14) ? 2 : 1));
-  switch (p.tokens_per_thread) {
-    case 4: return launch_tpt<4>(p, s);
-    case 2: return launch_tpt<2>(p, s);
-    default: return launch_tpt<1>(p, s);
-  }
+  p.tokens_per_thread = channel && rows >= (1 << 14) ? 2 : 1;
+  return p.tokens_per_thread == 2 ? launch_tpt<2>(p, s) : launch_tpt<1>(p, s);
 }
 
 }  // namespace mj
