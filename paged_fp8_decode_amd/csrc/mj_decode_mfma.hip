@@ -213,6 +213,24 @@ __device__ __forceinline__ float max_jj(float x, float inf) {
 // loads in flight instead of draining every load.
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Head groups on token-major pages: one 128-byte line holds parts of
+// neighbouring heads' rows (e2m3's 96-byte rows straddle lines, e2m1 packs two
+// heads per line), read by different waves.  Left alone the waves drift apart
+// over a long item and a line leaves the L2 between its two readers (cfg3's
+// shape in e2m3 fetched 1.35 times its KV bytes).  A workgroup barrier before
+// every P-th granule keeps them within P granules of each other (e2m3 1.02
+// times).  It is taken only among a wave's first `end` granules, which every
+// wave of the workgroup has, so that every wave passes the same barriers;
+// global loads stay in flight across it.  P = 0: none.
+template <int P>
+__device__ __forceinline__ void group_lockstep(int& it, int end) {
+  if constexpr (P > 0) {
+    static_assert((P & (P - 1)) == 0, "power of two");
+    if (it < end && (it & (P - 1)) == 0) __builtin_amdgcn_s_barrier();
+    ++it;
+  }
+}
+
 // 2^x with the hardware instruction alone: arguments are <= 0 (a logit
 // minus a running max at least as large) or -inf, and results below the
 // smallest normal flush to 0, which no sum of probabilities can see.
@@ -952,6 +970,13 @@ void decode_mfma_kernel(DecodeParams p) {
   const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
   int gi = wave % kWph;
   const bool run = gi < ngr;
+  // lockstep period per format (cfg3's shape, kernel GB/s against none:
+  // e2m3 every 4 granules +4.7 %, e2m1 every 2 +6.9 %; nvfp4, whose shared
+  // lines are its block-scale rows across the two groups of an item, gained
+  // nothing at any period)
+  constexpr int kLock = HG == 1 || F::kBlockScaled ? 0 : (F::kPacked6 ? 4 : 2);
+  const int lock_end = ngr / kWph;
+  int lock_it = 0;
   KRows<FMT> K0 = load_k<FMT, (CP & 1) != 0>(c, gi), K1;
   VRows<FMT> V0 = load_v<FMT, (CP & 2) != 0>(c, gi, K0.pg), V1;
   if constexpr (PF == 2) {
@@ -1109,12 +1134,14 @@ void decode_mfma_kernel(DecodeParams p) {
     // register ring of PF + 1 granules, rotated by unrolling
     if constexpr (PF == 1) {
       while (true) {
+        group_lockstep<kLock>(lock_it, lock_end);
         K1 = load_k<FMT, (CP & 1) != 0>(c, gi + kWph);
         V1 = load_v<FMT, (CP & 2) != 0>(c, gi + kWph, K1.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K0, V0, st);
         gi += kWph;
         if (gi >= ngr) break;
+        group_lockstep<kLock>(lock_it, lock_end);
         K0 = load_k<FMT, (CP & 1) != 0>(c, gi + kWph);
         V0 = load_v<FMT, (CP & 2) != 0>(c, gi + kWph, K0.pg);
         issue_fence();
@@ -1124,18 +1151,21 @@ void decode_mfma_kernel(DecodeParams p) {
       }
     } else {
       while (true) {
+        group_lockstep<kLock>(lock_it, lock_end);
         KRows<FMT> K2 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWph);
         VRows<FMT> V2 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWph, K2.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K0, V0, st);
         gi += kWph;
         if (gi >= ngr) break;
+        group_lockstep<kLock>(lock_it, lock_end);
         K0 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWph);
         V0 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWph, K0.pg);
         issue_fence();
         granule_any<FMT, NQB, NRB, PF>(c, qo, row_tok, gi, K1, V1, st);
         gi += kWph;
         if (gi >= ngr) break;
+        group_lockstep<kLock>(lock_it, lock_end);
         K1 = load_k<FMT, (CP & 1) != 0>(c, gi + 2 * kWph);
         V1 = load_v<FMT, (CP & 2) != 0>(c, gi + 2 * kWph, K1.pg);
         issue_fence();

@@ -10,6 +10,10 @@ of percent while every numeric test still passed:
   means the loop drains every load each granule -- seen when a pending load
   of uncertain provenance reached the loop, and when block-table reads
   turned into vector loads);
+* head-group instances of the packed formats (e2m3, e3m2, e2m1) keep their
+  waves together with one workgroup barrier in the main loop, and no wait on
+  memory precedes it (a wait there would drain the granule loads in flight);
+  nvfp4 instances have none;
 * no scaled MFMA has its E8M0 scale register rewritten within the next 24
   instructions: the instruction still reads it after issue and the compiler
   does not wait for that (a register-only probe whose scale register was
@@ -99,6 +103,19 @@ def test_main_loop_keeps_loads_in_flight(asm, inst):
                 any("buffer_load" in x for x in body[j:j + 300]))
     waits = [int(re.search(r"vmcnt\((\d+)\)", x).group(1)) for x in body[loop:loop + 1500] if "vmcnt(" in x][:4]
     assert len(waits) == 4 and min(waits) >= 8, waits
+
+
+@pytest.mark.parametrize("inst", [i for i in DEFAULT if i.endswith("Li4E")])
+def test_head_group_lockstep_barrier(asm, inst):
+    body, _ = _body(asm, inst)
+    code = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", ".")) and
+            not l.strip().endswith(":")]
+    bars = [j for j, l in enumerate(code) if l.startswith("s_barrier")]
+    # the other barriers (Q quantization, epilogue) follow their LDS writes'
+    # lgkmcnt wait
+    free = [j for j in bars if not any(x.startswith("s_waitcnt") for x in code[j - 4:j])]
+    fmt = int(re.findall(r"Li(\d+)E", inst)[0])
+    assert len(free) == (0 if fmt in (5, 6) else 1), [code[j - 4:j + 1] for j in bars]
 
 
 def _writes(line, reg):
