@@ -60,17 +60,17 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "c8240530deadf256",
-    "32k": dict(fetch_bytes=4297995464, write_bytes=4325676),
-    "cfg2": dict(fetch_bytes=269360985, write_bytes=1081620),
-    "cfg3": dict(fetch_bytes=1284624024, write_bytes=4182780),
-    "cfg4c": dict(fetch_bytes=270888223, write_bytes=4259977),
-    "cfg5": dict(fetch_bytes=806206338, write_bytes=540681),
-    "cfg5_e2m1": dict(fetch_bytes=538434012, write_bytes=1081363),
-    "cfg5_nvfp4": dict(fetch_bytes=604671791, write_bytes=1081362),
-    "cfg3_e2m3": dict(fetch_bytes=1158248455, write_bytes=4011172),
-    "cfg3_e2m1": dict(fetch_bytes=657845728, write_bytes=4102795),
-    "cfg3_nvfp4": dict(fetch_bytes=784736756, write_bytes=4094412),
+    "sources_sha256_16": "0620cba350448aa0",
+    "32k": dict(fetch_bytes=4297993971, write_bytes=4325669),
+    "cfg2": dict(fetch_bytes=269361268, write_bytes=1081620),
+    "cfg3": dict(fetch_bytes=1284623139, write_bytes=4182778),
+    "cfg4c": dict(fetch_bytes=270887964, write_bytes=4259977),
+    "cfg5": dict(fetch_bytes=806207498, write_bytes=540681),
+    "cfg5_e2m1": dict(fetch_bytes=538445533, write_bytes=1081362),
+    "cfg5_nvfp4": dict(fetch_bytes=604679625, write_bytes=1081362),
+    "cfg3_e2m3": dict(fetch_bytes=875298041, write_bytes=4011136),
+    "cfg3_e2m1": dict(fetch_bytes=652848515, write_bytes=4102776),
+    "cfg3_nvfp4": dict(fetch_bytes=784536046, write_bytes=4094414),
 }
 
 
