@@ -165,7 +165,15 @@ typedef struct mj_config {
  * workgroups per CU; four waves of items of >= 2048 tokens balance the tail
  * across CUs and XCDs); e2m1 / nvfp4 with n_q <= 32 -> 2 / 1; everything
  * else (16 < n_q <= 32, fp6 (e2m3 / e3m2), n_q > 32) -> 1 / 1 (one wave).
- * min_chunk_tokens is rounded up to whole KV tiles. */
+ * min_chunk_tokens is rounded up to whole KV tiles.  A batch whose
+ * num_seqs*h_k*ceil(n_q/64) workgroups already reach every CU, and whose
+ * block-table rows allow no split of more than 2*num_cus workgroups
+ * (min(S, num_seqs*max(1, min(max_splits, floor(row tiles / min chunk
+ * tiles)))) items at the default: the chunks of at least the floor that a
+ * full row holds), plans one workgroup per CU instead: such a split
+ * balances nothing and only adds the merge (32 sequences of 4K tokens x 8 KV
+ * heads on 256 CUs: the same kernel time, a graph step 7 us shorter).  A
+ * wgs_per_cu or slots_override given in the config is always kept. */
 
 /* What a plan decided (runner.py, StepPlan). */
 typedef struct mj_plan_info {
@@ -179,7 +187,8 @@ typedef struct mj_plan_info {
   int32_t kv_tile_tokens;
   int32_t min_chunk_tiles;  /* floor of the chunk for this q_len                */
   int32_t wgs_per_cu;       /* workgroups per CU the slot count was sized with
-                               (the config's value or the default above)      */
+                               (the config's value or the default above, for
+                               this batch size and table width)              */
 } mj_plan_info;
 
 /* Arguments of mj_paged_decode.  All strides are in BYTES for the KV cache and

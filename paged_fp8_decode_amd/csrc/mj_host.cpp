@@ -102,18 +102,54 @@ bool splittable(const mj_config* c, const Derived& d, int q_len, int max_blocks)
   return (table_tokens(c, max_blocks) + d.kv_tile - 1) / d.kv_tile > min_chunk_tiles(c, d, q_len);
 }
 
-bool plan_splits(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
-  return c->max_splits > 1 && num_seqs < slots_for(c, d, q_len) && splittable(c, d, q_len, max_blocks);
+// Workgroups per CU a batch's plan targets: the format's default, except one
+// when the batch's (sequence, KV head, row tile) workgroups already reach
+// every CU and a split its table width allows could not make more than two
+// per CU (one resident round of the four-wave kernel), counting the chunks of
+// at least the floor that a full row holds (a shorter remainder adds a short
+// workgroup, not a round): such a split balances nothing and only adds the
+// merge.  Measured on 32 sequences of 4K tokens x
+// 8 KV heads on 256 CUs: the decode kernel 46.7 us whole and 46.9 us in two
+// splits; the graph step 56.3 and 63.7 us.  Decided by the configuration,
+// the batch size, q_len and the table width (fixed when a graph is
+// captured), never by the lengths; explicit wgs_per_cu or slots_override
+// settings are kept as given.
+int wgs_for(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
+  const int w = plan_shape(c, d, q_len).wgs_per_cu;
+  if (c->wgs_per_cu > 0 || c->slots_override > 0 || w <= 1) return w;
+  const int64_t per_seq = (int64_t)c->h_k * row_tiles(c, q_len);
+  if ((int64_t)num_seqs * per_seq < d.num_cus) return w;
+  const int64_t tiles = (table_tokens(c, max_blocks) + d.kv_tile - 1) / d.kv_tile;
+  const int64_t mc = min_chunk_tiles(c, d, q_len);
+  const int64_t per_row = std::max<int64_t>(1, std::min<int64_t>(c->max_splits, tiles / mc));
+  const int64_t most = std::min<int64_t>(slots_for(c, d, q_len), (int64_t)num_seqs * per_row);
+  return most * per_seq <= 2 * (int64_t)d.num_cus ? 1 : w;
 }
 
-// The grid of a plan: fixed by the config, q_len and the table width.
-int work_for(const mj_config* c, const Derived& d, int q_len, int max_blocks) {
-  return splittable(c, d, q_len, max_blocks) ? cap_for(c, d, q_len) : c->max_num_seqs;
+// The slots (work items of one round) of a batch's plan: slots_for at the
+// batch's workgroups per CU.
+int batch_slots(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
+  if (c->slots_override > 0) return c->slots_override;
+  const int64_t denom = (int64_t)c->h_k * row_tiles(c, q_len);
+  return (int)std::max<int64_t>(1, ((int64_t)d.num_cus * wgs_for(c, d, num_seqs, q_len, max_blocks)) / denom);
+}
+
+bool plan_splits(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
+  return c->max_splits > 1 && num_seqs < batch_slots(c, d, num_seqs, q_len, max_blocks) &&
+         splittable(c, d, q_len, max_blocks);
+}
+
+// The grid of a plan: fixed by the config, the batch size, q_len and the
+// table width (at most cap_for, which the plan buffer is laid out for).
+int work_for(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
+  return splittable(c, d, q_len, max_blocks)
+             ? std::max(batch_slots(c, d, num_seqs, q_len, max_blocks), c->max_num_seqs)
+             : c->max_num_seqs;
 }
 
 void shape_info(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks, mj_plan_info* info) {
-  info->num_work = work_for(c, d, q_len, max_blocks);
-  info->slots = slots_for(c, d, q_len);
+  info->num_work = work_for(c, d, num_seqs, q_len, max_blocks);
+  info->slots = batch_slots(c, d, num_seqs, q_len, max_blocks);
   info->chunk_tiles = -1;
   info->num_chunks = -1;
   info->with_reduction = plan_splits(c, d, num_seqs, q_len, max_blocks) ? 1 : 0;
@@ -121,7 +157,7 @@ void shape_info(const mj_config* c, const Derived& d, int num_seqs, int q_len, i
   info->q_len = q_len;
   info->kv_tile_tokens = d.kv_tile;
   info->min_chunk_tiles = min_chunk_tiles(c, d, q_len);
-  info->wgs_per_cu = plan_shape(c, d, q_len).wgs_per_cu;
+  info->wgs_per_cu = wgs_for(c, d, num_seqs, q_len, max_blocks);
 }
 
 mj_status derive(const mj_config* c, Derived* d) {
@@ -267,8 +303,8 @@ mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, in
   }
   auto ceil_div = [](int64_t a, int64_t b) -> int64_t { return (a + b - 1) / b; };
 
-  const int S = slots_for(cfg, d, q_len);
-  const int cap = work_for(cfg, d, q_len, max_blocks_per_seq);
+  const int S = batch_slots(cfg, d, num_seqs, q_len, max_blocks_per_seq);
+  const int cap = work_for(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   const bool split = plan_splits(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   int64_t c = std::max<int64_t>(1, max_tiles);
   if (split) {
@@ -328,7 +364,7 @@ mj_status mj_plan_compute(const mj_config* cfg, const int32_t* seq_lens_host, in
   info->q_len = q_len;
   info->kv_tile_tokens = d.kv_tile;
   info->min_chunk_tiles = min_chunk_tiles(cfg, d, q_len);
-  info->wgs_per_cu = plan_shape(cfg, d, q_len).wgs_per_cu;
+  info->wgs_per_cu = wgs_for(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   return MJ_OK;
 }
 
@@ -375,7 +411,7 @@ static mj_status plan_device(const mj_config* cfg, const Derived& d, const int32
     return MJ_EINVAL;
   if (num_seqs > cfg->max_num_seqs || q_len > cfg->max_q_len) return MJ_ECAPACITY;
   if (!aligned(plan_dev, 16) || !aligned(seq_lens_dev, 4)) return MJ_EALIGN;
-  const int S = slots_for(cfg, d, q_len);
+  const int S = batch_slots(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   const bool split = plan_splits(cfg, d, num_seqs, q_len, max_blocks_per_seq);
   mj::PlanParams p;
   p.seq_lens = seq_lens_dev;
@@ -455,7 +491,7 @@ static mj_status fill_decode(const mj_config* cfg, const Derived& d, const mj_de
         a->v_bs_head_stride % 8)
       return MJ_EALIGN;
   }
-  if (a->num_work != work_for(cfg, d, a->q_len, a->max_blocks_per_seq)) return MJ_EINVAL;
+  if (a->num_work != work_for(cfg, d, a->num_seqs, a->q_len, a->max_blocks_per_seq)) return MJ_EINVAL;
   const bool split = plan_splits(cfg, d, a->num_seqs, a->q_len, a->max_blocks_per_seq);
   if ((a->with_reduction != 0) != split) return MJ_EINVAL;
   const WorkspaceLayout wl = workspace_layout(cfg, d);
@@ -599,7 +635,7 @@ mj_status mj_decode_step(const mj_config* cfg, const mj_step_args* sa, hipStream
     p.plan_in_kernel = 1;
     p.plan_margin = sa->margin;
     p.plan_max_splits = cfg->max_splits;
-    p.plan_slots = slots_for(cfg, d, a.q_len);
+    p.plan_slots = batch_slots(cfg, d, a.num_seqs, a.q_len, a.max_blocks_per_seq);
     p.plan_split = a.with_reduction ? 1 : 0;
     p.plan_min_chunk = min_chunk_tiles(cfg, d, a.q_len);
     p.ns_out = const_cast<int32_t*>(p.n_splits);

@@ -423,15 +423,17 @@ def test_library_default_plan_parameters(fmt, n_q, wgs, floor_tiles):
 # as the sequences):
 #   cfg1: e4m3 4 rows: S = 256*8/2 = 1024; the 32-page row is 4 tiles <= the
 #         16-tile floor: never split, one item, no merge, grid max_num_seqs = 1.
-#   cfg2: S = 256*8/8 = 256; 32 tiles > 16; c = max(ceil(32/16), 16) = 16 ->
-#         2 items x 32 = 64 <= 256; grid 256.
+#   cfg2: 32 x 8 workgroups reach all 256 CUs, and the 256-page row (32
+#         tiles, 2 chunks of the 16-tile floor) could make at most 64 items
+#         x 8 = 512 = two workgroups per CU: one workgroup per CU, S =
+#         256/8 = 32 = b: no split, no merge, grid 32.
 #   cfg4: 32 rows: S = 256/8 = 32; 64 tiles; 16*ceil(64/c) <= 32 -> c = 32,
 #         2 x 16 = 32 items; grid 32.
 #   cfg5: e2m3: S = 32; 1024 tiles; 4*ceil(1024/c) <= 32 -> c = 128, 8 x 4.
 #   32k:  S = 256; 256 tiles; 64*ceil(256/c) <= 256 -> c = 64, 4 x 64 = 256.
 @pytest.mark.parametrize("b,h_q,h_k,q_len,L,P_,fmt,expect", [
     (1, 8, 2, 1, 512, 16, "e4m3", (1024, 4, 1, 1, 0, 1)),
-    (32, 32, 8, 1, 4096, 16, "e4m3", (256, 16, 2, 64, 1, 256)),
+    (32, 32, 8, 1, 4096, 16, "e4m3", (32, 32, 1, 32, 0, 32)),
     (16, 64, 8, 4, 8192, 32, "e4m3", (32, 32, 2, 32, 1, 32)),
     (4, 32, 8, 1, 131072, 128, "e2m3", (32, 128, 8, 32, 1, 32)),
     (64, 32, 8, 1, 32768, 64, "e4m3", (256, 64, 4, 256, 1, 256)),
@@ -442,6 +444,29 @@ def test_library_default_workload_plans(b, h_q, h_k, q_len, L, P_, fmt, expect):
     work, ns, _ = _unpack(cfg, img, q_len)
     items = int(np.sum(work[:, 0] >= 0))
     assert (info.slots, info.chunk_tiles, int(ns[0]), items, info.with_reduction, info.num_work) == expect
+
+
+# Batches that already reach every CU plan one workgroup per CU when no split
+# their block-table rows allow could make more than two workgroups per CU (a
+# split would only add the merge); wider rows, smaller batches and explicit
+# settings keep the format's default.
+@pytest.mark.parametrize("b,max_blocks,wgs_cfg,expect", [
+    # (workgroups per CU, slots, with_reduction, num_work); max_num_seqs 64
+    (32, 256, 0, (1, 32, 0, 64)),      # cfg2's shape: 32 x 8 pairs, rows of 4K tokens
+    (32, 258, 0, (1, 32, 0, 64)),      # two pages more: a 33rd tile is no third chunk
+    (32, 384, 0, (8, 256, 1, 256)),    # rows of 6K tokens: three chunks of the floor
+    (32, 2048, 0, (8, 256, 1, 256)),   # rows of 32K tokens: splits can add rounds
+    (16, 256, 0, (8, 256, 1, 256)),    # 16 x 8 pairs leave CUs idle
+    (64, 256, 0, (8, 256, 1, 256)),    # 64 x 8 pairs in two chunks: four per CU
+    (32, 256, 8, (8, 256, 1, 256)),    # wgs_per_cu given: kept
+    (32, 16, 0, (1, 32, 0, 64)),       # rows within the chunk floor: never split
+])
+def test_one_round_batches_do_not_split(b, max_blocks, wgs_cfg, expect):
+    cfg = _cfg(h_q=32, h_k=8, page_size=16, max_num_seqs=64, max_q_len=1, wgs_per_cu=wgs_cfg, kv_format="e4m3")
+    shp = mj.mj_plan_shape(cfg, b, 1, max_blocks)
+    _, info = mj.mj_plan_compute(cfg, [max_blocks * 16] * b, 1, 0, max_blocks)
+    got = (info.wgs_per_cu, info.slots, info.with_reduction, info.num_work)
+    assert got == (shp.wgs_per_cu, shp.slots, shp.with_reduction, shp.num_work) == expect
 
 
 @no_gpu
