@@ -62,7 +62,7 @@ TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_intern
 TRAFFIC = {
     "sources_sha256_16": "0620cba350448aa0",
     "32k": dict(fetch_bytes=4297993971, write_bytes=4325669),
-    "cfg2": dict(fetch_bytes=269361268, write_bytes=1081620),
+    "cfg2": dict(fetch_bytes=269030430, write_bytes=266786),
     "cfg3": dict(fetch_bytes=1284623139, write_bytes=4182778),
     "cfg4c": dict(fetch_bytes=270887964, write_bytes=4259977),
     "cfg5": dict(fetch_bytes=806207498, write_bytes=540681),
