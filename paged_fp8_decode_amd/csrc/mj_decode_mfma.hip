@@ -800,8 +800,9 @@ __device__ __forceinline__ void granule_any(const Ctx& c, const QOps<FMT, NRB>& 
 // OCC: waves per SIMD the register budget is fitted to.
 // CP: cache policy of the KV loads, bit 0 = K non-temporal, bit 1 = V
 // non-temporal.
-// W: waves per workgroup (4, or 8 for a 32-row tile that runs alone on its
-// CU: two waves per SIMD without cutting the item into more splits).
+// W: waves per workgroup (4; 8 for a 32-row tile that runs alone on its
+// CU, two waves per SIMD without cutting the item into more splits, and for
+// two-head groups).
 // HG: KV heads per workgroup (1; 2 or 4 for token-major pages of packed
 // rows): head h of the group gets waves [h W / HG, (h + 1) W / HG), which
 // share its granules as the W waves of a one-head workgroup do.  The heads'
@@ -970,11 +971,13 @@ void decode_mfma_kernel(DecodeParams p) {
   const int ngr = (c.j1 - c.j0 + kGran - 1) / kGran;
   int gi = wave % kWph;
   const bool run = gi < ngr;
-  // lockstep period per format (cfg3's shape, kernel GB/s against none:
-  // e2m3 every 4 granules +4.7 %, e2m1 every 2 +6.9 %; nvfp4, whose shared
-  // lines are its block-scale rows across the two groups of an item, gained
-  // nothing at any period)
-  constexpr int kLock = HG == 1 || F::kBlockScaled ? 0 : (F::kPacked6 ? 4 : 2);
+  // lockstep period per format (cfg3's shape; with two waves per head,
+  // kernel GB/s against none: e2m3 every 4 granules +4.7 %, e2m1 every 2
+  // +6.9 %; with one wave per head, kernel us at periods 2 / 4 / 8 (e2m3)
+  // and 1 / 2 / 4 (e2m1): 179.9 / 181.8 / 183.7 and 133.2 / 132.9 / 130.0;
+  // nvfp4, whose shared lines are its block-scale rows across the two groups
+  // of an item, gained nothing at any period)
+  constexpr int kLock = HG == 1 || F::kBlockScaled ? 0 : (F::kPacked6 ? 2 : 4);
   const int lock_end = ngr / kWph;
   int lock_it = 0;
   KRows<FMT> K0 = load_k<FMT, (CP & 1) != 0>(c, gi), K1;
@@ -1348,12 +1351,16 @@ hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Head groups (hg = 2 or 4 KV heads per workgroup, eight waves) for the
-// packed formats at up to 16 rows.
+// Head groups for the packed formats at up to 16 rows: four KV heads per
+// workgroup in four waves, one per head (two workgroups per CU, so that one
+// group's prologue and epilogue overlap another's streaming; against eight
+// waves, two per head, one workgroup per CU on the ragged batch in
+// token-major pages: e2m3 196 -> 183 us, e2m1 140 -> 133, nvfp4 170 -> 164),
+// or two heads in eight waves.
 template <int FMT, int NQB>
 hipError_t launch_groups(const DecodeParams& p, int cp, int hg, hipStream_t s) {
   if constexpr (Fmt<FMT>::kPacked6 || FMT == 4 || FMT == 5 || FMT == 6) {
-    return hg == 4 ? launch_shape<FMT, NQB, 1, 1, 2, 8, 4>(p, cp, s) : launch_shape<FMT, NQB, 1, 1, 2, 8, 2>(p, cp, s);
+    return hg == 4 ? launch_shape<FMT, NQB, 1, 1, 2, 4, 4>(p, cp, s) : launch_shape<FMT, NQB, 1, 1, 2, 8, 2>(p, cp, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -45,11 +45,11 @@ DEFAULT = [
            "Li4ELi16ELi2ELi2ELi1ELi2ELi8ELi1E", "Li5ELi4ELi1ELi2ELi1ELi2ELi4ELi1E", "Li5ELi8ELi1ELi2ELi1ELi2ELi4ELi1E",
            "Li5ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li5ELi16ELi2ELi2ELi1ELi1ELi4ELi1E", "Li6ELi4ELi1ELi2ELi1ELi2ELi4ELi1E",
            "Li6ELi8ELi1ELi2ELi1ELi2ELi4ELi1E", "Li6ELi16ELi1ELi2ELi1ELi2ELi4ELi1E", "Li6ELi16ELi2ELi2ELi1ELi1ELi4ELi1E",
-           "Li1ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li1ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li1ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
-           "Li3ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li3ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li3ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
-           "Li4ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li4ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li4ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
-           "Li5ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li5ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li5ELi16ELi1ELi0ELi1ELi2ELi8ELi4E",
-           "Li6ELi4ELi1ELi0ELi1ELi2ELi8ELi4E", "Li6ELi8ELi1ELi0ELi1ELi2ELi8ELi4E", "Li6ELi16ELi1ELi0ELi1ELi2ELi8ELi4E"]
+           "Li1ELi4ELi1ELi0ELi1ELi2ELi4ELi4E", "Li1ELi8ELi1ELi0ELi1ELi2ELi4ELi4E", "Li1ELi16ELi1ELi0ELi1ELi2ELi4ELi4E",
+           "Li3ELi4ELi1ELi0ELi1ELi2ELi4ELi4E", "Li3ELi8ELi1ELi0ELi1ELi2ELi4ELi4E", "Li3ELi16ELi1ELi0ELi1ELi2ELi4ELi4E",
+           "Li4ELi4ELi1ELi0ELi1ELi2ELi4ELi4E", "Li4ELi8ELi1ELi0ELi1ELi2ELi4ELi4E", "Li4ELi16ELi1ELi0ELi1ELi2ELi4ELi4E",
+           "Li5ELi4ELi1ELi0ELi1ELi2ELi4ELi4E", "Li5ELi8ELi1ELi0ELi1ELi2ELi4ELi4E", "Li5ELi16ELi1ELi0ELi1ELi2ELi4ELi4E",
+           "Li6ELi4ELi1ELi0ELi1ELi2ELi4ELi4E", "Li6ELi8ELi1ELi0ELi1ELi2ELi4ELi4E", "Li6ELi16ELi1ELi0ELi1ELi2ELi4ELi4E"]
 
 
 @pytest.fixture(scope="module")
