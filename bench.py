@@ -60,17 +60,17 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "0620cba350448aa0",
-    "32k": dict(fetch_bytes=4297993971, write_bytes=4325669),
-    "cfg2": dict(fetch_bytes=269030430, write_bytes=266786),
-    "cfg3": dict(fetch_bytes=1284623139, write_bytes=4182778),
-    "cfg4c": dict(fetch_bytes=270887964, write_bytes=4259977),
-    "cfg5": dict(fetch_bytes=806207498, write_bytes=540681),
-    "cfg5_e2m1": dict(fetch_bytes=538445533, write_bytes=1081362),
-    "cfg5_nvfp4": dict(fetch_bytes=604679625, write_bytes=1081362),
-    "cfg3_e2m3": dict(fetch_bytes=875298041, write_bytes=4011136),
-    "cfg3_e2m1": dict(fetch_bytes=652848515, write_bytes=4102776),
-    "cfg3_nvfp4": dict(fetch_bytes=784536046, write_bytes=4094414),
+    "sources_sha256_16": "984c50e08637e38c",
+    "32k": dict(fetch_bytes=4297992207, write_bytes=4325671),
+    "cfg2": dict(fetch_bytes=269030447, write_bytes=266786),
+    "cfg3": dict(fetch_bytes=1284621854, write_bytes=4182779),
+    "cfg4c": dict(fetch_bytes=270888125, write_bytes=4259977),
+    "cfg5": dict(fetch_bytes=806187245, write_bytes=540681),
+    "cfg5_e2m1": dict(fetch_bytes=538439451, write_bytes=1081362),
+    "cfg5_nvfp4": dict(fetch_bytes=604666721, write_bytes=1081362),
+    "cfg3_e2m3": dict(fetch_bytes=861276858, write_bytes=4011294),
+    "cfg3_e2m1": dict(fetch_bytes=653109637, write_bytes=4102848),
+    "cfg3_nvfp4": dict(fetch_bytes=707356716, write_bytes=4094670),
 }
 
 
