@@ -108,12 +108,11 @@ bool splittable(const mj_config* c, const Derived& d, int q_len, int max_blocks)
 // per CU (one resident round of the four-wave kernel), counting the chunks of
 // at least the floor that a full row holds (a shorter remainder adds a short
 // workgroup, not a round): such a split balances nothing and only adds the
-// merge.  Measured on 32 sequences of 4K tokens x
-// 8 KV heads on 256 CUs: the decode kernel 46.7 us whole and 46.9 us in two
-// splits; the graph step 56.3 and 63.7 us.  Decided by the configuration,
-// the batch size, q_len and the table width (fixed when a graph is
-// captured), never by the lengths; explicit wgs_per_cu or slots_override
-// settings are kept as given.
+// merge.  Measured on 32 sequences of 4K tokens x 8 KV heads on 256 CUs: the
+// decode kernel 46.7 us whole and 46.9 us in two splits; the graph step 56.3
+// and 63.7 us.  Decided by the configuration, the batch size, q_len and the
+// table width (fixed when a graph is captured), never by the lengths;
+// explicit wgs_per_cu or slots_override settings are kept as given.
 int wgs_for(const mj_config* c, const Derived& d, int num_seqs, int q_len, int max_blocks) {
   const int w = plan_shape(c, d, q_len).wgs_per_cu;
   if (c->wgs_per_cu > 0 || c->slots_override > 0 || w <= 1) return w;
