@@ -141,10 +141,12 @@ typedef struct mj_config {
                               group of exactly one 32-row tile, e4m3 with
                               fp8 Q or e2m1; two granules of prefetch
                               always run four), bits 4-5 KV heads per
-                              workgroup (0 the library's choice, 1 one, 2
-                              two, 3 four; more than one only for the packed
-                              formats at up to 16 query rows per KV head,
-                              h_k a multiple, no in-kernel merge)            */
+                              workgroup (0 the library's choice: four for
+                              token-major packed pages, eight for e2m1 when
+                              h_k is a multiple of 8; 1 one, 2 two, 3 four;
+                              more than one only for the packed formats at
+                              up to 16 query rows per KV head, h_k a
+                              multiple, no in-kernel merge)                  */
   int32_t kv_cache_policy; /* matrix-core kernel KV loads: 0 the library's
                               choice (K cached, V non-temporal), 1 every load
                               cached, 2 every load non-temporal, 3 K cached

@@ -803,12 +803,13 @@ __device__ __forceinline__ void granule_any(const Ctx& c, const QOps<FMT, NRB>& 
 // W: waves per workgroup (4; 8 for a 32-row tile that runs alone on its
 // CU, two waves per SIMD without cutting the item into more splits, and for
 // two-head groups).
-// HG: KV heads per workgroup (1; 2 or 4 for token-major pages of packed
-// rows): head h of the group gets waves [h W / HG, (h + 1) W / HG), which
-// share its granules as the W waves of a one-head workgroup do.  The heads'
-// rows of one token are adjacent in such pages and fill whole 128-byte
-// lines together (4 x 96 bytes, 2 x 64), so that each line is fetched once,
-// by one CU, instead of once for each of the heads whose rows it holds.
+// HG: KV heads per workgroup (1; 2, 4 or 8 (e2m1) for token-major pages of
+// packed rows): head h of the group gets waves [h W / HG, (h + 1) W / HG),
+// which share its granules as the W waves of a one-head workgroup do.  The
+// heads' rows of one token are adjacent in such pages and fill whole
+// 128-byte lines together (4 x 96 bytes, 2 x 64), so that each line is
+// fetched once, by one CU, instead of once for each of the heads whose rows
+// it holds.
 template <int FMT, int NQB, int NRB, int CP, int PF, int OCC, int W, int HG = 1>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void decode_mfma_kernel(DecodeParams p) {
@@ -1356,10 +1357,16 @@ hipError_t launch_shape(const DecodeParams& p, int cp, hipStream_t s) {
 // group's prologue and epilogue overlap another's streaming; against eight
 // waves, two per head, one workgroup per CU on the ragged batch in
 // token-major pages: e2m3 196 -> 183 us, e2m1 140 -> 133, nvfp4 170 -> 164),
-// or two heads in eight waves.
+// eight heads in eight waves for e2m1 (a token's eight 64-byte rows are one
+// 512-byte run: 130.3 -> 127.1 us; e2m3 and nvfp4 were 2-3 % slower so), or
+// two heads in eight waves.
 template <int FMT, int NQB>
 hipError_t launch_groups(const DecodeParams& p, int cp, int hg, hipStream_t s) {
   if constexpr (Fmt<FMT>::kPacked6 || FMT == 4 || FMT == 5 || FMT == 6) {
+    if constexpr (FMT == 4) {
+      if (hg == 8) return launch_shape<FMT, NQB, 1, 1, 2, 8, 8>(p, cp, s);
+    }
+    if (hg == 8) return hipErrorInvalidValue;
     return hg == 4 ? launch_shape<FMT, NQB, 1, 1, 2, 4, 4>(p, cp, s) : launch_shape<FMT, NQB, 1, 1, 2, 8, 2>(p, cp, s);
   } else {
     return hipErrorInvalidValue;
@@ -1435,6 +1442,10 @@ hipError_t launch_decode_mfma(const DecodeParams& p_in, int kv_format, int cache
     const bool cp_ok = cache_policy < 0 || cache_policy == 0 || cache_policy == 2;
     if (adjacent && cp_ok && (int64_t)p.num_work * (p.h_k / want) >= p.num_cus) hg = want;
   }
+  // e2m1: all eight heads of a token in one workgroup where h_k allows it
+  // and the grid still gives every CU a workgroup
+  if (hsel == 0 && hg == 4 && kv_format == 3 && p.h_k % 8 == 0 && (int64_t)p.num_work * (p.h_k / 8) >= p.num_cus)
+    hg = 8;
   if (kv_format == 0 || p.n_q > 16 || p.counters || p.h_k % hg) hg = 1;
   // head groups share no lines across workgroups: the plain grid (measured:
   // e2m1 143.6 -> 136.5 us, nvfp4 169.5 -> 168.3)

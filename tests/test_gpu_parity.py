@@ -272,6 +272,28 @@ def test_sub_byte_edge_lengths_and_shapes(mj, gpu, key, variant):
             assert torch.all(out[:1].float() == 0)  # L = 0
 
 
+def test_e2m1_eight_head_groups(mj, gpu):
+    """e2m1 in token-major pages takes eight KV heads per workgroup when h_k
+    is a multiple of 8 and the grid still gives every CU a workgroup (a small
+    CU count in the config reaches that at these sizes).  Each head is one
+    wave over the same granules in the same order as in the four-head groups
+    (decode_kernel 58), so the outputs match those bit for bit, and the
+    oracle within the usual bounds; edge lengths as above."""
+    lens = (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, 1000)
+    for q_len, h_q, h_k in ((1, 32, 8), (2, 16, 8), (4, 8, 8), (2, 32, 8), (4, 32, 8), (1, 64, 16)):
+        wl = synth.build(synth.spec_for("cfg3_e2m1", small=True, b=len(lens), lens=lens, lens_loguniform=(),
+                                        q_len=q_len, h_q=h_q, h_k=h_k, causal=True, k_outliers=0,
+                                        slots_override=0), gpu)
+        say(f"  e2m1 eight-head groups q_len={q_len} h_q={h_q} h_k={h_k}")
+        out8, lse8, _ = _run(mj, wl, num_cus=2, **FINE)
+        out4, lse4, _ = _run(mj, wl, num_cus=2, decode_kernel=58, **FINE)
+        O, LSE = oracle_step(wl)
+        compare_out(out8, O, f"e2m1 eight-head q_len={q_len} h_q={h_q} h_k={h_k}")
+        compare_lse(lse8, LSE, f"e2m1 eight-head q_len={q_len} h_q={h_q} h_k={h_k}")
+        assert torch.equal(out8.view(torch.int16), out4.view(torch.int16))
+        assert torch.equal(lse8, lse4)
+
+
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
 def test_edge_lengths(mj, gpu, variant):
     # empty (padding) request, a single token, a length inside the first
