@@ -60,17 +60,17 @@ if ROOT not in sys.path:
 # kernel sources hash to the value the counters were taken with.
 TRAFFIC_SOURCES = ("mj_decode_mfma.hip", "mj_merge.h", "mj_device.h", "mj_internal.h")
 TRAFFIC = {
-    "sources_sha256_16": "984c50e08637e38c",
-    "32k": dict(fetch_bytes=4297992207, write_bytes=4325671),
-    "cfg2": dict(fetch_bytes=269030447, write_bytes=266786),
-    "cfg3": dict(fetch_bytes=1284621854, write_bytes=4182779),
-    "cfg4c": dict(fetch_bytes=270888125, write_bytes=4259977),
-    "cfg5": dict(fetch_bytes=806187245, write_bytes=540681),
-    "cfg5_e2m1": dict(fetch_bytes=538439451, write_bytes=1081362),
-    "cfg5_nvfp4": dict(fetch_bytes=604666721, write_bytes=1081362),
-    "cfg3_e2m3": dict(fetch_bytes=861276858, write_bytes=4011294),
-    "cfg3_e2m1": dict(fetch_bytes=653109637, write_bytes=4102848),
-    "cfg3_nvfp4": dict(fetch_bytes=707356716, write_bytes=4094670),
+    "sources_sha256_16": "00a425ce9c4ef621",
+    "32k": dict(fetch_bytes=4298008181, write_bytes=4325676),
+    "cfg2": dict(fetch_bytes=269040771, write_bytes=266786),
+    "cfg3": dict(fetch_bytes=1284662197, write_bytes=4182779),
+    "cfg4c": dict(fetch_bytes=270878984, write_bytes=4259977),
+    "cfg5": dict(fetch_bytes=806196733, write_bytes=540681),
+    "cfg5_e2m1": dict(fetch_bytes=538387600, write_bytes=1081363),
+    "cfg5_nvfp4": dict(fetch_bytes=604680679, write_bytes=1081362),
+    "cfg3_e2m3": dict(fetch_bytes=861220086, write_bytes=4011291),
+    "cfg3_e2m1": dict(fetch_bytes=653061632, write_bytes=4102751),
+    "cfg3_nvfp4": dict(fetch_bytes=708577277, write_bytes=4094649),
 }
 
 
